@@ -1,0 +1,279 @@
+"""CPU oracle for the W4A16 NVFP4 matrix multiply.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this package.  The product path
+(the HIP library and its Python binding) never imports, links or calls it, and
+the two share no code.
+
+Two independent implementations of the same plain definition live here:
+
+* the C oracle (``nvfp4_oracle.c``, fp64, OpenMP over output columns), used
+  for parity and for the CPU baseline timing;
+* a numpy twin (``*_np`` functions below), fp64 with ``np.matmul`` as its only
+  library step, used to pin the C oracle.
+
+The definition (see the header of ``nvfp4_oracle.c`` for the passages of the
+pages each step follows):
+
+    T[n,k]  = e2m1(code(n,k)) * e4m3(S[n, k//16])
+    g       = fp32(1/stored) if the global scale is stored as a divisor else stored
+    X'[m,k] = RNE_bf16(X[m,k] * s[k]) if a pre-quant scale s is given else X[m,k]
+    Y[m,n]  = g * sum_k X'[m,k] * T[n,k]          (fp64, never rounded)
+
+Grouped (MoE) form: rows offsets[e]..offsets[e+1]-1 use expert e's weights and
+global scale; the pre-quant scale is shared by all experts.
+
+Acceptance of a GPU result against the oracle (``accept``): relative Frobenius
+error <= 2e-3, every element within 1e-2 * (|ref| + rms(ref)), and every
+element finite.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nvfp4_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+REL_FRO_TOL = 2e-3
+ELEM_TOL = 1e-2
+
+# E2M1 magnitudes by 3-bit code, from the OCP MX specification's FP4 (E2M1)
+# encoding table: exponent bits 2..1 (bias 1), mantissa bit 0, code 1 subnormal.
+_E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle into ``oracle/_liboracle.so`` (gcc, fp64, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-shared", "-fPIC",
+                               "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            L = ctypes.CDLL(_LIB_PATH)
+            P, I64, I, F, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_double
+            L.oracle_e2m1.argtypes, L.oracle_e2m1.restype = [I], D
+            L.oracle_e4m3.argtypes, L.oracle_e4m3.restype = [I], D
+            L.oracle_round_bf16.argtypes, L.oracle_round_bf16.restype = [D], D
+            L.oracle_global_scale.argtypes, L.oracle_global_scale.restype = [F, I], D
+            L.oracle_dequant.argtypes, L.oracle_dequant.restype = [P, I64, P, I64, I64, I64, P], None
+            L.oracle_activation.argtypes, L.oracle_activation.restype = [P, I64, P, I64, I64, P], None
+            L.oracle_gemm.argtypes = [P, I64, P, P, I64, P, I64, F, I, I64, I64, I64, P, P, I, P]
+            L.oracle_gemm.restype = None
+            L.oracle_gemm_sampled.argtypes = [P, I64, P, P, I64, P, I64, F, I, I64, P, P, I64, P]
+            L.oracle_gemm_sampled.restype = None
+            L.oracle_grouped_gemm.argtypes = [P, I64, P, P, P, I64, P, I64, P, I, I64, I64, I64, I64, P]
+            L.oracle_grouped_gemm.restype = None
+            L.oracle_grouped_gemm_sampled.argtypes = [P, I64, P, P, P, I64, P, I64, P, I, I64, I64, I64,
+                                                      P, P, I64, P]
+            L.oracle_grouped_gemm_sampled.restype = None
+            L.oracle_max_threads.argtypes, L.oracle_max_threads.restype = [], I
+            _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---------------------------------------------------------------- C oracle ---
+
+def e2m1(code: int) -> float:
+    return lib().oracle_e2m1(int(code))
+
+
+def e4m3(byte: int) -> float:
+    return lib().oracle_e4m3(int(byte))
+
+
+def round_bf16(v: float) -> float:
+    return lib().oracle_round_bf16(float(v))
+
+
+def global_scale(stored: float, is_divisor: bool) -> float:
+    return lib().oracle_global_scale(float(stored), int(bool(is_divisor)))
+
+
+def dequant(w_packed: np.ndarray, w_scale: np.ndarray) -> np.ndarray:
+    """Weight tile T [N, K] (fp64) from canonical u8 [N, K/2] codes and u8 [N, K/16] E4M3 scales."""
+    w, s = _c(w_packed, np.uint8), _c(w_scale, np.uint8)
+    N, K = w.shape[0], w.shape[1] * 2
+    out = np.empty((N, K), dtype=np.float64)
+    lib().oracle_dequant(_ptr(w), w.shape[1], _ptr(s), s.shape[1], N, K, _ptr(out))
+    return out
+
+
+def activation(x_bits: np.ndarray, pre_bits: np.ndarray | None) -> np.ndarray:
+    x, p = _c(x_bits, np.uint16), _c(pre_bits, np.uint16)
+    out = np.empty(x.shape, dtype=np.float64)
+    lib().oracle_activation(_ptr(x), x.shape[1], _ptr(p), x.shape[0], x.shape[1], _ptr(out))
+    return out
+
+
+def gemm(x_bits, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None, threads=None) -> np.ndarray:
+    """Dense Y [M, N] in fp64.  x_bits: bf16 bit patterns (uint16) [M, K]."""
+    x, w, s, p = _c(x_bits, np.uint16), _c(w_packed, np.uint8), _c(w_scale, np.uint8), _c(pre_bits, np.uint16)
+    M, K = x.shape
+    N = w.shape[0]
+    assert w.shape[1] * 2 == K and s.shape == (N, K // 16)
+    L = lib()
+    threads = int(threads or L.oracle_max_threads())
+    out = np.empty((M, N), dtype=np.float64)
+    xbuf = np.empty((max(M, 1), K), dtype=np.float64)
+    tbuf = np.empty((threads, max(K, 1)), dtype=np.float64)
+    L.oracle_gemm(_ptr(x), K, _ptr(p), _ptr(w), w.shape[1], _ptr(s), s.shape[1], float(np.float32(g_stored)),
+                  int(bool(g_is_divisor)), M, N, K, _ptr(xbuf), _ptr(tbuf), threads, _ptr(out))
+    return out
+
+
+def gemm_sampled(x_bits, w_packed, w_scale, g_stored, g_is_divisor, pre_bits, rows, cols) -> np.ndarray:
+    """Y[rows[i], cols[i]] for each i, each output computed on its own."""
+    x, w, s, p = _c(x_bits, np.uint16), _c(w_packed, np.uint8), _c(w_scale, np.uint8), _c(pre_bits, np.uint16)
+    r, c = _c(rows, np.int64), _c(cols, np.int64)
+    out = np.empty(r.shape[0], dtype=np.float64)
+    lib().oracle_gemm_sampled(_ptr(x), x.shape[1], _ptr(p), _ptr(w), w.shape[1], _ptr(s), s.shape[1],
+                              float(np.float32(g_stored)), int(bool(g_is_divisor)), x.shape[1],
+                              _ptr(r), _ptr(c), r.shape[0], _ptr(out))
+    return out
+
+
+def grouped_gemm(x_bits, offsets, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None) -> np.ndarray:
+    """Grouped Y [R, N] in fp64.  w_packed [E, N, K/2], w_scale [E, N, K/16], g_stored [E]."""
+    x, o = _c(x_bits, np.uint16), _c(offsets, np.int32)
+    w, s, g, p = _c(w_packed, np.uint8), _c(w_scale, np.uint8), _c(g_stored, np.float32), _c(pre_bits, np.uint16)
+    R, K = x.shape
+    E, N = w.shape[0], w.shape[1]
+    out = np.full((R, N), np.nan, dtype=np.float64)
+    lib().oracle_grouped_gemm(_ptr(x), K, _ptr(o), _ptr(p), _ptr(w), w.shape[2], _ptr(s), s.shape[2], _ptr(g),
+                              int(bool(g_is_divisor)), R, E, N, K, _ptr(out))
+    return out
+
+
+def grouped_gemm_sampled(x_bits, offsets, w_packed, w_scale, g_stored, g_is_divisor, pre_bits, rows, cols):
+    x, o = _c(x_bits, np.uint16), _c(offsets, np.int32)
+    w, s, g, p = _c(w_packed, np.uint8), _c(w_scale, np.uint8), _c(g_stored, np.float32), _c(pre_bits, np.uint16)
+    r, c = _c(rows, np.int64), _c(cols, np.int64)
+    E, N, K = w.shape[0], w.shape[1], x.shape[1]
+    out = np.empty(r.shape[0], dtype=np.float64)
+    lib().oracle_grouped_gemm_sampled(_ptr(x), K, _ptr(o), _ptr(p), _ptr(w), w.shape[2], _ptr(s), s.shape[2],
+                                      _ptr(g), int(bool(g_is_divisor)), E, N, K, _ptr(r), _ptr(c), r.shape[0],
+                                      _ptr(out))
+    return out
+
+
+def max_threads() -> int:
+    return int(lib().oracle_max_threads())
+
+
+# ------------------------------------------------------------ numpy twin ----
+# Independent of the C code: table lookup instead of bit arithmetic for E2M1,
+# vectorised E4M3 decode, an integer-bit bf16 rounding, and np.matmul.
+
+def e2m1_np(codes: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes).astype(np.int64)
+    return np.where(c & 8, -1.0, 1.0) * _E2M1_MAG[c & 7]
+
+
+def e4m3_np(b: np.ndarray) -> np.ndarray:
+    b = np.asarray(b).astype(np.int64)
+    e, m = (b >> 3) & 15, b & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.exp2(e.astype(np.float64) - 10))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(b & 128, -mag, mag)
+
+
+def bf16_np(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def rne_bf16_np(v: np.ndarray) -> np.ndarray:
+    """RNE to bf16 for values that are exact in fp32 (true for a bf16 x bf16 product)."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), np.asarray(v, dtype=np.float64), equal_nan=True), \
+        "rne_bf16_np needs values exact in fp32"
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) & 0xFFFF
+    nan = np.isnan(f)
+    r = np.where(nan, 0x7FC0, r)
+    return bf16_np(r.astype(np.uint16))
+
+
+def dequant_np(w_packed: np.ndarray, w_scale: np.ndarray) -> np.ndarray:
+    w = np.asarray(w_packed, dtype=np.uint8)
+    codes = np.stack([w & 15, w >> 4], axis=-1).reshape(w.shape[0], -1)   # even k = low nibble
+    scale = np.repeat(e4m3_np(w_scale), 16, axis=1)
+    return e2m1_np(codes) * scale
+
+
+def activation_np(x_bits, pre_bits=None) -> np.ndarray:
+    x = bf16_np(x_bits)
+    if pre_bits is not None:
+        x = rne_bf16_np(x * bf16_np(pre_bits)[None, :])
+    return x
+
+
+def global_scale_np(stored, is_divisor) -> float:
+    st = np.float32(stored)
+    return float(np.float32(1.0) / st) if is_divisor else float(st)
+
+
+def gemm_np(x_bits, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None) -> np.ndarray:
+    return global_scale_np(g_stored, g_is_divisor) * np.matmul(activation_np(x_bits, pre_bits),
+                                                               dequant_np(w_packed, w_scale).T)
+
+
+def grouped_gemm_np(x_bits, offsets, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None):
+    x = activation_np(x_bits, pre_bits)
+    E, N = w_packed.shape[0], w_packed.shape[1]
+    out = np.full((x.shape[0], N), np.nan)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            out[a:b] = global_scale_np(g_stored[e], g_is_divisor) * (x[a:b] @ dequant_np(w_packed[e], w_scale[e]).T)
+    return out
+
+
+# ------------------------------------------------------------ acceptance ----
+
+def accept(y, ref, rel_fro_tol: float = REL_FRO_TOL, elem_tol: float = ELEM_TOL):
+    """Return (ok, info) for a result y against the fp64 oracle ref (same shape).
+
+    ok requires: every y finite; ||y-ref||_F / ||ref||_F <= rel_fro_tol; and
+    |y-ref| <= elem_tol * (|ref| + rms(ref)) element-wise (rms over the set).
+    """
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert y.shape == ref.shape, (y.shape, ref.shape)
+    info = {"n": int(y.size)}
+    if y.size == 0:
+        return True, info
+    finite = bool(np.all(np.isfinite(y)))
+    err = np.abs(y - ref)
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(y - ref) / nref) if nref > 0 else float(np.linalg.norm(y - ref))
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    bound = elem_tol * (np.abs(ref) + rms)
+    with np.errstate(invalid="ignore"):
+        bad = int(np.count_nonzero(~(err <= bound)))
+    info.update(finite=finite, rel_fro=rel, bad_elems=bad, max_abs_err=float(np.nanmax(err)) if err.size else 0.0)
+    ok = finite and rel <= rel_fro_tol and bad == 0
+    return ok, info

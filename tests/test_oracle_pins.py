@@ -1,0 +1,324 @@
+"""Pins of the CPU oracle to facts outside itself (runs on CPU, no GPU).
+
+Each test ties the oracle to something it cannot have copied from itself: the
+format tables (OCP MX / OFP8), a library decoder (torch's float8_e4m3fn),
+closed-form hand cases, exact rational arithmetic on tiny inputs, an
+independent numpy twin, and invariants of the definition.  The negative
+controls plant a mistake in a copy of the numpy twin and check that the
+acceptance check catches it.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _same(a, b):
+    """Equal as numbers, NaN == NaN, and the sign of zero must agree."""
+    if math.isnan(a) or math.isnan(b):
+        return math.isnan(a) and math.isnan(b)
+    return a == b and math.copysign(1.0, a) == math.copysign(1.0, b)
+
+
+# ------------------------------------------------------------ formats ------
+
+def test_e2m1_all_codes_match_format_table():
+    table = {int(c): float(v) for c, v in _read_table("e2m1_codes.txt")}
+    assert sorted(table) == list(range(16))
+    for c in range(16):
+        assert _same(oracle.e2m1(c), table[c]), c
+        assert _same(float(oracle.e2m1_np(np.array([c]))[0]), table[c]), c
+
+
+def test_e4m3_named_codes_match_format_table():
+    for b, v in _read_table("e4m3_special.txt"):
+        assert _same(oracle.e4m3(int(b, 16)), float(v)), b
+
+
+def test_e4m3_all_256_codes_match_torch_float8_e4m3fn():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    lib = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = np.array([oracle.e4m3(b) for b in range(256)])
+    twin = oracle.e4m3_np(np.arange(256))
+    for b in range(256):
+        assert _same(mine[b], float(lib[b])), hex(b)
+        assert _same(twin[b], float(lib[b])), hex(b)
+    finite = np.isfinite(mine)
+    assert finite.sum() == 254 and np.nanmax(mine) == 448.0 and np.min(np.abs(mine[finite & (mine != 0)])) == 2.0 ** -9
+
+
+def test_all_code_scale_products_are_exact_in_bf16():
+    """Every e2m1 x finite-e4m3 product is a bf16 value: the decoded tile can be bit-exact."""
+    vals = np.array([oracle.e2m1(c) * oracle.e4m3(b) for c in range(16) for b in range(256)
+                     if math.isfinite(oracle.e4m3(b))])
+    assert vals.size == 16 * 254
+    t = torch.from_numpy(vals)
+    assert torch.equal(t.to(torch.bfloat16).to(torch.float64), t)
+
+
+# ------------------------------------------------------------ hand cases ---
+
+def _hand_inputs(case):
+    N, K = 16, 16
+    codes = np.zeros((N, K), dtype=np.uint8)
+    x = np.full((1, K), 1.0, dtype=np.float32)
+    s = np.full((N, 1), 0x38, dtype=np.uint8)
+    g, div, pre = 1.0, False, None
+    if case == "H1":
+        codes[:] = np.arange(N, dtype=np.uint8)[:, None]
+    elif case == "H2":
+        x[:] = 0.0
+        x[0, 1] = 1.0
+        codes[:] = (np.arange(N)[:, None] + np.arange(K)[None, :]) % 16
+    elif case == "H3":
+        codes[:] = 2
+        s[:, 0] = np.arange(1, N + 1)
+        g = 2.0 ** -4
+    elif case == "H4":
+        codes[:] = 2
+        x[:] = 1.0234375
+        pre = synth.bf16_bits_from_f32(np.full(K, 1.5, dtype=np.float32))
+        g, div = 0.25, True
+    return synth.bf16_bits_from_f32(x), synth.pack_codes(codes), s, g, div, pre
+
+
+@pytest.mark.parametrize("case", ["H1", "H2", "H3", "H4"])
+def test_hand_cases_closed_form(case):
+    expected = {r[0]: [float(v) for v in r[1:]] for r in _read_table("hand_cases.txt")}[case]
+    x, w, s, g, div, pre = _hand_inputs(case)
+    y = oracle.gemm(x, w, s, g, div, pre)
+    yn = oracle.gemm_np(x, w, s, g, div, pre)
+    for n in range(16):
+        assert y[0, n] == expected[n], (case, n, y[0, n], expected[n])
+        assert yn[0, n] == expected[n], (case, n)
+
+
+def test_hand_case_h2_detects_swapped_nibbles():
+    x, w, s, g, div, pre = _hand_inputs("H2")
+    swapped = ((w & 15) << 4) | (w >> 4)
+    y = oracle.gemm(x, swapped, s, g, div, pre)
+    expected = [float(v) for v in _read_table("hand_cases.txt")[1][1:]]
+    assert any(y[0, n] != expected[n] for n in range(16))
+
+
+# ------------------------------------------------------ exact arithmetic ---
+
+def _exact_gemm(x_bits, w, s, g_stored, div, pre_bits):
+    """Exact rational evaluation of the definition, pure Python loops (tiny inputs only)."""
+    def bfv(b):
+        return Fraction(float(oracle.bf16_np(np.array([b]))[0]))
+
+    def e2m1(c):
+        mag = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4),
+               Fraction(6)][c & 7]
+        return -mag if c & 8 else mag
+
+    def e4m3(b):
+        e, m = (b >> 3) & 15, b & 7
+        mag = Fraction(m, 512) if e == 0 else Fraction(8 + m, 8) * Fraction(2) ** (e - 7)
+        return -mag if b & 128 else mag
+
+    M, K = x_bits.shape
+    N = w.shape[0]
+    gv = Fraction(float(np.float32(1.0) / np.float32(g_stored))) if div else Fraction(float(np.float32(g_stored)))
+    out = [[None] * N for _ in range(M)]
+    for m in range(M):
+        xs = []
+        for k in range(K):
+            v = bfv(x_bits[m, k])
+            if pre_bits is not None:
+                v = Fraction(float(torch.tensor(float(v * bfv(pre_bits[k])), dtype=torch.float64)
+                                   .to(torch.bfloat16).to(torch.float64)))
+            xs.append(v)
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                code = (int(w[n, k >> 1]) >> (4 * (k & 1))) & 15
+                acc += xs[k] * e2m1(code) * e4m3(int(s[n, k >> 4]))
+            out[m][n] = gv * acc
+    return out
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_oracle_matches_exact_rational_arithmetic(seed):
+    g = synth.rng(seed)
+    M, N, K = 2, 3, 48
+    x = synth.normal_bf16(g, (M, K))
+    w = synth.random_codes(g, (N, K))
+    s = synth.scales_pow2_mant(g, (N, K // 16), umin=-9, umax=8)
+    pre = synth.awq_prescale(g, K)
+    for div, gst in ((False, 1.0 / 448.0), (True, 2688.0)):
+        for p in (None, pre):
+            y = oracle.gemm(x, w, s, gst, div, p)
+            ex = _exact_gemm(x, w, s, gst, div, p)
+            for m in range(M):
+                for n in range(N):
+                    # fp64 summation of K exact products: error <= K * 2^-52 * sum|terms|
+                    bound = 1e-13 * max(1.0, float(abs(ex[m][n])) * 10)
+                    assert abs(y[m, n] - float(ex[m][n])) <= bound, (m, n, y[m, n], float(ex[m][n]))
+
+
+# ------------------------------------------------------------- rounding ----
+
+def test_round_bf16_matches_torch_on_bf16_products():
+    """X' = RNE_bf16(x*s): for bf16 x bf16 products (exact in fp32) torch's fp32->bf16 cast is RNE."""
+    g = synth.rng(7)
+    a = synth.normal_bf16(g, 4096)
+    b = synth.awq_prescale(g, 4096)
+    prod = oracle.bf16_np(a) * oracle.bf16_np(b)
+    lib = torch.from_numpy(prod.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    mine = np.array([oracle.round_bf16(v) for v in prod])
+    assert np.array_equal(mine, lib)
+    assert np.array_equal(oracle.rne_bf16_np(prod), lib)
+
+
+def test_round_bf16_ties_and_limits():
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: to even -> 1.0; 1 + 3*2^-8 -> 1 + 2^-6
+    assert oracle.round_bf16(1.0 + 2.0 ** -8) == 1.0
+    assert oracle.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert oracle.round_bf16(-(1.0 + 2.0 ** -8)) == -1.0
+    assert oracle.round_bf16(1.0 + 2.0 ** -8 + 2.0 ** -40) == 1.0 + 2.0 ** -7
+    maxbf = (2 - 2.0 ** -7) * 2.0 ** 127
+    assert oracle.round_bf16(maxbf) == maxbf
+    assert oracle.round_bf16(2.0 ** 128 * (1 - 2.0 ** -9)) == math.inf   # halfway above max: to even = 2^128
+    assert oracle.round_bf16(2.0 ** -133) == 2.0 ** -133                  # min subnormal
+    assert oracle.round_bf16(2.0 ** -135) == 0.0
+
+
+def test_global_scale_inversion_is_fp32_reciprocal():
+    for v in [2688.0, 448.0 * 6, 3.0, 0.1, 7.0, 2.0 ** 120]:
+        st = np.float32(v)
+        assert oracle.global_scale(st, True) == float(np.float32(1.0) / st)
+        assert oracle.global_scale(st, False) == float(st)
+
+
+# ---------------------------------------------------------------- twin ----
+
+@pytest.mark.parametrize("case", ["tiny", "ragged"])
+def test_c_oracle_matches_numpy_twin(case):
+    c = synth.tiny_case() if case == "tiny" else synth.ragged_case()
+    y = oracle.gemm(c.x, c.w, c.s, c.g_stored, c.g_is_divisor, c.pre)
+    yn = oracle.gemm_np(c.x, c.w, c.s, c.g_stored, c.g_is_divisor, c.pre)
+    rel = np.linalg.norm(y - yn) / np.linalg.norm(yn)
+    assert rel <= 1e-12
+    assert np.array_equal(oracle.dequant(c.w, c.s), oracle.dequant_np(c.w, c.s))
+
+
+def test_sampled_and_grouped_agree_with_dense():
+    c = synth.ragged_case()
+    y = oracle.gemm(c.x, c.w, c.s, c.g_stored, c.g_is_divisor, c.pre)
+    g = synth.rng(3)
+    rows, cols = g.integers(0, c.M, 200), g.integers(0, c.N, 200)
+    ys = oracle.gemm_sampled(c.x, c.w, c.s, c.g_stored, c.g_is_divisor, c.pre, rows, cols)
+    assert np.allclose(ys, y[rows, cols], rtol=1e-13, atol=1e-13)
+    # grouped with one expert owning every row == dense
+    off = np.array([0, c.M], dtype=np.int32)
+    yg = oracle.grouped_gemm(c.x, off, c.w[None], c.s[None], np.array([c.g_stored], np.float32), c.g_is_divisor,
+                             c.pre)
+    assert np.allclose(yg, y, rtol=1e-13, atol=1e-13)
+
+
+def test_grouped_oracle_matches_twin_and_skips_empty_experts():
+    gc = synth.grouped_case(T=6, E=8, topk=2, N=48, K=64, seed=11)
+    assert len(gc.active) < gc.E or True
+    y = oracle.grouped_gemm(gc.x, gc.offsets, gc.w, gc.s, gc.g_stored, False, None)
+    yn = oracle.grouped_gemm_np(gc.x, gc.offsets, gc.w, gc.s, gc.g_stored, False, None)
+    assert np.allclose(y, yn, rtol=1e-12, atol=1e-12)
+    rows = np.arange(gc.R)
+    cols = np.arange(gc.R) % gc.N
+    ys = oracle.grouped_gemm_sampled(gc.x, gc.offsets, gc.w, gc.s, gc.g_stored, False, None, rows, cols)
+    assert np.allclose(ys, y[rows, cols], rtol=1e-13, atol=1e-13)
+
+
+# ----------------------------------------------------------- invariants ---
+
+def test_identity_activation_gives_transposed_tile():
+    c = synth.dense_case(1, 40, 64, seed=5)
+    eye = synth.bf16_bits_from_f32(np.eye(64, dtype=np.float32))
+    y = oracle.gemm(eye, c.w, c.s, 1.0, False, None)
+    assert np.array_equal(y, oracle.dequant(c.w, c.s).T)
+
+
+def test_power_of_two_scaling_and_prescale_equivalence():
+    c = synth.ragged_case()
+    y = oracle.gemm(c.x, c.w, c.s, c.g_stored, c.g_is_divisor, c.pre)
+    x2 = synth.bf16_bits_from_f32(oracle.bf16_np(c.x).astype(np.float32) * 4)
+    assert np.array_equal(oracle.gemm(x2, c.w, c.s, c.g_stored, c.g_is_divisor, c.pre), 4 * y)
+    xs = synth.bf16_bits_from_f32(oracle.activation(c.x, c.pre).astype(np.float32))
+    assert np.array_equal(oracle.gemm(xs, c.w, c.s, c.g_stored, c.g_is_divisor, None), y)
+    ginv = float(np.float32(1.0) / np.float32(c.g_stored))
+    assert np.array_equal(oracle.gemm(c.x, c.w, c.s, ginv, False, c.pre), y)
+
+
+def test_divisor_inversion_restores_finite_outputs():
+    """A huge divisor-stored scale is harmless once inverted and overflows bf16 if used as a multiplier."""
+    c = synth.tiny_case()
+    big = 2.0 ** 120
+    y = oracle.gemm(c.x, c.w, c.s, big, True, None)
+    assert np.all(np.isfinite(y))
+    assert np.all(np.isfinite([oracle.round_bf16(v) for v in y.ravel()[:512]]))
+    y_bad = oracle.gemm(c.x, c.w, c.s, big, False, None)
+    assert np.any(~np.isfinite([oracle.round_bf16(v) for v in y_bad.ravel()]))
+
+
+# ----------------------------------------------------- negative controls ---
+
+def _planted(kind, c):
+    x = oracle.activation_np(c.x, c.pre)
+    T = oracle.dequant_np(c.w, c.s)
+    g = oracle.global_scale_np(c.g_stored, c.g_is_divisor)
+    if kind == "drop_prescale":
+        x = oracle.activation_np(c.x, None)
+    elif kind == "drop_inversion":
+        g = float(np.float32(c.g_stored))
+    elif kind == "swap_nibbles":
+        T = oracle.dequant_np(((c.w & 15) << 4) | (c.w >> 4), c.s)
+    elif kind == "block_k_over_8":
+        codes = np.stack([c.w & 15, c.w >> 4], axis=-1).reshape(c.w.shape[0], -1)
+        idx = np.minimum(np.arange(c.K) >> 3, c.s.shape[1] - 1)
+        T = oracle.e2m1_np(codes) * oracle.e4m3_np(c.s[:, idx])
+    elif kind == "no_prescale_rounding":
+        x = oracle.bf16_np(c.x) * oracle.bf16_np(c.pre)[None, :]
+    elif kind == "truncate_output":
+        y = (g * (x @ T.T)).astype(np.float32)
+        return (y.view(np.uint32) & 0xFFFF0000).view(np.float32).astype(np.float64)
+    elif kind == "fold_g_into_bf16_tile":
+        T = torch.from_numpy(T * g).to(torch.bfloat16).to(torch.float64).numpy()
+        g = 1.0
+    y = (g * (x @ T.T)).astype(np.float32)
+    return torch.from_numpy(y).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_bf16_rounded_result_passes_acceptance():
+    """The correct result rounded once to bf16 (what the kernels store) is inside the bound."""
+    for c in (synth.tiny_case(), synth.ragged_case()):
+        ref = oracle.gemm(c.x, c.w, c.s, c.g_stored, c.g_is_divisor, c.pre)
+        ok, info = oracle.accept(_planted("none", c), ref)
+        assert ok, info
+
+
+@pytest.mark.parametrize("kind", ["drop_prescale", "drop_inversion", "swap_nibbles", "block_k_over_8",
+                                  "no_prescale_rounding", "truncate_output", "fold_g_into_bf16_tile"])
+def test_planted_mistakes_fail_acceptance(kind):
+    c = synth.dense_case(64, 512, 1024, seed=21, g_stored=2688.0, g_is_divisor=True, prescale=True)
+    ref = oracle.gemm(c.x, c.w, c.s, c.g_stored, c.g_is_divisor, c.pre)
+    ok, info = oracle.accept(_planted(kind, c), ref)
+    assert not ok, (kind, info)
