@@ -1,0 +1,155 @@
+/*
+ * nvfp4_w4a16.h -- C ABI of the MI355X (gfx950) W4A16 NVFP4 GEMM library.
+ *
+ * The operation (dense form):
+ *
+ *     Y[M,N] = g * (X[M,K] (.) s_pre[K]) . dequant(W)^T,
+ *     dequant(W)[n,k] = e2m1(code(n,k)) * e4m3(S[n, k/16])
+ *
+ * W is packed FP4 (E2M1, two codes per byte along K) with one FP8 (E4M3)
+ * scale per 16 consecutive K of a row and one fp32 global scale g; the
+ * activation X and the output Y stay bf16.  Where the operation is defined:
+ *   - packed FP4 weights + per-group FP8 scales + bf16/fp16 activations:
+ *     "Support nvfp4 w4a16 on sm120", Summary;
+ *   - E2M1 codebook lookup times a per-block FP8 scale and a per-tensor
+ *     global scale (linear and active-expert-only MoE dequant):
+ *     "Support Nemotron-H nvfp4 ckpt on Hopper", Walkthrough, Changes table;
+ *   - group size 16 with E4M3 group scales and a real global scale, and the
+ *     divisor-stored global scale that must be inverted: SGLang
+ *     compressed-tensors NVFP4 weight-only page, Motivation and Modifications;
+ *   - the per-channel pre-quant scale multiplies the bf16 activation before
+ *     the GEMM (product kept in bf16), and a zero-token call launches no
+ *     kernel: "Apply the NVFP4_AWQ pre-quant scale in MegaMoE CuteDSL",
+ *     Description.
+ * The E2M1 values and the low-nibble-is-even-k order follow the OCP MX
+ * format; E4M3 is the OCP E4M3FN encoding (bias 7, max 448, NaN = 0x7F/0xFF).
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library allocates nothing and keeps no pointer after it returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Every call is asynchronous on that stream and never synchronises the
+ *     host, so it can be captured into a HIP graph.
+ *   - Arguments are checked on the host before anything is launched; on an
+ *     error nothing has been enqueued and nvfp4_last_error() (thread-local)
+ *     names the argument and the violated constraint.
+ *   - Device-resident values (global scales, expert offsets) are not read by
+ *     the host and are not checked: offsets that are not a non-decreasing
+ *     sequence from 0 to R are undefined behaviour; a stored divisor of 0
+ *     gives non-finite outputs.
+ *   - bf16 values are IEEE binary32 upper halves; all rounding to bf16 is
+ *     round-to-nearest-even.
+ */
+#ifndef NVFP4_W4A16_H
+#define NVFP4_W4A16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_ERR_INVALID_ARG = 1,     /* a size, pointer or flag is invalid */
+    NVFP4_ERR_ALIGNMENT = 2,       /* a pointer or leading dimension is misaligned */
+    NVFP4_ERR_BUFFER_TOO_SMALL = 3,/* out_bytes / workspace_bytes below the size query */
+    NVFP4_ERR_HIP = 4              /* the HIP runtime reported an error at launch */
+} nvfp4_status;
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* nvfp4_last_error(void);
+
+/* ---------------------------------------------------------------- repack --
+ * One-time re-tiling of canonical weights into the layout the GEMM kernels
+ * stream (a step the pages perform as the Marlin weight transformation with
+ * K/N padding: "Support nvfp4 w4a16 on sm120", Changes, Linear).
+ *
+ * Canonical input, E experts (E = 1 for a dense layer):
+ *   w_packed : uint8 [E][N][ld_w], row (e,n) at w_packed + (e*N + n)*ld_w;
+ *              byte j holds codes k = 2j (low nibble) and k = 2j+1 (high
+ *              nibble); ld_w >= K/2.
+ *   w_scale  : uint8 [E][N][ld_s] E4M3 bytes, row (e,n) at w_scale +
+ *              (e*N + n)*ld_s; byte b scales k in [16b, 16b+16); ld_s >= K/16.
+ * Output: `out`, nvfp4_repack_bytes(E,N,K) bytes, 16-byte aligned.  The blob
+ * is pure derived state: repacking the same input again gives the same bytes,
+ * and the canonical input is never modified.  N is padded to a multiple of
+ * 16 and K to a multiple of 128 with zero codes and zero scales.
+ * Errors: E < 1, N < 1, K < 16, K % 16 != 0, ld_w < K/2, ld_s < K/16, NULL
+ * pointer -> INVALID_ARG; out not 16-byte aligned -> ALIGNMENT; out_bytes too
+ * small -> BUFFER_TOO_SMALL. */
+int64_t nvfp4_repack_bytes(int64_t E, int64_t N, int64_t K); /* < 0 if invalid */
+nvfp4_status nvfp4_repack(const uint8_t* w_packed, int64_t ld_w, const uint8_t* w_scale, int64_t ld_s,
+                          int64_t E, int64_t N, int64_t K, void* out, int64_t out_bytes, void* stream);
+
+/* ------------------------------------------------------------ dense GEMM --
+ * Y = RNE_bf16(g * sum_k X'[m,k] * dequant(W)[n,k]) with
+ *   X'[m,k] = pre_scale ? RNE_bf16(X[m,k] * pre_scale[k]) : X[m,k]
+ *   g       = global_scale_is_divisor ? fp32(1 / *global_scale) : *global_scale
+ * (the inversion happens at use, in the epilogue; *global_scale is never
+ * rewritten).  Accumulation is fp32; the summation order is fixed, so
+ * results are bitwise reproducible run to run.
+ *   x         : bf16 [M][ld_x] (16-byte aligned, ld_x >= K, ld_x % 8 == 0)
+ *   pre_scale : bf16 [K] (16-byte aligned) or NULL
+ *   w_repacked: output of nvfp4_repack with E = 1 and the same N, K
+ *   global_scale: device pointer to one fp32
+ *   y         : bf16 [M][ld_y] (2-byte aligned, ld_y >= N)
+ *   workspace : device scratch of nvfp4_w4a16_gemm_workspace_bytes(M,N,K)
+ *               bytes (may be NULL when that is 0)
+ * M == 0 returns NVFP4_OK without launching anything.
+ * Errors: M < 0, N < 1, K < 16, K % 16 != 0, ld_x < K, ld_y < N, NULL
+ * x / w_repacked / global_scale / y (x may be NULL when M == 0) ->
+ * INVALID_ARG; misaligned x, pre_scale, w_repacked or y, or ld_x % 8 != 0
+ * -> ALIGNMENT; workspace too small -> BUFFER_TOO_SMALL. */
+int64_t nvfp4_w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+nvfp4_status nvfp4_w4a16_gemm(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
+                              const float* global_scale, int global_scale_is_divisor,
+                              void* y, int64_t ld_y, int64_t M, int64_t N, int64_t K,
+                              void* workspace, int64_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------- grouped GEMM --
+ * Active-expert-only MoE form ("Support Nemotron-H nvfp4 ckpt on Hopper",
+ * Walkthrough, Changes table, MoE rows: only experts that received tokens
+ * are dequantised).  Rows of x are grouped by expert: rows
+ * [expert_offsets[e], expert_offsets[e+1]) use expert e's weights and global
+ * scale; every other row of y is left untouched.  Experts with no rows read
+ * no weight bytes.  The tile schedule is built on the device from
+ * expert_offsets, with no host synchronisation.
+ *   x             : bf16 [R][ld_x] (same alignment rules as the dense form)
+ *   expert_offsets: device int32 [E+1], offsets[0] = 0, non-decreasing, offsets[E] = R
+ *   pre_scale     : bf16 [K] shared by all experts, or NULL
+ *   w_repacked    : output of nvfp4_repack with this E, N, K
+ *   global_scales : device fp32 [E]
+ *   y             : bf16 [R][ld_y]
+ * R == 0 returns NVFP4_OK without launching anything.
+ * Errors as for the dense form, plus E < 1 -> INVALID_ARG. */
+int64_t nvfp4_w4a16_grouped_gemm_workspace_bytes(int64_t R, int64_t E, int64_t N, int64_t K);
+nvfp4_status nvfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t* expert_offsets,
+                                      const void* pre_scale, const void* w_repacked,
+                                      const float* global_scales, int global_scale_is_divisor,
+                                      void* y, int64_t ld_y, int64_t R, int64_t E, int64_t N, int64_t K,
+                                      void* workspace, int64_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------- test exports --
+ * Decode a repacked blob back to bf16 [E][N][ld_out] in canonical order with
+ * the same device decode the GEMM kernels use (no global scale applied):
+ * out[e][n][k] = RNE_bf16(e2m1(code) * e4m3(scale)), which is exact.
+ * Errors: as for repack, ld_out < K -> INVALID_ARG. */
+nvfp4_status nvfp4_dequant_bf16(const void* w_repacked, int64_t E, int64_t N, int64_t K,
+                                void* out, int64_t ld_out, void* stream);
+
+/* Dense GEMM with the kernel variant forced instead of chosen from M:
+ *   variant 0 = automatic (same as nvfp4_w4a16_gemm),
+ *   variant 1 = small-M kernel (M <= 16 only; larger M -> INVALID_ARG),
+ *   variant 2 = large-M kernel (any M).
+ * Used to check that the variants agree on the same inputs. */
+nvfp4_status nvfp4_w4a16_gemm_variant(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
+                                      const float* global_scale, int global_scale_is_divisor,
+                                      void* y, int64_t ld_y, int64_t M, int64_t N, int64_t K,
+                                      void* workspace, int64_t workspace_bytes, int variant, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_W4A16_H */

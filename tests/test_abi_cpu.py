@@ -1,0 +1,110 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects invalid arguments on the host before any launch (no
+GPU is touched: every call here returns before reaching the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_only_fp4_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4_w4a16.h")
+
+OK, INVALID, ALIGN, SMALL = 0, 1, 2, 3
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared()
+    assert len(names) >= 9
+    L = nv.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_library_links_no_oracle_code():
+    with open(nv.LIB_PATH, "rb") as f:
+        blob = f.read()
+    assert b"oracle_" not in blob
+
+
+def test_repack_bytes_layout_size():
+    # 16-row units x 128-wide K chunks, 1024 code bytes + 128 scale bytes each
+    assert nv.repack_bytes(1, 16, 128) == 1152
+    assert nv.repack_bytes(1, 1000, 1040) == 63 * 9 * 1152
+    assert nv.repack_bytes(128, 1536, 2048) == 128 * 96 * 16 * 1152
+    assert nv.lib().nvfp4_repack_bytes(1, 16, 8) < 0
+    assert nv.lib().nvfp4_repack_bytes(0, 16, 16) < 0
+    assert nv.lib().nvfp4_repack_bytes(1, 0, 16) < 0
+
+
+def _p(v):
+    return ctypes.c_void_p(v)
+
+
+A = 1 << 20   # a fake, 16-byte-aligned address; never dereferenced (calls fail on the host first)
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(K=24), INVALID, "multiple of 16"),
+    (dict(K=0), INVALID, "multiple of 16"),
+    (dict(N=0), INVALID, "N ="),
+    (dict(M=-1), INVALID, "negative"),
+    (dict(ld_x=100), INVALID, "ld_x"),
+    (dict(ld_y=10), INVALID, "ld_y"),
+    (dict(w=None), INVALID, "w_repacked"),
+    (dict(g=None), INVALID, "global scale"),
+    (dict(x=A + 2), ALIGN, "16-byte"),
+    (dict(ld_x=132), ALIGN, "ld_x"),
+    (dict(y=A + 1), ALIGN, "y must be"),
+    (dict(pre=A, ws=A, wsb=10), SMALL, "workspace"),
+    (dict(variant=1, M=17), INVALID, "small-M"),
+    (dict(variant=7), INVALID, "variant"),
+])
+def test_gemm_argument_errors(args, status, needle):
+    a = dict(x=A, ld_x=128, pre=None, w=A, g=A, div=0, y=A, ld_y=32, M=4, N=32, K=128, ws=None, wsb=0, variant=0)
+    a.update(args)
+    L = nv.lib()
+    st = L.nvfp4_w4a16_gemm_variant(_p(a["x"]), a["ld_x"], _p(a["pre"]), _p(a["w"]), _p(a["g"]), a["div"],
+                                    _p(a["y"]), a["ld_y"], a["M"], a["N"], a["K"], _p(a["ws"]), a["wsb"],
+                                    a["variant"], None)
+    assert st == status
+    assert needle in L.nvfp4_last_error().decode()
+
+
+def test_zero_rows_launch_nothing_and_succeed():
+    L = nv.lib()
+    assert L.nvfp4_w4a16_gemm(None, 128, None, _p(A), _p(A), 0, None, 32, 0, 32, 128, None, 0, None) == OK
+    assert L.nvfp4_last_error().decode() == ""
+    assert L.nvfp4_w4a16_grouped_gemm(None, 128, _p(A), None, _p(A), _p(A), 0, None, 32, 0, 4, 32, 128,
+                                      None, 0, None) == OK
+
+
+def test_grouped_and_repack_argument_errors():
+    L = nv.lib()
+    st = L.nvfp4_w4a16_grouped_gemm(_p(A), 128, None, None, _p(A), _p(A), 0, _p(A), 32, 8, 4, 32, 128, None, 0, None)
+    assert st == INVALID and "expert_offsets" in L.nvfp4_last_error().decode()
+    st = L.nvfp4_w4a16_grouped_gemm(_p(A), 128, _p(A), None, _p(A), _p(A), 0, _p(A), 32, 8, 0, 32, 128, None, 0, None)
+    assert st == INVALID and "E =" in L.nvfp4_last_error().decode()
+    n = nv.repack_bytes(1, 32, 128)
+    assert L.nvfp4_repack(_p(A), 32, _p(A), 8, 1, 32, 128, _p(A), n, None) == INVALID      # ld_w < K/2
+    assert L.nvfp4_repack(_p(A), 64, _p(A), 4, 1, 32, 128, _p(A), n, None) == INVALID      # ld_s < K/16
+    assert L.nvfp4_repack(_p(A), 64, _p(A), 8, 1, 32, 128, _p(A + 8), n, None) == ALIGN
+    assert L.nvfp4_repack(_p(A), 64, _p(A), 8, 1, 32, 128, _p(A), n - 1, None) == SMALL
+    assert L.nvfp4_repack(None, 64, _p(A), 8, 1, 32, 128, _p(A), n, None) == INVALID
+    assert L.nvfp4_dequant_bf16(_p(A), 1, 32, 128, _p(A), 64, None) == INVALID             # ld_out < K
+
+
+def test_workspace_queries():
+    L = nv.lib()
+    assert L.nvfp4_w4a16_gemm_workspace_bytes(33, 1000, 1040) >= 33 * 1040 * 2
+    assert L.nvfp4_w4a16_gemm_workspace_bytes(0, 1000, 1040) == 0
+    assert L.nvfp4_w4a16_grouped_gemm_workspace_bytes(128, 128, 1536, 2048) >= 128 * 2048 * 2
+    assert L.nvfp4_w4a16_gemm_workspace_bytes(-1, 10, 16) < 0

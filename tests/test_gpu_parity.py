@@ -1,0 +1,316 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Bars: decoded weight tiles bit-exact; GEMM outputs within the acceptance
+bound of ``oracle.accept`` (relative Frobenius error <= 2e-3, every element
+within 1e-2 * (|ref| + rms(ref)), all finite); hand cases, the identity
+product and the scale invariants bit-exact.  Small sizes use the full oracle;
+the full-size workloads use outputs the oracle computes one by one.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import weight_only_fp4_amd as nv
+from gpu_util import DEV, DenseDev, GroupedDev, bf16_bits, bf16_dev, f32_dev, to_f64, u8_dev
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def accept_or_fail(y, ref, what):
+    ok, info = oracle.accept(y, ref)
+    assert ok, (what, info)
+    return info
+
+
+def oracle_bf16_bits(t64: np.ndarray) -> np.ndarray:
+    """fp64 values exactly representable in bf16 -> bf16 bit patterns (sign of zero kept)."""
+    f = t64.astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), t64, equal_nan=True)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# ------------------------------------------------------------ decode tiles --
+
+def _enumeration_weight():
+    """254 rows (one per finite E4M3 code) x 256 k; each 16-wide block holds all 16 codes, rotated per row."""
+    finite = [b for b in range(256) if b not in (0x7F, 0xFF)]
+    N, K = len(finite), 256
+    codes = (np.arange(K)[None, :] + np.arange(N)[:, None]) % 16
+    w = synth.pack_codes(codes.astype(np.uint8))
+    s = np.repeat(np.array(finite, dtype=np.uint8)[:, None], K // 16, axis=1)
+    return w, s
+
+
+@pytest.mark.parametrize("case", ["enumeration", "ragged", "grouped"])
+def test_dequant_tiles_bit_exact(case):
+    say(f"dequant {case}")
+    if case == "enumeration":
+        w, s = _enumeration_weight()
+        w, s = w[None], s[None]
+    elif case == "ragged":
+        c = synth.ragged_case()
+        w, s = c.w[None], c.s[None]
+    else:
+        gc = synth.grouped_case(T=8, E=3, topk=2, N=40, K=272, seed=5)
+        w, s = gc.w, gc.s
+    E, N, K = w.shape[0], w.shape[1], w.shape[2] * 2
+    blob = nv.repack(u8_dev(w if E > 1 else w[0]), u8_dev(s if E > 1 else s[0]))
+    got = bf16_bits(nv.dequant(blob, E, N, K))
+    for e in range(E):
+        ref = oracle_bf16_bits(oracle.dequant(w[e], s[e]))
+        assert np.array_equal(got[e], ref), (case, e, np.argwhere(got[e] != ref)[:5])
+
+
+def test_repack_is_deterministic_and_pure():
+    say("repack twice")
+    c = synth.ragged_case()
+    w, s = u8_dev(c.w), u8_dev(c.s)
+    w0, s0 = w.clone(), s.clone()
+    b1, b2 = nv.repack(w, s), nv.repack(w, s)
+    torch.cuda.synchronize()
+    assert torch.equal(b1, b2)
+    assert torch.equal(w, w0) and torch.equal(s, s0)
+
+
+# -------------------------------------------------------------- hand cases --
+
+def _read_hand():
+    rows = {}
+    for line in open(os.path.join(GOLDEN, "hand_cases.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            p = line.split()
+            rows[p[0]] = [float(v) for v in p[1:]]
+    return rows
+
+
+@pytest.mark.parametrize("variant", [nv.VARIANT_SMALL_M, nv.VARIANT_LARGE_M])
+@pytest.mark.parametrize("case", ["H1", "H2", "H3", "H4"])
+def test_hand_cases_exact(case, variant):
+    from test_oracle_pins import _hand_inputs
+    say(f"hand case {case} variant {variant}")
+    x, w, s, g, div, pre = _hand_inputs(case)
+    blob = nv.repack(u8_dev(w), u8_dev(s))
+    y = nv.gemm_variant(bf16_dev(x), blob, 16, 16, f32_dev(g), div, None if pre is None else bf16_dev(pre),
+                        variant=variant)
+    got = to_f64(y)[0]
+    exp = _read_hand()[case]
+    for n in range(16):
+        assert got[n] == exp[n], (case, variant, n, got[n], exp[n])
+
+
+@pytest.mark.parametrize("variant,M,N", [(nv.VARIANT_SMALL_M, 16, 40), (nv.VARIANT_LARGE_M, 256, 300)])
+def test_identity_activation_gives_tile_bit_exact(variant, M, N):
+    """X = I_K, g = 1: every output is one exact product, so Y = T^T bit for bit (signed zeros compare equal)."""
+    K = M
+    say(f"identity variant {variant} K={K} N={N}")
+    c = synth.dense_case(1, N, K, seed=9)
+    eye = synth.bf16_bits_from_f32(np.eye(K, dtype=np.float32))
+    blob = nv.repack(u8_dev(c.w), u8_dev(c.s))
+    y = to_f64(nv.gemm_variant(bf16_dev(eye), blob, N, K, f32_dev(1.0), False, None, variant=variant))
+    assert np.array_equal(y, oracle.dequant(c.w, c.s).T)
+
+
+# ------------------------------------------------------------ dense parity --
+
+DENSE_FULL = [
+    ("tiny", lambda: synth.tiny_case()),
+    ("ragged_33x1000x1040", lambda: synth.ragged_case()),
+    ("ragged_M13", lambda: synth.dense_case(13, 1000, 1040, 1003, g_stored=2688.0, g_is_divisor=True, prescale=True)),
+    ("mid_300x700x2048", lambda: synth.dense_case(300, 700, 2048, 77, scales="log_uniform", g_stored=1 / 2688)),
+    ("decode_M1", lambda: synth.decode_case(1)),
+    ("decode_M8", lambda: synth.decode_case(8)),
+    ("decode_M16", lambda: synth.decode_case(16)),
+    ("decode_T_M1", lambda: synth.decode_case(1, N=4096, K=14336)),
+    ("decode_T_M16", lambda: synth.decode_case(16, N=4096, K=14336)),
+    ("lmhead_M1", lambda: synth.lmhead_case(1)),
+]
+
+
+@pytest.mark.parametrize("name,make", DENSE_FULL, ids=[d[0] for d in DENSE_FULL])
+def test_dense_parity_full_oracle(name, make):
+    c = make()
+    say(f"dense {name} M={c.M} N={c.N} K={c.K} pre={c.pre is not None} div={c.g_is_divisor}")
+    d = DenseDev(c)
+    ref = oracle.gemm(c.x, c.w, c.s, c.g_stored, c.g_is_divisor, c.pre)
+    variants = [nv.VARIANT_AUTO, nv.VARIANT_LARGE_M] + ([nv.VARIANT_SMALL_M] if c.M <= 16 else [])
+    for v in variants:
+        accept_or_fail(to_f64(d.run(v)), ref, (name, v))
+
+
+DENSE_SAMPLED = [
+    ("prefill_4096x14336x4096", lambda: synth.prefill_case()),
+    ("prefill_8192x17408x5120", lambda: synth.prefill_case(8192, 17408, 5120)),
+    ("lmhead_M64", lambda: synth.lmhead_case(64)),
+]
+
+
+@pytest.mark.parametrize("name,make", DENSE_SAMPLED, ids=[d[0] for d in DENSE_SAMPLED])
+def test_dense_parity_full_size_sampled(name, make):
+    c = make()
+    say(f"dense sampled {name}")
+    d = DenseDev(c)
+    y = to_f64(d.run())
+    assert np.all(np.isfinite(y))
+    g = synth.rng(123)
+    cnt = 4096
+    rows = g.integers(0, c.M, cnt)
+    cols = g.integers(0, c.N, cnt)
+    # every row tile and every column tile of the launch is hit at least once, plus the last row/col
+    rows[:2] = [0, c.M - 1]
+    cols[:2] = [c.N - 1, 0]
+    ref = oracle.gemm_sampled(c.x, c.w, c.s, c.g_stored, c.g_is_divisor, c.pre, rows, cols)
+    accept_or_fail(y[rows, cols], ref, name)
+
+
+def test_small_and_large_variants_agree():
+    c = synth.decode_case(8, N=2048, K=4096, seed=31)
+    say("variants agree M=8")
+    d = DenseDev(c)
+    a, b = to_f64(d.run(nv.VARIANT_SMALL_M)), to_f64(d.run(nv.VARIANT_LARGE_M))
+    ok, info = oracle.accept(a, b)
+    assert ok, info
+
+
+# ---------------------------------------------------------- grouped parity --
+
+@pytest.mark.parametrize("fc", ["fc1", "fc2"])
+def test_grouped_parity_T16_full_oracle(fc):
+    gc = synth.moe_fc1_case(16) if fc == "fc1" else synth.moe_fc2_case(16)
+    say(f"grouped {fc} T=16 R={gc.R} active={len(gc.active)}")
+    assert len(gc.active) < gc.E      # some experts receive no rows
+    d = GroupedDev(gc)
+    y = to_f64(d.run())
+    ref = oracle.grouped_gemm(gc.x, gc.offsets, gc.w, gc.s, gc.g_stored, gc.g_is_divisor, gc.pre)
+    accept_or_fail(y, ref, fc)
+
+
+@pytest.mark.parametrize("fc", ["fc1", "fc2"])
+def test_grouped_parity_T2048_sampled(fc):
+    gc = synth.moe_fc1_case(2048) if fc == "fc1" else synth.moe_fc2_case(2048)
+    say(f"grouped {fc} T=2048 R={gc.R} active={len(gc.active)}")
+    d = GroupedDev(gc)
+    y = to_f64(d.run())
+    assert np.all(np.isfinite(y))
+    g = synth.rng(7)
+    rows, cols = [], []
+    for e in gc.active:
+        a, b = int(gc.offsets[e]), int(gc.offsets[e + 1])
+        rr = np.unique(np.concatenate([[a, b - 1], g.integers(a, b, 2)]))
+        for r in rr:
+            rows.extend([r] * 16)
+            cols.extend(g.integers(0, gc.N, 16).tolist())
+    rows, cols = np.array(rows), np.array(cols)
+    ref = oracle.grouped_gemm_sampled(gc.x, gc.offsets, gc.w, gc.s, gc.g_stored, gc.g_is_divisor, gc.pre, rows, cols)
+    accept_or_fail(y[rows, cols], ref, fc)
+
+
+def test_grouped_prescale_and_divisor_small_experts():
+    gc = synth.grouped_case(T=40, E=6, topk=2, N=72, K=160, seed=3, prescale=True)
+    gc.g_is_divisor = True
+    gc.g_stored = (1.0 / gc.g_stored).astype(np.float32)
+    say("grouped prescale+divisor")
+    d = GroupedDev(gc)
+    ref = oracle.grouped_gemm(gc.x, gc.offsets, gc.w, gc.s, gc.g_stored, True, gc.pre)
+    accept_or_fail(to_f64(d.run()), ref, "grouped prescale")
+
+
+def test_grouped_matches_per_expert_dense_calls():
+    gc = synth.grouped_case(T=64, E=8, topk=2, N=96, K=256, seed=8)
+    say("grouped vs per-expert dense")
+    d = GroupedDev(gc)
+    y = d.run()
+    for e in gc.active:
+        a, b = int(gc.offsets[e]), int(gc.offsets[e + 1])
+        blob = nv.repack(d.w[e], d.s[e])
+        ye = nv.gemm(d.x[a:b], blob, gc.N, gc.K, d.g[e:e + 1], False)
+        ok, info = oracle.accept(to_f64(y[a:b]), to_f64(ye))
+        assert ok, (e, info)
+
+
+# -------------------------------------------------------------- invariants --
+
+@pytest.mark.parametrize("variant", [nv.VARIANT_SMALL_M, nv.VARIANT_LARGE_M])
+def test_scale_invariants_bit_exact(variant):
+    c = synth.dense_case(16, 520, 1040, seed=41, g_stored=2688.0, g_is_divisor=True, prescale=True)
+    say(f"invariants variant {variant}")
+    d = DenseDev(c)
+    y = bf16_bits(d.run(variant))
+    # divisor flag == multiplier RN(1/v)
+    ginv = np.float32(1.0) / np.float32(c.g_stored)
+    assert np.array_equal(bf16_bits(d.run(variant, g=f32_dev(ginv), divisor=False)), y)
+    # pre-scale == activation rounded on the host by the oracle's own rule, no pre-scale
+    xs = synth.bf16_bits_from_f32(oracle.activation(c.x, c.pre).astype(np.float32))
+    assert np.array_equal(bf16_bits(d.run(variant, x=bf16_dev(xs), pre=None)), y)
+    # power-of-two scaling of X scales Y exactly
+    x4 = synth.bf16_bits_from_f32(oracle.bf16_np(xs).astype(np.float32) * 4)
+    y4 = to_f64(d.run(variant, x=bf16_dev(x4), pre=None))
+    assert np.array_equal(y4, 4 * to_f64(d.run(variant)))
+
+
+def test_divisor_inversion_restores_finite_outputs():
+    c = synth.tiny_case()
+    say("divisor inversion finite")
+    d = DenseDev(c)
+    big = f32_dev(2.0 ** 120)
+    assert torch.isfinite(d.run(g=big, divisor=True)).all()
+    assert not torch.isfinite(d.run(g=big, divisor=False)).all()   # used as a multiplier it overflows
+
+
+# ------------------------------------------------------------------- edges --
+
+def test_zero_rows_leave_output_untouched():
+    c = synth.tiny_case()
+    say("zero rows")
+    d = DenseDev(c)
+    out = torch.full((0, c.N), 7.0, dtype=torch.bfloat16, device=DEV)
+    nv.gemm(d.x[:0], d.blob, c.N, c.K, d.g, out=out)
+    gc = synth.grouped_case(T=4, E=3, topk=1, N=32, K=64, seed=2)
+    gd = GroupedDev(gc)
+    off0 = torch.zeros(gc.E + 1, dtype=torch.int32, device=DEV)
+    nv.grouped_gemm(gd.x[:0], off0, gd.blob, gc.E, gc.N, gc.K, gd.g)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("variant", [nv.VARIANT_SMALL_M, nv.VARIANT_LARGE_M])
+def test_strided_io_and_untouched_padding(variant):
+    c = synth.dense_case(5, 40, 96, seed=13)
+    say(f"strided io variant {variant}")
+    d = DenseDev(c)
+    xbig = torch.zeros((c.M, 200), dtype=torch.bfloat16, device=DEV)
+    xbig[:, 96:] = float("nan")            # beyond K: must never be read
+    xbig[:, :96] = d.x
+    ybig = torch.full((c.M, 48), 5.0, dtype=torch.bfloat16, device=DEV)
+    nv.gemm_variant(xbig[:, :96], d.blob, c.N, c.K, d.g, False, None, out=ybig[:, :40], variant=variant)
+    ref = oracle.gemm(c.x, c.w, c.s, c.g_stored, False, None)
+    accept_or_fail(to_f64(ybig[:, :40]), ref, "strided")
+    assert torch.all(ybig[:, 40:] == 5.0)
+
+
+def test_smallest_shapes():
+    for M, N, K in [(1, 1, 16), (1, 17, 16), (17, 1, 32), (16, 16, 16)]:
+        say(f"shape {M}x{N}x{K}")
+        c = synth.dense_case(M, N, K, seed=M * 100 + N)
+        d = DenseDev(c)
+        ref = oracle.gemm(c.x, c.w, c.s, c.g_stored, False, None)
+        for v in [nv.VARIANT_LARGE_M] + ([nv.VARIANT_SMALL_M] if M <= 16 else []):
+            accept_or_fail(to_f64(d.run(v)), ref, (M, N, K, v))
+
+
+def test_run_to_run_bitwise_determinism():
+    for make in (lambda: synth.decode_case(16, N=2048, K=4096, seed=3), lambda: synth.dense_case(200, 512, 1024, 4)):
+        c = make()
+        say(f"determinism M={c.M}")
+        d = DenseDev(c)
+        assert torch.equal(d.run(), d.run())

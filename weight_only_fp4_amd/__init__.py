@@ -1,0 +1,189 @@
+"""Python binding of the MI355X W4A16 NVFP4 GEMM library (``libnvfp4_w4a16.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/nvfp4_w4a16.h``.  torch is
+used for device memory and the current stream.  There is no fallback: if the
+built library is missing, or a tensor is not on the GPU, the call raises.
+
+    blob = repack(w_packed, w_scale)                       # once per weight
+    y = gemm(x, blob, N, K, global_scale, divisor=False, pre_scale=None)
+    y = grouped_gemm(x_sorted, expert_offsets, blob, E, N, K, global_scales)
+
+Formats: w_packed uint8 [(E,) N, K/2], two E2M1 codes per byte, even k in the
+low nibble; w_scale uint8 or float8_e4m3fn [(E,) N, K/16]; x bf16 [M, K];
+global scale(s) fp32 on the device ([1] or [E]); pre_scale bf16 [K].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["repack", "repack_bytes", "gemm", "gemm_variant", "grouped_gemm", "dequant", "lib", "Nvfp4Error",
+           "VARIANT_AUTO", "VARIANT_SMALL_M", "VARIANT_LARGE_M", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4_w4a16.so")
+VARIANT_AUTO, VARIANT_SMALL_M, VARIANT_LARGE_M = 0, 1, 2
+_STATUS = {0: "OK", 1: "INVALID_ARG", 2: "ALIGNMENT", 3: "BUFFER_TOO_SMALL", 4: "HIP"}
+_lib = None
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library (never builds; see weight_only_fp4_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m weight_only_fp4_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.nvfp4_last_error.argtypes, L.nvfp4_last_error.restype = [], ctypes.c_char_p
+        L.nvfp4_repack_bytes.argtypes, L.nvfp4_repack_bytes.restype = [I64, I64, I64], I64
+        L.nvfp4_repack.argtypes, L.nvfp4_repack.restype = [P, I64, P, I64, I64, I64, I64, P, I64, P], I
+        L.nvfp4_dequant_bf16.argtypes, L.nvfp4_dequant_bf16.restype = [P, I64, I64, I64, P, I64, P], I
+        L.nvfp4_w4a16_gemm_workspace_bytes.argtypes = [I64, I64, I64]
+        L.nvfp4_w4a16_gemm_workspace_bytes.restype = I64
+        L.nvfp4_w4a16_gemm.argtypes = [P, I64, P, P, P, I, P, I64, I64, I64, I64, P, I64, P]
+        L.nvfp4_w4a16_gemm.restype = I
+        L.nvfp4_w4a16_gemm_variant.argtypes = [P, I64, P, P, P, I, P, I64, I64, I64, I64, P, I64, I, P]
+        L.nvfp4_w4a16_gemm_variant.restype = I
+        L.nvfp4_w4a16_grouped_gemm_workspace_bytes.argtypes = [I64, I64, I64, I64]
+        L.nvfp4_w4a16_grouped_gemm_workspace_bytes.restype = I64
+        L.nvfp4_w4a16_grouped_gemm.argtypes = [P, I64, P, P, P, P, I, P, I64, I64, I64, I64, I64, P, I64, P]
+        L.nvfp4_w4a16_grouped_gemm.restype = I
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise Nvfp4Error(status, lib().nvfp4_last_error().decode())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(name, t, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() not in (ndim if isinstance(ndim, tuple) else (ndim,)):
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if t.dim() and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride in its last dim")
+    return t
+
+
+def repack_bytes(E: int, N: int, K: int) -> int:
+    n = lib().nvfp4_repack_bytes(E, N, K)
+    if n < 0:
+        raise ValueError(f"invalid weight shape E={E} N={N} K={K} (K must be a positive multiple of 16)")
+    return n
+
+
+def repack(w_packed: torch.Tensor, w_scale: torch.Tensor) -> torch.Tensor:
+    """Canonical uint8 [(E,) N, K/2] codes + E4M3 [(E,) N, K/16] scales -> repacked uint8 blob."""
+    _dev("w_packed", w_packed, torch.uint8, (2, 3))
+    _dev("w_scale", w_scale, (torch.uint8, torch.float8_e4m3fn), w_packed.dim())
+    if w_scale.dtype != torch.uint8:
+        w_scale = w_scale.view(torch.uint8)
+    E = w_packed.shape[0] if w_packed.dim() == 3 else 1
+    N, K = w_packed.shape[-2], w_packed.shape[-1] * 2
+    if tuple(w_scale.shape[-2:]) != (N, K // 16) or (w_packed.dim() == 3 and w_scale.shape[0] != E):
+        raise ValueError(f"w_scale shape {tuple(w_scale.shape)} does not match w_packed {tuple(w_packed.shape)}")
+    for name, t in (("w_packed", w_packed), ("w_scale", w_scale)):
+        if w_packed.dim() == 3 and t.stride(0) != t.shape[1] * t.stride(1):
+            raise ValueError(f"{name}: experts must be stored back to back (stride(0) == N * stride(1))")
+    nbytes = repack_bytes(E, N, K)
+    out = torch.empty(nbytes, dtype=torch.uint8, device=w_packed.device)
+    _check(lib().nvfp4_repack(_ptr(w_packed), w_packed.stride(-2), _ptr(w_scale), w_scale.stride(-2), E, N, K,
+                              _ptr(out), nbytes, _stream(w_packed.device)))
+    return out
+
+
+def dequant(blob: torch.Tensor, E: int, N: int, K: int) -> torch.Tensor:
+    """Repacked blob -> bf16 [E, N, K] (exact e2m1 * e4m3, no global scale)."""
+    _dev("blob", blob, torch.uint8, 1)
+    out = torch.empty((E, N, K), dtype=torch.bfloat16, device=blob.device)
+    _check(lib().nvfp4_dequant_bf16(_ptr(blob), E, N, K, _ptr(out), K, _stream(blob.device)))
+    return out
+
+
+def _gemm_args(x, blob, N, K, global_scale, pre_scale, out, rows_name="M"):
+    _dev("x", x, torch.bfloat16, 2)
+    _dev("blob", blob, torch.uint8, 1)
+    _dev("global_scale", global_scale, torch.float32)
+    if not global_scale.is_contiguous():
+        raise ValueError("global_scale must be contiguous")
+    if x.shape[1] != K:
+        raise ValueError(f"x has {x.shape[1]} columns, K = {K}")
+    if pre_scale is not None:
+        _dev("pre_scale", pre_scale, torch.bfloat16, 1)
+        if pre_scale.shape[0] != K or not pre_scale.is_contiguous():
+            raise ValueError(f"pre_scale must be a contiguous bf16 [{K}]")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _dev("out", out, torch.bfloat16, 2)
+        if out.shape[0] != M or out.shape[1] != N:
+            raise ValueError(f"out must be [{M}, {N}]")
+    return M, out
+
+
+def gemm(x, blob, N, K, global_scale, divisor=False, pre_scale=None, out=None, workspace=None):
+    """Y[M, N] = g * (x (.) pre_scale) . dequant(W)^T in bf16 (dense linear / LM head)."""
+    return gemm_variant(x, blob, N, K, global_scale, divisor, pre_scale, out, workspace, VARIANT_AUTO)
+
+
+def gemm_variant(x, blob, N, K, global_scale, divisor=False, pre_scale=None, out=None, workspace=None,
+                 variant=VARIANT_AUTO):
+    M, out = _gemm_args(x, blob, N, K, global_scale, pre_scale, out)
+    wsb = 0
+    if pre_scale is not None:
+        need = lib().nvfp4_w4a16_gemm_workspace_bytes(M, N, K)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        wsb = workspace.numel()
+    _check(lib().nvfp4_w4a16_gemm_variant(_ptr(x), x.stride(0), _ptr(pre_scale), _ptr(blob), _ptr(global_scale),
+                                          int(bool(divisor)), _ptr(out), out.stride(0), M, N, K, _ptr(workspace),
+                                          wsb, int(variant), _stream(x.device)))
+    return out
+
+
+def grouped_gemm(x, expert_offsets, blob, E, N, K, global_scales, divisor=False, pre_scale=None, out=None,
+                 workspace=None):
+    """Grouped (MoE) form: rows [offsets[e], offsets[e+1]) of x use expert e.  Rows owned by no expert are left
+    untouched in ``out`` (a fresh ``out`` is zero-filled)."""
+    _dev("expert_offsets", expert_offsets, torch.int32, 1)
+    if expert_offsets.shape[0] != E + 1 or not expert_offsets.is_contiguous():
+        raise ValueError(f"expert_offsets must be a contiguous int32 [{E + 1}]")
+    if global_scales.numel() != E:
+        raise ValueError(f"global_scales must hold {E} values")
+    if out is None:
+        out = torch.zeros((x.shape[0], N), dtype=torch.bfloat16, device=x.device)
+    R, out = _gemm_args(x, blob, N, K, global_scales, pre_scale, out)
+    wsb = 0
+    if pre_scale is not None:
+        need = lib().nvfp4_w4a16_grouped_gemm_workspace_bytes(R, E, N, K)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        wsb = workspace.numel()
+    _check(lib().nvfp4_w4a16_grouped_gemm(_ptr(x), x.stride(0), _ptr(expert_offsets), _ptr(pre_scale), _ptr(blob),
+                                          _ptr(global_scales), int(bool(divisor)), _ptr(out), out.stride(0), R, E,
+                                          N, K, _ptr(workspace), wsb, _stream(x.device)))
+    return out

@@ -1,0 +1,105 @@
+// Device-side number formats: E4M3 scale bytes, E2M1 codes, bf16 rounding.
+//
+// The hardware conversion v_cvt_scalef32_pk_{f32,bf16}_fp4 turns two E2M1
+// codes (one byte, low nibble first) into two values and multiplies them by
+// 2^exponent(scale operand): only the exponent field of the fp32 scale is
+// used, its sign and mantissa are ignored.  An E4M3 scale has a 4-bit
+// significand, so the decode applies the scale in two parts: the power of
+// two inside the conversion (or a multiply by 1.0 there and a full fp32
+// multiply after it), and the remaining significand factor by an fp32
+// multiply.  e2m1 * e4m3 has at most 6 significant bits and lies in
+// [2^-10, 2688], so every product is exact in fp32 and in bf16.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// E4M3 (OCP E4M3FN: bias 7, subnormal m * 2^-9, 0x7F / 0xFF NaN) -> fp32, exact.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+    if ((b & 0x7Fu) == 0x7Fu) mag = __uint_as_float(0x7FC00000u);
+    return (b & 0x80u) ? -mag : mag;
+}
+
+// Split a scale s into the operand handed to the exponent-only conversion
+// (its exponent is applied there) and the fp32 factor that completes it:
+// e2m1 * s == (e2m1 * 2^exp(cvt_scale)) * factor, exactly.  Zero and NaN
+// scales convert with 1.0 and carry the whole value in the factor.
+__device__ __forceinline__ void split_scale(float s, float& cvt_scale, float& factor) {
+    const uint32_t u = __float_as_uint(s);
+    const bool special = (s == 0.0f) || (s != s);
+    cvt_scale = special ? 1.0f : s;
+    factor = special ? s : __uint_as_float((u & 0x807FFFFFu) | 0x3F800000u);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bit pattern (NaN kept quiet, sign kept).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Upper halves of two fp32 values -> one dword of two bf16 (lo first).  Exact
+// when both values are representable in bf16 (true for decoded weights).
+__device__ __forceinline__ uint32_t pack_hi_halves(float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Eight E2M1 codes of one dword (code of the lowest k in the lowest nibble)
+// times a full fp32 scale -> eight bf16 in k order, exact.
+__device__ __forceinline__ uint4 decode8_bf16(uint32_t codes, float scale) {
+    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+    uint4 r;
+    r.x = pack_hi_halves(p0.x * scale, p0.y * scale);
+    r.y = pack_hi_halves(p1.x * scale, p1.y * scale);
+    r.z = pack_hi_halves(p2.x * scale, p2.y * scale);
+    r.w = pack_hi_halves(p3.x * scale, p3.y * scale);
+    return r;
+}
+
+// Four E2M1 codes (two bytes of a dword, BYTE and BYTE + 1) times
+// 2^exp(cvt_scale) -> four bf16 in k order, exact.
+template <int BYTE>
+__device__ __forceinline__ s16x4 decode4_bf16_pow2(uint32_t codes, float cvt_scale) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, cvt_scale, BYTE);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, cvt_scale, BYTE + 1);
+    const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
+    s16x4 r;
+    r[0] = (short)(ua & 0xFFFFu);
+    r[1] = (short)(ua >> 16);
+    r[2] = (short)(ub & 0xFFFFu);
+    r[3] = (short)(ub >> 16);
+    return r;
+}
+
+__device__ __forceinline__ s16x4 dwords_to_s16x4(uint32_t lo, uint32_t hi) {
+    s16x4 r;
+    r[0] = (short)(lo & 0xFFFFu);
+    r[1] = (short)(lo >> 16);
+    r[2] = (short)(hi & 0xFFFFu);
+    r[3] = (short)(hi >> 16);
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 uint4_to_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Global scale as used in the epilogue: the stored value, or its correctly
+// rounded fp32 reciprocal when it is stored as a divisor.
+__device__ __forceinline__ float effective_global_scale(float stored, int is_divisor) {
+    return is_divisor ? __fdiv_rn(1.0f, stored) : stored;
+}
+
+}  // namespace nvfp4

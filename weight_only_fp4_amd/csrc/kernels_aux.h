@@ -1,0 +1,104 @@
+// Repack, dequantise (test export) and pre-quant-scale kernels.
+#pragma once
+#include "decode.h"
+#include "layout.h"
+
+namespace nvfp4 {
+
+// One thread per (expert, row unit, K chunk, lane): gathers the 16 canonical
+// code bytes and the 2 scale bytes the lane owns in the repacked layout and
+// writes them with one 128-bit and one 16-bit store.  Positions past N or K
+// are written as zero.
+__global__ void __launch_bounds__(256) k_repack(const uint8_t* __restrict__ w, int64_t ld_w,
+                                                const uint8_t* __restrict__ s, int64_t ld_s,
+                                                int64_t N, int64_t K, int64_t NU, int64_t KC, int64_t total_lanes,
+                                                uint8_t* __restrict__ codes_out, uint8_t* __restrict__ scales_out) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= total_lanes) return;
+    const int lane = (int)(t & 63);
+    const int64_t blk = t >> 6;              // (e * NU + u) * KC + c
+    const int64_t c = blk % KC;
+    const int64_t eu = blk / KC;
+    const int64_t u = eu % NU;
+    const int64_t e = eu / NU;
+    const int64_t n = u * kUnitN + (lane & 15);
+    const int64_t kbyte0 = c * (kChunkK / 2) + (lane >> 4) * 16;   // canonical byte of the lane's first code
+    const int64_t kbytes = K / 2;
+    uint32_t q[4] = {0u, 0u, 0u, 0u};
+    uint32_t sc = 0u;
+    if (n < N) {
+        const uint8_t* row = w + (e * N + n) * ld_w;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t j = kbyte0 + i;
+            const uint32_t b = (j < kbytes) ? (uint32_t)row[j] : 0u;
+            q[i >> 2] |= b << (8 * (i & 3));
+        }
+        const uint8_t* srow = s + (e * N + n) * ld_s;
+        const int64_t sb0 = c * (kChunkK / 16) + (lane >> 4) * 2;
+        const int64_t nblk = K / 16;
+        const uint32_t s0 = (sb0 < nblk) ? (uint32_t)srow[sb0] : 0u;
+        const uint32_t s1 = (sb0 + 1 < nblk) ? (uint32_t)srow[sb0 + 1] : 0u;
+        sc = s0 | (s1 << 8);
+    }
+    *reinterpret_cast<uint4*>(codes_out + blk * kCodeBlock + lane * 16) = make_uint4(q[0], q[1], q[2], q[3]);
+    *reinterpret_cast<uint16_t*>(scales_out + blk * kScaleBlock + lane * 2) = (uint16_t)sc;
+}
+
+// Decode a repacked blob to bf16 [E][N][ld_out] with the GEMM kernels' decode
+// (decode8_bf16).  One thread per (expert, row unit, K chunk, lane).
+__global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                                 int64_t N, int64_t K, int64_t NU, int64_t KC, int64_t total_lanes,
+                                                 uint16_t* __restrict__ out, int64_t ld_out) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= total_lanes) return;
+    const int lane = (int)(t & 63);
+    const int64_t blk = t >> 6;
+    const int64_t c = blk % KC;
+    const int64_t eu = blk / KC;
+    const int64_t u = eu % NU;
+    const int64_t e = eu / NU;
+    const int64_t n = u * kUnitN + (lane & 15);
+    if (n >= N) return;
+    const uint4 q = *reinterpret_cast<const uint4*>(codes + blk * kCodeBlock + lane * 16);
+    const uint32_t sc = *reinterpret_cast<const uint16_t*>(scales + blk * kScaleBlock + lane * 2);
+    const float s0 = e4m3_to_f32(sc & 0xFFu), s1 = e4m3_to_f32(sc >> 8);
+    const uint32_t qd[4] = {q.x, q.y, q.z, q.w};
+    const int64_t k0 = c * kChunkK + (lane >> 4) * 32;
+    uint16_t* row = out + (e * N + n) * ld_out;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint4 v = decode8_bf16(qd[d], d < 2 ? s0 : s1);
+        const uint32_t vd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t k = k0 + d * 8 + i;
+            if (k < K) row[k] = (uint16_t)((vd[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+        }
+    }
+}
+
+// X'[r][k] = RNE_bf16(X[r][k] * s[k]) for r < rows, k < K, eight elements per
+// thread (K is a multiple of 16).  The product of two bf16 values is exact in
+// fp32, so a single rounding to bf16 gives the correctly rounded result.
+__global__ void __launch_bounds__(256) k_prescale(const uint16_t* __restrict__ x, int64_t ld_x,
+                                                  const uint16_t* __restrict__ pre, int64_t rows, int64_t K,
+                                                  uint16_t* __restrict__ out, int64_t ld_out) {
+    const int64_t per_row = K / 8;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= rows * per_row) return;
+    const int64_t r = t / per_row, k = (t % per_row) * 8;
+    const uint4 xv = *reinterpret_cast<const uint4*>(x + r * ld_x + k);
+    const uint4 sv = *reinterpret_cast<const uint4*>(pre + k);
+    const uint32_t xd[4] = {xv.x, xv.y, xv.z, xv.w}, sd[4] = {sv.x, sv.y, sv.z, sv.w};
+    uint32_t od[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a0 = bf16_to_f32(xd[i] & 0xFFFFu) * bf16_to_f32(sd[i] & 0xFFFFu);
+        const float a1 = bf16_to_f32(xd[i] >> 16) * bf16_to_f32(sd[i] >> 16);
+        od[i] = f32_to_bf16_rne(a0) | (f32_to_bf16_rne(a1) << 16);
+    }
+    *reinterpret_cast<uint4*>(out + r * ld_out + k) = make_uint4(od[0], od[1], od[2], od[3]);
+}
+
+}  // namespace nvfp4

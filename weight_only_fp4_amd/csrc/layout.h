@@ -1,0 +1,46 @@
+// Repacked weight layout shared by every kernel of the library.
+//
+// A weight matrix of N rows (output features) and K columns (reduction) is
+// cut into units of 16 rows by 128 columns.  N is padded to a multiple of 16
+// and K to a multiple of 128 with zero codes and zero scale bytes, which
+// decode to +0 and contribute nothing.  Per expert the units are stored
+// row-unit major, the K chunks of one row-unit contiguous, so a wave that
+// walks K reads one contiguous stream.
+//
+// codes region  : [E][NU][KC] blocks of 1024 bytes.  In a block, lane l of a
+//                 wave owns bytes [16 l, 16 l + 16): the canonical bytes of
+//                 row 16 u + (l & 15) covering k in [128 c + 32 (l >> 4), +32)
+//                 (low nibble = even k, as in the canonical input).  One
+//                 128-bit load per lane therefore hands lane l the 32 codes
+//                 of one row and one 32-wide K group, and a wave's load is
+//                 one contiguous kilobyte.
+// scales region : [E][NU][KC] blocks of 128 bytes.  Lane l owns bytes
+//                 [2 l, 2 l + 2): the E4M3 scales of the two 16-wide blocks
+//                 of its 32-wide K group (low byte = lower k).
+//
+// Total size: E * NU * KC * 1152 bytes, i.e. 0.5625 bytes per weight plus
+// padding.
+#pragma once
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kUnitN = 16;
+constexpr int kChunkK = 128;
+constexpr int kCodeBlock = 1024;
+constexpr int kScaleBlock = 128;
+
+struct Layout {
+    int64_t E, N, K;
+    int64_t NU;   // row units (ceil(N / 16))
+    int64_t KC;   // K chunks (ceil(K / 128))
+    int64_t blocks() const { return E * NU * KC; }
+    int64_t code_bytes() const { return blocks() * kCodeBlock; }
+    int64_t total_bytes() const { return blocks() * (kCodeBlock + kScaleBlock); }
+};
+
+inline Layout make_layout(int64_t E, int64_t N, int64_t K) {
+    return Layout{E, N, K, (N + kUnitN - 1) / kUnitN, (K + kChunkK - 1) / kChunkK};
+}
+
+}  // namespace nvfp4

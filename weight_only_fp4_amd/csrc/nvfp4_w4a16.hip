@@ -1,0 +1,270 @@
+// C ABI of the W4A16 NVFP4 GEMM library (see include/nvfp4_w4a16.h).
+//
+// Host side: argument checks (all before any launch), size queries, kernel
+// choice and launches.  Everything is stream-ordered and asynchronous; the
+// host never waits on the device and never reads device memory.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/nvfp4_w4a16.h"
+#include "kernels_aux.h"
+#include "kernels_gemm.h"
+
+using namespace nvfp4;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+nvfp4_status fail(nvfp4_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+nvfp4_status ok() {
+    g_err[0] = '\0';
+    return NVFP4_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+nvfp4_status launched(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+nvfp4_status check_weight_shape(const char* fn, int64_t E, int64_t N, int64_t K) {
+    if (E < 1 || E > kMaxExperts) return fail(NVFP4_ERR_INVALID_ARG, "%s: E = %lld must be in [1, %d]", fn, (long long)E, kMaxExperts);
+    if (N < 1 || N > (int64_t)1 << 30) return fail(NVFP4_ERR_INVALID_ARG, "%s: N = %lld must be in [1, 2^30]", fn, (long long)N);
+    if (K < 16 || K % 16 != 0 || K > (int64_t)1 << 30)
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: K = %lld must be a positive multiple of 16 (one E4M3 scale per 16 K)", fn, (long long)K);
+    return NVFP4_OK;
+}
+
+// Bytes of the pre-scaled activation copy kept in the workspace.
+int64_t prescale_bytes(int64_t rows, int64_t K) { return round_up(rows * K * 2, 256); }
+
+enum Variant { kAuto = 0, kSmall = 1, kLarge = 2 };
+
+// Waves per workgroup of the small-M kernel: about four 128-wide K chunks per wave.
+int small_m_waves(int64_t KC) {
+    int w = 1;
+    while (w < 16 && (int64_t)(w * 2) * 4 <= KC) w *= 2;
+    return w;
+}
+
+template <bool GROUPED>
+nvfp4_status launch_small(const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob, const float* gs,
+                          int g_div, uint16_t* y, int64_t ld_y, int64_t rows_dense, const int32_t* offsets,
+                          hipStream_t st) {
+    const uint8_t* codes = blob;
+    const uint8_t* scales = blob + L.code_bytes();
+    const dim3 grid((unsigned)L.NU, GROUPED ? (unsigned)L.E : 1u);
+    const int W = small_m_waves(L.KC);
+#define NVFP4_SMALL(WW)                                                                                          \
+    hipLaunchKernelGGL((k_gemm_small_m<WW, GROUPED>), grid, dim3(WW * 64), 0, st, x, ld_x, codes, scales,         \
+                       (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows_dense, offsets)
+    switch (W) {
+        case 1: NVFP4_SMALL(1); break;
+        case 2: NVFP4_SMALL(2); break;
+        case 4: NVFP4_SMALL(4); break;
+        case 8: NVFP4_SMALL(8); break;
+        default: NVFP4_SMALL(16); break;
+    }
+#undef NVFP4_SMALL
+    return launched("small-M GEMM");
+}
+
+template <bool GROUPED>
+nvfp4_status launch_large(const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob, const float* gs,
+                          int g_div, uint16_t* y, int64_t ld_y, int64_t rows, const int32_t* offsets,
+                          hipStream_t st) {
+    const uint8_t* codes = blob;
+    const uint8_t* scales = blob + L.code_bytes();
+    const int64_t mtiles = GROUPED ? (rows + kLargeBM - 1) / kLargeBM + L.E : (rows + kLargeBM - 1) / kLargeBM;
+    if (mtiles > 65535) return fail(NVFP4_ERR_INVALID_ARG, "large-M GEMM: %lld row tiles exceed the grid limit", (long long)mtiles);
+    const dim3 grid((unsigned)((L.NU + kLargeUnits - 1) / kLargeUnits), (unsigned)mtiles);
+    hipLaunchKernelGGL((k_gemm_large_m<GROUPED>), grid, dim3(256), 0, st, x, ld_x, codes, scales, (int)L.NU,
+                       (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, (int)L.E);
+    return launched("large-M GEMM");
+}
+
+// Shared checks of the activation / output / pre-scale / workspace arguments.
+nvfp4_status check_gemm_io(const char* fn, const void* x, int64_t ld_x, const void* pre, const void* w,
+                           const void* gs, const void* y, int64_t ld_y, int64_t rows, int64_t N, int64_t K,
+                           const void* ws, int64_t ws_bytes) {
+    if (rows < 0) return fail(NVFP4_ERR_INVALID_ARG, "%s: row count %lld is negative", fn, (long long)rows);
+    if (ld_x < K) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_x = %lld < K = %lld", fn, (long long)ld_x, (long long)K);
+    if (ld_y < N) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_y = %lld < N = %lld", fn, (long long)ld_y, (long long)N);
+    if (!w) return fail(NVFP4_ERR_INVALID_ARG, "%s: w_repacked is NULL", fn);
+    if (!gs) return fail(NVFP4_ERR_INVALID_ARG, "%s: global scale pointer is NULL", fn);
+    if (rows > 0 && !x) return fail(NVFP4_ERR_INVALID_ARG, "%s: x is NULL", fn);
+    if (rows > 0 && !y) return fail(NVFP4_ERR_INVALID_ARG, "%s: y is NULL", fn);
+    if (!aligned(x, 16) || ld_x % 8 != 0)
+        return fail(NVFP4_ERR_ALIGNMENT, "%s: x must be 16-byte aligned with ld_x %% 8 == 0 (ld_x = %lld)", fn, (long long)ld_x);
+    if (pre && !aligned(pre, 16)) return fail(NVFP4_ERR_ALIGNMENT, "%s: pre_scale must be 16-byte aligned", fn);
+    if (!aligned(w, 16)) return fail(NVFP4_ERR_ALIGNMENT, "%s: w_repacked must be 16-byte aligned", fn);
+    if (!aligned(y, 2)) return fail(NVFP4_ERR_ALIGNMENT, "%s: y must be 2-byte aligned", fn);
+    if (pre) {
+        const int64_t need = prescale_bytes(rows, K);
+        if (ws_bytes < need || (need > 0 && !ws))
+            return fail(NVFP4_ERR_BUFFER_TOO_SMALL, "%s: workspace of %lld bytes is below the %lld bytes a pre_scale needs", fn,
+                        (long long)ws_bytes, (long long)need);
+        if (!aligned(ws, 16)) return fail(NVFP4_ERR_ALIGNMENT, "%s: workspace must be 16-byte aligned", fn);
+    }
+    return NVFP4_OK;
+}
+
+// Pre-quant scale: X' = RNE_bf16(X * s) into the workspace; returns the
+// activation the GEMM kernel reads.
+nvfp4_status apply_prescale(const void* x, int64_t& ld_x, const void* pre, int64_t rows, int64_t K, void* ws,
+                            const uint16_t*& xp, hipStream_t st) {
+    xp = static_cast<const uint16_t*>(x);
+    if (!pre) return NVFP4_OK;
+    const int64_t threads = rows * (K / 8);
+    hipLaunchKernelGGL(k_prescale, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(x), ld_x, static_cast<const uint16_t*>(pre), rows, K,
+                       static_cast<uint16_t*>(ws), K);
+    const nvfp4_status s = launched("pre-quant scale");
+    if (s != NVFP4_OK) return s;
+    xp = static_cast<const uint16_t*>(ws);
+    ld_x = K;
+    return NVFP4_OK;
+}
+
+nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void* w, const float* gs, int g_div,
+                        void* y, int64_t ld_y, int64_t M, int64_t N, int64_t K, void* ws, int64_t ws_bytes,
+                        int variant, void* stream) {
+    const char* fn = "nvfp4_w4a16_gemm";
+    nvfp4_status s = check_weight_shape(fn, 1, N, K);
+    if (s != NVFP4_OK) return s;
+    s = check_gemm_io(fn, x, ld_x, pre, w, gs, y, ld_y, M, N, K, ws, ws_bytes);
+    if (s != NVFP4_OK) return s;
+    if (variant < kAuto || variant > kLarge) return fail(NVFP4_ERR_INVALID_ARG, "%s: unknown variant %d", fn, variant);
+    if (variant == kSmall && M > kSmallRows)
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: the small-M variant takes M <= %d (M = %lld)", fn, kSmallRows, (long long)M);
+    if (M == 0) return ok();   // zero rows: nothing is launched
+    if (M * (K / 8) > (int64_t)0xFFFFFFFF * 256) return fail(NVFP4_ERR_INVALID_ARG, "%s: M * K too large", fn);
+    const Layout L = make_layout(1, N, K);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint16_t* xp;
+    s = apply_prescale(x, ld_x, pre, M, K, ws, xp, st);
+    if (s != NVFP4_OK) return s;
+    const bool small = variant == kSmall || (variant == kAuto && M <= kSmallRows);
+    const uint8_t* blob = static_cast<const uint8_t*>(w);
+    uint16_t* yo = static_cast<uint16_t*>(y);
+    return small ? launch_small<false>(L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, st)
+                 : launch_large<false>(L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_last_error(void) { return g_err; }
+
+int64_t nvfp4_repack_bytes(int64_t E, int64_t N, int64_t K) {
+    if (check_weight_shape("nvfp4_repack_bytes", E, N, K) != NVFP4_OK) return -1;
+    return make_layout(E, N, K).total_bytes();
+}
+
+nvfp4_status nvfp4_repack(const uint8_t* w_packed, int64_t ld_w, const uint8_t* w_scale, int64_t ld_s, int64_t E,
+                          int64_t N, int64_t K, void* out, int64_t out_bytes, void* stream) {
+    const char* fn = "nvfp4_repack";
+    nvfp4_status s = check_weight_shape(fn, E, N, K);
+    if (s != NVFP4_OK) return s;
+    if (!w_packed) return fail(NVFP4_ERR_INVALID_ARG, "%s: w_packed is NULL", fn);
+    if (!w_scale) return fail(NVFP4_ERR_INVALID_ARG, "%s: w_scale is NULL", fn);
+    if (!out) return fail(NVFP4_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if (ld_w < K / 2) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_w = %lld < K/2 = %lld", fn, (long long)ld_w, (long long)(K / 2));
+    if (ld_s < K / 16) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_s = %lld < K/16 = %lld", fn, (long long)ld_s, (long long)(K / 16));
+    if (!aligned(out, 16)) return fail(NVFP4_ERR_ALIGNMENT, "%s: out must be 16-byte aligned", fn);
+    const Layout L = make_layout(E, N, K);
+    if (out_bytes < L.total_bytes())
+        return fail(NVFP4_ERR_BUFFER_TOO_SMALL, "%s: out_bytes = %lld < %lld", fn, (long long)out_bytes, (long long)L.total_bytes());
+    const int64_t lanes = L.blocks() * 64;
+    uint8_t* o = static_cast<uint8_t*>(out);
+    hipLaunchKernelGGL(k_repack, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       w_packed, ld_w, w_scale, ld_s, N, K, L.NU, L.KC, lanes, o, o + L.code_bytes());
+    return launched(fn);
+}
+
+nvfp4_status nvfp4_dequant_bf16(const void* w_repacked, int64_t E, int64_t N, int64_t K, void* out, int64_t ld_out,
+                                void* stream) {
+    const char* fn = "nvfp4_dequant_bf16";
+    nvfp4_status s = check_weight_shape(fn, E, N, K);
+    if (s != NVFP4_OK) return s;
+    if (!w_repacked || !out) return fail(NVFP4_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (ld_out < K) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_out = %lld < K", fn, (long long)ld_out);
+    if (!aligned(w_repacked, 16) || !aligned(out, 2)) return fail(NVFP4_ERR_ALIGNMENT, "%s: misaligned pointer", fn);
+    const Layout L = make_layout(E, N, K);
+    const int64_t lanes = L.blocks() * 64;
+    const uint8_t* b = static_cast<const uint8_t*>(w_repacked);
+    hipLaunchKernelGGL(k_dequant, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, static_cast<hipStream_t>(stream), b,
+                       b + L.code_bytes(), N, K, L.NU, L.KC, lanes, static_cast<uint16_t*>(out), ld_out);
+    return launched(fn);
+}
+
+int64_t nvfp4_w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || check_weight_shape("nvfp4_w4a16_gemm_workspace_bytes", 1, N, K) != NVFP4_OK) return -1;
+    return prescale_bytes(M, K);
+}
+
+nvfp4_status nvfp4_w4a16_gemm(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
+                              const float* global_scale, int global_scale_is_divisor, void* y, int64_t ld_y,
+                              int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                              void* stream) {
+    return dense_gemm(x, ld_x, pre_scale, w_repacked, global_scale, global_scale_is_divisor != 0, y, ld_y, M, N, K,
+                      workspace, workspace_bytes, kAuto, stream);
+}
+
+nvfp4_status nvfp4_w4a16_gemm_variant(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
+                                      const float* global_scale, int global_scale_is_divisor, void* y, int64_t ld_y,
+                                      int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                                      int variant, void* stream) {
+    return dense_gemm(x, ld_x, pre_scale, w_repacked, global_scale, global_scale_is_divisor != 0, y, ld_y, M, N, K,
+                      workspace, workspace_bytes, variant, stream);
+}
+
+int64_t nvfp4_w4a16_grouped_gemm_workspace_bytes(int64_t R, int64_t E, int64_t N, int64_t K) {
+    if (R < 0 || check_weight_shape("nvfp4_w4a16_grouped_gemm_workspace_bytes", E, N, K) != NVFP4_OK) return -1;
+    return prescale_bytes(R, K);
+}
+
+nvfp4_status nvfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t* expert_offsets, const void* pre_scale,
+                                      const void* w_repacked, const float* global_scales, int global_scale_is_divisor,
+                                      void* y, int64_t ld_y, int64_t R, int64_t E, int64_t N, int64_t K,
+                                      void* workspace, int64_t workspace_bytes, void* stream) {
+    const char* fn = "nvfp4_w4a16_grouped_gemm";
+    nvfp4_status s = check_weight_shape(fn, E, N, K);
+    if (s != NVFP4_OK) return s;
+    s = check_gemm_io(fn, x, ld_x, pre_scale, w_repacked, global_scales, y, ld_y, R, N, K, workspace, workspace_bytes);
+    if (s != NVFP4_OK) return s;
+    if (!expert_offsets) return fail(NVFP4_ERR_INVALID_ARG, "%s: expert_offsets is NULL", fn);
+    if (!aligned(expert_offsets, 4)) return fail(NVFP4_ERR_ALIGNMENT, "%s: expert_offsets must be 4-byte aligned", fn);
+    if (R > (int64_t)1 << 31) return fail(NVFP4_ERR_INVALID_ARG, "%s: R = %lld exceeds int32 offsets", fn, (long long)R);
+    if (R == 0) return ok();   // zero rows: nothing is launched
+    const Layout L = make_layout(E, N, K);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint16_t* xp;
+    s = apply_prescale(x, ld_x, pre_scale, R, K, workspace, xp, st);
+    if (s != NVFP4_OK) return s;
+    const uint8_t* blob = static_cast<const uint8_t*>(w_repacked);
+    uint16_t* yo = static_cast<uint16_t*>(y);
+    const int g_div = global_scale_is_divisor != 0;
+    // Few rows per expert on average: the weight stream dominates, use the small-M kernel (passes of 16 rows).
+    if (R <= (int64_t)kSmallRows * E)
+        return launch_small<true>(L, xp, ld_x, blob, global_scales, g_div, yo, ld_y, 0, expert_offsets, st);
+    return launch_large<true>(L, xp, ld_x, blob, global_scales, g_div, yo, ld_y, R, expert_offsets, st);
+}
+
+}  // extern "C"
