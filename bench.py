@@ -1,0 +1,404 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 NVFP4 GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--only NAME] [--no-extra] [--no-cpu]
+
+A step is one call of the hot path on one batch: the decode-shaped dense
+linear Y[16, 14336] = g * X[16, 4096] . dequant(W)^T, the workload the HBM
+target is quoted on.  Inputs are resident in HBM before the timed region.
+The weight is rotated over 16 distinct copies (528 MB, more than twice the
+256 MB Infinity Cache), so each step streams its weight from HBM.
+
+Timing: W untimed eager warmup calls, then the K timed calls are captured in
+one HIP graph (uploaded by one untimed replay), and the timed replay is
+bracketed by torch.cuda.synchronize() on both sides.  HIP events recorded
+inside the graph around every call give the per-launch kernel durations used
+for the roofline fraction; the events around the whole replay give
+ms_per_step.
+
+Prints ONE JSON line (rank 0, one GPU): metric/value for the step, plus
+"roofline" (dominant kernel vs HBM peak 8 TB/s), "cpu_baseline" (the CPU
+oracle timed on a bounded sample of the same workload on the host cores) and
+"extra" (the other workloads, each timed the same way: throughput in GB/s and
+TFLOP/s with their roofline fractions).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+HEADLINE = "decode_M16_N14336_K4096"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--only", default=None, help="time one workload only (for profiling runs)")
+    p.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain device copy of 512 MiB per step (calibrates HBM byte counters)")
+    p.add_argument("--list", action="store_true")
+    return p.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "weight_only_fp4_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+# ------------------------------------------------------------- workloads ---
+
+class Workload:
+    def __init__(self, name, kind, kernel, alg_bytes, flops, launch, copies, meta, bound):
+        self.name, self.kind, self.kernel = name, kind, kernel
+        self.alg_bytes, self.flops, self.launch, self.copies = alg_bytes, flops, launch, copies
+        self.meta, self.bound = meta, bound
+
+
+def dense_bytes(M, N, K, pre):
+    return 0.5625 * N * K + 2.0 * M * K + 2.0 * M * N + (2.0 * K if pre else 0.0) + 4.0
+
+
+def make_dense(name, M, N, K, *, seed, scales="pow2_mant", g_stored=1.0 / 2688.0, divisor=False, prescale=False,
+               copies=1, host_case=None):
+    import torch
+    import synth
+    import weight_only_fp4_amd as nv
+    dev = "cuda:0"
+    if host_case is not None:
+        c = host_case
+        x = torch.from_numpy(c.x.view("int16")).view(torch.bfloat16).to(dev)
+        w = torch.from_numpy(c.w).to(dev)
+        s = torch.from_numpy(c.s).to(dev)
+        pre = None if c.pre is None else torch.from_numpy(c.pre.view("int16")).view(torch.bfloat16).to(dev)
+        g_stored, divisor = c.g_stored, c.g_is_divisor
+    else:
+        x = synth.device_normal_bf16((M, K), seed, dev)
+        w = synth.device_codes((N, K // 2), seed + 1, dev)
+        s = synth.device_scales((N, K // 16), seed + 2, scales, dev)
+        pre = synth.device_prescale(K, seed + 3, dev) if prescale else None
+    g = torch.tensor([g_stored], dtype=torch.float32, device=dev)
+    blob = nv.repack(w, s)
+    del w, s
+    blobs = [blob] + [blob.clone() for _ in range(copies - 1)]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = None
+    if pre is not None:
+        ws = torch.empty(max(nv.lib().nvfp4_w4a16_gemm_workspace_bytes(M, N, K), 1), dtype=torch.uint8, device=dev)
+
+    def launch(i):
+        nv.gemm(x, blobs[i % copies], N, K, g, divisor, pre, out=y, workspace=ws)
+
+    kernel = "k_gemm_small_m" if M <= 16 else "k_gemm_large_m"
+    flops = 2.0 * M * N * K
+    ab = dense_bytes(M, N, K, pre is not None)
+    bound = "hbm" if flops / ab < (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) else "mfma"
+    meta = {"M": M, "N": N, "K": K, "prescale": pre is not None, "divisor": bool(divisor), "weight_copies": copies}
+    wl = Workload(name, "dense", kernel, ab, flops, launch, copies, meta, bound)
+    wl.tensors = dict(x=x, y=y, g=g, blobs=blobs)
+    return wl
+
+
+def make_grouped(name, T, fc, *, seed=1004, copies=1, E=128, topk=8):
+    import numpy as np
+    import torch
+    import synth
+    import weight_only_fp4_amd as nv
+    dev = "cuda:0"
+    K, N = (2048, 2 * 768) if fc == "fc1" else (768, 2048)
+    route = synth.zipf_routing(synth.rng(synth.routing_seed(seed)), T, E, topk)
+    counts = np.bincount(route.reshape(-1), minlength=E)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    R = int(offsets[-1])
+    active = int(np.count_nonzero(counts))
+    sd = seed * 10 + (1 if fc == "fc1" else 2)
+    x = synth.device_normal_bf16((R, K), sd, dev)
+    w = synth.device_codes((E, N, K // 2), sd + 1, dev)
+    s = synth.device_scales((E, N, K // 16), sd + 2, "pow2_mant", dev)
+    v = synth.rng(sd + 3).integers(-2, 3, size=E)
+    gs = torch.tensor((np.exp2(v.astype(np.float64)) / 2688.0).astype(np.float32), device=dev)
+    off = torch.from_numpy(offsets).to(dev)
+    blob = nv.repack(w, s)
+    del w, s
+    blobs = [blob] + [blob.clone() for _ in range(copies - 1)]
+    y = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
+
+    def launch(i):
+        nv.grouped_gemm(x, off, blobs[i % copies], E, N, K, gs, False, None, out=y)
+
+    ab = active * 0.5625 * N * K + 2.0 * R * K + 2.0 * R * N + 4.0 * E + 4.0 * (E + 1)
+    flops = 2.0 * R * N * K
+    kernel = "k_gemm_small_m" if R <= 16 * E else "k_gemm_large_m"
+    bound = "hbm" if flops / ab < (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) else "mfma"
+    meta = {"E": E, "topk": topk, "T": T, "R": R, "N": N, "K": K, "active_experts": active, "weight_copies": copies}
+    wl = Workload(name, "grouped", kernel, ab, flops, launch, copies, meta, bound)
+    wl.tensors = dict(x=x, y=y, blobs=blobs)
+    return wl
+
+
+def workload_specs():
+    """name -> builder (the headline first)."""
+    return {
+        HEADLINE: lambda: make_dense(HEADLINE, 16, 14336, 4096, seed=1001, g_stored=1 / (448 * 6), copies=16),
+        "decode_M1_N14336_K4096": lambda: make_dense("decode_M1_N14336_K4096", 1, 14336, 4096, seed=1001,
+                                                     g_stored=1 / (448 * 6), copies=16),
+        "decode_M8_N14336_K4096": lambda: make_dense("decode_M8_N14336_K4096", 8, 14336, 4096, seed=1001,
+                                                     g_stored=1 / (448 * 6), copies=16),
+        "decode_M1_N4096_K14336": lambda: make_dense("decode_M1_N4096_K14336", 1, 4096, 14336, seed=1001,
+                                                     g_stored=1 / (448 * 6), copies=16),
+        "decode_M16_N4096_K14336": lambda: make_dense("decode_M16_N4096_K14336", 16, 4096, 14336, seed=1001,
+                                                      g_stored=1 / (448 * 6), copies=16),
+        "prefill_M4096_N14336_K4096": lambda: make_dense("prefill_M4096_N14336_K4096", 4096, 14336, 4096, seed=1002,
+                                                         scales="log_uniform", copies=1),
+        "prefill_M8192_N17408_K5120": lambda: make_dense("prefill_M8192_N17408_K5120", 8192, 17408, 5120, seed=1002,
+                                                         scales="log_uniform", copies=1),
+        "lmhead_M1_N131072_K4096": lambda: make_dense("lmhead_M1_N131072_K4096", 1, 131072, 4096, seed=1003,
+                                                      g_stored=2688.0, divisor=True, prescale=True, copies=2),
+        "lmhead_M64_N131072_K4096": lambda: make_dense("lmhead_M64_N131072_K4096", 64, 131072, 4096, seed=1003,
+                                                       g_stored=2688.0, divisor=True, prescale=True, copies=2),
+        "ragged_M33_N1000_K1040": lambda: make_dense("ragged_M33_N1000_K1040", 33, 1000, 1040, seed=1003,
+                                                     g_stored=2688.0, divisor=True, prescale=True, copies=1),
+        "tiny_M4_N256_K512": lambda: make_dense("tiny_M4_N256_K512", 4, 256, 512, seed=1000, g_stored=1 / 448,
+                                                copies=1),
+        "moe_fc1_T16": lambda: make_grouped("moe_fc1_T16", 16, "fc1", copies=2),
+        "moe_fc2_T16": lambda: make_grouped("moe_fc2_T16", 16, "fc2", copies=2),
+        "moe_fc1_T2048": lambda: make_grouped("moe_fc1_T2048", 2048, "fc1", copies=1),
+        "moe_fc2_T2048": lambda: make_grouped("moe_fc2_T2048", 2048, "fc2", copies=1),
+    }
+
+
+# ---------------------------------------------------------------- timing ---
+
+def time_workload(wl, steps, warmup):
+    """Return dict: ms_per_step (events around the timed replay), per-launch kernel ms (events inside the graph)."""
+    import torch
+    for i in range(warmup):
+        wl.launch(i)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        wl.launch(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    def capture(with_events):
+        graph = torch.cuda.CUDAGraph()
+        evs = [(torch.cuda.Event(enable_timing=True, external=True), torch.cuda.Event(enable_timing=True, external=True))
+               for _ in range(steps)] if with_events else None
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                if evs:
+                    evs[i][0].record()
+                wl.launch(warmup + i)
+                if evs:
+                    evs[i][1].record()
+        return graph, evs
+
+    try:
+        graph, evs = capture(True)
+    except Exception as exc:   # event nodes in graphs unsupported: fall back to whole-replay timing
+        print(f"[bench] per-launch events in graph unavailable ({type(exc).__name__}: {exc}); using replay mean",
+              file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        graph, evs = capture(False)
+    graph.replay()                       # uploads the graph; untimed
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    per = [a.elapsed_time(b) for a, b in evs] if evs else None
+    del graph
+    return {"ms_per_step": total_ms / steps, "wall_ms_per_step": 1e3 * wall / steps,
+            "kernel_ms": (sum(per) / len(per)) if per else total_ms / steps,
+            "kernel_ms_min": min(per) if per else None, "kernel_ms_source": "events_in_graph" if per else "replay_mean"}
+
+
+def summarize(wl, t):
+    ms = t["ms_per_step"]
+    kms = t["kernel_ms"]
+    gbs = wl.alg_bytes / (ms * 1e-3) / 1e9
+    tfl = wl.flops / (ms * 1e-3) / 1e12
+    kgbs = wl.alg_bytes / (kms * 1e-3) / 1e9
+    ktfl = wl.flops / (kms * 1e-3) / 1e12
+    return {"us_per_step": round(ms * 1e3, 3), "us_per_launch_kernel": round(kms * 1e3, 3),
+            "GBps": round(gbs, 1), "TFLOPs": round(tfl, 2),
+            "hbm_frac": round(kgbs / HBM_PEAK_GBS, 4), "mfma_frac": round(ktfl / BF16_PEAK_TFLOPS, 4),
+            "bound": wl.bound, "alg_bytes": wl.alg_bytes, "flops": wl.flops, **wl.meta}
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    for r in rec.get("records", []):
+        if r.get("workload") == workload and r.get("kernel") == kernel and r.get("source_sha256") == source_digest():
+            return r.get("hbm_bytes_per_launch")
+    return None
+
+
+# ----------------------------------------------------------- cpu baseline ---
+
+def cpu_baseline(case, target_s=12.0):
+    """The CPU oracle, as is, on a bounded column sample of the headline workload; weight GB/s."""
+    import oracle
+    thr = oracle.max_threads()
+    n = 64
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm(case.x, case.w[:n], case.s[:n], case.g_stored, case.g_is_divisor, case.pre)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or n >= case.N:
+            break
+        n = min(case.N, max(n * 2, int(n * target_s / max(dt, 1e-3) * 1.05)))
+    wbytes = 0.5625 * n * case.K
+    return {"value": round(wbytes / dt / 1e9, 4), "unit": "GB/s", "cores": thr, "kind": "oracle",
+            "sample": f"M={case.M}, K={case.K}, first {n} of N={case.N} weight rows ({dt:.1f} s, fp64, OpenMP)"}
+
+
+def sanity_parity(case, y):
+    """Sampled outputs of the benchmarked call against the oracle (not timed)."""
+    import numpy as np
+    import oracle
+    import synth
+    g = synth.rng(5)
+    rows, cols = g.integers(0, case.M, 512), g.integers(0, case.N, 512)
+    ref = oracle.gemm_sampled(case.x, case.w, case.s, case.g_stored, case.g_is_divisor, case.pre, rows, cols)
+    got = y.float().cpu().numpy().astype(np.float64)[rows, cols]
+    ok, info = oracle.accept(got, ref)
+    return {"ok": bool(ok), "rel_fro": info.get("rel_fro"), "samples": len(rows)}
+
+
+# ------------------------------------------------------------------ main ---
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1 (the multi-GPU sharding is "
+                                   "described in DESIGN.md and not built)", "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    if args.list:
+        print("\n".join(workload_specs()))
+        return
+    import torch
+    import weight_only_fp4_amd as nv
+    nv.lib()
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    device = {"name": props.name, "cus": props.multi_processor_count, "arch": getattr(props, "gcnArchName", "")}
+
+    if args.copy_calibration:
+        nbytes = 512 << 20
+        a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        a.fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(args.warmup):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            b.copy_(a)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "ms": ms,
+                          "GBps": 2 * nbytes / ms / 1e6, "steps": args.steps}), flush=True)
+        return
+
+    specs = workload_specs()
+    head_name = args.only or HEADLINE
+    if head_name not in specs:
+        raise SystemExit(f"unknown workload {head_name}; --list shows them")
+
+    host_case = None
+    if head_name == HEADLINE:
+        import synth
+        host_case = synth.decode_case(16)
+        wl = make_dense(HEADLINE, 16, 14336, 4096, seed=1001, copies=16, host_case=host_case)
+    else:
+        wl = specs[head_name]()
+    print(f"[bench] timing {wl.name} ({args.steps} steps, {args.warmup} warmup)", file=sys.stderr, flush=True)
+    t = time_workload(wl, args.steps, args.warmup)
+    s = summarize(wl, t)
+    parity = sanity_parity(host_case, wl.tensors["y"]) if host_case is not None else None
+
+    kms = t["kernel_ms"]
+    if wl.bound == "hbm":
+        ach = wl.alg_bytes / (kms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        ach = wl.flops / (kms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+    roof.update({"traffic": traffic_for(wl.kernel, wl.name), "kernel": wl.kernel,
+                 "alg_units_per_launch": wl.alg_bytes if wl.bound == "hbm" else wl.flops,
+                 "kernel_us": round(kms * 1e3, 3), "timing": t["kernel_ms_source"]})
+
+    value = s["GBps"] if wl.bound == "hbm" else s["TFLOPs"]
+    unit = "GB/s" if wl.bound == "hbm" else "TFLOP/s"
+    metric = (f"W4A16 NVFP4 GEMM weight-stream throughput ({wl.name})" if wl.bound == "hbm"
+              else f"W4A16 NVFP4 GEMM throughput ({wl.name})")
+    out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(t["ms_per_step"], 6), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": wl.name, **wl.meta, "parallelism": "single-gpu"},
+           "roofline": roof, "device": device, "source_sha256": source_digest()[:16]}
+    if parity is not None:
+        out["parity"] = parity
+    del wl
+    torch.cuda.empty_cache()
+
+    if not args.only and not args.no_extra:
+        extra = {}
+        for name, build in specs.items():
+            if name == HEADLINE:
+                continue
+            print(f"[bench] timing {name}", file=sys.stderr, flush=True)
+            w2 = build()
+            t2 = time_workload(w2, min(args.steps, 20), min(args.warmup, 5))
+            extra[name] = summarize(w2, t2)
+            del w2
+            torch.cuda.empty_cache()
+        out["extra"] = extra
+
+    if not args.only and not args.no_cpu:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(host_case)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -203,3 +203,39 @@ def moe_fc1_case(T: int, seed: int = 1004, E: int = 128, topk: int = 8, prescale
 def moe_fc2_case(T: int, seed: int = 1004, E: int = 128, topk: int = 8) -> GroupedCase:
     """Grouped FC2: K=768 -> N=2048 per expert, fresh N(0,1) input rows, same routing as FC1 of this seed."""
     return grouped_case(T, E, topk, 2048, 768, seed + 100, x_source="fresh", seed0=seed, name=f"moe_fc2_T{T}")
+
+
+# ------------------------------------------------------- device generators ---
+# Same distributions as above, drawn on the GPU with a seeded torch generator,
+# for benchmark workloads too large to draw quickly on the host.  (A different
+# random stream than the numpy recipes: used only where no oracle comparison
+# is made on the exact values.)
+
+def _tgen(seed: int, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def device_codes(shape, seed: int, device="cuda") -> torch.Tensor:
+    """Packed codes [..., K/2]: uniform bytes = two independent uniform 4-bit codes."""
+    return torch.randint(0, 256, shape, dtype=torch.uint8, device=device, generator=_tgen(seed, device))
+
+
+def device_scales(shape, seed: int, kind: str = "pow2_mant", device="cuda") -> torch.Tensor:
+    g = _tgen(seed, device)
+    if kind == "pow2_mant":
+        u = torch.randint(-4, 3, shape, device=device, generator=g)
+        m = torch.randint(0, 8, shape, device=device, generator=g)
+        return (((u + 7) << 3) | m).to(torch.uint8)
+    u = torch.rand(shape, device=device, generator=g, dtype=torch.float32) * 9.0 - 6.0
+    return torch.exp2(u).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def device_normal_bf16(shape, seed: int, device="cuda") -> torch.Tensor:
+    return torch.randn(shape, device=device, generator=_tgen(seed, device), dtype=torch.float32).to(torch.bfloat16)
+
+
+def device_prescale(K: int, seed: int, device="cuda") -> torch.Tensor:
+    g = _tgen(seed, device)
+    return (torch.rand(K, device=device, generator=g) * (math.e - 1.0 / math.e) + 1.0 / math.e).to(torch.bfloat16)

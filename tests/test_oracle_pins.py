@@ -322,3 +322,23 @@ def test_planted_mistakes_fail_acceptance(kind):
     ref = oracle.gemm(c.x, c.w, c.s, c.g_stored, c.g_is_divisor, c.pre)
     ok, info = oracle.accept(_planted(kind, c), ref)
     assert not ok, (kind, info)
+
+
+def test_round_bf16_np_matches_c_oracle():
+    g = synth.rng(17)
+    v = np.concatenate([g.standard_normal(2000) * 10.0 ** g.integers(-30, 30, 2000),
+                        [1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 2.0 ** -133, 2.0 ** -135, 0.0, -0.0]])
+    assert np.array_equal(oracle.round_bf16_np(v), np.array([oracle.round_bf16(a) for a in v]))
+
+
+def test_acceptance_floor_only_lifts_tiny_outputs():
+    """From 1024 outputs up the bound is 2e-3; the correctly rounded result meets it there."""
+    c = synth.tiny_case()                       # 4 x 256 = 1024 outputs
+    ref = oracle.gemm(c.x, c.w, c.s, c.g_stored, False, None)
+    ok, info = oracle.accept(oracle.round_bf16_np(ref), ref)
+    assert ok and info["rel_fro_bound"] == 2e-3
+    # a 17-output column dominated by one element: rounding alone exceeds 2e-3, the bound follows it
+    r = np.array([0.0272096, 0.0712413, 0.0512778, 0.0185412, 0.0525297, -0.0131747, -0.0721159, 0.0510564,
+                  -0.12936933, -0.0099833, 0.01, 0.02, -0.03, 0.004, 0.005, -0.006, 0.007])
+    ok, info = oracle.accept(oracle.round_bf16_np(r), r)
+    assert ok and info["rel_fro"] > 2e-3

@@ -17,6 +17,8 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
     # packed fp32 VALU ops are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the small-M kernel post-processes every result with VALU FMAs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
 ]
 

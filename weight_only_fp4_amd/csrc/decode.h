@@ -22,11 +22,15 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // E4M3 (OCP E4M3FN: bias 7, subnormal m * 2^-9, 0x7F / 0xFF NaN) -> fp32, exact.
+// Branch-free: the exponent and mantissa bits are placed under an fp32
+// exponent field biased by 120, so normal codes become 2^(e-127) (1 + m/8)
+// and subnormal codes (e = 0) the fp32 denormal m 2^-129; one multiply by
+// 2^120 then gives 2^(e-7) (1 + m/8), resp. m 2^-9, exactly (fp32 denormals
+// are kept, the default of this target).
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-    if ((b & 0x7Fu) == 0x7Fu) mag = __uint_as_float(0x7FC00000u);
-    return (b & 0x80u) ? -mag : mag;
+    const float mag = __uint_as_float((b & 0x7Fu) << 20) * 0x1p120f;
+    const float v = ((b & 0x7Fu) == 0x7Fu) ? __uint_as_float(0x7FC00000u) : mag;
+    return __uint_as_float(__float_as_uint(v) | ((b & 0x80u) << 24));
 }
 
 // Split a scale s into the operand handed to the exponent-only conversion
@@ -95,6 +99,18 @@ __device__ __forceinline__ s16x4 dwords_to_s16x4(uint32_t lo, uint32_t hi) {
 }
 
 __device__ __forceinline__ bf16x8 uint4_to_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Streaming loads of weight codes and scales: every byte is read exactly
+// once, so the loads are marked non-temporal and do not displace the
+// activations (which are reused) from the caches.
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream_u4(const uint8_t* p) {
+    const u32x4v t = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+    return make_uint4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ uint32_t load_stream_u16(const uint8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+}
 
 // Global scale as used in the epilogue: the stored value, or its correctly
 // rounded fp32 reciprocal when it is stored as a divisor.

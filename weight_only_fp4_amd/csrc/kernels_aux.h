@@ -12,15 +12,17 @@ namespace nvfp4 {
 __global__ void __launch_bounds__(256) k_repack(const uint8_t* __restrict__ w, int64_t ld_w,
                                                 const uint8_t* __restrict__ s, int64_t ld_s,
                                                 int64_t N, int64_t K, int64_t NU, int64_t KC, int64_t total_lanes,
-                                                uint8_t* __restrict__ codes_out, uint8_t* __restrict__ scales_out) {
+                                                BlobView v, uint8_t* __restrict__ codes_out,
+                                                uint8_t* __restrict__ scales_out) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= total_lanes) return;
     const int lane = (int)(t & 63);
-    const int64_t blk = t >> 6;              // (e * NU + u) * KC + c
-    const int64_t c = blk % KC;
-    const int64_t eu = blk / KC;
+    const int64_t idx = t >> 6;              // (e * NU + u) * KC + c
+    const int64_t c = idx % KC;
+    const int64_t eu = idx / KC;
     const int64_t u = eu % NU;
     const int64_t e = eu / NU;
+    const int64_t blk = v.block(e, u, c);
     const int64_t n = u * kUnitN + (lane & 15);
     const int64_t kbyte0 = c * (kChunkK / 2) + (lane >> 4) * 16;   // canonical byte of the lane's first code
     const int64_t kbytes = K / 2;
@@ -47,29 +49,29 @@ __global__ void __launch_bounds__(256) k_repack(const uint8_t* __restrict__ w, i
 
 // Decode a repacked blob to bf16 [E][N][ld_out] with the GEMM kernels' decode
 // (decode8_bf16).  One thread per (expert, row unit, K chunk, lane).
-__global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                                                 int64_t N, int64_t K, int64_t NU, int64_t KC, int64_t total_lanes,
-                                                 uint16_t* __restrict__ out, int64_t ld_out) {
+__global__ void __launch_bounds__(256) k_dequant(BlobView v, int64_t N, int64_t K, int64_t NU, int64_t KC,
+                                                 int64_t total_lanes, uint16_t* __restrict__ out, int64_t ld_out) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= total_lanes) return;
     const int lane = (int)(t & 63);
-    const int64_t blk = t >> 6;
-    const int64_t c = blk % KC;
-    const int64_t eu = blk / KC;
+    const int64_t idx = t >> 6;
+    const int64_t c = idx % KC;
+    const int64_t eu = idx / KC;
     const int64_t u = eu % NU;
     const int64_t e = eu / NU;
+    const int64_t blk = v.block(e, u, c);
     const int64_t n = u * kUnitN + (lane & 15);
     if (n >= N) return;
-    const uint4 q = *reinterpret_cast<const uint4*>(codes + blk * kCodeBlock + lane * 16);
-    const uint32_t sc = *reinterpret_cast<const uint16_t*>(scales + blk * kScaleBlock + lane * 2);
+    const uint4 q = *reinterpret_cast<const uint4*>(v.codes + blk * kCodeBlock + lane * 16);
+    const uint32_t sc = *reinterpret_cast<const uint16_t*>(v.scales + blk * kScaleBlock + lane * 2);
     const float s0 = e4m3_to_f32(sc & 0xFFu), s1 = e4m3_to_f32(sc >> 8);
     const uint32_t qd[4] = {q.x, q.y, q.z, q.w};
     const int64_t k0 = c * kChunkK + (lane >> 4) * 32;
     uint16_t* row = out + (e * N + n) * ld_out;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        const uint4 v = decode8_bf16(qd[d], d < 2 ? s0 : s1);
-        const uint32_t vd[4] = {v.x, v.y, v.z, v.w};
+        const uint4 dv = decode8_bf16(qd[d], d < 2 ? s0 : s1);
+        const uint32_t vd[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int64_t k = k0 + d * 8 + i;

@@ -55,11 +55,55 @@ int64_t prescale_bytes(int64_t rows, int64_t K) { return round_up(rows * K * 2, 
 
 enum Variant { kAuto = 0, kSmall = 1, kLarge = 2 };
 
-// Waves per workgroup of the small-M kernel: about four 128-wide K chunks per wave.
-int small_m_waves(int64_t KC) {
-    int w = 1;
-    while (w < 16 && (int64_t)(w * 2) * 4 <= KC) w *= 2;
-    return w;
+// Small-M launch shape.  The weights stream through the vector caches with
+// non-temporal loads; measured on MI355X, a CU streams best with roughly
+// 32 KB of weight loads in flight (one kilobyte per wave and ring slot), so
+// the product workgroups x waves x ring depth is aimed at 256 CUs x 32 KB.
+// Rows 9..16 use the 16x16x32 form with two units per wave sharing one
+// activation fragment.
+struct SmallShape {
+    int mg, nt, w, d;
+};
+
+SmallShape small_m_shape(const Layout& L, int64_t rows, bool grouped) {
+    SmallShape s;
+    s.mg = grouped ? 0 : (rows <= 8 ? (int)((rows + 3) / 4) : 16);
+    s.nt = (!grouped && rows > 4 && L.NU >= 512) ? 2 : 1;
+    s.d = (s.mg == 0 || s.mg <= 2) ? 4 : 2;
+    const int64_t ctas = (L.NU + s.nt - 1) / s.nt * (grouped ? (L.E + 1) / 2 : 1);
+    s.w = 1;
+    while (s.w < 16 && ctas * (2 * s.w) * s.d <= 8192 && L.KC >= 4 * (2 * s.w)) s.w *= 2;
+    if (s.w < 2 && L.KC >= 8) s.w = 2;
+    if (s.mg == 16 && s.w > 8) s.w = 8;
+    return s;
+}
+
+template <int MG, int NT, int W, bool GROUPED>
+void launch_small_t(dim3 grid, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* codes,
+                    const uint8_t* scales, const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows,
+                    const int32_t* offsets, hipStream_t st) {
+    constexpr int D = (MG == 0 || MG <= 2) ? 4 : 2;   // small_m_shape's d
+    const BlobView bv = make_view(L, codes);
+    (void)scales;
+    if (L.K % kChunkK == 0)
+        hipLaunchKernelGGL((k_gemm_small_m<MG, NT, W, D, GROUPED, true>), grid, dim3(W * 64), 0, st, x, ld_x, bv,
+                           (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets);
+    else
+        hipLaunchKernelGGL((k_gemm_small_m<MG, NT, W, D, GROUPED, false>), grid, dim3(W * 64), 0, st, x, ld_x, bv,
+                           (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets);
+}
+
+template <int MG, int NT, bool GROUPED>
+void launch_small_w(int w, dim3 grid, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* codes,
+                    const uint8_t* scales, const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows,
+                    const int32_t* offsets, hipStream_t st) {
+    switch (w) {
+        case 1: launch_small_t<MG, NT, 1, GROUPED>(grid, L, x, ld_x, codes, scales, gs, g_div, y, ld_y, rows, offsets, st); break;
+        case 2: launch_small_t<MG, NT, 2, GROUPED>(grid, L, x, ld_x, codes, scales, gs, g_div, y, ld_y, rows, offsets, st); break;
+        case 4: launch_small_t<MG, NT, 4, GROUPED>(grid, L, x, ld_x, codes, scales, gs, g_div, y, ld_y, rows, offsets, st); break;
+        case 8: launch_small_t<MG, NT, 8, GROUPED>(grid, L, x, ld_x, codes, scales, gs, g_div, y, ld_y, rows, offsets, st); break;
+        default: launch_small_t<MG, NT, 16, GROUPED>(grid, L, x, ld_x, codes, scales, gs, g_div, y, ld_y, rows, offsets, st); break;
+    }
 }
 
 template <bool GROUPED>
@@ -68,17 +112,23 @@ nvfp4_status launch_small(const Layout& L, const uint16_t* x, int64_t ld_x, cons
                           hipStream_t st) {
     const uint8_t* codes = blob;
     const uint8_t* scales = blob + L.code_bytes();
-    const dim3 grid((unsigned)L.NU, GROUPED ? (unsigned)L.E : 1u);
-    const int W = small_m_waves(L.KC);
-#define NVFP4_SMALL(WW)                                                                                          \
-    hipLaunchKernelGGL((k_gemm_small_m<WW, GROUPED>), grid, dim3(WW * 64), 0, st, x, ld_x, codes, scales,         \
-                       (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows_dense, offsets)
-    switch (W) {
-        case 1: NVFP4_SMALL(1); break;
-        case 2: NVFP4_SMALL(2); break;
-        case 4: NVFP4_SMALL(4); break;
-        case 8: NVFP4_SMALL(8); break;
-        default: NVFP4_SMALL(16); break;
+    const SmallShape s = small_m_shape(L, rows_dense, GROUPED);
+    const dim3 grid((unsigned)((L.NU + s.nt - 1) / s.nt), GROUPED ? (unsigned)L.E : 1u);
+#define NVFP4_SMALL(MG, NT) \
+    launch_small_w<MG, NT, GROUPED>(s.w, grid, L, x, ld_x, codes, scales, gs, g_div, y, ld_y, rows_dense, offsets, st)
+    if (GROUPED) {
+        NVFP4_SMALL(0, 1);
+    } else if (s.nt == 1) {
+        switch (s.mg) {
+            case 1: NVFP4_SMALL(1, 1); break;
+            case 2: NVFP4_SMALL(2, 1); break;
+            default: NVFP4_SMALL(16, 1); break;
+        }
+    } else {
+        switch (s.mg) {
+            case 2: NVFP4_SMALL(2, 2); break;
+            default: NVFP4_SMALL(16, 2); break;
+        }
     }
 #undef NVFP4_SMALL
     return launched("small-M GEMM");
@@ -93,7 +143,7 @@ nvfp4_status launch_large(const Layout& L, const uint16_t* x, int64_t ld_x, cons
     const int64_t mtiles = GROUPED ? (rows + kLargeBM - 1) / kLargeBM + L.E : (rows + kLargeBM - 1) / kLargeBM;
     if (mtiles > 65535) return fail(NVFP4_ERR_INVALID_ARG, "large-M GEMM: %lld row tiles exceed the grid limit", (long long)mtiles);
     const dim3 grid((unsigned)((L.NU + kLargeUnits - 1) / kLargeUnits), (unsigned)mtiles);
-    hipLaunchKernelGGL((k_gemm_large_m<GROUPED>), grid, dim3(256), 0, st, x, ld_x, codes, scales, (int)L.NU,
+    hipLaunchKernelGGL((k_gemm_large_m<GROUPED>), grid, dim3(256), 0, st, x, ld_x, make_view(L, codes), (int)L.NU,
                        (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, (int)L.E);
     return launched("large-M GEMM");
 }
@@ -194,7 +244,7 @@ nvfp4_status nvfp4_repack(const uint8_t* w_packed, int64_t ld_w, const uint8_t* 
     const int64_t lanes = L.blocks() * 64;
     uint8_t* o = static_cast<uint8_t*>(out);
     hipLaunchKernelGGL(k_repack, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       w_packed, ld_w, w_scale, ld_s, N, K, L.NU, L.KC, lanes, o, o + L.code_bytes());
+                       w_packed, ld_w, w_scale, ld_s, N, K, L.NU, L.KC, lanes, make_view(L, o), o, o + L.code_bytes());
     return launched(fn);
 }
 
@@ -209,8 +259,8 @@ nvfp4_status nvfp4_dequant_bf16(const void* w_repacked, int64_t E, int64_t N, in
     const Layout L = make_layout(E, N, K);
     const int64_t lanes = L.blocks() * 64;
     const uint8_t* b = static_cast<const uint8_t*>(w_repacked);
-    hipLaunchKernelGGL(k_dequant, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, static_cast<hipStream_t>(stream), b,
-                       b + L.code_bytes(), N, K, L.NU, L.KC, lanes, static_cast<uint16_t*>(out), ld_out);
+    hipLaunchKernelGGL(k_dequant, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       make_view(L, b), N, K, L.NU, L.KC, lanes, static_cast<uint16_t*>(out), ld_out);
     return launched(fn);
 }
 
