@@ -98,14 +98,12 @@ def make_dense(name, M, N, K, *, seed, scales="pow2_mant", g_stored=1.0 / 2688.0
     del w, s
     blobs = [blob] + [blob.clone() for _ in range(copies - 1)]
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    ws = None
-    if pre is not None:
-        ws = torch.empty(max(nv.lib().nvfp4_w4a16_gemm_workspace_bytes(M, N, K), 1), dtype=torch.uint8, device=dev)
+    ws = nv.workspace(nv.gemm_workspace_bytes(M, N, K), dev)
 
     def launch(i):
-        nv.gemm(x, blobs[i % copies], N, K, g, divisor, pre, out=y, workspace=ws)
+        nv.gemm(x, blobs[i % copies], N, K, g, divisor, pre, out=y, workspace_buf=ws)
 
-    kernel = "k_gemm_small_m" if M <= 16 else "k_gemm_large_m"
+    kernel = "k_gemm_small_m" if M <= 8 else "k_gemm_tile"
     flops = 2.0 * M * N * K
     ab = dense_bytes(M, N, K, pre is not None)
     bound = "hbm" if flops / ab < (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) else "mfma"
@@ -139,13 +137,14 @@ def make_grouped(name, T, fc, *, seed=1004, copies=1, E=128, topk=8):
     del w, s
     blobs = [blob] + [blob.clone() for _ in range(copies - 1)]
     y = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
+    ws = nv.workspace(nv.lib().nvfp4_w4a16_grouped_gemm_workspace_bytes(R, E, N, K), dev)
 
     def launch(i):
-        nv.grouped_gemm(x, off, blobs[i % copies], E, N, K, gs, False, None, out=y)
+        nv.grouped_gemm(x, off, blobs[i % copies], E, N, K, gs, False, None, out=y, workspace_buf=ws)
 
     ab = active * 0.5625 * N * K + 2.0 * R * K + 2.0 * R * N + 4.0 * E + 4.0 * (E + 1)
     flops = 2.0 * R * N * K
-    kernel = "k_gemm_small_m" if R <= 16 * E else "k_gemm_large_m"
+    kernel = "k_gemm_small_m" if R <= 16 * E else "k_gemm_tile"
     bound = "hbm" if flops / ab < (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) else "mfma"
     meta = {"E": E, "topk": topk, "T": T, "R": R, "N": N, "K": K, "active_experts": active, "weight_copies": copies}
     wl = Workload(name, "grouped", kernel, ab, flops, launch, copies, meta, bound)

@@ -95,12 +95,19 @@ nvfp4_status nvfp4_repack(const uint8_t* w_packed, int64_t ld_w, const uint8_t* 
  *   global_scale: device pointer to one fp32
  *   y         : bf16 [M][ld_y] (2-byte aligned, ld_y >= N)
  *   workspace : device scratch of nvfp4_w4a16_gemm_workspace_bytes(M,N,K)
- *               bytes (may be NULL when that is 0)
+ *               bytes, 256-byte aligned (may be NULL when that is 0).  It
+ *               must be zero-filled before its first use; every call leaves
+ *               the part that has to be zero zeroed again, so one workspace
+ *               can serve any number of calls issued one after another.
+ *               Calls that may overlap in time (other streams) need their
+ *               own workspace.  The size covers either kernel variant, with
+ *               or without a pre-scale.
  * M == 0 returns NVFP4_OK without launching anything.
  * Errors: M < 0, N < 1, K < 16, K % 16 != 0, ld_x < K, ld_y < N, NULL
  * x / w_repacked / global_scale / y (x may be NULL when M == 0) ->
- * INVALID_ARG; misaligned x, pre_scale, w_repacked or y, or ld_x % 8 != 0
- * -> ALIGNMENT; workspace too small -> BUFFER_TOO_SMALL. */
+ * INVALID_ARG; misaligned x, pre_scale, w_repacked, y or workspace, or
+ * ld_x % 8 != 0 -> ALIGNMENT; workspace smaller than this call needs ->
+ * BUFFER_TOO_SMALL. */
 int64_t nvfp4_w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 nvfp4_status nvfp4_w4a16_gemm(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
                               const float* global_scale, int global_scale_is_divisor,
@@ -121,6 +128,7 @@ nvfp4_status nvfp4_w4a16_gemm(const void* x, int64_t ld_x, const void* pre_scale
  *   w_repacked    : output of nvfp4_repack with this E, N, K
  *   global_scales : device fp32 [E]
  *   y             : bf16 [R][ld_y]
+ *   workspace     : as for the dense form, nvfp4_w4a16_grouped_gemm_workspace_bytes bytes
  * R == 0 returns NVFP4_OK without launching anything.
  * Errors as for the dense form, plus E < 1 -> INVALID_ARG. */
 int64_t nvfp4_w4a16_grouped_gemm_workspace_bytes(int64_t R, int64_t E, int64_t N, int64_t K);

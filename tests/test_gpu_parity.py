@@ -129,6 +129,10 @@ DENSE_FULL = [
     ("ragged_33x1000x1040", lambda: synth.ragged_case()),
     ("ragged_M13", lambda: synth.dense_case(13, 1000, 1040, 1003, g_stored=2688.0, g_is_divisor=True, prescale=True)),
     ("mid_300x700x2048", lambda: synth.dense_case(300, 700, 2048, 77, scales="log_uniform", g_stored=1 / 2688)),
+    # split-K across workgroups with a ragged N tail / 2-tile rows / ragged last K chunk
+    ("split_M24_N2000_K4096", lambda: synth.dense_case(24, 2000, 4096, 1005)),
+    ("split_M48_N1000_K2176_pre", lambda: synth.dense_case(48, 1000, 2176, 1006, prescale=True)),
+    ("split_M16_N4000_K2064", lambda: synth.dense_case(16, 4000, 2064, 1007, scales="log_uniform")),
     ("decode_M1", lambda: synth.decode_case(1)),
     ("decode_M8", lambda: synth.decode_case(8)),
     ("decode_M16", lambda: synth.decode_case(16)),

@@ -21,6 +21,7 @@ import os
 import torch
 
 __all__ = ["repack", "repack_bytes", "gemm", "gemm_variant", "grouped_gemm", "dequant", "lib", "Nvfp4Error",
+           "workspace", "gemm_workspace_bytes",
            "VARIANT_AUTO", "VARIANT_SMALL_M", "VARIANT_LARGE_M", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4_w4a16.so")
@@ -145,28 +146,38 @@ def _gemm_args(x, blob, N, K, global_scale, pre_scale, out, rows_name="M"):
     return M, out
 
 
-def gemm(x, blob, N, K, global_scale, divisor=False, pre_scale=None, out=None, workspace=None):
-    """Y[M, N] = g * (x (.) pre_scale) . dequant(W)^T in bf16 (dense linear / LM head)."""
-    return gemm_variant(x, blob, N, K, global_scale, divisor, pre_scale, out, workspace, VARIANT_AUTO)
+def gemm(x, blob, N, K, global_scale, divisor=False, pre_scale=None, out=None, workspace_buf=None):
+    """Y[M, N] = g * (x (.) pre_scale) . dequant(W)^T in bf16 (dense linear / LM head).  workspace_buf: an optional
+    buffer from ``workspace(gemm_workspace_bytes(M, N, K), device)``, reusable across calls on one stream."""
+    return gemm_variant(x, blob, N, K, global_scale, divisor, pre_scale, out, workspace_buf, VARIANT_AUTO)
 
 
-def gemm_variant(x, blob, N, K, global_scale, divisor=False, pre_scale=None, out=None, workspace=None,
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A workspace for the GEMM calls: zero-filled once (the split-K counters in it must start at zero; every call
+    leaves them zero again, so the buffer can be reused by later calls on the same stream)."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().nvfp4_w4a16_gemm_workspace_bytes(M, N, K))
+
+
+def gemm_variant(x, blob, N, K, global_scale, divisor=False, pre_scale=None, out=None, workspace_buf=None,
                  variant=VARIANT_AUTO):
     M, out = _gemm_args(x, blob, N, K, global_scale, pre_scale, out)
-    wsb = 0
-    if pre_scale is not None:
-        need = lib().nvfp4_w4a16_gemm_workspace_bytes(M, N, K)
-        if workspace is None:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-        wsb = workspace.numel()
+    need = gemm_workspace_bytes(M, N, K)
+    if need < 0:
+        raise ValueError(f"invalid GEMM shape M={M} N={N} K={K}")
+    if workspace_buf is None:
+        workspace_buf = workspace(need, x.device)
     _check(lib().nvfp4_w4a16_gemm_variant(_ptr(x), x.stride(0), _ptr(pre_scale), _ptr(blob), _ptr(global_scale),
-                                          int(bool(divisor)), _ptr(out), out.stride(0), M, N, K, _ptr(workspace),
-                                          wsb, int(variant), _stream(x.device)))
+                                          int(bool(divisor)), _ptr(out), out.stride(0), M, N, K, _ptr(workspace_buf),
+                                          workspace_buf.numel(), int(variant), _stream(x.device)))
     return out
 
 
 def grouped_gemm(x, expert_offsets, blob, E, N, K, global_scales, divisor=False, pre_scale=None, out=None,
-                 workspace=None):
+                 workspace_buf=None):
     """Grouped (MoE) form: rows [offsets[e], offsets[e+1]) of x use expert e.  Rows owned by no expert are left
     untouched in ``out`` (a fresh ``out`` is zero-filled)."""
     _dev("expert_offsets", expert_offsets, torch.int32, 1)
@@ -177,13 +188,12 @@ def grouped_gemm(x, expert_offsets, blob, E, N, K, global_scales, divisor=False,
     if out is None:
         out = torch.zeros((x.shape[0], N), dtype=torch.bfloat16, device=x.device)
     R, out = _gemm_args(x, blob, N, K, global_scales, pre_scale, out)
-    wsb = 0
-    if pre_scale is not None:
-        need = lib().nvfp4_w4a16_grouped_gemm_workspace_bytes(R, E, N, K)
-        if workspace is None:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-        wsb = workspace.numel()
+    need = int(lib().nvfp4_w4a16_grouped_gemm_workspace_bytes(R, E, N, K))
+    if need < 0:
+        raise ValueError(f"invalid grouped GEMM shape R={R} E={E} N={N} K={K}")
+    if workspace_buf is None:
+        workspace_buf = workspace(need, x.device)
     _check(lib().nvfp4_w4a16_grouped_gemm(_ptr(x), x.stride(0), _ptr(expert_offsets), _ptr(pre_scale), _ptr(blob),
                                           _ptr(global_scales), int(bool(divisor)), _ptr(out), out.stride(0), R, E,
-                                          N, K, _ptr(workspace), wsb, _stream(x.device)))
+                                          N, K, _ptr(workspace_buf), workspace_buf.numel(), _stream(x.device)))
     return out

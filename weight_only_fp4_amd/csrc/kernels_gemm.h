@@ -3,9 +3,10 @@
 //   Y[m,n] = RNE_bf16(g * sum_k X'[m,k] * e2m1(code(n,k)) * e4m3(S[n,k/16]))
 //
 // X' is the activation (already multiplied by the pre-quant scale when one
-// is given).  Two kernels, chosen by the number of rows:
+// is given).  This file holds the small-M kernel, used for up to 8 rows
+// (the host planner's choice; a pass covers up to 16 rows):
 //
-// small-M (rows <= 16 per pass; HBM-bound): one workgroup per 16-row unit
+// small-M (HBM-bound): one workgroup per 16-row unit
 //   of W, its W waves splitting K.  Each wave streams its K range of the
 //   unit with one 128-bit load per lane per 128-wide chunk and contracts it
 //   with v_mfma_f32_4x4x4bf16_1k in the 16-block form: block b of the
@@ -20,21 +21,9 @@
 //   every lane loads one distinct 16-byte piece per four rows.  Partial sums are reduced across K
 //   groups with lane shuffles and across waves through LDS in a fixed order.
 //
-// large-M (MFMA-bound): 128 x 256 output tile per workgroup of four waves.
-//   The activation tile (128 rows x 128 k) is staged through LDS with double
-//   buffering; each wave owns 64 output columns, decodes its weight
-//   fragments straight into registers (exact bf16) and runs
-//   v_mfma_f32_16x16x32_bf16 over 8 x 4 sub-tiles with fp32 accumulators.
-//   The 32 K slots of one MFMA step map to k = 32 g + 8 t + e for lane group
-//   g, step t, element e, on both operands, so the weight lanes read whole
-//   32-wide K groups from the repacked layout.
-//
-// Both kernels exist in a dense and a grouped (MoE) form.  The grouped form
-// reads expert_offsets on the device: the small-M grid has one slice per
-// expert and slices of experts without rows exit at once; the large-M grid
-// has an upper bound of (R / 128 + E) row tiles, mapped to (expert, tile) by
-// a wave-wide prefix scan of the per-expert tile counts, extra tiles exit.
-// Experts without rows therefore read no weight bytes.
+// Rows above 8 go to the tile kernel (kernels_tile.h).  The small-M grouped
+// form reads expert_offsets on the device: one grid slice per expert, and
+// slices of experts without rows exit at once, so they read no weight bytes.
 #pragma once
 #include "decode.h"
 #include "layout.h"
@@ -42,9 +31,6 @@
 namespace nvfp4 {
 
 constexpr int kSmallRows = 16;      // rows per pass of the small-M kernel
-constexpr int kLargeBM = 128;       // rows per tile of the large-M kernel
-constexpr int kLargeUnits = 16;     // 16-row units of W per large-M tile (256 columns)
-constexpr int kLargeLDA = 136;      // bf16 per LDS row of the activation tile (128 + 8 pad)
 constexpr int kMaxExperts = 4096;
 
 // ----------------------------------------------------------------- small-M --
@@ -362,167 +348,6 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
         }
         __syncthreads();
     }
-}
-
-// ----------------------------------------------------------------- large-M --
-
-template <bool GROUPED>
-__global__ void __launch_bounds__(256, 1) k_gemm_large_m(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
-                                                         int NU, int KC, int K,
-                                                         int N, const float* __restrict__ gscale, int g_is_div,
-                                                         uint16_t* __restrict__ y, int64_t ld_y, int64_t rows_dense,
-                                                         const int32_t* __restrict__ offsets, int E) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][kLargeBM * kLargeLDA];
-    __shared__ int s_map[2];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4;
-
-    int e = 0;
-    int64_t row0, rows;
-    if (GROUPED) {
-        if (tid == 0) s_map[0] = -1;
-        __syncthreads();
-        if (w == 0) {
-            const int by = (int)blockIdx.y;
-            int carry = 0;
-            for (int base = 0; base < E; base += 64) {
-                const int ex = base + lane;
-                const int cnt = ex < E ? (offsets[ex + 1] - offsets[ex]) : 0;
-                const int tiles = (cnt + kLargeBM - 1) / kLargeBM;
-                int v = tiles;
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const int t = __shfl_up(v, d);
-                    if (lane >= d) v += t;
-                }
-                const int incl = carry + v, excl = incl - tiles;
-                if (tiles > 0 && by >= excl && by < incl) {
-                    s_map[0] = ex;
-                    s_map[1] = by - excl;
-                }
-                carry += __shfl(v, 63);
-            }
-        }
-        __syncthreads();
-        e = s_map[0];
-        if (e < 0) return;   // uniform: a slot past the last active tile
-        row0 = (int64_t)offsets[e] + (int64_t)s_map[1] * kLargeBM;
-        rows = (int64_t)offsets[e + 1] - row0;
-    } else {
-        row0 = (int64_t)blockIdx.y * kLargeBM;
-        rows = rows_dense - row0;
-    }
-    if (rows > kLargeBM) rows = kLargeBM;
-
-    // This wave's four 16-row units of W (64 output columns).
-    const int u_base = (int)blockIdx.x * kLargeUnits + w * 4;
-    const uint8_t* cpj[4];
-    const uint8_t* spj[4];
-    const int64_t cstr = bv.chunk_stride * kCodeBlock;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t blk = bv.block(e, (u_base + j) < NU ? u_base + j : 0, 0);
-        cpj[j] = bv.codes + blk * kCodeBlock + lane * 16;
-        spj[j] = bv.scales + blk * kScaleBlock + lane * 2;
-    }
-
-    // Activation tile loader: 128 rows x 16 pieces of 8 bf16; thread -> 8 pieces.
-    const int a_piece = tid & 15, a_row0 = tid >> 4;
-    const uint16_t* xbase = x + row0 * ld_x;
-    uint4 areg[8];
-    // Unconditional loads from clamped addresses, masked afterwards (no
-    // lane-divergent branches around loads; see small_m_pass).
-    // Rows past `rows` read row 0 (their outputs are never stored); pieces
-    // past K are zeroed when written to LDS, not at load time.
-    auto load_a = [&](int c) {
-        const int k = c * kChunkK + a_piece * 8;
-        const int kk = k < K ? k : 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = a_row0 + 16 * i;
-            areg[i] = *reinterpret_cast<const uint4*>(xbase + (int64_t)(r < rows ? r : 0) * ld_x + kk);
-        }
-    };
-    auto store_a = [&](int buf, int c) {
-        const bool kin = c * kChunkK + a_piece * 8 < K;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint4 v = areg[i];
-            *reinterpret_cast<uint4*>(&As[buf][(a_row0 + 16 * i) * kLargeLDA + a_piece * 8]) =
-                make_uint4(kin ? v.x : 0u, kin ? v.y : 0u, kin ? v.z : 0u, kin ? v.w : 0u);
-        }
-    };
-    uint4 bc[4], bc_n[4];
-    uint32_t bs[4], bs_n[4];
-    // Units past NU read unit 0 (their columns are never stored).
-    auto load_b = [&](int c) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            bc_n[j] = load_stream_u4(cpj[j] + (int64_t)c * cstr);
-            bs_n[j] = load_stream_u16(spj[j] + (((int64_t)c * cstr) >> 3));
-        }
-    };
-
-    f32x4 acc[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    load_a(0);
-    load_b(0);
-    store_a(0, 0);
-    __syncthreads();
-
-    for (int c = 0; c < KC; ++c) {
-        const int buf = c & 1;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            bc[j] = bc_n[j];
-            bs[j] = bs_n[j];
-        }
-        const bool more = (c + 1) < KC;
-        if (more) {
-            load_a(c + 1);
-            load_b(c + 1);
-        }
-        float slo[4], shi[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            slo[j] = e4m3_to_f32(bs[j] & 0xFFu);
-            shi[j] = e4m3_to_f32(bs[j] >> 8);
-        }
-        const uint16_t* abase = &As[buf][(lane & 15) * kLargeLDA + g * 32];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            bf16x8 bf[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t d = t == 0 ? bc[j].x : t == 1 ? bc[j].y : t == 2 ? bc[j].z : bc[j].w;
-                bf[j] = uint4_to_bf16x8(decode8_bf16(d, t < 2 ? slo[j] : shi[j]));
-            }
-#pragma unroll
-            for (int ms = 0; ms < 8; ++ms) {
-                const bf16x8 af = uint4_to_bf16x8(*reinterpret_cast<const uint4*>(abase + ms * 16 * kLargeLDA + t * 8));
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[ms][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[ms][j], 0, 0, 0);
-            }
-        }
-        if (more) store_a(buf ^ 1, c + 1);
-        __syncthreads();
-    }
-
-    const float gv = effective_global_scale(gscale[e], g_is_div);
-#pragma unroll
-    for (int ms = 0; ms < 8; ++ms)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t n = (int64_t)(u_base + j) * kUnitN + (lane & 15);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = ms * 16 + g * 4 + i;
-                if (m < rows && n < N) y[(row0 + m) * ld_y + n] = (uint16_t)f32_to_bf16_rne(gv * acc[ms][j][i]);
-            }
-        }
 }
 
 }  // namespace nvfp4

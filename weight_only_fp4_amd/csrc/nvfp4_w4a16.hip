@@ -12,6 +12,7 @@
 #include "../../include/nvfp4_w4a16.h"
 #include "kernels_aux.h"
 #include "kernels_gemm.h"
+#include "kernels_tile.h"
 
 using namespace nvfp4;
 
@@ -134,24 +135,107 @@ nvfp4_status launch_small(const Layout& L, const uint16_t* x, int64_t ld_x, cons
     return launched("small-M GEMM");
 }
 
-template <bool GROUPED>
-nvfp4_status launch_large(const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob, const float* gs,
-                          int g_div, uint16_t* y, int64_t ld_y, int64_t rows, const int32_t* offsets,
-                          hipStream_t st) {
-    const uint8_t* codes = blob;
-    const uint8_t* scales = blob + L.code_bytes();
-    const int64_t mtiles = GROUPED ? (rows + kLargeBM - 1) / kLargeBM + L.E : (rows + kLargeBM - 1) / kLargeBM;
-    if (mtiles > 65535) return fail(NVFP4_ERR_INVALID_ARG, "large-M GEMM: %lld row tiles exceed the grid limit", (long long)mtiles);
-    const dim3 grid((unsigned)((L.NU + kLargeUnits - 1) / kLargeUnits), (unsigned)mtiles);
-    hipLaunchKernelGGL((k_gemm_large_m<GROUPED>), grid, dim3(256), 0, st, x, ld_x, make_view(L, codes), (int)L.NU,
-                       (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, (int)L.E);
-    return launched("large-M GEMM");
+// ------------------------------------------------------------- tile path --
+// Tile shapes by row count, from launch-shape sweeps on MI355X.  K is split
+// across workgroups (grid z) while the tile count stays below the shape's
+// target and each split keeps >= 8 chunks.  The choice is a pure function of
+// (rows, N, K), so the workspace query reproduces it.
+struct TileShape {
+    int ms, nt, w, d, S;
+    int64_t groups, mtiles;
+    int64_t tiles() const { return groups * mtiles; }
+    int bm() const { return 16 * ms; }
+    int ug() const { return nt * w; }
+};
+
+TileShape tile_shape(const Layout& L, int64_t rows, bool grouped) {
+    TileShape t;
+    int64_t target;   // workgroups the split may grow to
+    if (grouped) {
+        t.ms = 4; t.nt = 4; t.w = 4; t.d = 2; target = 0;
+    } else if (rows <= 16) {
+        t.ms = 1; t.nt = 1; t.w = 4; t.d = 4; target = 1024;
+    } else if (rows <= 32) {
+        t.ms = 2; t.nt = 2; t.w = 4; t.d = 4; target = 256;
+    } else if (rows <= 64) {
+        t.ms = 4; t.nt = 2; t.w = 8; t.d = 2; target = 256;
+        if ((L.NU + 15) / 16 < 256) { t.w = 4; t.d = 4; }
+    } else {
+        t.ms = 8; t.nt = 4; t.w = 4; t.d = 2; target = 0;
+    }
+    t.groups = (L.NU + t.ug() - 1) / t.ug();
+    t.mtiles = (rows + t.bm() - 1) / t.bm() + (grouped ? L.E : 0);
+    t.S = 1;
+    while (t.S < 16 && t.tiles() * 2 * t.S <= target && L.KC >= 8 * (2 * t.S)) t.S *= 2;
+    return t;
 }
+
+// Byte offsets in the caller's workspace: split-K counters (must be zero
+// before the first call; every call leaves them zero), split-K partials, and
+// the pre-scaled activation.
+struct Workspace {
+    int64_t counters, partials, prescale, total;
+};
+
+Workspace workspace_layout(const TileShape* t, int64_t rows, int64_t K, bool pre) {
+    Workspace w{0, 0, 0, 0};
+    int64_t off = 0;
+    if (t && t->S > 1) {
+        w.counters = off;
+        off += round_up(t->tiles() * 4, 256);
+        w.partials = off;
+        off += round_up((int64_t)t->S * t->tiles() * t->bm() * t->ug() * 16 * 4, 256);
+    }
+    if (pre) {
+        w.prescale = off;
+        off += prescale_bytes(rows, K);
+    }
+    w.total = off;
+    return w;
+}
+
+template <int MS, int NT, int W, int D, bool GROUPED>
+void launch_tile_t(const TileShape& t, const Layout& L, const uint16_t* x, int64_t ld_x, BlobView bv, const float* gs,
+                   int g_div, uint16_t* y, int64_t ld_y, int64_t rows, const int32_t* offsets, SplitK sk,
+                   hipStream_t st) {
+    const dim3 grid((unsigned)t.groups, (unsigned)t.mtiles, (unsigned)t.S);
+    if (L.K % kChunkK == 0)
+        hipLaunchKernelGGL((k_gemm_tile<MS, NT, W, D, GROUPED, true>), grid, dim3(W * 64), 0, st, x, ld_x, bv,
+                           (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, (int)L.E, sk);
+    else
+        hipLaunchKernelGGL((k_gemm_tile<MS, NT, W, D, GROUPED, false>), grid, dim3(W * 64), 0, st, x, ld_x, bv,
+                           (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, (int)L.E, sk);
+}
+
+template <bool GROUPED>
+nvfp4_status launch_tile(const TileShape& t, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
+                         const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows, const int32_t* offsets,
+                         uint8_t* ws, const Workspace& wl, hipStream_t st) {
+    if (t.mtiles > 65535) return fail(NVFP4_ERR_INVALID_ARG, "tile GEMM: %lld row tiles exceed the grid limit", (long long)t.mtiles);
+    SplitK sk{t.S, t.S > 1 ? reinterpret_cast<float*>(ws + wl.partials) : nullptr,
+              t.S > 1 ? reinterpret_cast<int*>(ws + wl.counters) : nullptr};
+    const BlobView bv = make_view(L, blob);
+#define NVFP4_TILE(MS, NT, W, D) launch_tile_t<MS, NT, W, D, GROUPED>(t, L, x, ld_x, bv, gs, g_div, y, ld_y, rows, offsets, sk, st)
+    if constexpr (GROUPED) {
+        NVFP4_TILE(4, 4, 4, 2);
+    } else {
+        if (t.ms == 1) NVFP4_TILE(1, 1, 4, 4);
+        else if (t.ms == 2) NVFP4_TILE(2, 2, 4, 4);
+        else if (t.ms == 4 && t.w == 8) NVFP4_TILE(4, 2, 8, 2);
+        else if (t.ms == 4) NVFP4_TILE(4, 2, 4, 4);
+        else NVFP4_TILE(8, 4, 4, 2);
+    }
+#undef NVFP4_TILE
+    return launched("tile GEMM");
+}
+
+// Rows at or below this use the small-M kernel when the variant is automatic.
+constexpr int64_t kSmallAuto = 8;
 
 // Shared checks of the activation / output / pre-scale / workspace arguments.
 nvfp4_status check_gemm_io(const char* fn, const void* x, int64_t ld_x, const void* pre, const void* w,
                            const void* gs, const void* y, int64_t ld_y, int64_t rows, int64_t N, int64_t K,
-                           const void* ws, int64_t ws_bytes) {
+                           const void* ws, int64_t ws_bytes, int64_t ws_need) {
     if (rows < 0) return fail(NVFP4_ERR_INVALID_ARG, "%s: row count %lld is negative", fn, (long long)rows);
     if (ld_x < K) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_x = %lld < K = %lld", fn, (long long)ld_x, (long long)K);
     if (ld_y < N) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_y = %lld < N = %lld", fn, (long long)ld_y, (long long)N);
@@ -164,12 +248,11 @@ nvfp4_status check_gemm_io(const char* fn, const void* x, int64_t ld_x, const vo
     if (pre && !aligned(pre, 16)) return fail(NVFP4_ERR_ALIGNMENT, "%s: pre_scale must be 16-byte aligned", fn);
     if (!aligned(w, 16)) return fail(NVFP4_ERR_ALIGNMENT, "%s: w_repacked must be 16-byte aligned", fn);
     if (!aligned(y, 2)) return fail(NVFP4_ERR_ALIGNMENT, "%s: y must be 2-byte aligned", fn);
-    if (pre) {
-        const int64_t need = prescale_bytes(rows, K);
-        if (ws_bytes < need || (need > 0 && !ws))
-            return fail(NVFP4_ERR_BUFFER_TOO_SMALL, "%s: workspace of %lld bytes is below the %lld bytes a pre_scale needs", fn,
-                        (long long)ws_bytes, (long long)need);
-        if (!aligned(ws, 16)) return fail(NVFP4_ERR_ALIGNMENT, "%s: workspace must be 16-byte aligned", fn);
+    if (rows > 0 && ws_need > 0) {
+        if (ws_bytes < ws_need || !ws)
+            return fail(NVFP4_ERR_BUFFER_TOO_SMALL, "%s: workspace of %lld bytes is below the %lld bytes this call needs", fn,
+                        (long long)ws_bytes, (long long)ws_need);
+        if (!aligned(ws, 256)) return fail(NVFP4_ERR_ALIGNMENT, "%s: workspace must be 256-byte aligned", fn);
     }
     return NVFP4_OK;
 }
@@ -191,29 +274,38 @@ nvfp4_status apply_prescale(const void* x, int64_t& ld_x, const void* pre, int64
     return NVFP4_OK;
 }
 
+// Workspace bytes of a dense call: enough for either kernel, with or without a pre-scale.
+int64_t dense_workspace_bytes(const Layout& L, int64_t M) {
+    const TileShape t = tile_shape(L, M, false);
+    return workspace_layout(&t, M, L.K, true).total;
+}
+
 nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void* w, const float* gs, int g_div,
                         void* y, int64_t ld_y, int64_t M, int64_t N, int64_t K, void* ws, int64_t ws_bytes,
                         int variant, void* stream) {
     const char* fn = "nvfp4_w4a16_gemm";
     nvfp4_status s = check_weight_shape(fn, 1, N, K);
     if (s != NVFP4_OK) return s;
-    s = check_gemm_io(fn, x, ld_x, pre, w, gs, y, ld_y, M, N, K, ws, ws_bytes);
-    if (s != NVFP4_OK) return s;
     if (variant < kAuto || variant > kLarge) return fail(NVFP4_ERR_INVALID_ARG, "%s: unknown variant %d", fn, variant);
     if (variant == kSmall && M > kSmallRows)
         return fail(NVFP4_ERR_INVALID_ARG, "%s: the small-M variant takes M <= %d (M = %lld)", fn, kSmallRows, (long long)M);
-    if (M == 0) return ok();   // zero rows: nothing is launched
-    if (M * (K / 8) > (int64_t)0xFFFFFFFF * 256) return fail(NVFP4_ERR_INVALID_ARG, "%s: M * K too large", fn);
+    if (M > (int64_t)1 << 31) return fail(NVFP4_ERR_INVALID_ARG, "%s: M = %lld too large", fn, (long long)M);
     const Layout L = make_layout(1, N, K);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const uint16_t* xp;
-    s = apply_prescale(x, ld_x, pre, M, K, ws, xp, st);
+    const bool small = variant == kSmall || (variant == kAuto && M <= kSmallAuto);
+    const TileShape t = tile_shape(L, M, false);
+    const Workspace wl = workspace_layout(small ? nullptr : &t, M, K, pre != nullptr);
+    s = check_gemm_io(fn, x, ld_x, pre, w, gs, y, ld_y, M, N, K, ws, ws_bytes, wl.total);
     if (s != NVFP4_OK) return s;
-    const bool small = variant == kSmall || (variant == kAuto && M <= kSmallRows);
+    if (M == 0) return ok();   // zero rows: nothing is launched
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    const uint16_t* xp;
+    s = apply_prescale(x, ld_x, pre, M, K, pre ? wsb + wl.prescale : nullptr, xp, st);
+    if (s != NVFP4_OK) return s;
     const uint8_t* blob = static_cast<const uint8_t*>(w);
     uint16_t* yo = static_cast<uint16_t*>(y);
     return small ? launch_small<false>(L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, st)
-                 : launch_large<false>(L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, st);
+                 : launch_tile<false>(t, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, wsb, wl, st);
 }
 
 }  // namespace
@@ -266,7 +358,7 @@ nvfp4_status nvfp4_dequant_bf16(const void* w_repacked, int64_t E, int64_t N, in
 
 int64_t nvfp4_w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || check_weight_shape("nvfp4_w4a16_gemm_workspace_bytes", 1, N, K) != NVFP4_OK) return -1;
-    return prescale_bytes(M, K);
+    return dense_workspace_bytes(make_layout(1, N, K), M);
 }
 
 nvfp4_status nvfp4_w4a16_gemm(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
@@ -287,7 +379,7 @@ nvfp4_status nvfp4_w4a16_gemm_variant(const void* x, int64_t ld_x, const void* p
 
 int64_t nvfp4_w4a16_grouped_gemm_workspace_bytes(int64_t R, int64_t E, int64_t N, int64_t K) {
     if (R < 0 || check_weight_shape("nvfp4_w4a16_grouped_gemm_workspace_bytes", E, N, K) != NVFP4_OK) return -1;
-    return prescale_bytes(R, K);
+    return workspace_layout(nullptr, R, K, true).total;
 }
 
 nvfp4_status nvfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t* expert_offsets, const void* pre_scale,
@@ -297,7 +389,9 @@ nvfp4_status nvfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t
     const char* fn = "nvfp4_w4a16_grouped_gemm";
     nvfp4_status s = check_weight_shape(fn, E, N, K);
     if (s != NVFP4_OK) return s;
-    s = check_gemm_io(fn, x, ld_x, pre_scale, w_repacked, global_scales, y, ld_y, R, N, K, workspace, workspace_bytes);
+    const Workspace wl = workspace_layout(nullptr, R, K, pre_scale != nullptr);
+    s = check_gemm_io(fn, x, ld_x, pre_scale, w_repacked, global_scales, y, ld_y, R, N, K, workspace, workspace_bytes,
+                      wl.total);
     if (s != NVFP4_OK) return s;
     if (!expert_offsets) return fail(NVFP4_ERR_INVALID_ARG, "%s: expert_offsets is NULL", fn);
     if (!aligned(expert_offsets, 4)) return fail(NVFP4_ERR_ALIGNMENT, "%s: expert_offsets must be 4-byte aligned", fn);
@@ -305,8 +399,9 @@ nvfp4_status nvfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t
     if (R == 0) return ok();   // zero rows: nothing is launched
     const Layout L = make_layout(E, N, K);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* wsb = static_cast<uint8_t*>(workspace);
     const uint16_t* xp;
-    s = apply_prescale(x, ld_x, pre_scale, R, K, workspace, xp, st);
+    s = apply_prescale(x, ld_x, pre_scale, R, K, pre_scale ? wsb + wl.prescale : nullptr, xp, st);
     if (s != NVFP4_OK) return s;
     const uint8_t* blob = static_cast<const uint8_t*>(w_repacked);
     uint16_t* yo = static_cast<uint16_t*>(y);
@@ -314,7 +409,8 @@ nvfp4_status nvfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t
     // Few rows per expert on average: the weight stream dominates, use the small-M kernel (passes of 16 rows).
     if (R <= (int64_t)kSmallRows * E)
         return launch_small<true>(L, xp, ld_x, blob, global_scales, g_div, yo, ld_y, 0, expert_offsets, st);
-    return launch_large<true>(L, xp, ld_x, blob, global_scales, g_div, yo, ld_y, R, expert_offsets, st);
+    const TileShape t = tile_shape(L, R, true);
+    return launch_tile<true>(t, L, xp, ld_x, blob, global_scales, g_div, yo, ld_y, R, expert_offsets, wsb, wl, st);
 }
 
 }  // extern "C"
