@@ -103,7 +103,7 @@ def make_dense(name, M, N, K, *, seed, scales="pow2_mant", g_stored=1.0 / 2688.0
     def launch(i):
         nv.gemm(x, blobs[i % copies], N, K, g, divisor, pre, out=y, workspace_buf=ws)
 
-    kernel = "k_gemm_small_m" if M <= 8 else "k_gemm_tile"
+    kernel = "k_gemm_small_m" if M <= 4 else "k_gemm_tile"
     flops = 2.0 * M * N * K
     ab = dense_bytes(M, N, K, pre is not None)
     bound = "hbm" if flops / ab < (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) else "mfma"

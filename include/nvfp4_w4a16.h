@@ -89,7 +89,7 @@ nvfp4_status nvfp4_repack(const uint8_t* w_packed, int64_t ld_w, const uint8_t* 
  * (the inversion happens at use, in the epilogue; *global_scale is never
  * rewritten).  Accumulation is fp32; the summation order is fixed, so
  * results are bitwise reproducible run to run.
- *   x         : bf16 [M][ld_x] (16-byte aligned, ld_x >= K, ld_x % 8 == 0)
+ *   x         : bf16 [M][ld_x] (16-byte aligned, K <= ld_x <= 2^23, ld_x % 8 == 0)
  *   pre_scale : bf16 [K] (16-byte aligned) or NULL
  *   w_repacked: output of nvfp4_repack with E = 1 and the same N, K
  *   global_scale: device pointer to one fp32
@@ -103,7 +103,7 @@ nvfp4_status nvfp4_repack(const uint8_t* w_packed, int64_t ld_w, const uint8_t* 
  *               own workspace.  The size covers either kernel variant, with
  *               or without a pre-scale.
  * M == 0 returns NVFP4_OK without launching anything.
- * Errors: M < 0, N < 1, K < 16, K % 16 != 0, ld_x < K, ld_y < N, NULL
+ * Errors: M < 0, N < 1, K < 16, K % 16 != 0, ld_x < K, ld_x > 2^23, ld_y < N, NULL
  * x / w_repacked / global_scale / y (x may be NULL when M == 0) ->
  * INVALID_ARG; misaligned x, pre_scale, w_repacked, y or workspace, or
  * ld_x % 8 != 0 -> ALIGNMENT; workspace smaller than this call needs ->
@@ -149,7 +149,7 @@ nvfp4_status nvfp4_dequant_bf16(const void* w_repacked, int64_t E, int64_t N, in
 /* Dense GEMM with the kernel variant forced instead of chosen from M:
  *   variant 0 = automatic (same as nvfp4_w4a16_gemm),
  *   variant 1 = small-M kernel (M <= 16 only; larger M -> INVALID_ARG),
- *   variant 2 = large-M kernel (any M).
+ *   variant 2 = tile kernel (any M).
  * Used to check that the variants agree on the same inputs. */
 nvfp4_status nvfp4_w4a16_gemm_variant(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
                                       const float* global_scale, int global_scale_is_divisor,

@@ -65,7 +65,8 @@ A = 1 << 20   # a fake, 16-byte-aligned address; never dereferenced (calls fail 
     (dict(ld_x=132), ALIGN, "ld_x"),
     (dict(y=A + 1), ALIGN, "y must be"),
     (dict(pre=A, ws=A, wsb=10), SMALL, "workspace"),
-    (dict(M=16, N=14336, K=4096, ld_x=4096, ld_y=14336, variant=2, ws=A + 16, wsb=1 << 30), ALIGN, "workspace"),
+    (dict(M=16, N=4096, K=14336, ld_x=14336, ld_y=4096, variant=2, ws=A + 16, wsb=1 << 30), ALIGN, "workspace"),
+    (dict(ld_x=(1 << 23) + 8), INVALID, "exceeds"),
     (dict(variant=1, M=17), INVALID, "small-M"),
     (dict(variant=7), INVALID, "variant"),
 ])
@@ -107,7 +108,7 @@ def test_workspace_queries():
     L = nv.lib()
     assert L.nvfp4_w4a16_gemm_workspace_bytes(33, 1000, 1040) >= 33 * 1040 * 2
     assert L.nvfp4_w4a16_gemm_workspace_bytes(0, 1000, 1040) >= 0
-    # decode shape M=16: K split across workgroups -> fp32 partials of 16 x 14336 per split, plus counters
-    assert L.nvfp4_w4a16_gemm_workspace_bytes(16, 14336, 4096) > 16 * 14336 * 4
+    # M=16, N=4096, K=14336: K split across workgroups -> fp32 partials of 16 x 4096 per split, plus counters
+    assert L.nvfp4_w4a16_gemm_workspace_bytes(16, 4096, 14336) > 2 * 16 * 4096 * 4
     assert L.nvfp4_w4a16_grouped_gemm_workspace_bytes(128, 128, 1536, 2048) >= 128 * 2048 * 2
     assert L.nvfp4_w4a16_gemm_workspace_bytes(-1, 10, 16) < 0

@@ -3,7 +3,7 @@
 //   Y[m,n] = RNE_bf16(g * sum_k X'[m,k] * e2m1(code(n,k)) * e4m3(S[n,k/16]))
 //
 // X' is the activation (already multiplied by the pre-quant scale when one
-// is given).  This file holds the small-M kernel, used for up to 8 rows
+// is given).  This file holds the small-M kernel, used for up to 4 rows
 // (the host planner's choice; a pass covers up to 16 rows):
 //
 // small-M (HBM-bound): one workgroup per 16-row unit
@@ -21,7 +21,7 @@
 //   every lane loads one distinct 16-byte piece per four rows.  Partial sums are reduced across K
 //   groups with lane shuffles and across waves through LDS in a fixed order.
 //
-// Rows above 8 go to the tile kernel (kernels_tile.h).  The small-M grouped
+// Rows above 4 go to the tile kernel (kernels_tile.h).  The small-M grouped
 // form reads expert_offsets on the device: one grid slice per expert, and
 // slices of experts without rows exit at once, so they read no weight bytes.
 #pragma once

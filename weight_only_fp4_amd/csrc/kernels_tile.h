@@ -1,20 +1,25 @@
-// Tile GEMM for rows > 8: a BM x (16 NT W) output tile per workgroup.
+// Tile GEMM for rows > 4: a BM x (16 NT UW) output tile per workgroup.
 //
-//   BM = 16 MS rows.  The activation chunk (BM rows x 128 k) is staged once
-//   per workgroup in a double-buffered LDS ring and shared by all W waves;
-//   its global loads ride in the same D-deep register ring as the weights,
-//   so no chunk waits on a load issued in its own iteration;
-//   wave w owns NT consecutive 16-row units of W, decodes their codes straight
-//   into exact bf16 v_mfma_f32_16x16x32_bf16 fragments and accumulates MS x NT
-//   16x16 sub-tiles in fp32.  The 32 K slots of an MFMA step map to
+//   BM = 16 MS rows.  The workgroup's UW x KW waves are UW unit-waves times
+//   KW k-parts: wave (uw, q) owns NT consecutive 16-row units of W and the
+//   q-th contiguous part of the workgroup's K range.  At every step the
+//   workgroup stages one activation chunk (BM rows x 128 k) per k-part in a
+//   double-buffered LDS ring, shared by the UW unit-waves of that part; the
+//   global loads of a step's activation pieces ride in the same D-deep
+//   register ring as the weight blocks, so no step waits on a load issued
+//   in its own iteration.  Each wave decodes its codes straight into exact
+//   bf16 v_mfma_f32_16x16x32_bf16 fragments and accumulates MS x NT 16x16
+//   sub-tiles in fp32.  The 32 K slots of an MFMA step map to
 //   k = 32 g + 8 t + e (lane group g, step t, element e) on both operands, so
 //   each weight lane reads a whole 32-wide K group of the repacked layout.
+//   The KW partial tiles are summed through LDS in part order 0..KW-1.
 //
-//   K may be split S ways across workgroups (grid z).  Each split writes its
-//   fp32 partial tile to the workspace, then bumps the tile's counter; the
-//   workgroup that arrives last adds the S partials in split order (0..S-1,
-//   independent of arrival order, so the result is bitwise reproducible),
-//   applies the epilogue and resets the counter to zero for the next call.
+//   K may also be split S ways across workgroups (grid z).  Each split
+//   writes its fp32 partial tile to the workspace, then bumps the tile's
+//   counter; the workgroup that arrives last adds the S partials in split
+//   order (0..S-1, independent of arrival order, so the result is bitwise
+//   reproducible), applies the epilogue and resets the counter to zero for
+//   the next call.
 //
 //   Grouped (MoE) form: grid y has R/BM + E row-tile slots, mapped to
 //   (expert, tile) by a wave-wide prefix scan of the per-expert tile counts
@@ -34,23 +39,29 @@ struct SplitK {
     int* counters;      // [row tiles][unit groups], zero between calls
 };
 
-template <int MS, int NT, int W, int D, bool GROUPED, bool KFULL>
-__global__ void __launch_bounds__(W * 64) k_gemm_tile(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
-                                                      int NU, int KC, int K, int N,
-                                                      const float* __restrict__ gscale, int g_is_div,
-                                                      uint16_t* __restrict__ y, int64_t ld_y, int64_t rows_dense,
-                                                      const int32_t* __restrict__ offsets, int E, SplitK sk) {
+template <int MS, int NT, int UW, int KW, int D, bool GROUPED, bool KFULL>
+__global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
+                                                            int NU, int KC, int K, int N,
+                                                            const float* __restrict__ gscale, int g_is_div,
+                                                            uint16_t* __restrict__ y, int64_t ld_y, int64_t rows_dense,
+                                                            const int32_t* __restrict__ offsets, int E, SplitK sk) {
+    constexpr int W = UW * KW;                                     // waves per workgroup
     constexpr int BM = 16 * MS;
-    constexpr int UG = NT * W;                                     // units per workgroup
-    constexpr int APIECES = BM * 16;                               // 16-byte pieces per activation chunk
+    constexpr int UG = NT * UW;                                    // units per workgroup
+    constexpr int CPIECES = BM * 16;                               // 16-byte pieces per activation chunk
+    constexpr int APIECES = KW * CPIECES;                          // pieces per step
     constexpr int APT = (APIECES + W * 64 - 1) / (W * 64);         // pieces per thread
-    static_assert(D >= 2, "the ring stages chunk c + 1 from another slot while refilling chunk c's");
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kTileLDA];
+    constexpr int kStage = KW * BM * kTileLDA;                     // bf16 per stage buffer
+    constexpr int kRedTile = MS * NT * 256;                        // floats of one wave's partial tile
+    static_assert(D >= 2, "the ring stages step i + 1 from another slot while refilling step i's");
+    static_assert((KW - 1) * UW * kRedTile * 4 <= 2 * kStage * 2, "k-part reduction fits in the stage buffers");
+    __shared__ __attribute__((aligned(16))) uint16_t As[2 * kStage];
     __shared__ float2 lut[256];
     __shared__ int s_map[3];
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int uw = w % UW, q = w / UW;
 
     // ---- which rows: dense m-tile, or (expert, m-tile) of the grouped form
     int e = 0;
@@ -91,9 +102,13 @@ __global__ void __launch_bounds__(W * 64) k_gemm_tile(const uint16_t* __restrict
     if (rows > BM) rows = BM;
     build_scale_table(lut);
 
+    // ---- K ranges: split s of the workgroup (grid z), part q of the wave
     const int S = sk.S, s = (int)blockIdx.z;
-    const int c0 = (int)((int64_t)KC * s / S), c1 = (int)((int64_t)KC * (s + 1) / S);
-    const int u_w = (int)blockIdx.x * UG + w * NT;                 // this wave's first unit
+    const int C0 = (int)((int64_t)KC * s / S), span = (int)((int64_t)KC * (s + 1) / S) - C0;
+    auto part_begin = [&](int qq) { return C0 + span * qq / KW; };
+    const int c0 = part_begin(q), len = part_begin(q + 1) - c0;   // this wave's chunks [c0, c0 + len)
+    const int steps = (span + KW - 1) / KW;                          // the longest part
+    const int u_w = (int)blockIdx.x * UG + uw * NT;                 // this wave's first unit
     const int64_t cstr = bv.chunk_stride * kCodeBlock;
     const uint8_t* cb[NT];
     const uint8_t* sb[NT];
@@ -105,19 +120,36 @@ __global__ void __launch_bounds__(W * 64) k_gemm_tile(const uint16_t* __restrict
         sb[j] = bv.scales + blk * kScaleBlock;
     }
 
-    // ---- per-wave ring of D chunks: NT code blocks + scale pairs, and this
-    // thread's share of the activation chunk (staged to LDS one chunk ahead
-    // of its use, so its load is issued D - 1 chunks before it is needed).
-    // Activation piece p = thread + i * threads: row p >> 4, k piece p & 15.
+    // ---- this thread's activation pieces (fixed across steps): piece
+    // p = tid + i * threads is row (p % CPIECES) >> 4, k piece p & 15 of the
+    // chunk of part p / CPIECES.  Rows past `rows` read row 0 (outputs never
+    // stored); pieces past K are zeroed when staged.  Offsets within the
+    // row tile fit 32 bits (the host bounds ld_x).
+    const uint16_t* xtile = x + row0 * ld_x;
+    uint32_t a_xo[APT], a_off[APT];
+    int a_c0[APT], a_last[APT];
+#pragma unroll
+    for (int i = 0; i < APT; ++i) {
+        const int p = tid + i * W * 64;
+        const int qa = KW == 1 ? 0 : (p < APIECES ? p : 0) / CPIECES, within = p % CPIECES;
+        const int pr = within >> 4;
+        a_c0[i] = part_begin(qa);
+        const int la = part_begin(qa + 1) - a_c0[i];
+        a_last[i] = la > 0 ? la - 1 : 0;
+        a_xo[i] = (uint32_t)((pr < rows ? pr : 0) * ld_x);
+        a_off[i] = (uint32_t)(qa * BM * kTileLDA + pr * kTileLDA + (within & 15) * 8);
+    }
+
+    // ---- per-wave ring of D steps: NT code blocks + scale pairs of this
+    // wave's chunk, and this thread's activation pieces of the step
     struct Slot {
         uint4 cw[NT];
         uint32_t sw[NT];
         uint4 a[APT];
     };
-    const uint16_t* xbase = x + row0 * ld_x;
-    const int c_last = c1 - 1;
-    auto load_slot = [&](Slot& b, int c_req) {
-        const int c = c_req < c_last ? c_req : c_last;
+    const int w_last = len > 0 ? len - 1 : 0;
+    auto load_slot = [&](Slot& b, int step) {
+        const int c = c0 + (step < w_last ? step : w_last);
         const int64_t boff = (int64_t)c * cstr;
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
@@ -126,22 +158,20 @@ __global__ void __launch_bounds__(W * 64) k_gemm_tile(const uint16_t* __restrict
         }
 #pragma unroll
         for (int i = 0; i < APT; ++i) {
-            const int p = tid + i * W * 64;
-            const int pr = (p >> 4) < BM ? (p >> 4) : 0, pk = p & 15;
-            const int k = c * kChunkK + pk * 8;
-            // rows past `rows` read row 0 (outputs never stored); pieces past K are zeroed at store
-            b.a[i] = *reinterpret_cast<const uint4*>(xbase + (int64_t)(pr < rows ? pr : 0) * ld_x + (k < K ? k : 0));
+            const int ca = a_c0[i] + (step < a_last[i] ? step : a_last[i]);
+            const int k = ca * kChunkK + (int)((tid + i * W * 64) & 15) * 8;
+            b.a[i] = *reinterpret_cast<const uint4*>(xtile + a_xo[i] + (uint32_t)(KFULL || k < K ? k : 0));
         }
     };
-    auto store_a = [&](int buf, const Slot& b, int c) {
+    auto store_a = [&](int buf, const Slot& b, int step) {
 #pragma unroll
         for (int i = 0; i < APT; ++i) {
             const int p = tid + i * W * 64;
             if (APIECES % (W * 64) != 0 && p >= APIECES) break;
-            const int pr = p >> 4, pk = p & 15;
-            const bool kin = KFULL || (c * kChunkK + pk * 8 < K);
+            const int ca = a_c0[i] + (step < a_last[i] ? step : a_last[i]);
+            const bool kin = KFULL || (ca * kChunkK + (p & 15) * 8 < K);
             const uint4 v = b.a[i];
-            *reinterpret_cast<uint4*>(&As[buf][pr * kTileLDA + pk * 8]) =
+            *reinterpret_cast<uint4*>(&As[buf * kStage + a_off[i]]) =
                 make_uint4(kin ? v.x : 0u, kin ? v.y : 0u, kin ? v.z : 0u, kin ? v.w : 0u);
         }
     };
@@ -153,7 +183,7 @@ __global__ void __launch_bounds__(W * 64) k_gemm_tile(const uint16_t* __restrict
         for (int j = 0; j < NT; ++j) acc[ms][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](const Slot& b, int buf) {
-        const uint16_t* abase = &As[buf][r * kTileLDA + g * 32];
+        const uint16_t* abase = &As[buf * kStage + q * BM * kTileLDA + r * kTileLDA + g * 32];
         float sc[NT][2];
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
@@ -179,43 +209,67 @@ __global__ void __launch_bounds__(W * 64) k_gemm_tile(const uint16_t* __restrict
         }
     };
 
-    if (c0 < c1) {
+    if (steps > 0) {
         Slot ring[D];
 #pragma unroll
-        for (int d = 0; d < D; ++d) load_slot(ring[d], c0 + d);
-        store_a(0, ring[0], c0);
-        __syncthreads();   // scale table and first activation chunk ready
-        // Iteration for chunk cc (ring slot d, LDS buffer (cc - c0) & 1):
-        // stage chunk cc + 1 into the other buffer, refill slot d with chunk
-        // cc + D, contract chunk cc, then one barrier.
-        int c = c0;
-        for (; c + D <= c1; c += D) {
+        for (int d = 0; d < D; ++d) load_slot(ring[d], d);
+        store_a(0, ring[0], 0);
+        __syncthreads();   // scale table and first activation step ready
+        // Step i (ring slot i % D, LDS buffer i & 1): stage step i + 1 into
+        // the other buffer, refill the slot with step i + D, contract step i
+        // (waves whose part is shorter skip its last step), then one barrier.
+        int i = 0;
+        for (; i + D <= steps; i += D) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                const int cc = c + d;
-                if (cc + 1 < c1) store_a((cc + 1 - c0) & 1, ring[(d + 1) % D], cc + 1);
+                const int ii = i + d;
+                if (ii + 1 < steps) store_a((ii + 1) & 1, ring[(d + 1) % D], ii + 1);
                 const Slot cur = ring[d];
-                load_slot(ring[d], cc + D);
-                compute(cur, (cc - c0) & 1);
+                load_slot(ring[d], ii + D);
+                if (ii < len) compute(cur, ii & 1);
                 __syncthreads();
             }
         }
 #pragma unroll
         for (int d = 0; d < D - 1; ++d) {
-            const int cc = c + d;
-            if (cc < c1) {
-                if (cc + 1 < c1) store_a((cc + 1 - c0) & 1, ring[d + 1], cc + 1);
-                compute(ring[d], (cc - c0) & 1);
+            const int ii = i + d;
+            if (ii < steps) {
+                if (ii + 1 < steps) store_a((ii + 1) & 1, ring[d + 1], ii + 1);
+                if (ii < len) compute(ring[d], ii & 1);
                 __syncthreads();
             }
         }
-    } else {
+    }
+
+    // ---- sum the k-parts through LDS, in part order
+    if (KW > 1) {
         __syncthreads();
+        float* red = reinterpret_cast<float*>(As);
+        if (q > 0) {
+            float* mine = red + ((q - 1) * UW + uw) * kRedTile + lane * 4;
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    *reinterpret_cast<f32x4*>(mine + (ms * NT + j) * 256) = acc[ms][j];
+        }
+        __syncthreads();
+        if (q == 0) {
+#pragma unroll
+            for (int qq = 1; qq < KW; ++qq) {
+                const float* other = red + ((qq - 1) * UW + uw) * kRedTile + lane * 4;
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                    for (int j = 0; j < NT; ++j)
+                        acc[ms][j] += *reinterpret_cast<const f32x4*>(other + (ms * NT + j) * 256);
+            }
+        }
     }
 
     const float gv = effective_global_scale(gscale[e], g_is_div);
-    // lane (r, g) holds rows 16 ms + 4 g + i of column 16 (u_w + j) + r
-    if (S == 1) {
+    // lane (r, g) of a part-0 wave holds rows 16 ms + 4 g + i of column 16 (u_w + j) + r
+    auto store_y = [&]() {
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
@@ -227,6 +281,9 @@ __global__ void __launch_bounds__(W * 64) k_gemm_tile(const uint16_t* __restrict
                     if (m < rows && n < N) y[(row0 + m) * ld_y + n] = (uint16_t)f32_to_bf16_rne(gv * acc[ms][j][i]);
                 }
             }
+    };
+    if (S == 1) {
+        if (q == 0) store_y();
         return;
     }
 
@@ -239,26 +296,28 @@ __global__ void __launch_bounds__(W * 64) k_gemm_tile(const uint16_t* __restrict
     // device before the counter can return S - 1.
     const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
     const int64_t tiles = (int64_t)gridDim.x * gridDim.y;
-    constexpr int64_t kTilePairs = (int64_t)MS * NT * W * 64 * 2;   // float pairs per partial tile
+    constexpr int64_t kTilePairs = (int64_t)MS * NT * UW * 64 * 2;   // float pairs per partial tile
     uint64_t* parts = reinterpret_cast<uint64_t*>(sk.partials);
-    auto pidx = [&](int ms, int j, int h) { return (((ms * NT + j) * W + w) * 64 + lane) * 2 + h; };
-    uint64_t* my_part = parts + ((int64_t)s * tiles + tile) * kTilePairs;
+    auto pidx = [&](int ms, int j, int h) { return (((ms * NT + j) * UW + uw) * 64 + lane) * 2 + h; };
+    if (q == 0) {
+        uint64_t* my_part = parts + ((int64_t)s * tiles + tile) * kTilePairs;
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
+        for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
+            for (int j = 0; j < NT; ++j)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint64_t v = (uint64_t)__float_as_uint(acc[ms][j][2 * h]) |
-                                   ((uint64_t)__float_as_uint(acc[ms][j][2 * h + 1]) << 32);
-                __hip_atomic_store(my_part + pidx(ms, j, h), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+                for (int h = 0; h < 2; ++h) {
+                    const uint64_t v = (uint64_t)__float_as_uint(acc[ms][j][2 * h]) |
+                                       ((uint64_t)__float_as_uint(acc[ms][j][2 * h + 1]) << 32);
+                    __hip_atomic_store(my_part + pidx(ms, j, h), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+    }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);   // all of this wave's partial stores acknowledged
     __syncthreads();
     if (tid == 0) s_map[2] = atomicAdd(&sk.counters[tile], 1);
     __syncthreads();
-    if (s_map[2] != S - 1) return;   // uniform: not the last split of this tile
+    if (s_map[2] != S - 1 || q != 0) return;   // uniform per wave: not the last split, or not a part-0 wave
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
@@ -282,17 +341,7 @@ __global__ void __launch_bounds__(W * 64) k_gemm_tile(const uint16_t* __restrict
                 acc[ms][j][2 * h + 1] = v1;
             }
     if (tid == 0) __hip_atomic_store(&sk.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const int64_t n = (int64_t)(u_w + j) * kUnitN + r;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = ms * 16 + g * 4 + i;
-                if (m < rows && n < N) y[(row0 + m) * ld_y + n] = (uint16_t)f32_to_bf16_rne(gv * acc[ms][j][i]);
-            }
-        }
+    store_y();
 }
 
 }  // namespace nvfp4

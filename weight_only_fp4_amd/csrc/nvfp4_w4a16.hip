@@ -136,37 +136,39 @@ nvfp4_status launch_small(const Layout& L, const uint16_t* x, int64_t ld_x, cons
 }
 
 // ------------------------------------------------------------- tile path --
-// Tile shapes by row count, from launch-shape sweeps on MI355X.  K is split
-// across workgroups (grid z) while the tile count stays below the shape's
-// target and each split keeps >= 8 chunks.  The choice is a pure function of
-// (rows, N, K), so the workspace query reproduces it.
+// Tile shapes by row count, from launch-shape sweeps on MI355X: the fastest
+// decode-sized shapes run about one 16-wave workgroup per CU, four unit-waves
+// times four k-parts.  K is further split across workgroups (grid z) while
+// the workgroup count stays at or below 256 and every wave keeps >= 2
+// chunks.  The choice is a pure function of (rows, N, K), so the workspace
+// query reproduces it.
 struct TileShape {
-    int ms, nt, w, d, S;
+    int ms, nt, uw, kw, d, S;
     int64_t groups, mtiles;
     int64_t tiles() const { return groups * mtiles; }
     int bm() const { return 16 * ms; }
-    int ug() const { return nt * w; }
+    int ug() const { return nt * uw; }
 };
 
 TileShape tile_shape(const Layout& L, int64_t rows, bool grouped) {
     TileShape t;
-    int64_t target;   // workgroups the split may grow to
+    bool split = true;
     if (grouped) {
-        t.ms = 4; t.nt = 4; t.w = 4; t.d = 2; target = 0;
+        t.ms = 4; t.nt = 4; t.uw = 4; t.kw = 1; t.d = 2; split = false;
     } else if (rows <= 16) {
-        t.ms = 1; t.nt = 1; t.w = 4; t.d = 4; target = 1024;
+        t.ms = 1; t.nt = 1; t.uw = 4; t.kw = 4; t.d = 2;
     } else if (rows <= 32) {
-        t.ms = 2; t.nt = 2; t.w = 4; t.d = 4; target = 256;
+        t.ms = 2; t.nt = 1; t.uw = 4; t.kw = 2; t.d = 4;
     } else if (rows <= 64) {
-        t.ms = 4; t.nt = 2; t.w = 8; t.d = 2; target = 256;
-        if ((L.NU + 15) / 16 < 256) { t.w = 4; t.d = 4; }
+        if (L.NU >= 4096) { t.ms = 4; t.nt = 4; t.uw = 4; t.kw = 1; t.d = 2; }
+        else { t.ms = 4; t.nt = 1; t.uw = 4; t.kw = 4; t.d = 2; }
     } else {
-        t.ms = 8; t.nt = 4; t.w = 4; t.d = 2; target = 0;
+        t.ms = 8; t.nt = 2; t.uw = 8; t.kw = 1; t.d = 2; split = false;
     }
     t.groups = (L.NU + t.ug() - 1) / t.ug();
     t.mtiles = (rows + t.bm() - 1) / t.bm() + (grouped ? L.E : 0);
     t.S = 1;
-    while (t.S < 16 && t.tiles() * 2 * t.S <= target && L.KC >= 8 * (2 * t.S)) t.S *= 2;
+    while (split && t.S < 16 && t.tiles() * 2 * t.S <= 256 && L.KC >= 2 * t.kw * (2 * t.S)) t.S *= 2;
     return t;
 }
 
@@ -194,17 +196,17 @@ Workspace workspace_layout(const TileShape* t, int64_t rows, int64_t K, bool pre
     return w;
 }
 
-template <int MS, int NT, int W, int D, bool GROUPED>
+template <int MS, int NT, int UW, int KW, int D, bool GROUPED>
 void launch_tile_t(const TileShape& t, const Layout& L, const uint16_t* x, int64_t ld_x, BlobView bv, const float* gs,
                    int g_div, uint16_t* y, int64_t ld_y, int64_t rows, const int32_t* offsets, SplitK sk,
                    hipStream_t st) {
     const dim3 grid((unsigned)t.groups, (unsigned)t.mtiles, (unsigned)t.S);
     if (L.K % kChunkK == 0)
-        hipLaunchKernelGGL((k_gemm_tile<MS, NT, W, D, GROUPED, true>), grid, dim3(W * 64), 0, st, x, ld_x, bv,
-                           (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, (int)L.E, sk);
+        hipLaunchKernelGGL((k_gemm_tile<MS, NT, UW, KW, D, GROUPED, true>), grid, dim3(UW * KW * 64), 0, st, x, ld_x,
+                           bv, (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, (int)L.E, sk);
     else
-        hipLaunchKernelGGL((k_gemm_tile<MS, NT, W, D, GROUPED, false>), grid, dim3(W * 64), 0, st, x, ld_x, bv,
-                           (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, (int)L.E, sk);
+        hipLaunchKernelGGL((k_gemm_tile<MS, NT, UW, KW, D, GROUPED, false>), grid, dim3(UW * KW * 64), 0, st, x, ld_x,
+                           bv, (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, (int)L.E, sk);
 }
 
 template <bool GROUPED>
@@ -215,22 +217,26 @@ nvfp4_status launch_tile(const TileShape& t, const Layout& L, const uint16_t* x,
     SplitK sk{t.S, t.S > 1 ? reinterpret_cast<float*>(ws + wl.partials) : nullptr,
               t.S > 1 ? reinterpret_cast<int*>(ws + wl.counters) : nullptr};
     const BlobView bv = make_view(L, blob);
-#define NVFP4_TILE(MS, NT, W, D) launch_tile_t<MS, NT, W, D, GROUPED>(t, L, x, ld_x, bv, gs, g_div, y, ld_y, rows, offsets, sk, st)
+#define NVFP4_TILE(MS, NT, UW, KW, D) \
+    launch_tile_t<MS, NT, UW, KW, D, GROUPED>(t, L, x, ld_x, bv, gs, g_div, y, ld_y, rows, offsets, sk, st)
     if constexpr (GROUPED) {
-        NVFP4_TILE(4, 4, 4, 2);
+        NVFP4_TILE(4, 4, 4, 1, 2);
     } else {
-        if (t.ms == 1) NVFP4_TILE(1, 1, 4, 4);
-        else if (t.ms == 2) NVFP4_TILE(2, 2, 4, 4);
-        else if (t.ms == 4 && t.w == 8) NVFP4_TILE(4, 2, 8, 2);
-        else if (t.ms == 4) NVFP4_TILE(4, 2, 4, 4);
-        else NVFP4_TILE(8, 4, 4, 2);
+        if (t.ms == 1) NVFP4_TILE(1, 1, 4, 4, 2);
+        else if (t.ms == 2) NVFP4_TILE(2, 1, 4, 2, 4);
+        else if (t.ms == 4 && t.kw == 1) NVFP4_TILE(4, 4, 4, 1, 2);
+        else if (t.ms == 4) NVFP4_TILE(4, 1, 4, 4, 2);
+        else NVFP4_TILE(8, 2, 8, 1, 2);
     }
 #undef NVFP4_TILE
     return launched("tile GEMM");
 }
 
+// Activation row stride limit: offsets within a 128-row tile stay in 32 bits.
+constexpr int64_t kMaxLdX = int64_t(1) << 23;
+
 // Rows at or below this use the small-M kernel when the variant is automatic.
-constexpr int64_t kSmallAuto = 8;
+constexpr int64_t kSmallAuto = 4;
 
 // Shared checks of the activation / output / pre-scale / workspace arguments.
 nvfp4_status check_gemm_io(const char* fn, const void* x, int64_t ld_x, const void* pre, const void* w,
@@ -243,6 +249,8 @@ nvfp4_status check_gemm_io(const char* fn, const void* x, int64_t ld_x, const vo
     if (!gs) return fail(NVFP4_ERR_INVALID_ARG, "%s: global scale pointer is NULL", fn);
     if (rows > 0 && !x) return fail(NVFP4_ERR_INVALID_ARG, "%s: x is NULL", fn);
     if (rows > 0 && !y) return fail(NVFP4_ERR_INVALID_ARG, "%s: y is NULL", fn);
+    if (ld_x > kMaxLdX)
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_x = %lld exceeds %lld", fn, (long long)ld_x, (long long)kMaxLdX);
     if (!aligned(x, 16) || ld_x % 8 != 0)
         return fail(NVFP4_ERR_ALIGNMENT, "%s: x must be 16-byte aligned with ld_x %% 8 == 0 (ld_x = %lld)", fn, (long long)ld_x);
     if (pre && !aligned(pre, 16)) return fail(NVFP4_ERR_ALIGNMENT, "%s: pre_scale must be 16-byte aligned", fn);
