@@ -111,6 +111,17 @@ __device__ __forceinline__ uint4 load_stream_u4(const uint8_t* p) {
 __device__ __forceinline__ uint32_t load_stream_u16(const uint8_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
 }
+// Scale bytes of a 128-byte scale block: lanes 2i and 2i + 1 load the same
+// dword (a dword load needs no zero extension, which spares the register
+// copies the compiler otherwise inserts around 16-bit loads kept in flight
+// across a loop).  The raw dword is kept in the prefetch ring and the lane's
+// two bytes are selected only when the chunk is used (scale_pair), so no
+// arithmetic touches a load result before its slot is consumed.
+__device__ __forceinline__ uint32_t load_scale_dword(const uint8_t* block, int lane) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(block + ((lane >> 1) << 2)));
+}
+// The lane's two scale bytes (low byte = lower k) in bits 0..15 of the result.
+__device__ __forceinline__ uint32_t scale_pair(uint32_t raw, int lane) { return raw >> ((lane & 1) << 4); }
 
 // Global scale as used in the epilogue: the stored value, or its correctly
 // rounded fp32 reciprocal when it is stored as a divisor.

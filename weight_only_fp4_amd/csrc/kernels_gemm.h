@@ -61,7 +61,7 @@ __device__ __forceinline__ void build_scale_table(float2* lut) {
 // from the clamped address cannot reach the sums (the weights there are zero
 // padding, but the activation might not be finite).
 template <int MG, int NT, bool KFULL>
-__device__ __forceinline__ void small_m_chunk(const SmallSlot<MG, NT>& s, bool kin, const float2* lut,
+__device__ __forceinline__ void small_m_chunk(const SmallSlot<MG, NT>& s, bool kin, const float2* lut, int lane,
                                               f32x4 (&acc)[NT][MG]) {
     s16x4 alo[MG], ahi[MG];
 #pragma unroll
@@ -77,7 +77,8 @@ __device__ __forceinline__ void small_m_chunk(const SmallSlot<MG, NT>& s, bool k
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-        const float2 s0 = lut[s.sw[j] & 0xFFu], s1 = lut[(s.sw[j] >> 8) & 0xFFu];
+        const uint32_t sp = scale_pair(s.sw[j], lane);
+        const float2 s0 = lut[sp & 0xFFu], s1 = lut[(sp >> 8) & 0xFFu];
         const uint4 cw = s.cw[j];
         const s16x4 b0 = decode4_bf16_pow2<0>(cw.x, s0.x), b1 = decode4_bf16_pow2<2>(cw.x, s0.x);
         const s16x4 b2 = decode4_bf16_pow2<0>(cw.y, s0.x), b3 = decode4_bf16_pow2<2>(cw.y, s0.x);
@@ -102,85 +103,111 @@ __device__ __forceinline__ void small_m_chunk(const SmallSlot<MG, NT>& s, bool k
     }
 }
 
-// One wave's share of a pass: rows [0, rows) (rows <= 4 MG) of the activation
-// block starting at xrow0, NT consecutive units whose code / scale blocks
-// start at the wave-uniform cbase / sbase (unit j, chunk c at + j * ustr +
-// c * cstr code bytes, an eighth of that in scale bytes), K chunks [c0, c1).  Operands of the next D chunks are kept in flight in a
-// register ring.  Lane l = 16 g + 4 q + i holds rows 4 mg + i of the
-// activation at k = 128 c + 32 g + 8 q .. +7; MFMA step t (k = 32 g + 4 t ..
-// +3) broadcasts A from block q = t >> 1 of each group of four blocks
-// (cbsz = 2, abid = t >> 1).  On return the wave's partial sums, reduced over
-// its four K groups, are in red_w[row * red_ld + col] for rows < 4 MG and
-// cols < 16 NT.
-template <int MG, int NT, int D, bool KFULL>
-__device__ __forceinline__ void small_m_pass(const uint16_t* __restrict__ xrow0, int64_t ld_x, int rows,
-                                             const uint8_t* __restrict__ cbase, const uint8_t* __restrict__ sbase,
-                                             int64_t ustr, int64_t cstr, int nt_valid, int c0, int c1, int K,
-                                             const float2* lut, float* red_w, int red_ld, int lane) {
-    const int g = lane >> 4, q = (lane >> 2) & 3, ai = lane & 3;
-    f32x4 acc[NT][MG];
-    uint32_t xoff[MG];   // byte offset of the lane's activation piece in chunk 0
+// Prefetch ring over n chunks (indices 0..n-1) of one wave: D slots, each
+// consumed and then refilled with the chunk D ahead.  Scheduling barriers pin
+// the issue order, so the wait before a slot's use only covers loads issued
+// D - 1 slots earlier (left to itself the scheduler sinks refills to the end
+// of the unrolled body and drains the ring every D chunks).  The steady loop
+// runs only while every refill is in range, so its wait counts are static
+// and no chunk is loaded twice; the last < 2D chunks drain with guarded
+// refills.  `mid` runs once, after the first D loads are issued (the caller
+// builds its LDS tables and synchronises there, under the load latency).
+// Every wave must call this (mid may hold a barrier).  The first D loads are
+// unconditional (a conditional prologue leaves the compiler unable to count
+// them at the loop head), so load(slot, 0) must be in bounds even when
+// n == 0; chunks past n - 1 repeat chunk n - 1 (short waves only).
+template <int D, typename Slot, typename LoadF, typename UseF, typename MidF>
+__device__ __forceinline__ void run_ring(int n, LoadF&& load, UseF&& use, MidF&& mid) {
+    Slot ring[D];
+    const int last = n > 1 ? n - 1 : 0;
 #pragma unroll
-    for (int mg = 0; mg < MG; ++mg) {
-        const int m = 4 * mg + ai;
-        xoff[mg] = (uint32_t)(((int64_t)(m < rows ? m : 0) * ld_x + g * 32 + q * 8) * 2);
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[j][mg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < D; ++d) {
+        load(ring[d], d < last ? d : last);
+        __builtin_amdgcn_sched_barrier(0);
     }
-    if (c0 >= c1) {
+    mid();
+    if (n <= 0) return;
+    int i = 0;
+    for (; i + 2 * D <= n; i += D) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-            for (int mg = 0; mg < MG; ++mg)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (lane < 16) red_w[(4 * mg + i) * red_ld + j * 16 + lane] = 0.f;
-        return;
+        for (int d = 0; d < D; ++d) {
+            use(ring[d], i + d);
+            __builtin_amdgcn_sched_barrier(0);
+            load(ring[d], i + D + d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        if (i + d < n) use(ring[d], i + d);
+        if (i + D + d < n) load(ring[d], i + D + d);
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if (i + D + d < n) use(ring[d], i + D + d);
+}
 
-    // Loads are issued unconditionally from clamped, in-bounds addresses and
-    // never masked at load time: a load under a lane-divergent branch, or a
-    // select right after it, makes the compiler wait for the load there,
-    // which would serialise the prefetch ring.  Rows past `rows` and units
-    // past nt_valid read valid but unrelated data; they only feed output
-    // rows / columns that are never stored.  Addresses are a wave-uniform
-    // base plus a 32-bit lane offset.
-    const int c_last = c1 - 1;
-    const int kpiece = g * 32 + q * 8;
-    const uint8_t* xb = reinterpret_cast<const uint8_t*>(xrow0);
-    auto load = [&](SmallSlot<MG, NT>& s, int c_req) {
-        const int c = c_req < c_last ? c_req : c_last;
+// Weight-side addressing of one wave: NT consecutive units whose code / scale
+// blocks start at the wave-uniform cbase / sbase (unit j, chunk c at
+// + j * ustr + c * cstr code bytes, an eighth of that in scale bytes).  Units
+// past nt_valid re-read unit 0 (their columns are never stored).
+struct WaveWeights {
+    const uint8_t* cbase;
+    const uint8_t* sbase;
+    int64_t ustr, cstr;
+    int nt_valid;
+    template <int NT>
+    __device__ __forceinline__ void load(uint4 (&cw)[NT], uint32_t (&sw)[NT], int c, int lane) const {
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             const int64_t jj = j < nt_valid ? j : 0;
             const int64_t boff = jj * ustr + (int64_t)c * cstr;   // wave-uniform
-            s.cw[j] = load_stream_u4(cbase + boff + (uint32_t)(lane * 16));
-            s.sw[j] = load_stream_u16(sbase + (boff >> 3) + (uint32_t)(lane * 2));
+            cw[j] = load_stream_u4(cbase + boff + (uint32_t)(lane * 16));
+            sw[j] = load_scale_dword(sbase + (boff >> 3), lane);
         }
-        const uint32_t kb = (KFULL || c * kChunkK + kpiece < K) ? (uint32_t)(c * kChunkK * 2) : 0u;
+    }
+};
+
+// One wave's share of a pass in the 4x4x4 form: rows [0, rows) (rows <= 4 MG)
+// of the activation block starting at xrow0, NT units, chunks [c0, c1).  Lane
+// l = 16 g + 4 q + i holds rows 4 mg + i of the activation at k = 128 c +
+// 32 g + 8 q .. +7 (for each row group, the 16 lanes of a row read its 256
+// contiguous bytes of the chunk); MFMA step t (k = 32 g + 4 t .. +3)
+// broadcasts A from block q = t >> 1 of each group of four blocks (cbsz = 2,
+// abid = t >> 1).  On return the wave's partial sums, reduced over its four K
+// groups, are in red_w[row * red_ld + col] for rows < 4 MG, cols < 16 NT.
+template <int MG, int NT, int D, bool KFULL, typename MidF>
+__device__ __forceinline__ void small_m_pass(const uint16_t* __restrict__ xrow0, int64_t ld_x, int rows,
+                                             const WaveWeights& ww, int c0, int c1, int K, const float2* lut,
+                                             float* red_w, int red_ld, int lane, MidF&& mid) {
+    const int g = lane >> 4, q = (lane >> 2) & 3, ai = lane & 3;
+    f32x4 acc[NT][MG];
+    uint32_t xoff[MG];   // byte offset of the lane's activation row
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) {
+        const int m = 4 * mg + ai;
+        xoff[mg] = (uint32_t)((int64_t)(m < rows ? m : 0) * ld_x * 2);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[j][mg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // Loads are issued unconditionally from in-bounds addresses and masked
+    // only at use: a load under a lane-divergent branch, or a select right
+    // after it, makes the compiler wait for the load there.  Rows past
+    // `rows` read row 0 and only feed output rows that are never stored;
+    // activation pieces past K read k = 0..7 of their row (valid: K >= 16)
+    // and are zeroed at use.
+    const int kpiece = g * 32 + q * 8;
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(xrow0);
+    auto kin = [&](int c) { return KFULL || (c * kChunkK + kpiece < K); };
+    auto load = [&](SmallSlot<MG, NT>& s, int i) {
+        const int c = c0 + i;
+        ww.load<NT>(s.cw, s.sw, c, lane);
+        const uint32_t kb = kin(c) ? (uint32_t)((c * kChunkK + kpiece) * 2) : 0u;
 #pragma unroll
         for (int mg = 0; mg < MG; ++mg) s.xa[mg] = *reinterpret_cast<const uint4*>(xb + (xoff[mg] + kb));
     };
-    auto kin = [&](int c) { return KFULL || (c * kChunkK + kpiece < K); };
-
-    // Straight-line main loop over D chunks (each slot is refilled D chunks
-    // ahead as soon as it has been read), then a load-free tail for the last
-    // (c1 - c0) % D chunks, which are already in the ring.
-    SmallSlot<MG, NT> ring[D];
-#pragma unroll
-    for (int d = 0; d < D; ++d) load(ring[d], c0 + d);
-    int c = c0;
-    for (; c + D <= c1; c += D) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const SmallSlot<MG, NT> cur = ring[d];
-            load(ring[d], c + D + d);
-            small_m_chunk<MG, NT, KFULL>(cur, kin(c + d), lut, acc);
-        }
-    }
-#pragma unroll
-    for (int d = 0; d < D - 1; ++d)
-        if (c + d < c1) small_m_chunk<MG, NT, KFULL>(ring[d], kin(c + d), lut, acc);
+    auto use = [&](const SmallSlot<MG, NT>& s, int i) { small_m_chunk<MG, NT, KFULL>(s, kin(c0 + i), lut, lane, acc); };
+    run_ring<D, SmallSlot<MG, NT>>(c1 - c0, load, use, mid);
 
     // Sum the four K groups: lanes l, l^16, l^32, l^48 hold the same outputs;
     // lane l < 16 then holds column l of each unit, rows 4 mg + i.
@@ -197,14 +224,13 @@ __device__ __forceinline__ void small_m_pass(const uint16_t* __restrict__ xrow0,
             }
 }
 
-// Rows 9..16 of a pass: v_mfma_f32_16x16x32_bf16 on fully scaled bf16
-// weight fragments (decode8_bf16), 4 MFMAs per unit and chunk instead of the
-// 32 the 4x4x4 form needs for 16 rows.  Lane l = 16 g + r holds activation
-// row r at k = 128 c + 32 g + 8 t .. +7 for MFMA step t (four 16-byte pieces
-// per chunk) and the codes of weight row 16 u + r at the same k; the MFMA
-// sums over the four lane groups, so no K-group reduction is needed.  On
-// return red_w[row * red_ld + col] holds the wave's partial sums for rows <
-// 16 and cols < 16 NT.
+// One wave's share of a pass in the 16x16x32 form (rows <= 16):
+// v_mfma_f32_16x16x32_bf16 on fully scaled bf16 weight fragments
+// (decode8_bf16), 4 MFMAs per unit and chunk.  Lane l = 16 g + r holds
+// activation row r at k = 128 c + 32 g + 8 t .. +7 for MFMA step t (four
+// 16-byte pieces per chunk) and the codes of weight row 16 u + r at the same
+// k; the MFMA sums over the four lane groups.  On return red_w[row * red_ld
+// + col] holds the wave's partial sums for rows < 16 and cols < 16 NT.
 template <int NT>
 struct Slot16 {
     uint4 cw[NT];
@@ -212,71 +238,48 @@ struct Slot16 {
     uint4 xa[4];
 };
 
-template <int NT, int D, bool KFULL>
+template <int NT, int D, bool KFULL, typename MidF>
 __device__ __forceinline__ void small_m_pass16(const uint16_t* __restrict__ xrow0, int64_t ld_x, int rows,
-                                               const uint8_t* __restrict__ cbase, const uint8_t* __restrict__ sbase,
-                                               int64_t ustr, int64_t cstr, int nt_valid, int c0, int c1, int K,
-                                               const float2* lut, float* red_w, int red_ld, int lane) {
+                                               const WaveWeights& ww, int c0, int c1, int K, const float2* lut,
+                                               float* red_w, int red_ld, int lane, MidF&& mid) {
     const int g = lane >> 4, r = lane & 15;
     f32x4 acc[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint32_t xoff = (uint32_t)(((int64_t)(r < rows ? r : 0) * ld_x + g * 32) * 2);
-    if (c0 < c1) {
-        const int c_last = c1 - 1;
-        const uint8_t* xb = reinterpret_cast<const uint8_t*>(xrow0);
-        auto load = [&](Slot16<NT>& s, int c_req) {
-            const int c = c_req < c_last ? c_req : c_last;
+    const uint32_t xoff = (uint32_t)((int64_t)(r < rows ? r : 0) * ld_x * 2);   // the lane's activation row
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(xrow0);
+    auto kin = [&](int c, int t) { return KFULL || (c * kChunkK + g * 32 + t * 8 < K); };
+    auto load = [&](Slot16<NT>& s, int i) {
+        const int c = c0 + i;
+        ww.load<NT>(s.cw, s.sw, c, lane);
+        // pieces past K read k = 0..7 of the row (valid: K >= 16) and are zeroed at use
 #pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                const int64_t jj = j < nt_valid ? j : 0;
-                const int64_t boff = jj * ustr + (int64_t)c * cstr;   // wave-uniform
-                s.cw[j] = load_stream_u4(cbase + boff + (uint32_t)(lane * 16));
-                s.sw[j] = load_stream_u16(sbase + (boff >> 3) + (uint32_t)(lane * 2));
-            }
+        for (int t = 0; t < 4; ++t)
+            s.xa[t] = *reinterpret_cast<const uint4*>(
+                xb + xoff + (kin(c, t) ? (uint32_t)((c * kChunkK + g * 32 + t * 8) * 2) : 0u));
+    };
+    auto use = [&](const Slot16<NT>& s, int i) {
+        const int c = c0 + i;
+        bf16x8 a[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const bool kin = KFULL || (c * kChunkK + g * 32 + t * 8 < K);
-                s.xa[t] = *reinterpret_cast<const uint4*>(xb + xoff + (kin ? (uint32_t)((c * kChunkK + t * 8) * 2)
-                                                                         : 0u));
-            }
-        };
-        auto chunk = [&](const Slot16<NT>& s, int c) {
-            bf16x8 a[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const bool kin = KFULL || (c * kChunkK + g * 32 + t * 8 < K);
-                const uint4 v = s.xa[t];
-                a[t] = uint4_to_bf16x8(kin ? v : make_uint4(0u, 0u, 0u, 0u));
-            }
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                const float2 l0 = lut[s.sw[j] & 0xFFu], l1 = lut[(s.sw[j] >> 8) & 0xFFu];
-                // the full scale: 2^exponent(conversion operand) times the factor, exact
-                const float s0 = __uint_as_float(__float_as_uint(l0.x) & 0x7F800000u) * l0.y;
-                const float s1 = __uint_as_float(__float_as_uint(l1.x) & 0x7F800000u) * l1.y;
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], uint4_to_bf16x8(decode8_bf16(s.cw[j].x, s0)), acc[j], 0, 0, 0);
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], uint4_to_bf16x8(decode8_bf16(s.cw[j].y, s0)), acc[j], 0, 0, 0);
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], uint4_to_bf16x8(decode8_bf16(s.cw[j].z, s1)), acc[j], 0, 0, 0);
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], uint4_to_bf16x8(decode8_bf16(s.cw[j].w, s1)), acc[j], 0, 0, 0);
-            }
-        };
-        Slot16<NT> ring[D];
-#pragma unroll
-        for (int d = 0; d < D; ++d) load(ring[d], c0 + d);
-        int c = c0;
-        for (; c + D <= c1; c += D) {
-#pragma unroll
-            for (int d = 0; d < D; ++d) {
-                const Slot16<NT> cur = ring[d];
-                load(ring[d], c + D + d);
-                chunk(cur, c + d);
-            }
+        for (int t = 0; t < 4; ++t) {
+            const uint4 v = s.xa[t];
+            a[t] = uint4_to_bf16x8(kin(c, t) ? v : make_uint4(0u, 0u, 0u, 0u));
         }
 #pragma unroll
-        for (int d = 0; d < D - 1; ++d)
-            if (c + d < c1) chunk(ring[d], c + d);
-    }
+        for (int j = 0; j < NT; ++j) {
+            const uint32_t sp = scale_pair(s.sw[j], lane);
+            const float2 l0 = lut[sp & 0xFFu], l1 = lut[(sp >> 8) & 0xFFu];
+            // the full scale: 2^exponent(conversion operand) times the factor, exact
+            const float s0 = __uint_as_float(__float_as_uint(l0.x) & 0x7F800000u) * l0.y;
+            const float s1 = __uint_as_float(__float_as_uint(l1.x) & 0x7F800000u) * l1.y;
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], uint4_to_bf16x8(decode8_bf16(s.cw[j].x, s0)), acc[j], 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], uint4_to_bf16x8(decode8_bf16(s.cw[j].y, s0)), acc[j], 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], uint4_to_bf16x8(decode8_bf16(s.cw[j].z, s1)), acc[j], 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], uint4_to_bf16x8(decode8_bf16(s.cw[j].w, s1)), acc[j], 0, 0, 0);
+        }
+    };
+    run_ring<D, Slot16<NT>>(c1 - c0, load, use, mid);
     // lane l holds rows 4 (l >> 4) + i of column l & 15 of each unit
 #pragma unroll
     for (int j = 0; j < NT; ++j)
@@ -287,9 +290,11 @@ __device__ __forceinline__ void small_m_pass16(const uint16_t* __restrict__ xrow
 // Small-M GEMM: one workgroup per NT consecutive 16-row units of W (and per
 // expert in the grouped form); its W waves split K into contiguous chunk
 // ranges, and the per-wave partial sums are added in wave order through LDS.
-// MG in 1..4: every pass uses MG row groups of the 4x4x4 form (rows <= 4 MG).
+// MG in 1, 2, 4: every pass uses MG row groups of the 4x4x4 form (rows <= 4 MG).
 // MG == 16: every pass uses the 16x16x32 form (rows <= 16).
 // MG == 0: each pass of up to 16 rows picks one or four row groups (grouped).
+// The first weight loads of a wave are issued before the scale table is
+// built, so the table build and its barrier run under the load latency.
 template <int MG, int NT, int W, int D, bool GROUPED, bool KFULL>
 __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                          int NU, int KC, int K,
@@ -307,42 +312,46 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
         count = (int64_t)offsets[e + 1] - row0;
     }
     if (count <= 0 || u0 >= NU) return;   // uniform over the workgroup
-    build_scale_table(lut);
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: keeps the chunk loop scalar
+    // chunks [c0, c1); c0 <= KC - 1 even for an empty range, so the ring's
+    // unconditional first loads stay in bounds
     const int c0 = (int)((int64_t)KC * w / W), c1 = (int)((int64_t)KC * (w + 1) / W);
-    const int nt_valid = (NU - u0) < NT ? (NU - u0) : NT;
     const int64_t blk0 = bv.block(e, u0, 0);
-    const uint8_t* cbase = bv.codes + blk0 * kCodeBlock;
-    const uint8_t* sbase = bv.scales + blk0 * kScaleBlock;
-    const int64_t ustr = bv.unit_stride * kCodeBlock, cstr = bv.chunk_stride * kCodeBlock;
-    const float gv = effective_global_scale(gscale[e], g_is_div);
-    __syncthreads();   // scale table ready
+    const WaveWeights ww{bv.codes + blk0 * kCodeBlock, bv.scales + blk0 * kScaleBlock,
+                         bv.unit_stride * kCodeBlock, bv.chunk_stride * kCodeBlock,
+                         (NU - u0) < NT ? (NU - u0) : NT};
+    bool first = true;
+    auto mid = [&]() {
+        if (first) {
+            build_scale_table(lut);
+            __syncthreads();   // scale table ready
+            first = false;
+        }
+    };
 
     for (int64_t p0 = 0; p0 < count; p0 += kSmallRows) {
         const int rows = (int)((count - p0) < kSmallRows ? (count - p0) : kSmallRows);
         const uint16_t* xrow0 = x + (row0 + p0) * ld_x;
         if constexpr (MG == 16) {
-            small_m_pass16<NT, D, KFULL>(xrow0, ld_x, rows, cbase, sbase, ustr, cstr, nt_valid, c0, c1, K, lut, red[w],
-                                         RLD, lane);
+            small_m_pass16<NT, D, KFULL>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane, mid);
         } else if constexpr (MG > 0) {
-            small_m_pass<MG, NT, D, KFULL>(xrow0, ld_x, rows, cbase, sbase, ustr, cstr, nt_valid, c0, c1, K, lut,
-                                           red[w], RLD, lane);
+            small_m_pass<MG, NT, D, KFULL>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane, mid);
         } else {
             if (rows <= 4)
-                small_m_pass<1, NT, D, KFULL>(xrow0, ld_x, rows, cbase, sbase, ustr, cstr, nt_valid, c0, c1, K, lut,
-                                              red[w], RLD, lane);
+                small_m_pass<1, NT, D, KFULL>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane, mid);
             else
-                small_m_pass<4, NT, (D > 2 ? 2 : D), KFULL>(xrow0, ld_x, rows, cbase, sbase, ustr, cstr, nt_valid, c0,
-                                                           c1, K, lut, red[w], RLD, lane);
+                small_m_pass<4, NT, (D > 2 ? 2 : D), KFULL>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane,
+                                                           mid);
         }
         __syncthreads();
+        const float gv = effective_global_scale(gscale[e], g_is_div);
         for (int t = threadIdx.x; t < rows * RLD; t += W * 64) {
             const int r = t / RLD, col = t % RLD;
             float acc = 0.f;
 #pragma unroll
-            for (int ww = 0; ww < W; ++ww) acc += red[ww][r * RLD + col];
+            for (int wi = 0; wi < W; ++wi) acc += red[wi][r * RLD + col];
             const int64_t n = (int64_t)u0 * kUnitN + col;
             if (n < N) y[(row0 + p0 + r) * ld_y + n] = (uint16_t)f32_to_bf16_rne(gv * acc);
         }

@@ -68,7 +68,7 @@ struct SmallShape {
 
 SmallShape small_m_shape(const Layout& L, int64_t rows, bool grouped) {
     SmallShape s;
-    s.mg = grouped ? 0 : (rows <= 8 ? (int)((rows + 3) / 4) : 16);
+    s.mg = grouped ? 0 : (rows <= 4 ? 1 : rows <= 8 ? 2 : 4);
     s.nt = (!grouped && rows > 4 && L.NU >= 512) ? 2 : 1;
     s.d = (s.mg == 0 || s.mg <= 2) ? 4 : 2;
     const int64_t ctas = (L.NU + s.nt - 1) / s.nt * (grouped ? (L.E + 1) / 2 : 1);
@@ -123,11 +123,14 @@ nvfp4_status launch_small(const Layout& L, const uint16_t* x, int64_t ld_x, cons
         switch (s.mg) {
             case 1: NVFP4_SMALL(1, 1); break;
             case 2: NVFP4_SMALL(2, 1); break;
+            case 4: NVFP4_SMALL(4, 1); break;
             default: NVFP4_SMALL(16, 1); break;
         }
     } else {
         switch (s.mg) {
+            case 1: NVFP4_SMALL(1, 2); break;
             case 2: NVFP4_SMALL(2, 2); break;
+            case 4: NVFP4_SMALL(4, 2); break;
             default: NVFP4_SMALL(16, 2); break;
         }
     }
