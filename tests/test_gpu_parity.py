@@ -33,6 +33,11 @@ def accept_or_fail(y, ref, what):
     return info
 
 
+def dense_variants(M: int, K: int):
+    """Every kernel variant that takes this shape: automatic, tile, small-M (M <= 16)."""
+    return [nv.VARIANT_AUTO, nv.VARIANT_LARGE_M] + ([nv.VARIANT_SMALL_M] if M <= 16 else [])
+
+
 def oracle_bf16_bits(t64: np.ndarray) -> np.ndarray:
     """fp64 values exactly representable in bf16 -> bf16 bit patterns (sign of zero kept)."""
     f = t64.astype(np.float32)
@@ -110,7 +115,8 @@ def test_hand_cases_exact(case, variant):
         assert got[n] == exp[n], (case, variant, n, got[n], exp[n])
 
 
-@pytest.mark.parametrize("variant,M,N", [(nv.VARIANT_SMALL_M, 16, 40), (nv.VARIANT_LARGE_M, 256, 300)])
+@pytest.mark.parametrize("variant,M,N", [(nv.VARIANT_SMALL_M, 16, 40), (nv.VARIANT_LARGE_M, 256, 300),
+])
 def test_identity_activation_gives_tile_bit_exact(variant, M, N):
     """X = I_K, g = 1: every output is one exact product, so Y = T^T bit for bit (signed zeros compare equal)."""
     K = M
@@ -148,8 +154,7 @@ def test_dense_parity_full_oracle(name, make):
     say(f"dense {name} M={c.M} N={c.N} K={c.K} pre={c.pre is not None} div={c.g_is_divisor}")
     d = DenseDev(c)
     ref = oracle.gemm(c.x, c.w, c.s, c.g_stored, c.g_is_divisor, c.pre)
-    variants = [nv.VARIANT_AUTO, nv.VARIANT_LARGE_M] + ([nv.VARIANT_SMALL_M] if c.M <= 16 else [])
-    for v in variants:
+    for v in dense_variants(c.M, c.K):
         accept_or_fail(to_f64(d.run(v)), ref, (name, v))
 
 
@@ -308,7 +313,7 @@ def test_smallest_shapes():
         c = synth.dense_case(M, N, K, seed=M * 100 + N)
         d = DenseDev(c)
         ref = oracle.gemm(c.x, c.w, c.s, c.g_stored, False, None)
-        for v in [nv.VARIANT_LARGE_M] + ([nv.VARIANT_SMALL_M] if M <= 16 else []):
+        for v in dense_variants(M, K):
             accept_or_fail(to_f64(d.run(v)), ref, (M, N, K, v))
 
 

@@ -123,6 +123,19 @@ __device__ __forceinline__ uint32_t load_scale_dword(const uint8_t* block, int l
 // The lane's two scale bytes (low byte = lower k) in bits 0..15 of the result.
 __device__ __forceinline__ uint32_t scale_pair(uint32_t raw, int lane) { return raw >> ((lane & 1) << 4); }
 
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt in bits 3..0 and 15..14, expcnt 6..4, lgkmcnt 11..8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt lgkmcnt(0) with the other counters left alone.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
 // Global scale as used in the epilogue: the stored value, or its correctly
 // rounded fp32 reciprocal when it is stored as a divisor.
 __device__ __forceinline__ float effective_global_scale(float stored, int is_divisor) {

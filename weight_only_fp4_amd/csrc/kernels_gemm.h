@@ -33,6 +33,45 @@ namespace nvfp4 {
 constexpr int kSmallRows = 16;      // rows per pass of the small-M kernel
 constexpr int kMaxExperts = 4096;
 
+// K split across workgroups (grid z).  Each split publishes its fp32 partial
+// tile to the workspace and bumps the tile's counter; the workgroup that
+// arrives last adds the S partials in split order 0..S-1 (independent of the
+// arrival order, so results are bitwise reproducible), applies the epilogue
+// and resets the counter to zero for the next call.  Partials are stored and
+// loaded with device-scope (sc1) accesses, which are coherent across the
+// XCDs' separate L2 caches; an agent-scope fence would instead write back and
+// invalidate the whole L2 of the XCD.
+struct SplitK {
+    int S;              // K splits (grid z)
+    float* partials;    // [S][tiles][tile floats], used when S > 1
+    int* counters;      // [tiles], zero between calls
+};
+
+__device__ __forceinline__ void store_partial(float* p, float v) {
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_partial(const float* p) {
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Called by every thread of a workgroup after it has stored its split's
+// partial with store_partial: waits until the stores are acknowledged, then
+// bumps the counter of `tile`.  Returns true in the workgroup that arrived
+// last (the one that must reduce); that workgroup also resets the counter.
+__device__ __forceinline__ bool split_arrive(int* counters, int64_t tile, int S, int* s_flag) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);   // all of this wave's partial stores acknowledged
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int prev = atomicAdd(&counters[tile], 1);
+        *s_flag = prev;
+        if (prev == S - 1) __hip_atomic_store(&counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    return *s_flag == S - 1;
+}
+
 // ----------------------------------------------------------------- small-M --
 
 // One chunk's operands for one wave: NT weight code blocks, their scale pairs,
@@ -288,8 +327,10 @@ __device__ __forceinline__ void small_m_pass16(const uint16_t* __restrict__ xrow
 }
 
 // Small-M GEMM: one workgroup per NT consecutive 16-row units of W (and per
-// expert in the grouped form); its W waves split K into contiguous chunk
-// ranges, and the per-wave partial sums are added in wave order through LDS.
+// expert in the grouped form); its W waves split the workgroup's K range into
+// contiguous chunk ranges, and the per-wave partial sums are added in wave
+// order through LDS.  The dense form may also split K across S workgroups
+// (grid z, SplitK).
 // MG in 1, 2, 4: every pass uses MG row groups of the 4x4x4 form (rows <= 4 MG).
 // MG == 16: every pass uses the 16x16x32 form (rows <= 16).
 // MG == 0: each pass of up to 16 rows picks one or four row groups (grouped).
@@ -300,10 +341,13 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
                                                          int NU, int KC, int K,
                                                          int N, const float* __restrict__ gscale, int g_is_div,
                                                          uint16_t* __restrict__ y, int64_t ld_y, int64_t rows_dense,
-                                                         const int32_t* __restrict__ offsets) {
+                                                         const int32_t* __restrict__ offsets, SplitK sk) {
     constexpr int RLD = NT * 16;
-    __shared__ float red[W][kSmallRows * RLD];
+    constexpr int kTileFloats = kSmallRows * RLD;
+    constexpr int kPer = (kTileFloats + W * 64 - 1) / (W * 64);   // partial-tile floats per thread
+    __shared__ float red[W][kTileFloats];
     __shared__ float2 lut[256];
+    __shared__ int s_flag;
     const int u0 = blockIdx.x * NT;
     const int e = GROUPED ? (int)blockIdx.y : 0;
     int64_t row0 = 0, count = rows_dense;
@@ -315,9 +359,12 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: keeps the chunk loop scalar
-    // chunks [c0, c1); c0 <= KC - 1 even for an empty range, so the ring's
-    // unconditional first loads stay in bounds
-    const int c0 = (int)((int64_t)KC * w / W), c1 = (int)((int64_t)KC * (w + 1) / W);
+    // this split's chunks [C0, C0 + span), this wave's [c0, c1); c0 <= KC - 1
+    // even for an empty range, so the ring's unconditional first loads stay
+    // in bounds
+    const int S = GROUPED ? 1 : sk.S, s = GROUPED ? 0 : (int)blockIdx.z;
+    const int C0 = (int)((int64_t)KC * s / S), span = (int)((int64_t)KC * (s + 1) / S) - C0;
+    const int c0 = C0 + (int)((int64_t)span * w / W), c1 = C0 + (int)((int64_t)span * (w + 1) / W);
     const int64_t blk0 = bv.block(e, u0, 0);
     const WaveWeights ww{bv.codes + blk0 * kCodeBlock, bv.scales + blk0 * kScaleBlock,
                          bv.unit_stride * kCodeBlock, bv.chunk_stride * kCodeBlock,
@@ -326,7 +373,12 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
     auto mid = [&]() {
         if (first) {
             build_scale_table(lut);
-            __syncthreads();   // scale table ready
+            // scale table ready.  Only LDS writes need to be visible, so the
+            // barrier waits for lgkmcnt alone: the compiler's own barrier
+            // would wait for every outstanding load (the ring's first slots)
+            // whenever copies into LDS are in flight.
+            wait_lgkmcnt0();
+            asm volatile("s_barrier" ::: "memory");
             first = false;
         }
     };
@@ -347,15 +399,46 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
         }
         __syncthreads();
         const float gv = effective_global_scale(gscale[e], g_is_div);
-        for (int t = threadIdx.x; t < rows * RLD; t += W * 64) {
+        auto store_y = [&](int t, float acc) {
             const int r = t / RLD, col = t % RLD;
-            float acc = 0.f;
-#pragma unroll
-            for (int wi = 0; wi < W; ++wi) acc += red[wi][r * RLD + col];
             const int64_t n = (int64_t)u0 * kUnitN + col;
             if (n < N) y[(row0 + p0 + r) * ld_y + n] = (uint16_t)f32_to_bf16_rne(gv * acc);
+        };
+        if (S == 1) {
+            for (int t = threadIdx.x; t < rows * RLD; t += W * 64) {
+                float acc = 0.f;
+#pragma unroll
+                for (int wi = 0; wi < W; ++wi) acc += red[wi][t];
+                store_y(t, acc);
+            }
+            __syncthreads();
+            continue;
         }
-        __syncthreads();
+        // split K (dense form, one pass): publish, the last arrival reduces
+        const int64_t tile = blockIdx.x, tiles = gridDim.x;
+        float part[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int t = threadIdx.x + i * W * 64;
+            part[i] = 0.f;
+            if (t < rows * RLD) {
+#pragma unroll
+                for (int wi = 0; wi < W; ++wi) part[i] += red[wi][t];
+                store_partial(sk.partials + ((int64_t)s * tiles + tile) * kTileFloats + t, part[i]);
+            }
+        }
+        if (!split_arrive(sk.counters, tile, S, &s_flag)) return;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int t = threadIdx.x + i * W * 64;
+            if (t < rows * RLD) {
+                float acc = 0.f;   // splits added in order 0..S-1 whichever arrived last
+                for (int ss = 0; ss < S; ++ss)
+                    acc += ss == s ? part[i] : load_partial(sk.partials + ((int64_t)ss * tiles + tile) * kTileFloats + t);
+                store_y(t, acc);
+            }
+        }
+        return;
     }
 }
 

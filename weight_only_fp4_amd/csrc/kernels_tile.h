@@ -33,11 +33,6 @@ namespace nvfp4 {
 
 constexpr int kTileLDA = 136;   // bf16 per LDS row of the activation stage (128 + 8 pad)
 
-struct SplitK {
-    int S;              // K splits (grid z)
-    float* partials;    // [S][tiles][BM * units * 16] fp32 in lane order, used when S > 1
-    int* counters;      // [row tiles][unit groups], zero between calls
-};
 
 template <int MS, int NT, int UW, int KW, int D, bool GROUPED, bool KFULL>
 __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,

@@ -56,85 +56,105 @@ int64_t prescale_bytes(int64_t rows, int64_t K) { return round_up(rows * K * 2, 
 
 enum Variant { kAuto = 0, kSmall = 1, kLarge = 2 };
 
-// Small-M launch shape.  The weights stream through the vector caches with
-// non-temporal loads; measured on MI355X, a CU streams best with roughly
-// 32 KB of weight loads in flight (one kilobyte per wave and ring slot), so
-// the product workgroups x waves x ring depth is aimed at 256 CUs x 32 KB.
-// Rows 9..16 use the 16x16x32 form with two units per wave sharing one
-// activation fragment.
+// Small-M launch shape: row form mg (1, 2: 4x4x4 with that many row groups;
+// 16: 16x16x32), nt units per wave, w waves per workgroup, ring depth d, and
+// K splits S across workgroups (dense only).  Only the (mg, nt, w, d) tuples
+// listed in NVFP4_SMALL_CONFIGS are compiled.
 struct SmallShape {
-    int mg, nt, w, d;
+    int mg, nt, w, d, S;
+    int64_t groups;   // workgroups along N (units / nt)
 };
 
+// (mg, nt, w, d) for the dense form; the grouped form is always (0, 1, w, 4).
+#define NVFP4_SMALL_CONFIGS(X) \
+    X(1, 1, 1, 4) X(1, 1, 2, 4) X(1, 1, 4, 4) X(1, 1, 8, 4) X(1, 1, 16, 4) \
+    X(2, 1, 1, 4) X(2, 1, 2, 4) X(2, 1, 4, 4) X(2, 1, 8, 4) X(2, 2, 2, 4) X(2, 2, 4, 4) X(2, 2, 8, 4) \
+    X(16, 2, 4, 2) X(16, 2, 8, 2) X(16, 4, 4, 2) X(16, 4, 8, 2) X(16, 8, 4, 2) X(16, 8, 8, 2)
+
+// Is (mg, nt, w, d) one of the compiled dense shapes?
+bool small_compiled(const SmallShape& s) {
+    bool found = false;
+#define NVFP4_SMALL_FIND(MG, NT, W, D) found = found || (s.mg == MG && s.nt == NT && s.w == W && s.d == D);
+    NVFP4_SMALL_CONFIGS(NVFP4_SMALL_FIND)
+#undef NVFP4_SMALL_FIND
+    return found;
+}
+
+// Shapes from launch sweeps on MI355X (graph-replayed, weights rotated past
+// the Infinity Cache).  Rows <= 8: one unit per wave, waves sized so the
+// workgroups x waves x ring depth product aims at about 32 KB of weight
+// loads in flight per CU.  Rows 9..16 (16x16x32 form, about two VALU
+// operations per weight to decode) share each activation fragment over four
+// units per wave; the automatic choice sends those rows to the tile kernel,
+// which measured as fast.
 SmallShape small_m_shape(const Layout& L, int64_t rows, bool grouped) {
     SmallShape s;
-    s.mg = grouped ? 0 : (rows <= 4 ? 1 : rows <= 8 ? 2 : 4);
-    s.nt = (!grouped && rows > 4 && L.NU >= 512) ? 2 : 1;
-    s.d = (s.mg == 0 || s.mg <= 2) ? 4 : 2;
-    const int64_t ctas = (L.NU + s.nt - 1) / s.nt * (grouped ? (L.E + 1) / 2 : 1);
+    s.S = 1;
+    if (grouped) {
+        s.mg = 0; s.nt = 1; s.d = 4;
+    } else if (rows <= 8) {
+        s.mg = rows <= 4 ? 1 : 2; s.nt = 1; s.d = 4;
+    } else {
+        s.mg = 16; s.nt = 4; s.d = 2; s.w = 4;
+    }
+    s.groups = (L.NU + s.nt - 1) / s.nt;
+    if (s.mg == 16) {
+        // a K split costs a device-scope publish / count / reload round trip
+        // at the end of the kernel: split only grids that fill under half
+        // of the CUs
+        while (s.S < 8 && s.groups * s.S < 128 && L.KC >= 2 * s.w * 2 * s.S) s.S *= 2;
+        return s;
+    }
+    const int64_t ctas = s.groups * (grouped ? (L.E + 1) / 2 : 1);
     s.w = 1;
-    while (s.w < 16 && ctas * (2 * s.w) * s.d <= 8192 && L.KC >= 4 * (2 * s.w)) s.w *= 2;
+    // 16 waves cap a kernel at 128 VGPRs: only the one-row-group form fits
+    const int wmax = s.mg == 1 ? 16 : 8;
+    while (s.w < wmax && ctas * (2 * s.w) * s.d <= 8192 && L.KC >= 4 * (2 * s.w)) s.w *= 2;
     if (s.w < 2 && L.KC >= 8) s.w = 2;
-    if (s.mg == 16 && s.w > 8) s.w = 8;
+    while (!grouped && s.w > 1 && !small_compiled(s)) s.w /= 2;
     return s;
 }
 
-template <int MG, int NT, int W, bool GROUPED>
-void launch_small_t(dim3 grid, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* codes,
-                    const uint8_t* scales, const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows,
-                    const int32_t* offsets, hipStream_t st) {
-    constexpr int D = (MG == 0 || MG <= 2) ? 4 : 2;   // small_m_shape's d
-    const BlobView bv = make_view(L, codes);
-    (void)scales;
+
+template <int MG, int NT, int W, int D, bool GROUPED>
+void launch_small_t(const SmallShape& s, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
+                    const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows, const int32_t* offsets,
+                    SplitK sk, hipStream_t st) {
+    const BlobView bv = make_view(L, blob);
+    const dim3 grid((unsigned)s.groups, GROUPED ? (unsigned)L.E : 1u, (unsigned)s.S);
     if (L.K % kChunkK == 0)
         hipLaunchKernelGGL((k_gemm_small_m<MG, NT, W, D, GROUPED, true>), grid, dim3(W * 64), 0, st, x, ld_x, bv,
-                           (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets);
+                           (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, sk);
     else
         hipLaunchKernelGGL((k_gemm_small_m<MG, NT, W, D, GROUPED, false>), grid, dim3(W * 64), 0, st, x, ld_x, bv,
-                           (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets);
-}
-
-template <int MG, int NT, bool GROUPED>
-void launch_small_w(int w, dim3 grid, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* codes,
-                    const uint8_t* scales, const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows,
-                    const int32_t* offsets, hipStream_t st) {
-    switch (w) {
-        case 1: launch_small_t<MG, NT, 1, GROUPED>(grid, L, x, ld_x, codes, scales, gs, g_div, y, ld_y, rows, offsets, st); break;
-        case 2: launch_small_t<MG, NT, 2, GROUPED>(grid, L, x, ld_x, codes, scales, gs, g_div, y, ld_y, rows, offsets, st); break;
-        case 4: launch_small_t<MG, NT, 4, GROUPED>(grid, L, x, ld_x, codes, scales, gs, g_div, y, ld_y, rows, offsets, st); break;
-        case 8: launch_small_t<MG, NT, 8, GROUPED>(grid, L, x, ld_x, codes, scales, gs, g_div, y, ld_y, rows, offsets, st); break;
-        default: launch_small_t<MG, NT, 16, GROUPED>(grid, L, x, ld_x, codes, scales, gs, g_div, y, ld_y, rows, offsets, st); break;
-    }
+                           (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, sk);
 }
 
 template <bool GROUPED>
-nvfp4_status launch_small(const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob, const float* gs,
-                          int g_div, uint16_t* y, int64_t ld_y, int64_t rows_dense, const int32_t* offsets,
-                          hipStream_t st) {
-    const uint8_t* codes = blob;
-    const uint8_t* scales = blob + L.code_bytes();
-    const SmallShape s = small_m_shape(L, rows_dense, GROUPED);
-    const dim3 grid((unsigned)((L.NU + s.nt - 1) / s.nt), GROUPED ? (unsigned)L.E : 1u);
-#define NVFP4_SMALL(MG, NT) \
-    launch_small_w<MG, NT, GROUPED>(s.w, grid, L, x, ld_x, codes, scales, gs, g_div, y, ld_y, rows_dense, offsets, st)
-    if (GROUPED) {
-        NVFP4_SMALL(0, 1);
-    } else if (s.nt == 1) {
-        switch (s.mg) {
-            case 1: NVFP4_SMALL(1, 1); break;
-            case 2: NVFP4_SMALL(2, 1); break;
-            case 4: NVFP4_SMALL(4, 1); break;
-            default: NVFP4_SMALL(16, 1); break;
+nvfp4_status launch_small(const SmallShape& s, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
+                          const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows_dense,
+                          const int32_t* offsets, SplitK sk, hipStream_t st) {
+    bool done = false;
+    if constexpr (GROUPED) {
+        switch (s.w) {
+            case 1: launch_small_t<0, 1, 1, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st); break;
+            case 2: launch_small_t<0, 1, 2, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st); break;
+            case 4: launch_small_t<0, 1, 4, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st); break;
+            default: launch_small_t<0, 1, 8, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st); break;
         }
+        done = true;
     } else {
-        switch (s.mg) {
-            case 1: NVFP4_SMALL(1, 2); break;
-            case 2: NVFP4_SMALL(2, 2); break;
-            case 4: NVFP4_SMALL(4, 2); break;
-            default: NVFP4_SMALL(16, 2); break;
-        }
+#define NVFP4_SMALL_DISPATCH(MG, NT, W, D)                                                                        \
+    if (!done && s.mg == MG && s.nt == NT && s.w == W && s.d == D) {                                            \
+        launch_small_t<MG, NT, W, D, false>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, rows_dense, nullptr, sk, st); \
+        done = true;                                                                                            \
     }
-#undef NVFP4_SMALL
+        NVFP4_SMALL_CONFIGS(NVFP4_SMALL_DISPATCH)
+#undef NVFP4_SMALL_DISPATCH
+    }
+    if (!done)
+        return fail(NVFP4_ERR_INVALID_ARG, "small-M GEMM: no compiled kernel for shape mg=%d nt=%d w=%d d=%d", s.mg,
+                    s.nt, s.w, s.d);
     return launched("small-M GEMM");
 }
 
@@ -182,14 +202,15 @@ struct Workspace {
     int64_t counters, partials, prescale, total;
 };
 
-Workspace workspace_layout(const TileShape* t, int64_t rows, int64_t K, bool pre) {
+// split_tiles tiles of tile_floats fp32 each, S splits (no split-K area when S == 1).
+Workspace workspace_layout(int S, int64_t split_tiles, int64_t tile_floats, int64_t rows, int64_t K, bool pre) {
     Workspace w{0, 0, 0, 0};
     int64_t off = 0;
-    if (t && t->S > 1) {
+    if (S > 1) {
         w.counters = off;
-        off += round_up(t->tiles() * 4, 256);
+        off += round_up(split_tiles * 4, 256);
         w.partials = off;
-        off += round_up((int64_t)t->S * t->tiles() * t->bm() * t->ug() * 16 * 4, 256);
+        off += round_up((int64_t)S * split_tiles * tile_floats * 4, 256);
     }
     if (pre) {
         w.prescale = off;
@@ -197,6 +218,19 @@ Workspace workspace_layout(const TileShape* t, int64_t rows, int64_t K, bool pre
     }
     w.total = off;
     return w;
+}
+
+Workspace workspace_for(const TileShape& t, int64_t rows, int64_t K, bool pre) {
+    return workspace_layout(t.S, t.tiles(), (int64_t)t.bm() * t.ug() * 16, rows, K, pre);
+}
+
+Workspace workspace_for(const SmallShape& s, int64_t rows, int64_t K, bool pre) {
+    return workspace_layout(s.S, s.groups, (int64_t)kSmallRows * 16 * s.nt, rows, K, pre);
+}
+
+SplitK split_k(int S, uint8_t* ws, const Workspace& wl) {
+    return SplitK{S, S > 1 ? reinterpret_cast<float*>(ws + wl.partials) : nullptr,
+                  S > 1 ? reinterpret_cast<int*>(ws + wl.counters) : nullptr};
 }
 
 template <int MS, int NT, int UW, int KW, int D, bool GROUPED>
@@ -217,8 +251,7 @@ nvfp4_status launch_tile(const TileShape& t, const Layout& L, const uint16_t* x,
                          const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows, const int32_t* offsets,
                          uint8_t* ws, const Workspace& wl, hipStream_t st) {
     if (t.mtiles > 65535) return fail(NVFP4_ERR_INVALID_ARG, "tile GEMM: %lld row tiles exceed the grid limit", (long long)t.mtiles);
-    SplitK sk{t.S, t.S > 1 ? reinterpret_cast<float*>(ws + wl.partials) : nullptr,
-              t.S > 1 ? reinterpret_cast<int*>(ws + wl.counters) : nullptr};
+    const SplitK sk = split_k(t.S, ws, wl);
     const BlobView bv = make_view(L, blob);
 #define NVFP4_TILE(MS, NT, UW, KW, D) \
     launch_tile_t<MS, NT, UW, KW, D, GROUPED>(t, L, x, ld_x, bv, gs, g_div, y, ld_y, rows, offsets, sk, st)
@@ -287,8 +320,12 @@ nvfp4_status apply_prescale(const void* x, int64_t& ld_x, const void* pre, int64
 
 // Workspace bytes of a dense call: enough for either kernel, with or without a pre-scale.
 int64_t dense_workspace_bytes(const Layout& L, int64_t M) {
-    const TileShape t = tile_shape(L, M, false);
-    return workspace_layout(&t, M, L.K, true).total;
+    int64_t need = workspace_for(tile_shape(L, M, false), M, L.K, true).total;
+    if (M <= kSmallRows) {
+        const int64_t small = workspace_for(small_m_shape(L, M, false), M, L.K, true).total;
+        need = small > need ? small : need;
+    }
+    return need;
 }
 
 nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void* w, const float* gs, int g_div,
@@ -302,9 +339,10 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
         return fail(NVFP4_ERR_INVALID_ARG, "%s: the small-M variant takes M <= %d (M = %lld)", fn, kSmallRows, (long long)M);
     if (M > (int64_t)1 << 31) return fail(NVFP4_ERR_INVALID_ARG, "%s: M = %lld too large", fn, (long long)M);
     const Layout L = make_layout(1, N, K);
-    const bool small = variant == kSmall || (variant == kAuto && M <= kSmallAuto);
     const TileShape t = tile_shape(L, M, false);
-    const Workspace wl = workspace_layout(small ? nullptr : &t, M, K, pre != nullptr);
+    const SmallShape sm = small_m_shape(L, M, false);
+    const bool small = variant == kSmall || (variant == kAuto && M <= kSmallAuto);
+    const Workspace wl = small ? workspace_for(sm, M, K, pre != nullptr) : workspace_for(t, M, K, pre != nullptr);
     s = check_gemm_io(fn, x, ld_x, pre, w, gs, y, ld_y, M, N, K, ws, ws_bytes, wl.total);
     if (s != NVFP4_OK) return s;
     if (M == 0) return ok();   // zero rows: nothing is launched
@@ -315,8 +353,9 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
     if (s != NVFP4_OK) return s;
     const uint8_t* blob = static_cast<const uint8_t*>(w);
     uint16_t* yo = static_cast<uint16_t*>(y);
-    return small ? launch_small<false>(L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, st)
-                 : launch_tile<false>(t, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, wsb, wl, st);
+    if (small)
+        return launch_small<false>(sm, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, split_k(sm.S, wsb, wl), st);
+    return launch_tile<false>(t, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, wsb, wl, st);
 }
 
 }  // namespace
@@ -390,7 +429,7 @@ nvfp4_status nvfp4_w4a16_gemm_variant(const void* x, int64_t ld_x, const void* p
 
 int64_t nvfp4_w4a16_grouped_gemm_workspace_bytes(int64_t R, int64_t E, int64_t N, int64_t K) {
     if (R < 0 || check_weight_shape("nvfp4_w4a16_grouped_gemm_workspace_bytes", E, N, K) != NVFP4_OK) return -1;
-    return workspace_layout(nullptr, R, K, true).total;
+    return workspace_layout(1, 0, 0, R, K, true).total;   // the grouped kernels never split K
 }
 
 nvfp4_status nvfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t* expert_offsets, const void* pre_scale,
@@ -400,7 +439,7 @@ nvfp4_status nvfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t
     const char* fn = "nvfp4_w4a16_grouped_gemm";
     nvfp4_status s = check_weight_shape(fn, E, N, K);
     if (s != NVFP4_OK) return s;
-    const Workspace wl = workspace_layout(nullptr, R, K, pre_scale != nullptr);
+    const Workspace wl = workspace_layout(1, 0, 0, R, K, pre_scale != nullptr);
     s = check_gemm_io(fn, x, ld_x, pre_scale, w_repacked, global_scales, y, ld_y, R, N, K, workspace, workspace_bytes,
                       wl.total);
     if (s != NVFP4_OK) return s;
@@ -419,7 +458,8 @@ nvfp4_status nvfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t
     const int g_div = global_scale_is_divisor != 0;
     // Few rows per expert on average: the weight stream dominates, use the small-M kernel (passes of 16 rows).
     if (R <= (int64_t)kSmallRows * E)
-        return launch_small<true>(L, xp, ld_x, blob, global_scales, g_div, yo, ld_y, 0, expert_offsets, st);
+        return launch_small<true>(small_m_shape(L, R, true), L, xp, ld_x, blob, global_scales, g_div, yo, ld_y, 0,
+                                  expert_offsets, split_k(1, wsb, wl), st);
     const TileShape t = tile_shape(L, R, true);
     return launch_tile<true>(t, L, xp, ld_x, blob, global_scales, g_div, yo, ld_y, R, expert_offsets, wsb, wl, st);
 }
