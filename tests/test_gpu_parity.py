@@ -34,8 +34,8 @@ def accept_or_fail(y, ref, what):
 
 
 def dense_variants(M: int, K: int):
-    """Every kernel variant that takes this shape: automatic, tile, small-M (M <= 16)."""
-    return [nv.VARIANT_AUTO, nv.VARIANT_LARGE_M] + ([nv.VARIANT_SMALL_M] if M <= 16 else [])
+    """Every kernel variant that takes this shape: automatic, tile, MFMA-bound, small-M (M <= 16)."""
+    return [nv.VARIANT_AUTO, nv.VARIANT_LARGE_M, nv.VARIANT_MFMA] + ([nv.VARIANT_SMALL_M] if M <= 16 else [])
 
 
 def oracle_bf16_bits(t64: np.ndarray) -> np.ndarray:
@@ -100,7 +100,7 @@ def _read_hand():
     return rows
 
 
-@pytest.mark.parametrize("variant", [nv.VARIANT_SMALL_M, nv.VARIANT_LARGE_M])
+@pytest.mark.parametrize("variant", [nv.VARIANT_SMALL_M, nv.VARIANT_LARGE_M, nv.VARIANT_MFMA])
 @pytest.mark.parametrize("case", ["H1", "H2", "H3", "H4"])
 def test_hand_cases_exact(case, variant):
     from test_oracle_pins import _hand_inputs
@@ -250,7 +250,7 @@ def test_grouped_matches_per_expert_dense_calls():
 
 # -------------------------------------------------------------- invariants --
 
-@pytest.mark.parametrize("variant", [nv.VARIANT_SMALL_M, nv.VARIANT_LARGE_M])
+@pytest.mark.parametrize("variant", [nv.VARIANT_SMALL_M, nv.VARIANT_LARGE_M, nv.VARIANT_MFMA])
 def test_scale_invariants_bit_exact(variant):
     c = synth.dense_case(16, 520, 1040, seed=41, g_stored=2688.0, g_is_divisor=True, prescale=True)
     say(f"invariants variant {variant}")
@@ -292,7 +292,7 @@ def test_zero_rows_leave_output_untouched():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("variant", [nv.VARIANT_SMALL_M, nv.VARIANT_LARGE_M])
+@pytest.mark.parametrize("variant", [nv.VARIANT_SMALL_M, nv.VARIANT_LARGE_M, nv.VARIANT_MFMA])
 def test_strided_io_and_untouched_padding(variant):
     c = synth.dense_case(5, 40, 96, seed=13)
     say(f"strided io variant {variant}")

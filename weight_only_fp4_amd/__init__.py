@@ -22,10 +22,10 @@ import torch
 
 __all__ = ["repack", "repack_bytes", "gemm", "gemm_variant", "grouped_gemm", "dequant", "lib", "Nvfp4Error",
            "workspace", "gemm_workspace_bytes",
-           "VARIANT_AUTO", "VARIANT_SMALL_M", "VARIANT_LARGE_M", "LIB_PATH"]
+           "VARIANT_AUTO", "VARIANT_SMALL_M", "VARIANT_LARGE_M", "VARIANT_MFMA", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4_w4a16.so")
-VARIANT_AUTO, VARIANT_SMALL_M, VARIANT_LARGE_M = 0, 1, 2
+VARIANT_AUTO, VARIANT_SMALL_M, VARIANT_LARGE_M, VARIANT_MFMA = 0, 1, 2, 3
 _STATUS = {0: "OK", 1: "INVALID_ARG", 2: "ALIGNMENT", 3: "BUFFER_TOO_SMALL", 4: "HIP"}
 _lib = None
 

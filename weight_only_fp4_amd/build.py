@@ -7,35 +7,59 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "csrc", "nvfp4_w4a16.hip")
+CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4_w4a16.so")
 ARCH = "gfx950"
 
-HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
+COMMON = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA results in VGPRs: the small-M kernel post-processes every result with VALU FMAs
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
 ]
+# (source, extra flags)
+SOURCES = [
+    # MFMA results in VGPRs: the small-M kernel post-processes every result with VALU FMAs
+    ("nvfp4_w4a16.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+    # the MFMA-bound kernel keeps its 256 accumulators in AGPRs
+    ("nvfp4_mfma.hip", []),
+]
+NOISE = "not a recognized feature for this target"
+
+
+def _run(cmd):
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if NOISE not in l and l.strip())
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + msgs)
+    return msgs
 
 
 def build(verbose: bool = False) -> str:
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc, *HIPCC_FLAGS, SRC, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "not a recognized feature for this target"
-    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l and l.strip())
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + msgs)
-    if msgs and verbose:
-        print(msgs, flush=True)
+    with tempfile.TemporaryDirectory(prefix="nvfp4_build_") as tmpd:
+        jobs = []
+        for src, extra in SOURCES:
+            obj = os.path.join(tmpd, src + ".o")
+            jobs.append((obj, [hipcc, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]))
+        with ThreadPoolExecutor(len(jobs)) as ex:
+            outs = list(ex.map(lambda j: (j[1], _run(j[1])), jobs))
+        for cmd, msgs in outs:
+            if verbose:
+                print(" ".join(cmd), flush=True)
+                if msgs:
+                    print(msgs, flush=True)
+        tmp = LIB + ".tmp%d" % os.getpid()
+        link = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[o for o, _ in jobs], "-o", tmp]
+        msgs = _run(link)
+        if verbose:
+            print(" ".join(link), flush=True)
+            if msgs:
+                print(msgs, flush=True)
     os.replace(tmp, LIB)
     return LIB
 

@@ -13,6 +13,7 @@
 #include "kernels_aux.h"
 #include "kernels_gemm.h"
 #include "kernels_tile.h"
+#include "launch_mfma.h"
 
 using namespace nvfp4;
 
@@ -54,7 +55,7 @@ nvfp4_status check_weight_shape(const char* fn, int64_t E, int64_t N, int64_t K)
 // Bytes of the pre-scaled activation copy kept in the workspace.
 int64_t prescale_bytes(int64_t rows, int64_t K) { return round_up(rows * K * 2, 256); }
 
-enum Variant { kAuto = 0, kSmall = 1, kLarge = 2 };
+enum Variant { kAuto = 0, kSmall = 1, kLarge = 2, kMfma = 3 };
 
 // Small-M launch shape: row form mg (1, 2: 4x4x4 with that many row groups;
 // 16: 16x16x32), nt units per wave, w waves per workgroup, ring depth d, and
@@ -274,6 +275,9 @@ constexpr int64_t kMaxLdX = int64_t(1) << 23;
 // Rows at or below this use the small-M kernel when the variant is automatic.
 constexpr int64_t kSmallAuto = 4;
 
+// Rows at or above this use the MFMA-bound kernel when the variant is automatic.
+constexpr int64_t kMfmaAuto = 256;
+
 // Shared checks of the activation / output / pre-scale / workspace arguments.
 nvfp4_status check_gemm_io(const char* fn, const void* x, int64_t ld_x, const void* pre, const void* w,
                            const void* gs, const void* y, int64_t ld_y, int64_t rows, int64_t N, int64_t K,
@@ -334,7 +338,7 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
     const char* fn = "nvfp4_w4a16_gemm";
     nvfp4_status s = check_weight_shape(fn, 1, N, K);
     if (s != NVFP4_OK) return s;
-    if (variant < kAuto || variant > kLarge) return fail(NVFP4_ERR_INVALID_ARG, "%s: unknown variant %d", fn, variant);
+    if (variant < kAuto || variant > kMfma) return fail(NVFP4_ERR_INVALID_ARG, "%s: unknown variant %d", fn, variant);
     if (variant == kSmall && M > kSmallRows)
         return fail(NVFP4_ERR_INVALID_ARG, "%s: the small-M variant takes M <= %d (M = %lld)", fn, kSmallRows, (long long)M);
     if (M > (int64_t)1 << 31) return fail(NVFP4_ERR_INVALID_ARG, "%s: M = %lld too large", fn, (long long)M);
@@ -342,7 +346,10 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
     const TileShape t = tile_shape(L, M, false);
     const SmallShape sm = small_m_shape(L, M, false);
     const bool small = variant == kSmall || (variant == kAuto && M <= kSmallAuto);
-    const Workspace wl = small ? workspace_for(sm, M, K, pre != nullptr) : workspace_for(t, M, K, pre != nullptr);
+    const bool mfma = variant == kMfma || (variant == kAuto && M >= kMfmaAuto);
+    const Workspace wl = small  ? workspace_for(sm, M, K, pre != nullptr)
+                         : mfma ? workspace_layout(1, 0, 0, M, K, pre != nullptr)
+                                : workspace_for(t, M, K, pre != nullptr);
     s = check_gemm_io(fn, x, ld_x, pre, w, gs, y, ld_y, M, N, K, ws, ws_bytes, wl.total);
     if (s != NVFP4_OK) return s;
     if (M == 0) return ok();   // zero rows: nothing is launched
@@ -355,6 +362,11 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
     uint16_t* yo = static_cast<uint16_t*>(y);
     if (small)
         return launch_small<false>(sm, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, split_k(sm.S, wsb, wl), st);
+    if (mfma) {
+        const hipError_t e = launch_gemm_mfma(L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, st);
+        if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "%s: MFMA GEMM launch failed: %s", fn, hipGetErrorString(e));
+        return ok();
+    }
     return launch_tile<false>(t, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, wsb, wl, st);
 }
 
