@@ -136,6 +136,16 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
     __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
 
+// A pointer the compiler must keep in scalar registers: every lane holds the
+// same value, and passing it through readfirstlane stops the compiler from
+// folding a per-lane offset into a loop-invariant 64-bit vector address.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+}
+
 // Global scale as used in the epilogue: the stored value, or its correctly
 // rounded fp32 reciprocal when it is stored as a divisor.
 __device__ __forceinline__ float effective_global_scale(float stored, int is_divisor) {

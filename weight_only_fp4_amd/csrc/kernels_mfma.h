@@ -27,13 +27,34 @@ namespace nvfp4 {
 
 constexpr int kMfmaBM = 128;                   // rows per workgroup tile
 constexpr int kMfmaStage = kMfmaBM * 256;      // LDS bytes of one staged activation chunk
-constexpr int kMfmaLds = 2 * kMfmaStage;       // double buffer
+
+// LDS address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Asynchronous copy global -> LDS: lane l moves the 16 (4) bytes at
+// base + voff (base wave-uniform) to LDS address lds + 16 l (4 l).  Written
+// as inline assembly so that the compiler, which cannot tell which LDS bytes
+// such a copy writes, does not wait for every copy in flight before each LDS
+// read; the kernel waits for its own copies (vmcnt) before the barrier that
+// publishes them.  M0 carries the LDS base and needs one wait state.
+__device__ __forceinline__ void lds_copy16(uint32_t lds, const uint8_t* base, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(uint32_t lds, const uint8_t* base, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
 
 template <int NT, int WN, bool KFULL>
 __global__ void __launch_bounds__(WN * 64) k_gemm_mfma(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv, int NU,
                                                    int KC, int K, int N, const float* __restrict__ gscale,
                                                    int g_is_div, uint16_t* __restrict__ y, int64_t ld_y, int M) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[2][kMfmaStage];            // activations
+    __shared__ __attribute__((aligned(16))) uint8_t wcodes[2][WN][NT * kCodeBlock];   // per-wave weights
+    __shared__ __attribute__((aligned(16))) uint8_t wscale[2][WN][NT * kScaleBlock];
     __shared__ float2 lut[256];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -56,26 +77,25 @@ __global__ void __launch_bounds__(WN * 64) k_gemm_mfma(const uint16_t* __restric
         const int grow = m0 + row < M ? m0 + row : M - 1;
         a_src[k] = (uint32_t)(((int64_t)grow * ld_x + (q ^ (row & 15)) * 8) * 2);
     }
-    const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
+    const uint8_t* xb = uniform_ptr(reinterpret_cast<const uint8_t*>(x));
     auto copy_a = [&](int c, int buf) {
+        const uint32_t dst = lds_addr(stage[buf]);
 #pragma unroll
         for (int k = 0; k < kCopiesPerWave; ++k) {
             const int i = (w + WN * k) < kCopies ? w + WN * k : w, row = 4 * i + (lane >> 4);
             uint32_t off = a_src[k] + (uint32_t)(c * kChunkK * 2);
             if (!KFULL && c * kChunkK + (q ^ (row & 15)) * 8 >= K) off = a_src[k] - (q ^ (row & 15)) * 16;   // k = 0 of the row
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xb + off),
-                                             (__attribute__((address_space(3))) void*)(smem + buf * kMfmaStage + i * 1024),
-                                             16, 0, 0);
+            lds_copy16(dst + i * 1024, xb, off);
         }
     };
     // zero the staged pieces of the last chunk that lie at k >= K (their
     // copies read k = 0 of the row)
-    auto zero_tail = [&](int buf) {
+    auto zero_tail = [&](uint8_t* dst) {
         const int c = KC - 1;
         for (int t = tid; t < kMfmaBM * 16; t += WN * 64) {
             const int row = t >> 4, slot = t & 15;
             if (c * kChunkK + (slot ^ (row & 15)) * 8 >= K)
-                *reinterpret_cast<uint4*>(smem + buf * kMfmaStage + row * 256 + slot * 16) = make_uint4(0u, 0u, 0u, 0u);
+                *reinterpret_cast<uint4*>(dst + row * 256 + slot * 16) = make_uint4(0u, 0u, 0u, 0u);
         }
     };
 
@@ -89,17 +109,88 @@ __global__ void __launch_bounds__(WN * 64) k_gemm_mfma(const uint16_t* __restric
         sb[j] = bv.scales + blk * kScaleBlock;
     }
     const int64_t cstr = bv.chunk_stride * kCodeBlock;
+    // Weight copies of a chunk go to the wave's own LDS slice (no other wave
+    // reads it, so only this wave's copies have to be waited for): NT code
+    // blocks of 1 KB (lane l moves bytes 16 l .. 16 l + 15) and NT / 2 scale
+    // copies of 256 B (lanes 0..31 move unit 2 p's 128-byte block, lanes
+    // 32..63 unit 2 p + 1's).
+    static_assert(NT % 2 == 0, "scale copies move two units");
     const uint32_t lane16 = (uint32_t)(lane * 16);
-    struct BRegs {
-        uint4 cw[NT];
-        uint32_t sw[NT];
+    // scale copy p: uniform base = the lower of the two blocks, per-lane
+    // 32-bit offsets (so the copies use scalar-base addressing)
+    const uint8_t* s_base[NT / 2];
+    uint32_t s_off[NT / 2];
+#pragma unroll
+    for (int p = 0; p < NT / 2; ++p) {
+        const uint8_t* lo = sb[2 * p] < sb[2 * p + 1] ? sb[2 * p] : sb[2 * p + 1];
+        s_base[p] = lo;
+        s_off[p] = (uint32_t)((lane < 32 ? sb[2 * p] : sb[2 * p + 1]) - lo) + (uint32_t)((lane & 31) * 4);
+    }
+    auto copy_b = [&](int c, int buf) {
+        const int64_t co = (int64_t)c * cstr;
+        const uint32_t codes = lds_addr(wcodes[buf][w]), scl = lds_addr(wscale[buf][w]);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) lds_copy16(codes + j * kCodeBlock, uniform_ptr(cb[j] + co), lane16);
+#pragma unroll
+        for (int p = 0; p < NT / 2; ++p) lds_copy4(scl + p * 2 * kScaleBlock, uniform_ptr(s_base[p] + (co >> 3)), s_off[p]);
     };
-    auto load_b = [&](BRegs& b, int c) {
+
+    // ---- contraction of one chunk as 32 issue groups f = 8 t + ms (MFMA
+    // step t, row block ms).  Group f issues the LDS read of activation
+    // fragment f + 2 (three-slot ring), the NT MFMAs of fragment f against
+    // the B fragments of step t, and a slice of the VALU work for step t + 1:
+    // in steps 0..2 half a unit's decode (8 VALU per 4 MFMAs); in step 3 the
+    // next chunk's code blocks and scales are read from LDS and its step-0
+    // fragments decoded.  A scheduling fence closes every group, so each
+    // MFMA has VALU work beside it and each LDS read two groups of lead.
+    static_assert(NT == 4, "the issue groups spread 4 units' decode over 8 row blocks");
+    uint4 cw[NT];             // the lane's 16 code bytes of each unit, this chunk
+    float s0[NT], s1[NT];     // full scales of the lane's two 16-k blocks, per unit
+    uint4 bfa[NT], bfb[NT];   // B fragments: even steps in bfa, odd steps in bfb
+    uint32_t sp[NT];
+    float2 l0[NT], l1[NT];
+
+    auto read_b = [&](int buf) {   // code blocks and scale pairs of a staged chunk
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            b.cw[j] = load_stream_u4(cb[j] + (int64_t)c * cstr + lane16);
-            b.sw[j] = load_scale_dword(sb[j] + (((int64_t)c * cstr) >> 3), lane);
+            cw[j] = *reinterpret_cast<const uint4*>(wcodes[buf][w] + j * kCodeBlock + lane16);
+            sp[j] = *reinterpret_cast<const uint16_t*>(wscale[buf][w] + j * kScaleBlock + lane * 2);
         }
+    };
+    auto lut_b = [&]() {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            l0[j] = lut[sp[j] & 0xFFu];
+            l1[j] = lut[sp[j] >> 8];
+        }
+    };
+    auto scales_b = [&]() {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            s0[j] = __uint_as_float(__float_as_uint(l0[j].x) & 0x7F800000u) * l0[j].y;
+            s1[j] = __uint_as_float(__float_as_uint(l1[j].x) & 0x7F800000u) * l1[j].y;
+        }
+    };
+    // half h (elements 4 h .. 4 h + 3) of unit j's B fragment for step t
+    auto decode_half = [&](int t, int j, int h, uint4& out) {
+        const uint32_t d = t == 0 ? cw[j].x : t == 1 ? cw[j].y : t == 2 ? cw[j].z : cw[j].w;
+        const float sc = t < 2 ? s0[j] : s1[j];
+        const f32x2 p = h == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0)
+                               : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
+        const f32x2 q = h == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1)
+                               : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
+        const uint32_t lo = pack_hi_halves(p.x * sc, p.y * sc), hi = pack_hi_halves(q.x * sc, q.y * sc);
+        if (h == 0) {
+            out.x = lo;
+            out.y = hi;
+        } else {
+            out.z = lo;
+            out.w = hi;
+        }
+    };
+    auto decode_full = [&](int t, int j, uint4& out) {
+        decode_half(t, j, 0, out);
+        decode_half(t, j, 1, out);
     };
 
     f32x4 acc[8][NT];
@@ -108,60 +199,76 @@ __global__ void __launch_bounds__(WN * 64) k_gemm_mfma(const uint16_t* __restric
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[ms][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // One chunk: four MFMA steps; per step the B fragments of the wave's NT
-    // units are decoded, then 8 x NT MFMAs run.  Two waves share each SIMD,
-    // so one wave's decode overlaps the other's MFMAs.
-    auto compute = [&](const BRegs& b, int buf) {
-        float s0[NT], s1[NT];
+    auto frag = [&](const uint8_t* a, int f) {   // activation fragment f = 8 t + ms
+        const int t = f >> 3, ms = f & 7;
+        return *reinterpret_cast<const uint4*>(a + (16 * ms + r) * 256 + (((4 * g + t) ^ r) << 4));
+    };
+    auto chunk = [&](int c, int buf) {
+        const uint8_t* a = stage[buf];
+        uint4 af[3];
+        af[0] = frag(a, 0);
+        af[1] = frag(a, 1);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const uint32_t sp = scale_pair(b.sw[j], lane);
-            const float2 l0 = lut[sp & 0xFFu], l1 = lut[(sp >> 8) & 0xFFu];
-            s0[j] = __uint_as_float(__float_as_uint(l0.x) & 0x7F800000u) * l0.y;
-            s1[j] = __uint_as_float(__float_as_uint(l1.x) & 0x7F800000u) * l1.y;
-        }
-        const uint8_t* abase = smem + buf * kMfmaStage + r * 256;
+        for (int f = 0; f < 32; ++f) {
+            const int t = f >> 3, ms = f & 7;
+            if (f + 2 < 32) af[(f + 2) % 3] = frag(a, f + 2);
+            const uint4* bf = (t & 1) ? bfb : bfa;
+            uint4* nb = (t & 1) ? bfa : bfb;   // step t + 1's fragments
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            bf16x8 bf[NT];
+            for (int j = 0; j < NT; ++j)
+                acc[ms][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uint4_to_bf16x8(af[f % 3]), uint4_to_bf16x8(bf[j]),
+                                                                    acc[ms][j], 0, 0, 0);
+            if (t < 3) {
+                decode_half(t + 1, ms >> 1, ms & 1, nb[ms >> 1]);
+            } else if (ms == 0) {
+                // this wave's copies of chunk c + 1 landed.  In the last
+                // chunk the other stage holds chunk c - 1: the reads and
+                // decodes below run anyway (their results are not used), so
+                // that none of their registers has to live across chunks.
+                __builtin_amdgcn_s_waitcnt(0);
+                read_b(buf ^ 1);
+            } else if (ms == 1) {
+                lut_b();
+            } else if (ms == 2) {
+                scales_b();
+            } else if (ms < 7) {
+                decode_full(0, ms - 3, nb[ms - 3]);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
-                const uint32_t d = t == 0 ? b.cw[j].x : t == 1 ? b.cw[j].y : t == 2 ? b.cw[j].z : b.cw[j].w;
-                bf[j] = uint4_to_bf16x8(decode8_bf16(d, t < 2 ? s0[j] : s1[j]));
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
             }
-#pragma unroll
-            for (int ms = 0; ms < 8; ++ms) {
-                const bf16x8 af = uint4_to_bf16x8(
-                    *reinterpret_cast<const uint4*>(abase + ms * 16 * 256 + (((4 * g + t) ^ r) << 4)));
-#pragma unroll
-                for (int j = 0; j < NT; ++j)
-                    acc[ms][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[ms][j], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);   // keep each step's fragments local (register pressure)
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // ---- chunk pipeline: one loop body per chunk, so the accumulators keep
-    // one register assignment (an unrolled pair of bodies made the compiler
-    // shuffle them between register files); the next chunk's weight
-    // registers are copied into place once they have landed
-    BRegs bc, bn;
+    // ---- chunk pipeline.  Chunk c is contracted from stage c & 1; the copies
+    // of chunk c + 1 into the other stage are issued first and waited for in
+    // the last MFMA step.  One barrier per chunk.
     copy_a(0, 0);
-    load_b(bc, 0);
+    copy_b(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
-    if (!KFULL && KC == 1) zero_tail(0);
+    if (!KFULL && KC == 1) zero_tail(stage[0]);
     __syncthreads();
+    read_b(0);
+    lut_b();
+    scales_b();
+#pragma unroll
+    for (int j = 0; j < NT; ++j) decode_full(0, j, bfa[j]);
     for (int c = 0; c < KC; ++c) {
         const int buf = c & 1;
         if (c + 1 < KC) {
             copy_a(c + 1, buf ^ 1);
-            load_b(bn, c + 1);
+            copy_b(c + 1, buf ^ 1);
         }
-        compute(bc, buf);
-        __builtin_amdgcn_s_waitcnt(0);   // chunk c + 1 landed (issued before chunk c was contracted)
-        if (!KFULL && c + 1 == KC - 1) zero_tail(buf ^ 1);
-        __syncthreads();                 // every wave is done with this buffer and sees the next
-        bc = bn;
+        chunk(c, buf);
+        if (!KFULL && c + 1 == KC - 1) zero_tail(stage[buf ^ 1]);
+        // every wave is done with stage `buf`, and the activation copies into
+        // the other stage (waited for above by each wave) are published
+        wait_lgkmcnt0();
+        asm volatile("s_barrier" ::: "memory");
     }
 
     // ---- epilogue: lane (r, g) holds rows 16 ms + 4 g + i of column 16 (u_w + j) + r

@@ -12,12 +12,8 @@ constexpr int kMfmaWN = 8;   // waves per workgroup (two per SIMD): 128 x 512 ou
 template <bool KFULL>
 static hipError_t launch_mfma_k(const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob, const float* gs,
                                 int g_div, uint16_t* y, int64_t ld_y, int64_t M, hipStream_t st) {
-    // 128 KB of dynamic LDS (the double-buffered activation chunk) has to be enabled per kernel
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_mfma<kMfmaNT, kMfmaWN, KFULL>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kMfmaLds);
-    if (e != hipSuccess) return e;
     const dim3 grid((unsigned)((L.NU + kMfmaNT * kMfmaWN - 1) / (kMfmaNT * kMfmaWN)), (unsigned)((M + kMfmaBM - 1) / kMfmaBM));
-    hipLaunchKernelGGL((k_gemm_mfma<kMfmaNT, kMfmaWN, KFULL>), grid, dim3(kMfmaWN * 64), kMfmaLds, st, x, ld_x, make_view(L, blob), (int)L.NU,
+    hipLaunchKernelGGL((k_gemm_mfma<kMfmaNT, kMfmaWN, KFULL>), grid, dim3(kMfmaWN * 64), 0, st, x, ld_x, make_view(L, blob), (int)L.NU,
                        (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, (int)M);
     return hipGetLastError();
 }

@@ -276,7 +276,7 @@ constexpr int64_t kMaxLdX = int64_t(1) << 23;
 constexpr int64_t kSmallAuto = 4;
 
 // Rows at or above this use the MFMA-bound kernel when the variant is automatic.
-constexpr int64_t kMfmaAuto = 256;
+constexpr int64_t kMfmaAuto = 512;
 
 // Shared checks of the activation / output / pre-scale / workspace arguments.
 nvfp4_status check_gemm_io(const char* fn, const void* x, int64_t ld_x, const void* pre, const void* w,
