@@ -1,106 +1,175 @@
 // Dense GEMM for many rows (prefill-sized M): MFMA-bound.
 //
-//   Workgroup tile 128 rows x 16 NT WN columns: WN waves side by side, each
-//   owning all 128 rows and NT units (16 NT columns) as 8 x NT tiles of
-//   16 x 16 (v_mfma_f32_16x16x32_bf16, fp32 accumulators in AGPRs).  The
-//   tile is wide in N because an activation byte costs 2 B per element and a
-//   weight byte 0.5625: with 512 columns per workgroup each staged activation
-//   chunk feeds 8 waves.  K advances one 128-wide chunk at a time:
-//     - the activation chunk (128 rows x 256 bytes = 32 KB) is copied to LDS
-//       with global_load_lds_dwordx4 (1 KB per copy: four rows), double
-//       buffered, in the XOR-swizzled layout of the other kernels (slot q of
-//       a 256-byte row holds piece q ^ (row & 15)), so every fragment read is
-//       a conflict-free ds_read_b128;
-//     - each wave loads its NT units' code blocks and scale pairs into
-//       registers (one 128-bit and one 32-bit load per unit and lane) and
-//       decodes them into exact bf16 B fragments (decode8_bf16);
-//     - the loads of chunk c + 1 are issued before chunk c is contracted, so
-//       the one barrier per chunk finds them landed.
-//   The 32 K slots of an MFMA step map to k = 32 g + 8 t + e (lane group g,
-//   step t, element e) on both operands, as in the tile kernel.
+//   One wave per SIMD, four per workgroup.  A wave owns 16 MS rows x 64
+//   columns (NT = 4 units) as MS x 4 tiles of 16 x 16, contracted with
+//   v_mfma_f32_16x16x32_bf16; a workgroup owns 16 MS rows x 256 columns.
+//   The cost that bounds this kernel beside the MFMAs is decoding the weights
+//   (about two VALU per decoded element); a decoded B fragment feeds MS
+//   MFMAs, so the tall wave tile (MS = 16: 256 rows, 256 accumulators, which
+//   needs the register file of a wave that has its SIMD to itself) halves the
+//   decode per MFMA of a 128-row tile.
+//
+//   K advances one 128-wide chunk at a time:
+//     - the activation chunk (16 MS rows x 256 bytes) is copied into LDS with
+//       asynchronous global -> LDS copies, double buffered, in the
+//       XOR-swizzled layout (slot q of a 256-byte row holds piece q ^ (row &
+//       15)), so every fragment read is a conflict-free ds_read_b128;
+//     - each wave loads its four units' code blocks and scale pairs straight
+//       into registers, one chunk ahead, and decodes them into exact bf16
+//       fragments;
+//     - the chunk is issued as 4 MS groups (MFMA step t, row block ms): the
+//       LDS read of the fragment three groups ahead, the four MFMAs of the
+//       group, and a slice of the next step's decode, closed by a
+//       scheduling fence, so that every MFMA has independent work beside it.
+//   The MFMA takes the weights as its first operand, so the accumulators hold
+//   the transposed tile: a lane ends with four adjacent output columns of one
+//   row (one 8-byte store).  The 32 K slots of a step map to k = 32 g + 8 t +
+//   e (lane group g, step t, element e) on both operands.
 #pragma once
+#include <type_traits>
+
 #include "decode.h"
 #include "kernels_gemm.h"
 #include "layout.h"
 
 namespace nvfp4 {
 
-constexpr int kMfmaBM = 128;                   // rows per workgroup tile
-constexpr int kMfmaStage = kMfmaBM * 256;      // LDS bytes of one staged activation chunk
+constexpr int kMfmaNT = 4;                                 // units per wave
+constexpr int kMfmaWN = 4;                                 // waves per workgroup, one per SIMD
+constexpr int kMfmaUnits = kMfmaNT * kMfmaWN;              // units per workgroup tile (256 columns)
+constexpr int kMfmaTileRows = 256;                         // rows of a whole tile (MS = 16)
 
 // LDS address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Asynchronous copy global -> LDS: lane l moves the 16 (4) bytes at
-// base + voff (base wave-uniform) to LDS address lds + 16 l (4 l).  Written
-// as inline assembly so that the compiler, which cannot tell which LDS bytes
-// such a copy writes, does not wait for every copy in flight before each LDS
-// read; the kernel waits for its own copies (vmcnt) before the barrier that
-// publishes them.  M0 carries the LDS base and needs one wait state.
+// Asynchronous copy global -> LDS: lane l moves the 16 bytes at base + voff
+// (base wave-uniform) to LDS address lds + 16 l.  Written as inline assembly
+// so that the compiler, which cannot tell which LDS bytes such a copy
+// writes, does not wait for every copy in flight before each LDS read; the
+// kernel waits for its own copies (vmcnt) before the barrier that publishes
+// them.  M0 carries the LDS base and needs one wait state.
 __device__ __forceinline__ void lds_copy16(uint32_t lds, const uint8_t* base, uint32_t voff) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
                  : "memory", "m0");
 }
-__device__ __forceinline__ void lds_copy4(uint32_t lds, const uint8_t* base, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base)
-                 : "memory", "m0");
+
+// acc += A . B for one 16 x 16 x 32 bf16 step, accumulating in place in
+// accumulation registers.  Written as inline assembly because the compiler,
+// left to itself, renames most accumulators of a 256-accumulator tile in
+// every chunk and copies them back through VGPRs at the loop edge.  The
+// compiler cannot see this hazard-wise: its operands are produced at least
+// one issue group before use, and the accumulators are read only after the
+// drain in mfma_drain.
+__device__ __forceinline__ void mfma_acc(f32x4& acc, const uint4& a, const uint4& b) {
+    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+        : "+a"(acc)
+        : "v"(__builtin_bit_cast(u32x4v, a)), "v"(__builtin_bit_cast(u32x4v, b)));
+}
+// Wait states after the last MFMA before its accumulators are read (more
+// than the longest MFMA pipeline).
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+// Streaming (non-temporal) loads through a pointer known to be global
+// memory: a pointer rebuilt by uniform_ptr has lost its address space, and a
+// flat load would also count against the LDS wait counter.
+typedef const __attribute__((address_space(1))) u32x4v* global_u32x4_ptr;
+typedef const __attribute__((address_space(1))) uint32_t* global_u32_ptr;
+__device__ __forceinline__ uint4 global_stream_u4(const uint8_t* p) {
+    const u32x4v t = __builtin_nontemporal_load((global_u32x4_ptr)p);
+    return make_uint4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ uint32_t global_stream_u32(const uint8_t* p) {
+    return __builtin_nontemporal_load((global_u32_ptr)p);
 }
 
-template <int NT, int WN, bool KFULL>
-__global__ void __launch_bounds__(WN * 64) k_gemm_mfma(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv, int NU,
-                                                   int KC, int K, int N, const float* __restrict__ gscale,
-                                                   int g_is_div, uint16_t* __restrict__ y, int64_t ld_y, int M) {
-    __shared__ __attribute__((aligned(16))) uint8_t stage[2][kMfmaStage];            // activations
-    __shared__ __attribute__((aligned(16))) uint8_t wcodes[2][WN][NT * kCodeBlock];   // per-wave weights
-    __shared__ __attribute__((aligned(16))) uint8_t wscale[2][WN][NT * kScaleBlock];
-    __shared__ float2 lut[256];
+// Calls f(std::integral_constant<int, i>) for i = I .. N - 1: a loop whose
+// index is a compile-time constant in every iteration (register arrays
+// indexed by it stay in registers however large the body).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// Output tile (mt, nt) at position t of the tile order, which walks four
+// tile rows at a time across all tile columns (the workgroups running
+// together then share activation rows and weight columns in the caches).
+__device__ __forceinline__ void mfma_tile(int t, int MT, int NTn, int& mt, int& nt) {
+    constexpr int kGroupRows = 4;
+    const int grp = t / (kGroupRows * NTn), in = t % (kGroupRows * NTn);
+    const int rows = MT - grp * kGroupRows < kGroupRows ? MT - grp * kGroupRows : kGroupRows;
+    mt = grp * kGroupRows + in % rows;
+    nt = in / rows;
+}
+
+// Workgroup id covers part id % P (P = 16 / MS row parts of 16 MS rows) of
+// tile t0 + id / P of the tile order (whole tiles are 256 rows x 256 columns).
+template <int MS, bool KFULL>
+__global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
+                                                        int NU, int KC, int K, int N, const float* __restrict__ gscale,
+                                                        int g_is_div, uint16_t* __restrict__ y, int64_t ld_y, int M,
+                                                        int t0, int vec_store) {
+    constexpr int NT = kMfmaNT, WN = kMfmaWN;
+    constexpr int kRows = 16 * MS;              // rows of this workgroup
+    constexpr int kStage = kRows * 256;         // LDS bytes of one staged activation chunk
+    constexpr int kParts = kMfmaTileRows / kRows;
+    constexpr int kGroups = 4 * MS;             // issue groups per chunk
+    constexpr int kAhead = 3;                   // fragment reads in flight
+    static_assert(MS == 8 || MS == 16, "row blocks per wave");
+    __shared__ __attribute__((aligned(16))) uint8_t stage[2][kStage];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    constexpr int kCopies = kMfmaBM / 4;                  // 1 KB activation copies per chunk
-    constexpr int kCopiesPerWave = (kCopies + WN - 1) / WN;
-    const int m0 = (int)blockIdx.y * kMfmaBM;
-    const int u_w = (int)blockIdx.x * NT * WN + NT * w;   // this wave's first unit
 
-    build_scale_table(lut);
+    int mt, nt;
+    mfma_tile(t0 + (int)blockIdx.x / kParts, (M + kMfmaTileRows - 1) / kMfmaTileRows, (NU + kMfmaUnits - 1) / kMfmaUnits,
+              mt, nt);
+    const int m0 = mt * kMfmaTileRows + ((int)blockIdx.x % kParts) * kRows;
+    if (m0 >= M) return;                        // a lower part past the last row (uniform per workgroup)
+    const int u_w = nt * kMfmaUnits + NT * w;   // this wave's first unit
 
-    // ---- activation copies: copy i (0 .. kCopies - 1) of a chunk moves rows
-    // 4 i .. 4 i + 3; wave w issues copies w, w + WN, ..; lane l takes row
+    // ---- activation copies: copy i (0 .. 4 MS - 1) of a chunk moves rows
+    // 4 i .. 4 i + 3; wave w issues copies w, w + 4, ..; lane l takes row
     // 4 i + (l >> 4) and the piece stored in slot l & 15.  Rows past M read
-    // row M - 1 (never stored); copies past kCopies repeat copy w.
+    // row M - 1 (never stored).
+    constexpr int kCopiesPerWave = kRows / 4 / WN;
     const int q = lane & 15;
     uint32_t a_src[kCopiesPerWave];   // byte offset of the lane's piece in chunk 0, per copy
 #pragma unroll
     for (int k = 0; k < kCopiesPerWave; ++k) {
-        const int i = (w + WN * k) < kCopies ? w + WN * k : w, row = 4 * i + (lane >> 4);
+        const int row = 4 * (w + WN * k) + (lane >> 4);
         const int grow = m0 + row < M ? m0 + row : M - 1;
         a_src[k] = (uint32_t)(((int64_t)grow * ld_x + (q ^ (row & 15)) * 8) * 2);
     }
     const uint8_t* xb = uniform_ptr(reinterpret_cast<const uint8_t*>(x));
-    auto copy_a = [&](int c, int buf) {
-        const uint32_t dst = lds_addr(stage[buf]);
-#pragma unroll
-        for (int k = 0; k < kCopiesPerWave; ++k) {
-            const int i = (w + WN * k) < kCopies ? w + WN * k : w, row = 4 * i + (lane >> 4);
-            uint32_t off = a_src[k] + (uint32_t)(c * kChunkK * 2);
-            if (!KFULL && c * kChunkK + (q ^ (row & 15)) * 8 >= K) off = a_src[k] - (q ^ (row & 15)) * 16;   // k = 0 of the row
-            lds_copy16(dst + i * 1024, xb, off);
-        }
+    auto copy_piece = [&](int c, int buf, int k) {   // copy w + 4 k of chunk c into stage buf
+        const int i = w + WN * k, row = 4 * i + (lane >> 4);
+        uint32_t off = a_src[k] + (uint32_t)(c * kChunkK * 2);
+        if (!KFULL && c * kChunkK + (q ^ (row & 15)) * 8 >= K) off = a_src[k] - (q ^ (row & 15)) * 16;   // k = 0 of the row
+        lds_copy16(lds_addr(stage[buf]) + i * 1024, xb, off);
     };
-    // zero the staged pieces of the last chunk that lie at k >= K (their
-    // copies read k = 0 of the row)
-    auto zero_tail = [&](uint8_t* dst) {
+    auto copy_a = [&](int c, int buf) {
+#pragma unroll
+        for (int k = 0; k < kCopiesPerWave; ++k) copy_piece(c, buf, k);
+    };
+    // Zero the staged pieces of the last chunk that lie at k >= K (their
+    // copies read k = 0 of the row).  Thread t zeroes slot t & 15 of row
+    // t >> 4, which this thread's own wave copied (rows 4 i .. 4 i + 3 come
+    // from copy i, issued by wave i % 4), so its own wait covers the copy.
+    auto zero_tail = [&](int buf) {
         const int c = KC - 1;
-        for (int t = tid; t < kMfmaBM * 16; t += WN * 64) {
+        for (int t = tid; t < kRows * 16; t += WN * 64) {
             const int row = t >> 4, slot = t & 15;
             if (c * kChunkK + (slot ^ (row & 15)) * 8 >= K)
-                *reinterpret_cast<uint4*>(dst + row * 256 + slot * 16) = make_uint4(0u, 0u, 0u, 0u);
+                *reinterpret_cast<uint4*>(stage[buf] + row * 256 + slot * 16) = make_uint4(0u, 0u, 0u, 0u);
         }
     };
 
-    // ---- weight blocks of this wave's NT units (units past NU read unit 0, never stored)
-    const uint8_t* cb[NT];   // wave-uniform block bases; the lane offset is added at the load
+    // ---- weights of this wave's units (units past NU read unit 0, never stored)
+    const uint8_t* cb[NT];
     const uint8_t* sb[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -109,181 +178,187 @@ __global__ void __launch_bounds__(WN * 64) k_gemm_mfma(const uint16_t* __restric
         sb[j] = bv.scales + blk * kScaleBlock;
     }
     const int64_t cstr = bv.chunk_stride * kCodeBlock;
-    // Weight copies of a chunk go to the wave's own LDS slice (no other wave
-    // reads it, so only this wave's copies have to be waited for): NT code
-    // blocks of 1 KB (lane l moves bytes 16 l .. 16 l + 15) and NT / 2 scale
-    // copies of 256 B (lanes 0..31 move unit 2 p's 128-byte block, lanes
-    // 32..63 unit 2 p + 1's).
-    static_assert(NT % 2 == 0, "scale copies move two units");
     const uint32_t lane16 = (uint32_t)(lane * 16);
-    // scale copy p: uniform base = the lower of the two blocks, per-lane
-    // 32-bit offsets (so the copies use scalar-base addressing)
-    const uint8_t* s_base[NT / 2];
-    uint32_t s_off[NT / 2];
-#pragma unroll
-    for (int p = 0; p < NT / 2; ++p) {
-        const uint8_t* lo = sb[2 * p] < sb[2 * p + 1] ? sb[2 * p] : sb[2 * p + 1];
-        s_base[p] = lo;
-        s_off[p] = (uint32_t)((lane < 32 ? sb[2 * p] : sb[2 * p + 1]) - lo) + (uint32_t)((lane & 31) * 4);
-    }
-    auto copy_b = [&](int c, int buf) {
+    struct BRegs {
+        uint4 cw[NT];       // the lane's 16 code bytes (row l & 15, k-group l >> 4) per unit
+        uint32_t sw[NT];    // the scale dword holding the lane's two scale bytes, per unit
+    };
+    auto load_b = [&](BRegs& b, int c) {
         const int64_t co = (int64_t)c * cstr;
-        const uint32_t codes = lds_addr(wcodes[buf][w]), scl = lds_addr(wscale[buf][w]);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) lds_copy16(codes + j * kCodeBlock, uniform_ptr(cb[j] + co), lane16);
-#pragma unroll
-        for (int p = 0; p < NT / 2; ++p) lds_copy4(scl + p * 2 * kScaleBlock, uniform_ptr(s_base[p] + (co >> 3)), s_off[p]);
+        for (int j = 0; j < NT; ++j) {
+            b.cw[j] = global_stream_u4(uniform_ptr(cb[j] + co) + lane16);
+            b.sw[j] = global_stream_u32(uniform_ptr(sb[j] + (co >> 3)) + ((lane >> 1) << 2));   // lanes 2i, 2i + 1: one dword
+        }
     };
 
-    // ---- contraction of one chunk as 32 issue groups f = 8 t + ms (MFMA
-    // step t, row block ms).  Group f issues the LDS read of activation
-    // fragment f + 2 (three-slot ring), the NT MFMAs of fragment f against
-    // the B fragments of step t, and a slice of the VALU work for step t + 1:
-    // in steps 0..2 half a unit's decode (8 VALU per 4 MFMAs); in step 3 the
-    // next chunk's code blocks and scales are read from LDS and its step-0
-    // fragments decoded.  A scheduling fence closes every group, so each
-    // MFMA has VALU work beside it and each LDS read two groups of lead.
-    static_assert(NT == 4, "the issue groups spread 4 units' decode over 8 row blocks");
-    uint4 cw[NT];             // the lane's 16 code bytes of each unit, this chunk
     float s0[NT], s1[NT];     // full scales of the lane's two 16-k blocks, per unit
-    uint4 bfa[NT], bfb[NT];   // B fragments: even steps in bfa, odd steps in bfb
-    uint32_t sp[NT];
-    float2 l0[NT], l1[NT];
 
-    auto read_b = [&](int buf) {   // code blocks and scale pairs of a staged chunk
+    f32x4 acc[MS][NT];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            cw[j] = *reinterpret_cast<const uint4*>(wcodes[buf][w] + j * kCodeBlock + lane16);
-            sp[j] = *reinterpret_cast<const uint16_t*>(wscale[buf][w] + j * kScaleBlock + lane * 2);
-        }
-    };
-    auto lut_b = [&]() {
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            l0[j] = lut[sp[j] & 0xFFu];
-            l1[j] = lut[sp[j] >> 8];
-        }
-    };
-    auto scales_b = [&]() {
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            s0[j] = __uint_as_float(__float_as_uint(l0[j].x) & 0x7F800000u) * l0[j].y;
-            s1[j] = __uint_as_float(__float_as_uint(l1[j].x) & 0x7F800000u) * l1[j].y;
-        }
-    };
-    // half h (elements 4 h .. 4 h + 3) of unit j's B fragment for step t
-    auto decode_half = [&](int t, int j, int h, uint4& out) {
-        const uint32_t d = t == 0 ? cw[j].x : t == 1 ? cw[j].y : t == 2 ? cw[j].z : cw[j].w;
-        const float sc = t < 2 ? s0[j] : s1[j];
-        const f32x2 p = h == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0)
-                               : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
-        const f32x2 q = h == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1)
-                               : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
-        const uint32_t lo = pack_hi_halves(p.x * sc, p.y * sc), hi = pack_hi_halves(q.x * sc, q.y * sc);
-        if (h == 0) {
-            out.x = lo;
-            out.y = hi;
-        } else {
-            out.z = lo;
-            out.w = hi;
-        }
-    };
-    auto decode_full = [&](int t, int j, uint4& out) {
-        decode_half(t, j, 0, out);
-        decode_half(t, j, 1, out);
-    };
-
-    f32x4 acc[8][NT];
-#pragma unroll
-    for (int ms = 0; ms < 8; ++ms)
+    for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[ms][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mfma_drain();             // the zeroed accumulators are read by the first MFMAs
 
-    auto frag = [&](const uint8_t* a, int f) {   // activation fragment f = 8 t + ms
-        const int t = f >> 3, ms = f & 7;
-        return *reinterpret_cast<const uint4*>(a + (16 * ms + r) * 256 + (((4 * g + t) ^ r) << 4));
+    // ---- B fragments.  Unit u's fragment of step t is four dwords (two bf16
+    // each); dword d is decoded in four VALU operations (convert, two scale
+    // multiplies, pack), so that one operation can sit beside each MFMA.
+    uint4 bfa[NT], bfb[NT];   // even steps in bfa, odd steps in bfb
+    struct DwordJob {
+        f32x2 p;
+        float x, y;
     };
-    auto chunk = [&](int c, int buf) {
-        const uint8_t* a = stage[buf];
-        uint4 af[3];
-        af[0] = frag(a, 0);
-        af[1] = frag(a, 1);
-#pragma unroll
-        for (int f = 0; f < 32; ++f) {
-            const int t = f >> 3, ms = f & 7;
-            if (f + 2 < 32) af[(f + 2) % 3] = frag(a, f + 2);
-            const uint4* bf = (t & 1) ? bfb : bfa;
-            uint4* nb = (t & 1) ? bfa : bfb;   // step t + 1's fragments
-#pragma unroll
-            for (int j = 0; j < NT; ++j)
-                acc[ms][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uint4_to_bf16x8(af[f % 3]), uint4_to_bf16x8(bf[j]),
-                                                                    acc[ms][j], 0, 0, 0);
-            if (t < 3) {
-                decode_half(t + 1, ms >> 1, ms & 1, nb[ms >> 1]);
-            } else if (ms == 0) {
-                // this wave's copies of chunk c + 1 landed.  In the last
-                // chunk the other stage holds chunk c - 1: the reads and
-                // decodes below run anyway (their results are not used), so
-                // that none of their registers has to live across chunks.
-                __builtin_amdgcn_s_waitcnt(0);
-                read_b(buf ^ 1);
-            } else if (ms == 1) {
-                lut_b();
-            } else if (ms == 2) {
-                scales_b();
-            } else if (ms < 7) {
-                decode_full(0, ms - 3, nb[ms - 3]);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+    auto set_dword = [](uint4& v, int d, uint32_t val) {
+        if (d == 0) v.x = val;
+        else if (d == 1) v.y = val;
+        else if (d == 2) v.z = val;
+        else v.w = val;
+    };
+    // operation op (0..3) of decoding dword d (unit d >> 2, dword d & 3) of step t from b into nb
+    auto dword_op = [&](const BRegs& b, int t, int d, int op, DwordJob& jb, uint4* nb) {
+        const int u = d >> 2, e = d & 3;
+        const uint32_t cw = t == 0 ? b.cw[u].x : t == 1 ? b.cw[u].y : t == 2 ? b.cw[u].z : b.cw[u].w;
+        const float sc = t < 2 ? s0[u] : s1[u];
+        if (op == 0) {
+            jb.p = e == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0)
+                 : e == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1)
+                 : e == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2)
+                          : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3);
+        } else if (op == 1) {
+            jb.x = jb.p.x * sc;
+        } else if (op == 2) {
+            jb.y = jb.p.y * sc;
+        } else {
+            set_dword(nb[u], e, pack_hi_halves(jb.x, jb.y));
+        }
+    };
+    auto scale_op = [&](const BRegs& b, int u) {   // scales of unit u of chunk b
+        const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(scale_pair(b.sw[u], lane), 1.0f, false);   // E4M3 x 2
+        s0[u] = v.x;
+        s1[u] = v.y;
+    };
+
+    // ---- activation fragments: group f = MS t + ms reads fragment f + 3
+    // into slot (f + 3) % 8 of a ring that spans chunk boundaries (the first
+    // three fragments of chunk c + 1 are read while chunk c's last three
+    // groups run).
+    constexpr int kRing = 8;
+    static_assert(kGroups % kRing == 0, "ring slots line up across chunks");
+    uint4 af[kRing];
+    auto frag = [&](int buf, int f) {
+        const int t = f / MS, ms = f % MS;
+        return *reinterpret_cast<const uint4*>(stage[buf] + (16 * ms + r) * 256 + (((4 * g + t) ^ r) << 4));
+    };
+
+    // One issue group: the read of fragment f + 3 (if it is in this chunk),
+    // then four MFMAs, each followed by its share of the VALU work and a
+    // scheduling fence.  VALU work: in steps 0..2 the decode of step t + 1
+    // (16 / MS dwords per group); in step 3 the next chunk's scales (group 0)
+    // and its step-0 decode (groups 1 .. MS - 1).
+    auto group = [&](auto fc, int c, int buf, const BRegs& b, const BRegs& bn) {
+        constexpr int f = decltype(fc)::value, t = f / MS, ms = f % MS;
+        if constexpr (f + kAhead < kGroups) af[(f + kAhead) % kRing] = frag(buf, f + kAhead);
+        // the activation copies of chunk c + 1 (into the other stage, free
+        // since the last barrier) are spread over the first groups
+        if constexpr (f < kCopiesPerWave) {
+            if (c + 1 < KC) copy_piece(c + 1, buf ^ 1, f);
+        }
+        uint4* bf = (t & 1) ? bfb : bfa;
+        uint4* nb = (t & 1) ? bfa : bfb;
+        constexpr int d_lo = t < 3 ? ms * 16 / MS : (ms == 0 ? 0 : ((ms - 1) * 16 + MS - 2) / (MS - 1));
+        constexpr int d_hi = t < 3 ? (ms + 1) * 16 / MS : (ms == 0 ? 0 : (ms * 16 + MS - 2) / (MS - 1));
+        DwordJob jobs[4];
+        static_for<0, NT>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            mfma_acc(acc[ms][j], bf[j], af[f % kRing]);
+            if constexpr (t < 3) {
+                static_for<d_lo, d_hi>([&](auto dc) {
+                    constexpr int d = decltype(dc)::value;
+                    dword_op(b, t + 1, d, j, jobs[d - d_lo], nb);
+                });
+            } else if constexpr (ms == 0) {
+                scale_op(bn, j);
+            } else {
+                static_for<d_lo, d_hi>([&](auto dc) {
+                    constexpr int d = decltype(dc)::value;
+                    dword_op(bn, 0, d, j, jobs[d - d_lo], nb);
+                });
             }
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
     };
 
-    // ---- chunk pipeline.  Chunk c is contracted from stage c & 1; the copies
-    // of chunk c + 1 into the other stage are issued first and waited for in
-    // the last MFMA step.  One barrier per chunk.
-    copy_a(0, 0);
-    copy_b(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    if (!KFULL && KC == 1) zero_tail(stage[0]);
-    __syncthreads();
-    read_b(0);
-    lut_b();
-    scales_b();
-#pragma unroll
-    for (int j = 0; j < NT; ++j) decode_full(0, j, bfa[j]);
-    for (int c = 0; c < KC; ++c) {
-        const int buf = c & 1;
-        if (c + 1 < KC) {
-            copy_a(c + 1, buf ^ 1);
-            copy_b(c + 1, buf ^ 1);
-        }
-        chunk(c, buf);
-        if (!KFULL && c + 1 == KC - 1) zero_tail(stage[buf ^ 1]);
-        // every wave is done with stage `buf`, and the activation copies into
-        // the other stage (waited for above by each wave) are published
+    // One chunk on stage buf with weights b; bn holds the next chunk's
+    // weights (loaded a chunk ago).  The first groups issue the activation
+    // copies of chunk c + 1.  After group kGroups - 4 the wave waits for its
+    // copies and meets the others at the barrier; then it loads the weights
+    // of chunk c + 2 (into b, free now), reads the first fragments of chunk
+    // c + 1, and runs the last three groups, whose fragments are already in
+    // registers.
+    auto chunk = [&](int c, int buf, BRegs& b, const BRegs& bn) {
+        static_for<0, kGroups - kAhead>([&](auto fc) { group(fc, c, buf, b, bn); });
+        wait_vmcnt<0>();
+        if (!KFULL && c + 1 == KC - 1) zero_tail(buf ^ 1);
         wait_lgkmcnt0();
         asm volatile("s_barrier" ::: "memory");
-    }
+        if (c + 2 < KC) load_b(b, c + 2);
+        if (c + 1 < KC) {
+            static_for<0, kAhead>([&](auto fc) {
+                constexpr int f = decltype(fc)::value;
+                af[f] = frag(buf ^ 1, f);
+            });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<kGroups - kAhead, kGroups>([&](auto fc) { group(fc, c, buf, b, bn); });
+    };
 
-    // ---- epilogue: lane (r, g) holds rows 16 ms + 4 g + i of column 16 (u_w + j) + r
+    // ---- pipeline: two chunks in flight (stages and weight register sets
+    // alternate, so the loop is unrolled by two)
+    BRegs b0, b1;
+    copy_a(0, 0);
+    load_b(b0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    if (!KFULL && KC == 1) zero_tail(0);
+    __syncthreads();
+    if (KC > 1) load_b(b1, 1);
+    static_for<0, NT>([&](auto jc) { scale_op(b0, decltype(jc)::value); });
+    static_for<0, 16>([&](auto dc) {
+        DwordJob jb;
+        static_for<0, 4>([&](auto oc) { dword_op(b0, 0, decltype(dc)::value, decltype(oc)::value, jb, bfa); });
+    });
+    static_for<0, kAhead>([&](auto fc) { af[decltype(fc)::value] = frag(0, decltype(fc)::value); });
+    int c = 0;
+    for (; c + 1 < KC; c += 2) {
+        chunk(c, 0, b0, b1);
+        chunk(c + 1, 1, b1, b0);
+    }
+    if (c < KC) chunk(c, 0, b0, b1);
+    mfma_drain();
+
+    // ---- epilogue: lane (r, g) holds, for row 16 ms + r, the four columns
+    // 16 (u_w + j) + 4 g + i
     const float gv = effective_global_scale(gscale[0], g_is_div);
-#pragma unroll
-    for (int ms = 0; ms < 8; ++ms)
+    static_for<0, MS>([&](auto msc) {
+        constexpr int ms = decltype(msc)::value;
+        const int m = m0 + 16 * ms + r;
+        if (m >= M) return;
+        uint16_t* yr = y + (int64_t)m * ld_y;
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            const int64_t n = (int64_t)(u_w + j) * kUnitN + r;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = m0 + 16 * ms + 4 * g + i;
-                if (m < M && n < N) y[(int64_t)m * ld_y + n] = (uint16_t)f32_to_bf16_rne(gv * acc[ms][j][i]);
+            const int n = (u_w + j) * kUnitN + 4 * g;
+            const uint32_t b0 = f32_to_bf16_rne(gv * acc[ms][j][0]), b1 = f32_to_bf16_rne(gv * acc[ms][j][1]);
+            const uint32_t b2 = f32_to_bf16_rne(gv * acc[ms][j][2]), b3 = f32_to_bf16_rne(gv * acc[ms][j][3]);
+            if (vec_store && n + 3 < N) {
+                *reinterpret_cast<uint2*>(yr + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+            } else {
+                if (n < N) yr[n] = (uint16_t)b0;
+                if (n + 1 < N) yr[n + 1] = (uint16_t)b1;
+                if (n + 2 < N) yr[n + 2] = (uint16_t)b2;
+                if (n + 3 < N) yr[n + 3] = (uint16_t)b3;
             }
         }
+    });
 }
 
 }  // namespace nvfp4

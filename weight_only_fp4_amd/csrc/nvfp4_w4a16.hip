@@ -363,7 +363,7 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
     if (small)
         return launch_small<false>(sm, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, split_k(sm.S, wsb, wl), st);
     if (mfma) {
-        const hipError_t e = launch_gemm_mfma(L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, st);
+        const hipError_t e = launch_gemm_mfma(mfma_plan(L, M), L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, st);
         if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "%s: MFMA GEMM launch failed: %s", fn, hipGetErrorString(e));
         return ok();
     }
