@@ -134,17 +134,18 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     // ---- activation copies: copy i (0 .. 4 MS - 1) of a chunk moves rows
     // 4 i .. 4 i + 3; wave w issues copies w, w + 4, ..; lane l takes row
     // 4 i + (l >> 4) and the piece stored in slot l & 15.  Rows past M read
-    // row M - 1 (never stored).
+    // row M - 1 (never stored).  Offsets are 32-bit from the workgroup's
+    // first row (at most 255 rows of ld_x <= 2^23 elements: below 2^32 bytes).
     constexpr int kCopiesPerWave = kRows / 4 / WN;
     const int q = lane & 15;
     uint32_t a_src[kCopiesPerWave];   // byte offset of the lane's piece in chunk 0, per copy
 #pragma unroll
     for (int k = 0; k < kCopiesPerWave; ++k) {
         const int row = 4 * (w + WN * k) + (lane >> 4);
-        const int grow = m0 + row < M ? m0 + row : M - 1;
-        a_src[k] = (uint32_t)(((int64_t)grow * ld_x + (q ^ (row & 15)) * 8) * 2);
+        const int rrow = m0 + row < M ? row : M - 1 - m0;
+        a_src[k] = (uint32_t)(((int64_t)rrow * ld_x + (q ^ (row & 15)) * 8) * 2);
     }
-    const uint8_t* xb = uniform_ptr(reinterpret_cast<const uint8_t*>(x));
+    const uint8_t* xb = uniform_ptr(reinterpret_cast<const uint8_t*>(x + (int64_t)m0 * ld_x));
     auto copy_piece = [&](int c, int buf, int k) {   // copy w + 4 k of chunk c into stage buf
         const int i = w + WN * k, row = 4 * i + (lane >> 4);
         uint32_t off = a_src[k] + (uint32_t)(c * kChunkK * 2);

@@ -183,11 +183,12 @@ TileShape tile_shape(const Layout& L, int64_t rows, bool grouped) {
         t.ms = 1; t.nt = 1; t.uw = 4; t.kw = 4; t.d = 2;
     } else if (rows <= 32) {
         t.ms = 2; t.nt = 1; t.uw = 4; t.kw = 2; t.d = 4;
-    } else if (rows <= 64) {
+    } else if (rows <= 192) {
+        // 64-row tiles: up to three row tiles still beat 128-row tiles here (measured)
         if (L.NU >= 4096) { t.ms = 4; t.nt = 4; t.uw = 4; t.kw = 1; t.d = 2; }
         else { t.ms = 4; t.nt = 1; t.uw = 4; t.kw = 4; t.d = 2; }
     } else {
-        t.ms = 8; t.nt = 2; t.uw = 8; t.kw = 1; t.d = 2; split = false;
+        t.ms = 8; t.nt = 2; t.uw = 8; t.kw = 1; t.d = 2;
     }
     t.groups = (L.NU + t.ug() - 1) / t.ug();
     t.mtiles = (rows + t.bm() - 1) / t.bm() + (grouped ? L.E : 0);
@@ -275,8 +276,11 @@ constexpr int64_t kMaxLdX = int64_t(1) << 23;
 // Rows at or below this use the small-M kernel when the variant is automatic.
 constexpr int64_t kSmallAuto = 4;
 
-// Rows at or above this use the MFMA-bound kernel when the variant is automatic.
-constexpr int64_t kMfmaAuto = 512;
+// The automatic variant uses the MFMA-bound kernel from this many rows on,
+// when the call has at least kMfmaMinTiles of its 256 x 256 tiles (with fewer
+// the chip is not filled and the tile kernel, which can split K, is faster).
+constexpr int64_t kMfmaAuto = 256;
+constexpr int64_t kMfmaMinTiles = 48;
 
 // Shared checks of the activation / output / pre-scale / workspace arguments.
 nvfp4_status check_gemm_io(const char* fn, const void* x, int64_t ld_x, const void* pre, const void* w,
@@ -346,7 +350,7 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
     const TileShape t = tile_shape(L, M, false);
     const SmallShape sm = small_m_shape(L, M, false);
     const bool small = variant == kSmall || (variant == kAuto && M <= kSmallAuto);
-    const bool mfma = variant == kMfma || (variant == kAuto && M >= kMfmaAuto);
+    const bool mfma = variant == kMfma || (variant == kAuto && M >= kMfmaAuto && mfma_plan(L, M).tiles >= kMfmaMinTiles);
     const Workspace wl = small  ? workspace_for(sm, M, K, pre != nullptr)
                          : mfma ? workspace_layout(1, 0, 0, M, K, pre != nullptr)
                                 : workspace_for(t, M, K, pre != nullptr);
