@@ -84,6 +84,24 @@ __device__ __forceinline__ uint32_t global_stream_u32(const uint8_t* p) {
     return __builtin_nontemporal_load((global_u32_ptr)p);
 }
 
+// fp32 pair -> bf16 pair (round to nearest even; NaN stays NaN), first value in the low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_t));
+}
+// Exchange rows of 16 lanes between two registers: odd rows of a with even
+// rows of b (lane_swap16), rows 2-3 of a with rows 0-1 of b (lane_swap32).
+__device__ __forceinline__ void lane_swap16(uint32_t& a, uint32_t& b) {
+    const auto v = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = v[0];
+    b = v[1];
+}
+__device__ __forceinline__ void lane_swap32(uint32_t& a, uint32_t& b) {
+    const auto v = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = v[0];
+    b = v[1];
+}
+
 // Calls f(std::integral_constant<int, i>) for i = I .. N - 1: a loop whose
 // index is a compile-time constant in every iteration (register arrays
 // indexed by it stay in registers however large the body).
@@ -338,25 +356,39 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     mfma_drain();
 
     // ---- epilogue: lane (r, g) holds, for row 16 ms + r, the four columns
-    // 16 (u_w + j) + 4 g + i
+    // 16 (u_w + j) + 4 g + i.  They are scaled, rounded to bf16 pairs, and
+    // transposed across the four lane rows g and the four units j with two
+    // lane-swap rounds, after which lane row g holds the 16 adjacent columns
+    // 16 (u_w + g) .. + 15 of its row: two 16-byte stores per row block.
     const float gv = effective_global_scale(gscale[0], g_is_div);
     static_for<0, MS>([&](auto msc) {
         constexpr int ms = decltype(msc)::value;
-        const int m = m0 + 16 * ms + r;
-        if (m >= M) return;
-        uint16_t* yr = y + (int64_t)m * ld_y;
+        uint32_t pk[NT][2];   // bf16 pairs of columns 4 g + 2 d, + 1 of unit j (then of unit g: 4 j + 2 d)
+        static_for<0, NT>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            pk[j][0] = pack_bf16x2(gv * acc[ms][j][0], gv * acc[ms][j][1]);
+            pk[j][1] = pack_bf16x2(gv * acc[ms][j][2], gv * acc[ms][j][3]);
+        });
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const int n = (u_w + j) * kUnitN + 4 * g;
-            const uint32_t b0 = f32_to_bf16_rne(gv * acc[ms][j][0]), b1 = f32_to_bf16_rne(gv * acc[ms][j][1]);
-            const uint32_t b2 = f32_to_bf16_rne(gv * acc[ms][j][2]), b3 = f32_to_bf16_rne(gv * acc[ms][j][3]);
-            if (vec_store && n + 3 < N) {
-                *reinterpret_cast<uint2*>(yr + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+        for (int d = 0; d < 2; ++d) {
+            lane_swap32(pk[0][d], pk[2][d]);
+            lane_swap32(pk[1][d], pk[3][d]);
+            lane_swap16(pk[0][d], pk[1][d]);
+            lane_swap16(pk[2][d], pk[3][d]);
+        }
+        const int m = m0 + 16 * ms + r;
+        if (m < M) {
+            uint16_t* yr = y + (int64_t)m * ld_y;
+            const int n0 = (u_w + g) * kUnitN;
+            if (vec_store && n0 + 15 < N) {
+                *reinterpret_cast<uint4*>(yr + n0) = make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]);
+                *reinterpret_cast<uint4*>(yr + n0 + 8) = make_uint4(pk[2][0], pk[2][1], pk[3][0], pk[3][1]);
             } else {
-                if (n < N) yr[n] = (uint16_t)b0;
-                if (n + 1 < N) yr[n + 1] = (uint16_t)b1;
-                if (n + 2 < N) yr[n + 2] = (uint16_t)b2;
-                if (n + 3 < N) yr[n + 3] = (uint16_t)b3;
+#pragma unroll
+                for (int k = 0; k < NT; ++k)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n0 + 4 * k + e < N) yr[n0 + 4 * k + e] = (uint16_t)(pk[k][e >> 1] >> (16 * (e & 1)));
             }
         }
     });

@@ -38,8 +38,8 @@ static hipError_t launch_part(int64_t wgs, int64_t t0, const Layout& L, const ui
                               const uint8_t* blob, const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t M,
                               hipStream_t st) {
     if (wgs == 0) return hipSuccess;
-    // 8-byte output stores need 8-byte aligned rows
-    const int vec = (ld_y % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % 8 == 0);
+    // 16-byte output stores need 16-byte aligned rows
+    const int vec = (ld_y % 8 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
     hipLaunchKernelGGL((k_gemm_mfma<MS, KFULL>), dim3((unsigned)wgs), dim3(kMfmaWN * 64), 0, st, x, ld_x,
                        make_view(L, blob), (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, (int)M, (int)t0,
                        vec);
