@@ -39,6 +39,11 @@ constexpr int kMfmaWN = 4;                                 // waves per workgrou
 constexpr int kMfmaUnits = kMfmaNT * kMfmaWN;              // units per workgroup tile (256 columns)
 constexpr int kMfmaTileRows = 256;                         // rows of a whole tile (MS = 16)
 
+// Raw (untyped, unswizzled) buffer descriptor word 3 for gfx950, and the
+// cache-policy operand of a non-temporal buffer load.
+constexpr int kRawBufferFlags = 0x00020000;
+constexpr int kNonTemporal = 2;
+
 // LDS address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -70,19 +75,6 @@ __device__ __forceinline__ void mfma_acc(f32x4& acc, const uint4& a, const uint4
 // Wait states after the last MFMA before its accumulators are read (more
 // than the longest MFMA pipeline).
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
-
-// Streaming (non-temporal) loads through a pointer known to be global
-// memory: a pointer rebuilt by uniform_ptr has lost its address space, and a
-// flat load would also count against the LDS wait counter.
-typedef const __attribute__((address_space(1))) u32x4v* global_u32x4_ptr;
-typedef const __attribute__((address_space(1))) uint32_t* global_u32_ptr;
-__device__ __forceinline__ uint4 global_stream_u4(const uint8_t* p) {
-    const u32x4v t = __builtin_nontemporal_load((global_u32x4_ptr)p);
-    return make_uint4(t[0], t[1], t[2], t[3]);
-}
-__device__ __forceinline__ uint32_t global_stream_u32(const uint8_t* p) {
-    return __builtin_nontemporal_load((global_u32_ptr)p);
-}
 
 // fp32 pair -> bf16 pair (round to nearest even; NaN stays NaN), first value in the low half.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -138,6 +130,7 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     constexpr int kGroups = 4 * MS;             // issue groups per chunk
     constexpr int kAhead = 3;                   // fragment reads in flight
     static_assert(MS == 8 || MS == 16, "row blocks per wave");
+    static_assert(kAhead * 3 >= 2 * kMfmaNT, "the last kAhead groups carry the 8 weight loads");
     __shared__ __attribute__((aligned(16))) uint8_t stage[2][kStage];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -187,27 +180,35 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
         }
     };
 
-    // ---- weights of this wave's units (units past NU read unit 0, never stored)
-    const uint8_t* cb[NT];
-    const uint8_t* sb[NT];
+    // ---- weights of this wave's units (units past NU read unit 0, never
+    // stored).  Loaded through buffer descriptors over the code and scale
+    // regions: the per-unit, per-chunk block offset is a scalar operand and the
+    // lane offset a constant register, so a load costs no address arithmetic.
+    // (The host keeps both regions below 2^31 bytes for this kernel.)
+    uint32_t cbo[NT], sbo[NT];   // byte offsets of unit j's chunk-0 code and scale blocks
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         const int64_t blk = bv.block(0, (u_w + j) < NU ? u_w + j : 0, 0);
-        cb[j] = bv.codes + blk * kCodeBlock;
-        sb[j] = bv.scales + blk * kScaleBlock;
+        cbo[j] = (uint32_t)(blk * kCodeBlock);
+        sbo[j] = (uint32_t)(blk * kScaleBlock);
     }
-    const int64_t cstr = bv.chunk_stride * kCodeBlock;
-    const uint32_t lane16 = (uint32_t)(lane * 16);
+    const uint32_t code_bytes = (uint32_t)((int64_t)NU * KC * kCodeBlock);
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(bv.codes), (short)0,
+                                                                         (int)code_bytes, kRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(bv.scales), (short)0,
+                                                                         (int)(code_bytes / 8), kRawBufferFlags);
+    const uint32_t cstr = (uint32_t)(bv.chunk_stride * kCodeBlock);
+    const int lane16 = lane * 16, lane_sc = (lane >> 1) << 2;   // lanes 2i, 2i + 1 share one scale dword
     struct BRegs {
         uint4 cw[NT];       // the lane's 16 code bytes (row l & 15, k-group l >> 4) per unit
         uint32_t sw[NT];    // the scale dword holding the lane's two scale bytes, per unit
     };
     auto load_b = [&](BRegs& b, int c) {
-        const int64_t co = (int64_t)c * cstr;
+        const uint32_t co = (uint32_t)c * cstr;
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            b.cw[j] = global_stream_u4(uniform_ptr(cb[j] + co) + lane16);
-            b.sw[j] = global_stream_u32(uniform_ptr(sb[j] + (co >> 3)) + ((lane >> 1) << 2));   // lanes 2i, 2i + 1: one dword
+            b.cw[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, lane16, (int)(cbo[j] + co), kNonTemporal));
+            b.sw[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane_sc, (int)(sbo[j] + (co >> 3)), kNonTemporal);
         }
     };
 
@@ -275,13 +276,26 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     // scheduling fence.  VALU work: in steps 0..2 the decode of step t + 1
     // (16 / MS dwords per group); in step 3 the next chunk's scales (group 0)
     // and its step-0 decode (groups 1 .. MS - 1).
-    auto group = [&](auto fc, int c, int buf, const BRegs& b, const BRegs& bn) {
+    auto group = [&](auto fc, int c, int buf, BRegs& b, const BRegs& bn) {
         constexpr int f = decltype(fc)::value, t = f / MS, ms = f % MS;
         if constexpr (f + kAhead < kGroups) af[(f + kAhead) % kRing] = frag(buf, f + kAhead);
-        // the activation copies of chunk c + 1 (into the other stage, free
-        // since the last barrier) are spread over the first groups
-        if constexpr (f < kCopiesPerWave) {
-            if (c + 1 < KC) copy_piece(c + 1, buf ^ 1, f);
+        // The activation copies of chunk c + 1 (into the other stage, free
+        // since the last barrier) go out on every second group of the first
+        // half, and the weight loads of chunk c + 2 (into b, free after step
+        // 2) on the last three groups, so that no group issues a burst of
+        // vector memory instructions.  Both are unconditional: past the last
+        // chunk they repeat it, into buffers nothing reads any more (a branch
+        // per group cost more than the extra traffic).
+        if constexpr (f % 2 == 0 && f / 2 < kCopiesPerWave) copy_piece(c + 1 < KC ? c + 1 : KC - 1, buf ^ 1, f / 2);
+        if constexpr (f >= kGroups - kAhead) {
+            const uint32_t co = (uint32_t)(c + 2 < KC ? c + 2 : KC - 1) * cstr;
+            static_for<0, 3>([&](auto pc) {
+                constexpr int p = (f - (kGroups - kAhead)) * 3 + decltype(pc)::value;
+                if constexpr (p < NT)
+                    b.cw[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, lane16, (int)(cbo[p] + co), kNonTemporal));
+                else if constexpr (p < 2 * NT)
+                    b.sw[p - NT] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane_sc, (int)(sbo[p - NT] + (co >> 3)), kNonTemporal);
+            });
         }
         uint4* bf = (t & 1) ? bfb : bfa;
         uint4* nb = (t & 1) ? bfa : bfb;
@@ -309,19 +323,17 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     };
 
     // One chunk on stage buf with weights b; bn holds the next chunk's
-    // weights (loaded a chunk ago).  The first groups issue the activation
-    // copies of chunk c + 1.  After group kGroups - 4 the wave waits for its
-    // copies and meets the others at the barrier; then it loads the weights
-    // of chunk c + 2 (into b, free now), reads the first fragments of chunk
-    // c + 1, and runs the last three groups, whose fragments are already in
-    // registers.
+    // weights (loaded a chunk ago).  After group kGroups - 4 the wave waits
+    // for its copies of chunk c + 1 and meets the others at the barrier; then
+    // it reads the first fragments of chunk c + 1 and runs the last three
+    // groups, whose fragments are already in registers (and which load the
+    // weights of chunk c + 2).
     auto chunk = [&](int c, int buf, BRegs& b, const BRegs& bn) {
         static_for<0, kGroups - kAhead>([&](auto fc) { group(fc, c, buf, b, bn); });
         wait_vmcnt<0>();
         if (!KFULL && c + 1 == KC - 1) zero_tail(buf ^ 1);
         wait_lgkmcnt0();
         asm volatile("s_barrier" ::: "memory");
-        if (c + 2 < KC) load_b(b, c + 2);
         if (c + 1 < KC) {
             static_for<0, kAhead>([&](auto fc) {
                 constexpr int f = decltype(fc)::value;

@@ -350,7 +350,12 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
     const TileShape t = tile_shape(L, M, false);
     const SmallShape sm = small_m_shape(L, M, false);
     const bool small = variant == kSmall || (variant == kAuto && M <= kSmallAuto);
-    const bool mfma = variant == kMfma || (variant == kAuto && M >= kMfmaAuto && mfma_plan(L, M).tiles >= kMfmaMinTiles);
+    // the MFMA-bound kernel addresses the code and scale regions with 32-bit offsets
+    const bool mfma_fits = L.code_bytes() < ((int64_t)1 << 31);
+    if (variant == kMfma && !mfma_fits)
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: the MFMA-bound variant takes weights below 2 GiB of codes", fn);
+    const bool mfma = variant == kMfma ||
+                      (variant == kAuto && mfma_fits && M >= kMfmaAuto && mfma_plan(L, M).tiles >= kMfmaMinTiles);
     const Workspace wl = small  ? workspace_for(sm, M, K, pre != nullptr)
                          : mfma ? workspace_layout(1, 0, 0, M, K, pre != nullptr)
                                 : workspace_for(t, M, K, pre != nullptr);
