@@ -41,6 +41,11 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
                                                             uint16_t* __restrict__ y, int64_t ld_y, int64_t rows_dense,
                                                             const int32_t* __restrict__ offsets, int E, SplitK sk) {
     constexpr int W = UW * KW;                                     // waves per workgroup
+    // Weights stream past the caches (non-temporal) when one row tile covers
+    // all rows (tiles of up to 32 rows, dense): no other workgroup reads the
+    // same chunk.  With several row tiles a chunk is read once per row tile
+    // and caching it is faster (measured).
+    constexpr bool kStreamWeights = MS <= 2 && !GROUPED;
     constexpr int BM = 16 * MS;
     constexpr int UG = NT * UW;                                    // units per workgroup
     constexpr int CPIECES = BM * 16;                               // 16-byte pieces per activation chunk
@@ -148,8 +153,15 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
         const int64_t boff = (int64_t)c * cstr;
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            b.cw[j] = load_stream_u4(cb[j] + boff + (uint32_t)(lane * 16));
-            b.sw[j] = load_stream_u16(sb[j] + (boff >> 3) + (uint32_t)(lane * 2));
+            const uint8_t* cp = cb[j] + boff + (uint32_t)(lane * 16);
+            const uint8_t* sp = sb[j] + (boff >> 3) + (uint32_t)(lane * 2);
+            if constexpr (kStreamWeights) {
+                b.cw[j] = load_stream_u4(cp);
+                b.sw[j] = load_stream_u16(sp);
+            } else {
+                b.cw[j] = *reinterpret_cast<const uint4*>(cp);
+                b.sw[j] = *reinterpret_cast<const uint16_t*>(sp);
+            }
         }
 #pragma unroll
         for (int i = 0; i < APT; ++i) {
