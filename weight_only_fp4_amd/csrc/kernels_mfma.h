@@ -14,9 +14,9 @@
 //       asynchronous global -> LDS copies, double buffered, in the
 //       XOR-swizzled layout (slot q of a 256-byte row holds piece q ^ (row &
 //       15)), so every fragment read is a conflict-free ds_read_b128;
-//     - each wave loads its four units' code blocks and scale pairs straight
-//       into registers, one chunk ahead, and decodes them into exact bf16
-//       fragments;
+//     - each wave copies its four units' code and scale blocks into its own
+//       LDS slice a chunk ahead, reads them into registers when the chunk's
+//       first decode is due, and decodes them into exact bf16 fragments;
 //     - the chunk is issued as 4 MS groups (MFMA step t, row block ms): the
 //       LDS read of the fragment three groups ahead, the four MFMAs of the
 //       group, and a slice of the next step's decode, closed by a
@@ -39,20 +39,13 @@ constexpr int kMfmaWN = 4;                                 // waves per workgrou
 constexpr int kMfmaUnits = kMfmaNT * kMfmaWN;              // units per workgroup tile (256 columns)
 constexpr int kMfmaTileRows = 256;                         // rows of a whole tile (MS = 16)
 
-// Raw (untyped, unswizzled) buffer descriptor word 3 for gfx950, and the
-// cache policy of the weight loads: default caching, since every row tile of
-// a column reads the same weight chunk (non-temporal loads measured 6 %
-// slower: the chunk left L2 before the next row tile needed it).
-constexpr int kRawBufferFlags = 0x00020000;
-constexpr int kWeightPolicy = 0;
-
 // LDS address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Asynchronous copy global -> LDS: lane l moves the 16 bytes at base + voff
-// (base wave-uniform) to LDS address lds + 16 l.  Written as inline assembly
+// Asynchronous copy global -> LDS: lane l moves the 16 (lds_copy4: 4) bytes
+// at base + voff (base wave-uniform) to LDS address lds + 16 l (4 l).  Written as inline assembly
 // so that the compiler, which cannot tell which LDS bytes such a copy
 // writes, does not wait for every copy in flight before each LDS read; the
 // kernel waits for its own copies (vmcnt) before the barrier that publishes
@@ -107,6 +100,11 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
+__device__ __forceinline__ void lds_copy4(uint32_t lds, const uint8_t* base, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
+
 // Output tile (mt, nt) at position t of the tile order, which walks four
 // tile rows at a time across all tile columns (the workgroups running
 // together then share activation rows and weight columns in the caches).
@@ -118,8 +116,9 @@ __device__ __forceinline__ void mfma_tile(int t, int MT, int NTn, int& mt, int& 
     nt = in / rows;
 }
 
-// Workgroup id covers part id % P (P = 16 / MS row parts of 16 MS rows) of
-// tile t0 + id / P of the tile order (whole tiles are 256 rows x 256 columns).
+// Work item p (the workgroup id after the XCD remap below) covers part p % P
+// (P = 16 / MS row parts of 16 MS rows) of tile t0 + p / P of the tile order
+// (whole tiles are 256 rows x 256 columns).
 template <int MS, bool KFULL>
 __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                         int NU, int KC, int K, int N, const float* __restrict__ gscale,
@@ -132,15 +131,23 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     constexpr int kGroups = 4 * MS;             // issue groups per chunk
     constexpr int kAhead = 3;                   // fragment reads in flight
     static_assert(MS == 8 || MS == 16, "row blocks per wave");
-    static_assert(kAhead * 3 >= 2 * kMfmaNT, "the last kAhead groups carry the 8 weight loads");
     __shared__ __attribute__((aligned(16))) uint8_t stage[2][kStage];
+    constexpr int kWStage = kMfmaNT * (kCodeBlock + kScaleBlock);   // one chunk of a wave's weights
+    __shared__ __attribute__((aligned(16))) uint8_t wstage[kMfmaWN][kWStage];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
+    // The hardware deals workgroups to the eight XCDs round-robin (id % 8);
+    // each XCD is given a contiguous range of the tile order instead, so the
+    // ~32 workgroups an XCD runs together form a block of about 4 tile rows x
+    // 8 tile columns whose activations and weights its own L2 holds.
+    const int xid = [&] {
+        const int n = (int)gridDim.x, q8 = n / 8, rem = n % 8, x = (int)blockIdx.x % 8, k = (int)blockIdx.x / 8;
+        return x * q8 + (x < rem ? x : rem) + k;
+    }();
     int mt, nt;
-    mfma_tile(t0 + (int)blockIdx.x / kParts, (M + kMfmaTileRows - 1) / kMfmaTileRows, (NU + kMfmaUnits - 1) / kMfmaUnits,
-              mt, nt);
-    const int m0 = mt * kMfmaTileRows + ((int)blockIdx.x % kParts) * kRows;
+    mfma_tile(t0 + xid / kParts, (M + kMfmaTileRows - 1) / kMfmaTileRows, (NU + kMfmaUnits - 1) / kMfmaUnits, mt, nt);
+    const int m0 = mt * kMfmaTileRows + (xid % kParts) * kRows;
     if (m0 >= M) return;                        // a lower part past the last row (uniform per workgroup)
     const int u_w = nt * kMfmaUnits + NT * w;   // this wave's first unit
 
@@ -183,34 +190,49 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     };
 
     // ---- weights of this wave's units (units past NU read unit 0, never
-    // stored).  Loaded through buffer descriptors over the code and scale
-    // regions: the per-unit, per-chunk block offset is a scalar operand and the
-    // lane offset a constant register, so a load costs no address arithmetic.
-    // (The host keeps both regions below 2^31 bytes for this kernel.)
-    uint32_t cbo[NT], sbo[NT];   // byte offsets of unit j's chunk-0 code and scale blocks
+    // stored).  A chunk of them (4 code blocks, 4 scale blocks) is copied
+    // global -> LDS into the wave's own slice of LDS (no other wave reads it,
+    // so only this wave's own wait is needed), then read into registers in
+    // one go when the chunk's first decode is due, which frees the slice for
+    // the next copy.  (Copying into LDS measured cheaper than loading into
+    // registers beside the MFMAs.)
+    const uint8_t* cb[NT];   // chunk-0 code block of unit j
+    const uint8_t* s_lo[NT / 2];
+    uint32_t s_off[NT / 2];  // scale copy p moves unit 2p (lanes 0..31) and 2p + 1 (lanes 32..63)
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-        const int64_t blk = bv.block(0, (u_w + j) < NU ? u_w + j : 0, 0);
-        cbo[j] = (uint32_t)(blk * kCodeBlock);
-        sbo[j] = (uint32_t)(blk * kScaleBlock);
+    for (int j = 0; j < NT; ++j) cb[j] = bv.codes + bv.block(0, (u_w + j) < NU ? u_w + j : 0, 0) * kCodeBlock;
+#pragma unroll
+    for (int p = 0; p < NT / 2; ++p) {
+        const uint8_t* s0p = bv.scales + bv.block(0, (u_w + 2 * p) < NU ? u_w + 2 * p : 0, 0) * kScaleBlock;
+        const uint8_t* s1p = bv.scales + bv.block(0, (u_w + 2 * p + 1) < NU ? u_w + 2 * p + 1 : 0, 0) * kScaleBlock;
+        s_lo[p] = s0p < s1p ? s0p : s1p;
+        s_off[p] = (uint32_t)((lane < 32 ? s0p : s1p) - s_lo[p]) + (uint32_t)((lane & 31) * 4);
     }
-    const uint32_t code_bytes = (uint32_t)((int64_t)NU * KC * kCodeBlock);
-    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(bv.codes), (short)0,
-                                                                         (int)code_bytes, kRawBufferFlags);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(bv.scales), (short)0,
-                                                                         (int)(code_bytes / 8), kRawBufferFlags);
-    const uint32_t cstr = (uint32_t)(bv.chunk_stride * kCodeBlock);
-    const int lane16 = lane * 16, lane_sc = (lane >> 1) << 2;   // lanes 2i, 2i + 1 share one scale dword
+    const int64_t cstr = bv.chunk_stride * kCodeBlock;
+    const uint32_t lane16 = (uint32_t)(lane * 16);
+    const uint32_t wdst = lds_addr(wstage[w]);
+    // copies of chunk c (clamped to the last chunk: past it they repeat it into a slice nothing reads)
+    auto copy_b_codes = [&](int c) {
+        const int64_t co = (int64_t)(c < KC ? c : KC - 1) * cstr;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) lds_copy16(wdst + j * kCodeBlock, uniform_ptr(cb[j] + co), lane16);
+    };
+    auto copy_b_scales = [&](int c) {
+        const int64_t so = ((int64_t)(c < KC ? c : KC - 1) * cstr) >> 3;
+#pragma unroll
+        for (int p = 0; p < NT / 2; ++p)
+            lds_copy4(wdst + NT * kCodeBlock + p * 2 * kScaleBlock, uniform_ptr(s_lo[p] + so), s_off[p]);
+    };
     struct BRegs {
         uint4 cw[NT];       // the lane's 16 code bytes (row l & 15, k-group l >> 4) per unit
         uint32_t sw[NT];    // the scale dword holding the lane's two scale bytes, per unit
     };
-    auto load_b = [&](BRegs& b, int c) {
-        const uint32_t co = (uint32_t)c * cstr;
+    auto read_b = [&](BRegs& b) {
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            b.cw[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, lane16, (int)(cbo[j] + co), kWeightPolicy));
-            b.sw[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane_sc, (int)(sbo[j] + (co >> 3)), kWeightPolicy);
+            b.cw[j] = *reinterpret_cast<const uint4*>(wstage[w] + j * kCodeBlock + lane16);
+            b.sw[j] = *reinterpret_cast<const uint32_t*>(wstage[w] + NT * kCodeBlock + (j >> 1) * 2 * kScaleBlock +
+                                                         (j & 1) * kScaleBlock + ((lane >> 1) << 2));
         }
     };
 
@@ -278,27 +300,26 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     // scheduling fence.  VALU work: in steps 0..2 the decode of step t + 1
     // (16 / MS dwords per group); in step 3 the next chunk's scales (group 0)
     // and its step-0 decode (groups 1 .. MS - 1).
-    auto group = [&](auto fc, int c, int buf, BRegs& b, const BRegs& bn) {
+    auto group = [&](auto fc, int c, int buf, BRegs& b) {
         constexpr int f = decltype(fc)::value, t = f / MS, ms = f % MS;
         if constexpr (f + kAhead < kGroups) af[(f + kAhead) % kRing] = frag(buf, f + kAhead);
         // The activation copies of chunk c + 1 (into the other stage, free
         // since the last barrier) go out on every second group of the first
-        // half, and the weight loads of chunk c + 2 (into b, free after step
-        // 2) on the last three groups, so that no group issues a burst of
-        // vector memory instructions.  Both are unconditional: past the last
-        // chunk they repeat it, into buffers nothing reads any more (a branch
-        // per group cost more than the extra traffic).
+        // half, unconditionally (past the last chunk they repeat it into a
+        // stage nothing reads; a branch per group cost more than the traffic).
         if constexpr (f % 2 == 0 && f / 2 < kCopiesPerWave) copy_piece(c + 1 < KC ? c + 1 : KC - 1, buf ^ 1, f / 2);
-        if constexpr (f >= kGroups - kAhead) {
-            const uint32_t co = (uint32_t)(c + 2 < KC ? c + 2 : KC - 1) * cstr;
-            static_for<0, 3>([&](auto pc) {
-                constexpr int p = (f - (kGroups - kAhead)) * 3 + decltype(pc)::value;
-                if constexpr (p < NT)
-                    b.cw[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, lane16, (int)(cbo[p] + co), kWeightPolicy));
-                else if constexpr (p < 2 * NT)
-                    b.sw[p - NT] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane_sc, (int)(sbo[p - NT] + (co >> 3)), kWeightPolicy);
-            });
+        // Step 3: the weights of chunk c + 1 (copied a chunk ago; the 16
+        // activation copies issued since may still fly) replace chunk c's in
+        // registers, then the slice takes the copies of chunk c + 2.
+        if constexpr (f == 3 * MS) {
+            wait_vmcnt<kCopiesPerWave>();
+            read_b(b);
         }
+        if constexpr (f == 3 * MS + 1) {
+            wait_lgkmcnt0();
+            copy_b_codes(c + 2);
+        }
+        if constexpr (f == 3 * MS + 2) copy_b_scales(c + 2);
         uint4* bf = (t & 1) ? bfb : bfa;
         uint4* nb = (t & 1) ? bfa : bfb;
         constexpr int d_lo = t < 3 ? ms * 16 / MS : (ms == 0 ? 0 : ((ms - 1) * 16 + MS - 2) / (MS - 1));
@@ -313,26 +334,27 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
                     dword_op(b, t + 1, d, j, jobs[d - d_lo], nb);
                 });
             } else if constexpr (ms == 0) {
-                scale_op(bn, j);
+                scale_op(b, j);
             } else {
                 static_for<d_lo, d_hi>([&](auto dc) {
                     constexpr int d = decltype(dc)::value;
-                    dword_op(bn, 0, d, j, jobs[d - d_lo], nb);
+                    dword_op(b, 0, d, j, jobs[d - d_lo], nb);
                 });
             }
             __builtin_amdgcn_sched_barrier(0);
         });
     };
 
-    // One chunk on stage buf with weights b; bn holds the next chunk's
-    // weights (loaded a chunk ago).  After group kGroups - 4 the wave waits
-    // for its copies of chunk c + 1 and meets the others at the barrier; then
-    // it reads the first fragments of chunk c + 1 and runs the last three
-    // groups, whose fragments are already in registers (and which load the
-    // weights of chunk c + 2).
-    auto chunk = [&](int c, int buf, BRegs& b, const BRegs& bn) {
-        static_for<0, kGroups - kAhead>([&](auto fc) { group(fc, c, buf, b, bn); });
-        wait_vmcnt<0>();
+    // One chunk on stage buf; b holds its weights until step 3, then the
+    // next chunk's.  After group kGroups - 4 the wave waits for its
+    // activation copies of chunk c + 1 (the weight copies of chunk c + 2,
+    // issued after them, may still fly) and meets the others at the barrier;
+    // then it reads the first fragments of chunk c + 1 and runs the last
+    // three groups, whose fragments are already in registers.
+    constexpr int kWCopies = NT + NT / 2;   // weight copies per chunk
+    auto chunk = [&](int c, int buf, BRegs& b) {
+        static_for<0, kGroups - kAhead>([&](auto fc) { group(fc, c, buf, b); });
+        wait_vmcnt<kWCopies>();
         if (!KFULL && c + 1 == KC - 1) zero_tail(buf ^ 1);
         wait_lgkmcnt0();
         asm volatile("s_barrier" ::: "memory");
@@ -343,30 +365,28 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
             });
         }
         __builtin_amdgcn_sched_barrier(0);
-        static_for<kGroups - kAhead, kGroups>([&](auto fc) { group(fc, c, buf, b, bn); });
+        static_for<kGroups - kAhead, kGroups>([&](auto fc) { group(fc, c, buf, b); });
     };
 
-    // ---- pipeline: two chunks in flight (stages and weight register sets
-    // alternate, so the loop is unrolled by two)
-    BRegs b0, b1;
+    // ---- pipeline: chunk c on stage c & 1
+    BRegs b;
     copy_a(0, 0);
-    load_b(b0, 0);
+    copy_b_codes(0);
+    copy_b_scales(0);
     __builtin_amdgcn_s_waitcnt(0);
     if (!KFULL && KC == 1) zero_tail(0);
     __syncthreads();
-    if (KC > 1) load_b(b1, 1);
-    static_for<0, NT>([&](auto jc) { scale_op(b0, decltype(jc)::value); });
+    read_b(b);
+    wait_lgkmcnt0();
+    copy_b_codes(1);
+    copy_b_scales(1);
+    static_for<0, NT>([&](auto jc) { scale_op(b, decltype(jc)::value); });
     static_for<0, 16>([&](auto dc) {
         DwordJob jb;
-        static_for<0, 4>([&](auto oc) { dword_op(b0, 0, decltype(dc)::value, decltype(oc)::value, jb, bfa); });
+        static_for<0, 4>([&](auto oc) { dword_op(b, 0, decltype(dc)::value, decltype(oc)::value, jb, bfa); });
     });
     static_for<0, kAhead>([&](auto fc) { af[decltype(fc)::value] = frag(0, decltype(fc)::value); });
-    int c = 0;
-    for (; c + 1 < KC; c += 2) {
-        chunk(c, 0, b0, b1);
-        chunk(c + 1, 1, b1, b0);
-    }
-    if (c < KC) chunk(c, 0, b0, b1);
+    for (int c = 0; c < KC; ++c) chunk(c, c & 1, b);
     mfma_drain();
 
     // ---- epilogue: lane (r, g) holds, for row 16 ms + r, the four columns
