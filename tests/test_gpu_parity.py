@@ -225,6 +225,24 @@ def test_grouped_parity_T2048_sampled(fc):
     accept_or_fail(y[rows, cols], ref, fc)
 
 
+def test_grouped_tile_path_ragged_experts():
+    """Enough rows per expert for the grouped tile kernel (64-row tiles): experts of 300, 0, 129, 1 and 70
+    rows (an empty expert, whole tiles plus one row, a single row), N and K not multiples of 256 and 128,
+    per-expert global scales stored as divisors, and a pre-quant scale."""
+    counts = [300, 0, 129, 1, 70]
+    route = np.repeat(np.arange(len(counts)), counts)
+    synth.rng(17).shuffle(route)
+    gc = synth.grouped_case(T=len(route), E=len(counts), topk=1, N=300, K=272, seed=12, prescale=True,
+                            routing=route[:, None])
+    gc.g_is_divisor = True
+    gc.g_stored = (1.0 / gc.g_stored).astype(np.float32)
+    assert list(np.diff(gc.offsets)) == counts
+    say(f"grouped tile path R={gc.R} E={gc.E}")
+    d = GroupedDev(gc)
+    ref = oracle.grouped_gemm(gc.x, gc.offsets, gc.w, gc.s, gc.g_stored, True, gc.pre)
+    accept_or_fail(to_f64(d.run()), ref, "grouped ragged experts")
+
+
 def test_grouped_prescale_and_divisor_small_experts():
     gc = synth.grouped_case(T=40, E=6, topk=2, N=72, K=160, seed=3, prescale=True)
     gc.g_is_divisor = True
