@@ -343,3 +343,50 @@ def test_run_to_run_bitwise_determinism():
         assert torch.equal(d.run(), d.run())
         # the MFMA kernel splits this shape's tiles over K: the order of the split sums is fixed
         assert torch.equal(d.run(nv.VARIANT_MFMA), d.run(nv.VARIANT_MFMA))
+
+
+# ------------------------------------------------------------ graph replay --
+
+def test_graph_replays_match_eager():
+    """Calls captured in a HIP graph give the eager results on every replay, with eager work on the outputs
+    between replays.  The split-K counters live in workspaces zeroed once before capture: the kernels themselves
+    must leave them zero after every call, since nothing clears them between replays."""
+    say("graph replays")
+    cases = [(synth.decode_case(16, N=4096, K=14336, seed=3), nv.VARIANT_AUTO),    # tile, K split 2 ways
+             (synth.decode_case(1, N=2048, K=4096, seed=4), nv.VARIANT_AUTO),      # small-M, K split
+             (synth.dense_case(300, 700, 2048, 5, prescale=True), nv.VARIANT_MFMA),  # two MFMA launches + pre-scale
+             (synth.dense_case(24, 2000, 4096, 1005), nv.VARIANT_LARGE_M)]          # tile, split with N tail
+    devs = [DenseDev(c) for c, _ in cases]
+    wss = [nv.workspace(nv.gemm_workspace_bytes(c.M, c.N, c.K), DEV) for c, _ in cases]
+    ys = [torch.empty((c.M, c.N), dtype=torch.bfloat16, device=DEV) for c, _ in cases]
+    gc = synth.grouped_case(T=16, E=8, topk=2, N=96, K=256, seed=6)
+    gd = GroupedDev(gc)
+    gws = nv.workspace(nv.lib().nvfp4_w4a16_grouped_gemm_workspace_bytes(gc.R, gc.E, gc.N, gc.K), DEV)
+    gy = torch.zeros((gc.R, gc.N), dtype=torch.bfloat16, device=DEV)
+
+    def run_all():
+        for (c, v), d, ws, y in zip(cases, devs, wss, ys):
+            nv.gemm_variant(d.x, d.blob, c.N, c.K, d.g, c.g_is_divisor, d.pre, out=y, workspace_buf=ws, variant=v)
+        nv.grouped_gemm(gd.x, gd.off, gd.blob, gc.E, gc.N, gc.K, gd.g, False, gd.pre, out=gy, workspace_buf=gws)
+
+    run_all()
+    torch.cuda.synchronize()
+    ref = [y.clone() for y in ys] + [gy.clone()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_all()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_all()
+    for rep in range(3):
+        for y in ys + [gy]:
+            y.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (y, r) in enumerate(zip(ys + [gy], ref)):
+            assert torch.equal(y, r), (rep, i)
+        run_all()      # eager calls between replays share the workspaces
+        torch.cuda.synchronize()
