@@ -183,6 +183,21 @@ def test_dense_parity_full_size_sampled(name, make):
     accept_or_fail(y[rows, cols], ref, name)
 
 
+def test_wide_n_tile_ragged_sampled():
+    """The wide-N 64-row tile shape (512 columns per workgroup) with N one unit past a multiple of 512 columns,
+    K not a multiple of 128 and a pre-quant scale; every row and the last columns are sampled."""
+    c = synth.dense_case(40, 65552, 1040, 1008, prescale=True, g_stored=2688.0, g_is_divisor=True)
+    say(f"wide-N tile M={c.M} N={c.N} K={c.K}")
+    d = DenseDev(c)
+    y = to_f64(d.run(nv.VARIANT_LARGE_M))
+    assert np.all(np.isfinite(y))
+    g = synth.rng(321)
+    rows = np.concatenate([np.arange(c.M).repeat(8), g.integers(0, c.M, 512)])
+    cols = np.concatenate([np.tile(np.arange(c.N - 8, c.N), c.M), g.integers(0, c.N, 512)])
+    ref = oracle.gemm_sampled(c.x, c.w, c.s, c.g_stored, c.g_is_divisor, c.pre, rows, cols)
+    accept_or_fail(y[rows, cols], ref, "wide-N tile")
+
+
 def test_small_and_large_variants_agree():
     c = synth.decode_case(8, N=2048, K=4096, seed=31)
     say("variants agree M=8")

@@ -184,8 +184,10 @@ TileShape tile_shape(const Layout& L, int64_t rows, bool grouped) {
     } else if (rows <= 32) {
         t.ms = 2; t.nt = 1; t.uw = 4; t.kw = 2; t.d = 4;
     } else if (rows <= 192) {
-        // 64-row tiles: up to three row tiles still beat 128-row tiles here (measured)
-        if (L.NU >= 4096) { t.ms = 4; t.nt = 4; t.uw = 4; t.kw = 1; t.d = 2; }
+        // 64-row tiles: up to three row tiles still beat 128-row tiles here
+        // (measured); wide N (LM heads) takes 512 columns per workgroup with
+        // a 3-deep weight ring
+        if (L.NU >= 4096) { t.ms = 4; t.nt = 4; t.uw = 8; t.kw = 1; t.d = 3; }
         else { t.ms = 4; t.nt = 1; t.uw = 4; t.kw = 4; t.d = 2; }
     } else {
         t.ms = 8; t.nt = 2; t.uw = 8; t.kw = 1; t.d = 2;
@@ -262,7 +264,7 @@ nvfp4_status launch_tile(const TileShape& t, const Layout& L, const uint16_t* x,
     } else {
         if (t.ms == 1) NVFP4_TILE(1, 1, 4, 4, 2);
         else if (t.ms == 2) NVFP4_TILE(2, 1, 4, 2, 4);
-        else if (t.ms == 4 && t.kw == 1) NVFP4_TILE(4, 4, 4, 1, 2);
+        else if (t.ms == 4 && t.kw == 1) NVFP4_TILE(4, 4, 8, 1, 3);
         else if (t.ms == 4) NVFP4_TILE(4, 1, 4, 4, 2);
         else NVFP4_TILE(8, 2, 8, 1, 2);
     }
