@@ -25,9 +25,11 @@ TFLOP/s with their roofline fractions).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -289,8 +291,59 @@ def cpu_baseline(case, target_s=12.0):
         oracle.gemm(case.x, case.w, case.s, case.g_stored, case.g_is_divisor, case.pre)
     dt = time.perf_counter() - t0
     wbytes = 0.5625 * case.N * case.K * reps
+    # one thread on the tiny configuration (M=4, N=256, K=512), as a reference point
+    import synth
+    tiny = synth.tiny_case()
+    t0 = time.perf_counter()
+    for _ in range(10):
+        oracle.gemm(tiny.x, tiny.w, tiny.s, tiny.g_stored, tiny.g_is_divisor, tiny.pre, threads=1)
+    tiny_ms = (time.perf_counter() - t0) * 100.0
     return {"value": round(wbytes / dt / 1e9, 4), "unit": "GB/s", "cores": thr, "kind": "oracle",
-            "sample": f"{reps} whole calls of M={case.M}, N={case.N}, K={case.K} ({dt:.1f} s, fp64, {thr} threads)"}
+            "sample": f"{reps} whole calls of M={case.M}, N={case.N}, K={case.K} ({dt:.1f} s, fp64, {thr} threads)",
+            "cpu_model": cpu_model(), "tiny_M4_N256_K512_one_thread_ms": round(tiny_ms, 3)}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def max_sclk_mhz():
+    """Peak engine clock of device 0 from the HIP runtime (hipDeviceAttributeClockRate, kHz), or None."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        kHIP_ATTR_CLOCK_RATE = 5   # position of hipDeviceAttributeClockRate in hipDeviceAttribute_t
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), kHIP_ATTR_CLOCK_RATE, 0) == 0 and v.value > 0:
+            return v.value / 1000.0
+    except OSError:
+        pass
+    return None
+
+
+def stream_copy_gbps(torch, nbytes=512 << 20, reps=10):
+    """Device-to-device copy rate (bytes read + written per second), as context for the HBM numbers."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return round(2 * nbytes / ms / 1e6, 1)
 
 
 def sanity_parity(case, y):
@@ -326,6 +379,11 @@ def main():
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
     device = {"name": props.name, "cus": props.multi_processor_count, "arch": getattr(props, "gcnArchName", "")}
+    sclk = max_sclk_mhz()
+    if sclk:
+        # dense bf16 MFMA: 4096 flop per compute unit per clock (2.5 PFLOP/s at 256 CUs and 2.4 GHz)
+        device["max_sclk_mhz"] = sclk
+        device["bf16_peak_at_max_sclk_tflops"] = round(props.multi_processor_count * sclk * 1e6 * 4096 / 1e12, 1)
 
     if args.copy_calibration:
         nbytes = 512 << 20
@@ -404,9 +462,13 @@ def main():
             t2 = time_workload(w2, n2, min(args.warmup, 5))
             t2["steps"] = n2
             extra[name] = summarize(w2, t2)
+            if "bf16_peak_at_max_sclk_tflops" in device:
+                extra[name]["mfma_frac_at_max_sclk"] = round(extra[name]["TFLOPs"] / device["bf16_peak_at_max_sclk_tflops"], 4)
             del w2
             torch.cuda.empty_cache()
         out["extra"] = extra
+        out["context"] = {"stream_copy_GBps": stream_copy_gbps(torch),
+                          "note": "512 MiB device copy, bytes read + written per second"}
 
     if not args.only and not args.no_cpu:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
