@@ -340,6 +340,50 @@ def test_strided_io_and_untouched_padding(variant):
     assert torch.all(ybig[:, 40:] == 5.0)
 
 
+def test_nan_scale_codes_propagate():
+    """E4M3 NaN scale bytes (0x7F, 0xFF) decode to NaN (read literally): the decoded tile holds NaN exactly on
+    their blocks, every output column whose weights hold one is NaN in every variant, and the other columns are
+    unaffected."""
+    c = synth.dense_case(16, 64, 256, seed=77)
+    s = c.s.copy()
+    bad = [(3, 0, 0x7F), (17, 5, 0xFF), (40, 15, 0x7F)]       # (row n, block, byte)
+    for n, b, v in bad:
+        s[n, b] = v
+    c.s = s
+    say("nan scale codes")
+    d = DenseDev(c)
+    tile = bf16_bits(nv.dequant(d.blob, 1, c.N, c.K))[0].astype(np.uint32)
+    is_nan = ((tile & 0x7F80) == 0x7F80) & ((tile & 0x7F) != 0)
+    exp = np.zeros((c.N, c.K), dtype=bool)
+    for n, b, _ in bad:
+        exp[n, 16 * b:16 * b + 16] = True
+    assert np.array_equal(is_nan, exp)
+    ref = oracle.gemm(c.x, c.w, c.s, c.g_stored, False, None)
+    nan_cols = sorted({n for n, _, _ in bad})
+    assert np.all(np.isnan(ref[:, nan_cols]))
+    keep = [n for n in range(c.N) if n not in nan_cols]
+    for v in dense_variants(c.M, c.K):
+        y = to_f64(d.run(v))
+        assert np.all(np.isnan(y[:, nan_cols])), v
+        accept_or_fail(y[:, keep], ref[:, keep], ("nan scales", v))
+
+
+def test_largest_activation_stride():
+    """ld_x at its limit (2^23 elements): the kernels address a tile's rows with 32-bit offsets from the tile's
+    first row, which must not wrap at this stride (up to 255 rows x 2^24 bytes)."""
+    c = synth.dense_case(300, 272, 256, seed=78)
+    say("ld_x = 2^23")
+    d = DenseDev(c)
+    big = torch.empty((c.M, 1 << 23), dtype=torch.bfloat16, device=DEV)
+    big[:, :c.K] = d.x
+    ref = oracle.gemm(c.x, c.w, c.s, c.g_stored, False, None)
+    for v in (nv.VARIANT_AUTO, nv.VARIANT_LARGE_M, nv.VARIANT_MFMA):
+        y = to_f64(d.run(v, x=big[:, :c.K]))
+        accept_or_fail(y, ref, ("ld_x max", v))
+    del big
+    torch.cuda.empty_cache()
+
+
 def test_smallest_shapes():
     for M, N, K in [(1, 1, 16), (1, 17, 16), (17, 1, 32), (16, 16, 16)]:
         say(f"shape {M}x{N}x{K}")
