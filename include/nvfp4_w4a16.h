@@ -138,6 +138,72 @@ nvfp4_status nvfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t
                                       void* y, int64_t ld_y, int64_t R, int64_t E, int64_t N, int64_t K,
                                       void* workspace, int64_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------ MoE glue --
+ * The steps either side of the grouped GEMM in a mixture-of-experts layer
+ * whose experts take only the tokens routed to them ("Support Nemotron-H
+ * nvfp4 ckpt on Hopper", Changes table, MoE W4A16 execution path: the layer
+ * dispatches tokens to their active experts and runs a fused MoE over them;
+ * the gated FC1 holds the gate and up projections together, the SGLang
+ * compressed-tensors NVFP4 weight-only page, review discussion of the w13
+ * sizing for gated and non-gated experts).  A layer of T tokens, top-k
+ * routing over E experts, hidden size Hd and expert width I runs as
+ *   nvfp4_moe_route -> nvfp4_w4a16_grouped_gemm_gather (FC1, N = 2 I)
+ *   -> nvfp4_moe_silu_mul -> nvfp4_w4a16_grouped_gemm (FC2, K = I, N = Hd)
+ *   -> nvfp4_moe_combine,
+ * every step stream-ordered, with no host synchronisation.
+ *
+ * Routing: topk_ids is device int32 [T][k] (row t: the k experts of token
+ * t, values in [0, E); the caller keeps them distinct per token).  The
+ * (token, slot) pairs p = t*k + j are ordered by expert, ties in pair order
+ * (a stable sort), which defines the grouped rows:
+ *   expert_offsets[e] : first grouped row of expert e; [E] = T*k,
+ *   row_token[r]      : token of grouped row r,              [T*k]
+ *   token_row[p]      : grouped row of pair p = t*k + j,     [T*k]
+ * all device int32, 4-byte aligned.  One workgroup; the result does not
+ * depend on timing.  Ids outside [0, E) give undefined (but in-bounds)
+ * results.  T == 0 returns NVFP4_OK without launching anything (the
+ * outputs are not written).
+ * Errors: T < 0, E < 1 or E > 1024, k < 1 or k > E, T*k >= 2^31, a NULL
+ * array -> INVALID_ARG; misaligned array -> ALIGNMENT. */
+nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int64_t k, int64_t E, int32_t* expert_offsets,
+                             int32_t* row_token, int32_t* token_row, void* stream);
+
+/* Grouped GEMM whose activation rows are gathered on the fly: grouped row r
+ * reads row row_token[r] of x (bf16 [T][ld_x], the tokens in their own
+ * order), so the expert-ordered copy of the activation is never written.
+ * Otherwise as nvfp4_w4a16_grouped_gemm (y is in grouped row order; the
+ * pre-scale, if any, applies to the T token rows).  row_token values must be
+ * in [0, T) (device data, not checked: undefined behaviour otherwise).
+ * Errors: as for nvfp4_w4a16_grouped_gemm, plus T < 0, R > 0 with T == 0,
+ * T * ld_x >= 2^31, row_token NULL (R > 0) -> INVALID_ARG; row_token not
+ * 4-byte aligned -> ALIGNMENT. */
+int64_t nvfp4_w4a16_grouped_gemm_gather_workspace_bytes(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K);
+nvfp4_status nvfp4_w4a16_grouped_gemm_gather(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
+                                             const int32_t* expert_offsets, const void* pre_scale,
+                                             const void* w_repacked, const float* global_scales,
+                                             int global_scale_is_divisor, void* y, int64_t ld_y, int64_t R,
+                                             int64_t E, int64_t N, int64_t K, void* workspace,
+                                             int64_t workspace_bytes, void* stream);
+
+/* Gated SiLU between FC1 and FC2: h is bf16 [R][ld_h] holding the gate
+ * projection in columns [0, I) and the up projection in [I, 2I) (the w13
+ * order, gate first); a[r][i] = RNE_bf16(silu(h[r][i]) * h[r][I + i]) with
+ * silu(v) = v / (1 + exp(-v)) evaluated in fp32.  a is bf16 [R][ld_a].
+ * Errors: R < 0, I < 1, ld_h < 2I, ld_a < I, NULL (R > 0) -> INVALID_ARG;
+ * odd addresses -> ALIGNMENT. */
+nvfp4_status nvfp4_moe_silu_mul(const void* h, int64_t ld_h, int64_t R, int64_t I, void* a, int64_t ld_a,
+                                void* stream);
+
+/* Top-k weighted combine back to token order: out[t][c] =
+ * RNE_bf16(sum_{j=0..k-1} topk_weights[t*k + j] * y[token_row[t*k + j]][c]),
+ * accumulated in fp32 in slot order.  y: bf16 [R][ld_y] (FC2 output in
+ * grouped row order), token_row: from nvfp4_moe_route, topk_weights: device
+ * fp32 [T][k], out: bf16 [T][ld_o].
+ * Errors: T < 0, k < 1, H < 1, ld_y < H, ld_o < H, NULL (T > 0) ->
+ * INVALID_ARG; misaligned pointer -> ALIGNMENT. */
+nvfp4_status nvfp4_moe_combine(const void* y, int64_t ld_y, const int32_t* token_row, const float* topk_weights,
+                               int64_t T, int64_t k, int64_t H, void* out, int64_t ld_o, void* stream);
+
 /* --------------------------------------------------------- test exports --
  * Decode a repacked blob back to bf16 [E][N][ld_out] in canonical order with
  * the same device decode the GEMM kernels use (no global scale applied):

@@ -23,6 +23,17 @@ pages each step follows):
 Grouped (MoE) form: rows offsets[e]..offsets[e+1]-1 use expert e's weights and
 global scale; the pre-quant scale is shared by all experts.
 
+MoE glue (numpy, fp64; the steps either side of the grouped GEMM in a
+mixture-of-experts layer: "Support Nemotron-H nvfp4 ckpt on Hopper", Changes
+table, MoE W4A16 execution path; the gate and up projections held together in
+FC1: SGLang compressed-tensors NVFP4 weight-only page, review discussion):
+
+    moe_route   : the (token, slot) pairs p = t*k + j sorted by expert, ties in
+                  pair order; offsets, row -> token and pair -> row
+    silu_mul    : a = silu(gate) * up with gate = h[:, :I], up = h[:, I:],
+                  silu(v) = v / (1 + exp(-v))                    (fp64, not rounded)
+    combine     : out[t] = sum_j w[t, j] * y[row of (t, j)]      (fp64, not rounded)
+
 Acceptance of a GPU result against the oracle (``accept``): relative Frobenius
 error <= 2e-3, every element within 1e-2 * (|ref| + rms(ref)), and every
 element finite.
@@ -300,3 +311,40 @@ def accept(y, ref, rel_fro_tol: float = REL_FRO_TOL, elem_tol: float = ELEM_TOL)
                 max_abs_err=float(np.nanmax(err)) if err.size else 0.0)
     ok = finite and rel <= tol and bad == 0
     return ok, info
+
+
+# ------------------------------------------------------------ MoE glue ------
+# Plain definitions of the steps around the grouped GEMM.
+
+def moe_route(topk_ids: np.ndarray, E: int):
+    """(offsets [E+1], row_token [T*k], token_row [T*k]) of the pairs p = t*k + j sorted by expert, ties in pair
+    order (numpy's stable sort is the definition written out)."""
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    order = np.argsort(flat, kind="stable")             # grouped row r holds pair order[r]
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(np.bincount(flat, minlength=E))
+    token_row = np.empty(T * k, dtype=np.int64)
+    token_row[order] = np.arange(T * k)
+    return offsets, order // k, token_row
+
+
+def silu_mul(h_bits: np.ndarray) -> np.ndarray:
+    """h bf16 bits [R, 2I] (gate | up) -> silu(gate) * up in fp64, not rounded."""
+    h = bf16_np(h_bits)
+    I = h.shape[1] // 2
+    g, u = h[:, :I], h[:, I:]
+    return g / (1.0 + np.exp(-g)) * u
+
+
+def combine(y_bits: np.ndarray, token_row: np.ndarray, weights: np.ndarray) -> np.ndarray:
+    """y bf16 bits [R, H] in grouped row order, token_row [T*k], weights fp32 [T, k] -> [T, H] fp64, not rounded."""
+    y = bf16_np(y_bits)
+    w = np.asarray(weights, dtype=np.float32).astype(np.float64)
+    T, k = w.shape
+    rows = np.asarray(token_row, dtype=np.int64).reshape(T, k)
+    out = np.zeros((T, y.shape[1]), dtype=np.float64)
+    for j in range(k):
+        out += w[:, j:j + 1] * y[rows[:, j]]
+    return out

@@ -112,3 +112,38 @@ def test_workspace_queries():
     assert L.nvfp4_w4a16_gemm_workspace_bytes(16, 4096, 14336) > 2 * 16 * 4096 * 4
     assert L.nvfp4_w4a16_grouped_gemm_workspace_bytes(128, 128, 1536, 2048) >= 128 * 2048 * 2
     assert L.nvfp4_w4a16_gemm_workspace_bytes(-1, 10, 16) < 0
+
+
+def test_moe_glue_argument_errors_and_empty_calls():
+    L = nv.lib()
+    route = L.nvfp4_moe_route
+    assert route(_p(A), 4, 2, 0, _p(A), _p(A), _p(A), None) == INVALID and "E =" in L.nvfp4_last_error().decode()
+    assert route(_p(A), 4, 2, 2000, _p(A), _p(A), _p(A), None) == INVALID
+    assert route(_p(A), 4, 0, 8, _p(A), _p(A), _p(A), None) == INVALID and "k =" in L.nvfp4_last_error().decode()
+    assert route(_p(A), 4, 9, 8, _p(A), _p(A), _p(A), None) == INVALID
+    assert route(_p(A), -1, 2, 8, _p(A), _p(A), _p(A), None) == INVALID
+    assert route(_p(A), 4, 2, 8, None, _p(A), _p(A), None) == INVALID
+    assert route(_p(A + 2), 4, 2, 8, _p(A), _p(A), _p(A), None) == ALIGN
+    assert route(None, 0, 2, 8, _p(A), None, None, None) == OK                      # zero tokens: no launch
+    silu = L.nvfp4_moe_silu_mul
+    assert silu(_p(A), 100, 4, 64, _p(A), 64, None) == INVALID and "ld_h" in L.nvfp4_last_error().decode()
+    assert silu(_p(A), 128, 4, 64, _p(A), 32, None) == INVALID and "ld_a" in L.nvfp4_last_error().decode()
+    assert silu(_p(A + 1), 128, 4, 64, _p(A), 64, None) == ALIGN
+    assert silu(None, 128, 0, 64, None, 64, None) == OK
+    comb = L.nvfp4_moe_combine
+    assert comb(_p(A), 64, _p(A), _p(A), 4, 2, 0, _p(A), 64, None) == INVALID
+    assert comb(_p(A), 32, _p(A), _p(A), 4, 2, 64, _p(A), 64, None) == INVALID
+    assert comb(_p(A), 64, _p(A + 2), _p(A), 4, 2, 64, _p(A), 64, None) == ALIGN
+    assert comb(None, 64, None, None, 0, 2, 64, None, 64, None) == OK
+    gg = L.nvfp4_w4a16_grouped_gemm_gather
+    args = lambda **kw: [kw.get(n, d) for n, d in [
+        ("x", _p(A)), ("ld_x", 128), ("T", 16), ("rt", _p(A)), ("off", _p(A)), ("pre", None), ("w", _p(A)),
+        ("g", _p(A)), ("div", 0), ("y", _p(A)), ("ld_y", 32), ("R", 32), ("E", 4), ("N", 32), ("K", 128),
+        ("ws", None), ("wsb", 0), ("st", None)]]
+    assert gg(*args(rt=None)) == INVALID and "row_token" in L.nvfp4_last_error().decode()
+    assert gg(*args(rt=_p(A + 2))) == ALIGN
+    assert gg(*args(T=0)) == INVALID
+    assert gg(*args(T=1 << 20, ld_x=1 << 12)) == INVALID and "2^31" in L.nvfp4_last_error().decode()
+    assert gg(*args(R=0)) == OK                                                      # zero rows: no launch
+    assert L.nvfp4_w4a16_grouped_gemm_gather_workspace_bytes(16, 32, 4, 32, 128) == 16 * 128 * 2   # pre-scaled tokens
+    assert L.nvfp4_w4a16_grouped_gemm_gather_workspace_bytes(-1, 32, 4, 32, 128) == -1

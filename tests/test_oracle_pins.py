@@ -342,3 +342,66 @@ def test_acceptance_floor_only_lifts_tiny_outputs():
                   -0.12936933, -0.0099833, 0.01, 0.02, -0.03, 0.004, 0.005, -0.006, 0.007])
     ok, info = oracle.accept(oracle.round_bf16_np(r), r)
     assert ok and info["rel_fro"] > 2e-3
+
+
+# ------------------------------------------------------------ MoE glue -------
+
+def test_moe_route_hand_case():
+    """Tokens 0..2 with top-2 experts (2,0), (0,1), (2,3) over E = 4.  Pairs p = 2t + j choose experts
+    2,0,0,1,2,3; sorted by expert with ties in pair order the rows hold pairs 1,2 | 3 | 0,4 | 5."""
+    off, row_token, token_row = oracle.moe_route(np.array([[2, 0], [0, 1], [2, 3]]), 4)
+    assert off.tolist() == [0, 2, 3, 5, 6]
+    assert row_token.tolist() == [0, 1, 1, 0, 2, 2]
+    assert token_row.tolist() == [3, 0, 1, 2, 4, 5]
+
+
+@pytest.mark.parametrize("T,k,E", [(16, 8, 128), (200, 3, 7), (5, 1, 1), (9, 4, 4)])
+def test_moe_route_matches_brute_force(T, k, E):
+    """Every expert's rows hold exactly its pairs in increasing pair order (an O(P E) scan), and token_row is the
+    inverse of the row order."""
+    g = synth.rng(T * 31 + E)
+    ids = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)])
+    off, row_token, token_row = oracle.moe_route(ids, E)
+    r = 0
+    for e in range(E):
+        assert off[e] == r
+        for p in range(T * k):
+            if ids.reshape(-1)[p] == e:
+                assert row_token[r] == p // k and token_row[p] == r
+                r += 1
+    assert off[E] == r == T * k
+
+
+def test_silu_mul_closed_forms():
+    """silu(v) = v * sigmoid(v) at a few points (math.exp), silu(v) - silu(-v) = v, and up scales the result."""
+    vals = np.array([0.0, 0.5, -0.5, 1.0, -3.0, 4.0, -8.0, 10.0], dtype=np.float32)
+    gate = synth.bf16_bits_from_f32(vals)
+
+    def run(gate_bits, up):
+        up_bits = synth.bf16_bits_from_f32(np.full_like(vals, up))
+        return oracle.silu_mul(np.concatenate([gate_bits[None], up_bits[None]], axis=1))[0]
+
+    v = oracle.bf16_np(gate)
+    s = run(gate, 1.0)
+    for a, x in zip(s, v):
+        assert a == pytest.approx(x / (1.0 + math.exp(-x)), rel=1e-15, abs=0)
+    assert np.allclose(s - run(synth.bf16_bits_from_f32(-vals), 1.0), v, rtol=0, atol=1e-12)
+    assert np.array_equal(run(gate, 2.0), 2 * s)
+
+
+def test_combine_matches_loops_and_one_hot_gather():
+    g = synth.rng(5)
+    T, k, H, E = 6, 3, 40, 5
+    ids = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)])
+    _, _, token_row = oracle.moe_route(ids, E)
+    y = synth.normal_bf16(g, (T * k, H))
+    w = g.random((T, k)).astype(np.float32)
+    out = oracle.combine(y, token_row, w)
+    yv = oracle.bf16_np(y)
+    for t in range(T):
+        for c in range(H):
+            ref = sum(float(w[t, j]) * float(yv[token_row[t * k + j], c]) for j in range(k))
+            assert out[t, c] == pytest.approx(ref, rel=1e-13, abs=1e-300)
+    onehot = np.zeros((T, k), dtype=np.float32)
+    onehot[:, 1] = 1.0
+    assert np.array_equal(oracle.combine(y, token_row, onehot), yv[token_row.reshape(T, k)[:, 1]])

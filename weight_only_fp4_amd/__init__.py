@@ -21,7 +21,7 @@ import os
 import torch
 
 __all__ = ["repack", "repack_bytes", "gemm", "gemm_variant", "grouped_gemm", "dequant", "lib", "Nvfp4Error",
-           "workspace", "gemm_workspace_bytes",
+           "workspace", "gemm_workspace_bytes", "grouped_gemm_gather", "moe_route", "moe_silu_mul", "moe_combine",
            "VARIANT_AUTO", "VARIANT_SMALL_M", "VARIANT_LARGE_M", "VARIANT_MFMA", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4_w4a16.so")
@@ -58,6 +58,14 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_w4a16_grouped_gemm_workspace_bytes.restype = I64
         L.nvfp4_w4a16_grouped_gemm.argtypes = [P, I64, P, P, P, P, I, P, I64, I64, I64, I64, I64, P, I64, P]
         L.nvfp4_w4a16_grouped_gemm.restype = I
+        L.nvfp4_w4a16_grouped_gemm_gather_workspace_bytes.argtypes = [I64, I64, I64, I64, I64]
+        L.nvfp4_w4a16_grouped_gemm_gather_workspace_bytes.restype = I64
+        L.nvfp4_w4a16_grouped_gemm_gather.argtypes = [P, I64, I64, P, P, P, P, P, I, P, I64, I64, I64, I64, I64, P,
+                                                      I64, P]
+        L.nvfp4_w4a16_grouped_gemm_gather.restype = I
+        L.nvfp4_moe_route.argtypes, L.nvfp4_moe_route.restype = [P, I64, I64, I64, P, P, P, P], I
+        L.nvfp4_moe_silu_mul.argtypes, L.nvfp4_moe_silu_mul.restype = [P, I64, I64, I64, P, I64, P], I
+        L.nvfp4_moe_combine.argtypes, L.nvfp4_moe_combine.restype = [P, I64, P, P, I64, I64, I64, P, I64, P], I
         _lib = L
     return _lib
 
@@ -196,4 +204,88 @@ def grouped_gemm(x, expert_offsets, blob, E, N, K, global_scales, divisor=False,
     _check(lib().nvfp4_w4a16_grouped_gemm(_ptr(x), x.stride(0), _ptr(expert_offsets), _ptr(pre_scale), _ptr(blob),
                                           _ptr(global_scales), int(bool(divisor)), _ptr(out), out.stride(0), R, E,
                                           N, K, _ptr(workspace_buf), workspace_buf.numel(), _stream(x.device)))
+    return out
+
+
+# ------------------------------------------------------------------ MoE glue --
+
+def moe_route(topk_ids, E):
+    """topk_ids int32 [T, k] -> (expert_offsets [E+1], row_token [T*k], token_row [T*k]), all int32 on the device:
+    the (token, slot) pairs sorted by expert, ties in pair order."""
+    _dev("topk_ids", topk_ids, torch.int32, 2)
+    if not topk_ids.is_contiguous():
+        raise ValueError("topk_ids must be contiguous")
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    offsets = torch.zeros(E + 1, dtype=torch.int32, device=dev)
+    row_token = torch.empty(T * k, dtype=torch.int32, device=dev)
+    token_row = torch.empty(T * k, dtype=torch.int32, device=dev)
+    _check(lib().nvfp4_moe_route(_ptr(topk_ids), T, k, E, _ptr(offsets), _ptr(row_token), _ptr(token_row),
+                                 _stream(dev)))
+    return offsets, row_token, token_row
+
+
+def grouped_gemm_gather(x, row_token, expert_offsets, blob, E, N, K, global_scales, divisor=False, pre_scale=None,
+                        out=None, workspace_buf=None):
+    """Grouped GEMM whose row r reads token row row_token[r] of x [T, K] (no gathered copy of x is made)."""
+    _dev("x", x, torch.bfloat16, 2)
+    _dev("row_token", row_token, torch.int32, 1)
+    _dev("expert_offsets", expert_offsets, torch.int32, 1)
+    if expert_offsets.shape[0] != E + 1 or not expert_offsets.is_contiguous() or not row_token.is_contiguous():
+        raise ValueError(f"expert_offsets must be a contiguous int32 [{E + 1}], row_token contiguous")
+    if global_scales.numel() != E:
+        raise ValueError(f"global_scales must hold {E} values")
+    T, R = x.shape[0], row_token.shape[0]
+    if x.shape[1] != K:
+        raise ValueError(f"x must be [T, {K}]")
+    if pre_scale is not None:
+        _dev("pre_scale", pre_scale, torch.bfloat16, 1)
+    if out is None:
+        out = torch.zeros((R, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _dev("out", out, torch.bfloat16, 2)
+        if tuple(out.shape) != (R, N):
+            raise ValueError(f"out must be [{R}, {N}]")
+    need = int(lib().nvfp4_w4a16_grouped_gemm_gather_workspace_bytes(T, R, E, N, K))
+    if need < 0:
+        raise ValueError(f"invalid grouped GEMM shape T={T} R={R} E={E} N={N} K={K}")
+    if workspace_buf is None:
+        workspace_buf = workspace(need, x.device)
+    _check(lib().nvfp4_w4a16_grouped_gemm_gather(_ptr(x), x.stride(0), T, _ptr(row_token), _ptr(expert_offsets),
+                                                 _ptr(pre_scale), _ptr(blob), _ptr(global_scales),
+                                                 int(bool(divisor)), _ptr(out), out.stride(0), R, E, N, K,
+                                                 _ptr(workspace_buf), workspace_buf.numel(), _stream(x.device)))
+    return out
+
+
+def moe_silu_mul(h, out=None):
+    """h bf16 [R, 2I] (gate | up) -> silu(gate) * up, bf16 [R, I]."""
+    _dev("h", h, torch.bfloat16, 2)
+    R, I2 = h.shape
+    if I2 % 2:
+        raise ValueError("h must have an even number of columns (gate | up)")
+    I = I2 // 2
+    if out is None:
+        out = torch.empty((R, I), dtype=torch.bfloat16, device=h.device)
+    else:
+        _dev("out", out, torch.bfloat16, 2)
+    _check(lib().nvfp4_moe_silu_mul(_ptr(h), h.stride(0), R, I, _ptr(out), out.stride(0), _stream(h.device)))
+    return out
+
+
+def moe_combine(y, token_row, topk_weights, out=None):
+    """y bf16 [R, H] in grouped row order, token_row int32 [T*k], topk_weights fp32 [T, k] -> bf16 [T, H]."""
+    _dev("y", y, torch.bfloat16, 2)
+    _dev("token_row", token_row, torch.int32, 1)
+    _dev("topk_weights", topk_weights, torch.float32, 2)
+    if not topk_weights.is_contiguous() or not token_row.is_contiguous():
+        raise ValueError("topk_weights and token_row must be contiguous")
+    T, k = topk_weights.shape
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    else:
+        _dev("out", out, torch.bfloat16, 2)
+    _check(lib().nvfp4_moe_combine(_ptr(y), y.stride(0), _ptr(token_row), _ptr(topk_weights), T, k, H, _ptr(out),
+                                   out.stride(0), _stream(y.device)))
     return out

@@ -218,14 +218,15 @@ struct WaveWeights {
 template <int MG, int NT, int D, bool KFULL, typename MidF>
 __device__ __forceinline__ void small_m_pass(const uint16_t* __restrict__ xrow0, int64_t ld_x, int rows,
                                              const WaveWeights& ww, int c0, int c1, int K, const float2* lut,
-                                             float* red_w, int red_ld, int lane, MidF&& mid) {
+                                             float* red_w, int red_ld, int lane, MidF&& mid,
+                                             const int32_t* __restrict__ rix = nullptr) {
     const int g = lane >> 4, q = (lane >> 2) & 3, ai = lane & 3;
     f32x4 acc[NT][MG];
-    uint32_t xoff[MG];   // byte offset of the lane's activation row
+    uint32_t xoff[MG];   // byte offset of the lane's activation row (row rix[m] of xrow0 when gathering)
 #pragma unroll
     for (int mg = 0; mg < MG; ++mg) {
-        const int m = 4 * mg + ai;
-        xoff[mg] = (uint32_t)((int64_t)(m < rows ? m : 0) * ld_x * 2);
+        const int m = 4 * mg + ai, mm = m < rows ? m : 0;
+        xoff[mg] = (uint32_t)((int64_t)(rix ? rix[mm] : mm) * ld_x * 2);
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[j][mg] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -341,7 +342,8 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
                                                          int NU, int KC, int K,
                                                          int N, const float* __restrict__ gscale, int g_is_div,
                                                          uint16_t* __restrict__ y, int64_t ld_y, int64_t rows_dense,
-                                                         const int32_t* __restrict__ offsets, SplitK sk) {
+                                                         const int32_t* __restrict__ offsets, SplitK sk,
+                                                         const int32_t* __restrict__ row_index) {
     constexpr int RLD = NT * 16;
     constexpr int kTileFloats = kSmallRows * RLD;
     constexpr int kPer = (kTileFloats + W * 64 - 1) / (W * 64);   // partial-tile floats per thread
@@ -385,17 +387,19 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
 
     for (int64_t p0 = 0; p0 < count; p0 += kSmallRows) {
         const int rows = (int)((count - p0) < kSmallRows ? (count - p0) : kSmallRows);
-        const uint16_t* xrow0 = x + (row0 + p0) * ld_x;
+        // grouped row r reads activation row row_index[r] when gathering
+        const int32_t* rix = GROUPED && row_index ? row_index + row0 + p0 : nullptr;
+        const uint16_t* xrow0 = rix ? x : x + (row0 + p0) * ld_x;
         if constexpr (MG == 16) {
             small_m_pass16<NT, D, KFULL>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane, mid);
         } else if constexpr (MG > 0) {
             small_m_pass<MG, NT, D, KFULL>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane, mid);
         } else {
             if (rows <= 4)
-                small_m_pass<1, NT, D, KFULL>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane, mid);
+                small_m_pass<1, NT, D, KFULL>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane, mid, rix);
             else
                 small_m_pass<4, NT, (D > 2 ? 2 : D), KFULL>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane,
-                                                           mid);
+                                                           mid, rix);
         }
         __syncthreads();
         const float gv = effective_global_scale(gscale[e], g_is_div);

@@ -39,7 +39,8 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
                                                             int NU, int KC, int K, int N,
                                                             const float* __restrict__ gscale, int g_is_div,
                                                             uint16_t* __restrict__ y, int64_t ld_y, int64_t rows_dense,
-                                                            const int32_t* __restrict__ offsets, int E, SplitK sk) {
+                                                            const int32_t* __restrict__ offsets, int E, SplitK sk,
+                                                            const int32_t* __restrict__ row_index) {
     constexpr int W = UW * KW;                                     // waves per workgroup
     // Weights stream past the caches (non-temporal) when one row tile covers
     // all rows (tiles of up to 32 rows, dense): no other workgroup reads the
@@ -125,7 +126,9 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
     // chunk of part p / CPIECES.  Rows past `rows` read row 0 (outputs never
     // stored); pieces past K are zeroed when staged.  Offsets within the
     // row tile fit 32 bits (the host bounds ld_x).
-    const uint16_t* xtile = x + row0 * ld_x;
+    // grouped row r reads activation row row_index[r] when gathering
+    const bool gather = GROUPED && row_index != nullptr;
+    const uint16_t* xtile = gather ? x : x + row0 * ld_x;
     uint32_t a_xo[APT], a_off[APT];
     int a_c0[APT], a_last[APT];
 #pragma unroll
@@ -136,7 +139,8 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
         a_c0[i] = part_begin(qa);
         const int la = part_begin(qa + 1) - a_c0[i];
         a_last[i] = la > 0 ? la - 1 : 0;
-        a_xo[i] = (uint32_t)((pr < rows ? pr : 0) * ld_x);
+        const int prr = pr < rows ? pr : 0;
+        a_xo[i] = (uint32_t)((gather ? (int64_t)row_index[row0 + prr] : (int64_t)prr) * ld_x);
         a_off[i] = (uint32_t)(qa * BM * kTileLDA + pr * kTileLDA + (within & 15) * 8);
     }
 

@@ -12,6 +12,7 @@
 #include "../../include/nvfp4_w4a16.h"
 #include "kernels_aux.h"
 #include "kernels_gemm.h"
+#include "kernels_moe.h"
 #include "kernels_tile.h"
 #include "launch_mfma.h"
 
@@ -120,28 +121,28 @@ SmallShape small_m_shape(const Layout& L, int64_t rows, bool grouped) {
 template <int MG, int NT, int W, int D, bool GROUPED>
 void launch_small_t(const SmallShape& s, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
                     const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows, const int32_t* offsets,
-                    SplitK sk, hipStream_t st) {
+                    SplitK sk, hipStream_t st, const int32_t* row_index = nullptr) {
     const BlobView bv = make_view(L, blob);
     const dim3 grid((unsigned)s.groups, GROUPED ? (unsigned)L.E : 1u, (unsigned)s.S);
     if (L.K % kChunkK == 0)
         hipLaunchKernelGGL((k_gemm_small_m<MG, NT, W, D, GROUPED, true>), grid, dim3(W * 64), 0, st, x, ld_x, bv,
-                           (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, sk);
+                           (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, sk, row_index);
     else
         hipLaunchKernelGGL((k_gemm_small_m<MG, NT, W, D, GROUPED, false>), grid, dim3(W * 64), 0, st, x, ld_x, bv,
-                           (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, sk);
+                           (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, sk, row_index);
 }
 
 template <bool GROUPED>
 nvfp4_status launch_small(const SmallShape& s, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
                           const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows_dense,
-                          const int32_t* offsets, SplitK sk, hipStream_t st) {
+                          const int32_t* offsets, SplitK sk, hipStream_t st, const int32_t* row_index = nullptr) {
     bool done = false;
     if constexpr (GROUPED) {
         switch (s.w) {
-            case 1: launch_small_t<0, 1, 1, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st); break;
-            case 2: launch_small_t<0, 1, 2, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st); break;
-            case 4: launch_small_t<0, 1, 4, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st); break;
-            default: launch_small_t<0, 1, 8, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st); break;
+            case 1: launch_small_t<0, 1, 1, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st, row_index); break;
+            case 2: launch_small_t<0, 1, 2, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st, row_index); break;
+            case 4: launch_small_t<0, 1, 4, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st, row_index); break;
+            default: launch_small_t<0, 1, 8, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st, row_index); break;
         }
         done = true;
     } else {
@@ -240,25 +241,27 @@ SplitK split_k(int S, uint8_t* ws, const Workspace& wl) {
 template <int MS, int NT, int UW, int KW, int D, bool GROUPED>
 void launch_tile_t(const TileShape& t, const Layout& L, const uint16_t* x, int64_t ld_x, BlobView bv, const float* gs,
                    int g_div, uint16_t* y, int64_t ld_y, int64_t rows, const int32_t* offsets, SplitK sk,
-                   hipStream_t st) {
+                   hipStream_t st, const int32_t* row_index) {
     const dim3 grid((unsigned)t.groups, (unsigned)t.mtiles, (unsigned)t.S);
     if (L.K % kChunkK == 0)
         hipLaunchKernelGGL((k_gemm_tile<MS, NT, UW, KW, D, GROUPED, true>), grid, dim3(UW * KW * 64), 0, st, x, ld_x,
-                           bv, (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, (int)L.E, sk);
+                           bv, (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, (int)L.E, sk,
+                           row_index);
     else
         hipLaunchKernelGGL((k_gemm_tile<MS, NT, UW, KW, D, GROUPED, false>), grid, dim3(UW * KW * 64), 0, st, x, ld_x,
-                           bv, (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, (int)L.E, sk);
+                           bv, (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, (int)L.E, sk,
+                           row_index);
 }
 
 template <bool GROUPED>
 nvfp4_status launch_tile(const TileShape& t, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
                          const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows, const int32_t* offsets,
-                         uint8_t* ws, const Workspace& wl, hipStream_t st) {
+                         uint8_t* ws, const Workspace& wl, hipStream_t st, const int32_t* row_index = nullptr) {
     if (t.mtiles > 65535) return fail(NVFP4_ERR_INVALID_ARG, "tile GEMM: %lld row tiles exceed the grid limit", (long long)t.mtiles);
     const SplitK sk = split_k(t.S, ws, wl);
     const BlobView bv = make_view(L, blob);
 #define NVFP4_TILE(MS, NT, UW, KW, D) \
-    launch_tile_t<MS, NT, UW, KW, D, GROUPED>(t, L, x, ld_x, bv, gs, g_div, y, ld_y, rows, offsets, sk, st)
+    launch_tile_t<MS, NT, UW, KW, D, GROUPED>(t, L, x, ld_x, bv, gs, g_div, y, ld_y, rows, offsets, sk, st, row_index)
     if constexpr (GROUPED) {
         NVFP4_TILE(4, 4, 4, 1, 2);
     } else {
@@ -381,6 +384,41 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
     return launch_tile<false>(t, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, wsb, wl, st);
 }
 
+// Grouped GEMM, shared by the plain and the gathering entry points: the
+// activation has x_rows rows; grouped row r reads row row_index[r] of it
+// (row r itself when row_index is NULL).
+nvfp4_status grouped_gemm(const char* fn, const void* x, int64_t ld_x, int64_t x_rows, const int32_t* row_index,
+                          const int32_t* expert_offsets, const void* pre_scale, const void* w_repacked,
+                          const float* global_scales, int global_scale_is_divisor, void* y, int64_t ld_y, int64_t R,
+                          int64_t E, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes, void* stream) {
+    nvfp4_status s = check_weight_shape(fn, E, N, K);
+    if (s != NVFP4_OK) return s;
+    const Workspace wl = workspace_layout(1, 0, 0, x_rows, K, pre_scale != nullptr);
+    s = check_gemm_io(fn, x, ld_x, pre_scale, w_repacked, global_scales, y, ld_y, R, N, K, workspace, workspace_bytes,
+                      wl.total);
+    if (s != NVFP4_OK) return s;
+    if (!expert_offsets) return fail(NVFP4_ERR_INVALID_ARG, "%s: expert_offsets is NULL", fn);
+    if (!aligned(expert_offsets, 4)) return fail(NVFP4_ERR_ALIGNMENT, "%s: expert_offsets must be 4-byte aligned", fn);
+    if (R > (int64_t)1 << 31) return fail(NVFP4_ERR_INVALID_ARG, "%s: R = %lld exceeds int32 offsets", fn, (long long)R);
+    if (R == 0) return ok();   // zero rows: nothing is launched
+    const Layout L = make_layout(E, N, K);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* wsb = static_cast<uint8_t*>(workspace);
+    const uint16_t* xp;
+    s = apply_prescale(x, ld_x, pre_scale, x_rows, K, pre_scale ? wsb + wl.prescale : nullptr, xp, st);
+    if (s != NVFP4_OK) return s;
+    const uint8_t* blob = static_cast<const uint8_t*>(w_repacked);
+    uint16_t* yo = static_cast<uint16_t*>(y);
+    const int g_div = global_scale_is_divisor != 0;
+    // Few rows per expert on average: the weight stream dominates, use the small-M kernel (passes of 16 rows).
+    if (R <= (int64_t)kSmallRows * E)
+        return launch_small<true>(small_m_shape(L, R, true), L, xp, ld_x, blob, global_scales, g_div, yo, ld_y, 0,
+                                  expert_offsets, split_k(1, wsb, wl), st, row_index);
+    const TileShape t = tile_shape(L, R, true);
+    return launch_tile<true>(t, L, xp, ld_x, blob, global_scales, g_div, yo, ld_y, R, expert_offsets, wsb, wl, st,
+                             row_index);
+}
+
 }  // namespace
 
 extern "C" {
@@ -459,32 +497,86 @@ nvfp4_status nvfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t
                                       const void* w_repacked, const float* global_scales, int global_scale_is_divisor,
                                       void* y, int64_t ld_y, int64_t R, int64_t E, int64_t N, int64_t K,
                                       void* workspace, int64_t workspace_bytes, void* stream) {
-    const char* fn = "nvfp4_w4a16_grouped_gemm";
-    nvfp4_status s = check_weight_shape(fn, E, N, K);
-    if (s != NVFP4_OK) return s;
-    const Workspace wl = workspace_layout(1, 0, 0, R, K, pre_scale != nullptr);
-    s = check_gemm_io(fn, x, ld_x, pre_scale, w_repacked, global_scales, y, ld_y, R, N, K, workspace, workspace_bytes,
-                      wl.total);
-    if (s != NVFP4_OK) return s;
+    return grouped_gemm("nvfp4_w4a16_grouped_gemm", x, ld_x, R, nullptr, expert_offsets, pre_scale, w_repacked,
+                        global_scales, global_scale_is_divisor, y, ld_y, R, E, N, K, workspace, workspace_bytes, stream);
+}
+
+int64_t nvfp4_w4a16_grouped_gemm_gather_workspace_bytes(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K) {
+    if (T < 0 || R < 0 || check_weight_shape("nvfp4_w4a16_grouped_gemm_gather_workspace_bytes", E, N, K) != NVFP4_OK)
+        return -1;
+    return workspace_layout(1, 0, 0, T, K, true).total;   // the pre-scaled token rows
+}
+
+nvfp4_status nvfp4_w4a16_grouped_gemm_gather(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
+                                             const int32_t* expert_offsets, const void* pre_scale,
+                                             const void* w_repacked, const float* global_scales,
+                                             int global_scale_is_divisor, void* y, int64_t ld_y, int64_t R,
+                                             int64_t E, int64_t N, int64_t K, void* workspace,
+                                             int64_t workspace_bytes, void* stream) {
+    const char* fn = "nvfp4_w4a16_grouped_gemm_gather";
+    if (T < 0) return fail(NVFP4_ERR_INVALID_ARG, "%s: token count %lld is negative", fn, (long long)T);
+    if (R > 0 && !row_token) return fail(NVFP4_ERR_INVALID_ARG, "%s: row_token is NULL", fn);
+    if (!aligned(row_token, 4)) return fail(NVFP4_ERR_ALIGNMENT, "%s: row_token must be 4-byte aligned", fn);
+    if (R > 0 && T == 0) return fail(NVFP4_ERR_INVALID_ARG, "%s: %lld rows gather from 0 tokens", fn, (long long)R);
+    // the kernels address a gathered row with a 32-bit byte offset from x
+    if (T * ld_x >= ((int64_t)1 << 31))
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: T * ld_x = %lld must stay below 2^31", fn, (long long)(T * ld_x));
+    return grouped_gemm(fn, x, ld_x, T, row_token, expert_offsets, pre_scale, w_repacked, global_scales,
+                        global_scale_is_divisor, y, ld_y, R, E, N, K, workspace, workspace_bytes, stream);
+}
+
+// ------------------------------------------------------------------ MoE --
+
+nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int64_t k, int64_t E, int32_t* expert_offsets,
+                             int32_t* row_token, int32_t* token_row, void* stream) {
+    const char* fn = "nvfp4_moe_route";
+    if (T < 0) return fail(NVFP4_ERR_INVALID_ARG, "%s: token count %lld is negative", fn, (long long)T);
+    if (E < 1 || E > kRouteMaxExperts)
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: E = %lld must be in [1, %d]", fn, (long long)E, kRouteMaxExperts);
+    if (k < 1 || k > E) return fail(NVFP4_ERR_INVALID_ARG, "%s: k = %lld must be in [1, E]", fn, (long long)k);
+    if (T * k >= ((int64_t)1 << 31)) return fail(NVFP4_ERR_INVALID_ARG, "%s: T * k must stay below 2^31", fn);
     if (!expert_offsets) return fail(NVFP4_ERR_INVALID_ARG, "%s: expert_offsets is NULL", fn);
-    if (!aligned(expert_offsets, 4)) return fail(NVFP4_ERR_ALIGNMENT, "%s: expert_offsets must be 4-byte aligned", fn);
-    if (R > (int64_t)1 << 31) return fail(NVFP4_ERR_INVALID_ARG, "%s: R = %lld exceeds int32 offsets", fn, (long long)R);
-    if (R == 0) return ok();   // zero rows: nothing is launched
-    const Layout L = make_layout(E, N, K);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    uint8_t* wsb = static_cast<uint8_t*>(workspace);
-    const uint16_t* xp;
-    s = apply_prescale(x, ld_x, pre_scale, R, K, pre_scale ? wsb + wl.prescale : nullptr, xp, st);
-    if (s != NVFP4_OK) return s;
-    const uint8_t* blob = static_cast<const uint8_t*>(w_repacked);
-    uint16_t* yo = static_cast<uint16_t*>(y);
-    const int g_div = global_scale_is_divisor != 0;
-    // Few rows per expert on average: the weight stream dominates, use the small-M kernel (passes of 16 rows).
-    if (R <= (int64_t)kSmallRows * E)
-        return launch_small<true>(small_m_shape(L, R, true), L, xp, ld_x, blob, global_scales, g_div, yo, ld_y, 0,
-                                  expert_offsets, split_k(1, wsb, wl), st);
-    const TileShape t = tile_shape(L, R, true);
-    return launch_tile<true>(t, L, xp, ld_x, blob, global_scales, g_div, yo, ld_y, R, expert_offsets, wsb, wl, st);
+    if (T > 0 && (!topk_ids || !row_token || !token_row))
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: topk_ids, row_token and token_row must not be NULL", fn);
+    if (!aligned(topk_ids, 4) || !aligned(expert_offsets, 4) || !aligned(row_token, 4) || !aligned(token_row, 4))
+        return fail(NVFP4_ERR_ALIGNMENT, "%s: int32 arrays must be 4-byte aligned", fn);
+    if (T == 0) return ok();   // zero tokens: nothing is launched
+    hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(kRouteThreads), 0, static_cast<hipStream_t>(stream), topk_ids,
+                       T * k, (int)E, expert_offsets, row_token, token_row, (int)k);
+    return launched(fn);
+}
+
+nvfp4_status nvfp4_moe_silu_mul(const void* h, int64_t ld_h, int64_t R, int64_t I, void* a, int64_t ld_a,
+                                void* stream) {
+    const char* fn = "nvfp4_moe_silu_mul";
+    if (R < 0 || I < 1) return fail(NVFP4_ERR_INVALID_ARG, "%s: R = %lld, I = %lld", fn, (long long)R, (long long)I);
+    if (ld_h < 2 * I) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_h = %lld < 2 I = %lld", fn, (long long)ld_h, (long long)(2 * I));
+    if (ld_a < I) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_a = %lld < I = %lld", fn, (long long)ld_a, (long long)I);
+    if (R > 0 && (!h || !a)) return fail(NVFP4_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(h, 2) || !aligned(a, 2)) return fail(NVFP4_ERR_ALIGNMENT, "%s: bf16 arrays must be 2-byte aligned", fn);
+    if (R == 0) return ok();
+    const int64_t threads = R * ((I + 7) / 8);
+    hipLaunchKernelGGL(k_moe_silu_mul, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(h), ld_h, R, I,
+                       static_cast<uint16_t*>(a), ld_a);
+    return launched(fn);
+}
+
+nvfp4_status nvfp4_moe_combine(const void* y, int64_t ld_y, const int32_t* token_row, const float* topk_weights,
+                               int64_t T, int64_t k, int64_t H, void* out, int64_t ld_o, void* stream) {
+    const char* fn = "nvfp4_moe_combine";
+    if (T < 0 || k < 1 || H < 1)
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: T = %lld, k = %lld, H = %lld", fn, (long long)T, (long long)k, (long long)H);
+    if (ld_y < H || ld_o < H) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_y and ld_o must be >= H", fn);
+    if (T > 0 && (!y || !token_row || !topk_weights || !out)) return fail(NVFP4_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(y, 2) || !aligned(out, 2) || !aligned(token_row, 4) || !aligned(topk_weights, 4))
+        return fail(NVFP4_ERR_ALIGNMENT, "%s: misaligned pointer", fn);
+    if (T == 0) return ok();
+    const int64_t threads = T * ((H + 7) / 8);
+    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(y), ld_y, token_row,
+                       topk_weights, T, (int)k, H, static_cast<uint16_t*>(out), ld_o);
+    return launched(fn);
 }
 
 }  // extern "C"
