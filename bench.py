@@ -160,6 +160,64 @@ def make_grouped(name, T, fc, *, seed=1004, E=128, topk=8):
     return wl
 
 
+def make_moe_layer(name, T, *, seed=1004, E=128, topk=8, hidden=2048, inter=768):
+    """A whole MoE layer on the device: routing, FC1 with the token gather fused (N = 2 inter), gated SiLU,
+    FC2 (K = inter), top-k combine.  Weight copies rotate as for the grouped workloads."""
+    import numpy as np
+    import torch
+    import synth
+    import weight_only_fp4_amd as nv
+    dev = "cuda:0"
+    route = synth.zipf_routing(synth.rng(synth.routing_seed(seed)), T, E, topk)
+    counts = np.bincount(route.reshape(-1), minlength=E)
+    R, active = T * topk, int(np.count_nonzero(counts))
+    w_bytes = active * 0.5625 * (2 * inter * hidden + hidden * inter)
+    copies = max(1, -(-(512 << 20) // int(w_bytes)))
+    sd = seed * 10 + 5
+    ids = torch.from_numpy(route.astype(np.int32)).to(dev)
+    x = synth.device_normal_bf16((T, hidden), sd, dev)
+    wts = torch.from_numpy(synth.rng(sd + 1).random((T, topk)).astype(np.float32)).to(dev)
+    b1 = nv.repack(synth.device_codes((E, 2 * inter, hidden // 2), sd + 2, dev),
+                   synth.device_scales((E, 2 * inter, hidden // 16), sd + 3, "pow2_mant", dev))
+    b2 = nv.repack(synth.device_codes((E, hidden, inter // 2), sd + 4, dev),
+                   synth.device_scales((E, hidden, inter // 16), sd + 5, "pow2_mant", dev))
+    blobs = [(b1, b2)] + [(b1.clone(), b2.clone()) for _ in range(copies - 1)]
+    v = synth.rng(sd + 6).integers(-2, 3, size=(2, E))
+    g1 = torch.tensor((np.exp2(v[0].astype(np.float64)) / 2688.0).astype(np.float32), device=dev)
+    g2 = torch.tensor((np.exp2(v[1].astype(np.float64)) / 2688.0).astype(np.float32), device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_token = torch.empty(R, dtype=torch.int32, device=dev)
+    token_row = torch.empty(R, dtype=torch.int32, device=dev)
+    h = torch.empty((R, 2 * inter), dtype=torch.bfloat16, device=dev)
+    a = torch.empty((R, inter), dtype=torch.bfloat16, device=dev)
+    y2 = torch.empty((R, hidden), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, hidden), dtype=torch.bfloat16, device=dev)
+    L = nv.lib()
+    ws1 = nv.workspace(L.nvfp4_w4a16_grouped_gemm_gather_workspace_bytes(T, R, E, 2 * inter, hidden), dev)
+    ws2 = nv.workspace(L.nvfp4_w4a16_grouped_gemm_workspace_bytes(R, E, hidden, inter), dev)
+    wsr = nv.workspace(L.nvfp4_moe_route_workspace_bytes(T, topk, E), dev)
+    st = lambda: nv._stream(x.device)
+
+    def launch(i):
+        w1, w2 = blobs[i % copies]
+        nv._check(L.nvfp4_moe_route(nv._ptr(ids), T, topk, E, nv._ptr(off), nv._ptr(row_token), nv._ptr(token_row),
+                                    nv._ptr(wsr), wsr.numel(), st()))
+        nv.grouped_gemm_gather(x, row_token, off, w1, E, 2 * inter, hidden, g1, out=h, workspace_buf=ws1)
+        nv.moe_silu_mul(h, out=a)
+        nv.grouped_gemm(a, off, w2, E, hidden, inter, g2, out=y2, workspace_buf=ws2)
+        nv.moe_combine(y2, token_row, wts, out=out)
+
+    # algorithmic bytes of the layer: active weights, the tokens in and out, routing ids and weights
+    ab = w_bytes + 2.0 * T * hidden * 2 + 8.0 * T * topk
+    flops = 2.0 * R * hidden * (2 * inter) + 2.0 * R * inter * hidden
+    bound = "hbm" if flops / ab < (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) else "mfma"
+    meta = {"E": E, "topk": topk, "T": T, "R": R, "hidden": hidden, "inter": inter, "active_experts": active,
+            "weight_copies": copies, "steps_per_call": "route, FC1 (gather), SiLU, FC2, combine"}
+    wl = Workload(name, "moe_layer", "moe_layer", ab, flops, launch, copies, meta, bound)
+    wl.tensors = dict(x=x, out=out, blobs=blobs)
+    return wl
+
+
 def workload_specs():
     """name -> builder (the headline first)."""
     return {
@@ -188,6 +246,8 @@ def workload_specs():
         "moe_fc2_T16": lambda: make_grouped("moe_fc2_T16", 16, "fc2"),
         "moe_fc1_T2048": lambda: make_grouped("moe_fc1_T2048", 2048, "fc1"),
         "moe_fc2_T2048": lambda: make_grouped("moe_fc2_T2048", 2048, "fc2"),
+        "moe_layer_T16": lambda: make_moe_layer("moe_layer_T16", 16),
+        "moe_layer_T2048": lambda: make_moe_layer("moe_layer_T2048", 2048),
     }
 
 

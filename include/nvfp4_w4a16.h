@@ -159,14 +159,19 @@ nvfp4_status nvfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t
  *   expert_offsets[e] : first grouped row of expert e; [E] = T*k,
  *   row_token[r]      : token of grouped row r,              [T*k]
  *   token_row[p]      : grouped row of pair p = t*k + j,     [T*k]
- * all device int32, 4-byte aligned.  One workgroup; the result does not
- * depend on timing.  Ids outside [0, E) give undefined (but in-bounds)
- * results.  T == 0 returns NVFP4_OK without launching anything (the
- * outputs are not written).
+ * all device int32, 4-byte aligned.  The result does not depend on timing.
+ * workspace: nvfp4_moe_route_workspace_bytes(T, k, E) bytes of device
+ * scratch (4-byte aligned, no initial contents needed; calls that may
+ * overlap in time need their own).  Ids outside [0, E) give undefined (but
+ * in-bounds) results.  T == 0 returns NVFP4_OK without launching anything
+ * (the outputs are not written).
  * Errors: T < 0, E < 1 or E > 1024, k < 1 or k > E, T*k >= 2^31, a NULL
- * array -> INVALID_ARG; misaligned array -> ALIGNMENT. */
+ * array -> INVALID_ARG; misaligned array or workspace -> ALIGNMENT;
+ * workspace too small -> BUFFER_TOO_SMALL. */
+int64_t nvfp4_moe_route_workspace_bytes(int64_t T, int64_t k, int64_t E);   /* < 0 if invalid */
 nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int64_t k, int64_t E, int32_t* expert_offsets,
-                             int32_t* row_token, int32_t* token_row, void* stream);
+                             int32_t* row_token, int32_t* token_row, void* workspace, int64_t workspace_bytes,
+                             void* stream);
 
 /* Grouped GEMM whose activation rows are gathered on the fly: grouped row r
  * reads row row_token[r] of x (bf16 [T][ld_x], the tokens in their own

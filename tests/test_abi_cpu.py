@@ -116,15 +116,18 @@ def test_workspace_queries():
 
 def test_moe_glue_argument_errors_and_empty_calls():
     L = nv.lib()
-    route = L.nvfp4_moe_route
-    assert route(_p(A), 4, 2, 0, _p(A), _p(A), _p(A), None) == INVALID and "E =" in L.nvfp4_last_error().decode()
-    assert route(_p(A), 4, 2, 2000, _p(A), _p(A), _p(A), None) == INVALID
-    assert route(_p(A), 4, 0, 8, _p(A), _p(A), _p(A), None) == INVALID and "k =" in L.nvfp4_last_error().decode()
-    assert route(_p(A), 4, 9, 8, _p(A), _p(A), _p(A), None) == INVALID
-    assert route(_p(A), -1, 2, 8, _p(A), _p(A), _p(A), None) == INVALID
-    assert route(_p(A), 4, 2, 8, None, _p(A), _p(A), None) == INVALID
-    assert route(_p(A + 2), 4, 2, 8, _p(A), _p(A), _p(A), None) == ALIGN
-    assert route(None, 0, 2, 8, _p(A), None, None, None) == OK                      # zero tokens: no launch
+    route = lambda ids, T, k, E, off, rt, tr, ws=_p(A), wsb=1 << 20: L.nvfp4_moe_route(ids, T, k, E, off, rt, tr,
+                                                                                       ws, wsb, None)
+    assert route(_p(A), 4, 2, 0, _p(A), _p(A), _p(A)) == INVALID and "E =" in L.nvfp4_last_error().decode()
+    assert route(_p(A), 4, 2, 2000, _p(A), _p(A), _p(A)) == INVALID
+    assert route(_p(A), 4, 0, 8, _p(A), _p(A), _p(A)) == INVALID and "k =" in L.nvfp4_last_error().decode()
+    assert route(_p(A), 4, 9, 8, _p(A), _p(A), _p(A)) == INVALID
+    assert route(_p(A), -1, 2, 8, _p(A), _p(A), _p(A)) == INVALID
+    assert route(_p(A), 4, 2, 8, None, _p(A), _p(A)) == INVALID
+    assert route(_p(A + 2), 4, 2, 8, _p(A), _p(A), _p(A)) == ALIGN
+    assert route(_p(A), 4, 2, 8, _p(A), _p(A), _p(A), wsb=8) == SMALL and "workspace" in L.nvfp4_last_error().decode()
+    assert route(None, 0, 2, 8, _p(A), None, None, None, 0) == OK                    # zero tokens: no launch
+    assert L.nvfp4_moe_route_workspace_bytes(2048, 8, 128) == 16 * 128 * 4            # one count per block, expert
     silu = L.nvfp4_moe_silu_mul
     assert silu(_p(A), 100, 4, 64, _p(A), 64, None) == INVALID and "ld_h" in L.nvfp4_last_error().decode()
     assert silu(_p(A), 128, 4, 64, _p(A), 32, None) == INVALID and "ld_a" in L.nvfp4_last_error().decode()

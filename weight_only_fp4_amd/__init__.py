@@ -63,7 +63,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_w4a16_grouped_gemm_gather.argtypes = [P, I64, I64, P, P, P, P, P, I, P, I64, I64, I64, I64, I64, P,
                                                       I64, P]
         L.nvfp4_w4a16_grouped_gemm_gather.restype = I
-        L.nvfp4_moe_route.argtypes, L.nvfp4_moe_route.restype = [P, I64, I64, I64, P, P, P, P], I
+        L.nvfp4_moe_route_workspace_bytes.argtypes = [I64, I64, I64]
+        L.nvfp4_moe_route_workspace_bytes.restype = I64
+        L.nvfp4_moe_route.argtypes, L.nvfp4_moe_route.restype = [P, I64, I64, I64, P, P, P, P, I64, P], I
         L.nvfp4_moe_silu_mul.argtypes, L.nvfp4_moe_silu_mul.restype = [P, I64, I64, I64, P, I64, P], I
         L.nvfp4_moe_combine.argtypes, L.nvfp4_moe_combine.restype = [P, I64, P, P, I64, I64, I64, P, I64, P], I
         _lib = L
@@ -220,8 +222,12 @@ def moe_route(topk_ids, E):
     offsets = torch.zeros(E + 1, dtype=torch.int32, device=dev)
     row_token = torch.empty(T * k, dtype=torch.int32, device=dev)
     token_row = torch.empty(T * k, dtype=torch.int32, device=dev)
+    need = int(lib().nvfp4_moe_route_workspace_bytes(T, k, E))
+    if need < 0:
+        raise ValueError(f"invalid routing shape T={T} k={k} E={E}")
+    ws = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
     _check(lib().nvfp4_moe_route(_ptr(topk_ids), T, k, E, _ptr(offsets), _ptr(row_token), _ptr(token_row),
-                                 _stream(dev)))
+                                 _ptr(ws), ws.numel(), _stream(dev)))
     return offsets, row_token, token_row
 
 

@@ -9,9 +9,9 @@
 
 namespace nvfp4 {
 
-constexpr int kRouteThreads = 1024;          // one workgroup
+constexpr int kRouteThreads = 1024;                 // pairs per workgroup
 constexpr int kRouteWaves = kRouteThreads / 64;
-constexpr int kRouteMaxExperts = 1024;       // LDS: per-wave count table of kRouteWaves x E
+constexpr int kRouteMaxExperts = kRouteThreads;     // one expert per thread in the scans
 
 // Routing of P = T k (token, slot) pairs, pair p = t k + j choosing expert
 // ids[p].  Grouped rows are the pairs sorted by expert, ties kept in pair
@@ -19,102 +19,160 @@ constexpr int kRouteMaxExperts = 1024;       // LDS: per-wave count table of kRo
 //   offsets[e]     = number of pairs with an expert below e (offsets[E] = P),
 //   row_token[r]   = token of grouped row r,
 //   token_row[p]   = grouped row of pair p.
-// One workgroup: the pairs are counted with LDS atomics (a sum, order-free),
-// the counts scanned, then the pairs are placed in rounds of 1024: each wave
-// ranks its 64 pairs among equal experts with ballots over the expert bits,
-// and a wave's pairs follow those of the earlier waves of the round and of
-// earlier rounds.  Ids outside [0, E) are clamped for addressing only (the
-// result is then meaningless, but every access stays in bounds).
-__global__ void __launch_bounds__(kRouteThreads) k_moe_route(const int32_t* __restrict__ ids, int64_t P, int E,
-                                                              int32_t* __restrict__ offsets,
-                                                              int32_t* __restrict__ row_token,
-                                                              int32_t* __restrict__ token_row, int k) {
-    __shared__ int cnt[kRouteWaves][kRouteMaxExperts];
-    __shared__ int running[kRouteMaxExperts + 1];
-    __shared__ int wsum[kRouteWaves];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    auto expert = [&](int64_t p) {
-        const int e = ids[p];
-        return e < 0 ? 0 : (e >= E ? E - 1 : e);
-    };
+// Three launches over blocks of kRouteThreads pairs (block b: pairs
+// 1024 b .. 1024 b + 1023, wave w of its workgroup: 64 of them):
+//   count  - per block and expert, the number of pairs (hist[b][e]);
+//   scan   - offsets, and each block's first row per expert
+//            (hist[b][e] = offsets[e] + the pairs of e in blocks before b);
+//   place  - a pair's row is its block's first row for its expert, plus the
+//            pairs of that expert in the earlier waves of the block, plus its
+//            rank among the equal-expert lanes of its wave.
+// A wave finds the lanes holding the same expert as each lane with one
+// ballot per expert bit; the lowest such lane speaks for the group.  Ids
+// outside [0, E) are clamped for addressing only (the result is then
+// meaningless, but every access stays in bounds).
+struct RouteMatch {
+    int e;           // the lane's expert (clamped; 0 past the end)
+    uint64_t same;   // lanes of the wave with the same expert (0 past the end)
+    int rank;        // lanes of the group below this one
+};
 
-    // ---- counts and their exclusive scan
-    for (int e = tid; e < E; e += kRouteThreads) running[e] = 0;
-    __syncthreads();
-    for (int64_t p = tid; p < P; p += kRouteThreads) atomicAdd(&running[expert(p)], 1);
-    __syncthreads();
-    {
-        // each thread scans a contiguous run of experts, then the runs' totals are scanned
-        constexpr int kPer = kRouteMaxExperts / kRouteThreads > 0 ? kRouteMaxExperts / kRouteThreads : 1;
-        const int e0 = tid * kPer;
-        int local[kPer];
-        int sum = 0;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            local[i] = e0 + i < E ? running[e0 + i] : 0;
-            sum += local[i];
-        }
-        // inclusive scan of the per-thread sums: within the wave, then across waves
-        int v = sum;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int t = __shfl_up(v, d);
-            if (lane >= d) v += t;
-        }
-        if (lane == 63) wsum[w] = v;
-        __syncthreads();
-        int before = 0;
-        for (int i = 0; i < w; ++i) before += wsum[i];
-        int run = before + v - sum;   // exclusive prefix of this thread's run
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            if (e0 + i < E) {
-                running[e0 + i] = run;
-                offsets[e0 + i] = run;
-            }
-            run += local[i];
-        }
-        if (tid == kRouteThreads - 1) offsets[E] = (int)P;
-    }
-    __syncthreads();
-
-    // ---- stable placement, 1024 pairs per round
+__device__ __forceinline__ RouteMatch route_match(const int32_t* __restrict__ ids, int64_t p, int64_t P, int E) {
+    const int lane = threadIdx.x & 63;
+    const bool valid = p < P;
+    const int v = valid ? ids[p] : 0;
+    RouteMatch m;
+    m.e = v < 0 ? 0 : (v >= E ? E - 1 : v);
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
-    for (int64_t base = 0; base < P; base += kRouteThreads) {
-        for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) cnt[i / E][i % E] = 0;
-        __syncthreads();
-        const int64_t p = base + tid;
-        const bool valid = p < P;
-        const int e = valid ? expert(p) : 0;
-        uint64_t same = __ballot(valid);
-        for (int b = 0; b < nbits; ++b) {
-            const uint64_t ones = __ballot(valid && ((e >> b) & 1));
-            same &= ((e >> b) & 1) ? ones : ~ones;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const uint64_t ones = __ballot(valid && ((m.e >> b) & 1));
+        same &= ((m.e >> b) & 1) ? ones : ~ones;
+    }
+    m.same = valid ? same : 0ull;
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    m.rank = __popcll(m.same & below);
+    return m;
+}
+
+__global__ void __launch_bounds__(kRouteThreads) k_moe_route_count(const int32_t* __restrict__ ids, int64_t P, int E,
+                                                                    int32_t* __restrict__ hist) {
+    __shared__ int cnt[kRouteMaxExperts];
+    const int tid = threadIdx.x;
+    if (tid < E) cnt[tid] = 0;
+    __syncthreads();
+    const RouteMatch m = route_match(ids, (int64_t)blockIdx.x * kRouteThreads + tid, P, E);
+    if (m.same != 0 && m.rank == 0) atomicAdd(&cnt[m.e], __popcll(m.same));   // a sum: order-free
+    __syncthreads();
+    if (tid < E) hist[(int64_t)blockIdx.x * E + tid] = cnt[tid];
+}
+
+// Exclusive scan over the experts of a per-expert value held by thread e
+// (e < E <= kRouteThreads), for the whole workgroup.
+__device__ __forceinline__ int route_block_scan(int v_in, int* wsum) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int v = v_in;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(v, d);
+        if (lane >= d) v += t;
+    }
+    if (lane == 63) wsum[w] = v;
+    __syncthreads();
+    int before = 0;
+    for (int i = 0; i < w; ++i) before += wsum[i];
+    return before + v - v_in;
+}
+
+__global__ void __launch_bounds__(kRouteThreads) k_moe_route_scan(int32_t* __restrict__ hist, int64_t blocks, int E,
+                                                                   int64_t P, int32_t* __restrict__ offsets) {
+    __shared__ int wsum[kRouteWaves];
+    const int tid = threadIdx.x;
+    // expert tid: the pairs of blocks before b, in place (16 blocks' loads in
+    // flight at a time); then its total
+    constexpr int kBatch = 16;
+    int total = 0;
+    if (tid < E) {
+        for (int64_t b0 = 0; b0 < blocks; b0 += kBatch) {
+            int c[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) c[i] = b0 + i < blocks ? hist[(b0 + i) * E + tid] : 0;
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                if (b0 + i < blocks) hist[(b0 + i) * E + tid] = total;
+                total += c[i];
+            }
         }
-        const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-        const int rank = __popcll(same & below);
-        if (valid && rank == 0) cnt[w][e] = __popcll(same);   // the lowest lane of each expert group
-        __syncthreads();
-        if (valid) {
-            int row = running[e] + rank;
-            for (int ww = 0; ww < w; ++ww) row += cnt[ww][e];
-            row_token[row] = (int32_t)(p / k);
-            token_row[p] = row;
+    }
+    const int first = route_block_scan(total, wsum);
+    if (tid < E) {
+        offsets[tid] = first;
+        for (int64_t b = 0; b < blocks; ++b) hist[b * E + tid] += first;
+    }
+    if (tid == 0) offsets[E] = (int)P;
+}
+
+// hist == NULL: a single block (P <= kRouteThreads) that also derives the
+// offsets from its own counts, so routing takes one launch.
+__global__ void __launch_bounds__(kRouteThreads) k_moe_route_place(const int32_t* __restrict__ ids, int64_t P, int E,
+                                                                    const int32_t* __restrict__ hist,
+                                                                    int32_t* __restrict__ row_token,
+                                                                    int32_t* __restrict__ token_row, int k,
+                                                                    int32_t* __restrict__ offsets) {
+    __shared__ int cnt[kRouteWaves * kRouteMaxExperts];   // [wave][expert], row stride E
+    __shared__ int wsum[kRouteWaves];
+    const int tid = threadIdx.x, w = tid >> 6;
+    for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) cnt[i] = 0;
+    __syncthreads();
+    const int64_t p = (int64_t)blockIdx.x * kRouteThreads + tid;
+    const RouteMatch m = route_match(ids, p, P, E);
+    if (m.same != 0 && m.rank == 0) cnt[w * E + m.e] = __popcll(m.same);   // the lowest lane of each group
+    __syncthreads();
+    // expert tid: each wave's first row, in place
+    int c[kRouteWaves];
+    int total = 0;
+    if (tid < E) {
+#pragma unroll
+        for (int ww = 0; ww < kRouteWaves; ++ww) {
+            c[ww] = cnt[ww * E + tid];
+            total += c[ww];
         }
-        __syncthreads();
-        for (int ee = tid; ee < E; ee += kRouteThreads) {
-            int add = 0;
-            for (int ww = 0; ww < kRouteWaves; ++ww) add += cnt[ww][ee];
-            running[ee] += add;
+    }
+    int first = 0;
+    if (hist == nullptr) {   // single block: the offsets are the scan of its own counts
+        first = route_block_scan(tid < E ? total : 0, wsum);
+        if (tid < E) offsets[tid] = first;
+        if (tid == 0) offsets[E] = (int)P;
+    }
+    if (tid < E) {
+        int run = hist ? hist[(int64_t)blockIdx.x * E + tid] : first;
+#pragma unroll
+        for (int ww = 0; ww < kRouteWaves; ++ww) {
+            cnt[ww * E + tid] = run;
+            run += c[ww];
         }
-        __syncthreads();
+    }
+    __syncthreads();
+    if (m.same != 0) {
+        const int row = cnt[w * E + m.e] + m.rank;
+        row_token[row] = (int32_t)((int)p / k);
+        token_row[p] = row;
     }
 }
 
 // Gated SiLU: a[r, i] = RNE_bf16(silu(gate) * up) with gate = h[r, i] and
-// up = h[r, I + i], silu(v) = v / (1 + e^-v), in fp32.  Thread: 8 columns.
+// up = h[r, I + i], silu(v) = v / (1 + e^-v), in fp32.  Thread: 8 columns,
+// moved with 16-byte loads and stores when VEC (the host checks that every
+// row start and I keep 16-byte alignment).
+__device__ __forceinline__ uint32_t silu_mul_pair(uint32_t g2, uint32_t u2) {
+    const float g0 = bf16_to_f32(g2 & 0xFFFFu), g1 = bf16_to_f32(g2 >> 16);
+    const float u0 = bf16_to_f32(u2 & 0xFFFFu), u1 = bf16_to_f32(u2 >> 16);
+    const float a0 = g0 / (1.0f + expf(-g0)) * u0, a1 = g1 / (1.0f + expf(-g1)) * u1;
+    return f32_to_bf16_rne(a0) | (f32_to_bf16_rne(a1) << 16);
+}
+
+template <bool VEC>
 __global__ void k_moe_silu_mul(const uint16_t* __restrict__ h, int64_t ld_h, int64_t R, int64_t I,
                                uint16_t* __restrict__ a, int64_t ld_a) {
     const int64_t per_row = (I + 7) / 8;
@@ -123,15 +181,20 @@ __global__ void k_moe_silu_mul(const uint16_t* __restrict__ h, int64_t ld_h, int
     const int64_t r = idx / per_row, i0 = (idx % per_row) * 8;
     const uint16_t* hr = h + r * ld_h;
     uint16_t* ar = a + r * ld_a;
-    for (int e = 0; e < 8 && i0 + e < I; ++e) {
-        const float g = bf16_to_f32(hr[i0 + e]), u = bf16_to_f32(hr[I + i0 + e]);
-        const float sg = g / (1.0f + expf(-g));
-        ar[i0 + e] = (uint16_t)f32_to_bf16_rne(sg * u);
+    if (VEC && i0 + 8 <= I) {
+        const uint4 g = *reinterpret_cast<const uint4*>(hr + i0), u = *reinterpret_cast<const uint4*>(hr + I + i0);
+        *reinterpret_cast<uint4*>(ar + i0) =
+            make_uint4(silu_mul_pair(g.x, u.x), silu_mul_pair(g.y, u.y), silu_mul_pair(g.z, u.z), silu_mul_pair(g.w, u.w));
+        return;
     }
+    for (int e = 0; e < 8 && i0 + e < I; ++e)
+        ar[i0 + e] = (uint16_t)(silu_mul_pair(hr[i0 + e], hr[I + i0 + e]) & 0xFFFFu);
 }
 
 // Top-k weighted combine: out[t, c] = RNE_bf16(sum_j wt[t, j] * y[token_row[t k + j], c]),
-// summed in fp32 in slot order j = 0 .. k - 1.  Thread: 8 columns.
+// summed in fp32 in slot order j = 0 .. k - 1.  Thread: 8 columns, 16-byte
+// loads and stores when VEC.
+template <bool VEC>
 __global__ void k_moe_combine(const uint16_t* __restrict__ y, int64_t ld_y, const int32_t* __restrict__ token_row,
                               const float* __restrict__ wt, int64_t T, int k, int64_t H, uint16_t* __restrict__ out,
                               int64_t ld_o) {
@@ -139,18 +202,36 @@ __global__ void k_moe_combine(const uint16_t* __restrict__ y, int64_t ld_y, cons
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= T * per_row) return;
     const int64_t t = idx / per_row, c0 = (idx % per_row) * 8;
+    const bool full = VEC && c0 + 8 <= H;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
         const float wj = wt[t * k + j];
-        const uint16_t* yr = y + (int64_t)token_row[t * k + j] * ld_y;
+        const uint16_t* yr = y + (int64_t)token_row[t * k + j] * ld_y + c0;
+        if (full) {
+            const uint4 v = *reinterpret_cast<const uint4*>(yr);
+            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if (c0 + e < H) acc[e] = __builtin_fmaf(wj, bf16_to_f32(yr[c0 + e]), acc[e]);
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] = __builtin_fmaf(wj, bf16_to_f32(d[e] & 0xFFFFu), acc[2 * e]);
+                acc[2 * e + 1] = __builtin_fmaf(wj, bf16_to_f32(d[e] >> 16), acc[2 * e + 1]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (c0 + e < H) acc[e] = __builtin_fmaf(wj, bf16_to_f32(yr[e]), acc[e]);
+        }
     }
-    uint16_t* orow = out + t * ld_o;
+    uint16_t* orow = out + t * ld_o + c0;
+    if (full) {
+        uint32_t p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = f32_to_bf16_rne(acc[2 * e]) | (f32_to_bf16_rne(acc[2 * e + 1]) << 16);
+        *reinterpret_cast<uint4*>(orow) = make_uint4(p[0], p[1], p[2], p[3]);
+        return;
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-        if (c0 + e < H) orow[c0 + e] = (uint16_t)f32_to_bf16_rne(acc[e]);
+        if (c0 + e < H) orow[e] = (uint16_t)f32_to_bf16_rne(acc[e]);
 }
 
 }  // namespace nvfp4

@@ -527,8 +527,14 @@ nvfp4_status nvfp4_w4a16_grouped_gemm_gather(const void* x, int64_t ld_x, int64_
 
 // ------------------------------------------------------------------ MoE --
 
+int64_t nvfp4_moe_route_workspace_bytes(int64_t T, int64_t k, int64_t E) {
+    if (T < 0 || k < 1 || E < 1 || E > kRouteMaxExperts || T * k >= ((int64_t)1 << 31)) return -1;
+    return (T * k + kRouteThreads - 1) / kRouteThreads * E * 4;
+}
+
 nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int64_t k, int64_t E, int32_t* expert_offsets,
-                             int32_t* row_token, int32_t* token_row, void* stream) {
+                             int32_t* row_token, int32_t* token_row, void* workspace, int64_t workspace_bytes,
+                             void* stream) {
     const char* fn = "nvfp4_moe_route";
     if (T < 0) return fail(NVFP4_ERR_INVALID_ARG, "%s: token count %lld is negative", fn, (long long)T);
     if (E < 1 || E > kRouteMaxExperts)
@@ -540,9 +546,25 @@ nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int64_t k, int6
         return fail(NVFP4_ERR_INVALID_ARG, "%s: topk_ids, row_token and token_row must not be NULL", fn);
     if (!aligned(topk_ids, 4) || !aligned(expert_offsets, 4) || !aligned(row_token, 4) || !aligned(token_row, 4))
         return fail(NVFP4_ERR_ALIGNMENT, "%s: int32 arrays must be 4-byte aligned", fn);
+    const int64_t need = nvfp4_moe_route_workspace_bytes(T, k, E);
+    if (T > 0 && (workspace_bytes < need || !workspace))
+        return fail(NVFP4_ERR_BUFFER_TOO_SMALL, "%s: workspace of %lld bytes is below the %lld bytes this call needs",
+                    fn, (long long)workspace_bytes, (long long)need);
+    if (!aligned(workspace, 4)) return fail(NVFP4_ERR_ALIGNMENT, "%s: workspace must be 4-byte aligned", fn);
     if (T == 0) return ok();   // zero tokens: nothing is launched
-    hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(kRouteThreads), 0, static_cast<hipStream_t>(stream), topk_ids,
-                       T * k, (int)E, expert_offsets, row_token, token_row, (int)k);
+    const int64_t P = T * k, blocks = (P + kRouteThreads - 1) / kRouteThreads;
+    if (blocks > INT32_MAX) return fail(NVFP4_ERR_INVALID_ARG, "%s: too many pairs", fn);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t* hist = static_cast<int32_t*>(workspace);
+    if (blocks == 1) {   // one workgroup counts, scans and places
+        hipLaunchKernelGGL(k_moe_route_place, dim3(1), dim3(kRouteThreads), 0, st, topk_ids, P, (int)E,
+                           (const int32_t*)nullptr, row_token, token_row, (int)k, expert_offsets);
+        return launched(fn);
+    }
+    hipLaunchKernelGGL(k_moe_route_count, dim3((unsigned)blocks), dim3(kRouteThreads), 0, st, topk_ids, P, (int)E, hist);
+    hipLaunchKernelGGL(k_moe_route_scan, dim3(1), dim3(kRouteThreads), 0, st, hist, blocks, (int)E, P, expert_offsets);
+    hipLaunchKernelGGL(k_moe_route_place, dim3((unsigned)blocks), dim3(kRouteThreads), 0, st, topk_ids, P, (int)E,
+                       hist, row_token, token_row, (int)k, expert_offsets);
     return launched(fn);
 }
 
@@ -556,9 +578,14 @@ nvfp4_status nvfp4_moe_silu_mul(const void* h, int64_t ld_h, int64_t R, int64_t 
     if (!aligned(h, 2) || !aligned(a, 2)) return fail(NVFP4_ERR_ALIGNMENT, "%s: bf16 arrays must be 2-byte aligned", fn);
     if (R == 0) return ok();
     const int64_t threads = R * ((I + 7) / 8);
-    hipLaunchKernelGGL(k_moe_silu_mul, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(h), ld_h, R, I,
-                       static_cast<uint16_t*>(a), ld_a);
+    const bool vec = ld_h % 8 == 0 && I % 8 == 0 && ld_a % 8 == 0 && aligned(h, 16) && aligned(a, 16);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (vec)
+        hipLaunchKernelGGL(k_moe_silu_mul<true>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                           static_cast<const uint16_t*>(h), ld_h, R, I, static_cast<uint16_t*>(a), ld_a);
+    else
+        hipLaunchKernelGGL(k_moe_silu_mul<false>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                           static_cast<const uint16_t*>(h), ld_h, R, I, static_cast<uint16_t*>(a), ld_a);
     return launched(fn);
 }
 
@@ -573,9 +600,16 @@ nvfp4_status nvfp4_moe_combine(const void* y, int64_t ld_y, const int32_t* token
         return fail(NVFP4_ERR_ALIGNMENT, "%s: misaligned pointer", fn);
     if (T == 0) return ok();
     const int64_t threads = T * ((H + 7) / 8);
-    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(y), ld_y, token_row,
-                       topk_weights, T, (int)k, H, static_cast<uint16_t*>(out), ld_o);
+    const bool vec = ld_y % 8 == 0 && ld_o % 8 == 0 && aligned(y, 16) && aligned(out, 16);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (vec)
+        hipLaunchKernelGGL(k_moe_combine<true>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                           static_cast<const uint16_t*>(y), ld_y, token_row, topk_weights, T, (int)k, H,
+                           static_cast<uint16_t*>(out), ld_o);
+    else
+        hipLaunchKernelGGL(k_moe_combine<false>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                           static_cast<const uint16_t*>(y), ld_y, token_row, topk_weights, T, (int)k, H,
+                           static_cast<uint16_t*>(out), ld_o);
     return launched(fn);
 }
 
