@@ -199,6 +199,14 @@ nvfp4_status nvfp4_w4a16_grouped_gemm_gather(const void* x, int64_t ld_x, int64_
 nvfp4_status nvfp4_moe_silu_mul(const void* h, int64_t ld_h, int64_t R, int64_t I, void* a, int64_t ld_a,
                                 void* stream);
 
+/* Non-gated squared ReLU for experts without a gate projection (the SGLang
+ * compressed-tensors NVFP4 weight-only page, review discussion: non-gated
+ * relu2 experts hold one FC1 projection): a[r][i] = RNE_bf16(max(h[r][i], 0)^2)
+ * evaluated in fp32; h is bf16 [R][ld_h] with I columns, a bf16 [R][ld_a].
+ * Errors: R < 0, I < 1, ld_h < I, ld_a < I, NULL (R > 0) -> INVALID_ARG; odd
+ * addresses -> ALIGNMENT. */
+nvfp4_status nvfp4_moe_relu2(const void* h, int64_t ld_h, int64_t R, int64_t I, void* a, int64_t ld_a, void* stream);
+
 /* Top-k weighted combine back to token order: out[t][c] =
  * RNE_bf16(sum_{j=0..k-1} topk_weights[t*k + j] * y[token_row[t*k + j]][c]),
  * accumulated in fp32 in slot order.  y: bf16 [R][ld_y] (FC2 output in

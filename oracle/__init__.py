@@ -32,6 +32,7 @@ FC1: SGLang compressed-tensors NVFP4 weight-only page, review discussion):
                   pair order; offsets, row -> token and pair -> row
     silu_mul    : a = silu(gate) * up with gate = h[:, :I], up = h[:, I:],
                   silu(v) = v / (1 + exp(-v))                    (fp64, not rounded)
+    relu2       : a = max(h, 0)^2 (non-gated experts)            (fp64, not rounded)
     combine     : out[t] = sum_j w[t, j] * y[row of (t, j)]      (fp64, not rounded)
 
 Acceptance of a GPU result against the oracle (``accept``): relative Frobenius
@@ -336,6 +337,12 @@ def silu_mul(h_bits: np.ndarray) -> np.ndarray:
     I = h.shape[1] // 2
     g, u = h[:, :I], h[:, I:]
     return g / (1.0 + np.exp(-g)) * u
+
+
+def relu2(h_bits: np.ndarray) -> np.ndarray:
+    """h bf16 bits [R, I] -> max(h, 0)^2 in fp64, not rounded."""
+    h = bf16_np(h_bits)
+    return np.where(h > 0, h, 0.0) ** 2
 
 
 def combine(y_bits: np.ndarray, token_row: np.ndarray, weights: np.ndarray) -> np.ndarray:

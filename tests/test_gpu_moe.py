@@ -1,7 +1,8 @@
-"""Parity of the MoE glue around the grouped GEMM (routing, the gathering grouped GEMM, the gated SiLU and the
-top-k combine) with the CPU oracle, on the GPU.  Routing is integer work: bit-exact.  The gathering GEMM runs the
-same kernels as the grouped GEMM on pre-gathered rows: bit-exact against it, and within the acceptance bound of
-``oracle.accept`` against the oracle, as are the SiLU and the combine."""
+"""Parity of the MoE glue around the grouped GEMM (routing, the gathering grouped GEMM, the gated SiLU, the
+non-gated squared ReLU and the top-k combine) with the CPU oracle, on the GPU.  Routing is integer work:
+bit-exact.  The gathering GEMM runs the same kernels as the grouped GEMM on pre-gathered rows: bit-exact against
+it, and within the acceptance bound of ``oracle.accept`` against the oracle, as are the activations and the
+combine."""
 import numpy as np
 import pytest
 import torch
@@ -86,6 +87,18 @@ def test_silu_mul(R, I):
     nv.moe_silu_mul(hbig[:, :2 * I], out=abig[:, :I])
     accept_or_fail(to_f64(abig[:, :I]), oracle.silu_mul(h), "silu")
     assert torch.all(abig[:, I:] == 7.0)
+
+
+@pytest.mark.parametrize("R,I", [(128, 768), (37, 100)])
+def test_relu2(R, I):
+    say(f"relu2 R={R} I={I}")
+    g = synth.rng(R * 11 + I)
+    h = synth.bf16_bits_from_f32((g.standard_normal((R, I)) * 4).astype(np.float32))
+    a = nv.moe_relu2(bf16_dev(h))
+    ref = oracle.relu2(h)
+    y = to_f64(a)
+    assert np.all(y[ref == 0] == 0)               # exact zeros where the input is not positive
+    accept_or_fail(y, ref, "relu2")
 
 
 @pytest.mark.parametrize("T,k,E,H", [(16, 8, 128, 2048), (300, 2, 8, 100), (1, 1, 1, 8)])

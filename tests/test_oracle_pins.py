@@ -405,3 +405,14 @@ def test_combine_matches_loops_and_one_hot_gather():
     onehot = np.zeros((T, k), dtype=np.float32)
     onehot[:, 1] = 1.0
     assert np.array_equal(oracle.combine(y, token_row, onehot), yv[token_row.reshape(T, k)[:, 1]])
+
+
+def test_relu2_closed_forms():
+    """relu2 is 0 for v <= 0 (signed zero and negatives) and v*v above; a bf16 v has at most 8 significant bits,
+    so v*v is exact in fp64."""
+    vals = np.array([-2.0, -0.0, 0.0, 0.5, 1.5, 3.0, -1e-3, 255.0], dtype=np.float32)
+    bits = synth.bf16_bits_from_f32(vals)[None]
+    v = oracle.bf16_np(bits)[0]
+    out = oracle.relu2(bits)[0]
+    assert np.array_equal(out, np.array([x * x if x > 0 else 0.0 for x in v]))
+    assert np.all(out[v <= 0] == 0)

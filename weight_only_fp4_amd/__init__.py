@@ -21,7 +21,8 @@ import os
 import torch
 
 __all__ = ["repack", "repack_bytes", "gemm", "gemm_variant", "grouped_gemm", "dequant", "lib", "Nvfp4Error",
-           "workspace", "gemm_workspace_bytes", "grouped_gemm_gather", "moe_route", "moe_silu_mul", "moe_combine",
+           "workspace", "gemm_workspace_bytes", "grouped_gemm_gather", "moe_route", "moe_silu_mul", "moe_relu2",
+           "moe_combine",
            "VARIANT_AUTO", "VARIANT_SMALL_M", "VARIANT_LARGE_M", "VARIANT_MFMA", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4_w4a16.so")
@@ -68,6 +69,7 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_moe_route.argtypes, L.nvfp4_moe_route.restype = [P, I64, I64, I64, P, P, P, P, I64, P], I
         L.nvfp4_moe_silu_mul.argtypes, L.nvfp4_moe_silu_mul.restype = [P, I64, I64, I64, P, I64, P], I
         L.nvfp4_moe_combine.argtypes, L.nvfp4_moe_combine.restype = [P, I64, P, P, I64, I64, I64, P, I64, P], I
+        L.nvfp4_moe_relu2.argtypes, L.nvfp4_moe_relu2.restype = [P, I64, I64, I64, P, I64, P], I
         _lib = L
     return _lib
 
@@ -276,6 +278,18 @@ def moe_silu_mul(h, out=None):
     else:
         _dev("out", out, torch.bfloat16, 2)
     _check(lib().nvfp4_moe_silu_mul(_ptr(h), h.stride(0), R, I, _ptr(out), out.stride(0), _stream(h.device)))
+    return out
+
+
+def moe_relu2(h, out=None):
+    """h bf16 [R, I] -> max(h, 0)^2, bf16 [R, I] (non-gated experts)."""
+    _dev("h", h, torch.bfloat16, 2)
+    R, I = h.shape
+    if out is None:
+        out = torch.empty((R, I), dtype=torch.bfloat16, device=h.device)
+    else:
+        _dev("out", out, torch.bfloat16, 2)
+    _check(lib().nvfp4_moe_relu2(_ptr(h), h.stride(0), R, I, _ptr(out), out.stride(0), _stream(h.device)))
     return out
 
 

@@ -191,6 +191,30 @@ __global__ void k_moe_silu_mul(const uint16_t* __restrict__ h, int64_t ld_h, int
         ar[i0 + e] = (uint16_t)(silu_mul_pair(hr[i0 + e], hr[I + i0 + e]) & 0xFFFFu);
 }
 
+// Non-gated squared ReLU: a[r, i] = RNE_bf16(max(h[r, i], 0)^2) in fp32.
+// Thread: 8 columns, 16-byte loads and stores when VEC.
+__device__ __forceinline__ uint32_t relu2_pair(uint32_t h2) {
+    const float a0 = fmaxf(bf16_to_f32(h2 & 0xFFFFu), 0.0f), a1 = fmaxf(bf16_to_f32(h2 >> 16), 0.0f);
+    return f32_to_bf16_rne(a0 * a0) | (f32_to_bf16_rne(a1 * a1) << 16);
+}
+
+template <bool VEC>
+__global__ void k_moe_relu2(const uint16_t* __restrict__ h, int64_t ld_h, int64_t R, int64_t I,
+                            uint16_t* __restrict__ a, int64_t ld_a) {
+    const int64_t per_row = (I + 7) / 8;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= R * per_row) return;
+    const int64_t r = idx / per_row, i0 = (idx % per_row) * 8;
+    const uint16_t* hr = h + r * ld_h;
+    uint16_t* ar = a + r * ld_a;
+    if (VEC && i0 + 8 <= I) {
+        const uint4 v = *reinterpret_cast<const uint4*>(hr + i0);
+        *reinterpret_cast<uint4*>(ar + i0) = make_uint4(relu2_pair(v.x), relu2_pair(v.y), relu2_pair(v.z), relu2_pair(v.w));
+        return;
+    }
+    for (int e = 0; e < 8 && i0 + e < I; ++e) ar[i0 + e] = (uint16_t)(relu2_pair(hr[i0 + e]) & 0xFFFFu);
+}
+
 // Top-k weighted combine: out[t, c] = RNE_bf16(sum_j wt[t, j] * y[token_row[t k + j], c]),
 // summed in fp32 in slot order j = 0 .. k - 1.  Thread: 8 columns, 16-byte
 // loads and stores when VEC.

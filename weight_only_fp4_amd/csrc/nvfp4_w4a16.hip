@@ -589,6 +589,27 @@ nvfp4_status nvfp4_moe_silu_mul(const void* h, int64_t ld_h, int64_t R, int64_t 
     return launched(fn);
 }
 
+nvfp4_status nvfp4_moe_relu2(const void* h, int64_t ld_h, int64_t R, int64_t I, void* a, int64_t ld_a,
+                             void* stream) {
+    const char* fn = "nvfp4_moe_relu2";
+    if (R < 0 || I < 1) return fail(NVFP4_ERR_INVALID_ARG, "%s: R = %lld, I = %lld", fn, (long long)R, (long long)I);
+    if (ld_h < I) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_h = %lld < I = %lld", fn, (long long)ld_h, (long long)I);
+    if (ld_a < I) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_a = %lld < I = %lld", fn, (long long)ld_a, (long long)I);
+    if (R > 0 && (!h || !a)) return fail(NVFP4_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(h, 2) || !aligned(a, 2)) return fail(NVFP4_ERR_ALIGNMENT, "%s: bf16 arrays must be 2-byte aligned", fn);
+    if (R == 0) return ok();
+    const int64_t threads = R * ((I + 7) / 8);
+    const bool vec = ld_h % 8 == 0 && ld_a % 8 == 0 && aligned(h, 16) && aligned(a, 16);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (vec)
+        hipLaunchKernelGGL(k_moe_relu2<true>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                           static_cast<const uint16_t*>(h), ld_h, R, I, static_cast<uint16_t*>(a), ld_a);
+    else
+        hipLaunchKernelGGL(k_moe_relu2<false>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                           static_cast<const uint16_t*>(h), ld_h, R, I, static_cast<uint16_t*>(a), ld_a);
+    return launched(fn);
+}
+
 nvfp4_status nvfp4_moe_combine(const void* y, int64_t ld_y, const int32_t* token_row, const float* topk_weights,
                                int64_t T, int64_t k, int64_t H, void* out, int64_t ld_o, void* stream) {
     const char* fn = "nvfp4_moe_combine";
