@@ -229,7 +229,12 @@ nvfp4_status nvfp4_dequant_bf16(const void* w_repacked, int64_t E, int64_t N, in
  *   variant 0 = automatic (same as nvfp4_w4a16_gemm),
  *   variant 1 = small-M kernel (M <= 16 only; larger M -> INVALID_ARG),
  *   variant 2 = tile kernel (any M),
- *   variant 3 = MFMA-bound kernel (any M; launched as one or two kernels).
+ *   variant 3 = MFMA-bound kernel (any M; launched as one or two kernels),
+ *   variant 4 = activation-resident kernel (M <= 16, K <= 4096, N <= 32768;
+ *               otherwise INVALID_ARG).
+ * The automatic choice takes the small-M kernel up to 4 rows, the
+ * activation-resident kernel for 5..16 rows where it applies, the MFMA-bound
+ * kernel for large M and the tile kernel otherwise.
  * Used to check that the variants agree on the same inputs. */
 nvfp4_status nvfp4_w4a16_gemm_variant(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
                                       const float* global_scale, int global_scale_is_divisor,

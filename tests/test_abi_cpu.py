@@ -68,6 +68,9 @@ A = 1 << 20   # a fake, 16-byte-aligned address; never dereferenced (calls fail 
     (dict(M=16, N=4096, K=14336, ld_x=14336, ld_y=4096, variant=2, ws=A + 16, wsb=1 << 30), ALIGN, "workspace"),
     (dict(ld_x=(1 << 23) + 8), INVALID, "exceeds"),
     (dict(variant=1, M=17), INVALID, "small-M"),
+    (dict(variant=4, M=17), INVALID, "activation-resident"),
+    (dict(variant=4, K=4224, ld_x=4224), INVALID, "activation-resident"),
+    (dict(variant=4, N=32784, ld_y=32784), INVALID, "activation-resident"),
     (dict(variant=7), INVALID, "variant"),
 ])
 def test_gemm_argument_errors(args, status, needle):

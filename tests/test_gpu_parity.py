@@ -33,9 +33,11 @@ def accept_or_fail(y, ref, what):
     return info
 
 
-def dense_variants(M: int, K: int):
-    """Every kernel variant that takes this shape: automatic, tile, MFMA-bound, small-M (M <= 16)."""
-    return [nv.VARIANT_AUTO, nv.VARIANT_LARGE_M, nv.VARIANT_MFMA] + ([nv.VARIANT_SMALL_M] if M <= 16 else [])
+def dense_variants(M: int, K: int, N: int):
+    """Every kernel variant that takes this shape: automatic, tile, MFMA-bound, small-M (M <= 16) and
+    activation-resident (M <= 16, K <= 4096, N <= 32768)."""
+    v = [nv.VARIANT_AUTO, nv.VARIANT_LARGE_M, nv.VARIANT_MFMA] + ([nv.VARIANT_SMALL_M] if M <= 16 else [])
+    return v + ([nv.VARIANT_RESIDENT] if M <= 16 and K <= 4096 and N <= 32768 else [])
 
 
 def oracle_bf16_bits(t64: np.ndarray) -> np.ndarray:
@@ -100,7 +102,8 @@ def _read_hand():
     return rows
 
 
-@pytest.mark.parametrize("variant", [nv.VARIANT_SMALL_M, nv.VARIANT_LARGE_M, nv.VARIANT_MFMA])
+@pytest.mark.parametrize("variant", [nv.VARIANT_SMALL_M, nv.VARIANT_LARGE_M, nv.VARIANT_MFMA,
+                                     nv.VARIANT_RESIDENT])
 @pytest.mark.parametrize("case", ["H1", "H2", "H3", "H4"])
 def test_hand_cases_exact(case, variant):
     from test_oracle_pins import _hand_inputs
@@ -116,7 +119,7 @@ def test_hand_cases_exact(case, variant):
 
 
 @pytest.mark.parametrize("variant,M,N", [(nv.VARIANT_SMALL_M, 16, 40), (nv.VARIANT_LARGE_M, 256, 300),
-])
+                                         (nv.VARIANT_RESIDENT, 16, 40)])
 def test_identity_activation_gives_tile_bit_exact(variant, M, N):
     """X = I_K, g = 1: every output is one exact product, so Y = T^T bit for bit (signed zeros compare equal)."""
     K = M
@@ -154,7 +157,7 @@ def test_dense_parity_full_oracle(name, make):
     say(f"dense {name} M={c.M} N={c.N} K={c.K} pre={c.pre is not None} div={c.g_is_divisor}")
     d = DenseDev(c)
     ref = oracle.gemm(c.x, c.w, c.s, c.g_stored, c.g_is_divisor, c.pre)
-    for v in dense_variants(c.M, c.K):
+    for v in dense_variants(c.M, c.K, c.N):
         accept_or_fail(to_f64(d.run(v)), ref, (name, v))
 
 
@@ -283,7 +286,8 @@ def test_grouped_matches_per_expert_dense_calls():
 
 # -------------------------------------------------------------- invariants --
 
-@pytest.mark.parametrize("variant", [nv.VARIANT_SMALL_M, nv.VARIANT_LARGE_M, nv.VARIANT_MFMA])
+@pytest.mark.parametrize("variant", [nv.VARIANT_SMALL_M, nv.VARIANT_LARGE_M, nv.VARIANT_MFMA,
+                                     nv.VARIANT_RESIDENT])
 def test_scale_invariants_bit_exact(variant):
     c = synth.dense_case(16, 520, 1040, seed=41, g_stored=2688.0, g_is_divisor=True, prescale=True)
     say(f"invariants variant {variant}")
@@ -325,7 +329,8 @@ def test_zero_rows_leave_output_untouched():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("variant", [nv.VARIANT_SMALL_M, nv.VARIANT_LARGE_M, nv.VARIANT_MFMA])
+@pytest.mark.parametrize("variant", [nv.VARIANT_SMALL_M, nv.VARIANT_LARGE_M, nv.VARIANT_MFMA,
+                                     nv.VARIANT_RESIDENT])
 def test_strided_io_and_untouched_padding(variant):
     c = synth.dense_case(5, 40, 96, seed=13)
     say(f"strided io variant {variant}")
@@ -362,7 +367,7 @@ def test_nan_scale_codes_propagate():
     nan_cols = sorted({n for n, _, _ in bad})
     assert np.all(np.isnan(ref[:, nan_cols]))
     keep = [n for n in range(c.N) if n not in nan_cols]
-    for v in dense_variants(c.M, c.K):
+    for v in dense_variants(c.M, c.K, c.N):
         y = to_f64(d.run(v))
         assert np.all(np.isnan(y[:, nan_cols])), v
         accept_or_fail(y[:, keep], ref[:, keep], ("nan scales", v))
@@ -390,7 +395,7 @@ def test_smallest_shapes():
         c = synth.dense_case(M, N, K, seed=M * 100 + N)
         d = DenseDev(c)
         ref = oracle.gemm(c.x, c.w, c.s, c.g_stored, False, None)
-        for v in dense_variants(M, K):
+        for v in dense_variants(M, K, N):
             accept_or_fail(to_f64(d.run(v)), ref, (M, N, K, v))
 
 
@@ -414,7 +419,8 @@ def test_graph_replays_match_eager():
     cases = [(synth.decode_case(16, N=4096, K=14336, seed=3), nv.VARIANT_AUTO),    # tile, K split 2 ways
              (synth.decode_case(1, N=2048, K=4096, seed=4), nv.VARIANT_AUTO),      # small-M, K split
              (synth.dense_case(300, 700, 2048, 5, prescale=True), nv.VARIANT_MFMA),  # two MFMA launches + pre-scale
-             (synth.dense_case(24, 2000, 4096, 1005), nv.VARIANT_LARGE_M)]          # tile, split with N tail
+             (synth.dense_case(24, 2000, 4096, 1005), nv.VARIANT_LARGE_M),          # tile, split with N tail
+             (synth.decode_case(8, N=2064, K=3968, seed=6), nv.VARIANT_AUTO)]       # activation-resident, ragged
     devs = [DenseDev(c) for c, _ in cases]
     wss = [nv.workspace(nv.gemm_workspace_bytes(c.M, c.N, c.K), DEV) for c, _ in cases]
     ys = [torch.empty((c.M, c.N), dtype=torch.bfloat16, device=DEV) for c, _ in cases]
@@ -449,3 +455,29 @@ def test_graph_replays_match_eager():
             assert torch.equal(y, r), (rep, i)
         run_all()      # eager calls between replays share the workspaces
         torch.cuda.synchronize()
+
+
+# ---------------------------------------------------- activation-resident --
+
+XRES_SHAPES = [
+    (16, 14336, 4096),   # two chunks per wave, four units per workgroup (the decode workload's launch)
+    (9, 2064, 2048),     # one chunk per wave, N one unit past a multiple of 256 units
+    (16, 1000, 4000),    # K ragged in its last chunk, N ragged in its last unit
+    (5, 48, 272),        # most waves own no chunk (K = 2 chunks + 16)
+    (16, 32752, 1024),   # the widest N it takes (eight units per workgroup), last unit ragged
+]
+
+
+@pytest.mark.parametrize("M,N,K", XRES_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in XRES_SHAPES])
+def test_resident_variant_parity(M, N, K):
+    """The activation-resident kernel against the oracle over its launch shapes: chunks per wave (1, 2),
+    units per workgroup (1..8), waves without chunks, ragged K and N; with a pre-quant scale and a divisor-stored
+    global scale on the odd shapes.  Automatic dispatch takes this kernel for 5..16 rows."""
+    ragged = K % 128 != 0
+    c = synth.dense_case(M, N, K, seed=M + N + K, prescale=ragged, g_stored=2688.0 if ragged else 1 / 2688,
+                         g_is_divisor=ragged)
+    say(f"resident M={M} N={N} K={K}")
+    d = DenseDev(c)
+    y = to_f64(d.run(nv.VARIANT_RESIDENT))
+    accept_or_fail(y, oracle.gemm(c.x, c.w, c.s, c.g_stored, c.g_is_divisor, c.pre), ("resident", M, N, K))
+    assert torch.equal(d.run(nv.VARIANT_AUTO), d.run(nv.VARIANT_RESIDENT))

@@ -23,10 +23,10 @@ import torch
 __all__ = ["repack", "repack_bytes", "gemm", "gemm_variant", "grouped_gemm", "dequant", "lib", "Nvfp4Error",
            "workspace", "gemm_workspace_bytes", "grouped_gemm_gather", "moe_route", "moe_silu_mul", "moe_relu2",
            "moe_combine",
-           "VARIANT_AUTO", "VARIANT_SMALL_M", "VARIANT_LARGE_M", "VARIANT_MFMA", "LIB_PATH"]
+           "VARIANT_AUTO", "VARIANT_SMALL_M", "VARIANT_LARGE_M", "VARIANT_MFMA", "VARIANT_RESIDENT", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4_w4a16.so")
-VARIANT_AUTO, VARIANT_SMALL_M, VARIANT_LARGE_M, VARIANT_MFMA = 0, 1, 2, 3
+VARIANT_AUTO, VARIANT_SMALL_M, VARIANT_LARGE_M, VARIANT_MFMA, VARIANT_RESIDENT = 0, 1, 2, 3, 4
 _STATUS = {0: "OK", 1: "INVALID_ARG", 2: "ALIGNMENT", 3: "BUFFER_TOO_SMALL", 4: "HIP"}
 _lib = None
 

@@ -1,0 +1,171 @@
+// Decode-sized GEMM with the activation held in registers (rows <= 16).
+//
+//   Each of the W waves of a workgroup owns one contiguous K slice of CH
+//   chunks (128 k each).  A wave loads the activation rows of its slice once:
+//   coalesced 16-byte loads (each load instruction covers four rows x 256
+//   bytes, whole cache lines) go through a small private LDS area and come
+//   back in the register layout of the v_mfma_f32_16x16x32_bf16 A operand,
+//   where they stay for the whole kernel; the first weight load goes out
+//   before them, so the weight stream starts at once.  The workgroup then walks U
+//   consecutive 16-row units of W: every wave streams its slice of each unit
+//   through a D-deep register ring (one 128-bit code load and one scale
+//   dword per lane and chunk), decodes the codes into exact bf16 fragments
+//   and accumulates a 16 x 16 fp32 tile per unit.  The loop has no barrier,
+//   so each wave computes as soon as its own weights arrive instead of
+//   waiting for the slowest wave of the workgroup at every step.
+//
+//   Reduction, in a fixed order (bitwise reproducible): wave w + W/2 adds its
+//   tiles into wave w's through LDS, then the W/2 sums are added in wave
+//   order, scaled by the global scale and rounded to bf16.  K is not split
+//   across workgroups: the device-scope publish / count / reload round trip
+//   of a split measured slower than what it saves here.
+//
+//   K slots of an MFMA step map to k = 32 g + 8 t + e (lane group g, step t,
+//   element e) on both operands, as in the tile kernel, so a weight lane reads
+//   one 32-wide K group of the repacked layout.  Activation rows past `rows`
+//   and K pieces past K are zero (never loaded); units past NU read unit
+//   NU - 1 and store nothing.  FULL (K == 128 W CH: every wave owns CH whole
+//   chunks) compiles without any per-chunk condition; otherwise chunks past
+//   K re-read the last chunk with a zero scale, so they add exact zeros
+//   whatever that chunk holds (no branch in the loop).
+#pragma once
+#include "decode.h"
+#include "layout.h"
+
+namespace nvfp4 {
+
+constexpr int kXresRowBytes = 256 + 16;                // one row of a staged chunk, padded
+constexpr int kXresWaveBytes = 16 * kXresRowBytes;     // a wave's staging area
+
+template <int CH, int U, int W, int D, bool FULL>
+__global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
+                                                      int NU, int KC, int K, int N, const float* __restrict__ gscale,
+                                                      int g_is_div, uint16_t* __restrict__ y, int64_t ld_y, int rows) {
+    constexpr int NI = U * CH;          // ring items of a wave: (unit, chunk), unit-major
+    constexpr int H = W / 2;            // waves after the first reduction stage
+    constexpr int TILE = U * 256;       // fp32 outputs of the workgroup (16 rows x 16 U columns)
+    static_assert(D >= 1, "ring depth");
+    constexpr int DR = D < NI ? D : NI;   // ring slots in use
+    static_assert(W % 2 == 0, "the first reduction stage pairs waves w and w + W/2");
+    __shared__ __attribute__((aligned(16))) uint8_t xs[W * kXresWaveBytes];
+    __shared__ __attribute__((aligned(16))) float red[H * TILE];
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c0 = w * CH;                                                // first chunk of this wave's slice
+    const int nch = KC - c0 < CH ? (KC - c0 > 0 ? KC - c0 : 0) : CH;      // chunks that exist (wave-uniform)
+    const int u0 = (int)blockIdx.x * U;
+
+    // ---- weight ring
+    const int64_t cstr = bv.chunk_stride * kCodeBlock;
+    auto blk_of = [&](int it) {
+        // chunks past this wave's range re-read the last chunk of the matrix (never used)
+        const int u = u0 + it / CH, c = c0 + it % CH < KC ? c0 + it % CH : KC - 1;
+        return bv.block(0, u < NU ? u : NU - 1, 0) * kCodeBlock + (int64_t)c * cstr;   // code byte offset
+    };
+    uint4 cw[DR];
+    uint32_t sw[DR];
+    auto load_item = [&](int it, int slot) {
+        const int64_t off = blk_of(it);
+        cw[slot] = load_stream_u4(bv.codes + off + lane * 16);
+        sw[slot] = load_scale_dword(bv.scales + (off >> 3), lane);
+    };
+
+    // ---- activation chunk c of the slice, coalesced: load i takes rows
+    // 4 i + (lane >> 4), bytes 16 (lane & 15) of the chunk's 256 per row
+    uint4 xa[CH][4];
+    auto load_x = [&](int c) {
+        const int k = (c0 + c) * kChunkK + (lane & 15) * 8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * i + (lane >> 4);
+            xa[c][i] = (row < rows && (FULL || k < K)) ? *reinterpret_cast<const uint4*>(x + (int64_t)row * ld_x + k)
+                                                       : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    // through this wave's LDS area into the A-operand layout: lane (r, g)
+    // takes X[r][128 c + 32 g + 8 t + 0..7] (row stride = 16 mod 256 bytes:
+    // the 16 lanes of a lane group hit distinct banks).  LDS operations of a
+    // wave complete in order, so one area serves every chunk.
+    uint8_t* mine = xs + w * kXresWaveBytes;
+    uint4 xr[CH][4];
+    auto stage_x = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint4*>(mine + (4 * i + (lane >> 4)) * kXresRowBytes + (lane & 15) * 16) = xa[c][i];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            xr[c][t] = *reinterpret_cast<const uint4*>(mine + r * kXresRowBytes + g * 64 + t * 16);
+    };
+
+    // prologue: the first ring item, the whole activation slice, the rest of
+    // the ring; then the slice is staged into registers (the first chunk's
+    // work waits only for the first weights and the activation)
+    load_item(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) load_x(c);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 1; d < DR; ++d) {
+        load_item(d, d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) stage_x(c);
+
+    f32x4 acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+        const int slot = it % DR, u = it / CH, c = it % CH;
+        const uint4 cv = cw[slot];
+        const uint32_t sv = sw[slot];
+        if (it + DR < NI) {
+            load_item(it + DR, slot);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        f32x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(scale_pair(sv, lane), 1.0f, false);
+        if (!FULL) {
+            const bool have = c < nch;
+            sc.x = have ? sc.x : 0.f;
+            sc.y = have ? sc.y : 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t d = t == 0 ? cv.x : t == 1 ? cv.y : t == 2 ? cv.z : cv.w;
+            const bf16x8 bf = uint4_to_bf16x8(decode8_bf16(d, t < 2 ? sc.x : sc.y));
+            acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uint4_to_bf16x8(xr[c][t]), bf, acc[u], 0, 0, 0);
+        }
+    }
+
+    // ---- reduce the W wave tiles: lane (r, g) holds rows 4 g + i of column 16 u + r
+    if (w >= H) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) *reinterpret_cast<f32x4*>(&red[((w - H) * U + u) * 256 + lane * 4]) = acc[u];
+    }
+    __syncthreads();
+    if (w < H) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            f32x4* p = reinterpret_cast<f32x4*>(&red[(w * U + u) * 256 + lane * 4]);
+            *p = acc[u] + *p;
+        }
+    }
+    __syncthreads();
+    const float gv = effective_global_scale(gscale[0], g_is_div);
+    for (int o = tid; o < TILE; o += W * 64) {
+        // o = (u, m, n): consecutive threads take consecutive columns of one row
+        const int m = (o >> 4) & 15;
+        const int src = (o >> 8) * 256 + ((m >> 2) * 16 + (o & 15)) * 4 + (m & 3);
+        float a = red[src];
+#pragma unroll
+        for (int ww = 1; ww < H; ++ww) a += red[ww * TILE + src];
+        const int64_t col = (int64_t)(u0 + (o >> 8)) * kUnitN + (o & 15);
+        if (m < rows && col < N) y[(int64_t)m * ld_y + col] = (uint16_t)f32_to_bf16_rne(gv * a);
+    }
+}
+
+}  // namespace nvfp4

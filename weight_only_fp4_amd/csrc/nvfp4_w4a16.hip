@@ -14,6 +14,7 @@
 #include "kernels_gemm.h"
 #include "kernels_moe.h"
 #include "kernels_tile.h"
+#include "kernels_xres.h"
 #include "launch_mfma.h"
 
 using namespace nvfp4;
@@ -56,7 +57,7 @@ nvfp4_status check_weight_shape(const char* fn, int64_t E, int64_t N, int64_t K)
 // Bytes of the pre-scaled activation copy kept in the workspace.
 int64_t prescale_bytes(int64_t rows, int64_t K) { return round_up(rows * K * 2, 256); }
 
-enum Variant { kAuto = 0, kSmall = 1, kLarge = 2, kMfma = 3 };
+enum Variant { kAuto = 0, kSmall = 1, kLarge = 2, kMfma = 3, kResident = 4 };
 
 // Small-M launch shape: row form mg (1, 2: 4x4x4 with that many row groups;
 // 16: 16x16x32), nt units per wave, w waves per workgroup, ring depth d, and
@@ -275,6 +276,73 @@ nvfp4_status launch_tile(const TileShape& t, const Layout& L, const uint16_t* x,
     return launched("tile GEMM");
 }
 
+// ------------------------------------------------ activation-resident path --
+// (ch, u, w, d): chunks per wave, units per workgroup, waves, ring depth.
+// From launch sweeps on MI355X (graph-replayed, weights rotated past the
+// Infinity Cache): 16 waves with a 2-deep ring for K up to 4096, the
+// workgroup count near the CU count (u = ceil(row units / 256)).
+#define NVFP4_XRES_CONFIGS(X) \
+    X(1, 1, 16, 2) X(1, 2, 16, 2) X(1, 3, 16, 2) X(1, 4, 16, 2) X(1, 5, 16, 2) X(1, 6, 16, 2) X(1, 7, 16, 2) \
+    X(1, 8, 16, 2) X(2, 1, 16, 2) X(2, 2, 16, 2) X(2, 3, 16, 2) X(2, 4, 16, 2) X(2, 5, 16, 2) X(2, 6, 16, 2) \
+    X(2, 7, 16, 2) X(2, 8, 16, 2)
+
+// Rows from which the automatic choice takes the activation-resident kernel
+// (below it the small-M kernel, measured faster at one row).
+constexpr int64_t kXresAutoMin = 5;
+constexpr int kXresMaxK = 2 * 16 * kChunkK;   // two chunks for each of 16 waves
+constexpr int kXresMaxN = 8 * 256 * kUnitN;   // eight units for each of 256 workgroups
+
+struct XresShape {
+    int ch, u, w, d;
+    int64_t groups;
+};
+
+bool xres_compiled(const XresShape& s) {
+    bool found = false;
+#define NVFP4_XRES_FIND(CH, U, W, D) found = found || (s.ch == CH && s.u == U && s.w == W && s.d == D);
+    NVFP4_XRES_CONFIGS(NVFP4_XRES_FIND)
+#undef NVFP4_XRES_FIND
+    return found;
+}
+
+// 16 waves own one or two chunks each (K up to 4096), units per workgroup
+// by N.  A shape outside the compiled set means the kernel does not take the
+// call (K above 4096, or more than 2048 row units).
+XresShape xres_shape(const Layout& L) {
+    XresShape s{L.KC <= 16 ? 1 : 2, 0, 16, 2, 0};
+    const int64_t u = (L.NU + 255) / 256;
+    s.u = (int)(u < 1 ? 1 : u > 64 ? 64 : u);
+    s.groups = (L.NU + s.u - 1) / s.u;
+    return s;
+}
+
+// Does the activation-resident kernel take this dense call?
+bool xres_fits(const Layout& L, int64_t rows) {
+    const XresShape s = xres_shape(L);
+    return rows <= kSmallRows && (int64_t)s.w * s.ch >= L.KC && xres_compiled(s);
+}
+
+nvfp4_status launch_xres(const XresShape& s, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
+                         const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows, hipStream_t st) {
+    const BlobView bv = make_view(L, blob);
+    const dim3 grid((unsigned)s.groups);
+    bool done = false;
+#define NVFP4_XRES_DISPATCH(CH, U, W, D)                                                                          \
+    if (!done && s.ch == CH && s.u == U && s.w == W && s.d == D) {                                               \
+        if (L.K == (int64_t)CH * W * kChunkK)                                                                   \
+            hipLaunchKernelGGL((k_gemm_xres<CH, U, W, D, true>), grid, dim3(W * 64), 0, st, x, ld_x, bv,         \
+                               (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, (int)rows);        \
+        else                                                                                                     \
+            hipLaunchKernelGGL((k_gemm_xres<CH, U, W, D, false>), grid, dim3(W * 64), 0, st, x, ld_x, bv,        \
+                               (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, (int)rows);        \
+        done = true;                                                                                             \
+    }
+    NVFP4_XRES_CONFIGS(NVFP4_XRES_DISPATCH)
+#undef NVFP4_XRES_DISPATCH
+    if (!done) return fail(NVFP4_ERR_INVALID_ARG, "activation-resident GEMM: no compiled kernel for this shape");
+    return launched("activation-resident GEMM");
+}
+
 // Activation row stride limit: offsets within a 128-row tile stay in 32 bits.
 constexpr int64_t kMaxLdX = int64_t(1) << 23;
 
@@ -347,21 +415,29 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
     const char* fn = "nvfp4_w4a16_gemm";
     nvfp4_status s = check_weight_shape(fn, 1, N, K);
     if (s != NVFP4_OK) return s;
-    if (variant < kAuto || variant > kMfma) return fail(NVFP4_ERR_INVALID_ARG, "%s: unknown variant %d", fn, variant);
+    if (variant < kAuto || variant > kResident) return fail(NVFP4_ERR_INVALID_ARG, "%s: unknown variant %d", fn, variant);
     if (variant == kSmall && M > kSmallRows)
         return fail(NVFP4_ERR_INVALID_ARG, "%s: the small-M variant takes M <= %d (M = %lld)", fn, kSmallRows, (long long)M);
     if (M > (int64_t)1 << 31) return fail(NVFP4_ERR_INVALID_ARG, "%s: M = %lld too large", fn, (long long)M);
     const Layout L = make_layout(1, N, K);
     const TileShape t = tile_shape(L, M, false);
     const SmallShape sm = small_m_shape(L, M, false);
-    const bool small = variant == kSmall || (variant == kAuto && M <= kSmallAuto);
+    if (variant == kResident && !xres_fits(L, M))
+        return fail(NVFP4_ERR_INVALID_ARG,
+                    "%s: the activation-resident variant takes M <= %d, K <= %d and N <= %d (M = %lld, N = %lld, K = %lld)",
+                    fn, kSmallRows, kXresMaxK, kXresMaxN, (long long)M, (long long)N, (long long)K);
+    const bool resident =
+        variant == kResident || (variant == kAuto && M >= kXresAutoMin && xres_fits(L, M));
+    const XresShape xs = xres_shape(L);
+    const bool small = variant == kSmall || (variant == kAuto && !resident && M <= kSmallAuto);
     // the MFMA-bound kernel addresses the code and scale regions with 32-bit offsets
     const bool mfma_fits = L.code_bytes() < ((int64_t)1 << 31);
     if (variant == kMfma && !mfma_fits)
         return fail(NVFP4_ERR_INVALID_ARG, "%s: the MFMA-bound variant takes weights below 2 GiB of codes", fn);
     const bool mfma = variant == kMfma ||
                       (variant == kAuto && mfma_fits && M >= kMfmaAuto && mfma_plan(L, M).tiles >= kMfmaMinTiles);
-    const Workspace wl = small  ? workspace_for(sm, M, K, pre != nullptr)
+    const Workspace wl = resident ? workspace_layout(1, 0, 0, M, K, pre != nullptr)
+                         : small  ? workspace_for(sm, M, K, pre != nullptr)
                          : mfma ? workspace_layout(1, 0, 0, M, K, pre != nullptr)
                                 : workspace_for(t, M, K, pre != nullptr);
     s = check_gemm_io(fn, x, ld_x, pre, w, gs, y, ld_y, M, N, K, ws, ws_bytes, wl.total);
@@ -374,6 +450,7 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
     if (s != NVFP4_OK) return s;
     const uint8_t* blob = static_cast<const uint8_t*>(w);
     uint16_t* yo = static_cast<uint16_t*>(y);
+    if (resident) return launch_xres(xs, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, st);
     if (small)
         return launch_small<false>(sm, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, split_k(sm.S, wsb, wl), st);
     if (mfma) {
