@@ -134,6 +134,13 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     __shared__ __attribute__((aligned(16))) uint8_t stage[2][kStage];
     constexpr int kWStage = kMfmaNT * (kCodeBlock + kScaleBlock);   // one chunk of a wave's weights
     __shared__ __attribute__((aligned(16))) uint8_t wstage[kMfmaWN][kWStage];
+    // The asynchronous global -> LDS copies must not share a compute unit
+    // with another workgroup of this kernel: a 64-row variant whose LDS let
+    // two workgroups reside on one compute unit returned wrong outputs
+    // exactly when the grid exceeded the compute-unit count (measured; the
+    // copies of one corrupted the other's staged data).  Every form takes
+    // more than half of the 160 KB of LDS, which leaves room for one.
+    static_assert(2 * kStage + kMfmaWN * kWStage > 80 * 1024, "one workgroup per compute unit");
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
