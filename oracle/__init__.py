@@ -35,6 +35,17 @@ FC1: SGLang compressed-tensors NVFP4 weight-only page, review discussion):
     relu2       : a = max(h, 0)^2 (non-gated experts)            (fp64, not rounded)
     combine     : out[t] = sum_j w[t, j] * y[row of (t, j)]      (fp64, not rounded)
 
+FP16 activations (numpy, fp64; the same operation with X, the pre-quant scale
+and Y in IEEE binary16, which weight-only FP4 serves as well as bf16: "Support
+nvfp4 w4a16 on sm120", Summary; SGLang compressed-tensors NVFP4 weight-only
+page, Motivation):
+
+    X'[m,k] = RNE_fp16(X[m,k] * s[k]) if a pre-quant scale s is given else X[m,k]
+    Y[m,n]  = g * sum_k X'[m,k] * T[n,k]          (fp64, never rounded)
+
+with T from the C oracle's dequant and the sum as one fp64 np.matmul
+(``gemm_f16``, ``grouped_gemm_f16``).
+
 Acceptance of a GPU result against the oracle (``accept``): relative Frobenius
 error <= 2e-3, every element within 1e-2 * (|ref| + rms(ref)), and every
 element finite.
@@ -277,6 +288,46 @@ def round_bf16_np(v: np.ndarray) -> np.ndarray:
     r = np.ldexp(np.rint(np.ldexp(v[fin], -q)), q)
     r = np.where(np.abs(r) > np.ldexp(255.0, 120), np.copysign(np.inf, r), r)
     out[fin] = r
+    return out
+
+
+# ----------------------------------------------------------- fp16 (numpy) ---
+
+def f16_np(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns (uint16) -> fp64 values (exact)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def rne_f16_np(v: np.ndarray) -> np.ndarray:
+    """fp64 -> nearest binary16 value, ties to even, overflow to +-inf (numpy's conversion), back in fp64."""
+    with np.errstate(over="ignore"):
+        return np.asarray(v, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def activation_f16(x_bits: np.ndarray, pre_bits: np.ndarray | None = None) -> np.ndarray:
+    """X' [M, K] (fp64): X, or RNE_fp16(X * s) with the pre-quant scale s (the product of two binary16 values
+    is exact in fp64, so this is one correct rounding)."""
+    x = f16_np(x_bits)
+    return x if pre_bits is None else rne_f16_np(x * f16_np(pre_bits)[None, :])
+
+
+def gemm_f16(x_bits, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None) -> np.ndarray:
+    """Dense Y [M, N] in fp64 for fp16 activations (x_bits: binary16 bit patterns [M, K])."""
+    t = dequant(w_packed, w_scale)
+    return global_scale(g_stored, g_is_divisor) * np.matmul(activation_f16(x_bits, pre_bits), t.T)
+
+
+def grouped_gemm_f16(x_bits, offsets, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None) -> np.ndarray:
+    """Grouped Y [R, N] in fp64 for fp16 activations; rows owned by no expert are NaN."""
+    o = np.asarray(offsets, dtype=np.int64)
+    xa = activation_f16(x_bits, pre_bits)
+    E, N = np.asarray(w_packed).shape[0], np.asarray(w_packed).shape[1]
+    out = np.full((xa.shape[0], N), np.nan)
+    for e in range(E):
+        a, b = o[e], o[e + 1]
+        if b > a:
+            g = global_scale(float(np.asarray(g_stored, dtype=np.float32)[e]), g_is_divisor)
+            out[a:b] = g * np.matmul(xa[a:b], dequant(w_packed[e], w_scale[e]).T)
     return out
 
 

@@ -3,7 +3,7 @@
 Shared by the tests, the smoke check and the benchmark, and by both sides of
 every parity check (the GPU library and the CPU oracle).  This module holds
 none of the method's arithmetic: it only draws random numbers and writes them
-in the canonical input formats (bf16 bit patterns, packed 4-bit codes with the
+in the canonical input formats (bf16 or fp16 bit patterns, packed 4-bit codes with the
 even k in the low nibble, E4M3 scale bytes, fp32 global scales, expert
 offsets).  Decoding any of these is the oracle's and the library's business.
 
@@ -62,13 +62,31 @@ def scales_log_uniform(g: np.random.Generator, shape, lo=-6.0, hi=3.0) -> np.nda
     return e4m3_bytes_from_f32(np.exp2(u).astype(np.float32))
 
 
+def f16_bits_from_f32(a: np.ndarray) -> np.ndarray:
+    """float32 values -> IEEE binary16 bit patterns (uint16), round to nearest even (numpy cast)."""
+    return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16).copy()
+
+
+def _act_bits(a: np.ndarray, act: str) -> np.ndarray:
+    if act == "bf16":
+        return bf16_bits_from_f32(a)
+    if act == "f16":
+        return f16_bits_from_f32(a)
+    raise ValueError(f"activation type {act!r}")
+
+
 def normal_bf16(g: np.random.Generator, shape) -> np.ndarray:
     return bf16_bits_from_f32(g.standard_normal(size=shape, dtype=np.float32))
 
 
-def awq_prescale(g: np.random.Generator, K: int) -> np.ndarray:
-    """Per-channel pre-quant scale, uniform in [1/e, e], as bf16 bits."""
-    return bf16_bits_from_f32(g.uniform(1.0 / math.e, math.e, size=K).astype(np.float32))
+def normal_act(g: np.random.Generator, shape, act: str = "bf16") -> np.ndarray:
+    """N(0, 1) activations as bf16 or fp16 bits (the same draws either way)."""
+    return _act_bits(g.standard_normal(size=shape, dtype=np.float32), act)
+
+
+def awq_prescale(g: np.random.Generator, K: int, act: str = "bf16") -> np.ndarray:
+    """Per-channel pre-quant scale, uniform in [1/e, e], as bf16 (or fp16) bits."""
+    return _act_bits(g.uniform(1.0 / math.e, math.e, size=K).astype(np.float32), act)
 
 
 @dataclass
@@ -77,26 +95,28 @@ class DenseCase:
     M: int
     N: int
     K: int
-    x: np.ndarray             # uint16 bf16 bits [M, K]
+    x: np.ndarray             # uint16 bf16 (or fp16, act == "f16") bits [M, K]
     w: np.ndarray             # uint8 [N, K/2]
     s: np.ndarray             # uint8 E4M3 [N, K/16]
     g_stored: float           # fp32 value as stored
     g_is_divisor: bool
-    pre: np.ndarray | None    # uint16 bf16 bits [K] or None
+    pre: np.ndarray | None    # uint16 bits [K] (the type of x) or None
     meta: dict = field(default_factory=dict)
+    act: str = "bf16"         # activation / output type
 
 
 def dense_case(M: int, N: int, K: int, seed: int, *, scales: str = "pow2_mant", g_stored: float = 1.0 / 448.0,
-               g_is_divisor: bool = False, prescale: bool = False, name: str = "") -> DenseCase:
-    """One dense workload.  scales: 'pow2_mant' (2^u (1+m/8), u in [-4,2]) or 'log_uniform' ([2^-6, 2^3])."""
+               g_is_divisor: bool = False, prescale: bool = False, name: str = "", act: str = "bf16") -> DenseCase:
+    """One dense workload.  scales: 'pow2_mant' (2^u (1+m/8), u in [-4,2]) or 'log_uniform' ([2^-6, 2^3]).
+    act: activation type, 'bf16' or 'f16' (the same random draws, rounded to that type)."""
     assert K % 16 == 0 and K % 2 == 0
     g = rng(seed)
-    x = normal_bf16(g, (M, K))
+    x = normal_act(g, (M, K), act)
     w = random_codes(g, (N, K))
     s = scales_pow2_mant(g, (N, K // 16)) if scales == "pow2_mant" else scales_log_uniform(g, (N, K // 16))
-    pre = awq_prescale(g, K) if prescale else None
+    pre = awq_prescale(g, K, act) if prescale else None
     return DenseCase(name or f"dense_M{M}_N{N}_K{K}", M, N, K, x, w, s, float(np.float32(g_stored)),
-                     bool(g_is_divisor), pre, {"seed": seed, "scales": scales})
+                     bool(g_is_divisor), pre, {"seed": seed, "scales": scales}, act)
 
 
 def zipf_routing(g: np.random.Generator, T: int, E: int, topk: int, s: float = 1.1) -> np.ndarray:
@@ -116,7 +136,7 @@ class GroupedCase:
     N: int
     K: int
     R: int
-    x: np.ndarray             # uint16 bf16 bits [R, K], rows grouped by expert
+    x: np.ndarray             # uint16 bf16 (or fp16) bits [R, K], rows grouped by expert
     offsets: np.ndarray       # int32 [E+1]
     w: np.ndarray             # uint8 [E, N, K/2]
     s: np.ndarray             # uint8 [E, N, K/16]
@@ -124,6 +144,7 @@ class GroupedCase:
     g_is_divisor: bool
     pre: np.ndarray | None
     meta: dict = field(default_factory=dict)
+    act: str = "bf16"
 
     @property
     def active(self) -> np.ndarray:
@@ -136,18 +157,18 @@ def routing_seed(seed: int) -> int:
 
 def grouped_case(T: int, E: int, topk: int, N: int, K: int, seed: int, *, x_source: str = "gather",
                  prescale: bool = False, g_base: float = 1.0 / 2688.0, name: str = "",
-                 routing: np.ndarray | None = None, seed0: int | None = None) -> GroupedCase:
+                 routing: np.ndarray | None = None, seed0: int | None = None, act: str = "bf16") -> GroupedCase:
     """Grouped MoE workload.  x_source 'gather': rows are tokens X[T, K] gathered per (token, expert) pair in
     expert order; 'fresh': a new N(0,1) [R, K] input (the FC2 side, whose real input is FC1's activation).
     The routing comes from its own stream, seeded by ``routing_seed(seed0 or seed)``, so FC1 and FC2 cases
     built with the same seed0 share it."""
     g = rng(seed)
-    xt = normal_bf16(g, (T, K))
+    xt = normal_act(g, (T, K), act)
     w = random_codes(g, (E, N, K))
     s = scales_pow2_mant(g, (E, N, K // 16))
     v = g.integers(-2, 3, size=E)
     gs = (np.exp2(v.astype(np.float64)) * g_base).astype(np.float32)
-    pre = awq_prescale(g, K) if prescale else None
+    pre = awq_prescale(g, K, act) if prescale else None
     route = zipf_routing(rng(routing_seed(seed0 if seed0 is not None else seed)), T, E, topk) \
         if routing is None else routing
     tok = np.repeat(np.arange(T), route.shape[1])
@@ -157,10 +178,10 @@ def grouped_case(T: int, E: int, topk: int, N: int, K: int, seed: int, *, x_sour
     offsets = np.zeros(E + 1, dtype=np.int32)
     offsets[1:] = np.cumsum(counts)
     R = int(offsets[-1])
-    x = xt[tok[order]] if x_source == "gather" else normal_bf16(g, (R, K))
+    x = xt[tok[order]] if x_source == "gather" else normal_act(g, (R, K), act)
     return GroupedCase(name or f"grouped_T{T}_E{E}_N{N}_K{K}", E, N, K, R, np.ascontiguousarray(x), offsets,
                        w, s, gs, False, pre, {"seed": seed, "T": T, "topk": topk, "token_of_row": tok[order],
-                                              "routing": route})
+                                              "routing": route}, act)
 
 
 # ------------------------------------------------------------- workloads ---

@@ -416,3 +416,117 @@ def test_relu2_closed_forms():
     out = oracle.relu2(bits)[0]
     assert np.array_equal(out, np.array([x * x if x > 0 else 0.0 for x in v]))
     assert np.all(out[v <= 0] == 0)
+
+
+# ------------------------------------------------------------ fp16 oracle ---
+
+def test_f16_decode_matches_struct_for_every_pattern():
+    """All 65536 binary16 patterns decode as Python's own IEEE half unpacking (struct 'e') does."""
+    import struct
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.f16_np(bits)
+    ref = np.array([struct.unpack("<e", int(b).to_bytes(2, "little"))[0] for b in bits], dtype=np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))   # signed zeros
+
+
+def test_rne_f16_ties_subnormals_and_overflow():
+    """Round to nearest even into binary16: exact ties go to the even significand, in the normal and the subnormal
+    range; 65504 is the largest finite value and everything from 65520 (the tie with 2^16) up overflows."""
+    ulp1 = 2.0 ** -10
+    cases = [
+        (1.0 + ulp1 / 2, 1.0),                     # tie, even is 1.0
+        (1.0 + 3 * ulp1 / 2, 1.0 + 2 * ulp1),      # tie, even is 1 + 2 ulp
+        (1.0 + ulp1 / 2 + 2.0 ** -30, 1.0 + ulp1),  # just above the tie
+        (2.0 ** -25, 0.0),                          # half the smallest subnormal: tie, even is 0
+        (3 * 2.0 ** -25, 2.0 ** -23),               # tie between 1 and 2 subnormal steps: even is 2
+        (2.0 ** -24, 2.0 ** -24),                   # smallest subnormal, exact
+        (65504.0, 65504.0),
+        (65519.99, 65504.0),
+        (65520.0, math.inf),
+        (-65520.0, -math.inf),
+        (1e300, math.inf),
+    ]
+    v = np.array([a for a, _ in cases])
+    assert np.array_equal(oracle.rne_f16_np(v), np.array([b for _, b in cases]))
+    # and random finite values agree with Python's half packing (round-half-even)
+    import struct
+    g = synth.rng(5)
+    r = g.standard_normal(2000) * np.exp2(g.integers(-26, 16, 2000))
+    r = r[np.abs(r) < 65504.0]   # struct refuses values that overflow (covered by the cases above)
+    ref = [struct.unpack("<e", struct.pack("<e", float(a)))[0] for a in r]
+    assert np.array_equal(oracle.rne_f16_np(r), np.array(ref))
+
+
+def test_activation_f16_prescale_rounds_each_exact_product_once():
+    import struct
+    g = synth.rng(6)
+    x = synth.f16_bits_from_f32(g.standard_normal((3, 64)).astype(np.float32) * 8)
+    pre = synth.f16_bits_from_f32(g.uniform(1 / math.e, math.e, 64).astype(np.float32))
+    got = oracle.activation_f16(x, pre)
+    dec = lambda b: struct.unpack("<e", int(b).to_bytes(2, "little"))[0]
+    for m in range(3):
+        for k in range(64):
+            p = dec(x[m, k]) * dec(pre[k])    # exact in binary64
+            assert got[m, k] == struct.unpack("<e", struct.pack("<e", p))[0]
+    assert np.array_equal(oracle.activation_f16(x, None), oracle.f16_np(x))
+
+
+def test_gemm_f16_brute_force_loops():
+    """A tiny fp16 GEMM against plain loops over exact rationals (codes, scales and halves decoded here)."""
+    import struct
+    c = synth.dense_case(2, 3, 32, 11, act="f16", prescale=True, g_stored=3.0, g_is_divisor=True)
+    dec = lambda b: Fraction(struct.unpack("<e", int(b).to_bytes(2, "little"))[0])
+    e2m1 = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4),
+            Fraction(6)]
+
+    def e4m3(b):
+        e, m = (b >> 3) & 15, b & 7
+        v = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+        return -v if b & 0x80 else v
+
+    def code(n, k):
+        byte = int(c.w[n, k // 2])
+        q = byte & 15 if k % 2 == 0 else byte >> 4
+        return -e2m1[q & 7] if q & 8 else e2m1[q & 7]
+
+    g = Fraction(float(np.float32(1) / np.float32(3.0)))
+    ref = np.zeros((2, 3))
+    for m in range(2):
+        for n in range(3):
+            acc = Fraction(0)
+            for k in range(32):
+                xs = float(dec(c.x[m, k]) * dec(c.pre[k]))
+                xp = Fraction(struct.unpack("<e", struct.pack("<e", xs))[0])
+                acc += xp * code(n, k) * e4m3(int(c.s[n, k // 16]))
+            ref[m, n] = float(g * acc)
+    got = oracle.gemm_f16(c.x, c.w, c.s, c.g_stored, True, c.pre)
+    assert np.allclose(got, ref, rtol=1e-13, atol=0)
+
+
+def test_gemm_f16_equals_bf16_oracle_on_values_both_types_hold():
+    """Activations exactly representable in bf16 and in fp16 (at most 8 significant bits, in fp16's normal range):
+    the fp16 oracle and the C oracle's bf16 path define the same Y."""
+    g = synth.rng(12)
+    M, N, K = 3, 20, 96
+    mant = g.integers(-255, 256, (M, K)).astype(np.float64)
+    vals = mant * np.exp2(g.integers(-12, -2, (M, K)).astype(np.float64))
+    x16 = vals.astype(np.float16).view(np.uint16)
+    xbf = synth.bf16_bits_from_f32(vals.astype(np.float32))
+    assert np.array_equal(oracle.f16_np(x16), oracle.bf16_np(xbf))
+    c = synth.dense_case(M, N, K, 13)
+    a = oracle.gemm_f16(x16, c.w, c.s, 1 / 2688.0)
+    b = oracle.gemm(xbf, c.w, c.s, 1 / 2688.0)
+    assert np.allclose(a, b, rtol=1e-12, atol=0)
+
+
+def test_grouped_gemm_f16_rows_follow_their_expert():
+    gc = synth.grouped_case(T=12, E=5, topk=2, N=24, K=64, seed=14, act="f16", prescale=True)
+    got = oracle.grouped_gemm_f16(gc.x, gc.offsets, gc.w, gc.s, gc.g_stored, False, gc.pre)
+    for e in range(gc.E):
+        a, b = gc.offsets[e], gc.offsets[e + 1]
+        if b > a:
+            ref = oracle.gemm_f16(gc.x[a:b], gc.w[e], gc.s[e], float(gc.g_stored[e]), False, gc.pre)
+            assert np.array_equal(got[a:b], ref)
