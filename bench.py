@@ -78,7 +78,7 @@ def dense_bytes(M, N, K, pre):
 
 
 def make_dense(name, M, N, K, *, seed, scales="pow2_mant", g_stored=1.0 / 2688.0, divisor=False, prescale=False,
-               copies=1, host_case=None):
+               copies=1, host_case=None, f16=False):
     import torch
     import synth
     import weight_only_fp4_amd as nv
@@ -95,11 +95,14 @@ def make_dense(name, M, N, K, *, seed, scales="pow2_mant", g_stored=1.0 / 2688.0
         w = synth.device_codes((N, K // 2), seed + 1, dev)
         s = synth.device_scales((N, K // 16), seed + 2, scales, dev)
         pre = synth.device_prescale(K, seed + 3, dev) if prescale else None
+        if f16:   # the fp16 form: the same draws, rounded to fp16
+            x = x.to(torch.float16)
+            pre = None if pre is None else pre.to(torch.float16)
     g = torch.tensor([g_stored], dtype=torch.float32, device=dev)
     blob = nv.repack(w, s)
     del w, s
     blobs = [blob] + [blob.clone() for _ in range(copies - 1)]
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, N), dtype=x.dtype, device=dev)
     ws = nv.workspace(nv.gemm_workspace_bytes(M, N, K), dev)
 
     def launch(i):
@@ -118,7 +121,8 @@ def make_dense(name, M, N, K, *, seed, scales="pow2_mant", g_stored=1.0 / 2688.0
     flops = 2.0 * M * N * K
     ab = dense_bytes(M, N, K, pre is not None)
     bound = "hbm" if flops / ab < (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) else "mfma"
-    meta = {"M": M, "N": N, "K": K, "prescale": pre is not None, "divisor": bool(divisor), "weight_copies": copies}
+    meta = {"M": M, "N": N, "K": K, "prescale": pre is not None, "divisor": bool(divisor), "weight_copies": copies,
+            "activation": "f16" if f16 else "bf16"}
     wl = Workload(name, "dense", kernel, ab, flops, launch, copies, meta, bound)
     wl.tensors = dict(x=x, y=y, g=g, blobs=blobs)
     return wl
@@ -248,6 +252,10 @@ def workload_specs():
                                                      g_stored=2688.0, divisor=True, prescale=True, copies=1),
         "tiny_M4_N256_K512": lambda: make_dense("tiny_M4_N256_K512", 4, 256, 512, seed=1000, g_stored=1 / 448,
                                                 copies=1),
+        "decode_f16_M16_N14336_K4096": lambda: make_dense("decode_f16_M16_N14336_K4096", 16, 14336, 4096,
+                                                          seed=1001, g_stored=1 / (448 * 6), copies=16, f16=True),
+        "prefill_f16_M4096_N14336_K4096": lambda: make_dense("prefill_f16_M4096_N14336_K4096", 4096, 14336, 4096,
+                                                             seed=1002, scales="log_uniform", copies=1, f16=True),
         "moe_fc1_T16": lambda: make_grouped("moe_fc1_T16", 16, "fc1"),
         "moe_fc2_T16": lambda: make_grouped("moe_fc2_T16", 16, "fc2"),
         "moe_fc1_T2048": lambda: make_grouped("moe_fc1_T2048", 2048, "fc1"),

@@ -8,7 +8,8 @@
  *
  * W is packed FP4 (E2M1, two codes per byte along K) with one FP8 (E4M3)
  * scale per 16 consecutive K of a row and one fp32 global scale g; the
- * activation X and the output Y stay bf16.  Where the operation is defined:
+ * activation X and the output Y stay bf16 (fp16 in the *_f16 calls at the
+ * end of this file).  Where the operation is defined:
  *   - packed FP4 weights + per-group FP8 scales + bf16/fp16 activations:
  *     "Support nvfp4 w4a16 on sm120", Summary;
  *   - E2M1 codebook lookup times a per-block FP8 scale and a per-tensor
@@ -240,6 +241,36 @@ nvfp4_status nvfp4_w4a16_gemm_variant(const void* x, int64_t ld_x, const void* p
                                       const float* global_scale, int global_scale_is_divisor,
                                       void* y, int64_t ld_y, int64_t M, int64_t N, int64_t K,
                                       void* workspace, int64_t workspace_bytes, int variant, void* stream);
+
+/* ---- FP16 activations and outputs ------------------------------------------
+ *
+ * The same operations with X, the pre-quant scale and Y in IEEE binary16
+ * instead of bf16 (weight-only FP4 serves bf16 or fp16 activations: "Support
+ * nvfp4 w4a16 on sm120", Summary; SGLang compressed-tensors NVFP4
+ * weight-only page, Motivation).  Arguments, layouts, workspace sizes
+ * (nvfp4_w4a16_gemm_workspace_bytes / nvfp4_w4a16_grouped_gemm_workspace_bytes),
+ * kernel choice, ownership and errors are those of the bf16 calls above.
+ * The decoded weights are exact in fp16 (e2m1 * e4m3 lies in [2^-10, 2688]
+ * with at most 6 significant bits), the MFMAs take fp16 with fp32
+ * accumulation, the pre-scaled activation is RNE_fp16(X * s) and
+ * Y = RNE_fp16(g * acc); outputs beyond the fp16 range become +-infinity. */
+nvfp4_status nvfp4_w4a16_gemm_f16(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
+                                  const float* global_scale, int global_scale_is_divisor, void* y, int64_t ld_y,
+                                  int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                                  void* stream);
+
+/* nvfp4_w4a16_gemm_variant with fp16 activations and outputs. */
+nvfp4_status nvfp4_w4a16_gemm_variant_f16(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
+                                          const float* global_scale, int global_scale_is_divisor, void* y,
+                                          int64_t ld_y, int64_t M, int64_t N, int64_t K, void* workspace,
+                                          int64_t workspace_bytes, int variant, void* stream);
+
+/* nvfp4_w4a16_grouped_gemm with fp16 activations and outputs. */
+nvfp4_status nvfp4_w4a16_grouped_gemm_f16(const void* x, int64_t ld_x, const int32_t* expert_offsets,
+                                          const void* pre_scale, const void* w_repacked, const float* global_scales,
+                                          int global_scale_is_divisor, void* y, int64_t ld_y, int64_t R, int64_t E,
+                                          int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                                          void* stream);
 
 #ifdef __cplusplus
 }

@@ -55,10 +55,16 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_w4a16_gemm.restype = I
         L.nvfp4_w4a16_gemm_variant.argtypes = [P, I64, P, P, P, I, P, I64, I64, I64, I64, P, I64, I, P]
         L.nvfp4_w4a16_gemm_variant.restype = I
+        L.nvfp4_w4a16_gemm_f16.argtypes = [P, I64, P, P, P, I, P, I64, I64, I64, I64, P, I64, P]
+        L.nvfp4_w4a16_gemm_f16.restype = I
+        L.nvfp4_w4a16_gemm_variant_f16.argtypes = [P, I64, P, P, P, I, P, I64, I64, I64, I64, P, I64, I, P]
+        L.nvfp4_w4a16_gemm_variant_f16.restype = I
         L.nvfp4_w4a16_grouped_gemm_workspace_bytes.argtypes = [I64, I64, I64, I64]
         L.nvfp4_w4a16_grouped_gemm_workspace_bytes.restype = I64
         L.nvfp4_w4a16_grouped_gemm.argtypes = [P, I64, P, P, P, P, I, P, I64, I64, I64, I64, I64, P, I64, P]
         L.nvfp4_w4a16_grouped_gemm.restype = I
+        L.nvfp4_w4a16_grouped_gemm_f16.argtypes = [P, I64, P, P, P, P, I, P, I64, I64, I64, I64, I64, P, I64, P]
+        L.nvfp4_w4a16_grouped_gemm_f16.restype = I
         L.nvfp4_w4a16_grouped_gemm_gather_workspace_bytes.argtypes = [I64, I64, I64, I64, I64]
         L.nvfp4_w4a16_grouped_gemm_gather_workspace_bytes.restype = I64
         L.nvfp4_w4a16_grouped_gemm_gather.argtypes = [P, I64, I64, P, P, P, P, P, I, P, I64, I64, I64, I64, I64, P,
@@ -136,8 +142,15 @@ def dequant(blob: torch.Tensor, E: int, N: int, K: int) -> torch.Tensor:
     return out
 
 
+_ACT_DTYPES = (torch.bfloat16, torch.float16)
+
+
 def _gemm_args(x, blob, N, K, global_scale, pre_scale, out, rows_name="M"):
-    _dev("x", x, torch.bfloat16, 2)
+    """Checks shared by the GEMM calls.  x is bf16 or fp16; pre_scale and out must have x's dtype."""
+    if not isinstance(x, torch.Tensor) or x.dtype not in _ACT_DTYPES:
+        raise ValueError("x must be a bf16 or fp16 tensor")
+    dt = x.dtype
+    _dev("x", x, dt, 2)
     _dev("blob", blob, torch.uint8, 1)
     _dev("global_scale", global_scale, torch.float32)
     if not global_scale.is_contiguous():
@@ -145,21 +158,22 @@ def _gemm_args(x, blob, N, K, global_scale, pre_scale, out, rows_name="M"):
     if x.shape[1] != K:
         raise ValueError(f"x has {x.shape[1]} columns, K = {K}")
     if pre_scale is not None:
-        _dev("pre_scale", pre_scale, torch.bfloat16, 1)
+        _dev("pre_scale", pre_scale, dt, 1)
         if pre_scale.shape[0] != K or not pre_scale.is_contiguous():
-            raise ValueError(f"pre_scale must be a contiguous bf16 [{K}]")
+            raise ValueError(f"pre_scale must be a contiguous {dt} [{K}]")
     M = x.shape[0]
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+        out = torch.empty((M, N), dtype=dt, device=x.device)
     else:
-        _dev("out", out, torch.bfloat16, 2)
+        _dev("out", out, dt, 2)
         if out.shape[0] != M or out.shape[1] != N:
             raise ValueError(f"out must be [{M}, {N}]")
     return M, out
 
 
 def gemm(x, blob, N, K, global_scale, divisor=False, pre_scale=None, out=None, workspace_buf=None):
-    """Y[M, N] = g * (x (.) pre_scale) . dequant(W)^T in bf16 (dense linear / LM head).  workspace_buf: an optional
+    """Y[M, N] = g * (x (.) pre_scale) . dequant(W)^T in x's dtype, bf16 or fp16 (dense linear / LM head).
+    workspace_buf: an optional
     buffer from ``workspace(gemm_workspace_bytes(M, N, K), device)``, reusable across calls on one stream."""
     return gemm_variant(x, blob, N, K, global_scale, divisor, pre_scale, out, workspace_buf, VARIANT_AUTO)
 
@@ -182,9 +196,9 @@ def gemm_variant(x, blob, N, K, global_scale, divisor=False, pre_scale=None, out
         raise ValueError(f"invalid GEMM shape M={M} N={N} K={K}")
     if workspace_buf is None:
         workspace_buf = workspace(need, x.device)
-    _check(lib().nvfp4_w4a16_gemm_variant(_ptr(x), x.stride(0), _ptr(pre_scale), _ptr(blob), _ptr(global_scale),
-                                          int(bool(divisor)), _ptr(out), out.stride(0), M, N, K, _ptr(workspace_buf),
-                                          workspace_buf.numel(), int(variant), _stream(x.device)))
+    fn = lib().nvfp4_w4a16_gemm_variant_f16 if x.dtype == torch.float16 else lib().nvfp4_w4a16_gemm_variant
+    _check(fn(_ptr(x), x.stride(0), _ptr(pre_scale), _ptr(blob), _ptr(global_scale), int(bool(divisor)), _ptr(out),
+              out.stride(0), M, N, K, _ptr(workspace_buf), workspace_buf.numel(), int(variant), _stream(x.device)))
     return out
 
 
@@ -197,17 +211,18 @@ def grouped_gemm(x, expert_offsets, blob, E, N, K, global_scales, divisor=False,
         raise ValueError(f"expert_offsets must be a contiguous int32 [{E + 1}]")
     if global_scales.numel() != E:
         raise ValueError(f"global_scales must hold {E} values")
-    if out is None:
-        out = torch.zeros((x.shape[0], N), dtype=torch.bfloat16, device=x.device)
+    if out is None and isinstance(x, torch.Tensor) and x.dtype in _ACT_DTYPES:
+        out = torch.zeros((x.shape[0], N), dtype=x.dtype, device=x.device)
     R, out = _gemm_args(x, blob, N, K, global_scales, pre_scale, out)
     need = int(lib().nvfp4_w4a16_grouped_gemm_workspace_bytes(R, E, N, K))
     if need < 0:
         raise ValueError(f"invalid grouped GEMM shape R={R} E={E} N={N} K={K}")
     if workspace_buf is None:
         workspace_buf = workspace(need, x.device)
-    _check(lib().nvfp4_w4a16_grouped_gemm(_ptr(x), x.stride(0), _ptr(expert_offsets), _ptr(pre_scale), _ptr(blob),
-                                          _ptr(global_scales), int(bool(divisor)), _ptr(out), out.stride(0), R, E,
-                                          N, K, _ptr(workspace_buf), workspace_buf.numel(), _stream(x.device)))
+    fn = lib().nvfp4_w4a16_grouped_gemm_f16 if x.dtype == torch.float16 else lib().nvfp4_w4a16_grouped_gemm
+    _check(fn(_ptr(x), x.stride(0), _ptr(expert_offsets), _ptr(pre_scale), _ptr(blob), _ptr(global_scales),
+              int(bool(divisor)), _ptr(out), out.stride(0), R, E, N, K, _ptr(workspace_buf), workspace_buf.numel(),
+              _stream(x.device)))
     return out
 
 

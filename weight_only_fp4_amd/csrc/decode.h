@@ -100,6 +100,82 @@ __device__ __forceinline__ s16x4 dwords_to_s16x4(uint32_t lo, uint32_t hi) {
 
 __device__ __forceinline__ bf16x8 uint4_to_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// ---- activation element type: bf16 (F16 = false) or fp16 (F16 = true).
+// X and Y share the type; weights decode to it exactly (e2m1 * e4m3 has at
+// most 6 significant bits and lies in [2^-10, 2688], inside the normal range
+// of both types), and the MFMAs take it with fp32 accumulation.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two exact fp32 values -> one dword of two 16-bit values (lo first).
+template <bool F16>
+__device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
+    if constexpr (F16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+    else return pack_hi_halves(lo, hi);
+}
+
+// Eight E2M1 codes times a full fp32 scale -> eight values in k order, exact.
+template <bool F16>
+__device__ __forceinline__ uint4 decode8(uint32_t codes, float scale) {
+    if constexpr (!F16) return decode8_bf16(codes, scale);
+    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+    uint4 r;
+    r.x = pack_exact<true>(p0.x * scale, p0.y * scale);
+    r.y = pack_exact<true>(p1.x * scale, p1.y * scale);
+    r.z = pack_exact<true>(p2.x * scale, p2.y * scale);
+    r.w = pack_exact<true>(p3.x * scale, p3.y * scale);
+    return r;
+}
+
+// Four E2M1 codes (bytes BYTE, BYTE + 1) times 2^exp(cvt_scale) -> four values, exact.
+template <bool F16, int BYTE>
+__device__ __forceinline__ s16x4 decode4_pow2(uint32_t codes, float cvt_scale) {
+    if constexpr (!F16) return decode4_bf16_pow2<BYTE>(codes, cvt_scale);
+    const uint32_t ua = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, cvt_scale, BYTE));
+    const uint32_t ub =
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, cvt_scale, BYTE + 1));
+    return dwords_to_s16x4(ua, ub);
+}
+
+// acc + A . B for one 16 x 16 x 32 step; a and b hold eight values each.
+template <bool F16>
+__device__ __forceinline__ f32x4 mma16(uint4 a, uint4 b, f32x4 acc) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc,
+                                                      0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(uint4_to_bf16x8(a), uint4_to_bf16x8(b), acc, 0, 0, 0);
+}
+
+// acc + A . B in the 16-block 4 x 4 x 4 form (cbsz / abid broadcast controls).
+template <bool F16, int CBSZ, int ABID>
+__device__ __forceinline__ f32x4 mma4(s16x4 a, s16x4 b, f32x4 acc) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), acc, CBSZ,
+                                                  ABID, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, b, acc, CBSZ, ABID, 0);
+}
+
+// fp32 -> 16-bit output pattern, round to nearest even (NaN stays NaN;
+// fp16 overflows to infinity).
+template <bool F16>
+__device__ __forceinline__ uint32_t round_out(float v) {
+    if constexpr (F16) return __builtin_bit_cast(uint16_t, (_Float16)v);
+    else return f32_to_bf16_rne(v);
+}
+
+// 16-bit activation pattern -> fp32 (exact).
+template <bool F16>
+__device__ __forceinline__ float act_to_f32(uint32_t h) {
+    if constexpr (F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+    else return bf16_to_f32(h);
+}
+
 // Streaming loads of weight codes and scales: every byte is read exactly
 // once, so the loads are marked non-temporal and do not displace the
 // activations (which are reused) from the caches.

@@ -80,9 +80,12 @@ __global__ void __launch_bounds__(256) k_dequant(BlobView v, int64_t N, int64_t 
     }
 }
 
-// X'[r][k] = RNE_bf16(X[r][k] * s[k]) for r < rows, k < K, eight elements per
-// thread (K is a multiple of 16).  The product of two bf16 values is exact in
-// fp32, so a single rounding to bf16 gives the correctly rounded result.
+// X'[r][k] = RNE(X[r][k] * s[k]) for r < rows, k < K, eight elements per
+// thread (K is a multiple of 16), in bf16 (fp16 with F16).  The product of
+// two bf16 values, or of two fp16 values (11 x 11 significant bits, exponents
+// within fp32's range), is exact in fp32, so a single rounding to the 16-bit
+// type gives the correctly rounded result.
+template <bool F16 = false>
 __global__ void __launch_bounds__(256) k_prescale(const uint16_t* __restrict__ x, int64_t ld_x,
                                                   const uint16_t* __restrict__ pre, int64_t rows, int64_t K,
                                                   uint16_t* __restrict__ out, int64_t ld_out) {
@@ -96,9 +99,9 @@ __global__ void __launch_bounds__(256) k_prescale(const uint16_t* __restrict__ x
     uint32_t od[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float a0 = bf16_to_f32(xd[i] & 0xFFFFu) * bf16_to_f32(sd[i] & 0xFFFFu);
-        const float a1 = bf16_to_f32(xd[i] >> 16) * bf16_to_f32(sd[i] >> 16);
-        od[i] = f32_to_bf16_rne(a0) | (f32_to_bf16_rne(a1) << 16);
+        const float a0 = act_to_f32<F16>(xd[i] & 0xFFFFu) * act_to_f32<F16>(sd[i] & 0xFFFFu);
+        const float a1 = act_to_f32<F16>(xd[i] >> 16) * act_to_f32<F16>(sd[i] >> 16);
+        od[i] = round_out<F16>(a0) | (round_out<F16>(a1) << 16);
     }
     *reinterpret_cast<uint4*>(out + r * ld_out + k) = make_uint4(od[0], od[1], od[2], od[3]);
 }

@@ -1,6 +1,9 @@
 // W4A16 NVFP4 GEMM kernels for gfx950.
 //
-//   Y[m,n] = RNE_bf16(g * sum_k X'[m,k] * e2m1(code(n,k)) * e4m3(S[n,k/16]))
+//   Y[m,n] = RNE(g * sum_k X'[m,k] * e2m1(code(n,k)) * e4m3(S[n,k/16]))
+//
+// X and Y are bf16, or fp16 with F16 (the same kernels; weights decode exactly
+// to either type, MFMAs of that type, RNE to it in the epilogue).
 //
 // X' is the activation (already multiplied by the pre-quant scale when one
 // is given).  This file holds the small-M kernel, used for up to 4 rows
@@ -99,7 +102,7 @@ __device__ __forceinline__ void build_scale_table(float2* lut) {
 // always does.  Pieces past K are zeroed here, at use, so that data read
 // from the clamped address cannot reach the sums (the weights there are zero
 // padding, but the activation might not be finite).
-template <int MG, int NT, bool KFULL>
+template <int MG, int NT, bool KFULL, bool F16>
 __device__ __forceinline__ void small_m_chunk(const SmallSlot<MG, NT>& s, bool kin, const float2* lut, int lane,
                                               f32x4 (&acc)[NT][MG]) {
     s16x4 alo[MG], ahi[MG];
@@ -119,22 +122,22 @@ __device__ __forceinline__ void small_m_chunk(const SmallSlot<MG, NT>& s, bool k
         const uint32_t sp = scale_pair(s.sw[j], lane);
         const float2 s0 = lut[sp & 0xFFu], s1 = lut[(sp >> 8) & 0xFFu];
         const uint4 cw = s.cw[j];
-        const s16x4 b0 = decode4_bf16_pow2<0>(cw.x, s0.x), b1 = decode4_bf16_pow2<2>(cw.x, s0.x);
-        const s16x4 b2 = decode4_bf16_pow2<0>(cw.y, s0.x), b3 = decode4_bf16_pow2<2>(cw.y, s0.x);
-        const s16x4 b4 = decode4_bf16_pow2<0>(cw.z, s1.x), b5 = decode4_bf16_pow2<2>(cw.z, s1.x);
-        const s16x4 b6 = decode4_bf16_pow2<0>(cw.w, s1.x), b7 = decode4_bf16_pow2<2>(cw.w, s1.x);
+        const s16x4 b0 = decode4_pow2<F16, 0>(cw.x, s0.x), b1 = decode4_pow2<F16, 2>(cw.x, s0.x);
+        const s16x4 b2 = decode4_pow2<F16, 0>(cw.y, s0.x), b3 = decode4_pow2<F16, 2>(cw.y, s0.x);
+        const s16x4 b4 = decode4_pow2<F16, 0>(cw.z, s1.x), b5 = decode4_pow2<F16, 2>(cw.z, s1.x);
+        const s16x4 b6 = decode4_pow2<F16, 0>(cw.w, s1.x), b7 = decode4_pow2<F16, 2>(cw.w, s1.x);
 #pragma unroll
         for (int mg = 0; mg < MG; ++mg) {
             f32x4 p = {0.f, 0.f, 0.f, 0.f};
-            p = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(alo[mg], b0, p, 2, 0, 0);
-            p = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ahi[mg], b1, p, 2, 0, 0);
-            p = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(alo[mg], b2, p, 2, 1, 0);
-            p = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ahi[mg], b3, p, 2, 1, 0);
+            p = mma4<F16, 2, 0>(alo[mg], b0, p);
+            p = mma4<F16, 2, 0>(ahi[mg], b1, p);
+            p = mma4<F16, 2, 1>(alo[mg], b2, p);
+            p = mma4<F16, 2, 1>(ahi[mg], b3, p);
             f32x4 r = {0.f, 0.f, 0.f, 0.f};
-            r = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(alo[mg], b4, r, 2, 2, 0);
-            r = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ahi[mg], b5, r, 2, 2, 0);
-            r = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(alo[mg], b6, r, 2, 3, 0);
-            r = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ahi[mg], b7, r, 2, 3, 0);
+            r = mma4<F16, 2, 2>(alo[mg], b4, r);
+            r = mma4<F16, 2, 2>(ahi[mg], b5, r);
+            r = mma4<F16, 2, 3>(alo[mg], b6, r);
+            r = mma4<F16, 2, 3>(ahi[mg], b7, r);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 acc[j][mg][i] = __builtin_fmaf(s1.y, r[i], __builtin_fmaf(s0.y, p[i], acc[j][mg][i]));
@@ -215,7 +218,7 @@ struct WaveWeights {
 // broadcasts A from block q = t >> 1 of each group of four blocks (cbsz = 2,
 // abid = t >> 1).  On return the wave's partial sums, reduced over its four K
 // groups, are in red_w[row * red_ld + col] for rows < 4 MG, cols < 16 NT.
-template <int MG, int NT, int D, bool KFULL, typename MidF>
+template <int MG, int NT, int D, bool KFULL, bool F16, typename MidF>
 __device__ __forceinline__ void small_m_pass(const uint16_t* __restrict__ xrow0, int64_t ld_x, int rows,
                                              const WaveWeights& ww, int c0, int c1, int K, const float2* lut,
                                              float* red_w, int red_ld, int lane, MidF&& mid,
@@ -246,7 +249,7 @@ __device__ __forceinline__ void small_m_pass(const uint16_t* __restrict__ xrow0,
 #pragma unroll
         for (int mg = 0; mg < MG; ++mg) s.xa[mg] = *reinterpret_cast<const uint4*>(xb + (xoff[mg] + kb));
     };
-    auto use = [&](const SmallSlot<MG, NT>& s, int i) { small_m_chunk<MG, NT, KFULL>(s, kin(c0 + i), lut, lane, acc); };
+    auto use = [&](const SmallSlot<MG, NT>& s, int i) { small_m_chunk<MG, NT, KFULL, F16>(s, kin(c0 + i), lut, lane, acc); };
     run_ring<D, SmallSlot<MG, NT>>(c1 - c0, load, use, mid);
 
     // Sum the four K groups: lanes l, l^16, l^32, l^48 hold the same outputs;
@@ -278,7 +281,7 @@ struct Slot16 {
     uint4 xa[4];
 };
 
-template <int NT, int D, bool KFULL, typename MidF>
+template <int NT, int D, bool KFULL, bool F16, typename MidF>
 __device__ __forceinline__ void small_m_pass16(const uint16_t* __restrict__ xrow0, int64_t ld_x, int rows,
                                                const WaveWeights& ww, int c0, int c1, int K, const float2* lut,
                                                float* red_w, int red_ld, int lane, MidF&& mid) {
@@ -300,11 +303,11 @@ __device__ __forceinline__ void small_m_pass16(const uint16_t* __restrict__ xrow
     };
     auto use = [&](const Slot16<NT>& s, int i) {
         const int c = c0 + i;
-        bf16x8 a[4];
+        uint4 a[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint4 v = s.xa[t];
-            a[t] = uint4_to_bf16x8(kin(c, t) ? v : make_uint4(0u, 0u, 0u, 0u));
+            a[t] = kin(c, t) ? v : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
@@ -313,10 +316,10 @@ __device__ __forceinline__ void small_m_pass16(const uint16_t* __restrict__ xrow
             // the full scale: 2^exponent(conversion operand) times the factor, exact
             const float s0 = __uint_as_float(__float_as_uint(l0.x) & 0x7F800000u) * l0.y;
             const float s1 = __uint_as_float(__float_as_uint(l1.x) & 0x7F800000u) * l1.y;
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], uint4_to_bf16x8(decode8_bf16(s.cw[j].x, s0)), acc[j], 0, 0, 0);
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], uint4_to_bf16x8(decode8_bf16(s.cw[j].y, s0)), acc[j], 0, 0, 0);
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], uint4_to_bf16x8(decode8_bf16(s.cw[j].z, s1)), acc[j], 0, 0, 0);
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], uint4_to_bf16x8(decode8_bf16(s.cw[j].w, s1)), acc[j], 0, 0, 0);
+            acc[j] = mma16<F16>(a[0], decode8<F16>(s.cw[j].x, s0), acc[j]);
+            acc[j] = mma16<F16>(a[1], decode8<F16>(s.cw[j].y, s0), acc[j]);
+            acc[j] = mma16<F16>(a[2], decode8<F16>(s.cw[j].z, s1), acc[j]);
+            acc[j] = mma16<F16>(a[3], decode8<F16>(s.cw[j].w, s1), acc[j]);
         }
     };
     run_ring<D, Slot16<NT>>(c1 - c0, load, use, mid);
@@ -337,7 +340,7 @@ __device__ __forceinline__ void small_m_pass16(const uint16_t* __restrict__ xrow
 // MG == 0: each pass of up to 16 rows picks one or four row groups (grouped).
 // The first weight loads of a wave are issued before the scale table is
 // built, so the table build and its barrier run under the load latency.
-template <int MG, int NT, int W, int D, bool GROUPED, bool KFULL>
+template <int MG, int NT, int W, int D, bool GROUPED, bool KFULL, bool F16 = false>
 __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                          int NU, int KC, int K,
                                                          int N, const float* __restrict__ gscale, int g_is_div,
@@ -391,14 +394,14 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
         const int32_t* rix = GROUPED && row_index ? row_index + row0 + p0 : nullptr;
         const uint16_t* xrow0 = rix ? x : x + (row0 + p0) * ld_x;
         if constexpr (MG == 16) {
-            small_m_pass16<NT, D, KFULL>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane, mid);
+            small_m_pass16<NT, D, KFULL, F16>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane, mid);
         } else if constexpr (MG > 0) {
-            small_m_pass<MG, NT, D, KFULL>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane, mid);
+            small_m_pass<MG, NT, D, KFULL, F16>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane, mid);
         } else {
             if (rows <= 4)
-                small_m_pass<1, NT, D, KFULL>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane, mid, rix);
+                small_m_pass<1, NT, D, KFULL, F16>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane, mid, rix);
             else
-                small_m_pass<4, NT, (D > 2 ? 2 : D), KFULL>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane,
+                small_m_pass<4, NT, (D > 2 ? 2 : D), KFULL, F16>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane,
                                                            mid, rix);
         }
         __syncthreads();
@@ -406,7 +409,7 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
         auto store_y = [&](int t, float acc) {
             const int r = t / RLD, col = t % RLD;
             const int64_t n = (int64_t)u0 * kUnitN + col;
-            if (n < N) y[(row0 + p0 + r) * ld_y + n] = (uint16_t)f32_to_bf16_rne(gv * acc);
+            if (n < N) y[(row0 + p0 + r) * ld_y + n] = (uint16_t)round_out<F16>(gv * acc);
         };
         if (S == 1) {
             for (int t = threadIdx.x; t < rows * RLD; t += W * 64) {

@@ -62,19 +62,28 @@ __device__ __forceinline__ void lds_copy16(uint32_t lds, const uint8_t* base, ui
 // compiler cannot see this hazard-wise: its operands are produced at least
 // one issue group before use, and the accumulators are read only after the
 // drain in mfma_drain.
+template <bool F16>
 __device__ __forceinline__ void mfma_acc(f32x4& acc, const uint4& a, const uint4& b) {
-    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
-        : "+a"(acc)
-        : "v"(__builtin_bit_cast(u32x4v, a)), "v"(__builtin_bit_cast(u32x4v, b)));
+    if constexpr (F16)
+        asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
+            : "+a"(acc)
+            : "v"(__builtin_bit_cast(u32x4v, a)), "v"(__builtin_bit_cast(u32x4v, b)));
+    else
+        asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+            : "+a"(acc)
+            : "v"(__builtin_bit_cast(u32x4v, a)), "v"(__builtin_bit_cast(u32x4v, b)));
 }
 // Wait states after the last MFMA before its accumulators are read (more
 // than the longest MFMA pipeline).
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
-// fp32 pair -> bf16 pair (round to nearest even; NaN stays NaN), first value in the low half.
+// fp32 pair -> bf16 (fp16 with F16) pair, round to nearest even (NaN stays
+// NaN), first value in the low half.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_t));
+template <bool F16>
+__device__ __forceinline__ uint32_t pack_out2(float a, float b) {
+    if constexpr (F16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_t));
 }
 // Exchange rows of 16 lanes between two registers: odd rows of a with even
 // rows of b (lane_swap16), rows 2-3 of a with rows 0-1 of b (lane_swap32).
@@ -119,7 +128,7 @@ __device__ __forceinline__ void mfma_tile(int t, int MT, int NTn, int& mt, int& 
 // Work item p (the workgroup id after the XCD remap below) covers part p % P
 // (P = 16 / MS row parts of 16 MS rows) of tile t0 + p / P of the tile order
 // (whole tiles are 256 rows x 256 columns).
-template <int MS, bool KFULL>
+template <int MS, bool KFULL, bool F16 = false>
 __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                         int NU, int KC, int K, int N, const float* __restrict__ gscale,
                                                         int g_is_div, uint16_t* __restrict__ y, int64_t ld_y, int M,
@@ -281,7 +290,7 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
         } else if (op == 2) {
             jb.y = jb.p.y * sc;
         } else {
-            set_dword(nb[u], e, pack_hi_halves(jb.x, jb.y));
+            set_dword(nb[u], e, pack_exact<F16>(jb.x, jb.y));
         }
     };
     auto scale_op = [&](const BRegs& b, int u) {   // scales of unit u of chunk b
@@ -334,7 +343,7 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
         DwordJob jobs[4];
         static_for<0, NT>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
-            mfma_acc(acc[ms][j], bf[j], af[f % kRing]);
+            mfma_acc<F16>(acc[ms][j], bf[j], af[f % kRing]);
             if constexpr (t < 3) {
                 static_for<d_lo, d_hi>([&](auto dc) {
                     constexpr int d = decltype(dc)::value;
@@ -407,8 +416,8 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
         uint32_t pk[NT][2];   // bf16 pairs of columns 4 g + 2 d, + 1 of unit j (then of unit g: 4 j + 2 d)
         static_for<0, NT>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
-            pk[j][0] = pack_bf16x2(gv * acc[ms][j][0], gv * acc[ms][j][1]);
-            pk[j][1] = pack_bf16x2(gv * acc[ms][j][2], gv * acc[ms][j][3]);
+            pk[j][0] = pack_out2<F16>(gv * acc[ms][j][0], gv * acc[ms][j][1]);
+            pk[j][1] = pack_out2<F16>(gv * acc[ms][j][2], gv * acc[ms][j][3]);
         });
 #pragma unroll
         for (int d = 0; d < 2; ++d) {

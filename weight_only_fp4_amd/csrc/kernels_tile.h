@@ -34,7 +34,7 @@ namespace nvfp4 {
 constexpr int kTileLDA = 136;   // bf16 per LDS row of the activation stage (128 + 8 pad)
 
 
-template <int MS, int NT, int UW, int KW, int D, bool GROUPED, bool KFULL>
+template <int MS, int NT, int UW, int KW, int D, bool GROUPED, bool KFULL, bool F16 = false>
 __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                             int NU, int KC, int K, int N,
                                                             const float* __restrict__ gscale, int g_is_div,
@@ -204,18 +204,17 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            bf16x8 bf[NT];
+            uint4 bf[NT];
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 const uint32_t d = t == 0 ? b.cw[j].x : t == 1 ? b.cw[j].y : t == 2 ? b.cw[j].z : b.cw[j].w;
-                bf[j] = uint4_to_bf16x8(decode8_bf16(d, sc[j][t >> 1]));
+                bf[j] = decode8<F16>(d, sc[j][t >> 1]);
             }
 #pragma unroll
             for (int ms = 0; ms < MS; ++ms) {
-                const bf16x8 af = uint4_to_bf16x8(*reinterpret_cast<const uint4*>(abase + ms * 16 * kTileLDA + t * 8));
+                const uint4 af = *reinterpret_cast<const uint4*>(abase + ms * 16 * kTileLDA + t * 8);
 #pragma unroll
-                for (int j = 0; j < NT; ++j)
-                    acc[ms][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[ms][j], 0, 0, 0);
+                for (int j = 0; j < NT; ++j) acc[ms][j] = mma16<F16>(af, bf[j], acc[ms][j]);
             }
         }
     };
@@ -289,7 +288,7 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int m = ms * 16 + g * 4 + i;
-                    if (m < rows && n < N) y[(row0 + m) * ld_y + n] = (uint16_t)f32_to_bf16_rne(gv * acc[ms][j][i]);
+                    if (m < rows && n < N) y[(row0 + m) * ld_y + n] = (uint16_t)round_out<F16>(gv * acc[ms][j][i]);
                 }
             }
     };

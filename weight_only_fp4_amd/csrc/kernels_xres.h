@@ -16,7 +16,7 @@
 //
 //   Reduction, in a fixed order (bitwise reproducible): wave w + W/2 adds its
 //   tiles into wave w's through LDS, then the W/2 sums are added in wave
-//   order, scaled by the global scale and rounded to bf16.  K is not split
+//   order, scaled by the global scale and rounded to bf16 (fp16 with F16).  K is not split
 //   across workgroups: the device-scope publish / count / reload round trip
 //   of a split measured slower than what it saves here.
 //
@@ -37,7 +37,7 @@ namespace nvfp4 {
 constexpr int kXresRowBytes = 256 + 16;                // one row of a staged chunk, padded
 constexpr int kXresWaveBytes = 16 * kXresRowBytes;     // a wave's staging area
 
-template <int CH, int U, int W, int D, bool FULL>
+template <int CH, int U, int W, int D, bool FULL, bool F16 = false>
 __global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                       int NU, int KC, int K, int N, const float* __restrict__ gscale,
                                                       int g_is_div, uint16_t* __restrict__ y, int64_t ld_y, int rows) {
@@ -136,8 +136,7 @@ __global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint32_t d = t == 0 ? cv.x : t == 1 ? cv.y : t == 2 ? cv.z : cv.w;
-            const bf16x8 bf = uint4_to_bf16x8(decode8_bf16(d, t < 2 ? sc.x : sc.y));
-            acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uint4_to_bf16x8(xr[c][t]), bf, acc[u], 0, 0, 0);
+            acc[u] = mma16<F16>(xr[c][t], decode8<F16>(d, t < 2 ? sc.x : sc.y), acc[u]);
         }
     }
 
@@ -164,7 +163,7 @@ __global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict
 #pragma unroll
         for (int ww = 1; ww < H; ++ww) a += red[ww * TILE + src];
         const int64_t col = (int64_t)(u0 + (o >> 8)) * kUnitN + (o & 15);
-        if (m < rows && col < N) y[(int64_t)m * ld_y + col] = (uint16_t)f32_to_bf16_rne(gv * a);
+        if (m < rows && col < N) y[(int64_t)m * ld_y + col] = (uint16_t)round_out<F16>(gv * a);
     }
 }
 

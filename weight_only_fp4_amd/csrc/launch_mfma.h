@@ -21,9 +21,11 @@ struct MfmaPlan {
 MfmaPlan mfma_plan(const Layout& L, int64_t M);
 
 // Launches Y[M, N] = g * X[M, K] . dequant(W)^T on `st` (dense, E = 1) with
-// the work split of `plan` (at most two kernel launches).  Arguments are
-// checked by the caller; returns the launch status.
+// the work split of `plan` (at most two kernel launches); X and Y are bf16,
+// or fp16 when f16.  Arguments are checked by the caller; returns the launch
+// status.
 hipError_t launch_gemm_mfma(const MfmaPlan& plan, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
-                            const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t M, hipStream_t st);
+                            const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t M, hipStream_t st,
+                            bool f16);
 
 }  // namespace nvfp4

@@ -122,34 +122,41 @@ SmallShape small_m_shape(const Layout& L, int64_t rows, bool grouped) {
 template <int MG, int NT, int W, int D, bool GROUPED>
 void launch_small_t(const SmallShape& s, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
                     const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows, const int32_t* offsets,
-                    SplitK sk, hipStream_t st, const int32_t* row_index = nullptr) {
+                    SplitK sk, hipStream_t st, bool f16, const int32_t* row_index = nullptr) {
     const BlobView bv = make_view(L, blob);
     const dim3 grid((unsigned)s.groups, GROUPED ? (unsigned)L.E : 1u, (unsigned)s.S);
-    if (L.K % kChunkK == 0)
-        hipLaunchKernelGGL((k_gemm_small_m<MG, NT, W, D, GROUPED, true>), grid, dim3(W * 64), 0, st, x, ld_x, bv,
-                           (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, sk, row_index);
-    else
-        hipLaunchKernelGGL((k_gemm_small_m<MG, NT, W, D, GROUPED, false>), grid, dim3(W * 64), 0, st, x, ld_x, bv,
-                           (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, sk, row_index);
+    const bool kfull = L.K % kChunkK == 0;
+#define NVFP4_SMALL_LAUNCH(KF, F16)                                                                              \
+    hipLaunchKernelGGL((k_gemm_small_m<MG, NT, W, D, GROUPED, KF, F16>), grid, dim3(W * 64), 0, st, x, ld_x, bv, \
+                       (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, sk, row_index)
+    if (f16) {
+        if (kfull) NVFP4_SMALL_LAUNCH(true, true);
+        else NVFP4_SMALL_LAUNCH(false, true);
+    } else {
+        if (kfull) NVFP4_SMALL_LAUNCH(true, false);
+        else NVFP4_SMALL_LAUNCH(false, false);
+    }
+#undef NVFP4_SMALL_LAUNCH
 }
 
 template <bool GROUPED>
 nvfp4_status launch_small(const SmallShape& s, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
                           const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows_dense,
-                          const int32_t* offsets, SplitK sk, hipStream_t st, const int32_t* row_index = nullptr) {
+                          const int32_t* offsets, SplitK sk, hipStream_t st, bool f16,
+                          const int32_t* row_index = nullptr) {
     bool done = false;
     if constexpr (GROUPED) {
         switch (s.w) {
-            case 1: launch_small_t<0, 1, 1, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st, row_index); break;
-            case 2: launch_small_t<0, 1, 2, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st, row_index); break;
-            case 4: launch_small_t<0, 1, 4, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st, row_index); break;
-            default: launch_small_t<0, 1, 8, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st, row_index); break;
+            case 1: launch_small_t<0, 1, 1, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st, f16, row_index); break;
+            case 2: launch_small_t<0, 1, 2, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st, f16, row_index); break;
+            case 4: launch_small_t<0, 1, 4, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st, f16, row_index); break;
+            default: launch_small_t<0, 1, 8, 4, true>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, 0, offsets, sk, st, f16, row_index); break;
         }
         done = true;
     } else {
 #define NVFP4_SMALL_DISPATCH(MG, NT, W, D)                                                                        \
     if (!done && s.mg == MG && s.nt == NT && s.w == W && s.d == D) {                                            \
-        launch_small_t<MG, NT, W, D, false>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, rows_dense, nullptr, sk, st); \
+        launch_small_t<MG, NT, W, D, false>(s, L, x, ld_x, blob, gs, g_div, y, ld_y, rows_dense, nullptr, sk, st, f16); \
         done = true;                                                                                            \
     }
         NVFP4_SMALL_CONFIGS(NVFP4_SMALL_DISPATCH)
@@ -242,27 +249,33 @@ SplitK split_k(int S, uint8_t* ws, const Workspace& wl) {
 template <int MS, int NT, int UW, int KW, int D, bool GROUPED>
 void launch_tile_t(const TileShape& t, const Layout& L, const uint16_t* x, int64_t ld_x, BlobView bv, const float* gs,
                    int g_div, uint16_t* y, int64_t ld_y, int64_t rows, const int32_t* offsets, SplitK sk,
-                   hipStream_t st, const int32_t* row_index) {
+                   hipStream_t st, bool f16, const int32_t* row_index) {
     const dim3 grid((unsigned)t.groups, (unsigned)t.mtiles, (unsigned)t.S);
-    if (L.K % kChunkK == 0)
-        hipLaunchKernelGGL((k_gemm_tile<MS, NT, UW, KW, D, GROUPED, true>), grid, dim3(UW * KW * 64), 0, st, x, ld_x,
-                           bv, (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, (int)L.E, sk,
-                           row_index);
-    else
-        hipLaunchKernelGGL((k_gemm_tile<MS, NT, UW, KW, D, GROUPED, false>), grid, dim3(UW * KW * 64), 0, st, x, ld_x,
-                           bv, (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, (int)L.E, sk,
-                           row_index);
+    const bool kfull = L.K % kChunkK == 0;
+#define NVFP4_TILE_LAUNCH(KF, F16)                                                                                 \
+    hipLaunchKernelGGL((k_gemm_tile<MS, NT, UW, KW, D, GROUPED, KF, F16>), grid, dim3(UW * KW * 64), 0, st, x, ld_x, \
+                       bv, (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, rows, offsets, (int)L.E, sk,  \
+                       row_index)
+    if (f16) {
+        if (kfull) NVFP4_TILE_LAUNCH(true, true);
+        else NVFP4_TILE_LAUNCH(false, true);
+    } else {
+        if (kfull) NVFP4_TILE_LAUNCH(true, false);
+        else NVFP4_TILE_LAUNCH(false, false);
+    }
+#undef NVFP4_TILE_LAUNCH
 }
 
 template <bool GROUPED>
 nvfp4_status launch_tile(const TileShape& t, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
                          const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows, const int32_t* offsets,
-                         uint8_t* ws, const Workspace& wl, hipStream_t st, const int32_t* row_index = nullptr) {
+                         uint8_t* ws, const Workspace& wl, hipStream_t st, bool f16,
+                         const int32_t* row_index = nullptr) {
     if (t.mtiles > 65535) return fail(NVFP4_ERR_INVALID_ARG, "tile GEMM: %lld row tiles exceed the grid limit", (long long)t.mtiles);
     const SplitK sk = split_k(t.S, ws, wl);
     const BlobView bv = make_view(L, blob);
 #define NVFP4_TILE(MS, NT, UW, KW, D) \
-    launch_tile_t<MS, NT, UW, KW, D, GROUPED>(t, L, x, ld_x, bv, gs, g_div, y, ld_y, rows, offsets, sk, st, row_index)
+    launch_tile_t<MS, NT, UW, KW, D, GROUPED>(t, L, x, ld_x, bv, gs, g_div, y, ld_y, rows, offsets, sk, st, f16, row_index)
     if constexpr (GROUPED) {
         NVFP4_TILE(4, 4, 4, 1, 2);
     } else {
@@ -323,22 +336,26 @@ bool xres_fits(const Layout& L, int64_t rows) {
 }
 
 nvfp4_status launch_xres(const XresShape& s, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
-                         const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows, hipStream_t st) {
+                         const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows, hipStream_t st,
+                         bool f16) {
     const BlobView bv = make_view(L, blob);
     const dim3 grid((unsigned)s.groups);
     bool done = false;
+#define NVFP4_XRES_LAUNCH(CH, U, W, D, FULL, F16)                                                               \
+    hipLaunchKernelGGL((k_gemm_xres<CH, U, W, D, FULL, F16>), grid, dim3(W * 64), 0, st, x, ld_x, bv, (int)L.NU, \
+                       (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, (int)rows)
 #define NVFP4_XRES_DISPATCH(CH, U, W, D)                                                                          \
     if (!done && s.ch == CH && s.u == U && s.w == W && s.d == D) {                                               \
-        if (L.K == (int64_t)CH * W * kChunkK)                                                                   \
-            hipLaunchKernelGGL((k_gemm_xres<CH, U, W, D, true>), grid, dim3(W * 64), 0, st, x, ld_x, bv,         \
-                               (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, (int)rows);        \
-        else                                                                                                     \
-            hipLaunchKernelGGL((k_gemm_xres<CH, U, W, D, false>), grid, dim3(W * 64), 0, st, x, ld_x, bv,        \
-                               (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, (int)rows);        \
+        const bool full = L.K == (int64_t)CH * W * kChunkK;                                                     \
+        if (f16 && full) NVFP4_XRES_LAUNCH(CH, U, W, D, true, true);                                            \
+        else if (f16) NVFP4_XRES_LAUNCH(CH, U, W, D, false, true);                                              \
+        else if (full) NVFP4_XRES_LAUNCH(CH, U, W, D, true, false);                                             \
+        else NVFP4_XRES_LAUNCH(CH, U, W, D, false, false);                                                      \
         done = true;                                                                                             \
     }
     NVFP4_XRES_CONFIGS(NVFP4_XRES_DISPATCH)
 #undef NVFP4_XRES_DISPATCH
+#undef NVFP4_XRES_LAUNCH
     if (!done) return fail(NVFP4_ERR_INVALID_ARG, "activation-resident GEMM: no compiled kernel for this shape");
     return launched("activation-resident GEMM");
 }
@@ -385,13 +402,18 @@ nvfp4_status check_gemm_io(const char* fn, const void* x, int64_t ld_x, const vo
 // Pre-quant scale: X' = RNE_bf16(X * s) into the workspace; returns the
 // activation the GEMM kernel reads.
 nvfp4_status apply_prescale(const void* x, int64_t& ld_x, const void* pre, int64_t rows, int64_t K, void* ws,
-                            const uint16_t*& xp, hipStream_t st) {
+                            const uint16_t*& xp, hipStream_t st, bool f16) {
     xp = static_cast<const uint16_t*>(x);
     if (!pre) return NVFP4_OK;
     const int64_t threads = rows * (K / 8);
-    hipLaunchKernelGGL(k_prescale, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(x), ld_x, static_cast<const uint16_t*>(pre), rows, K,
-                       static_cast<uint16_t*>(ws), K);
+    if (f16)
+        hipLaunchKernelGGL(k_prescale<true>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const uint16_t*>(x), ld_x, static_cast<const uint16_t*>(pre), rows, K,
+                           static_cast<uint16_t*>(ws), K);
+    else
+        hipLaunchKernelGGL(k_prescale<false>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const uint16_t*>(x), ld_x, static_cast<const uint16_t*>(pre), rows, K,
+                           static_cast<uint16_t*>(ws), K);
     const nvfp4_status s = launched("pre-quant scale");
     if (s != NVFP4_OK) return s;
     xp = static_cast<const uint16_t*>(ws);
@@ -411,8 +433,7 @@ int64_t dense_workspace_bytes(const Layout& L, int64_t M) {
 
 nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void* w, const float* gs, int g_div,
                         void* y, int64_t ld_y, int64_t M, int64_t N, int64_t K, void* ws, int64_t ws_bytes,
-                        int variant, void* stream) {
-    const char* fn = "nvfp4_w4a16_gemm";
+                        int variant, void* stream, const char* fn, bool f16) {
     nvfp4_status s = check_weight_shape(fn, 1, N, K);
     if (s != NVFP4_OK) return s;
     if (variant < kAuto || variant > kResident) return fail(NVFP4_ERR_INVALID_ARG, "%s: unknown variant %d", fn, variant);
@@ -446,19 +467,20 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t* wsb = static_cast<uint8_t*>(ws);
     const uint16_t* xp;
-    s = apply_prescale(x, ld_x, pre, M, K, pre ? wsb + wl.prescale : nullptr, xp, st);
+    s = apply_prescale(x, ld_x, pre, M, K, pre ? wsb + wl.prescale : nullptr, xp, st, f16);
     if (s != NVFP4_OK) return s;
     const uint8_t* blob = static_cast<const uint8_t*>(w);
     uint16_t* yo = static_cast<uint16_t*>(y);
-    if (resident) return launch_xres(xs, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, st);
+    if (resident) return launch_xres(xs, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, st, f16);
     if (small)
-        return launch_small<false>(sm, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, split_k(sm.S, wsb, wl), st);
+        return launch_small<false>(sm, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, split_k(sm.S, wsb, wl), st,
+                                   f16);
     if (mfma) {
-        const hipError_t e = launch_gemm_mfma(mfma_plan(L, M), L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, st);
+        const hipError_t e = launch_gemm_mfma(mfma_plan(L, M), L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, st, f16);
         if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "%s: MFMA GEMM launch failed: %s", fn, hipGetErrorString(e));
         return ok();
     }
-    return launch_tile<false>(t, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, wsb, wl, st);
+    return launch_tile<false>(t, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, wsb, wl, st, f16);
 }
 
 // Grouped GEMM, shared by the plain and the gathering entry points: the
@@ -467,7 +489,8 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
 nvfp4_status grouped_gemm(const char* fn, const void* x, int64_t ld_x, int64_t x_rows, const int32_t* row_index,
                           const int32_t* expert_offsets, const void* pre_scale, const void* w_repacked,
                           const float* global_scales, int global_scale_is_divisor, void* y, int64_t ld_y, int64_t R,
-                          int64_t E, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes, void* stream) {
+                          int64_t E, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes, void* stream,
+                          bool f16) {
     nvfp4_status s = check_weight_shape(fn, E, N, K);
     if (s != NVFP4_OK) return s;
     const Workspace wl = workspace_layout(1, 0, 0, x_rows, K, pre_scale != nullptr);
@@ -482,7 +505,7 @@ nvfp4_status grouped_gemm(const char* fn, const void* x, int64_t ld_x, int64_t x
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t* wsb = static_cast<uint8_t*>(workspace);
     const uint16_t* xp;
-    s = apply_prescale(x, ld_x, pre_scale, x_rows, K, pre_scale ? wsb + wl.prescale : nullptr, xp, st);
+    s = apply_prescale(x, ld_x, pre_scale, x_rows, K, pre_scale ? wsb + wl.prescale : nullptr, xp, st, f16);
     if (s != NVFP4_OK) return s;
     const uint8_t* blob = static_cast<const uint8_t*>(w_repacked);
     uint16_t* yo = static_cast<uint16_t*>(y);
@@ -490,10 +513,10 @@ nvfp4_status grouped_gemm(const char* fn, const void* x, int64_t ld_x, int64_t x
     // Few rows per expert on average: the weight stream dominates, use the small-M kernel (passes of 16 rows).
     if (R <= (int64_t)kSmallRows * E)
         return launch_small<true>(small_m_shape(L, R, true), L, xp, ld_x, blob, global_scales, g_div, yo, ld_y, 0,
-                                  expert_offsets, split_k(1, wsb, wl), st, row_index);
+                                  expert_offsets, split_k(1, wsb, wl), st, f16, row_index);
     const TileShape t = tile_shape(L, R, true);
     return launch_tile<true>(t, L, xp, ld_x, blob, global_scales, g_div, yo, ld_y, R, expert_offsets, wsb, wl, st,
-                             row_index);
+                             f16, row_index);
 }
 
 }  // namespace
@@ -554,7 +577,15 @@ nvfp4_status nvfp4_w4a16_gemm(const void* x, int64_t ld_x, const void* pre_scale
                               int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
                               void* stream) {
     return dense_gemm(x, ld_x, pre_scale, w_repacked, global_scale, global_scale_is_divisor != 0, y, ld_y, M, N, K,
-                      workspace, workspace_bytes, kAuto, stream);
+                      workspace, workspace_bytes, kAuto, stream, "nvfp4_w4a16_gemm", false);
+}
+
+nvfp4_status nvfp4_w4a16_gemm_f16(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
+                                  const float* global_scale, int global_scale_is_divisor, void* y, int64_t ld_y,
+                                  int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                                  void* stream) {
+    return dense_gemm(x, ld_x, pre_scale, w_repacked, global_scale, global_scale_is_divisor != 0, y, ld_y, M, N, K,
+                      workspace, workspace_bytes, kAuto, stream, "nvfp4_w4a16_gemm_f16", true);
 }
 
 nvfp4_status nvfp4_w4a16_gemm_variant(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
@@ -562,7 +593,15 @@ nvfp4_status nvfp4_w4a16_gemm_variant(const void* x, int64_t ld_x, const void* p
                                       int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
                                       int variant, void* stream) {
     return dense_gemm(x, ld_x, pre_scale, w_repacked, global_scale, global_scale_is_divisor != 0, y, ld_y, M, N, K,
-                      workspace, workspace_bytes, variant, stream);
+                      workspace, workspace_bytes, variant, stream, "nvfp4_w4a16_gemm", false);
+}
+
+nvfp4_status nvfp4_w4a16_gemm_variant_f16(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
+                                          const float* global_scale, int global_scale_is_divisor, void* y,
+                                          int64_t ld_y, int64_t M, int64_t N, int64_t K, void* workspace,
+                                          int64_t workspace_bytes, int variant, void* stream) {
+    return dense_gemm(x, ld_x, pre_scale, w_repacked, global_scale, global_scale_is_divisor != 0, y, ld_y, M, N, K,
+                      workspace, workspace_bytes, variant, stream, "nvfp4_w4a16_gemm_f16", true);
 }
 
 int64_t nvfp4_w4a16_grouped_gemm_workspace_bytes(int64_t R, int64_t E, int64_t N, int64_t K) {
@@ -575,7 +614,18 @@ nvfp4_status nvfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t
                                       void* y, int64_t ld_y, int64_t R, int64_t E, int64_t N, int64_t K,
                                       void* workspace, int64_t workspace_bytes, void* stream) {
     return grouped_gemm("nvfp4_w4a16_grouped_gemm", x, ld_x, R, nullptr, expert_offsets, pre_scale, w_repacked,
-                        global_scales, global_scale_is_divisor, y, ld_y, R, E, N, K, workspace, workspace_bytes, stream);
+                        global_scales, global_scale_is_divisor, y, ld_y, R, E, N, K, workspace, workspace_bytes, stream,
+                        false);
+}
+
+nvfp4_status nvfp4_w4a16_grouped_gemm_f16(const void* x, int64_t ld_x, const int32_t* expert_offsets,
+                                          const void* pre_scale, const void* w_repacked, const float* global_scales,
+                                          int global_scale_is_divisor, void* y, int64_t ld_y, int64_t R, int64_t E,
+                                          int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                                          void* stream) {
+    return grouped_gemm("nvfp4_w4a16_grouped_gemm_f16", x, ld_x, R, nullptr, expert_offsets, pre_scale, w_repacked,
+                        global_scales, global_scale_is_divisor, y, ld_y, R, E, N, K, workspace, workspace_bytes, stream,
+                        true);
 }
 
 int64_t nvfp4_w4a16_grouped_gemm_gather_workspace_bytes(int64_t T, int64_t R, int64_t E, int64_t N, int64_t K) {
@@ -599,7 +649,7 @@ nvfp4_status nvfp4_w4a16_grouped_gemm_gather(const void* x, int64_t ld_x, int64_
     if (T * ld_x >= ((int64_t)1 << 31))
         return fail(NVFP4_ERR_INVALID_ARG, "%s: T * ld_x = %lld must stay below 2^31", fn, (long long)(T * ld_x));
     return grouped_gemm(fn, x, ld_x, T, row_token, expert_offsets, pre_scale, w_repacked, global_scales,
-                        global_scale_is_divisor, y, ld_y, R, E, N, K, workspace, workspace_bytes, stream);
+                        global_scale_is_divisor, y, ld_y, R, E, N, K, workspace, workspace_bytes, stream, false);
 }
 
 // ------------------------------------------------------------------ MoE --
