@@ -272,6 +272,23 @@ nvfp4_status nvfp4_w4a16_grouped_gemm_f16(const void* x, int64_t ld_x, const int
                                           int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
                                           void* stream);
 
+/* The MoE glue steps with fp16 activations (the routing is type-free): the
+ * gathering grouped GEMM, the gated SiLU, the squared ReLU and the top-k
+ * combine, each as its bf16 form above with every 16-bit array in IEEE
+ * binary16 and every rounding RNE to fp16 (overflow to +-infinity). */
+nvfp4_status nvfp4_w4a16_grouped_gemm_gather_f16(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
+                                                 const int32_t* expert_offsets, const void* pre_scale,
+                                                 const void* w_repacked, const float* global_scales,
+                                                 int global_scale_is_divisor, void* y, int64_t ld_y, int64_t R,
+                                                 int64_t E, int64_t N, int64_t K, void* workspace,
+                                                 int64_t workspace_bytes, void* stream);
+nvfp4_status nvfp4_moe_silu_mul_f16(const void* h, int64_t ld_h, int64_t R, int64_t I, void* a, int64_t ld_a,
+                                    void* stream);
+nvfp4_status nvfp4_moe_relu2_f16(const void* h, int64_t ld_h, int64_t R, int64_t I, void* a, int64_t ld_a,
+                                 void* stream);
+nvfp4_status nvfp4_moe_combine_f16(const void* y, int64_t ld_y, const int32_t* token_row, const float* topk_weights,
+                                   int64_t T, int64_t k, int64_t H, void* out, int64_t ld_o, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -382,23 +382,32 @@ def moe_route(topk_ids: np.ndarray, E: int):
     return offsets, order // k, token_row
 
 
-def silu_mul(h_bits: np.ndarray) -> np.ndarray:
-    """h bf16 bits [R, 2I] (gate | up) -> silu(gate) * up in fp64, not rounded."""
-    h = bf16_np(h_bits)
+def _act_np(bits: np.ndarray, act: str) -> np.ndarray:
+    if act == "bf16":
+        return bf16_np(bits)
+    if act == "f16":
+        return f16_np(bits)
+    raise ValueError(f"activation type {act!r}")
+
+
+def silu_mul(h_bits: np.ndarray, act: str = "bf16") -> np.ndarray:
+    """h bits [R, 2I] (gate | up; bf16, or fp16 with act='f16') -> silu(gate) * up in fp64, not rounded."""
+    h = _act_np(h_bits, act)
     I = h.shape[1] // 2
     g, u = h[:, :I], h[:, I:]
     return g / (1.0 + np.exp(-g)) * u
 
 
-def relu2(h_bits: np.ndarray) -> np.ndarray:
-    """h bf16 bits [R, I] -> max(h, 0)^2 in fp64, not rounded."""
-    h = bf16_np(h_bits)
+def relu2(h_bits: np.ndarray, act: str = "bf16") -> np.ndarray:
+    """h bits [R, I] (bf16, or fp16 with act='f16') -> max(h, 0)^2 in fp64, not rounded."""
+    h = _act_np(h_bits, act)
     return np.where(h > 0, h, 0.0) ** 2
 
 
-def combine(y_bits: np.ndarray, token_row: np.ndarray, weights: np.ndarray) -> np.ndarray:
-    """y bf16 bits [R, H] in grouped row order, token_row [T*k], weights fp32 [T, k] -> [T, H] fp64, not rounded."""
-    y = bf16_np(y_bits)
+def combine(y_bits: np.ndarray, token_row: np.ndarray, weights: np.ndarray, act: str = "bf16") -> np.ndarray:
+    """y bits [R, H] (bf16, or fp16 with act='f16') in grouped row order, token_row [T*k], weights fp32 [T, k]
+    -> [T, H] fp64, not rounded."""
+    y = _act_np(y_bits, act)
     w = np.asarray(weights, dtype=np.float32).astype(np.float64)
     T, k = w.shape
     rows = np.asarray(token_row, dtype=np.int64).reshape(T, k)

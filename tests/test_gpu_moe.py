@@ -10,7 +10,7 @@ import torch
 import oracle
 import synth
 import weight_only_fp4_amd as nv
-from gpu_util import DEV, bf16_bits, bf16_dev, f32_dev, to_f64, u8_dev
+from gpu_util import DEV, bf16_bits, bf16_dev, bits16, f16_dev, f32_dev, to_f64, u8_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -142,3 +142,37 @@ def test_moe_layer_chain(T):
     accept_or_fail(to_f64(a), oracle.silu_mul(bf16_bits(h)), "silu")
     accept_or_fail(to_f64(y2), oracle.grouped_gemm(bf16_bits(a), r_off, w2, s2, g2), "fc2")
     accept_or_fail(to_f64(out), oracle.combine(bf16_bits(y2), r_tr, wts), "combine")
+
+
+@pytest.mark.parametrize("T", [16, 256])
+def test_moe_layer_chain_f16(T):
+    """The fp16 form of the layer: route -> FC1 (gathered, fp16) -> SiLU -> FC2 -> combine, and the squared ReLU,
+    every stage checked against the oracle's fp16 definition applied to the GPU's own input of that stage."""
+    E, topk, Hd, I = 16, 4, 256, 192
+    g = synth.rng(T + 7)
+    ids = synth.zipf_routing(synth.rng(T + 8), T, E, topk)
+    say(f"moe layer fp16 T={T}")
+    xt = synth.normal_act(g, (T, Hd), "f16")
+    w1, s1 = synth.random_codes(g, (E, 2 * I, Hd)), synth.scales_pow2_mant(g, (E, 2 * I, Hd // 16))
+    w2, s2 = synth.random_codes(g, (E, Hd, I)), synth.scales_pow2_mant(g, (E, Hd, I // 16))
+    g1 = (np.exp2(g.integers(-2, 3, E).astype(np.float64)) / 2688).astype(np.float32)
+    g2 = (np.exp2(g.integers(-2, 3, E).astype(np.float64)) / 2688).astype(np.float32)
+    wts = g.random((T, topk)).astype(np.float32)
+    b1, b2 = nv.repack(u8_dev(w1), u8_dev(s1)), nv.repack(u8_dev(w2), u8_dev(s2))
+
+    off, row_token, token_row = nv.moe_route(i32_dev(ids), E)
+    h = nv.grouped_gemm_gather(f16_dev(xt), row_token, off, b1, E, 2 * I, Hd, f32_dev(g1))
+    a = nv.moe_silu_mul(h)
+    r2 = nv.moe_relu2(h[:, :I])
+    y2 = nv.grouped_gemm(a, off, b2, E, Hd, I, f32_dev(g2))
+    out = nv.moe_combine(y2, token_row, torch.from_numpy(wts).to(DEV))
+    torch.cuda.synchronize()
+    assert h.dtype == a.dtype == r2.dtype == y2.dtype == out.dtype == torch.float16
+
+    r_off, r_rt, r_tr = oracle.moe_route(ids, E)
+    accept_or_fail(to_f64(h), oracle.grouped_gemm_f16(xt[r_rt], r_off, w1, s1, g1), "fc1 f16")
+    accept_or_fail(to_f64(a), oracle.silu_mul(bits16(h), "f16"), "silu f16")
+    accept_or_fail(to_f64(r2), oracle.relu2(bits16(h[:, :I]), "f16"), "relu2 f16")
+    accept_or_fail(to_f64(y2), oracle.grouped_gemm_f16(bits16(a), r_off, w2, s2, g2), "fc2 f16")
+    accept_or_fail(to_f64(out), oracle.combine(bits16(y2), r_tr, wts, "f16"), "combine f16")
+

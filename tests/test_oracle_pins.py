@@ -530,3 +530,19 @@ def test_grouped_gemm_f16_rows_follow_their_expert():
         if b > a:
             ref = oracle.gemm_f16(gc.x[a:b], gc.w[e], gc.s[e], float(gc.g_stored[e]), False, gc.pre)
             assert np.array_equal(got[a:b], ref)
+
+
+def test_moe_glue_f16_decodes_inputs_as_binary16():
+    """The fp16 forms of the MoE elementwise steps: the same definitions on binary16-decoded inputs; closed forms
+    (silu(0) = 0, relu2 of a negative = 0, one-hot combine = the row) checked on fp16 bit patterns."""
+    import struct
+    h = np.array([[0x0000, 0x3C00, 0x4000, 0xBC00]], dtype=np.uint16)   # gate (0, 1) | up (2, -1) in fp16
+    a = oracle.silu_mul(h, "f16")
+    assert a[0, 0] == 0.0 and np.isclose(a[0, 1], (1 / (1 + math.exp(-1))) * -1.0, rtol=1e-15)
+    r = oracle.relu2(np.array([[0xC000, 0x4200]], dtype=np.uint16), "f16")    # -2, 3
+    assert r[0, 0] == 0.0 and r[0, 1] == 9.0
+    y = synth.f16_bits_from_f32(synth.rng(15).standard_normal((4, 8)).astype(np.float32))
+    out = oracle.combine(y, np.array([2, 0], dtype=np.int32), np.array([[1.0, 0.0]], dtype=np.float32), "f16")
+    dec = np.array([struct.unpack("<e", int(b).to_bytes(2, "little"))[0] for b in y[2]])
+    assert np.array_equal(out[0], dec)
+

@@ -76,6 +76,12 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_moe_silu_mul.argtypes, L.nvfp4_moe_silu_mul.restype = [P, I64, I64, I64, P, I64, P], I
         L.nvfp4_moe_combine.argtypes, L.nvfp4_moe_combine.restype = [P, I64, P, P, I64, I64, I64, P, I64, P], I
         L.nvfp4_moe_relu2.argtypes, L.nvfp4_moe_relu2.restype = [P, I64, I64, I64, P, I64, P], I
+        L.nvfp4_moe_silu_mul_f16.argtypes, L.nvfp4_moe_silu_mul_f16.restype = [P, I64, I64, I64, P, I64, P], I
+        L.nvfp4_moe_relu2_f16.argtypes, L.nvfp4_moe_relu2_f16.restype = [P, I64, I64, I64, P, I64, P], I
+        L.nvfp4_moe_combine_f16.argtypes = [P, I64, P, P, I64, I64, I64, P, I64, P]
+        L.nvfp4_moe_combine_f16.restype = I
+        L.nvfp4_w4a16_grouped_gemm_gather_f16.argtypes = L.nvfp4_w4a16_grouped_gemm_gather.argtypes
+        L.nvfp4_w4a16_grouped_gemm_gather_f16.restype = I
         _lib = L
     return _lib
 
@@ -143,6 +149,13 @@ def dequant(blob: torch.Tensor, E: int, N: int, K: int) -> torch.Tensor:
 
 
 _ACT_DTYPES = (torch.bfloat16, torch.float16)
+
+
+def _act_dtype(name, t):
+    """The activation type of tensor t (bf16 or fp16); anything else is an error."""
+    if not isinstance(t, torch.Tensor) or t.dtype not in _ACT_DTYPES:
+        raise ValueError(f"{name} must be a bf16 or fp16 tensor")
+    return t.dtype
 
 
 def _gemm_args(x, blob, N, K, global_scale, pre_scale, out, rows_name="M"):
@@ -250,8 +263,10 @@ def moe_route(topk_ids, E):
 
 def grouped_gemm_gather(x, row_token, expert_offsets, blob, E, N, K, global_scales, divisor=False, pre_scale=None,
                         out=None, workspace_buf=None):
-    """Grouped GEMM whose row r reads token row row_token[r] of x [T, K] (no gathered copy of x is made)."""
-    _dev("x", x, torch.bfloat16, 2)
+    """Grouped GEMM whose row r reads token row row_token[r] of x [T, K] (no gathered copy of x is made); x bf16 or
+    fp16, the output of x's type."""
+    dt = _act_dtype("x", x)
+    _dev("x", x, dt, 2)
     _dev("row_token", row_token, torch.int32, 1)
     _dev("expert_offsets", expert_offsets, torch.int32, 1)
     if expert_offsets.shape[0] != E + 1 or not expert_offsets.is_contiguous() or not row_token.is_contiguous():
@@ -262,11 +277,11 @@ def grouped_gemm_gather(x, row_token, expert_offsets, blob, E, N, K, global_scal
     if x.shape[1] != K:
         raise ValueError(f"x must be [T, {K}]")
     if pre_scale is not None:
-        _dev("pre_scale", pre_scale, torch.bfloat16, 1)
+        _dev("pre_scale", pre_scale, dt, 1)
     if out is None:
-        out = torch.zeros((R, N), dtype=torch.bfloat16, device=x.device)
+        out = torch.zeros((R, N), dtype=dt, device=x.device)
     else:
-        _dev("out", out, torch.bfloat16, 2)
+        _dev("out", out, dt, 2)
         if tuple(out.shape) != (R, N):
             raise ValueError(f"out must be [{R}, {N}]")
     need = int(lib().nvfp4_w4a16_grouped_gemm_gather_workspace_bytes(T, R, E, N, K))
@@ -274,43 +289,49 @@ def grouped_gemm_gather(x, row_token, expert_offsets, blob, E, N, K, global_scal
         raise ValueError(f"invalid grouped GEMM shape T={T} R={R} E={E} N={N} K={K}")
     if workspace_buf is None:
         workspace_buf = workspace(need, x.device)
-    _check(lib().nvfp4_w4a16_grouped_gemm_gather(_ptr(x), x.stride(0), T, _ptr(row_token), _ptr(expert_offsets),
-                                                 _ptr(pre_scale), _ptr(blob), _ptr(global_scales),
-                                                 int(bool(divisor)), _ptr(out), out.stride(0), R, E, N, K,
-                                                 _ptr(workspace_buf), workspace_buf.numel(), _stream(x.device)))
+    fn = lib().nvfp4_w4a16_grouped_gemm_gather_f16 if dt == torch.float16 else lib().nvfp4_w4a16_grouped_gemm_gather
+    _check(fn(_ptr(x), x.stride(0), T, _ptr(row_token), _ptr(expert_offsets), _ptr(pre_scale), _ptr(blob),
+              _ptr(global_scales), int(bool(divisor)), _ptr(out), out.stride(0), R, E, N, K, _ptr(workspace_buf),
+              workspace_buf.numel(), _stream(x.device)))
     return out
 
 
 def moe_silu_mul(h, out=None):
-    """h bf16 [R, 2I] (gate | up) -> silu(gate) * up, bf16 [R, I]."""
-    _dev("h", h, torch.bfloat16, 2)
+    """h [R, 2I] (gate | up) -> silu(gate) * up [R, I], bf16 or fp16 (h's type)."""
+    dt = _act_dtype("h", h)
+    _dev("h", h, dt, 2)
     R, I2 = h.shape
     if I2 % 2:
         raise ValueError("h must have an even number of columns (gate | up)")
     I = I2 // 2
     if out is None:
-        out = torch.empty((R, I), dtype=torch.bfloat16, device=h.device)
+        out = torch.empty((R, I), dtype=dt, device=h.device)
     else:
-        _dev("out", out, torch.bfloat16, 2)
-    _check(lib().nvfp4_moe_silu_mul(_ptr(h), h.stride(0), R, I, _ptr(out), out.stride(0), _stream(h.device)))
+        _dev("out", out, dt, 2)
+    fn = lib().nvfp4_moe_silu_mul_f16 if dt == torch.float16 else lib().nvfp4_moe_silu_mul
+    _check(fn(_ptr(h), h.stride(0), R, I, _ptr(out), out.stride(0), _stream(h.device)))
     return out
 
 
 def moe_relu2(h, out=None):
-    """h bf16 [R, I] -> max(h, 0)^2, bf16 [R, I] (non-gated experts)."""
-    _dev("h", h, torch.bfloat16, 2)
+    """h [R, I] -> max(h, 0)^2 [R, I] (non-gated experts), bf16 or fp16 (h's type)."""
+    dt = _act_dtype("h", h)
+    _dev("h", h, dt, 2)
     R, I = h.shape
     if out is None:
-        out = torch.empty((R, I), dtype=torch.bfloat16, device=h.device)
+        out = torch.empty((R, I), dtype=dt, device=h.device)
     else:
-        _dev("out", out, torch.bfloat16, 2)
-    _check(lib().nvfp4_moe_relu2(_ptr(h), h.stride(0), R, I, _ptr(out), out.stride(0), _stream(h.device)))
+        _dev("out", out, dt, 2)
+    fn = lib().nvfp4_moe_relu2_f16 if dt == torch.float16 else lib().nvfp4_moe_relu2
+    _check(fn(_ptr(h), h.stride(0), R, I, _ptr(out), out.stride(0), _stream(h.device)))
     return out
 
 
 def moe_combine(y, token_row, topk_weights, out=None):
-    """y bf16 [R, H] in grouped row order, token_row int32 [T*k], topk_weights fp32 [T, k] -> bf16 [T, H]."""
-    _dev("y", y, torch.bfloat16, 2)
+    """y [R, H] in grouped row order, token_row int32 [T*k], topk_weights fp32 [T, k] -> [T, H]; y and the output
+    bf16 or fp16 (y's type)."""
+    dt = _act_dtype("y", y)
+    _dev("y", y, dt, 2)
     _dev("token_row", token_row, torch.int32, 1)
     _dev("topk_weights", topk_weights, torch.float32, 2)
     if not topk_weights.is_contiguous() or not token_row.is_contiguous():
@@ -318,9 +339,10 @@ def moe_combine(y, token_row, topk_weights, out=None):
     T, k = topk_weights.shape
     H = y.shape[1]
     if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+        out = torch.empty((T, H), dtype=dt, device=y.device)
     else:
-        _dev("out", out, torch.bfloat16, 2)
-    _check(lib().nvfp4_moe_combine(_ptr(y), y.stride(0), _ptr(token_row), _ptr(topk_weights), T, k, H, _ptr(out),
-                                   out.stride(0), _stream(y.device)))
+        _dev("out", out, dt, 2)
+    fn = lib().nvfp4_moe_combine_f16 if dt == torch.float16 else lib().nvfp4_moe_combine
+    _check(fn(_ptr(y), y.stride(0), _ptr(token_row), _ptr(topk_weights), T, k, H, _ptr(out), out.stride(0),
+              _stream(y.device)))
     return out

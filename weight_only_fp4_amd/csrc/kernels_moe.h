@@ -161,18 +161,21 @@ __global__ void __launch_bounds__(kRouteThreads) k_moe_route_place(const int32_t
     }
 }
 
+// The elementwise steps take bf16, or fp16 with F16 (inputs and output).
+//
 // Gated SiLU: a[r, i] = RNE_bf16(silu(gate) * up) with gate = h[r, i] and
 // up = h[r, I + i], silu(v) = v / (1 + e^-v), in fp32.  Thread: 8 columns,
 // moved with 16-byte loads and stores when VEC (the host checks that every
 // row start and I keep 16-byte alignment).
+template <bool F16>
 __device__ __forceinline__ uint32_t silu_mul_pair(uint32_t g2, uint32_t u2) {
-    const float g0 = bf16_to_f32(g2 & 0xFFFFu), g1 = bf16_to_f32(g2 >> 16);
-    const float u0 = bf16_to_f32(u2 & 0xFFFFu), u1 = bf16_to_f32(u2 >> 16);
+    const float g0 = act_to_f32<F16>(g2 & 0xFFFFu), g1 = act_to_f32<F16>(g2 >> 16);
+    const float u0 = act_to_f32<F16>(u2 & 0xFFFFu), u1 = act_to_f32<F16>(u2 >> 16);
     const float a0 = g0 / (1.0f + expf(-g0)) * u0, a1 = g1 / (1.0f + expf(-g1)) * u1;
-    return f32_to_bf16_rne(a0) | (f32_to_bf16_rne(a1) << 16);
+    return round_out<F16>(a0) | (round_out<F16>(a1) << 16);
 }
 
-template <bool VEC>
+template <bool VEC, bool F16 = false>
 __global__ void k_moe_silu_mul(const uint16_t* __restrict__ h, int64_t ld_h, int64_t R, int64_t I,
                                uint16_t* __restrict__ a, int64_t ld_a) {
     const int64_t per_row = (I + 7) / 8;
@@ -184,21 +187,23 @@ __global__ void k_moe_silu_mul(const uint16_t* __restrict__ h, int64_t ld_h, int
     if (VEC && i0 + 8 <= I) {
         const uint4 g = *reinterpret_cast<const uint4*>(hr + i0), u = *reinterpret_cast<const uint4*>(hr + I + i0);
         *reinterpret_cast<uint4*>(ar + i0) =
-            make_uint4(silu_mul_pair(g.x, u.x), silu_mul_pair(g.y, u.y), silu_mul_pair(g.z, u.z), silu_mul_pair(g.w, u.w));
+            make_uint4(silu_mul_pair<F16>(g.x, u.x), silu_mul_pair<F16>(g.y, u.y), silu_mul_pair<F16>(g.z, u.z),
+                       silu_mul_pair<F16>(g.w, u.w));
         return;
     }
     for (int e = 0; e < 8 && i0 + e < I; ++e)
-        ar[i0 + e] = (uint16_t)(silu_mul_pair(hr[i0 + e], hr[I + i0 + e]) & 0xFFFFu);
+        ar[i0 + e] = (uint16_t)(silu_mul_pair<F16>(hr[i0 + e], hr[I + i0 + e]) & 0xFFFFu);
 }
 
 // Non-gated squared ReLU: a[r, i] = RNE_bf16(max(h[r, i], 0)^2) in fp32.
 // Thread: 8 columns, 16-byte loads and stores when VEC.
+template <bool F16>
 __device__ __forceinline__ uint32_t relu2_pair(uint32_t h2) {
-    const float a0 = fmaxf(bf16_to_f32(h2 & 0xFFFFu), 0.0f), a1 = fmaxf(bf16_to_f32(h2 >> 16), 0.0f);
-    return f32_to_bf16_rne(a0 * a0) | (f32_to_bf16_rne(a1 * a1) << 16);
+    const float a0 = fmaxf(act_to_f32<F16>(h2 & 0xFFFFu), 0.0f), a1 = fmaxf(act_to_f32<F16>(h2 >> 16), 0.0f);
+    return round_out<F16>(a0 * a0) | (round_out<F16>(a1 * a1) << 16);
 }
 
-template <bool VEC>
+template <bool VEC, bool F16 = false>
 __global__ void k_moe_relu2(const uint16_t* __restrict__ h, int64_t ld_h, int64_t R, int64_t I,
                             uint16_t* __restrict__ a, int64_t ld_a) {
     const int64_t per_row = (I + 7) / 8;
@@ -209,16 +214,17 @@ __global__ void k_moe_relu2(const uint16_t* __restrict__ h, int64_t ld_h, int64_
     uint16_t* ar = a + r * ld_a;
     if (VEC && i0 + 8 <= I) {
         const uint4 v = *reinterpret_cast<const uint4*>(hr + i0);
-        *reinterpret_cast<uint4*>(ar + i0) = make_uint4(relu2_pair(v.x), relu2_pair(v.y), relu2_pair(v.z), relu2_pair(v.w));
+        *reinterpret_cast<uint4*>(ar + i0) =
+            make_uint4(relu2_pair<F16>(v.x), relu2_pair<F16>(v.y), relu2_pair<F16>(v.z), relu2_pair<F16>(v.w));
         return;
     }
-    for (int e = 0; e < 8 && i0 + e < I; ++e) ar[i0 + e] = (uint16_t)(relu2_pair(hr[i0 + e]) & 0xFFFFu);
+    for (int e = 0; e < 8 && i0 + e < I; ++e) ar[i0 + e] = (uint16_t)(relu2_pair<F16>(hr[i0 + e]) & 0xFFFFu);
 }
 
 // Top-k weighted combine: out[t, c] = RNE_bf16(sum_j wt[t, j] * y[token_row[t k + j], c]),
 // summed in fp32 in slot order j = 0 .. k - 1.  Thread: 8 columns, 16-byte
 // loads and stores when VEC.
-template <bool VEC>
+template <bool VEC, bool F16 = false>
 __global__ void k_moe_combine(const uint16_t* __restrict__ y, int64_t ld_y, const int32_t* __restrict__ token_row,
                               const float* __restrict__ wt, int64_t T, int k, int64_t H, uint16_t* __restrict__ out,
                               int64_t ld_o) {
@@ -236,26 +242,26 @@ __global__ void k_moe_combine(const uint16_t* __restrict__ y, int64_t ld_y, cons
             const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc[2 * e] = __builtin_fmaf(wj, bf16_to_f32(d[e] & 0xFFFFu), acc[2 * e]);
-                acc[2 * e + 1] = __builtin_fmaf(wj, bf16_to_f32(d[e] >> 16), acc[2 * e + 1]);
+                acc[2 * e] = __builtin_fmaf(wj, act_to_f32<F16>(d[e] & 0xFFFFu), acc[2 * e]);
+                acc[2 * e + 1] = __builtin_fmaf(wj, act_to_f32<F16>(d[e] >> 16), acc[2 * e + 1]);
             }
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                if (c0 + e < H) acc[e] = __builtin_fmaf(wj, bf16_to_f32(yr[e]), acc[e]);
+                if (c0 + e < H) acc[e] = __builtin_fmaf(wj, act_to_f32<F16>(yr[e]), acc[e]);
         }
     }
     uint16_t* orow = out + t * ld_o + c0;
     if (full) {
         uint32_t p[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = f32_to_bf16_rne(acc[2 * e]) | (f32_to_bf16_rne(acc[2 * e + 1]) << 16);
+        for (int e = 0; e < 4; ++e) p[e] = round_out<F16>(acc[2 * e]) | (round_out<F16>(acc[2 * e + 1]) << 16);
         *reinterpret_cast<uint4*>(orow) = make_uint4(p[0], p[1], p[2], p[3]);
         return;
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-        if (c0 + e < H) orow[e] = (uint16_t)f32_to_bf16_rne(acc[e]);
+        if (c0 + e < H) orow[e] = (uint16_t)round_out<F16>(acc[e]);
 }
 
 }  // namespace nvfp4

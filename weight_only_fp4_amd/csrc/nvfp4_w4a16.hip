@@ -519,6 +519,69 @@ nvfp4_status grouped_gemm(const char* fn, const void* x, int64_t ld_x, int64_t x
                              f16, row_index);
 }
 
+// ---- MoE elementwise steps (bf16, or fp16 when f16)
+
+nvfp4_status moe_silu_mul(const char* fn, const void* h, int64_t ld_h, int64_t R, int64_t I, void* a, int64_t ld_a,
+                          void* stream, bool f16) {
+    if (R < 0 || I < 1) return fail(NVFP4_ERR_INVALID_ARG, "%s: R = %lld, I = %lld", fn, (long long)R, (long long)I);
+    if (ld_h < 2 * I) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_h = %lld < 2 I = %lld", fn, (long long)ld_h, (long long)(2 * I));
+    if (ld_a < I) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_a = %lld < I = %lld", fn, (long long)ld_a, (long long)I);
+    if (R > 0 && (!h || !a)) return fail(NVFP4_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(h, 2) || !aligned(a, 2)) return fail(NVFP4_ERR_ALIGNMENT, "%s: 16-bit arrays must be 2-byte aligned", fn);
+    if (R == 0) return ok();
+    const int64_t threads = R * ((I + 7) / 8);
+    const bool vec = ld_h % 8 == 0 && I % 8 == 0 && ld_a % 8 == 0 && aligned(h, 16) && aligned(a, 16);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (vec && f16) hipLaunchKernelGGL((k_moe_silu_mul<true, true>), grid, dim3(256), 0, st, static_cast<const uint16_t*>(h), ld_h, R, I, static_cast<uint16_t*>(a), ld_a);
+    else if (vec) hipLaunchKernelGGL((k_moe_silu_mul<true, false>), grid, dim3(256), 0, st, static_cast<const uint16_t*>(h), ld_h, R, I, static_cast<uint16_t*>(a), ld_a);
+    else if (f16) hipLaunchKernelGGL((k_moe_silu_mul<false, true>), grid, dim3(256), 0, st, static_cast<const uint16_t*>(h), ld_h, R, I, static_cast<uint16_t*>(a), ld_a);
+    else hipLaunchKernelGGL((k_moe_silu_mul<false, false>), grid, dim3(256), 0, st, static_cast<const uint16_t*>(h), ld_h, R, I, static_cast<uint16_t*>(a), ld_a);
+    return launched(fn);
+}
+
+nvfp4_status moe_relu2(const char* fn, const void* h, int64_t ld_h, int64_t R, int64_t I, void* a, int64_t ld_a,
+                       void* stream, bool f16) {
+    if (R < 0 || I < 1) return fail(NVFP4_ERR_INVALID_ARG, "%s: R = %lld, I = %lld", fn, (long long)R, (long long)I);
+    if (ld_h < I) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_h = %lld < I = %lld", fn, (long long)ld_h, (long long)I);
+    if (ld_a < I) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_a = %lld < I = %lld", fn, (long long)ld_a, (long long)I);
+    if (R > 0 && (!h || !a)) return fail(NVFP4_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(h, 2) || !aligned(a, 2)) return fail(NVFP4_ERR_ALIGNMENT, "%s: 16-bit arrays must be 2-byte aligned", fn);
+    if (R == 0) return ok();
+    const int64_t threads = R * ((I + 7) / 8);
+    const bool vec = ld_h % 8 == 0 && ld_a % 8 == 0 && aligned(h, 16) && aligned(a, 16);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (vec && f16) hipLaunchKernelGGL((k_moe_relu2<true, true>), grid, dim3(256), 0, st, static_cast<const uint16_t*>(h), ld_h, R, I, static_cast<uint16_t*>(a), ld_a);
+    else if (vec) hipLaunchKernelGGL((k_moe_relu2<true, false>), grid, dim3(256), 0, st, static_cast<const uint16_t*>(h), ld_h, R, I, static_cast<uint16_t*>(a), ld_a);
+    else if (f16) hipLaunchKernelGGL((k_moe_relu2<false, true>), grid, dim3(256), 0, st, static_cast<const uint16_t*>(h), ld_h, R, I, static_cast<uint16_t*>(a), ld_a);
+    else hipLaunchKernelGGL((k_moe_relu2<false, false>), grid, dim3(256), 0, st, static_cast<const uint16_t*>(h), ld_h, R, I, static_cast<uint16_t*>(a), ld_a);
+    return launched(fn);
+}
+
+nvfp4_status moe_combine(const char* fn, const void* y, int64_t ld_y, const int32_t* token_row,
+                         const float* topk_weights, int64_t T, int64_t k, int64_t H, void* out, int64_t ld_o,
+                         void* stream, bool f16) {
+    if (T < 0 || k < 1 || H < 1)
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: T = %lld, k = %lld, H = %lld", fn, (long long)T, (long long)k, (long long)H);
+    if (ld_y < H || ld_o < H) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_y and ld_o must be >= H", fn);
+    if (T > 0 && (!y || !token_row || !topk_weights || !out)) return fail(NVFP4_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(y, 2) || !aligned(out, 2) || !aligned(token_row, 4) || !aligned(topk_weights, 4))
+        return fail(NVFP4_ERR_ALIGNMENT, "%s: misaligned pointer", fn);
+    if (T == 0) return ok();
+    const int64_t threads = T * ((H + 7) / 8);
+    const bool vec = ld_y % 8 == 0 && ld_o % 8 == 0 && aligned(y, 16) && aligned(out, 16);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint16_t* yy = static_cast<const uint16_t*>(y);
+    uint16_t* oo = static_cast<uint16_t*>(out);
+    if (vec && f16) hipLaunchKernelGGL((k_moe_combine<true, true>), grid, dim3(256), 0, st, yy, ld_y, token_row, topk_weights, T, (int)k, H, oo, ld_o);
+    else if (vec) hipLaunchKernelGGL((k_moe_combine<true, false>), grid, dim3(256), 0, st, yy, ld_y, token_row, topk_weights, T, (int)k, H, oo, ld_o);
+    else if (f16) hipLaunchKernelGGL((k_moe_combine<false, true>), grid, dim3(256), 0, st, yy, ld_y, token_row, topk_weights, T, (int)k, H, oo, ld_o);
+    else hipLaunchKernelGGL((k_moe_combine<false, false>), grid, dim3(256), 0, st, yy, ld_y, token_row, topk_weights, T, (int)k, H, oo, ld_o);
+    return launched(fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -634,13 +697,12 @@ int64_t nvfp4_w4a16_grouped_gemm_gather_workspace_bytes(int64_t T, int64_t R, in
     return workspace_layout(1, 0, 0, T, K, true).total;   // the pre-scaled token rows
 }
 
-nvfp4_status nvfp4_w4a16_grouped_gemm_gather(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
-                                             const int32_t* expert_offsets, const void* pre_scale,
-                                             const void* w_repacked, const float* global_scales,
-                                             int global_scale_is_divisor, void* y, int64_t ld_y, int64_t R,
-                                             int64_t E, int64_t N, int64_t K, void* workspace,
-                                             int64_t workspace_bytes, void* stream) {
-    const char* fn = "nvfp4_w4a16_grouped_gemm_gather";
+static nvfp4_status grouped_gemm_gather(const char* fn, const void* x, int64_t ld_x, int64_t T,
+                                        const int32_t* row_token, const int32_t* expert_offsets,
+                                        const void* pre_scale, const void* w_repacked, const float* global_scales,
+                                        int global_scale_is_divisor, void* y, int64_t ld_y, int64_t R, int64_t E,
+                                        int64_t N, int64_t K, void* workspace, int64_t workspace_bytes, void* stream,
+                                        bool f16) {
     if (T < 0) return fail(NVFP4_ERR_INVALID_ARG, "%s: token count %lld is negative", fn, (long long)T);
     if (R > 0 && !row_token) return fail(NVFP4_ERR_INVALID_ARG, "%s: row_token is NULL", fn);
     if (!aligned(row_token, 4)) return fail(NVFP4_ERR_ALIGNMENT, "%s: row_token must be 4-byte aligned", fn);
@@ -649,7 +711,29 @@ nvfp4_status nvfp4_w4a16_grouped_gemm_gather(const void* x, int64_t ld_x, int64_
     if (T * ld_x >= ((int64_t)1 << 31))
         return fail(NVFP4_ERR_INVALID_ARG, "%s: T * ld_x = %lld must stay below 2^31", fn, (long long)(T * ld_x));
     return grouped_gemm(fn, x, ld_x, T, row_token, expert_offsets, pre_scale, w_repacked, global_scales,
-                        global_scale_is_divisor, y, ld_y, R, E, N, K, workspace, workspace_bytes, stream, false);
+                        global_scale_is_divisor, y, ld_y, R, E, N, K, workspace, workspace_bytes, stream, f16);
+}
+
+nvfp4_status nvfp4_w4a16_grouped_gemm_gather(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
+                                             const int32_t* expert_offsets, const void* pre_scale,
+                                             const void* w_repacked, const float* global_scales,
+                                             int global_scale_is_divisor, void* y, int64_t ld_y, int64_t R,
+                                             int64_t E, int64_t N, int64_t K, void* workspace,
+                                             int64_t workspace_bytes, void* stream) {
+    return grouped_gemm_gather("nvfp4_w4a16_grouped_gemm_gather", x, ld_x, T, row_token, expert_offsets, pre_scale,
+                               w_repacked, global_scales, global_scale_is_divisor, y, ld_y, R, E, N, K, workspace,
+                               workspace_bytes, stream, false);
+}
+
+nvfp4_status nvfp4_w4a16_grouped_gemm_gather_f16(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
+                                                 const int32_t* expert_offsets, const void* pre_scale,
+                                                 const void* w_repacked, const float* global_scales,
+                                                 int global_scale_is_divisor, void* y, int64_t ld_y, int64_t R,
+                                                 int64_t E, int64_t N, int64_t K, void* workspace,
+                                                 int64_t workspace_bytes, void* stream) {
+    return grouped_gemm_gather("nvfp4_w4a16_grouped_gemm_gather_f16", x, ld_x, T, row_token, expert_offsets,
+                               pre_scale, w_repacked, global_scales, global_scale_is_divisor, y, ld_y, R, E, N, K,
+                               workspace, workspace_bytes, stream, true);
 }
 
 // ------------------------------------------------------------------ MoE --
@@ -697,68 +781,32 @@ nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int64_t k, int6
 
 nvfp4_status nvfp4_moe_silu_mul(const void* h, int64_t ld_h, int64_t R, int64_t I, void* a, int64_t ld_a,
                                 void* stream) {
-    const char* fn = "nvfp4_moe_silu_mul";
-    if (R < 0 || I < 1) return fail(NVFP4_ERR_INVALID_ARG, "%s: R = %lld, I = %lld", fn, (long long)R, (long long)I);
-    if (ld_h < 2 * I) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_h = %lld < 2 I = %lld", fn, (long long)ld_h, (long long)(2 * I));
-    if (ld_a < I) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_a = %lld < I = %lld", fn, (long long)ld_a, (long long)I);
-    if (R > 0 && (!h || !a)) return fail(NVFP4_ERR_INVALID_ARG, "%s: NULL pointer", fn);
-    if (!aligned(h, 2) || !aligned(a, 2)) return fail(NVFP4_ERR_ALIGNMENT, "%s: bf16 arrays must be 2-byte aligned", fn);
-    if (R == 0) return ok();
-    const int64_t threads = R * ((I + 7) / 8);
-    const bool vec = ld_h % 8 == 0 && I % 8 == 0 && ld_a % 8 == 0 && aligned(h, 16) && aligned(a, 16);
-    const dim3 grid((unsigned)((threads + 255) / 256));
-    if (vec)
-        hipLaunchKernelGGL(k_moe_silu_mul<true>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
-                           static_cast<const uint16_t*>(h), ld_h, R, I, static_cast<uint16_t*>(a), ld_a);
-    else
-        hipLaunchKernelGGL(k_moe_silu_mul<false>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
-                           static_cast<const uint16_t*>(h), ld_h, R, I, static_cast<uint16_t*>(a), ld_a);
-    return launched(fn);
+    return moe_silu_mul("nvfp4_moe_silu_mul", h, ld_h, R, I, a, ld_a, stream, false);
+}
+
+nvfp4_status nvfp4_moe_silu_mul_f16(const void* h, int64_t ld_h, int64_t R, int64_t I, void* a, int64_t ld_a,
+                                    void* stream) {
+    return moe_silu_mul("nvfp4_moe_silu_mul_f16", h, ld_h, R, I, a, ld_a, stream, true);
 }
 
 nvfp4_status nvfp4_moe_relu2(const void* h, int64_t ld_h, int64_t R, int64_t I, void* a, int64_t ld_a,
                              void* stream) {
-    const char* fn = "nvfp4_moe_relu2";
-    if (R < 0 || I < 1) return fail(NVFP4_ERR_INVALID_ARG, "%s: R = %lld, I = %lld", fn, (long long)R, (long long)I);
-    if (ld_h < I) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_h = %lld < I = %lld", fn, (long long)ld_h, (long long)I);
-    if (ld_a < I) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_a = %lld < I = %lld", fn, (long long)ld_a, (long long)I);
-    if (R > 0 && (!h || !a)) return fail(NVFP4_ERR_INVALID_ARG, "%s: NULL pointer", fn);
-    if (!aligned(h, 2) || !aligned(a, 2)) return fail(NVFP4_ERR_ALIGNMENT, "%s: bf16 arrays must be 2-byte aligned", fn);
-    if (R == 0) return ok();
-    const int64_t threads = R * ((I + 7) / 8);
-    const bool vec = ld_h % 8 == 0 && ld_a % 8 == 0 && aligned(h, 16) && aligned(a, 16);
-    const dim3 grid((unsigned)((threads + 255) / 256));
-    if (vec)
-        hipLaunchKernelGGL(k_moe_relu2<true>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
-                           static_cast<const uint16_t*>(h), ld_h, R, I, static_cast<uint16_t*>(a), ld_a);
-    else
-        hipLaunchKernelGGL(k_moe_relu2<false>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
-                           static_cast<const uint16_t*>(h), ld_h, R, I, static_cast<uint16_t*>(a), ld_a);
-    return launched(fn);
+    return moe_relu2("nvfp4_moe_relu2", h, ld_h, R, I, a, ld_a, stream, false);
+}
+
+nvfp4_status nvfp4_moe_relu2_f16(const void* h, int64_t ld_h, int64_t R, int64_t I, void* a, int64_t ld_a,
+                                 void* stream) {
+    return moe_relu2("nvfp4_moe_relu2_f16", h, ld_h, R, I, a, ld_a, stream, true);
 }
 
 nvfp4_status nvfp4_moe_combine(const void* y, int64_t ld_y, const int32_t* token_row, const float* topk_weights,
                                int64_t T, int64_t k, int64_t H, void* out, int64_t ld_o, void* stream) {
-    const char* fn = "nvfp4_moe_combine";
-    if (T < 0 || k < 1 || H < 1)
-        return fail(NVFP4_ERR_INVALID_ARG, "%s: T = %lld, k = %lld, H = %lld", fn, (long long)T, (long long)k, (long long)H);
-    if (ld_y < H || ld_o < H) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_y and ld_o must be >= H", fn);
-    if (T > 0 && (!y || !token_row || !topk_weights || !out)) return fail(NVFP4_ERR_INVALID_ARG, "%s: NULL pointer", fn);
-    if (!aligned(y, 2) || !aligned(out, 2) || !aligned(token_row, 4) || !aligned(topk_weights, 4))
-        return fail(NVFP4_ERR_ALIGNMENT, "%s: misaligned pointer", fn);
-    if (T == 0) return ok();
-    const int64_t threads = T * ((H + 7) / 8);
-    const bool vec = ld_y % 8 == 0 && ld_o % 8 == 0 && aligned(y, 16) && aligned(out, 16);
-    const dim3 grid((unsigned)((threads + 255) / 256));
-    if (vec)
-        hipLaunchKernelGGL(k_moe_combine<true>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
-                           static_cast<const uint16_t*>(y), ld_y, token_row, topk_weights, T, (int)k, H,
-                           static_cast<uint16_t*>(out), ld_o);
-    else
-        hipLaunchKernelGGL(k_moe_combine<false>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
-                           static_cast<const uint16_t*>(y), ld_y, token_row, topk_weights, T, (int)k, H,
-                           static_cast<uint16_t*>(out), ld_o);
-    return launched(fn);
+    return moe_combine("nvfp4_moe_combine", y, ld_y, token_row, topk_weights, T, k, H, out, ld_o, stream, false);
+}
+
+nvfp4_status nvfp4_moe_combine_f16(const void* y, int64_t ld_y, const int32_t* token_row, const float* topk_weights,
+                                   int64_t T, int64_t k, int64_t H, void* out, int64_t ld_o, void* stream) {
+    return moe_combine("nvfp4_moe_combine_f16", y, ld_y, token_row, topk_weights, T, k, H, out, ld_o, stream, true);
 }
 
 }  // extern "C"
