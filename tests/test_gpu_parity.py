@@ -389,6 +389,20 @@ def test_largest_activation_stride():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("variant", [nv.VARIANT_SMALL_M, nv.VARIANT_RESIDENT])
+def test_largest_activation_stride_small_rows(variant):
+    """ld_x at its limit (2^23 elements) for the kernels of up to 16 rows."""
+    c = synth.dense_case(16, 272, 256, seed=79)
+    say(f"ld_x = 2^23 small rows variant {variant}")
+    d = DenseDev(c)
+    big = torch.empty((c.M, 1 << 23), dtype=torch.bfloat16, device=DEV)
+    big[:, :c.K] = d.x
+    accept_or_fail(to_f64(d.run(variant, x=big[:, :c.K])), oracle.gemm(c.x, c.w, c.s, c.g_stored, False, None),
+                   ("ld_x max", variant))
+    del big
+    torch.cuda.empty_cache()
+
+
 def test_smallest_shapes():
     for M, N, K in [(1, 1, 16), (1, 17, 16), (17, 1, 32), (16, 16, 16)]:
         say(f"shape {M}x{N}x{K}")
@@ -400,7 +414,8 @@ def test_smallest_shapes():
 
 
 def test_run_to_run_bitwise_determinism():
-    for make in (lambda: synth.decode_case(16, N=2048, K=4096, seed=3), lambda: synth.dense_case(200, 512, 1024, 4)):
+    for make in (lambda: synth.decode_case(16, N=2048, K=4096, seed=3), lambda: synth.dense_case(200, 512, 1024, 4),
+                 lambda: synth.dense_case(16, 2048, 4096, 5, act="f16")):
         c = make()
         say(f"determinism M={c.M}")
         d = DenseDev(c)
@@ -420,10 +435,11 @@ def test_graph_replays_match_eager():
              (synth.decode_case(1, N=2048, K=4096, seed=4), nv.VARIANT_AUTO),      # small-M, K split
              (synth.dense_case(300, 700, 2048, 5, prescale=True), nv.VARIANT_MFMA),  # two MFMA launches + pre-scale
              (synth.dense_case(24, 2000, 4096, 1005), nv.VARIANT_LARGE_M),          # tile, split with N tail
-             (synth.decode_case(8, N=2064, K=3968, seed=6), nv.VARIANT_AUTO)]       # activation-resident, ragged
+             (synth.decode_case(8, N=2064, K=3968, seed=6), nv.VARIANT_AUTO),       # activation-resident, ragged
+             (synth.dense_case(12, 1000, 2048, 8, act="f16", prescale=True), nv.VARIANT_AUTO)]   # fp16 + pre-scale
     devs = [DenseDev(c) for c, _ in cases]
     wss = [nv.workspace(nv.gemm_workspace_bytes(c.M, c.N, c.K), DEV) for c, _ in cases]
-    ys = [torch.empty((c.M, c.N), dtype=torch.bfloat16, device=DEV) for c, _ in cases]
+    ys = [torch.empty((c.M, c.N), dtype=d.x.dtype, device=DEV) for (c, _), d in zip(cases, devs)]
     gc = synth.grouped_case(T=16, E=8, topk=2, N=96, K=256, seed=6)
     gd = GroupedDev(gc)
     gws = nv.workspace(nv.lib().nvfp4_w4a16_grouped_gemm_workspace_bytes(gc.R, gc.E, gc.N, gc.K), DEV)
