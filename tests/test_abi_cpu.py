@@ -153,3 +153,18 @@ def test_moe_glue_argument_errors_and_empty_calls():
     assert gg(*args(R=0)) == OK                                                      # zero rows: no launch
     assert L.nvfp4_w4a16_grouped_gemm_gather_workspace_bytes(16, 32, 4, 32, 128) == 16 * 128 * 2   # pre-scaled tokens
     assert L.nvfp4_w4a16_grouped_gemm_gather_workspace_bytes(-1, 32, 4, 32, 128) == -1
+
+
+def test_f16_entry_points_check_arguments_and_name_themselves():
+    """The fp16 forms share the bf16 argument checks; their errors name the fp16 entry point."""
+    L = nv.lib()
+    st = L.nvfp4_w4a16_gemm_f16(_p(A), 128, None, _p(A), _p(A), 0, _p(A), 32, 4, 32, 24, None, 0, None)
+    assert st == INVALID and "nvfp4_w4a16_gemm_f16" in L.nvfp4_last_error().decode()
+    st = L.nvfp4_w4a16_gemm_variant_f16(_p(A), 128, None, _p(A), _p(A), 0, _p(A), 32, 17, 32, 128, None, 0, 1, None)
+    assert st == INVALID and "small-M" in L.nvfp4_last_error().decode()
+    st = L.nvfp4_w4a16_grouped_gemm_f16(_p(A), 100, _p(A), None, _p(A), _p(A), 0, _p(A), 32, 4, 2, 32, 128, None, 0,
+                                        None)
+    assert st == INVALID and "nvfp4_w4a16_grouped_gemm_f16" in L.nvfp4_last_error().decode()
+    st = L.nvfp4_moe_silu_mul_f16(_p(A), 10, 4, 8, _p(A), 8, None)
+    assert st == INVALID and "nvfp4_moe_silu_mul_f16" in L.nvfp4_last_error().decode()
+
