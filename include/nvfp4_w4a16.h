@@ -231,8 +231,9 @@ nvfp4_status nvfp4_dequant_bf16(const void* w_repacked, int64_t E, int64_t N, in
  *   variant 1 = small-M kernel (M <= 16 only; larger M -> INVALID_ARG),
  *   variant 2 = tile kernel (any M),
  *   variant 3 = MFMA-bound kernel (any M; launched as one or two kernels),
- *   variant 4 = activation-resident kernel (M <= 16, K <= 4096, N <= 32768;
- *               otherwise INVALID_ARG).
+ *   variant 4 = activation-resident kernel (M <= 16, K <= 32768 (K split
+ *               across workgroups beyond 4096), N <= 32768; otherwise
+ *               INVALID_ARG).
  * The automatic choice takes the small-M kernel up to 4 rows, the
  * activation-resident kernel for 5..16 rows where it applies, the MFMA-bound
  * kernel for large M and the tile kernel otherwise.

@@ -69,7 +69,7 @@ A = 1 << 20   # a fake, 16-byte-aligned address; never dereferenced (calls fail 
     (dict(ld_x=(1 << 23) + 8), INVALID, "exceeds"),
     (dict(variant=1, M=17), INVALID, "small-M"),
     (dict(variant=4, M=17), INVALID, "activation-resident"),
-    (dict(variant=4, K=4224, ld_x=4224), INVALID, "activation-resident"),
+    (dict(variant=4, K=32896, ld_x=32896), INVALID, "activation-resident"),
     (dict(variant=4, N=32784, ld_y=32784), INVALID, "activation-resident"),
     (dict(variant=7), INVALID, "variant"),
 ])

@@ -26,7 +26,7 @@ def accept_or_fail(y, ref, what):
 
 def variants(M, K, N):
     v = [nv.VARIANT_AUTO, nv.VARIANT_LARGE_M, nv.VARIANT_MFMA] + ([nv.VARIANT_SMALL_M] if M <= 16 else [])
-    return v + ([nv.VARIANT_RESIDENT] if M <= 16 and K <= 4096 and N <= 32768 else [])
+    return v + ([nv.VARIANT_RESIDENT] if M <= 16 and K <= 32768 and N <= 32768 else [])
 
 
 F16_DENSE = [

@@ -37,7 +37,7 @@ def dense_variants(M: int, K: int, N: int):
     """Every kernel variant that takes this shape: automatic, tile, MFMA-bound, small-M (M <= 16) and
     activation-resident (M <= 16, K <= 4096, N <= 32768)."""
     v = [nv.VARIANT_AUTO, nv.VARIANT_LARGE_M, nv.VARIANT_MFMA] + ([nv.VARIANT_SMALL_M] if M <= 16 else [])
-    return v + ([nv.VARIANT_RESIDENT] if M <= 16 and K <= 4096 and N <= 32768 else [])
+    return v + ([nv.VARIANT_RESIDENT] if M <= 16 and K <= 32768 and N <= 32768 else [])
 
 
 def oracle_bf16_bits(t64: np.ndarray) -> np.ndarray:
@@ -481,14 +481,16 @@ XRES_SHAPES = [
     (16, 1000, 4000),    # K ragged in its last chunk, N ragged in its last unit
     (5, 48, 272),        # most waves own no chunk (K = 2 chunks + 16)
     (16, 32752, 1024),   # the widest N it takes (eight units per workgroup), last unit ragged
+    (16, 4096, 14336),   # K split 4 ways across workgroups (the last split a half), published partials
+    (7, 1000, 8320),     # K split 3 ways, ragged K and N
 ]
 
 
 @pytest.mark.parametrize("M,N,K", XRES_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in XRES_SHAPES])
 def test_resident_variant_parity(M, N, K):
     """The activation-resident kernel against the oracle over its launch shapes: chunks per wave (1, 2),
-    units per workgroup (1..8), waves without chunks, ragged K and N; with a pre-quant scale and a divisor-stored
-    global scale on the odd shapes.  Automatic dispatch takes this kernel for 5..16 rows."""
+    units per workgroup (1..8), waves without chunks, K split across workgroups, ragged K and N; with a
+    pre-quant scale and a divisor-stored global scale on the odd shapes."""
     ragged = K % 128 != 0
     c = synth.dense_case(M, N, K, seed=M + N + K, prescale=ragged, g_stored=2688.0 if ragged else 1 / 2688,
                          g_is_divisor=ragged)
@@ -496,4 +498,4 @@ def test_resident_variant_parity(M, N, K):
     d = DenseDev(c)
     y = to_f64(d.run(nv.VARIANT_RESIDENT))
     accept_or_fail(y, oracle.gemm(c.x, c.w, c.s, c.g_stored, c.g_is_divisor, c.pre), ("resident", M, N, K))
-    assert torch.equal(d.run(nv.VARIANT_AUTO), d.run(nv.VARIANT_RESIDENT))
+    assert torch.equal(d.run(nv.VARIANT_RESIDENT), d.run(nv.VARIANT_RESIDENT))   # split order fixed

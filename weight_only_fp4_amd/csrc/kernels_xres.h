@@ -16,20 +16,23 @@
 //
 //   Reduction, in a fixed order (bitwise reproducible): wave w + W/2 adds its
 //   tiles into wave w's through LDS, then the W/2 sums are added in wave
-//   order, scaled by the global scale and rounded to bf16 (fp16 with F16).  K is not split
-//   across workgroups: the device-scope publish / count / reload round trip
-//   of a split measured slower than what it saves here.
+//   order, scaled by the global scale and rounded to bf16 (fp16 with F16).
+//   K beyond 16 waves x CH chunks is split S ways across workgroups (grid
+//   y): each split publishes its partial tile and the last arrival adds the
+//   S partials in split order (SplitK); the publish / count / reload round
+//   trip costs about 2 us, so shapes whose K fits one workgroup never split.
 //
 //   K slots of an MFMA step map to k = 32 g + 8 t + e (lane group g, step t,
 //   element e) on both operands, as in the tile kernel, so a weight lane reads
 //   one 32-wide K group of the repacked layout.  Activation rows past `rows`
 //   and K pieces past K are zero (never loaded); units past NU read unit
-//   NU - 1 and store nothing.  FULL (K == 128 W CH: every wave owns CH whole
+//   NU - 1 and store nothing.  FULL (K == 128 S W CH: every wave owns CH whole
 //   chunks) compiles without any per-chunk condition; otherwise chunks past
 //   K re-read the last chunk with a zero scale, so they add exact zeros
 //   whatever that chunk holds (no branch in the loop).
 #pragma once
 #include "decode.h"
+#include "kernels_gemm.h"
 #include "layout.h"
 
 namespace nvfp4 {
@@ -40,7 +43,8 @@ constexpr int kXresWaveBytes = 16 * kXresRowBytes;     // a wave's staging area
 template <int CH, int U, int W, int D, bool FULL, bool F16 = false>
 __global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                       int NU, int KC, int K, int N, const float* __restrict__ gscale,
-                                                      int g_is_div, uint16_t* __restrict__ y, int64_t ld_y, int rows) {
+                                                      int g_is_div, uint16_t* __restrict__ y, int64_t ld_y, int rows,
+                                                      SplitK sk) {
     constexpr int NI = U * CH;          // ring items of a wave: (unit, chunk), unit-major
     constexpr int H = W / 2;            // waves after the first reduction stage
     constexpr int TILE = U * 256;       // fp32 outputs of the workgroup (16 rows x 16 U columns)
@@ -48,11 +52,13 @@ __global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict
     constexpr int DR = D < NI ? D : NI;   // ring slots in use
     static_assert(W % 2 == 0, "the first reduction stage pairs waves w and w + W/2");
     __shared__ __attribute__((aligned(16))) uint8_t xs[W * kXresWaveBytes];
+    __shared__ int s_flag;
     __shared__ __attribute__((aligned(16))) float red[H * TILE];
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int c0 = w * CH;                                                // first chunk of this wave's slice
+    const int s = (int)blockIdx.y, S = sk.S;                              // K split of this workgroup
+    const int c0 = (s * W + w) * CH;                                      // first chunk of this wave's slice
     const int nch = KC - c0 < CH ? (KC - c0 > 0 ? KC - c0 : 0) : CH;      // chunks that exist (wave-uniform)
     const int u0 = (int)blockIdx.x * U;
 
@@ -154,16 +160,46 @@ __global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict
         }
     }
     __syncthreads();
-    const float gv = effective_global_scale(gscale[0], g_is_div);
-    for (int o = tid; o < TILE; o += W * 64) {
+    constexpr int PER = (TILE + W * 64 - 1) / (W * 64);   // outputs per thread
+    float v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
         // o = (u, m, n): consecutive threads take consecutive columns of one row
-        const int m = (o >> 4) & 15;
-        const int src = (o >> 8) * 256 + ((m >> 2) * 16 + (o & 15)) * 4 + (m & 3);
+        const int o = tid + j * W * 64, oc = o < TILE ? o : 0, m = (oc >> 4) & 15;
+        const int src = (oc >> 8) * 256 + ((m >> 2) * 16 + (oc & 15)) * 4 + (m & 3);
         float a = red[src];
 #pragma unroll
         for (int ww = 1; ww < H; ++ww) a += red[ww * TILE + src];
+        v[j] = a;
+    }
+    if (S > 1) {
+        // K splits: publish this split's partial tile; the last arrival adds
+        // the S partials in split order 0..S-1, whichever arrived last
+        const int64_t tile = blockIdx.x, tiles = gridDim.x;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int o = tid + j * W * 64;
+            if (o < TILE) store_partial(sk.partials + ((int64_t)s * tiles + tile) * TILE + o, v[j]);
+        }
+        if (!split_arrive(sk.counters, tile, S, &s_flag)) return;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int o = tid + j * W * 64;
+            if (o >= TILE) continue;
+            float a = 0.f;
+            for (int ss = 0; ss < S; ++ss) {
+                const float p = ss == s ? v[j] : load_partial(sk.partials + ((int64_t)ss * tiles + tile) * TILE + o);
+                a = ss == 0 ? p : a + p;
+            }
+            v[j] = a;
+        }
+    }
+    const float gv = effective_global_scale(gscale[0], g_is_div);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int o = tid + j * W * 64, m = (o >> 4) & 15;
         const int64_t col = (int64_t)(u0 + (o >> 8)) * kUnitN + (o & 15);
-        if (m < rows && col < N) y[(int64_t)m * ld_y + col] = (uint16_t)round_out<F16>(gv * a);
+        if (o < TILE && m < rows && col < N) y[(int64_t)m * ld_y + col] = (uint16_t)round_out<F16>(gv * v[j]);
     }
 }
 

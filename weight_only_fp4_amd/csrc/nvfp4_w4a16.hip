@@ -302,11 +302,12 @@ nvfp4_status launch_tile(const TileShape& t, const Layout& L, const uint16_t* x,
 // Rows from which the automatic choice takes the activation-resident kernel
 // (below it the small-M kernel, measured faster at one row).
 constexpr int64_t kXresAutoMin = 5;
-constexpr int kXresMaxK = 2 * 16 * kChunkK;   // two chunks for each of 16 waves
+constexpr int kXresMaxSplits = 8;
+constexpr int kXresMaxK = kXresMaxSplits * 2 * 16 * kChunkK;   // two chunks for each of 16 waves, per split
 constexpr int kXresMaxN = 8 * 256 * kUnitN;   // eight units for each of 256 workgroups
 
 struct XresShape {
-    int ch, u, w, d;
+    int ch, u, w, d, S;
     int64_t groups;
 };
 
@@ -318,12 +319,14 @@ bool xres_compiled(const XresShape& s) {
     return found;
 }
 
-// 16 waves own one or two chunks each (K up to 4096), units per workgroup
-// by N.  A shape outside the compiled set means the kernel does not take the
-// call (K above 4096, or more than 2048 row units).
+// 16 waves own one or two chunks each; K beyond 32 chunks is split S ways
+// across workgroups; units per workgroup by N and S, so that the grid is
+// about one workgroup per CU.  A shape outside the compiled set means the
+// kernel does not take the call (K above 8 splits, or too many row units).
 XresShape xres_shape(const Layout& L) {
-    XresShape s{L.KC <= 16 ? 1 : 2, 0, 16, 2, 0};
-    const int64_t u = (L.NU + 255) / 256;
+    XresShape s{L.KC <= 16 ? 1 : 2, 0, 16, 2, 1, 0};
+    s.S = (int)((L.KC + 31) / 32);
+    const int64_t u = (L.NU * s.S + 255) / 256;
     s.u = (int)(u < 1 ? 1 : u > 64 ? 64 : u);
     s.groups = (L.NU + s.u - 1) / s.u;
     return s;
@@ -332,21 +335,26 @@ XresShape xres_shape(const Layout& L) {
 // Does the activation-resident kernel take this dense call?
 bool xres_fits(const Layout& L, int64_t rows) {
     const XresShape s = xres_shape(L);
-    return rows <= kSmallRows && (int64_t)s.w * s.ch >= L.KC && xres_compiled(s);
+    return rows <= kSmallRows && s.S <= kXresMaxSplits && (int64_t)s.S * s.w * s.ch >= L.KC && xres_compiled(s) &&
+           s.groups <= 65535;
+}
+
+Workspace workspace_for(const XresShape& s, int64_t rows, int64_t K, bool pre) {
+    return workspace_layout(s.S, s.groups, (int64_t)s.u * 256, rows, K, pre);
 }
 
 nvfp4_status launch_xres(const XresShape& s, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
-                         const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows, hipStream_t st,
-                         bool f16) {
+                         const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t rows, SplitK sk,
+                         hipStream_t st, bool f16) {
     const BlobView bv = make_view(L, blob);
-    const dim3 grid((unsigned)s.groups);
+    const dim3 grid((unsigned)s.groups, (unsigned)s.S);
     bool done = false;
 #define NVFP4_XRES_LAUNCH(CH, U, W, D, FULL, F16)                                                               \
     hipLaunchKernelGGL((k_gemm_xres<CH, U, W, D, FULL, F16>), grid, dim3(W * 64), 0, st, x, ld_x, bv, (int)L.NU, \
-                       (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, (int)rows)
+                       (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, (int)rows, sk)
 #define NVFP4_XRES_DISPATCH(CH, U, W, D)                                                                          \
     if (!done && s.ch == CH && s.u == U && s.w == W && s.d == D) {                                               \
-        const bool full = L.K == (int64_t)CH * W * kChunkK;                                                     \
+        const bool full = L.K == (int64_t)s.S * CH * W * kChunkK;                                               \
         if (f16 && full) NVFP4_XRES_LAUNCH(CH, U, W, D, true, true);                                            \
         else if (f16) NVFP4_XRES_LAUNCH(CH, U, W, D, false, true);                                              \
         else if (full) NVFP4_XRES_LAUNCH(CH, U, W, D, true, false);                                             \
@@ -427,6 +435,8 @@ int64_t dense_workspace_bytes(const Layout& L, int64_t M) {
     if (M <= kSmallRows) {
         const int64_t small = workspace_for(small_m_shape(L, M, false), M, L.K, true).total;
         need = small > need ? small : need;
+        const int64_t xres = workspace_for(xres_shape(L), M, L.K, true).total;
+        need = xres > need ? xres : need;
     }
     return need;
 }
@@ -457,7 +467,7 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
         return fail(NVFP4_ERR_INVALID_ARG, "%s: the MFMA-bound variant takes weights below 2 GiB of codes", fn);
     const bool mfma = variant == kMfma ||
                       (variant == kAuto && mfma_fits && M >= kMfmaAuto && mfma_plan(L, M).tiles >= kMfmaMinTiles);
-    const Workspace wl = resident ? workspace_layout(1, 0, 0, M, K, pre != nullptr)
+    const Workspace wl = resident ? workspace_for(xs, M, K, pre != nullptr)
                          : small  ? workspace_for(sm, M, K, pre != nullptr)
                          : mfma ? workspace_layout(1, 0, 0, M, K, pre != nullptr)
                                 : workspace_for(t, M, K, pre != nullptr);
@@ -471,7 +481,7 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
     if (s != NVFP4_OK) return s;
     const uint8_t* blob = static_cast<const uint8_t*>(w);
     uint16_t* yo = static_cast<uint16_t*>(y);
-    if (resident) return launch_xres(xs, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, st, f16);
+    if (resident) return launch_xres(xs, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, split_k(xs.S, wsb, wl), st, f16);
     if (small)
         return launch_small<false>(sm, L, xp, ld_x, blob, gs, g_div, yo, ld_y, M, nullptr, split_k(sm.S, wsb, wl), st,
                                    f16);
