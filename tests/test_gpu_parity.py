@@ -431,7 +431,8 @@ def test_graph_replays_match_eager():
     between replays.  The split-K counters live in workspaces zeroed once before capture: the kernels themselves
     must leave them zero after every call, since nothing clears them between replays."""
     say("graph replays")
-    cases = [(synth.decode_case(16, N=4096, K=14336, seed=3), nv.VARIANT_AUTO),    # tile, K split 2 ways
+    cases = [(synth.decode_case(16, N=4096, K=14336, seed=3), nv.VARIANT_AUTO),    # activation-resident, K split 4 ways
+             (synth.decode_case(16, N=4096, K=14336, seed=3), nv.VARIANT_LARGE_M),  # tile, K split 2 ways
              (synth.decode_case(1, N=2048, K=4096, seed=4), nv.VARIANT_AUTO),      # small-M, K split
              (synth.dense_case(300, 700, 2048, 5, prescale=True), nv.VARIANT_MFMA),  # two MFMA launches + pre-scale
              (synth.dense_case(24, 2000, 4096, 1005), nv.VARIANT_LARGE_M),          # tile, split with N tail
