@@ -108,16 +108,8 @@ def make_dense(name, M, N, K, *, seed, scales="pow2_mant", g_stored=1.0 / 2688.0
     def launch(i):
         nv.gemm(x, blobs[i % copies], N, K, g, divisor, pre, out=y, workspace_buf=ws)
 
-    # the kernel the automatic dispatch picks: small-M up to 4 rows, activation-resident for 5..16 rows with
-    # K <= 32768 and N <= 32768, MFMA-bound from 256 rows when the call has at least 48 output tiles of
-    # 256 x 256, the tile kernel otherwise
-    mfma_tiles = -(-M // 256) * -(-N // 256)
-    if M <= 4:
-        kernel = "k_gemm_small_m"
-    elif M <= 16 and K <= 32768 and N <= 32768:
-        kernel = "k_gemm_xres"
-    else:
-        kernel = "k_gemm_mfma" if M >= 256 and mfma_tiles >= 48 else "k_gemm_tile"
+    # the kernel the automatic dispatch runs, as the library reports it
+    kernel = nv.VARIANT_KERNELS[nv.gemm_plan(M, N, K)]
     flops = 2.0 * M * N * K
     ab = dense_bytes(M, N, K, pre is not None)
     bound = "hbm" if flops / ab < (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) else "mfma"

@@ -61,6 +61,11 @@ typedef enum {
 /* Message of the last failed call on this thread ("" if none). */
 const char* nvfp4_last_error(void);
 
+/* Zero sizes: a call with no rows (M, R or T == 0) or no output columns
+ * (N == 0) checks its other arguments, returns NVFP4_OK and launches nothing
+ * (a zero-token chunk launches no kernel: "Apply the NVFP4_AWQ pre-quant
+ * scale in MegaMoE CuteDSL", Description). */
+
 /* ---------------------------------------------------------------- repack --
  * One-time re-tiling of canonical weights into the layout the GEMM kernels
  * stream (a step the pages perform as the Marlin weight transformation with
@@ -75,10 +80,11 @@ const char* nvfp4_last_error(void);
  * Output: `out`, nvfp4_repack_bytes(E,N,K) bytes, 16-byte aligned.  The blob
  * is pure derived state: repacking the same input again gives the same bytes,
  * and the canonical input is never modified.  N is padded to a multiple of
- * 16 and K to a multiple of 128 with zero codes and zero scales.
- * Errors: E < 1, N < 1, K < 16, K % 16 != 0, ld_w < K/2, ld_s < K/16, NULL
- * pointer -> INVALID_ARG; out not 16-byte aligned -> ALIGNMENT; out_bytes too
- * small -> BUFFER_TOO_SMALL. */
+ * 16 and K to a multiple of 128 with zero codes and zero scales.  N == 0
+ * needs 0 bytes and launches nothing.
+ * Errors: E < 1, N < 0, K < 16, K % 16 != 0, ld_w < K/2, ld_s < K/16, NULL
+ * pointer (N > 0) -> INVALID_ARG; out not 16-byte aligned -> ALIGNMENT;
+ * out_bytes too small -> BUFFER_TOO_SMALL. */
 int64_t nvfp4_repack_bytes(int64_t E, int64_t N, int64_t K); /* < 0 if invalid */
 nvfp4_status nvfp4_repack(const uint8_t* w_packed, int64_t ld_w, const uint8_t* w_scale, int64_t ld_s,
                           int64_t E, int64_t N, int64_t K, void* out, int64_t out_bytes, void* stream);
@@ -88,24 +94,26 @@ nvfp4_status nvfp4_repack(const uint8_t* w_packed, int64_t ld_w, const uint8_t* 
  *   X'[m,k] = pre_scale ? RNE_bf16(X[m,k] * pre_scale[k]) : X[m,k]
  *   g       = global_scale_is_divisor ? fp32(1 / *global_scale) : *global_scale
  * (the inversion happens at use, in the epilogue; *global_scale is never
- * rewritten).  Accumulation is fp32; the summation order is fixed, so
- * results are bitwise reproducible run to run.
+ * rewritten).  The pre-quant scale is applied where the kernels load the
+ * activation; X' is never written to memory.  Accumulation is fp32; the
+ * summation order is fixed, so results are bitwise reproducible run to run.
  *   x         : bf16 [M][ld_x] (16-byte aligned, K <= ld_x <= 2^23, ld_x % 8 == 0)
  *   pre_scale : bf16 [K] (16-byte aligned) or NULL
  *   w_repacked: output of nvfp4_repack with E = 1 and the same N, K
  *   global_scale: device pointer to one fp32
  *   y         : bf16 [M][ld_y] (2-byte aligned, ld_y >= N)
  *   workspace : device scratch of nvfp4_w4a16_gemm_workspace_bytes(M,N,K)
- *               bytes, 256-byte aligned (may be NULL when that is 0).  It
- *               must be zero-filled before its first use; every call leaves
- *               the part that has to be zero zeroed again, so one workspace
- *               can serve any number of calls issued one after another.
- *               Calls that may overlap in time (other streams) need their
- *               own workspace.  The size covers either kernel variant, with
- *               or without a pre-scale.
- * M == 0 returns NVFP4_OK without launching anything.
- * Errors: M < 0, N < 1, K < 16, K % 16 != 0, ld_x < K, ld_x > 2^23, ld_y < N, NULL
- * x / w_repacked / global_scale / y (x may be NULL when M == 0) ->
+ *               bytes, 256-byte aligned (may be NULL when that is 0; it is 0
+ *               unless the call's kernel splits K across workgroups).  It
+ *               holds split-K partial sums and arrival counters; it must be
+ *               zero-filled before its first use; every call leaves the
+ *               counters zero again, so one workspace can serve any number
+ *               of calls issued one after another.  Calls that may overlap
+ *               in time (other streams) need their own workspace.  The size
+ *               covers every kernel variant that takes the shape.
+ * M == 0 or N == 0 returns NVFP4_OK without launching anything.
+ * Errors: M < 0, N < 0, K < 16, K % 16 != 0, ld_x < K, ld_x > 2^23, ld_y < N, NULL
+ * x / w_repacked / global_scale / y (x and y may be NULL when M == 0) ->
  * INVALID_ARG; misaligned x, pre_scale, w_repacked, y or workspace, or
  * ld_x % 8 != 0 -> ALIGNMENT; workspace smaller than this call needs ->
  * BUFFER_TOO_SMALL. */
@@ -129,8 +137,9 @@ nvfp4_status nvfp4_w4a16_gemm(const void* x, int64_t ld_x, const void* pre_scale
  *   w_repacked    : output of nvfp4_repack with this E, N, K
  *   global_scales : device fp32 [E]
  *   y             : bf16 [R][ld_y]
- *   workspace     : as for the dense form, nvfp4_w4a16_grouped_gemm_workspace_bytes bytes
- * R == 0 returns NVFP4_OK without launching anything.
+ *   workspace     : as for the dense form, nvfp4_w4a16_grouped_gemm_workspace_bytes
+ *                   bytes (0: the grouped kernels never split K)
+ * R == 0 or N == 0 returns NVFP4_OK without launching anything.
  * Errors as for the dense form, plus E < 1 -> INVALID_ARG. */
 int64_t nvfp4_w4a16_grouped_gemm_workspace_bytes(int64_t R, int64_t E, int64_t N, int64_t K);
 nvfp4_status nvfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t* expert_offsets,
@@ -231,17 +240,29 @@ nvfp4_status nvfp4_dequant_bf16(const void* w_repacked, int64_t E, int64_t N, in
  *   variant 1 = small-M kernel (M <= 16 only; larger M -> INVALID_ARG),
  *   variant 2 = tile kernel (any M),
  *   variant 3 = MFMA-bound kernel (any M; launched as one or two kernels),
- *   variant 4 = activation-resident kernel (M <= 16, K <= 32768 (K split
- *               across workgroups beyond 4096), N <= 32768; otherwise
- *               INVALID_ARG).
+ *   variant 4 = activation-resident kernel: M <= 16, K <= 32768 (K split
+ *               across workgroups beyond 4096) and
+ *               ceil(N / 16) * ceil(K / 4096) <= 2048; otherwise INVALID_ARG,
+ *   variant 5 = MFMA-bound kernel with every 256 x 256 tile run as four
+ *               64-row workgroups (several then share a compute unit).
  * The automatic choice takes the small-M kernel up to 4 rows, the
  * activation-resident kernel for 5..16 rows where it applies, the MFMA-bound
- * kernel for large M and the tile kernel otherwise.
+ * kernel for large M and the tile kernel otherwise (nvfp4_w4a16_gemm_plan).
  * Used to check that the variants agree on the same inputs. */
 nvfp4_status nvfp4_w4a16_gemm_variant(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
                                       const float* global_scale, int global_scale_is_divisor,
                                       void* y, int64_t ld_y, int64_t M, int64_t N, int64_t K,
                                       void* workspace, int64_t workspace_bytes, int variant, void* stream);
+
+/* The variant (1..4 above) that nvfp4_w4a16_gemm runs for an M x N x K call,
+ * 0 when it launches nothing (M == 0 or N == 0), -1 for invalid sizes.  A
+ * pure host function of the sizes (bf16 and fp16 calls choose alike). */
+int nvfp4_w4a16_gemm_plan(int64_t M, int64_t N, int64_t K);
+
+/* 1 if nvfp4_w4a16_gemm_variant accepts `variant` for an M x N x K call, 0 if
+ * it rejects the shape (INVALID_ARG), -1 for invalid sizes or variants.  A
+ * pure host function of the sizes. */
+int nvfp4_w4a16_gemm_variant_takes(int64_t M, int64_t N, int64_t K, int variant);
 
 /* ---- FP16 activations and outputs ------------------------------------------
  *

@@ -42,7 +42,8 @@ def test_repack_bytes_layout_size():
     assert nv.repack_bytes(128, 1536, 2048) == 128 * 96 * 16 * 1152
     assert nv.lib().nvfp4_repack_bytes(1, 16, 8) < 0
     assert nv.lib().nvfp4_repack_bytes(0, 16, 16) < 0
-    assert nv.lib().nvfp4_repack_bytes(1, 0, 16) < 0
+    assert nv.lib().nvfp4_repack_bytes(1, 0, 16) == 0      # no rows: nothing to repack
+    assert nv.lib().nvfp4_repack_bytes(1, -1, 16) < 0
 
 
 def _p(v):
@@ -55,7 +56,7 @@ A = 1 << 20   # a fake, 16-byte-aligned address; never dereferenced (calls fail 
 @pytest.mark.parametrize("args,status,needle", [
     (dict(K=24), INVALID, "multiple of 16"),
     (dict(K=0), INVALID, "multiple of 16"),
-    (dict(N=0), INVALID, "N ="),
+    (dict(N=-1), INVALID, "N ="),
     (dict(M=-1), INVALID, "negative"),
     (dict(ld_x=100), INVALID, "ld_x"),
     (dict(ld_y=10), INVALID, "ld_y"),
@@ -64,13 +65,17 @@ A = 1 << 20   # a fake, 16-byte-aligned address; never dereferenced (calls fail 
     (dict(x=A + 2), ALIGN, "16-byte"),
     (dict(ld_x=132), ALIGN, "ld_x"),
     (dict(y=A + 1), ALIGN, "y must be"),
-    (dict(pre=A, ws=A, wsb=10), SMALL, "workspace"),
+    (dict(M=16, N=4096, K=14336, ld_x=14336, ld_y=4096, variant=2, pre=A, ws=A, wsb=10), SMALL, "workspace"),
     (dict(M=16, N=4096, K=14336, ld_x=14336, ld_y=4096, variant=2, ws=A + 16, wsb=1 << 30), ALIGN, "workspace"),
     (dict(ld_x=(1 << 23) + 8), INVALID, "exceeds"),
     (dict(variant=1, M=17), INVALID, "small-M"),
     (dict(variant=4, M=17), INVALID, "activation-resident"),
     (dict(variant=4, K=32896, ld_x=32896), INVALID, "activation-resident"),
     (dict(variant=4, N=32784, ld_y=32784), INVALID, "activation-resident"),
+    # ceil(N / 16) * ceil(K / 4096) = 2048 * 2 > 2048: beyond the resident kernel although N, K <= 32768
+    (dict(variant=4, M=16, N=32768, K=8192, ld_x=8192, ld_y=32768), INVALID, "ceil(N / 16) * ceil(K / 4096) <= 2048"),
+    (dict(variant=4, M=16, N=14336, K=16384, ld_x=16384, ld_y=14336), INVALID, "activation-resident"),
+    (dict(variant=5, K=24), INVALID, "multiple of 16"),
     (dict(variant=7), INVALID, "variant"),
 ])
 def test_gemm_argument_errors(args, status, needle):
@@ -84,12 +89,48 @@ def test_gemm_argument_errors(args, status, needle):
     assert needle in L.nvfp4_last_error().decode()
 
 
-def test_zero_rows_launch_nothing_and_succeed():
+def test_zero_sizes_launch_nothing_and_succeed():
+    """M == 0, R == 0 or N == 0: the call checks its arguments, returns OK and launches nothing (every pointer
+    here is fake; a launch would fail on this host, which has no GPU, and report NVFP4_ERR_HIP)."""
     L = nv.lib()
     assert L.nvfp4_w4a16_gemm(None, 128, None, _p(A), _p(A), 0, None, 32, 0, 32, 128, None, 0, None) == OK
     assert L.nvfp4_last_error().decode() == ""
     assert L.nvfp4_w4a16_grouped_gemm(None, 128, _p(A), None, _p(A), _p(A), 0, None, 32, 0, 4, 32, 128,
                                       None, 0, None) == OK
+    # no output columns: weights and output hold no bytes and may be NULL
+    assert L.nvfp4_w4a16_gemm(_p(A), 128, None, None, _p(A), 0, None, 0, 4, 0, 128, None, 0, None) == OK
+    assert L.nvfp4_w4a16_gemm_variant(_p(A), 128, None, None, _p(A), 0, None, 0, 4, 0, 128, None, 0, 4, None) == OK
+    assert L.nvfp4_w4a16_gemm_f16(_p(A), 128, _p(A), None, _p(A), 1, None, 0, 300, 0, 128, None, 0, None) == OK
+    assert L.nvfp4_w4a16_grouped_gemm(_p(A), 128, _p(A), None, None, _p(A), 0, None, 0, 8, 4, 0, 128,
+                                      None, 0, None) == OK
+    assert L.nvfp4_repack(None, 64, None, 8, 1, 0, 128, None, 0, None) == OK
+    assert L.nvfp4_repack_bytes(3, 0, 128) == 0
+    assert L.nvfp4_dequant_bf16(None, 1, 0, 128, None, 128, None) == OK
+    assert L.nvfp4_w4a16_gemm_workspace_bytes(16, 0, 4096) == 0
+    assert L.nvfp4_w4a16_gemm_plan(16, 0, 4096) == 0 and L.nvfp4_w4a16_gemm_plan(0, 4096, 4096) == 0
+    # the other arguments are still checked
+    assert L.nvfp4_w4a16_gemm(_p(A), 128, None, None, _p(A), 0, None, 0, 4, 0, 24, None, 0, None) == INVALID
+
+
+def test_gemm_plan_names_the_automatic_kernel():
+    """The automatic choice: small-M up to 4 rows, the activation-resident kernel for 5..16 rows where it takes the
+    shape, the MFMA-bound kernel from 256 rows when the call has at least 48 of its 256 x 256 tiles, the tile kernel
+    otherwise."""
+    plan = nv.gemm_plan
+    assert plan(1, 14336, 4096) == nv.VARIANT_SMALL_M and plan(4, 131072, 4096) == nv.VARIANT_SMALL_M
+    for M in (5, 8, 16):
+        assert plan(M, 14336, 4096) == nv.VARIANT_RESIDENT
+        assert plan(M, 4096, 14336) == nv.VARIANT_RESIDENT
+    assert plan(16, 16384, 8192) == nv.VARIANT_RESIDENT          # ceil(N/16) * ceil(K/4096) = 2048: the limit
+    assert plan(16, 32768, 8192) == nv.VARIANT_LARGE_M           # 4096 > 2048
+    assert plan(16, 131072, 4096) == nv.VARIANT_LARGE_M
+    assert plan(16, 4096, 40960) == nv.VARIANT_LARGE_M           # K above 32768
+    assert plan(17, 14336, 4096) == nv.VARIANT_LARGE_M
+    assert plan(4096, 14336, 4096) == nv.VARIANT_MFMA and plan(8192, 17408, 5120) == nv.VARIANT_MFMA
+    assert plan(256, 2048, 4096) == nv.VARIANT_LARGE_M           # 8 tiles: too few for the MFMA-bound kernel
+    assert plan(64, 131072, 4096) == nv.VARIANT_LARGE_M
+    with pytest.raises(ValueError):
+        plan(4, 32, 24)
 
 
 def test_grouped_and_repack_argument_errors():
@@ -108,12 +149,21 @@ def test_grouped_and_repack_argument_errors():
 
 
 def test_workspace_queries():
+    """The workspace holds split-K partials and counters only: the pre-quant scale is applied in the kernels'
+    activation loads, and calls whose kernels do not split K need none."""
     L = nv.lib()
-    assert L.nvfp4_w4a16_gemm_workspace_bytes(33, 1000, 1040) >= 33 * 1040 * 2
-    assert L.nvfp4_w4a16_gemm_workspace_bytes(0, 1000, 1040) >= 0
+    assert L.nvfp4_w4a16_gemm_workspace_bytes(0, 1000, 1040) == 0
     # M=16, N=4096, K=14336: K split across workgroups -> fp32 partials of 16 x 4096 per split, plus counters
     assert L.nvfp4_w4a16_gemm_workspace_bytes(16, 4096, 14336) > 2 * 16 * 4096 * 4
-    assert L.nvfp4_w4a16_grouped_gemm_workspace_bytes(128, 128, 1536, 2048) >= 128 * 2048 * 2
+    # the MFMA-bound prefill call never splits K
+    assert L.nvfp4_w4a16_gemm_workspace_bytes(4096, 14336, 4096) == 0
+    # shapes the activation-resident kernel does not take size for the kernels that do (no split at these
+    # widths): nothing, where the resident kernel's split area was counted before (16.8 MB, 134 MB, 2.16 GB)
+    assert L.nvfp4_w4a16_gemm_workspace_bytes(1, 131072, 8192) == 0
+    assert L.nvfp4_w4a16_gemm_workspace_bytes(1, 131072, 65536) == 0
+    assert L.nvfp4_w4a16_gemm_workspace_bytes(4, 131072, 1 << 20) == 0
+    assert L.nvfp4_w4a16_gemm_workspace_bytes(16, 32768, 8192) == 0
+    assert L.nvfp4_w4a16_grouped_gemm_workspace_bytes(128, 128, 1536, 2048) == 0
     assert L.nvfp4_w4a16_gemm_workspace_bytes(-1, 10, 16) < 0
 
 
@@ -151,7 +201,7 @@ def test_moe_glue_argument_errors_and_empty_calls():
     assert gg(*args(T=0)) == INVALID
     assert gg(*args(T=1 << 20, ld_x=1 << 12)) == INVALID and "2^31" in L.nvfp4_last_error().decode()
     assert gg(*args(R=0)) == OK                                                      # zero rows: no launch
-    assert L.nvfp4_w4a16_grouped_gemm_gather_workspace_bytes(16, 32, 4, 32, 128) == 16 * 128 * 2   # pre-scaled tokens
+    assert L.nvfp4_w4a16_grouped_gemm_gather_workspace_bytes(16, 32, 4, 32, 128) == 0   # no copy of the tokens
     assert L.nvfp4_w4a16_grouped_gemm_gather_workspace_bytes(-1, 32, 4, 32, 128) == -1
 
 

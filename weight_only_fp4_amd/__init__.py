@@ -23,10 +23,15 @@ import torch
 __all__ = ["repack", "repack_bytes", "gemm", "gemm_variant", "grouped_gemm", "dequant", "lib", "Nvfp4Error",
            "workspace", "gemm_workspace_bytes", "grouped_gemm_gather", "moe_route", "moe_silu_mul", "moe_relu2",
            "moe_combine",
-           "VARIANT_AUTO", "VARIANT_SMALL_M", "VARIANT_LARGE_M", "VARIANT_MFMA", "VARIANT_RESIDENT", "LIB_PATH"]
+           "gemm_plan", "gemm_variants", "VARIANT_AUTO", "VARIANT_SMALL_M", "VARIANT_LARGE_M", "VARIANT_MFMA", "VARIANT_RESIDENT",
+           "VARIANT_MFMA_QUARTER", "VARIANT_KERNELS", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4_w4a16.so")
 VARIANT_AUTO, VARIANT_SMALL_M, VARIANT_LARGE_M, VARIANT_MFMA, VARIANT_RESIDENT = 0, 1, 2, 3, 4
+VARIANT_MFMA_QUARTER = 5   # MFMA-bound kernel with 64-row workgroups (several per compute unit)
+# kernel symbol run by each variant (nvfp4_w4a16_gemm_plan names the variant the automatic choice takes)
+VARIANT_KERNELS = {VARIANT_SMALL_M: "k_gemm_small_m", VARIANT_LARGE_M: "k_gemm_tile", VARIANT_MFMA: "k_gemm_mfma",
+                   VARIANT_RESIDENT: "k_gemm_xres", VARIANT_MFMA_QUARTER: "k_gemm_mfma"}
 _STATUS = {0: "OK", 1: "INVALID_ARG", 2: "ALIGNMENT", 3: "BUFFER_TOO_SMALL", 4: "HIP"}
 _lib = None
 
@@ -55,6 +60,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_w4a16_gemm.restype = I
         L.nvfp4_w4a16_gemm_variant.argtypes = [P, I64, P, P, P, I, P, I64, I64, I64, I64, P, I64, I, P]
         L.nvfp4_w4a16_gemm_variant.restype = I
+        L.nvfp4_w4a16_gemm_plan.argtypes, L.nvfp4_w4a16_gemm_plan.restype = [I64, I64, I64], I
+        L.nvfp4_w4a16_gemm_variant_takes.argtypes = [I64, I64, I64, I]
+        L.nvfp4_w4a16_gemm_variant_takes.restype = I
         L.nvfp4_w4a16_gemm_f16.argtypes = [P, I64, P, P, P, I, P, I64, I64, I64, I64, P, I64, P]
         L.nvfp4_w4a16_gemm_f16.restype = I
         L.nvfp4_w4a16_gemm_variant_f16.argtypes = [P, I64, P, P, P, I, P, I64, I64, I64, I64, P, I64, I, P]
@@ -199,6 +207,21 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 
 def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(lib().nvfp4_w4a16_gemm_workspace_bytes(M, N, K))
+
+
+def gemm_variants(M: int, N: int, K: int) -> list:
+    """Every forced variant (VARIANT_*) that takes an M x N x K call, automatic first."""
+    L = lib()
+    return [v for v in (VARIANT_AUTO, VARIANT_SMALL_M, VARIANT_LARGE_M, VARIANT_MFMA, VARIANT_RESIDENT)
+            if L.nvfp4_w4a16_gemm_variant_takes(M, N, K, v) == 1]
+
+
+def gemm_plan(M: int, N: int, K: int) -> int:
+    """The variant (VARIANT_*) the automatic choice runs for an M x N x K call; 0 when it launches nothing."""
+    v = int(lib().nvfp4_w4a16_gemm_plan(M, N, K))
+    if v < 0:
+        raise ValueError(f"invalid GEMM shape M={M} N={N} K={K}")
+    return v
 
 
 def gemm_variant(x, blob, N, K, global_scale, divisor=False, pre_scale=None, out=None, workspace_buf=None,

@@ -21,12 +21,20 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
 ]
-# (source, extra flags)
+# (source, extra flags, object tag).  The kernel families are split into
+# translation units per activation type (and pre-scale form for the MFMA-bound
+# kernel) so that they compile in parallel.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]   # MFMA results in VGPRs (post-processed by VALU)
 SOURCES = [
-    # MFMA results in VGPRs: the small-M kernel post-processes every result with VALU FMAs
-    ("nvfp4_w4a16.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+    ("nvfp4_w4a16.hip", VGPR_FORM, "abi"),
+    ("nvfp4_mfma.hip", [], "mfma_plan"),
+] + [
+    (f"gemm_{fam}.hip", VGPR_FORM + [f"-DNVFP4_ACT_F16={f16}"], f"{fam}_{f16}")
+    for fam in ("small", "tile", "xres") for f16 in (0, 1)
+] + [
     # the MFMA-bound kernel keeps its 256 accumulators in AGPRs
-    ("nvfp4_mfma.hip", []),
+    ("gemm_mfma.hip", [f"-DNVFP4_ACT_F16={f16}", f"-DNVFP4_PRE={pre}"], f"mfma_{f16}{pre}")
+    for f16 in (0, 1) for pre in (0, 1)
 ]
 NOISE = "not a recognized feature for this target"
 
@@ -43,10 +51,10 @@ def build(verbose: bool = False) -> str:
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
     with tempfile.TemporaryDirectory(prefix="nvfp4_build_") as tmpd:
         jobs = []
-        for src, extra in SOURCES:
-            obj = os.path.join(tmpd, src + ".o")
+        for src, extra, tag in SOURCES:
+            obj = os.path.join(tmpd, tag + ".o")
             jobs.append((obj, [hipcc, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]))
-        with ThreadPoolExecutor(len(jobs)) as ex:
+        with ThreadPoolExecutor(min(len(jobs), max(1, os.cpu_count() or 1))) as ex:
             outs = list(ex.map(lambda j: (j[1], _run(j[1])), jobs))
         for cmd, msgs in outs:
             if verbose:

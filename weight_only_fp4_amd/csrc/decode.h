@@ -176,6 +176,39 @@ __device__ __forceinline__ float act_to_f32(uint32_t h) {
     else return bf16_to_f32(h);
 }
 
+// fp32 pair -> bf16 (fp16 with F16) pair, round to nearest even with the
+// hardware conversion (one instruction per pair; a NaN stays NaN), first
+// value in the low half.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack_round2(float a, float b) {
+    if constexpr (F16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// The pre-quant (AWQ) scale applied where an activation piece is loaded:
+// eight activation values (a 16-byte piece, k ascending) times the eight
+// scale values of the same k, each product rounded once to the activation
+// type.  A product of two bf16 values, or of two fp16 values, is exact in
+// fp32, so this is the correctly rounded RNE(X * s) of the definition.
+template <bool F16>
+__device__ __forceinline__ uint4 prescale8(uint4 x, uint4 s) {
+    const uint32_t xd[4] = {x.x, x.y, x.z, x.w}, sd[4] = {s.x, s.y, s.z, s.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float a0, a1;
+        if constexpr (F16) {
+            a0 = act_to_f32<true>(xd[i] & 0xFFFFu) * act_to_f32<true>(sd[i] & 0xFFFFu);
+            a1 = act_to_f32<true>(xd[i] >> 16) * act_to_f32<true>(sd[i] >> 16);
+        } else {
+            a0 = __uint_as_float(xd[i] << 16) * __uint_as_float(sd[i] << 16);
+            a1 = __uint_as_float(xd[i] & 0xFFFF0000u) * __uint_as_float(sd[i] & 0xFFFF0000u);
+        }
+        o[i] = pack_round2<F16>(a0, a1);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // Streaming loads of weight codes and scales: every byte is read exactly
 // once, so the loads are marked non-temporal and do not displace the
 // activations (which are reused) from the caches.

@@ -1,4 +1,4 @@
-// Repack, dequantise (test export) and pre-quant-scale kernels.
+// Repack and dequantise (test export) kernels.
 #pragma once
 #include "decode.h"
 #include "layout.h"
@@ -78,32 +78,6 @@ __global__ void __launch_bounds__(256) k_dequant(BlobView v, int64_t N, int64_t 
             if (k < K) row[k] = (uint16_t)((vd[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
         }
     }
-}
-
-// X'[r][k] = RNE(X[r][k] * s[k]) for r < rows, k < K, eight elements per
-// thread (K is a multiple of 16), in bf16 (fp16 with F16).  The product of
-// two bf16 values, or of two fp16 values (11 x 11 significant bits, exponents
-// within fp32's range), is exact in fp32, so a single rounding to the 16-bit
-// type gives the correctly rounded result.
-template <bool F16 = false>
-__global__ void __launch_bounds__(256) k_prescale(const uint16_t* __restrict__ x, int64_t ld_x,
-                                                  const uint16_t* __restrict__ pre, int64_t rows, int64_t K,
-                                                  uint16_t* __restrict__ out, int64_t ld_out) {
-    const int64_t per_row = K / 8;
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= rows * per_row) return;
-    const int64_t r = t / per_row, k = (t % per_row) * 8;
-    const uint4 xv = *reinterpret_cast<const uint4*>(x + r * ld_x + k);
-    const uint4 sv = *reinterpret_cast<const uint4*>(pre + k);
-    const uint32_t xd[4] = {xv.x, xv.y, xv.z, xv.w}, sd[4] = {sv.x, sv.y, sv.z, sv.w};
-    uint32_t od[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float a0 = act_to_f32<F16>(xd[i] & 0xFFFFu) * act_to_f32<F16>(sd[i] & 0xFFFFu);
-        const float a1 = act_to_f32<F16>(xd[i] >> 16) * act_to_f32<F16>(sd[i] >> 16);
-        od[i] = round_out<F16>(a0) | (round_out<F16>(a1) << 16);
-    }
-    *reinterpret_cast<uint4*>(out + r * ld_out + k) = make_uint4(od[0], od[1], od[2], od[3]);
 }
 
 }  // namespace nvfp4

@@ -5,9 +5,10 @@
 // X and Y are bf16, or fp16 with F16 (the same kernels; weights decode exactly
 // to either type, MFMAs of that type, RNE to it in the epilogue).
 //
-// X' is the activation (already multiplied by the pre-quant scale when one
-// is given).  This file holds the small-M kernel, used for up to 4 rows
-// (the host planner's choice; a pass covers up to 16 rows):
+// X' is the activation, multiplied by the pre-quant scale where each piece
+// is loaded when one is given (PRE; prescale8: RNE(X * s), never written
+// back to memory).  This file holds the small-M kernel, used for up to 4
+// rows (the host planner's choice; a pass covers up to 16 rows):
 //
 // small-M (HBM-bound): one workgroup per 16-row unit
 //   of W, its W waves splitting K.  Each wave streams its K range of the
@@ -78,12 +79,14 @@ __device__ __forceinline__ bool split_arrive(int* counters, int64_t tile, int S,
 // ----------------------------------------------------------------- small-M --
 
 // One chunk's operands for one wave: NT weight code blocks, their scale pairs,
-// and MG activation pieces.
+// MG activation pieces and the pre-quant scale piece of their k (used with
+// PRE only).
 template <int MG, int NT>
 struct SmallSlot {
     uint4 cw[NT];
     uint32_t sw[NT];
     uint4 xa[MG];
+    uint4 pa;
 };
 
 // Scale table in LDS: entry b = {operand for the exponent-only conversion,
@@ -102,13 +105,13 @@ __device__ __forceinline__ void build_scale_table(float2* lut) {
 // always does.  Pieces past K are zeroed here, at use, so that data read
 // from the clamped address cannot reach the sums (the weights there are zero
 // padding, but the activation might not be finite).
-template <int MG, int NT, bool KFULL, bool F16>
+template <int MG, int NT, bool KFULL, bool F16, bool PRE>
 __device__ __forceinline__ void small_m_chunk(const SmallSlot<MG, NT>& s, bool kin, const float2* lut, int lane,
                                               f32x4 (&acc)[NT][MG]) {
     s16x4 alo[MG], ahi[MG];
 #pragma unroll
     for (int mg = 0; mg < MG; ++mg) {
-        const uint4 v = s.xa[mg];
+        const uint4 v = PRE ? prescale8<F16>(s.xa[mg], s.pa) : s.xa[mg];
         if (KFULL) {
             alo[mg] = dwords_to_s16x4(v.x, v.y);
             ahi[mg] = dwords_to_s16x4(v.z, v.w);
@@ -218,11 +221,11 @@ struct WaveWeights {
 // broadcasts A from block q = t >> 1 of each group of four blocks (cbsz = 2,
 // abid = t >> 1).  On return the wave's partial sums, reduced over its four K
 // groups, are in red_w[row * red_ld + col] for rows < 4 MG, cols < 16 NT.
-template <int MG, int NT, int D, bool KFULL, bool F16, typename MidF>
+template <int MG, int NT, int D, bool KFULL, bool F16, bool PRE, typename MidF>
 __device__ __forceinline__ void small_m_pass(const uint16_t* __restrict__ xrow0, int64_t ld_x, int rows,
-                                             const WaveWeights& ww, int c0, int c1, int K, const float2* lut,
-                                             float* red_w, int red_ld, int lane, MidF&& mid,
-                                             const int32_t* __restrict__ rix = nullptr) {
+                                             const uint16_t* __restrict__ pre, const WaveWeights& ww, int c0,
+                                             int c1, int K, const float2* lut, float* red_w, int red_ld, int lane,
+                                             MidF&& mid, const int32_t* __restrict__ rix = nullptr) {
     const int g = lane >> 4, q = (lane >> 2) & 3, ai = lane & 3;
     f32x4 acc[NT][MG];
     uint32_t xoff[MG];   // byte offset of the lane's activation row (row rix[m] of xrow0 when gathering)
@@ -248,8 +251,11 @@ __device__ __forceinline__ void small_m_pass(const uint16_t* __restrict__ xrow0,
         const uint32_t kb = kin(c) ? (uint32_t)((c * kChunkK + kpiece) * 2) : 0u;
 #pragma unroll
         for (int mg = 0; mg < MG; ++mg) s.xa[mg] = *reinterpret_cast<const uint4*>(xb + (xoff[mg] + kb));
+        if constexpr (PRE) s.pa = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(pre) + kb);
     };
-    auto use = [&](const SmallSlot<MG, NT>& s, int i) { small_m_chunk<MG, NT, KFULL, F16>(s, kin(c0 + i), lut, lane, acc); };
+    auto use = [&](const SmallSlot<MG, NT>& s, int i) {
+        small_m_chunk<MG, NT, KFULL, F16, PRE>(s, kin(c0 + i), lut, lane, acc);
+    };
     run_ring<D, SmallSlot<MG, NT>>(c1 - c0, load, use, mid);
 
     // Sum the four K groups: lanes l, l^16, l^32, l^48 hold the same outputs;
@@ -279,12 +285,14 @@ struct Slot16 {
     uint4 cw[NT];
     uint32_t sw[NT];
     uint4 xa[4];
+    uint4 pa[4];   // pre-quant scale pieces (PRE only)
 };
 
-template <int NT, int D, bool KFULL, bool F16, typename MidF>
+template <int NT, int D, bool KFULL, bool F16, bool PRE, typename MidF>
 __device__ __forceinline__ void small_m_pass16(const uint16_t* __restrict__ xrow0, int64_t ld_x, int rows,
-                                               const WaveWeights& ww, int c0, int c1, int K, const float2* lut,
-                                               float* red_w, int red_ld, int lane, MidF&& mid) {
+                                               const uint16_t* __restrict__ pre, const WaveWeights& ww, int c0,
+                                               int c1, int K, const float2* lut, float* red_w, int red_ld, int lane,
+                                               MidF&& mid) {
     const int g = lane >> 4, r = lane & 15;
     f32x4 acc[NT];
 #pragma unroll
@@ -297,16 +305,18 @@ __device__ __forceinline__ void small_m_pass16(const uint16_t* __restrict__ xrow
         ww.load<NT>(s.cw, s.sw, c, lane);
         // pieces past K read k = 0..7 of the row (valid: K >= 16) and are zeroed at use
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            s.xa[t] = *reinterpret_cast<const uint4*>(
-                xb + xoff + (kin(c, t) ? (uint32_t)((c * kChunkK + g * 32 + t * 8) * 2) : 0u));
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t kb = kin(c, t) ? (uint32_t)((c * kChunkK + g * 32 + t * 8) * 2) : 0u;
+            s.xa[t] = *reinterpret_cast<const uint4*>(xb + xoff + kb);
+            if constexpr (PRE) s.pa[t] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(pre) + kb);
+        }
     };
     auto use = [&](const Slot16<NT>& s, int i) {
         const int c = c0 + i;
         uint4 a[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const uint4 v = s.xa[t];
+            const uint4 v = PRE ? prescale8<F16>(s.xa[t], s.pa[t]) : s.xa[t];
             a[t] = kin(c, t) ? v : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
@@ -340,13 +350,14 @@ __device__ __forceinline__ void small_m_pass16(const uint16_t* __restrict__ xrow
 // MG == 0: each pass of up to 16 rows picks one or four row groups (grouped).
 // The first weight loads of a wave are issued before the scale table is
 // built, so the table build and its barrier run under the load latency.
-template <int MG, int NT, int W, int D, bool GROUPED, bool KFULL, bool F16 = false>
+template <int MG, int NT, int W, int D, bool GROUPED, bool KFULL, bool F16 = false, bool PRE = false>
 __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                          int NU, int KC, int K,
                                                          int N, const float* __restrict__ gscale, int g_is_div,
                                                          uint16_t* __restrict__ y, int64_t ld_y, int64_t rows_dense,
                                                          const int32_t* __restrict__ offsets, SplitK sk,
-                                                         const int32_t* __restrict__ row_index) {
+                                                         const int32_t* __restrict__ row_index,
+                                                         const uint16_t* __restrict__ pre) {
     constexpr int RLD = NT * 16;
     constexpr int kTileFloats = kSmallRows * RLD;
     constexpr int kPer = (kTileFloats + W * 64 - 1) / (W * 64);   // partial-tile floats per thread
@@ -394,15 +405,17 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
         const int32_t* rix = GROUPED && row_index ? row_index + row0 + p0 : nullptr;
         const uint16_t* xrow0 = rix ? x : x + (row0 + p0) * ld_x;
         if constexpr (MG == 16) {
-            small_m_pass16<NT, D, KFULL, F16>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane, mid);
+            small_m_pass16<NT, D, KFULL, F16, PRE>(xrow0, ld_x, rows, pre, ww, c0, c1, K, lut, red[w], RLD, lane, mid);
         } else if constexpr (MG > 0) {
-            small_m_pass<MG, NT, D, KFULL, F16>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane, mid);
+            small_m_pass<MG, NT, D, KFULL, F16, PRE>(xrow0, ld_x, rows, pre, ww, c0, c1, K, lut, red[w], RLD, lane,
+                                                     mid);
         } else {
             if (rows <= 4)
-                small_m_pass<1, NT, D, KFULL, F16>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane, mid, rix);
+                small_m_pass<1, NT, D, KFULL, F16, PRE>(xrow0, ld_x, rows, pre, ww, c0, c1, K, lut, red[w], RLD, lane,
+                                                        mid, rix);
             else
-                small_m_pass<4, NT, (D > 2 ? 2 : D), KFULL, F16>(xrow0, ld_x, rows, ww, c0, c1, K, lut, red[w], RLD, lane,
-                                                           mid, rix);
+                small_m_pass<4, NT, (D > 2 ? 2 : D), KFULL, F16, PRE>(xrow0, ld_x, rows, pre, ww, c0, c1, K, lut, red[w],
+                                                                      RLD, lane, mid, rix);
         }
         __syncthreads();
         const float gv = effective_global_scale(gscale[e], g_is_div);

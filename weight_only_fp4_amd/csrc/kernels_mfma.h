@@ -77,14 +77,6 @@ __device__ __forceinline__ void mfma_acc(f32x4& acc, const uint4& a, const uint4
 // than the longest MFMA pipeline).
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
-// fp32 pair -> bf16 (fp16 with F16) pair, round to nearest even (NaN stays
-// NaN), first value in the low half.
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-template <bool F16>
-__device__ __forceinline__ uint32_t pack_out2(float a, float b) {
-    if constexpr (F16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
-    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_t));
-}
 // Exchange rows of 16 lanes between two registers: odd rows of a with even
 // rows of b (lane_swap16), rows 2-3 of a with rows 0-1 of b (lane_swap32).
 __device__ __forceinline__ void lane_swap16(uint32_t& a, uint32_t& b) {
@@ -128,28 +120,42 @@ __device__ __forceinline__ void mfma_tile(int t, int MT, int NTn, int& mt, int& 
 // Work item p (the workgroup id after the XCD remap below) covers part p % P
 // (P = 16 / MS row parts of 16 MS rows) of tile t0 + p / P of the tile order
 // (whole tiles are 256 rows x 256 columns).
-template <int MS, bool KFULL, bool F16 = false>
+//
+// Synchronisation of the asynchronous copies.  Every copy a wave issues is
+// counted by its own vmcnt, in issue order; the wave waits on exact counts
+// derived from the fixed issue schedule of a chunk (below), so nothing it
+// reads from LDS, and nothing another wave reads after the chunk's barrier,
+// can still be in flight, whatever the relative speed of the waves and of
+// other workgroups on the compute unit.  Per chunk c a wave issues, in order:
+// [PRE: the pre-scale chunk of c + 1], its kCopiesPerWave activation copies
+// of chunk c + 1 (groups 0, 2, ..), then the kWCopies weight copies of chunk
+// c + 2 (groups kReadB + 1, kReadB + 2, after the wait at kReadB that retires
+// the weight copies of chunk c + 1).  The barrier wait must retire the
+// activation copies of chunk c + 1: it may leave the weight copies of c + 2
+// in flight only when they were issued before it (tall tiles); with 64-row
+// tiles they go out after the barrier, and the wait must then be for zero
+// (waiting for kWCopies there, as an earlier form of this kernel did, left up
+// to kWCopies activation copies in flight past the barrier, a race whose
+// outcome depends on timing, and so on what else shares the compute unit).
+// The wave drains every copy before it exits, so no copy can land in the LDS
+// of a workgroup that starts on the compute unit after it.
+template <int MS, bool KFULL, bool F16 = false, bool PRE = false>
 __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                         int NU, int KC, int K, int N, const float* __restrict__ gscale,
                                                         int g_is_div, uint16_t* __restrict__ y, int64_t ld_y, int M,
-                                                        int t0, int vec_store) {
+                                                        int t0, int vec_store, const uint16_t* __restrict__ pre) {
     constexpr int NT = kMfmaNT, WN = kMfmaWN;
     constexpr int kRows = 16 * MS;              // rows of this workgroup
     constexpr int kStage = kRows * 256;         // LDS bytes of one staged activation chunk
     constexpr int kParts = kMfmaTileRows / kRows;
     constexpr int kGroups = 4 * MS;             // issue groups per chunk
     constexpr int kAhead = 3;                   // fragment reads in flight
-    static_assert(MS == 8 || MS == 16, "row blocks per wave");
+    static_assert(MS == 4 || MS == 8 || MS == 16, "row blocks per wave");
     __shared__ __attribute__((aligned(16))) uint8_t stage[2][kStage];
     constexpr int kWStage = kMfmaNT * (kCodeBlock + kScaleBlock);   // one chunk of a wave's weights
     __shared__ __attribute__((aligned(16))) uint8_t wstage[kMfmaWN][kWStage];
-    // The asynchronous global -> LDS copies must not share a compute unit
-    // with another workgroup of this kernel: a 64-row variant whose LDS let
-    // two workgroups reside on one compute unit returned wrong outputs
-    // exactly when the grid exceeded the compute-unit count (measured; the
-    // copies of one corrupted the other's staged data).  Every form takes
-    // more than half of the 160 KB of LDS, which leaves room for one.
-    static_assert(2 * kStage + kMfmaWN * kWStage > 80 * 1024, "one workgroup per compute unit");
+    // PRE: the 128 pre-quant scale values (256 bytes) of the chunk being staged, per wave
+    __shared__ __attribute__((aligned(16))) uint8_t pstage[PRE ? kMfmaWN : 1][PRE ? 2 * kChunkK : 16];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
@@ -191,6 +197,27 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     auto copy_a = [&](int c, int buf) {
 #pragma unroll
         for (int k = 0; k < kCopiesPerWave; ++k) copy_piece(c, buf, k);
+    };
+    // PRE: the pre-scale values of chunk c (clamped to the last chunk) into this
+    // wave's slice, lane l taking elements 2 l, 2 l + 1; elements at k >= K read
+    // k = 0 (their activation pieces are zeroed after the scaling).
+    const uint8_t* pb = PRE ? uniform_ptr(reinterpret_cast<const uint8_t*>(pre)) : nullptr;
+    auto copy_p = [&](int c) {
+        const int k = (c < KC ? c : KC - 1) * kChunkK + 2 * lane;
+        lds_copy4(lds_addr(pstage[w]), pb, (uint32_t)((KFULL || k < K ? k : 0) * 2));
+    };
+    // PRE: X' = RNE(X * s) in place on the pieces this lane copied into stage
+    // buf (its copies, and the pre-scale copy issued before them, must have
+    // landed).  All of a lane's pieces lie in one k slot: copy i = w + 4 k
+    // holds row 4 i + (lane >> 4), whose row & 15 is 4 w + (lane >> 4).
+    const int kslot = q ^ ((4 * w + (lane >> 4)) & 15);
+    auto rescale_a = [&](int buf) {
+        const uint4 sp = *reinterpret_cast<const uint4*>(pstage[w] + kslot * 16);
+#pragma unroll
+        for (int k = 0; k < kCopiesPerWave; ++k) {
+            uint4* pc = reinterpret_cast<uint4*>(stage[buf] + (w + WN * k) * 1024 + lane * 16);
+            *pc = prescale8<F16>(*pc, sp);
+        }
     };
     // Zero the staged pieces of the last chunk that lie at k >= K (their
     // copies read k = 0 of the row).  Thread t zeroes slot t & 15 of row
@@ -316,31 +343,44 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     // scheduling fence.  VALU work: in steps 0..2 the decode of step t + 1
     // (16 / MS dwords per group); in step 3 the next chunk's scales (group 0)
     // and its step-0 decode (groups 1 .. MS - 1).
+    // The copy schedule of a chunk (see the synchronisation note above).
+    constexpr int kWCopies = NT + NT / 2;                 // weight copies per chunk
+    constexpr int kReadB = 3 * MS;                        // group reading chunk c + 1's weights into registers
+    constexpr bool kWBeforeBarrier = kReadB + 2 < kGroups - kAhead;   // chunk c + 2's weight copies precede the barrier
+    constexpr int kBarrierWait = kWBeforeBarrier ? kWCopies : 0;      // copies allowed in flight at the barrier
+    static_assert(2 * (kCopiesPerWave - 1) < kReadB, "a chunk's activation copies go out before its weights are read");
+
     auto group = [&](auto fc, int c, int buf, BRegs& b) {
         constexpr int f = decltype(fc)::value, t = f / MS, ms = f % MS;
         if constexpr (f + kAhead < kGroups) af[(f + kAhead) % kRing] = frag(buf, f + kAhead);
         // The activation copies of chunk c + 1 (into the other stage, free
         // since the last barrier) go out on every second group of the first
         // half, unconditionally (past the last chunk they repeat it into a
-        // stage nothing reads; a branch per group cost more than the traffic).
+        // stage nothing reads; a branch per group cost more than the traffic),
+        // after the copy of that chunk's pre-scale values (PRE).
+        if constexpr (PRE && f == 0) copy_p(c + 1);
         if constexpr (f % 2 == 0 && f / 2 < kCopiesPerWave) copy_piece(c + 1 < KC ? c + 1 : KC - 1, buf ^ 1, f / 2);
-        // Step 3: the weights of chunk c + 1 (copied a chunk ago; the 16
-        // activation copies issued since may still fly) replace chunk c's in
-        // registers, then the slice takes the copies of chunk c + 2.
-        if constexpr (f == 3 * MS) {
+        // Step 3: the weights of chunk c + 1 (copied a chunk ago; only the
+        // copies issued since, this chunk's activation copies, may still fly)
+        // replace chunk c's in registers, then the slice takes the copies of
+        // chunk c + 2.
+        if constexpr (f == kReadB) {
             wait_vmcnt<kCopiesPerWave>();
             read_b(b);
         }
-        if constexpr (f == 3 * MS + 1) {
+        if constexpr (f == kReadB + 1) {
             wait_lgkmcnt0();
             copy_b_codes(c + 2);
         }
-        if constexpr (f == 3 * MS + 2) copy_b_scales(c + 2);
+        if constexpr (f == kReadB + 2) copy_b_scales(c + 2);
         uint4* bf = (t & 1) ? bfb : bfa;
         uint4* nb = (t & 1) ? bfa : bfb;
         constexpr int d_lo = t < 3 ? ms * 16 / MS : (ms == 0 ? 0 : ((ms - 1) * 16 + MS - 2) / (MS - 1));
         constexpr int d_hi = t < 3 ? (ms + 1) * 16 / MS : (ms == 0 ? 0 : (ms * 16 + MS - 2) / (MS - 1));
-        DwordJob jobs[4];
+        // dwords decoded in this group: 16 / MS in steps 0..2, up to ceil(16 / (MS - 1)) in step 3 (6 with
+        // 64-row tiles)
+        constexpr int kJobs = d_hi - d_lo > 0 ? d_hi - d_lo : 1;
+        DwordJob jobs[kJobs];
         static_for<0, NT>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             mfma_acc<F16>(acc[ms][j], bf[j], af[f % kRing]);
@@ -363,14 +403,17 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
 
     // One chunk on stage buf; b holds its weights until step 3, then the
     // next chunk's.  After group kGroups - 4 the wave waits for its
-    // activation copies of chunk c + 1 (the weight copies of chunk c + 2,
-    // issued after them, may still fly) and meets the others at the barrier;
-    // then it reads the first fragments of chunk c + 1 and runs the last
-    // three groups, whose fragments are already in registers.
-    constexpr int kWCopies = NT + NT / 2;   // weight copies per chunk
+    // activation copies of chunk c + 1 (the weight copies of chunk c + 2 may
+    // still fly if they were issued before this point), scales its own
+    // pieces of them (PRE), zeroes their part past K, and meets the others at
+    // the barrier; then it reads the first fragments of chunk c + 1 and runs
+    // the last three groups, whose fragments are already in registers.
     auto chunk = [&](int c, int buf, BRegs& b) {
         static_for<0, kGroups - kAhead>([&](auto fc) { group(fc, c, buf, b); });
-        wait_vmcnt<kWCopies>();
+        wait_vmcnt<kBarrierWait>();
+        if constexpr (PRE) {
+            if (c + 1 < KC) rescale_a(buf ^ 1);
+        }
         if (!KFULL && c + 1 == KC - 1) zero_tail(buf ^ 1);
         wait_lgkmcnt0();
         asm volatile("s_barrier" ::: "memory");
@@ -386,10 +429,12 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
 
     // ---- pipeline: chunk c on stage c & 1
     BRegs b;
+    if constexpr (PRE) copy_p(0);
     copy_a(0, 0);
     copy_b_codes(0);
     copy_b_scales(0);
     __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (PRE) rescale_a(0);
     if (!KFULL && KC == 1) zero_tail(0);
     __syncthreads();
     read_b(b);
@@ -403,6 +448,7 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     });
     static_for<0, kAhead>([&](auto fc) { af[decltype(fc)::value] = frag(0, decltype(fc)::value); });
     for (int c = 0; c < KC; ++c) chunk(c, c & 1, b);
+    wait_vmcnt<0>();   // the last chunk's clamped copies: none may land after the workgroup ends
     mfma_drain();
 
     // ---- epilogue: lane (r, g) holds, for row 16 ms + r, the four columns
@@ -416,8 +462,8 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
         uint32_t pk[NT][2];   // bf16 pairs of columns 4 g + 2 d, + 1 of unit j (then of unit g: 4 j + 2 d)
         static_for<0, NT>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
-            pk[j][0] = pack_out2<F16>(gv * acc[ms][j][0], gv * acc[ms][j][1]);
-            pk[j][1] = pack_out2<F16>(gv * acc[ms][j][2], gv * acc[ms][j][3]);
+            pk[j][0] = pack_round2<F16>(gv * acc[ms][j][0], gv * acc[ms][j][1]);
+            pk[j][1] = pack_round2<F16>(gv * acc[ms][j][2], gv * acc[ms][j][3]);
         });
 #pragma unroll
         for (int d = 0; d < 2; ++d) {

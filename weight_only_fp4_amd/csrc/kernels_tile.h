@@ -21,6 +21,10 @@
 //   reproducible), applies the epilogue and resets the counter to zero for
 //   the next call.
 //
+//   With PRE the pre-quant scale multiplies each activation piece as it is
+//   written into the LDS stage (prescale8: RNE(X * s), once per workgroup and
+//   piece, never written back to memory).
+//
 //   Grouped (MoE) form: grid y has R/BM + E row-tile slots, mapped to
 //   (expert, tile) by a wave-wide prefix scan of the per-expert tile counts
 //   read from expert_offsets; surplus slots exit before touching weights.
@@ -34,13 +38,14 @@ namespace nvfp4 {
 constexpr int kTileLDA = 136;   // bf16 per LDS row of the activation stage (128 + 8 pad)
 
 
-template <int MS, int NT, int UW, int KW, int D, bool GROUPED, bool KFULL, bool F16 = false>
+template <int MS, int NT, int UW, int KW, int D, bool GROUPED, bool KFULL, bool F16 = false, bool PRE = false>
 __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                             int NU, int KC, int K, int N,
                                                             const float* __restrict__ gscale, int g_is_div,
                                                             uint16_t* __restrict__ y, int64_t ld_y, int64_t rows_dense,
                                                             const int32_t* __restrict__ offsets, int E, SplitK sk,
-                                                            const int32_t* __restrict__ row_index) {
+                                                            const int32_t* __restrict__ row_index,
+                                                            const uint16_t* __restrict__ pre) {
     constexpr int W = UW * KW;                                     // waves per workgroup
     // Weights stream past the caches (non-temporal) when one row tile covers
     // all rows (tiles of up to 32 rows, dense): no other workgroup reads the
@@ -150,6 +155,7 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
         uint4 cw[NT];
         uint32_t sw[NT];
         uint4 a[APT];
+        uint4 pa[APT];   // pre-quant scale pieces of the activation pieces' k (PRE only)
     };
     const int w_last = len > 0 ? len - 1 : 0;
     auto load_slot = [&](Slot& b, int step) {
@@ -171,7 +177,9 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
         for (int i = 0; i < APT; ++i) {
             const int ca = a_c0[i] + (step < a_last[i] ? step : a_last[i]);
             const int k = ca * kChunkK + (int)((tid + i * W * 64) & 15) * 8;
-            b.a[i] = *reinterpret_cast<const uint4*>(xtile + a_xo[i] + (uint32_t)(KFULL || k < K ? k : 0));
+            const uint32_t kk = (uint32_t)(KFULL || k < K ? k : 0);
+            b.a[i] = *reinterpret_cast<const uint4*>(xtile + a_xo[i] + kk);
+            if constexpr (PRE) b.pa[i] = *reinterpret_cast<const uint4*>(pre + kk);
         }
     };
     auto store_a = [&](int buf, const Slot& b, int step) {
@@ -181,7 +189,7 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
             if (APIECES % (W * 64) != 0 && p >= APIECES) break;
             const int ca = a_c0[i] + (step < a_last[i] ? step : a_last[i]);
             const bool kin = KFULL || (ca * kChunkK + (p & 15) * 8 < K);
-            const uint4 v = b.a[i];
+            const uint4 v = PRE ? prescale8<F16>(b.a[i], b.pa[i]) : b.a[i];
             *reinterpret_cast<uint4*>(&As[buf * kStage + a_off[i]]) =
                 make_uint4(kin ? v.x : 0u, kin ? v.y : 0u, kin ? v.z : 0u, kin ? v.w : 0u);
         }

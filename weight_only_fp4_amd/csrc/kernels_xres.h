@@ -24,7 +24,9 @@
 //
 //   K slots of an MFMA step map to k = 32 g + 8 t + e (lane group g, step t,
 //   element e) on both operands, as in the tile kernel, so a weight lane reads
-//   one 32-wide K group of the repacked layout.  Activation rows past `rows`
+//   one 32-wide K group of the repacked layout.  With PRE the pre-quant
+//   scale is applied to each activation piece (prescale8) as the slice is
+//   staged, once per wave.  Activation rows past `rows`
 //   and K pieces past K are zero (never loaded); units past NU read unit
 //   NU - 1 and store nothing.  FULL (K == 128 S W CH: every wave owns CH whole
 //   chunks) compiles without any per-chunk condition; otherwise chunks past
@@ -40,11 +42,11 @@ namespace nvfp4 {
 constexpr int kXresRowBytes = 256 + 16;                // one row of a staged chunk, padded
 constexpr int kXresWaveBytes = 16 * kXresRowBytes;     // a wave's staging area
 
-template <int CH, int U, int W, int D, bool FULL, bool F16 = false>
+template <int CH, int U, int W, int D, bool FULL, bool F16 = false, bool PRE = false>
 __global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                       int NU, int KC, int K, int N, const float* __restrict__ gscale,
                                                       int g_is_div, uint16_t* __restrict__ y, int64_t ld_y, int rows,
-                                                      SplitK sk) {
+                                                      SplitK sk, const uint16_t* __restrict__ pre) {
     constexpr int NI = U * CH;          // ring items of a wave: (unit, chunk), unit-major
     constexpr int H = W / 2;            // waves after the first reduction stage
     constexpr int TILE = U * 256;       // fp32 outputs of the workgroup (16 rows x 16 U columns)
@@ -80,6 +82,7 @@ __global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict
     // ---- activation chunk c of the slice, coalesced: load i takes rows
     // 4 i + (lane >> 4), bytes 16 (lane & 15) of the chunk's 256 per row
     uint4 xa[CH][4];
+    uint4 pa[CH];   // pre-quant scale piece of the lane's k (PRE only; the same for its four rows)
     auto load_x = [&](int c) {
         const int k = (c0 + c) * kChunkK + (lane & 15) * 8;
 #pragma unroll
@@ -88,6 +91,7 @@ __global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict
             xa[c][i] = (row < rows && (FULL || k < K)) ? *reinterpret_cast<const uint4*>(x + (int64_t)row * ld_x + k)
                                                        : make_uint4(0u, 0u, 0u, 0u);
         }
+        if constexpr (PRE) pa[c] = *reinterpret_cast<const uint4*>(pre + (FULL || k < K ? k : 0));
     };
     // through this wave's LDS area into the A-operand layout: lane (r, g)
     // takes X[r][128 c + 32 g + 8 t + 0..7] (row stride = 16 mod 256 bytes:
@@ -98,7 +102,8 @@ __global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict
     auto stage_x = [&](int c) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4*>(mine + (4 * i + (lane >> 4)) * kXresRowBytes + (lane & 15) * 16) = xa[c][i];
+            *reinterpret_cast<uint4*>(mine + (4 * i + (lane >> 4)) * kXresRowBytes + (lane & 15) * 16) =
+                PRE ? prescale8<F16>(xa[c][i], pa[c]) : xa[c][i];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
             xr[c][t] = *reinterpret_cast<const uint4*>(mine + r * kXresRowBytes + g * 64 + t * 16);

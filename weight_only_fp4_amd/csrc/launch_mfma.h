@@ -1,7 +1,7 @@
-// Host launcher of the MFMA-bound dense kernel (kernels_mfma.h).  It lives
-// in its own translation unit, built without the register-form flag of the
-// other kernels' unit (this kernel keeps its accumulators in the
-// accumulation registers).
+// Host launcher of the MFMA-bound dense kernel (kernels_mfma.h).  Its
+// kernels live in their own translation units (gemm_mfma.hip), built without
+// the register-form flag of the other kernels' units (this kernel keeps its
+// accumulators in the accumulation registers).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -10,8 +10,9 @@
 
 namespace nvfp4 {
 
-// Rows of one whole output tile of the MFMA-bound kernel (256 x 256).
+// One whole output tile of the MFMA-bound kernel: 256 rows x 16 units (256 columns).
 constexpr int kMfmaRows = 256;
+constexpr int kMfmaTileUnits = 16;
 
 // Work split of one call: `tiles` output tiles; the first t_full run as whole
 // tiles, the rest as two half-height workgroups each.
@@ -20,12 +21,21 @@ struct MfmaPlan {
 };
 MfmaPlan mfma_plan(const Layout& L, int64_t M);
 
-// Launches Y[M, N] = g * X[M, K] . dequant(W)^T on `st` (dense, E = 1) with
-// the work split of `plan` (at most two kernel launches); X and Y are bf16,
-// or fp16 when f16.  Arguments are checked by the caller; returns the launch
-// status.
+// Launches Y[M, N] = g * (X[M, K] (.) pre) . dequant(W)^T on `st` (dense,
+// E = 1) with the work split of `plan` (at most two kernel launches); X, pre
+// and Y are bf16, or fp16 when f16; pre may be NULL.  quarter: every tile
+// runs as four 64-row workgroups instead (one launch; several workgroups
+// share a compute unit).  Arguments are checked by the caller; returns the
+// launch status.
 hipError_t launch_gemm_mfma(const MfmaPlan& plan, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
-                            const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t M, hipStream_t st,
-                            bool f16);
+                            const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t M, const uint16_t* pre,
+                            bool quarter, hipStream_t st, bool f16);
+
+// The launch of one activation type (F16) and pre-scale form (PRE), defined
+// in the gemm_mfma.hip unit compiled for that form.
+template <bool F16, bool PRE>
+hipError_t launch_mfma_t(const MfmaPlan& plan, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
+                         const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t M, const uint16_t* pre,
+                         bool quarter, hipStream_t st);
 
 }  // namespace nvfp4

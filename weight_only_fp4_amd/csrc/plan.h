@@ -1,0 +1,231 @@
+// Host-side planning shared by the library's translation units: the launch
+// shape of each GEMM kernel family (pure functions of the call's sizes, so
+// the workspace queries reproduce them), the arguments every GEMM launch
+// takes, and the launchers that each family's translation units define
+// (one unit per kernel family and activation type, compiled in parallel).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/nvfp4_w4a16.h"
+#include "kernels_gemm.h"
+#include "layout.h"
+
+namespace nvfp4 {
+
+// Error reporting (nvfp4_w4a16.hip): the message of the last failed call on
+// this thread, returned by nvfp4_last_error().
+nvfp4_status fail(nvfp4_status st, const char* fmt, ...);
+nvfp4_status ok();
+nvfp4_status launched(const char* what);   // HIP status of the last launch
+
+inline int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Everything a GEMM launch needs besides its shape.  rows: dense row count
+// (unused by the grouped forms, which read expert_offsets on the device).
+struct GemmArgs {
+    const uint16_t* x;
+    int64_t ld_x;
+    const uint8_t* blob;
+    const float* gs;
+    int g_div;
+    uint16_t* y;
+    int64_t ld_y;
+    int64_t rows;
+    const int32_t* offsets;     // grouped forms: expert_offsets [E + 1]
+    const int32_t* row_index;   // grouped forms: row r reads activation row row_index[r] (or NULL)
+    const uint16_t* pre;        // pre-quant scale [K] or NULL
+    SplitK sk;
+    hipStream_t st;
+};
+
+// ---------------------------------------------------------------- small-M --
+// Small-M launch shape: row form mg (1, 2: 4x4x4 with that many row groups;
+// 16: 16x16x32), nt units per wave, w waves per workgroup, ring depth d, and
+// K splits S across workgroups (dense only).  Only the (mg, nt, w, d) tuples
+// listed in NVFP4_SMALL_CONFIGS are compiled.
+struct SmallShape {
+    int mg, nt, w, d, S;
+    int64_t groups;   // workgroups along N (units / nt)
+};
+
+// (mg, nt, w, d) for the dense form; the grouped form is always (0, 1, w, 4).
+#define NVFP4_SMALL_CONFIGS(X) \
+    X(1, 1, 1, 4) X(1, 1, 2, 4) X(1, 1, 4, 4) X(1, 1, 8, 4) X(1, 1, 16, 4) \
+    X(2, 1, 1, 4) X(2, 1, 2, 4) X(2, 1, 4, 4) X(2, 1, 8, 4) X(2, 2, 2, 4) X(2, 2, 4, 4) X(2, 2, 8, 4) \
+    X(16, 2, 4, 2) X(16, 2, 8, 2) X(16, 4, 4, 2) X(16, 4, 8, 2) X(16, 8, 4, 2) X(16, 8, 8, 2)
+
+// Is (mg, nt, w, d) one of the compiled dense shapes?
+inline bool small_compiled(const SmallShape& s) {
+    bool found = false;
+#define NVFP4_SMALL_FIND(MG, NT, W, D) found = found || (s.mg == MG && s.nt == NT && s.w == W && s.d == D);
+    NVFP4_SMALL_CONFIGS(NVFP4_SMALL_FIND)
+#undef NVFP4_SMALL_FIND
+    return found;
+}
+
+// Shapes from launch sweeps on MI355X (graph-replayed, weights rotated past
+// the Infinity Cache).  Rows <= 8: one unit per wave, waves sized so the
+// workgroups x waves x ring depth product aims at about 32 KB of weight
+// loads in flight per CU.  Rows 9..16 (16x16x32 form, about two VALU
+// operations per weight to decode) share each activation fragment over four
+// units per wave; the automatic choice sends those rows to the
+// activation-resident kernel.
+inline SmallShape small_m_shape(const Layout& L, int64_t rows, bool grouped) {
+    SmallShape s;
+    s.S = 1;
+    if (grouped) {
+        s.mg = 0; s.nt = 1; s.d = 4;
+    } else if (rows <= 8) {
+        s.mg = rows <= 4 ? 1 : 2; s.nt = 1; s.d = 4;
+    } else {
+        s.mg = 16; s.nt = 4; s.d = 2; s.w = 4;
+    }
+    s.groups = (L.NU + s.nt - 1) / s.nt;
+    if (s.mg == 16) {
+        // a K split costs a device-scope publish / count / reload round trip
+        // at the end of the kernel: split only grids that fill under half
+        // of the CUs
+        while (s.S < 8 && s.groups * s.S < 128 && L.KC >= 2 * s.w * 2 * s.S) s.S *= 2;
+        return s;
+    }
+    const int64_t ctas = s.groups * (grouped ? (L.E + 1) / 2 : 1);
+    s.w = 1;
+    // 16 waves cap a kernel at 128 VGPRs: only the one-row-group form fits
+    const int wmax = s.mg == 1 ? 16 : 8;
+    while (s.w < wmax && ctas * (2 * s.w) * s.d <= 8192 && L.KC >= 4 * (2 * s.w)) s.w *= 2;
+    if (s.w < 2 && L.KC >= 8) s.w = 2;
+    while (!grouped && s.w > 1 && !small_compiled(s)) s.w /= 2;
+    return s;
+}
+
+// ------------------------------------------------------------------- tile --
+// Tile shapes by row count, from launch-shape sweeps on MI355X: the fastest
+// decode-sized shapes run about one 16-wave workgroup per CU, four unit-waves
+// times four k-parts.  K is further split across workgroups (grid z) while
+// the workgroup count stays at or below 256 and every wave keeps >= 2
+// chunks.
+struct TileShape {
+    int ms, nt, uw, kw, d, S;
+    int64_t groups, mtiles;
+    int64_t tiles() const { return groups * mtiles; }
+    int bm() const { return 16 * ms; }
+    int ug() const { return nt * uw; }
+};
+
+inline TileShape tile_shape(const Layout& L, int64_t rows, bool grouped) {
+    TileShape t;
+    bool split = true;
+    if (grouped) {
+        t.ms = 4; t.nt = 4; t.uw = 4; t.kw = 1; t.d = 2; split = false;
+    } else if (rows <= 16) {
+        t.ms = 1; t.nt = 1; t.uw = 4; t.kw = 4; t.d = 2;
+    } else if (rows <= 32) {
+        t.ms = 2; t.nt = 1; t.uw = 4; t.kw = 2; t.d = 4;
+    } else if (rows <= 192) {
+        // 64-row tiles: up to three row tiles still beat 128-row tiles here
+        // (measured); wide N (LM heads) takes 512 columns per workgroup with
+        // a 3-deep weight ring
+        if (L.NU >= 4096) { t.ms = 4; t.nt = 4; t.uw = 8; t.kw = 1; t.d = 3; }
+        else { t.ms = 4; t.nt = 1; t.uw = 4; t.kw = 4; t.d = 2; }
+    } else {
+        t.ms = 8; t.nt = 2; t.uw = 8; t.kw = 1; t.d = 2;
+    }
+    t.groups = (L.NU + t.ug() - 1) / t.ug();
+    t.mtiles = (rows + t.bm() - 1) / t.bm() + (grouped ? L.E : 0);
+    t.S = 1;
+    while (split && t.S < 16 && t.tiles() * 2 * t.S <= 256 && L.KC >= 2 * t.kw * (2 * t.S)) t.S *= 2;
+    return t;
+}
+
+// ---------------------------------------------------- activation-resident --
+// (ch, u, w, d): chunks per wave, units per workgroup, waves, ring depth.
+// From launch sweeps on MI355X (graph-replayed, weights rotated past the
+// Infinity Cache): 16 waves with a 2-deep ring for K up to 4096, the
+// workgroup count near the CU count (u = ceil(row units / 256)).
+#define NVFP4_XRES_CONFIGS(X) \
+    X(1, 1, 16, 2) X(1, 2, 16, 2) X(1, 3, 16, 2) X(1, 4, 16, 2) X(1, 5, 16, 2) X(1, 6, 16, 2) X(1, 7, 16, 2) \
+    X(1, 8, 16, 2) X(2, 1, 16, 2) X(2, 2, 16, 2) X(2, 3, 16, 2) X(2, 4, 16, 2) X(2, 5, 16, 2) X(2, 6, 16, 2) \
+    X(2, 7, 16, 2) X(2, 8, 16, 2)
+
+// Rows from which the automatic choice takes the activation-resident kernel
+// (below it the small-M kernel, measured faster at one row).
+constexpr int64_t kXresAutoMin = 5;
+constexpr int kXresMaxSplits = 8;
+
+struct XresShape {
+    int ch, u, w, d, S;
+    int64_t groups;
+};
+
+inline bool xres_compiled(const XresShape& s) {
+    bool found = false;
+#define NVFP4_XRES_FIND(CH, U, W, D) found = found || (s.ch == CH && s.u == U && s.w == W && s.d == D);
+    NVFP4_XRES_CONFIGS(NVFP4_XRES_FIND)
+#undef NVFP4_XRES_FIND
+    return found;
+}
+
+// 16 waves own one or two chunks each; K beyond 32 chunks is split S ways
+// across workgroups; units per workgroup by N and S, so that the grid is
+// about one workgroup per CU.  A shape outside the compiled set means the
+// kernel does not take the call (K above 8 splits, or too many row units).
+inline XresShape xres_shape(const Layout& L) {
+    XresShape s{L.KC <= 16 ? 1 : 2, 0, 16, 2, 1, 0};
+    s.S = (int)((L.KC + 31) / 32);
+    const int64_t u = (L.NU * s.S + 255) / 256;
+    s.u = (int)(u < 1 ? 1 : u > 64 ? 64 : u);
+    s.groups = (L.NU + s.u - 1) / s.u;
+    return s;
+}
+
+// Does the activation-resident kernel take this dense call?  (M <= 16,
+// K <= 32768, and ceil(N / 16) * ceil(K / 4096) <= 2048.)
+inline bool xres_fits(const Layout& L, int64_t rows) {
+    const XresShape s = xres_shape(L);
+    return rows <= kSmallRows && s.S <= kXresMaxSplits && (int64_t)s.S * s.w * s.ch >= L.KC && xres_compiled(s) &&
+           s.groups <= 65535;
+}
+
+// -------------------------------------------------------------- workspace --
+// Byte offsets in the caller's workspace: split-K counters (must be zero
+// before the first call; every call leaves them zero) and split-K partials.
+// A call without a K split needs no workspace.
+struct Workspace {
+    int64_t counters, partials, total;
+};
+
+// split_tiles tiles of tile_floats fp32 each, S splits (no split-K area when S == 1).
+inline Workspace workspace_layout(int S, int64_t split_tiles, int64_t tile_floats) {
+    Workspace w{0, 0, 0};
+    if (S > 1) {
+        w.counters = 0;
+        w.partials = round_up(split_tiles * 4, 256);
+        w.total = w.partials + round_up((int64_t)S * split_tiles * tile_floats * 4, 256);
+    }
+    return w;
+}
+
+inline Workspace workspace_for(const TileShape& t) {
+    return workspace_layout(t.S, t.tiles(), (int64_t)t.bm() * t.ug() * 16);
+}
+inline Workspace workspace_for(const SmallShape& s) {
+    return workspace_layout(s.S, s.groups, (int64_t)kSmallRows * 16 * s.nt);
+}
+inline Workspace workspace_for(const XresShape& s) { return workspace_layout(s.S, s.groups, (int64_t)s.u * 256); }
+
+inline SplitK split_k(int S, uint8_t* ws, const Workspace& wl) {
+    return SplitK{S, S > 1 ? reinterpret_cast<float*>(ws + wl.partials) : nullptr,
+                  S > 1 ? reinterpret_cast<int*>(ws + wl.counters) : nullptr};
+}
+
+// ---------------------------------------------------------------- launchers --
+// One translation unit per family and activation type (F16) defines each.
+template <bool F16>
+nvfp4_status launch_small(const SmallShape& s, const Layout& L, const GemmArgs& a, bool grouped);
+template <bool F16>
+nvfp4_status launch_tile(const TileShape& t, const Layout& L, const GemmArgs& a, bool grouped);
+template <bool F16>
+nvfp4_status launch_xres(const XresShape& s, const Layout& L, const GemmArgs& a);
+
+}  // namespace nvfp4
