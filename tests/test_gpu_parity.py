@@ -357,6 +357,22 @@ def test_zero_sizes_return_ok_and_write_nothing():
     assert tuple(nv.gemm(d.x[:0], d.blob, c.N, c.K, d.g).shape) == (0, c.N)
 
 
+def test_one_workspace_serves_calls_of_any_shape():
+    """One workspace, zero-filled once, shared by split-K calls of different shapes in a row (the later calls with
+    more split tiles, whose counters would sit where earlier calls left partial sums if the counters did not have
+    their own fixed prefix): every result is bitwise that of the call with a fresh workspace."""
+    say("workspace reuse across shapes")
+    shapes = [(16, 4096, 14336, nv.VARIANT_AUTO), (16, 16384, 8192, nv.VARIANT_AUTO), (1, 2048, 4096, nv.VARIANT_AUTO),
+              (24, 2000, 4096, nv.VARIANT_LARGE_M), (16, 4096, 14336, nv.VARIANT_LARGE_M), (8, 2064, 8192, nv.VARIANT_AUTO)]
+    ws = nv.workspace(max(nv.gemm_workspace_bytes(M, N, K) for M, N, K, _ in shapes), DEV)
+    for rnd in range(2):
+        for i, (M, N, K, v) in enumerate(shapes):
+            d = DenseDev(synth.dense_case(M, N, K, seed=4000 + i))
+            fresh = d.run(v)
+            shared = nv.gemm_variant(d.x, d.blob, N, K, d.g, False, None, workspace_buf=ws, variant=v)
+            assert torch.equal(shared, fresh), (rnd, M, N, K, v)
+
+
 @pytest.mark.parametrize("M,N,K", [(5, 14336, 4096), (8, 14336, 4096), (16, 14336, 4096), (16, 4096, 14336),
                                    (12, 2000, 3968)])
 def test_automatic_choice_runs_the_resident_kernel_for_5_to_16_rows(M, N, K):

@@ -154,9 +154,23 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
         return fail(NVFP4_ERR_INVALID_ARG, "%s: the MFMA-bound variant takes weights below 2 GiB of codes", fn);
     const int v = empty ? kAuto : variant == kAuto ? dense_auto_variant(L, M) : variant;
     Workspace wl{0, 0, 0};
-    if (v == kResident) wl = workspace_for(xres_shape(L));
-    else if (v == kSmall) wl = workspace_for(small_m_shape(L, M, false));
-    else if (v == kLarge) wl = workspace_for(tile_shape(L, M, false));
+    int64_t split_tiles = 0;
+    if (v == kResident) {
+        const XresShape xs = xres_shape(L);
+        wl = workspace_for(xs);
+        split_tiles = xs.S > 1 ? xs.groups : 0;
+    } else if (v == kSmall) {
+        const SmallShape sm = small_m_shape(L, M, false);
+        wl = workspace_for(sm);
+        split_tiles = sm.S > 1 ? sm.groups : 0;
+    } else if (v == kLarge) {
+        const TileShape t = tile_shape(L, M, false);
+        wl = workspace_for(t);
+        split_tiles = t.S > 1 ? t.tiles() : 0;
+    }
+    if (split_tiles > kMaxSplitTiles)   // the planners never split grids this large
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: %lld split-K tiles exceed the %lld counters of a workspace", fn,
+                    (long long)split_tiles, (long long)kMaxSplitTiles);
     s = check_gemm_io(fn, x, ld_x, pre, w, gs, y, ld_y, M, N, K, ws, ws_bytes, wl.total);
     if (s != NVFP4_OK) return s;
     if (empty) return ok();   // zero rows or zero columns: nothing is launched

@@ -188,19 +188,25 @@ inline bool xres_fits(const Layout& L, int64_t rows) {
 }
 
 // -------------------------------------------------------------- workspace --
-// Byte offsets in the caller's workspace: split-K counters (must be zero
-// before the first call; every call leaves them zero) and split-K partials.
-// A call without a K split needs no workspace.
+// Byte offsets in the caller's workspace: split-K arrival counters, then
+// split-K partials.  The counters take a fixed prefix of kMaxSplitTiles
+// entries, whatever the call, so that no call's partials overlap any call's
+// counters: every call leaves the counters it used at zero, so a workspace
+// (zero-filled once) can serve calls of any shapes one after another.  A
+// call without a K split needs no workspace.
+constexpr int64_t kMaxSplitTiles = 1024;
+
 struct Workspace {
     int64_t counters, partials, total;
 };
 
-// split_tiles tiles of tile_floats fp32 each, S splits (no split-K area when S == 1).
+// split_tiles tiles of tile_floats fp32 each, S splits (no split-K area when
+// S == 1).  The planners split only grids of at most a few hundred tiles.
 inline Workspace workspace_layout(int S, int64_t split_tiles, int64_t tile_floats) {
     Workspace w{0, 0, 0};
     if (S > 1) {
         w.counters = 0;
-        w.partials = round_up(split_tiles * 4, 256);
+        w.partials = kMaxSplitTiles * 4;
         w.total = w.partials + round_up((int64_t)S * split_tiles * tile_floats * 4, 256);
     }
     return w;
