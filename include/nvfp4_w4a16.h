@@ -264,6 +264,30 @@ int nvfp4_w4a16_gemm_plan(int64_t M, int64_t N, int64_t K);
  * pure host function of the sizes. */
 int nvfp4_w4a16_gemm_variant_takes(int64_t M, int64_t N, int64_t K, int variant);
 
+/* ------------------------------------------------- no-allocation entry --
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  nvfp4_w4a16_gemm without the workspace arguments: the split-K
+ * partial sums and arrival counters that some shapes need live in a static
+ * device array of the library, nvfp4_w4a16_gemm_noalloc_max_scratch_bytes()
+ * bytes (4 MiB) on every GPU the library runs on, held until the process
+ * ends.  The call allocates nothing (no hipMalloc, no allocating library
+ * routine); the caller still passes the inputs and the output.  The first
+ * call on a device looks up the array's device address and clears its
+ * counters on `stream` (a fill kernel); every call leaves the counters it
+ * used at zero.  All calls on one GPU share that GPU's array: calls that may
+ * overlap in time on one GPU (other streams, other threads) race and give
+ * undefined results; issue them one after another.
+ * Arguments, kernel choice, results (bitwise those of nvfp4_w4a16_gemm) and
+ * errors as for nvfp4_w4a16_gemm, plus: a call whose kernel needs more
+ * scratch than the array holds (nvfp4_w4a16_gemm_workspace_bytes above the
+ * maximum) -> BUFFER_TOO_SMALL, before anything is launched; the address
+ * lookup failing -> HIP. */
+int64_t nvfp4_w4a16_gemm_noalloc_max_scratch_bytes(void);
+nvfp4_status nvfp4_w4a16_gemm_noalloc(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
+                                      const float* global_scale, int global_scale_is_divisor, void* y, int64_t ld_y,
+                                      int64_t M, int64_t N, int64_t K, void* stream);
+
 /* ---- FP16 activations and outputs ------------------------------------------
  *
  * The same operations with X, the pre-quant scale and Y in IEEE binary16

@@ -112,6 +112,20 @@ def test_zero_sizes_launch_nothing_and_succeed():
     assert L.nvfp4_w4a16_gemm(_p(A), 128, None, None, _p(A), 0, None, 0, 4, 0, 24, None, 0, None) == INVALID
 
 
+def test_noalloc_entry_point_rejects_calls_beyond_its_scratch_before_any_launch():
+    """The no-allocation entry point checks its arguments and its scratch need on the host first (fake pointers:
+    nothing here reaches the GPU)."""
+    L = nv.lib()
+    cap = L.nvfp4_w4a16_gemm_noalloc_max_scratch_bytes()
+    assert cap == 4 << 20
+    assert L.nvfp4_w4a16_gemm_workspace_bytes(256, 512, 65536) > cap
+    st = L.nvfp4_w4a16_gemm_noalloc(_p(A), 65536, None, _p(A), _p(A), 0, _p(A), 512, 256, 512, 65536, None)
+    assert st == SMALL and "scratch" in L.nvfp4_last_error().decode()
+    st = L.nvfp4_w4a16_gemm_noalloc(_p(A), 128, None, _p(A), _p(A), 0, _p(A), 32, 4, 32, 24, None)
+    assert st == INVALID and "multiple of 16" in L.nvfp4_last_error().decode()
+    assert L.nvfp4_w4a16_gemm_noalloc(None, 128, None, _p(A), _p(A), 0, None, 32, 0, 32, 128, None) == OK
+
+
 def test_gemm_plan_names_the_automatic_kernel():
     """The automatic choice: small-M up to 4 rows, the activation-resident kernel for 5..16 rows where it takes the
     shape, the MFMA-bound kernel from 256 rows when the call has at least 48 of its 256 x 256 tiles, the tile kernel

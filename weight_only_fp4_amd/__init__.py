@@ -23,7 +23,7 @@ import torch
 __all__ = ["repack", "repack_bytes", "gemm", "gemm_variant", "grouped_gemm", "dequant", "lib", "Nvfp4Error",
            "workspace", "gemm_workspace_bytes", "grouped_gemm_gather", "moe_route", "moe_silu_mul", "moe_relu2",
            "moe_combine",
-           "gemm_plan", "gemm_variants", "VARIANT_AUTO", "VARIANT_SMALL_M", "VARIANT_LARGE_M", "VARIANT_MFMA", "VARIANT_RESIDENT",
+           "gemm_plan", "gemm_variants", "gemm_noalloc", "VARIANT_AUTO", "VARIANT_SMALL_M", "VARIANT_LARGE_M", "VARIANT_MFMA", "VARIANT_RESIDENT",
            "VARIANT_MFMA_QUARTER", "VARIANT_KERNELS", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4_w4a16.so")
@@ -61,6 +61,10 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_w4a16_gemm_variant.argtypes = [P, I64, P, P, P, I, P, I64, I64, I64, I64, P, I64, I, P]
         L.nvfp4_w4a16_gemm_variant.restype = I
         L.nvfp4_w4a16_gemm_plan.argtypes, L.nvfp4_w4a16_gemm_plan.restype = [I64, I64, I64], I
+        L.nvfp4_w4a16_gemm_noalloc.argtypes = [P, I64, P, P, P, I, P, I64, I64, I64, I64, P]
+        L.nvfp4_w4a16_gemm_noalloc.restype = I
+        L.nvfp4_w4a16_gemm_noalloc_max_scratch_bytes.argtypes = []
+        L.nvfp4_w4a16_gemm_noalloc_max_scratch_bytes.restype = I64
         L.nvfp4_w4a16_gemm_variant_takes.argtypes = [I64, I64, I64, I]
         L.nvfp4_w4a16_gemm_variant_takes.restype = I
         L.nvfp4_w4a16_gemm_f16.argtypes = [P, I64, P, P, P, I, P, I64, I64, I64, I64, P, I64, P]
@@ -235,6 +239,17 @@ def gemm_variant(x, blob, N, K, global_scale, divisor=False, pre_scale=None, out
     fn = lib().nvfp4_w4a16_gemm_variant_f16 if x.dtype == torch.float16 else lib().nvfp4_w4a16_gemm_variant
     _check(fn(_ptr(x), x.stride(0), _ptr(pre_scale), _ptr(blob), _ptr(global_scale), int(bool(divisor)), _ptr(out),
               out.stride(0), M, N, K, _ptr(workspace_buf), workspace_buf.numel(), int(variant), _stream(x.device)))
+    return out
+
+
+def gemm_noalloc(x, blob, N, K, global_scale, divisor=False, pre_scale=None, out=None):
+    """The dense bf16 GEMM through the entry point that allocates nothing (split-K scratch in the library's static
+    device array; calls on one GPU must not overlap in time).  ``out`` is allocated here only if not given."""
+    if x.dtype != torch.bfloat16:
+        raise ValueError("gemm_noalloc takes bf16 activations")
+    M, out = _gemm_args(x, blob, N, K, global_scale, pre_scale, out)
+    _check(lib().nvfp4_w4a16_gemm_noalloc(_ptr(x), x.stride(0), _ptr(pre_scale), _ptr(blob), _ptr(global_scale),
+                                          int(bool(divisor)), _ptr(out), out.stride(0), M, N, K, _stream(x.device)))
     return out
 
 

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/nvfp4_w4a16.h"
 #include "kernels_aux.h"
@@ -472,6 +473,87 @@ nvfp4_status nvfp4_w4a16_grouped_gemm_gather_f16(const void* x, int64_t ld_x, in
     return grouped_gemm_gather("nvfp4_w4a16_grouped_gemm_gather_f16", x, ld_x, T, row_token, expert_offsets,
                                pre_scale, w_repacked, global_scales, global_scale_is_divisor, y, ld_y, R, E, N, K,
                                workspace, workspace_bytes, stream, true);
+}
+
+// --------------------------------------------------- no-allocation entry --
+// nvfp4_w4a16_gemm_noalloc keeps its split-K partials and counters in a
+// file-scope device array instead of a caller's workspace.  The array's name
+// is a host-side stand-in in host code: the kernels get the address that
+// hipGetSymbolAddress returns for the current device, taken once per device
+// on that device's first call and kept.
+
+}  // extern "C"
+
+namespace {
+
+constexpr int64_t kScratchBytes = int64_t(4) << 20;   // 4 MiB per device (a call needing more is rejected)
+static_assert(kScratchBytes > kMaxSplitTiles * 4, "the counter prefix fits");
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// Zero n dwords (a fill kernel rather than a memset, so that a call under
+// graph capture records nothing but kernels).
+__global__ void __launch_bounds__(256) k_zero_dwords(uint32_t* __restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// The device address of this device's scratch array.  On the device's first
+// call: the address from hipGetSymbolAddress (checked), and the counter
+// prefix cleared on `st` (split-K calls leave the counters they use at zero,
+// so it stays clear from then on; the array starts zeroed when the code
+// object loads, the clear makes that explicit).
+nvfp4_status scratch_address(const char* fn, hipStream_t st, uint8_t** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: device %d beyond the %d this library tracks", fn, dev, kScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(NVFP4_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", fn, dev,
+                        hipGetErrorString(e));
+        hipLaunchKernelGGL(k_zero_dwords, dim3((unsigned)((kMaxSplitTiles + 255) / 256)), dim3(256), 0, st,
+                           static_cast<uint32_t*>(p), kMaxSplitTiles);
+        const nvfp4_status s = launched(fn);
+        if (s != NVFP4_OK) return s;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<uint8_t*>(g_scratch_ptr[dev]);
+    return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t nvfp4_w4a16_gemm_noalloc_max_scratch_bytes(void) { return kScratchBytes; }
+
+nvfp4_status nvfp4_w4a16_gemm_noalloc(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
+                                      const float* global_scale, int global_scale_is_divisor, void* y, int64_t ld_y,
+                                      int64_t M, int64_t N, int64_t K, void* stream) {
+    const char* fn = "nvfp4_w4a16_gemm_noalloc";
+    if (check_weight_shape(fn, 1, N, K) != NVFP4_OK) return NVFP4_ERR_INVALID_ARG;
+    if (M < 0 || M > (int64_t)1 << 31) return fail(NVFP4_ERR_INVALID_ARG, "%s: M = %lld out of range", fn, (long long)M);
+    const int64_t need = dense_workspace_bytes(make_layout(1, N, K), M);
+    if (need > kScratchBytes)
+        return fail(NVFP4_ERR_BUFFER_TOO_SMALL,
+                    "%s: this call needs %lld bytes of split-K scratch, above the %lld bytes of the no-allocation "
+                    "entry point (nvfp4_w4a16_gemm with a workspace takes it)",
+                    fn, (long long)need, (long long)kScratchBytes);
+    uint8_t* ws = nullptr;
+    if (need > 0) {
+        const nvfp4_status s = scratch_address(fn, static_cast<hipStream_t>(stream), &ws);
+        if (s != NVFP4_OK) return s;
+    }
+    return dense_gemm(x, ld_x, pre_scale, w_repacked, global_scale, global_scale_is_divisor != 0, y, ld_y, M, N, K,
+                      ws, need > 0 ? kScratchBytes : 0, kAuto, stream, fn, false);
 }
 
 // ------------------------------------------------------------------ MoE --
