@@ -288,6 +288,17 @@ nvfp4_status nvfp4_w4a16_gemm_noalloc(const void* x, int64_t ld_x, const void* p
                                       const float* global_scale, int global_scale_is_divisor, void* y, int64_t ld_y,
                                       int64_t M, int64_t N, int64_t K, void* stream);
 
+/* Measurement export: a plain read of `bytes` (a multiple of 16) at p
+ * (16-byte aligned), the bandwidth reference the GEMMs are measured against.
+ * `workgroups` workgroups of 256 threads each read a contiguous share with
+ * non-temporal 16-byte loads, `unroll` (1, 2, 4 or 8) loads per thread in
+ * flight; out (uint32 [workgroups], 4-byte aligned) is written only in the
+ * practically impossible case that a workgroup's data folds to a fixed value
+ * (it keeps the loads alive).  Errors: bad sizes or unroll -> INVALID_ARG,
+ * misaligned pointers -> ALIGNMENT. */
+nvfp4_status nvfp4_bench_stream_read(const void* p, int64_t bytes, uint32_t* out, int64_t workgroups, int unroll,
+                                     void* stream);
+
 /* ---- FP16 activations and outputs ------------------------------------------
  *
  * The same operations with X, the pre-quant scale and Y in IEEE binary16

@@ -23,7 +23,7 @@ import torch
 __all__ = ["repack", "repack_bytes", "gemm", "gemm_variant", "grouped_gemm", "dequant", "lib", "Nvfp4Error",
            "workspace", "gemm_workspace_bytes", "grouped_gemm_gather", "moe_route", "moe_silu_mul", "moe_relu2",
            "moe_combine",
-           "gemm_plan", "gemm_variants", "gemm_noalloc", "VARIANT_AUTO", "VARIANT_SMALL_M", "VARIANT_LARGE_M", "VARIANT_MFMA", "VARIANT_RESIDENT",
+           "gemm_plan", "gemm_variants", "gemm_noalloc", "stream_read", "VARIANT_AUTO", "VARIANT_SMALL_M", "VARIANT_LARGE_M", "VARIANT_MFMA", "VARIANT_RESIDENT",
            "VARIANT_MFMA_QUARTER", "VARIANT_KERNELS", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4_w4a16.so")
@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_w4a16_gemm_variant.argtypes = [P, I64, P, P, P, I, P, I64, I64, I64, I64, P, I64, I, P]
         L.nvfp4_w4a16_gemm_variant.restype = I
         L.nvfp4_w4a16_gemm_plan.argtypes, L.nvfp4_w4a16_gemm_plan.restype = [I64, I64, I64], I
+        L.nvfp4_bench_stream_read.argtypes, L.nvfp4_bench_stream_read.restype = [P, I64, P, I64, I, P], I
         L.nvfp4_w4a16_gemm_noalloc.argtypes = [P, I64, P, P, P, I, P, I64, I64, I64, I64, P]
         L.nvfp4_w4a16_gemm_noalloc.restype = I
         L.nvfp4_w4a16_gemm_noalloc_max_scratch_bytes.argtypes = []
@@ -251,6 +252,16 @@ def gemm_noalloc(x, blob, N, K, global_scale, divisor=False, pre_scale=None, out
     _check(lib().nvfp4_w4a16_gemm_noalloc(_ptr(x), x.stride(0), _ptr(pre_scale), _ptr(blob), _ptr(global_scale),
                                           int(bool(divisor)), _ptr(out), out.stride(0), M, N, K, _stream(x.device)))
     return out
+
+
+def stream_read(buf: torch.Tensor, out: torch.Tensor, workgroups: int, unroll: int = 4):
+    """Measurement: a plain read of the uint8 device buffer ``buf`` (its size a multiple of 16); ``out`` an int32
+    device tensor of at least ``workgroups`` elements."""
+    _dev("buf", buf, torch.uint8, 1)
+    _dev("out", out, torch.int32, 1)
+    if out.numel() < workgroups:
+        raise ValueError("out needs one element per workgroup")
+    _check(lib().nvfp4_bench_stream_read(_ptr(buf), buf.numel(), _ptr(out), workgroups, unroll, _stream(buf.device)))
 
 
 def grouped_gemm(x, expert_offsets, blob, E, N, K, global_scales, divisor=False, pre_scale=None, out=None,

@@ -80,4 +80,29 @@ __global__ void __launch_bounds__(256) k_dequant(BlobView v, int64_t N, int64_t 
     }
 }
 
+// Plain read of n16 16-byte words, the bandwidth reference the GEMMs are
+// measured against: workgroup b reads its contiguous share of the buffer with
+// non-temporal 16-byte loads, U per thread in flight, and folds them into one
+// dword per thread; a store that depends on every loaded word (taken only if
+// the fold hits a fixed value) keeps the loads from being dropped.
+template <int U>
+__global__ void __launch_bounds__(256) k_stream_read(const uint8_t* __restrict__ p, int64_t n16,
+                                                     uint32_t* __restrict__ out) {
+    const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const int64_t b0 = (int64_t)blockIdx.x * per;
+    const int64_t b1 = b0 + per < n16 ? b0 + per : n16;
+    uint32_t acc = 0u;
+    for (int64_t i = b0 + threadIdx.x; i < b1; i += 256 * U) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = i + u * 256;
+            v[u] = j < b1 ? load_stream_u4(p + j * 16) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    if (acc == 0x9E3779B9u) out[blockIdx.x] = acc;
+}
+
 }  // namespace nvfp4

@@ -5,8 +5,8 @@
 //   coalesced 16-byte loads (each load instruction covers four rows x 256
 //   bytes, whole cache lines) go through a small private LDS area and come
 //   back in the register layout of the v_mfma_f32_16x16x32_bf16 A operand,
-//   where they stay for the whole kernel; the first weight load goes out
-//   before them, so the weight stream starts at once.  The workgroup then walks U
+//   where they stay for the whole kernel; the weight ring goes out right
+//   after them.  The workgroup then walks U
 //   consecutive 16-row units of W: every wave streams its slice of each unit
 //   through a D-deep register ring (one 128-bit code load and one scale
 //   dword per lane and chunk), decodes the codes into exact bf16 fragments
@@ -109,16 +109,15 @@ __global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict
             xr[c][t] = *reinterpret_cast<const uint4*>(mine + r * kXresRowBytes + g * 64 + t * 16);
     };
 
-    // prologue: the first ring item, the whole activation slice, the rest of
-    // the ring; then the slice is staged into registers (the first chunk's
-    // work waits only for the first weights and the activation)
-    load_item(0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    // prologue: the whole activation slice, then the weight ring; the slice
+    // is staged into registers once its loads land.  Counters retire in issue
+    // order, so loading the activation first lets that wait leave the whole
+    // ring in flight (measured faster than a weight item first).
 #pragma unroll
     for (int c = 0; c < CH; ++c) load_x(c);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int d = 1; d < DR; ++d) {
+    for (int d = 0; d < DR; ++d) {
         load_item(d, d);
         __builtin_amdgcn_sched_barrier(0);
     }

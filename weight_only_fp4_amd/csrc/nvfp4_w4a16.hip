@@ -113,7 +113,7 @@ int64_t dense_workspace_bytes(const Layout& L, int64_t M) {
         need = small > need ? small : need;
     }
     if (xres_fits(L, M)) {
-        const int64_t xres = workspace_for(xres_shape(L)).total;
+        const int64_t xres = workspace_for(xres_shape(L, M)).total;
         need = xres > need ? xres : need;
     }
     return need;
@@ -157,7 +157,7 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
     Workspace wl{0, 0, 0};
     int64_t split_tiles = 0;
     if (v == kResident) {
-        const XresShape xs = xres_shape(L);
+        const XresShape xs = xres_shape(L, M);
         wl = workspace_for(xs);
         split_tiles = xs.S > 1 ? xs.groups : 0;
     } else if (v == kSmall) {
@@ -181,7 +181,7 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
                SplitK{1, nullptr, nullptr}, static_cast<hipStream_t>(stream)};
     switch (v) {
         case kResident: {
-            const XresShape xs = xres_shape(L);
+            const XresShape xs = xres_shape(L, M);
             a.sk = split_k(xs.S, wsb, wl);
             return f16 ? launch_xres<true>(xs, L, a) : launch_xres<false>(xs, L, a);
         }
@@ -347,6 +347,27 @@ nvfp4_status nvfp4_dequant_bf16(const void* w_repacked, int64_t E, int64_t N, in
     const uint8_t* b = static_cast<const uint8_t*>(w_repacked);
     hipLaunchKernelGGL(k_dequant, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, static_cast<hipStream_t>(stream),
                        make_view(L, b), N, K, L.NU, L.KC, lanes, static_cast<uint16_t*>(out), ld_out);
+    return launched(fn);
+}
+
+nvfp4_status nvfp4_bench_stream_read(const void* p, int64_t bytes, uint32_t* out, int64_t workgroups, int unroll,
+                                     void* stream) {
+    const char* fn = "nvfp4_bench_stream_read";
+    if (bytes < 0 || bytes % 16 != 0) return fail(NVFP4_ERR_INVALID_ARG, "%s: bytes = %lld must be a multiple of 16", fn, (long long)bytes);
+    if (workgroups < 1 || workgroups > (1 << 20)) return fail(NVFP4_ERR_INVALID_ARG, "%s: workgroups = %lld", fn, (long long)workgroups);
+    if (bytes > 0 && (!p || !out)) return fail(NVFP4_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(p, 16) || !aligned(out, 4)) return fail(NVFP4_ERR_ALIGNMENT, "%s: misaligned pointer", fn);
+    if (bytes == 0) return ok();
+    const uint8_t* src = static_cast<const uint8_t*>(p);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)workgroups);
+    switch (unroll) {
+        case 1: hipLaunchKernelGGL(k_stream_read<1>, grid, dim3(256), 0, st, src, bytes / 16, out); break;
+        case 2: hipLaunchKernelGGL(k_stream_read<2>, grid, dim3(256), 0, st, src, bytes / 16, out); break;
+        case 4: hipLaunchKernelGGL(k_stream_read<4>, grid, dim3(256), 0, st, src, bytes / 16, out); break;
+        case 8: hipLaunchKernelGGL(k_stream_read<8>, grid, dim3(256), 0, st, src, bytes / 16, out); break;
+        default: return fail(NVFP4_ERR_INVALID_ARG, "%s: unroll = %d must be 1, 2, 4 or 8", fn, unroll);
+    }
     return launched(fn);
 }
 

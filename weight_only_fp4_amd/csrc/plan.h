@@ -51,8 +51,8 @@ struct SmallShape {
 
 // (mg, nt, w, d) for the dense form; the grouped form is always (0, 1, w, 4).
 #define NVFP4_SMALL_CONFIGS(X) \
-    X(1, 1, 1, 4) X(1, 1, 2, 4) X(1, 1, 4, 4) X(1, 1, 8, 4) X(1, 1, 16, 4) \
-    X(2, 1, 1, 4) X(2, 1, 2, 4) X(2, 1, 4, 4) X(2, 1, 8, 4) X(2, 2, 2, 4) X(2, 2, 4, 4) X(2, 2, 8, 4) \
+    X(1, 1, 1, 4) X(1, 1, 2, 4) X(1, 1, 4, 4) X(1, 1, 8, 4) X(1, 1, 16, 4) X(1, 2, 1, 4) \
+    X(2, 1, 1, 4) X(2, 1, 2, 4) X(2, 1, 4, 4) X(2, 1, 8, 4) X(2, 2, 1, 4) X(2, 2, 2, 4) X(2, 2, 4, 4) X(2, 2, 8, 4) \
     X(16, 2, 4, 2) X(16, 2, 8, 2) X(16, 4, 4, 2) X(16, 4, 8, 2) X(16, 8, 4, 2) X(16, 8, 8, 2)
 
 // Is (mg, nt, w, d) one of the compiled dense shapes?
@@ -67,17 +67,21 @@ inline bool small_compiled(const SmallShape& s) {
 // Shapes from launch sweeps on MI355X (graph-replayed, weights rotated past
 // the Infinity Cache).  Rows <= 8: one unit per wave, waves sized so the
 // workgroups x waves x ring depth product aims at about 32 KB of weight
-// loads in flight per CU.  Rows 9..16 (16x16x32 form, about two VALU
-// operations per weight to decode) share each activation fragment over four
-// units per wave; the automatic choice sends those rows to the
-// activation-resident kernel.
+// loads in flight per CU; from 2048 row units on (N >= 32768, LM heads) two
+// units per wave and one wave per workgroup, which shares each activation
+// piece, and its pre-quant scaling, over two units (N = 131072, K = 4096:
+// 47.8 us with a pre-scale and 45-47 without, against 56.9 / 45.1 us with one
+// unit and two waves at M = 1, 46.6 against 54.8 us at M = 4).  Rows 9..16
+// (16x16x32 form, about two VALU operations per weight to decode) share each
+// activation fragment over four units per wave; the automatic choice sends
+// those rows to the activation-resident kernel.
 inline SmallShape small_m_shape(const Layout& L, int64_t rows, bool grouped) {
     SmallShape s;
     s.S = 1;
     if (grouped) {
         s.mg = 0; s.nt = 1; s.d = 4;
     } else if (rows <= 8) {
-        s.mg = rows <= 4 ? 1 : 2; s.nt = 1; s.d = 4;
+        s.mg = rows <= 4 ? 1 : 2; s.nt = L.NU >= 2048 ? 2 : 1; s.d = 4;
     } else {
         s.mg = 16; s.nt = 4; s.d = 2; s.w = 4;
     }
@@ -89,8 +93,9 @@ inline SmallShape small_m_shape(const Layout& L, int64_t rows, bool grouped) {
         while (s.S < 8 && s.groups * s.S < 128 && L.KC >= 2 * s.w * 2 * s.S) s.S *= 2;
         return s;
     }
-    const int64_t ctas = s.groups * (grouped ? (L.E + 1) / 2 : 1);
     s.w = 1;
+    if (!grouped && s.nt == 2) return s;   // wide N: one wave per workgroup
+    const int64_t ctas = s.groups * (grouped ? (L.E + 1) / 2 : 1);
     // 16 waves cap a kernel at 128 VGPRs: only the one-row-group form fits
     const int wmax = s.mg == 1 ? 16 : 8;
     while (s.w < wmax && ctas * (2 * s.w) * s.d <= 8192 && L.KC >= 4 * (2 * s.w)) s.w *= 2;
@@ -141,12 +146,15 @@ inline TileShape tile_shape(const Layout& L, int64_t rows, bool grouped) {
 // ---------------------------------------------------- activation-resident --
 // (ch, u, w, d): chunks per wave, units per workgroup, waves, ring depth.
 // From launch sweeps on MI355X (graph-replayed, weights rotated past the
-// Infinity Cache): 16 waves with a 2-deep ring for K up to 4096, the
-// workgroup count near the CU count (u = ceil(row units / 256)).
+// Infinity Cache; decode M = 16 / M = 8, K = 4096, N = 14336): 9..16 rows take
+// 16 waves with a 6-deep ring (9.5 us, against 10.1 with a 2-deep ring), up to
+// 8 rows 8 waves of twice the chunks with a 4-deep ring (8.7 us, against
+// 10.0 with 16 waves), where half the activation rows leave room for it; the
+// workgroup count near the CU count (u = ceil(row units x splits / 256)).
+#define NVFP4_XRES_U(X, CH, W, D) \
+    X(CH, 1, W, D) X(CH, 2, W, D) X(CH, 3, W, D) X(CH, 4, W, D) X(CH, 5, W, D) X(CH, 6, W, D) X(CH, 7, W, D) X(CH, 8, W, D)
 #define NVFP4_XRES_CONFIGS(X) \
-    X(1, 1, 16, 2) X(1, 2, 16, 2) X(1, 3, 16, 2) X(1, 4, 16, 2) X(1, 5, 16, 2) X(1, 6, 16, 2) X(1, 7, 16, 2) \
-    X(1, 8, 16, 2) X(2, 1, 16, 2) X(2, 2, 16, 2) X(2, 3, 16, 2) X(2, 4, 16, 2) X(2, 5, 16, 2) X(2, 6, 16, 2) \
-    X(2, 7, 16, 2) X(2, 8, 16, 2)
+    NVFP4_XRES_U(X, 1, 16, 6) NVFP4_XRES_U(X, 2, 16, 6) NVFP4_XRES_U(X, 2, 8, 4) NVFP4_XRES_U(X, 4, 8, 4)
 
 // Rows from which the automatic choice takes the activation-resident kernel
 // (below it the small-M kernel, measured faster at one row).
@@ -166,12 +174,15 @@ inline bool xres_compiled(const XresShape& s) {
     return found;
 }
 
-// 16 waves own one or two chunks each; K beyond 32 chunks is split S ways
-// across workgroups; units per workgroup by N and S, so that the grid is
-// about one workgroup per CU.  A shape outside the compiled set means the
-// kernel does not take the call (K above 8 splits, or too many row units).
-inline XresShape xres_shape(const Layout& L) {
-    XresShape s{L.KC <= 16 ? 1 : 2, 0, 16, 2, 1, 0};
+// A workgroup's waves own ch chunks each (32 chunks in all, 16 when K fits
+// 16 chunks); K beyond that is split S ways across workgroups; units per
+// workgroup by N and S, so that the grid is about one workgroup per CU.  A
+// shape outside the compiled set means the kernel does not take the call (K
+// above 8 splits, or too many row units).
+inline XresShape xres_shape(const Layout& L, int64_t rows) {
+    const bool eight = rows <= 8;
+    XresShape s{0, 0, eight ? 8 : 16, eight ? 4 : 6, 1, 0};
+    s.ch = (L.KC <= 16 ? 16 : 32) / s.w;
     s.S = (int)((L.KC + 31) / 32);
     const int64_t u = (L.NU * s.S + 255) / 256;
     s.u = (int)(u < 1 ? 1 : u > 64 ? 64 : u);
@@ -182,7 +193,7 @@ inline XresShape xres_shape(const Layout& L) {
 // Does the activation-resident kernel take this dense call?  (M <= 16,
 // K <= 32768, and ceil(N / 16) * ceil(K / 4096) <= 2048.)
 inline bool xres_fits(const Layout& L, int64_t rows) {
-    const XresShape s = xres_shape(L);
+    const XresShape s = xres_shape(L, rows);
     return rows <= kSmallRows && s.S <= kXresMaxSplits && (int64_t)s.S * s.w * s.ch >= L.KC && xres_compiled(s) &&
            s.groups <= 65535;
 }
