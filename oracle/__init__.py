@@ -23,6 +23,13 @@ pages each step follows):
 Grouped (MoE) form: rows offsets[e]..offsets[e+1]-1 use expert e's weights and
 global scale; the pre-quant scale is shared by all experts.
 
+MXFP4 weight-only (``fmt="mxfp4"``; SGLang compressed-tensors NVFP4
+weight-only page, Modifications, the paragraph on MXFP4: group_blocks == 2,
+E8M0 scales, no global_scale):
+
+    T[n,k]  = e2m1(code(n,k)) * e8m0(S[n, k//32]),   e8m0(e) = 2^(e-127), 0xFF NaN
+    Y[m,n]  = sum_k X'[m,k] * T[n,k]                 (no global scale)
+
 MoE glue (numpy, fp64; the steps either side of the grouped GEMM in a
 mixture-of-experts layer: "Support Nemotron-H nvfp4 ckpt on Hopper", Changes
 table, MoE W4A16 execution path; the gate and up projections held together in
@@ -94,6 +101,14 @@ def lib() -> ctypes.CDLL:
             P, I64, I, F, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_double
             L.oracle_e2m1.argtypes, L.oracle_e2m1.restype = [I], D
             L.oracle_e4m3.argtypes, L.oracle_e4m3.restype = [I], D
+            L.oracle_e8m0.argtypes, L.oracle_e8m0.restype = [I], D
+            L.oracle_dequant_fmt.argtypes, L.oracle_dequant_fmt.restype = [P, I64, P, I64, I64, I64, I, P], None
+            L.oracle_gemm_fmt.argtypes = [P, I64, P, P, I64, P, I64, F, I, I, I64, I64, I64, P, P, I, P]
+            L.oracle_gemm_fmt.restype = None
+            L.oracle_gemm_sampled_fmt.argtypes = [P, I64, P, P, I64, P, I64, F, I, I, I64, P, P, I64, P]
+            L.oracle_gemm_sampled_fmt.restype = None
+            L.oracle_grouped_gemm_fmt.argtypes = [P, I64, P, P, P, I64, P, I64, P, I, I, I64, I64, I64, I64, P]
+            L.oracle_grouped_gemm_fmt.restype = None
             L.oracle_round_bf16.argtypes, L.oracle_round_bf16.restype = [D], D
             L.oracle_global_scale.argtypes, L.oracle_global_scale.restype = [F, I], D
             L.oracle_dequant.argtypes, L.oracle_dequant.restype = [P, I64, P, I64, I64, I64, P], None
@@ -130,6 +145,24 @@ def e4m3(byte: int) -> float:
     return lib().oracle_e4m3(int(byte))
 
 
+def e8m0(byte: int) -> float:
+    return lib().oracle_e8m0(int(byte))
+
+
+_FMT = {"nvfp4": 0, "mxfp4": 1}
+
+
+def _fmt(fmt: str) -> int:
+    if fmt not in _FMT:
+        raise ValueError(f"weight format {fmt!r} (nvfp4 or mxfp4)")
+    return _FMT[fmt]
+
+
+def scale_group(fmt: str) -> int:
+    """K elements per block scale: 16 for NVFP4 (E4M3), 32 for MXFP4 (E8M0)."""
+    return 32 if _fmt(fmt) == 1 else 16
+
+
 def round_bf16(v: float) -> float:
     return lib().oracle_round_bf16(float(v))
 
@@ -138,12 +171,14 @@ def global_scale(stored: float, is_divisor: bool) -> float:
     return lib().oracle_global_scale(float(stored), int(bool(is_divisor)))
 
 
-def dequant(w_packed: np.ndarray, w_scale: np.ndarray) -> np.ndarray:
-    """Weight tile T [N, K] (fp64) from canonical u8 [N, K/2] codes and u8 [N, K/16] E4M3 scales."""
+def dequant(w_packed: np.ndarray, w_scale: np.ndarray, fmt: str = "nvfp4") -> np.ndarray:
+    """Weight tile T [N, K] (fp64) from canonical u8 [N, K/2] codes and u8 block scales: [N, K/16] E4M3 (NVFP4)
+    or [N, K/32] E8M0 (MXFP4)."""
     w, s = _c(w_packed, np.uint8), _c(w_scale, np.uint8)
     N, K = w.shape[0], w.shape[1] * 2
+    assert s.shape == (N, K // scale_group(fmt)), (s.shape, N, K, fmt)
     out = np.empty((N, K), dtype=np.float64)
-    lib().oracle_dequant(_ptr(w), w.shape[1], _ptr(s), s.shape[1], N, K, _ptr(out))
+    lib().oracle_dequant_fmt(_ptr(w), w.shape[1], _ptr(s), s.shape[1], N, K, _fmt(fmt), _ptr(out))
     return out
 
 
@@ -154,42 +189,48 @@ def activation(x_bits: np.ndarray, pre_bits: np.ndarray | None) -> np.ndarray:
     return out
 
 
-def gemm(x_bits, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None, threads=None) -> np.ndarray:
-    """Dense Y [M, N] in fp64.  x_bits: bf16 bit patterns (uint16) [M, K]."""
+def gemm(x_bits, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None, threads=None,
+         fmt: str = "nvfp4") -> np.ndarray:
+    """Dense Y [M, N] in fp64.  x_bits: bf16 bit patterns (uint16) [M, K].  MXFP4 (fmt="mxfp4") has no global
+    scale: g_stored and g_is_divisor are ignored."""
     x, w, s, p = _c(x_bits, np.uint16), _c(w_packed, np.uint8), _c(w_scale, np.uint8), _c(pre_bits, np.uint16)
     M, K = x.shape
     N = w.shape[0]
-    assert w.shape[1] * 2 == K and s.shape == (N, K // 16)
+    assert w.shape[1] * 2 == K and s.shape == (N, K // scale_group(fmt))
     L = lib()
     threads = int(threads or L.oracle_max_threads())
     out = np.empty((M, N), dtype=np.float64)
     xbuf = np.empty((max(M, 1), K), dtype=np.float64)
     tbuf = np.empty((threads, max(K, 1)), dtype=np.float64)
-    L.oracle_gemm(_ptr(x), K, _ptr(p), _ptr(w), w.shape[1], _ptr(s), s.shape[1], float(np.float32(g_stored)),
-                  int(bool(g_is_divisor)), M, N, K, _ptr(xbuf), _ptr(tbuf), threads, _ptr(out))
+    L.oracle_gemm_fmt(_ptr(x), K, _ptr(p), _ptr(w), w.shape[1], _ptr(s), s.shape[1], float(np.float32(g_stored)),
+                      int(bool(g_is_divisor)), _fmt(fmt), M, N, K, _ptr(xbuf), _ptr(tbuf), threads, _ptr(out))
     return out
 
 
-def gemm_sampled(x_bits, w_packed, w_scale, g_stored, g_is_divisor, pre_bits, rows, cols) -> np.ndarray:
+def gemm_sampled(x_bits, w_packed, w_scale, g_stored, g_is_divisor, pre_bits, rows, cols,
+                 fmt: str = "nvfp4") -> np.ndarray:
     """Y[rows[i], cols[i]] for each i, each output computed on its own."""
     x, w, s, p = _c(x_bits, np.uint16), _c(w_packed, np.uint8), _c(w_scale, np.uint8), _c(pre_bits, np.uint16)
     r, c = _c(rows, np.int64), _c(cols, np.int64)
     out = np.empty(r.shape[0], dtype=np.float64)
-    lib().oracle_gemm_sampled(_ptr(x), x.shape[1], _ptr(p), _ptr(w), w.shape[1], _ptr(s), s.shape[1],
-                              float(np.float32(g_stored)), int(bool(g_is_divisor)), x.shape[1],
-                              _ptr(r), _ptr(c), r.shape[0], _ptr(out))
+    lib().oracle_gemm_sampled_fmt(_ptr(x), x.shape[1], _ptr(p), _ptr(w), w.shape[1], _ptr(s), s.shape[1],
+                                  float(np.float32(g_stored)), int(bool(g_is_divisor)), _fmt(fmt), x.shape[1],
+                                  _ptr(r), _ptr(c), r.shape[0], _ptr(out))
     return out
 
 
-def grouped_gemm(x_bits, offsets, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None) -> np.ndarray:
-    """Grouped Y [R, N] in fp64.  w_packed [E, N, K/2], w_scale [E, N, K/16], g_stored [E]."""
+def grouped_gemm(x_bits, offsets, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None,
+                 fmt: str = "nvfp4") -> np.ndarray:
+    """Grouped Y [R, N] in fp64.  w_packed [E, N, K/2], w_scale [E, N, K/16] (NVFP4) or [E, N, K/32] (MXFP4),
+    g_stored [E] (ignored for MXFP4)."""
     x, o = _c(x_bits, np.uint16), _c(offsets, np.int32)
-    w, s, g, p = _c(w_packed, np.uint8), _c(w_scale, np.uint8), _c(g_stored, np.float32), _c(pre_bits, np.uint16)
+    w, s, p = _c(w_packed, np.uint8), _c(w_scale, np.uint8), _c(pre_bits, np.uint16)
     R, K = x.shape
     E, N = w.shape[0], w.shape[1]
+    g = _c(np.ones(E, np.float32) if g_stored is None else g_stored, np.float32)
     out = np.full((R, N), np.nan, dtype=np.float64)
-    lib().oracle_grouped_gemm(_ptr(x), K, _ptr(o), _ptr(p), _ptr(w), w.shape[2], _ptr(s), s.shape[2], _ptr(g),
-                              int(bool(g_is_divisor)), R, E, N, K, _ptr(out))
+    lib().oracle_grouped_gemm_fmt(_ptr(x), K, _ptr(o), _ptr(p), _ptr(w), w.shape[2], _ptr(s), s.shape[2], _ptr(g),
+                                  int(bool(g_is_divisor)), _fmt(fmt), R, E, N, K, _ptr(out))
     return out
 
 
@@ -218,6 +259,12 @@ def e2m1_np(codes: np.ndarray) -> np.ndarray:
     return np.where(c & 8, -1.0, 1.0) * _E2M1_MAG[c & 7]
 
 
+def e8m0_np(b: np.ndarray) -> np.ndarray:
+    """E8M0 bytes -> 2^(e - 127) (exact in fp64), NaN for 0xFF."""
+    e = np.asarray(b).astype(np.int64) & 255
+    return np.where(e == 255, np.nan, np.exp2((e - 127).astype(np.float64)))
+
+
 def e4m3_np(b: np.ndarray) -> np.ndarray:
     b = np.asarray(b).astype(np.int64)
     e, m = (b >> 3) & 15, b & 7
@@ -242,10 +289,13 @@ def rne_bf16_np(v: np.ndarray) -> np.ndarray:
     return bf16_np(r.astype(np.uint16))
 
 
-def dequant_np(w_packed: np.ndarray, w_scale: np.ndarray) -> np.ndarray:
+def dequant_np(w_packed: np.ndarray, w_scale: np.ndarray, fmt: str = "nvfp4") -> np.ndarray:
     w = np.asarray(w_packed, dtype=np.uint8)
     codes = np.stack([w & 15, w >> 4], axis=-1).reshape(w.shape[0], -1)   # even k = low nibble
-    scale = np.repeat(e4m3_np(w_scale), 16, axis=1)
+    if fmt == "mxfp4":
+        scale = np.repeat(e8m0_np(w_scale), 32, axis=1)
+    else:
+        scale = np.repeat(e4m3_np(w_scale), 16, axis=1)
     return e2m1_np(codes) * scale
 
 
@@ -261,19 +311,21 @@ def global_scale_np(stored, is_divisor) -> float:
     return float(np.float32(1.0) / st) if is_divisor else float(st)
 
 
-def gemm_np(x_bits, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None) -> np.ndarray:
-    return global_scale_np(g_stored, g_is_divisor) * np.matmul(activation_np(x_bits, pre_bits),
-                                                               dequant_np(w_packed, w_scale).T)
+def gemm_np(x_bits, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None, fmt: str = "nvfp4") -> np.ndarray:
+    g = 1.0 if fmt == "mxfp4" else global_scale_np(g_stored, g_is_divisor)
+    return g * np.matmul(activation_np(x_bits, pre_bits), dequant_np(w_packed, w_scale, fmt).T)
 
 
-def grouped_gemm_np(x_bits, offsets, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None):
+def grouped_gemm_np(x_bits, offsets, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None,
+                    fmt: str = "nvfp4"):
     x = activation_np(x_bits, pre_bits)
     E, N = w_packed.shape[0], w_packed.shape[1]
     out = np.full((x.shape[0], N), np.nan)
     for e in range(E):
         a, b = int(offsets[e]), int(offsets[e + 1])
         if b > a:
-            out[a:b] = global_scale_np(g_stored[e], g_is_divisor) * (x[a:b] @ dequant_np(w_packed[e], w_scale[e]).T)
+            g = 1.0 if fmt == "mxfp4" else global_scale_np(g_stored[e], g_is_divisor)
+            out[a:b] = g * (x[a:b] @ dequant_np(w_packed[e], w_scale[e], fmt).T)
     return out
 
 
@@ -312,13 +364,15 @@ def activation_f16(x_bits: np.ndarray, pre_bits: np.ndarray | None = None) -> np
     return x if pre_bits is None else rne_f16_np(x * f16_np(pre_bits)[None, :])
 
 
-def gemm_f16(x_bits, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None) -> np.ndarray:
+def gemm_f16(x_bits, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None, fmt: str = "nvfp4") -> np.ndarray:
     """Dense Y [M, N] in fp64 for fp16 activations (x_bits: binary16 bit patterns [M, K])."""
-    t = dequant(w_packed, w_scale)
-    return global_scale(g_stored, g_is_divisor) * np.matmul(activation_f16(x_bits, pre_bits), t.T)
+    t = dequant(w_packed, w_scale, fmt)
+    g = 1.0 if fmt == "mxfp4" else global_scale(g_stored, g_is_divisor)
+    return g * np.matmul(activation_f16(x_bits, pre_bits), t.T)
 
 
-def grouped_gemm_f16(x_bits, offsets, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None) -> np.ndarray:
+def grouped_gemm_f16(x_bits, offsets, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None,
+                     fmt: str = "nvfp4") -> np.ndarray:
     """Grouped Y [R, N] in fp64 for fp16 activations; rows owned by no expert are NaN."""
     o = np.asarray(offsets, dtype=np.int64)
     xa = activation_f16(x_bits, pre_bits)
@@ -327,12 +381,14 @@ def grouped_gemm_f16(x_bits, offsets, w_packed, w_scale, g_stored, g_is_divisor=
     for e in range(E):
         a, b = o[e], o[e + 1]
         if b > a:
-            g = global_scale(float(np.asarray(g_stored, dtype=np.float32)[e]), g_is_divisor)
-            out[a:b] = g * np.matmul(xa[a:b], dequant(w_packed[e], w_scale[e]).T)
+            g = 1.0 if fmt == "mxfp4" else global_scale(float(np.asarray(g_stored, dtype=np.float32)[e]),
+                                                        g_is_divisor)
+            out[a:b] = g * np.matmul(xa[a:b], dequant(w_packed[e], w_scale[e], fmt).T)
     return out
 
 
-def accumulation_slack(x_bits, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None, act="bf16"):
+def accumulation_slack(x_bits, w_packed, w_scale, g_stored, g_is_divisor=False, pre_bits=None, act="bf16",
+                       fmt: str = "nvfp4"):
     """Per-output bound d on how far a correct fp32 computation can be from the exact value before its one
     rounding to the output type (numpy, fp64; for small shapes).
 
@@ -344,8 +400,8 @@ def accumulation_slack(x_bits, w_packed, w_scale, g_stored, g_is_divisor=False, 
         d[m,n] = 2 K u |g| sum_k |X'[m,k] T[n,k]| + 2 u |Y_ref[m,n]|.
     """
     xa = activation_np(x_bits, pre_bits) if act == "bf16" else activation_f16(x_bits, pre_bits)
-    t = dequant_np(w_packed, w_scale)
-    g = abs(global_scale_np(g_stored, g_is_divisor))
+    t = dequant_np(w_packed, w_scale, fmt)
+    g = 1.0 if fmt == "mxfp4" else abs(global_scale_np(g_stored, g_is_divisor))
     K = xa.shape[1]
     u = 2.0 ** -24
     terms = np.abs(xa) @ np.abs(t).T

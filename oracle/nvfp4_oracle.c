@@ -31,6 +31,14 @@
  * floating point specification (OFP8) v1.0, E4M3 column of its format table.
  * Nibble order (low nibble = even k) is a reading the pages leave open.
  *
+ * MXFP4 weight-only (the *_fmt functions with fmt = 1): the same E2M1 codes
+ * with one E8M0 scale per group of 32 along K and no global scale (SGLang
+ * page, Modifications: the paragraph on MXFP4 names group_blocks == 2, E8M0
+ * scales and the missing global_scale as what sets it apart from NVFP4).
+ *   T[n,k] = e2m1(code(n,k)) * e8m0(S[n, k/32]),  Y[m,n] = sum_k X'[m,k] T[n,k]
+ * E8M0 follows the OCP MX specification v1.0 (section 5.4.1): 2^(e-127) for
+ * e = 0..254, NaN for 255, no sign and no zero.
+ *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (fp contraction off
  * so every product and sum is a separately rounded fp64 operation).
  */
@@ -58,6 +66,17 @@ double oracle_e4m3(int byte) {
     else mag = ldexp(1.0 + m / 8.0, e - 7);
     return s ? -mag : mag;
 }
+
+/* E8M0 (OCP MX scale): an unsigned biased exponent, 2^(e-127); 0xFF is NaN. */
+double oracle_e8m0(int byte) {
+    if ((byte & 255) == 255) return NAN;
+    return ldexp(1.0, (byte & 255) - 127);
+}
+
+/* Weight (n, k) of one expert in format fmt: 0 = NVFP4 (E4M3 scale per 16 k),
+ * 1 = MXFP4 (E8M0 scale per 32 k). */
+static double weight_value(const uint8_t* w, int64_t ld_w, const uint8_t* s, int64_t ld_s, int64_t n, int64_t k,
+                           int fmt);
 
 /* bf16 bit pattern -> value (bf16 is the upper half of an IEEE binary32). */
 double oracle_bf16_value(uint16_t bits) {
@@ -94,12 +113,23 @@ static int code_at(const uint8_t* w, int64_t ld_w, int64_t n, int64_t k) {
     return (w[n * ld_w + (k >> 1)] >> (4 * (k & 1))) & 15;
 }
 
+static double weight_value(const uint8_t* w, int64_t ld_w, const uint8_t* s, int64_t ld_s, int64_t n, int64_t k,
+                           int fmt) {
+    if (fmt == 1) return oracle_e2m1(code_at(w, ld_w, n, k)) * oracle_e8m0(s[n * ld_s + (k >> 5)]);
+    return oracle_e2m1(code_at(w, ld_w, n, k)) * oracle_e4m3(s[n * ld_s + (k >> 4)]);
+}
+
 /* Weight tile T[n,k] in fp64 for one expert, written to out[N*K]. */
-void oracle_dequant(const uint8_t* w, int64_t ld_w, const uint8_t* s, int64_t ld_s,
-                    int64_t N, int64_t K, double* out) {
+void oracle_dequant_fmt(const uint8_t* w, int64_t ld_w, const uint8_t* s, int64_t ld_s,
+                        int64_t N, int64_t K, int fmt, double* out) {
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; ++k)
-            out[n * K + k] = oracle_e2m1(code_at(w, ld_w, n, k)) * oracle_e4m3(s[n * ld_s + (k >> 4)]);
+            out[n * K + k] = weight_value(w, ld_w, s, ld_s, n, k, fmt);
+}
+
+void oracle_dequant(const uint8_t* w, int64_t ld_w, const uint8_t* s, int64_t ld_s,
+                    int64_t N, int64_t K, double* out) {
+    oracle_dequant_fmt(w, ld_w, s, ld_s, N, K, 0, out);
 }
 
 /* X'[m,k] in fp64: the activation, times the pre-quant scale rounded back to
@@ -118,12 +148,13 @@ void oracle_activation(const uint16_t* x, int64_t ld_x, const uint16_t* pre, int
  * Parallel over n: each thread decodes row n of T once into tbuf, then forms
  * one plain sequential sum per output.  xbuf[M*K] and tbuf[threads*K] are
  * caller-provided scratch. */
-void oracle_gemm(const uint16_t* x, int64_t ld_x, const uint16_t* pre,
-                 const uint8_t* w, int64_t ld_w, const uint8_t* s, int64_t ld_s,
-                 float g_stored, int g_is_divisor,
-                 int64_t M, int64_t N, int64_t K, double* xbuf, double* tbuf, int threads,
-                 double* out) {
-    double g = oracle_global_scale(g_stored, g_is_divisor);
+/* fmt as for oracle_dequant_fmt; MXFP4 has no global scale (g = 1). */
+void oracle_gemm_fmt(const uint16_t* x, int64_t ld_x, const uint16_t* pre,
+                     const uint8_t* w, int64_t ld_w, const uint8_t* s, int64_t ld_s,
+                     float g_stored, int g_is_divisor, int fmt,
+                     int64_t M, int64_t N, int64_t K, double* xbuf, double* tbuf, int threads,
+                     double* out) {
+    double g = fmt == 1 ? 1.0 : oracle_global_scale(g_stored, g_is_divisor);
     oracle_activation(x, ld_x, pre, M, K, xbuf);
 #pragma omp parallel num_threads(threads)
     {
@@ -131,7 +162,7 @@ void oracle_gemm(const uint16_t* x, int64_t ld_x, const uint16_t* pre,
 #pragma omp for schedule(static)
         for (int64_t n = 0; n < N; ++n) {
             for (int64_t k = 0; k < K; ++k)
-                t[k] = oracle_e2m1(code_at(w, ld_w, n, k)) * oracle_e4m3(s[n * ld_s + (k >> 4)]);
+                t[k] = weight_value(w, ld_w, s, ld_s, n, k, fmt);
             for (int64_t m = 0; m < M; ++m) {
                 double acc = 0.0;
                 for (int64_t k = 0; k < K; ++k) acc += xbuf[m * K + k] * t[k];
@@ -141,29 +172,50 @@ void oracle_gemm(const uint16_t* x, int64_t ld_x, const uint16_t* pre,
     }
 }
 
+void oracle_gemm(const uint16_t* x, int64_t ld_x, const uint16_t* pre,
+                 const uint8_t* w, int64_t ld_w, const uint8_t* s, int64_t ld_s,
+                 float g_stored, int g_is_divisor,
+                 int64_t M, int64_t N, int64_t K, double* xbuf, double* tbuf, int threads,
+                 double* out) {
+    oracle_gemm_fmt(x, ld_x, pre, w, ld_w, s, ld_s, g_stored, g_is_divisor, 0, M, N, K, xbuf, tbuf, threads, out);
+}
+
 int oracle_max_threads(void) { return omp_get_max_threads(); }
 
 /* One output of the dense form, computed on its own from the raw inputs. */
-double oracle_gemm_one(const uint16_t* x, int64_t ld_x, const uint16_t* pre,
+static double gemm_one(const uint16_t* x, int64_t ld_x, const uint16_t* pre,
                        const uint8_t* w, int64_t ld_w, const uint8_t* s, int64_t ld_s,
-                       float g_stored, int g_is_divisor, int64_t K, int64_t m, int64_t n) {
+                       float g_stored, int g_is_divisor, int fmt, int64_t K, int64_t m, int64_t n) {
     double acc = 0.0;
     for (int64_t k = 0; k < K; ++k) {
         double xv = oracle_bf16_value(x[m * ld_x + k]);
         if (pre) xv = oracle_round_bf16(xv * oracle_bf16_value(pre[k]));
-        acc += xv * (oracle_e2m1(code_at(w, ld_w, n, k)) * oracle_e4m3(s[n * ld_s + (k >> 4)]));
+        acc += xv * weight_value(w, ld_w, s, ld_s, n, k, fmt);
     }
-    return oracle_global_scale(g_stored, g_is_divisor) * acc;
+    return (fmt == 1 ? 1.0 : oracle_global_scale(g_stored, g_is_divisor)) * acc;
+}
+
+double oracle_gemm_one(const uint16_t* x, int64_t ld_x, const uint16_t* pre,
+                       const uint8_t* w, int64_t ld_w, const uint8_t* s, int64_t ld_s,
+                       float g_stored, int g_is_divisor, int64_t K, int64_t m, int64_t n) {
+    return gemm_one(x, ld_x, pre, w, ld_w, s, ld_s, g_stored, g_is_divisor, 0, K, m, n);
 }
 
 /* Sampled dense outputs: out[i] = Y[rows[i], cols[i]]. */
+void oracle_gemm_sampled_fmt(const uint16_t* x, int64_t ld_x, const uint16_t* pre,
+                             const uint8_t* w, int64_t ld_w, const uint8_t* s, int64_t ld_s,
+                             float g_stored, int g_is_divisor, int fmt, int64_t K,
+                             const int64_t* rows, const int64_t* cols, int64_t count, double* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = gemm_one(x, ld_x, pre, w, ld_w, s, ld_s, g_stored, g_is_divisor, fmt, K, rows[i], cols[i]);
+}
+
 void oracle_gemm_sampled(const uint16_t* x, int64_t ld_x, const uint16_t* pre,
                          const uint8_t* w, int64_t ld_w, const uint8_t* s, int64_t ld_s,
                          float g_stored, int g_is_divisor, int64_t K,
                          const int64_t* rows, const int64_t* cols, int64_t count, double* out) {
-#pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < count; ++i)
-        out[i] = oracle_gemm_one(x, ld_x, pre, w, ld_w, s, ld_s, g_stored, g_is_divisor, K, rows[i], cols[i]);
+    oracle_gemm_sampled_fmt(x, ld_x, pre, w, ld_w, s, ld_s, g_stored, g_is_divisor, 0, K, rows, cols, count, out);
 }
 
 /* Expert owning row r: the e with offsets[e] <= r < offsets[e+1] (-1 if none). */
@@ -177,10 +229,10 @@ static int64_t expert_of_row(const int32_t* offsets, int64_t E, int64_t r) {
  * and use that expert's weights w + e*N*ld_w, scales s + e*N*ld_s and global
  * scale g_stored[e]; the pre-scale (if any) is shared by all experts.
  * out[R*N]; rows outside every expert's range are left untouched. */
-void oracle_grouped_gemm(const uint16_t* x, int64_t ld_x, const int32_t* offsets, const uint16_t* pre,
-                         const uint8_t* w, int64_t ld_w, const uint8_t* s, int64_t ld_s,
-                         const float* g_stored, int g_is_divisor,
-                         int64_t R, int64_t E, int64_t N, int64_t K, double* out) {
+void oracle_grouped_gemm_fmt(const uint16_t* x, int64_t ld_x, const int32_t* offsets, const uint16_t* pre,
+                             const uint8_t* w, int64_t ld_w, const uint8_t* s, int64_t ld_s,
+                             const float* g_stored, int g_is_divisor, int fmt,
+                             int64_t R, int64_t E, int64_t N, int64_t K, double* out) {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < R; ++r) {
         int64_t e = expert_of_row(offsets, E, r);
@@ -188,9 +240,16 @@ void oracle_grouped_gemm(const uint16_t* x, int64_t ld_x, const int32_t* offsets
         const uint8_t* we = w + e * N * ld_w;
         const uint8_t* se = s + e * N * ld_s;
         for (int64_t n = 0; n < N; ++n)
-            out[r * N + n] = oracle_gemm_one(x, ld_x, pre, we, ld_w, se, ld_s, g_stored[e], g_is_divisor,
-                                             K, r, n);
+            out[r * N + n] = gemm_one(x, ld_x, pre, we, ld_w, se, ld_s, fmt == 1 ? 1.0f : g_stored[e], g_is_divisor,
+                                      fmt, K, r, n);
     }
+}
+
+void oracle_grouped_gemm(const uint16_t* x, int64_t ld_x, const int32_t* offsets, const uint16_t* pre,
+                         const uint8_t* w, int64_t ld_w, const uint8_t* s, int64_t ld_s,
+                         const float* g_stored, int g_is_divisor,
+                         int64_t R, int64_t E, int64_t N, int64_t K, double* out) {
+    oracle_grouped_gemm_fmt(x, ld_x, offsets, pre, w, ld_w, s, ld_s, g_stored, g_is_divisor, 0, R, E, N, K, out);
 }
 
 /* Sampled grouped outputs: out[i] = Y[rows[i], cols[i]] (NaN if the row has no expert). */
@@ -202,7 +261,7 @@ void oracle_grouped_gemm_sampled(const uint16_t* x, int64_t ld_x, const int32_t*
     for (int64_t i = 0; i < count; ++i) {
         int64_t e = expert_of_row(offsets, E, rows[i]);
         if (e < 0) { out[i] = NAN; continue; }
-        out[i] = oracle_gemm_one(x, ld_x, pre, w + e * N * ld_w, ld_w, s + e * N * ld_s, ld_s,
-                                 g_stored[e], g_is_divisor, K, rows[i], cols[i]);
+        out[i] = gemm_one(x, ld_x, pre, w + e * N * ld_w, ld_w, s + e * N * ld_s, ld_s,
+                          g_stored[e], g_is_divisor, 0, K, rows[i], cols[i]);
     }
 }

@@ -62,6 +62,11 @@ def scales_log_uniform(g: np.random.Generator, shape, lo=-6.0, hi=3.0) -> np.nda
     return e4m3_bytes_from_f32(np.exp2(u).astype(np.float32))
 
 
+def scales_e8m0(g: np.random.Generator, shape, umin=-9, umax=2) -> np.ndarray:
+    """E8M0 bytes (MXFP4 group scales) of 2^u, u uniform in [umin, umax]: byte = u + 127."""
+    return (g.integers(umin, umax + 1, size=shape) + 127).astype(np.uint8)
+
+
 def f16_bits_from_f32(a: np.ndarray) -> np.ndarray:
     """float32 values -> IEEE binary16 bit patterns (uint16), round to nearest even (numpy cast)."""
     return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16).copy()
@@ -97,26 +102,33 @@ class DenseCase:
     K: int
     x: np.ndarray             # uint16 bf16 (or fp16, act == "f16") bits [M, K]
     w: np.ndarray             # uint8 [N, K/2]
-    s: np.ndarray             # uint8 E4M3 [N, K/16]
-    g_stored: float           # fp32 value as stored
+    s: np.ndarray             # uint8 E4M3 [N, K/16] (NVFP4) or E8M0 [N, K/32] (MXFP4)
+    g_stored: float           # fp32 value as stored (MXFP4: no global scale, 1.0)
     g_is_divisor: bool
     pre: np.ndarray | None    # uint16 bits [K] (the type of x) or None
     meta: dict = field(default_factory=dict)
     act: str = "bf16"         # activation / output type
+    fmt: str = "nvfp4"        # weight format: nvfp4 or mxfp4
 
 
 def dense_case(M: int, N: int, K: int, seed: int, *, scales: str = "pow2_mant", g_stored: float = 1.0 / 448.0,
-               g_is_divisor: bool = False, prescale: bool = False, name: str = "", act: str = "bf16") -> DenseCase:
+               g_is_divisor: bool = False, prescale: bool = False, name: str = "", act: str = "bf16",
+               fmt: str = "nvfp4") -> DenseCase:
     """One dense workload.  scales: 'pow2_mant' (2^u (1+m/8), u in [-4,2]) or 'log_uniform' ([2^-6, 2^3]).
-    act: activation type, 'bf16' or 'f16' (the same random draws, rounded to that type)."""
-    assert K % 16 == 0 and K % 2 == 0
+    act: activation type, 'bf16' or 'f16' (the same random draws, rounded to that type).  fmt 'mxfp4': E8M0
+    scales 2^u, u in [-9, 2], one per 32 K, and no global scale (g_stored 1.0, not a divisor)."""
+    assert K % (32 if fmt == "mxfp4" else 16) == 0
     g = rng(seed)
     x = normal_act(g, (M, K), act)
     w = random_codes(g, (N, K))
-    s = scales_pow2_mant(g, (N, K // 16)) if scales == "pow2_mant" else scales_log_uniform(g, (N, K // 16))
+    if fmt == "mxfp4":
+        s = scales_e8m0(g, (N, K // 32))
+        g_stored, g_is_divisor, scales = 1.0, False, "e8m0"
+    else:
+        s = scales_pow2_mant(g, (N, K // 16)) if scales == "pow2_mant" else scales_log_uniform(g, (N, K // 16))
     pre = awq_prescale(g, K, act) if prescale else None
     return DenseCase(name or f"dense_M{M}_N{N}_K{K}", M, N, K, x, w, s, float(np.float32(g_stored)),
-                     bool(g_is_divisor), pre, {"seed": seed, "scales": scales}, act)
+                     bool(g_is_divisor), pre, {"seed": seed, "scales": scales}, act, fmt)
 
 
 def zipf_routing(g: np.random.Generator, T: int, E: int, topk: int, s: float = 1.1) -> np.ndarray:
@@ -139,12 +151,13 @@ class GroupedCase:
     x: np.ndarray             # uint16 bf16 (or fp16) bits [R, K], rows grouped by expert
     offsets: np.ndarray       # int32 [E+1]
     w: np.ndarray             # uint8 [E, N, K/2]
-    s: np.ndarray             # uint8 [E, N, K/16]
-    g_stored: np.ndarray      # float32 [E]
+    s: np.ndarray             # uint8 [E, N, K/16] (E8M0 [E, N, K/32] for MXFP4)
+    g_stored: np.ndarray      # float32 [E] (MXFP4: ones)
     g_is_divisor: bool
     pre: np.ndarray | None
     meta: dict = field(default_factory=dict)
     act: str = "bf16"
+    fmt: str = "nvfp4"
 
     @property
     def active(self) -> np.ndarray:
@@ -157,7 +170,8 @@ def routing_seed(seed: int) -> int:
 
 def grouped_case(T: int, E: int, topk: int, N: int, K: int, seed: int, *, x_source: str = "gather",
                  prescale: bool = False, g_base: float = 1.0 / 2688.0, name: str = "",
-                 routing: np.ndarray | None = None, seed0: int | None = None, act: str = "bf16") -> GroupedCase:
+                 routing: np.ndarray | None = None, seed0: int | None = None, act: str = "bf16",
+                 fmt: str = "nvfp4") -> GroupedCase:
     """Grouped MoE workload.  x_source 'gather': rows are tokens X[T, K] gathered per (token, expert) pair in
     expert order; 'fresh': a new N(0,1) [R, K] input (the FC2 side, whose real input is FC1's activation).
     The routing comes from its own stream, seeded by ``routing_seed(seed0 or seed)``, so FC1 and FC2 cases
@@ -165,9 +179,9 @@ def grouped_case(T: int, E: int, topk: int, N: int, K: int, seed: int, *, x_sour
     g = rng(seed)
     xt = normal_act(g, (T, K), act)
     w = random_codes(g, (E, N, K))
-    s = scales_pow2_mant(g, (E, N, K // 16))
+    s = scales_e8m0(g, (E, N, K // 32)) if fmt == "mxfp4" else scales_pow2_mant(g, (E, N, K // 16))
     v = g.integers(-2, 3, size=E)
-    gs = (np.exp2(v.astype(np.float64)) * g_base).astype(np.float32)
+    gs = (np.exp2(v.astype(np.float64)) * g_base).astype(np.float32) if fmt != "mxfp4" else np.ones(E, np.float32)
     pre = awq_prescale(g, K, act) if prescale else None
     route = zipf_routing(rng(routing_seed(seed0 if seed0 is not None else seed)), T, E, topk) \
         if routing is None else routing
@@ -181,7 +195,7 @@ def grouped_case(T: int, E: int, topk: int, N: int, K: int, seed: int, *, x_sour
     x = xt[tok[order]] if x_source == "gather" else normal_act(g, (R, K), act)
     return GroupedCase(name or f"grouped_T{T}_E{E}_N{N}_K{K}", E, N, K, R, np.ascontiguousarray(x), offsets,
                        w, s, gs, False, pre, {"seed": seed, "T": T, "topk": topk, "token_of_row": tok[order],
-                                              "routing": route}, act)
+                                              "routing": route}, act, fmt)
 
 
 # ------------------------------------------------------------- workloads ---

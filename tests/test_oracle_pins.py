@@ -592,3 +592,103 @@ def test_moe_glue_f16_decodes_inputs_as_binary16():
     dec = np.array([struct.unpack("<e", int(b).to_bytes(2, "little"))[0] for b in y[2]])
     assert np.array_equal(out[0], dec)
 
+
+
+# ------------------------------------------------------- MXFP4 weight-only ---
+# E2M1 codes with one E8M0 scale per 32 K and no global scale (SGLang compressed-tensors NVFP4 weight-only page,
+# Modifications, the paragraph on MXFP4: group_blocks == 2, E8M0 scales, no global_scale).  E8M0 per the OCP MX
+# specification: 2^(e - 127), 0xFF NaN.
+
+def test_e8m0_all_256_codes_match_closed_form_and_torch():
+    """Every E8M0 byte: 2^(e - 127) for e < 255 (a closed form) and NaN for 255; and torch's float8_e8m0fnu
+    decoder (a library routine) agrees on all 256 codes; the numpy twin too."""
+    codes = np.arange(256)
+    c = np.array([oracle.e8m0(int(b)) for b in codes])
+    closed = np.where(codes == 255, np.nan, np.ldexp(1.0, codes - 127))
+    assert np.array_equal(c, closed, equal_nan=True)
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert np.array_equal(c, t, equal_nan=True)
+    assert np.array_equal(oracle.e8m0_np(codes), c, equal_nan=True)
+    assert oracle.e8m0(0) == 2.0 ** -127 and oracle.e8m0(254) == 2.0 ** 127 and oracle.e8m0(127) == 1.0
+
+
+def test_mxfp4_tile_is_code_times_power_of_two_over_groups_of_32():
+    """Every code under every E8M0 scale: T = e2m1(code) * 2^(e-127) exactly (fp64); the scale index is k // 32
+    (a row whose 32-groups carry different scales: k = 31 and k = 32 take different scales, k = 0 and 31 the
+    same), and the numpy twin agrees."""
+    K = 256
+    N = 256                                   # row n: scale byte n on its first group, n ^ 0x55 on the others
+    codes = (np.arange(K)[None, :] + np.arange(N)[:, None]) % 16
+    w = synth.pack_codes(codes.astype(np.uint8))
+    s = np.empty((N, K // 32), dtype=np.uint8)
+    s[:, 0] = np.arange(N)
+    s[:, 1:] = (np.arange(N) ^ 0x55)[:, None]
+    t = oracle.dequant(w, s, "mxfp4")
+    exp = oracle.e2m1_np(codes) * np.repeat(np.where(s == 255, np.nan, np.ldexp(1.0, s.astype(np.int64) - 127)),
+                                            32, axis=1)
+    assert np.array_equal(t, exp, equal_nan=True)
+    assert np.array_equal(oracle.dequant_np(w, s, "mxfp4"), t, equal_nan=True)
+    n = 130
+    assert t[n, 31] / oracle.e2m1((31 + n) % 16) == 2.0 ** (130 - 127)
+    assert t[n, 32] / oracle.e2m1((32 + n) % 16) == 2.0 ** ((130 ^ 0x55) - 127)
+
+
+def test_mxfp4_hand_case_closed_form():
+    """1 x 64 x 4: X = 1 on k = 0..63; row n holds code 2 (1.0) on the first 32-group and code 4 (2.0) on the
+    second, scales 2^(n-1) and 2^-n: Y[0, n] = 32 * 2^(n-1) + 32 * 2 * 2^-n, exactly, with no global scale (the
+    stored value passed in is ignored)."""
+    N, K = 4, 64
+    codes = np.zeros((N, K), dtype=np.uint8)
+    codes[:, :32], codes[:, 32:] = 2, 4
+    w = synth.pack_codes(codes)
+    s = np.stack([np.arange(N) - 1 + 127, -np.arange(N) + 127], axis=1).astype(np.uint8)
+    x = np.full((1, K), 0x3F80, dtype=np.uint16)
+    y = oracle.gemm(x, w, s, 123.0, True, None, fmt="mxfp4")
+    exp = [32 * 2.0 ** (n - 1) + 64 * 2.0 ** -n for n in range(N)]
+    assert list(y[0]) == exp
+
+
+def test_mxfp4_gemm_matches_twin_sampled_grouped_and_exact_arithmetic():
+    c = synth.dense_case(17, 96, 320, 71, fmt="mxfp4", prescale=True)
+    assert c.s.shape == (96, 10) and c.g_stored == 1.0
+    ref = oracle.gemm(c.x, c.w, c.s, c.g_stored, False, c.pre, fmt="mxfp4")
+    tw = oracle.gemm_np(c.x, c.w, c.s, c.g_stored, False, c.pre, fmt="mxfp4")
+    assert np.max(np.abs(ref - tw)) <= 1e-12 * np.max(np.abs(ref))
+    rows, cols = np.array([0, 16, 5]), np.array([95, 0, 33])
+    assert np.array_equal(oracle.gemm_sampled(c.x, c.w, c.s, 1.0, False, c.pre, rows, cols, fmt="mxfp4"),
+                          ref[rows, cols])
+    # exact rational arithmetic on one output: every term is a dyadic rational
+    xa = oracle.activation_np(c.x, c.pre)
+    t = oracle.dequant(c.w, c.s, "mxfp4")
+    exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(xa[3], t[7]))
+    assert abs(Fraction(ref[3, 7]) - exact) <= abs(exact) * Fraction(1, 2 ** 45)
+    gc = synth.grouped_case(T=12, E=4, topk=2, N=40, K=128, seed=72, fmt="mxfp4")
+    assert gc.s.shape == (4, 40, 4)
+    g = oracle.grouped_gemm(gc.x, gc.offsets, gc.w, gc.s, None, False, None, fmt="mxfp4")
+    gt = oracle.grouped_gemm_np(gc.x, gc.offsets, gc.w, gc.s, None, False, None, fmt="mxfp4")
+    assert np.allclose(g, gt, rtol=1e-12, atol=0, equal_nan=True)
+
+
+def _planted_mx(kind, c):
+    codes = np.stack([c.w & 15, c.w >> 4], axis=-1).reshape(c.w.shape[0], -1)
+    x = oracle.activation_np(c.x, c.pre)
+    if kind == "group_16":        # scale index k // 16 (the NVFP4 grouping) instead of k // 32
+        idx = np.minimum(np.arange(c.K) >> 4, c.s.shape[1] - 1)
+        T = oracle.e2m1_np(codes) * oracle.e8m0_np(c.s[:, idx])
+    elif kind == "bias_128":      # E8M0 bias off by one
+        T = oracle.e2m1_np(codes) * np.repeat(np.exp2(c.s.astype(np.float64) - 128), 32, axis=1)
+    elif kind == "as_e4m3":       # scale bytes read as E4M3
+        T = oracle.e2m1_np(codes) * np.repeat(oracle.e4m3_np(c.s), 32, axis=1)
+    else:
+        T = oracle.dequant_np(c.w, c.s, "mxfp4")
+    y = (x @ T.T).astype(np.float32)
+    return torch.from_numpy(y).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("kind", ["group_16", "bias_128", "as_e4m3"])
+def test_mxfp4_planted_mistakes_fail_acceptance(kind):
+    c = synth.dense_case(64, 512, 1024, seed=73, fmt="mxfp4", prescale=True)
+    ref = oracle.gemm(c.x, c.w, c.s, c.g_stored, False, c.pre, fmt="mxfp4")
+    assert oracle.accept(_planted_mx("none", c), ref)[0]
+    ok, info = oracle.accept(_planted_mx(kind, c), ref)
+    assert not ok, (kind, info)
