@@ -299,6 +299,54 @@ nvfp4_status nvfp4_w4a16_gemm_noalloc(const void* x, int64_t ld_x, const void* p
 nvfp4_status nvfp4_bench_stream_read(const void* p, int64_t bytes, uint32_t* out, int64_t workgroups, int unroll,
                                      void* stream);
 
+/* ---- MXFP4 weights -----------------------------------------------------------
+ *
+ * Weight-only MXFP4: the same packed E2M1 codes with one E8M0 scale per 32
+ * consecutive K of a row and no global scale (SGLang compressed-tensors
+ * NVFP4 weight-only page, Modifications: the paragraph on MXFP4 names group
+ * size 32 (group_blocks == 2), E8M0 scales and the missing global scale as
+ * what sets it apart from NVFP4).  E8M0 is the OCP MX scale: byte e decodes
+ * to 2^(e-127), 0xFF is NaN.
+ *
+ *     Y = RNE(sum_k X'[m,k] * e2m1(code(n,k)) * e8m0(S[n, k/32]))
+ *
+ *   w_scale : uint8 E8M0 [E][N][ld_s], ld_s >= K/32; K must be a multiple of
+ *             32 (INVALID_ARG otherwise).
+ * The repacked blob has the size mxfp4_repack_bytes(E,N,K) (equal to
+ * nvfp4_repack_bytes) and may only be passed to the mxfp4_* calls.  The
+ * GEMMs take the arguments, kernel choice, workspace sizes
+ * (nvfp4_w4a16_gemm_workspace_bytes, nvfp4_w4a16_grouped_gemm_workspace_bytes),
+ * pre-quant scale, ownership, zero sizes and errors of the NVFP4 calls, minus
+ * the global scale; the _f16 forms take fp16 activations and outputs.
+ * Decoded weights are exact in bf16 while |e2m1 * 2^(e-127)| stays in bf16's
+ * normal range (scale bytes 2..252; the kernels may flush smaller ones to
+ * zero and larger ones overflow to infinity), in fp16 while it stays in
+ * fp16's (bytes 114..140 for every code). */
+int64_t mxfp4_repack_bytes(int64_t E, int64_t N, int64_t K); /* < 0 if invalid */
+nvfp4_status mxfp4_repack(const uint8_t* w_packed, int64_t ld_w, const uint8_t* w_scale, int64_t ld_s,
+                          int64_t E, int64_t N, int64_t K, void* out, int64_t out_bytes, void* stream);
+nvfp4_status mxfp4_w4a16_gemm(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked, void* y,
+                              int64_t ld_y, int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                              void* stream);
+nvfp4_status mxfp4_w4a16_gemm_f16(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked, void* y,
+                                  int64_t ld_y, int64_t M, int64_t N, int64_t K, void* workspace,
+                                  int64_t workspace_bytes, void* stream);
+nvfp4_status mxfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t* expert_offsets, const void* pre_scale,
+                                      const void* w_repacked, void* y, int64_t ld_y, int64_t R, int64_t E, int64_t N,
+                                      int64_t K, void* workspace, int64_t workspace_bytes, void* stream);
+nvfp4_status mxfp4_w4a16_grouped_gemm_f16(const void* x, int64_t ld_x, const int32_t* expert_offsets,
+                                          const void* pre_scale, const void* w_repacked, void* y, int64_t ld_y,
+                                          int64_t R, int64_t E, int64_t N, int64_t K, void* workspace,
+                                          int64_t workspace_bytes, void* stream);
+/* Test exports: the decoded tile (as nvfp4_dequant_bf16, E8M0 scales) and the
+ * dense GEMM with a forced kernel variant (as nvfp4_w4a16_gemm_variant; f16
+ * selects fp16 activations and outputs). */
+nvfp4_status mxfp4_dequant_bf16(const void* w_repacked, int64_t E, int64_t N, int64_t K, void* out, int64_t ld_out,
+                                void* stream);
+nvfp4_status mxfp4_w4a16_gemm_variant(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
+                                      void* y, int64_t ld_y, int64_t M, int64_t N, int64_t K, void* workspace,
+                                      int64_t workspace_bytes, int variant, int f16, void* stream);
+
 /* ---- FP16 activations and outputs ------------------------------------------
  *
  * The same operations with X, the pre-quant scale and Y in IEEE binary16

@@ -23,7 +23,8 @@ import torch
 __all__ = ["repack", "repack_bytes", "gemm", "gemm_variant", "grouped_gemm", "dequant", "lib", "Nvfp4Error",
            "workspace", "gemm_workspace_bytes", "grouped_gemm_gather", "moe_route", "moe_silu_mul", "moe_relu2",
            "moe_combine",
-           "gemm_plan", "gemm_variants", "gemm_noalloc", "stream_read", "VARIANT_AUTO", "VARIANT_SMALL_M", "VARIANT_LARGE_M", "VARIANT_MFMA", "VARIANT_RESIDENT",
+           "gemm_plan", "gemm_variants", "gemm_noalloc", "stream_read", "repack_mxfp4", "dequant_mxfp4",
+           "gemm_mxfp4", "gemm_variant_mxfp4", "grouped_gemm_mxfp4", "VARIANT_AUTO", "VARIANT_SMALL_M", "VARIANT_LARGE_M", "VARIANT_MFMA", "VARIANT_RESIDENT",
            "VARIANT_MFMA_QUARTER", "VARIANT_KERNELS", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4_w4a16.so")
@@ -62,6 +63,15 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_w4a16_gemm_variant.restype = I
         L.nvfp4_w4a16_gemm_plan.argtypes, L.nvfp4_w4a16_gemm_plan.restype = [I64, I64, I64], I
         L.nvfp4_bench_stream_read.argtypes, L.nvfp4_bench_stream_read.restype = [P, I64, P, I64, I, P], I
+        L.mxfp4_repack_bytes.argtypes, L.mxfp4_repack_bytes.restype = [I64, I64, I64], I64
+        L.mxfp4_repack.argtypes, L.mxfp4_repack.restype = [P, I64, P, I64, I64, I64, I64, P, I64, P], I
+        L.mxfp4_dequant_bf16.argtypes, L.mxfp4_dequant_bf16.restype = [P, I64, I64, I64, P, I64, P], I
+        for f in (L.mxfp4_w4a16_gemm, L.mxfp4_w4a16_gemm_f16):
+            f.argtypes, f.restype = [P, I64, P, P, P, I64, I64, I64, I64, P, I64, P], I
+        L.mxfp4_w4a16_gemm_variant.argtypes = [P, I64, P, P, P, I64, I64, I64, I64, P, I64, I, I, P]
+        L.mxfp4_w4a16_gemm_variant.restype = I
+        for f in (L.mxfp4_w4a16_grouped_gemm, L.mxfp4_w4a16_grouped_gemm_f16):
+            f.argtypes, f.restype = [P, I64, P, P, P, P, I64, I64, I64, I64, I64, P, I64, P], I
         L.nvfp4_w4a16_gemm_noalloc.argtypes = [P, I64, P, P, P, I, P, I64, I64, I64, I64, P]
         L.nvfp4_w4a16_gemm_noalloc.restype = I
         L.nvfp4_w4a16_gemm_noalloc_max_scratch_bytes.argtypes = []
@@ -251,6 +261,74 @@ def gemm_noalloc(x, blob, N, K, global_scale, divisor=False, pre_scale=None, out
     M, out = _gemm_args(x, blob, N, K, global_scale, pre_scale, out)
     _check(lib().nvfp4_w4a16_gemm_noalloc(_ptr(x), x.stride(0), _ptr(pre_scale), _ptr(blob), _ptr(global_scale),
                                           int(bool(divisor)), _ptr(out), out.stride(0), M, N, K, _stream(x.device)))
+    return out
+
+
+# -------------------------------------------------------------------- MXFP4 --
+
+def repack_mxfp4(w_packed: torch.Tensor, w_scale: torch.Tensor) -> torch.Tensor:
+    """MXFP4 weights: codes uint8 [(E,) N, K/2] + E8M0 scales uint8 or float8_e8m0fnu [(E,) N, K/32] -> repacked
+    blob (for the *_mxfp4 calls only)."""
+    _dev("w_packed", w_packed, torch.uint8, (2, 3))
+    _dev("w_scale", w_scale, (torch.uint8, torch.float8_e8m0fnu), w_packed.dim())
+    if w_scale.dtype != torch.uint8:
+        w_scale = w_scale.view(torch.uint8)
+    E = w_packed.shape[0] if w_packed.dim() == 3 else 1
+    N, K = w_packed.shape[-2], w_packed.shape[-1] * 2
+    if tuple(w_scale.shape[-2:]) != (N, K // 32) or (w_packed.dim() == 3 and w_scale.shape[0] != E):
+        raise ValueError(f"w_scale shape {tuple(w_scale.shape)} does not match w_packed {tuple(w_packed.shape)} "
+                         "(one E8M0 scale per 32 K)")
+    for name, t in (("w_packed", w_packed), ("w_scale", w_scale)):
+        if w_packed.dim() == 3 and t.stride(0) != t.shape[1] * t.stride(1):
+            raise ValueError(f"{name}: experts must be stored back to back (stride(0) == N * stride(1))")
+    nbytes = int(lib().mxfp4_repack_bytes(E, N, K))
+    if nbytes < 0:
+        raise ValueError(f"invalid MXFP4 weight shape E={E} N={N} K={K} (K must be a positive multiple of 32)")
+    out = torch.empty(nbytes, dtype=torch.uint8, device=w_packed.device)
+    _check(lib().mxfp4_repack(_ptr(w_packed), w_packed.stride(-2), _ptr(w_scale), w_scale.stride(-2), E, N, K,
+                              _ptr(out), nbytes, _stream(w_packed.device)))
+    return out
+
+
+def dequant_mxfp4(blob: torch.Tensor, E: int, N: int, K: int) -> torch.Tensor:
+    """Repacked MXFP4 blob -> bf16 [E, N, K] (e2m1 * e8m0)."""
+    _dev("blob", blob, torch.uint8, 1)
+    out = torch.empty((E, N, K), dtype=torch.bfloat16, device=blob.device)
+    _check(lib().mxfp4_dequant_bf16(_ptr(blob), E, N, K, _ptr(out), K, _stream(blob.device)))
+    return out
+
+
+def gemm_variant_mxfp4(x, blob, N, K, pre_scale=None, out=None, workspace_buf=None, variant=VARIANT_AUTO):
+    """Y[M, N] = (x (.) pre_scale) . dequant_mxfp4(W)^T in x's dtype (bf16 or fp16), no global scale."""
+    one = torch.ones(1, dtype=torch.float32, device=x.device) if isinstance(x, torch.Tensor) and x.is_cuda else None
+    M, out = _gemm_args(x, blob, N, K, one, pre_scale, out)
+    need = gemm_workspace_bytes(M, N, K)
+    if need < 0:
+        raise ValueError(f"invalid GEMM shape M={M} N={N} K={K}")
+    if workspace_buf is None:
+        workspace_buf = workspace(need, x.device)
+    _check(lib().mxfp4_w4a16_gemm_variant(_ptr(x), x.stride(0), _ptr(pre_scale), _ptr(blob), _ptr(out), out.stride(0),
+                                          M, N, K, _ptr(workspace_buf), workspace_buf.numel(), int(variant),
+                                          int(x.dtype == torch.float16), _stream(x.device)))
+    return out
+
+
+def gemm_mxfp4(x, blob, N, K, pre_scale=None, out=None, workspace_buf=None):
+    return gemm_variant_mxfp4(x, blob, N, K, pre_scale, out, workspace_buf, VARIANT_AUTO)
+
+
+def grouped_gemm_mxfp4(x, expert_offsets, blob, E, N, K, pre_scale=None, out=None):
+    """Grouped MXFP4 form: rows [offsets[e], offsets[e+1]) of x use expert e (no global scales)."""
+    _dev("expert_offsets", expert_offsets, torch.int32, 1)
+    if expert_offsets.shape[0] != E + 1 or not expert_offsets.is_contiguous():
+        raise ValueError(f"expert_offsets must be a contiguous int32 [{E + 1}]")
+    if out is None and isinstance(x, torch.Tensor) and x.dtype in _ACT_DTYPES:
+        out = torch.zeros((x.shape[0], N), dtype=x.dtype, device=x.device)
+    one = torch.ones(1, dtype=torch.float32, device=x.device)
+    R, out = _gemm_args(x, blob, N, K, one, pre_scale, out)
+    fn = lib().mxfp4_w4a16_grouped_gemm_f16 if x.dtype == torch.float16 else lib().mxfp4_w4a16_grouped_gemm
+    _check(fn(_ptr(x), x.stride(0), _ptr(expert_offsets), _ptr(pre_scale), _ptr(blob), _ptr(out), out.stride(0), R, E,
+              N, K, None, 0, _stream(x.device)))
     return out
 
 

@@ -10,6 +10,12 @@ import sys
 import tempfile
 from concurrent.futures import ThreadPoolExecutor
 
+if __package__:
+    from . import isa_check
+else:   # run as a script
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from weight_only_fp4_amd import isa_check
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4_w4a16.so")
@@ -22,19 +28,24 @@ COMMON = [
     "-Wall",
 ]
 # (source, extra flags, object tag).  The kernel families are split into
-# translation units per activation type (and pre-scale form for the MFMA-bound
-# kernel) so that they compile in parallel.
+# translation units per activation type (and scale format for the
+# activation-resident and MFMA-bound kernels, pre-scale form for the latter)
+# so that they compile in parallel.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]   # MFMA results in VGPRs (post-processed by VALU)
 SOURCES = [
     ("nvfp4_w4a16.hip", VGPR_FORM, "abi"),
     ("nvfp4_mfma.hip", [], "mfma_plan"),
 ] + [
     (f"gemm_{fam}.hip", VGPR_FORM + [f"-DNVFP4_ACT_F16={f16}"], f"{fam}_{f16}")
-    for fam in ("small", "tile", "xres") for f16 in (0, 1)
+    for fam in ("small", "tile") for f16 in (0, 1)
+] + [
+    # one unit per scale format too (NVFP4 / MXFP4)
+    ("gemm_xres.hip", VGPR_FORM + [f"-DNVFP4_ACT_F16={f16}", f"-DNVFP4_MX={mx}"], f"xres_{f16}{mx}")
+    for f16 in (0, 1) for mx in (0, 1)
 ] + [
     # the MFMA-bound kernel keeps its 256 accumulators in AGPRs
-    ("gemm_mfma.hip", [f"-DNVFP4_ACT_F16={f16}", f"-DNVFP4_PRE={pre}"], f"mfma_{f16}{pre}")
-    for f16 in (0, 1) for pre in (0, 1)
+    ("gemm_mfma.hip", [f"-DNVFP4_ACT_F16={f16}", f"-DNVFP4_PRE={pre}", f"-DNVFP4_MX={mx}"], f"mfma_{f16}{pre}{mx}")
+    for f16 in (0, 1) for pre in (0, 1) for mx in (0, 1)
 ]
 NOISE = "not a recognized feature for this target"
 
@@ -47,15 +58,36 @@ def _run(cmd):
     return msgs
 
 
+# Units whose kernels hold inline-asm MFMAs and copies: their assembly is
+# checked for the wait states the compiler does not insert around those.
+ASM_CHECKED = ("gemm_mfma.hip",)
+
+
+def _check_asm(cmd, path):
+    _run(cmd)
+    with open(path) as f:
+        found = isa_check.hazards(f.read())
+    if found:
+        raise RuntimeError("wait-state violations in the generated assembly of " + " ".join(cmd) + ":\n  "
+                           + "\n  ".join(found[:20]))
+    return ""
+
+
 def build(verbose: bool = False) -> str:
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
     with tempfile.TemporaryDirectory(prefix="nvfp4_build_") as tmpd:
-        jobs = []
+        jobs, checks = [], []
         for src, extra, tag in SOURCES:
             obj = os.path.join(tmpd, tag + ".o")
             jobs.append((obj, [hipcc, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]))
-        with ThreadPoolExecutor(min(len(jobs), max(1, os.cpu_count() or 1))) as ex:
-            outs = list(ex.map(lambda j: (j[1], _run(j[1])), jobs))
+            if src in ASM_CHECKED:
+                asm = os.path.join(tmpd, tag + ".s")
+                checks.append((asm, [hipcc, *COMMON, *extra, "--cuda-device-only", "-S",
+                                     os.path.join(CSRC, src), "-o", asm]))
+        with ThreadPoolExecutor(max(1, os.cpu_count() or 1)) as ex:
+            futs = [ex.submit(lambda j: (j[1], _run(j[1])), j) for j in jobs]
+            futs += [ex.submit(lambda c: (c[1], _check_asm(c[1], c[0])), c) for c in checks]
+            outs = [f.result() for f in futs]
         for cmd, msgs in outs:
             if verbose:
                 print(" ".join(cmd), flush=True)

@@ -33,6 +33,26 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
     return __uint_as_float(__float_as_uint(v) | ((b & 0x80u) << 24));
 }
 
+// E8M0 (OCP MX scale: 2^(e-127), 0xFF NaN) -> fp32, exact: the byte becomes
+// the fp32 exponent field, except 0 (2^-127, an fp32 denormal) and 0xFF.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+    b &= 0xFFu;
+    const uint32_t bits = b == 0u ? 0x00400000u : b == 0xFFu ? 0x7FC00000u : b << 23;
+    return __uint_as_float(bits);
+}
+
+// The two scale bytes of a lane (bits 0..15, low byte = lower k) -> fp32:
+// E4M3 by the hardware conversion (NVFP4), or E8M0 (MXFP4, where both bytes
+// hold the lane's one group scale).  The format is a compile-time choice so
+// that the NVFP4 loops carry no test of it.
+template <bool MX>
+__device__ __forceinline__ f32x2 scale_pair_f32(uint32_t sp) {
+    if constexpr (MX)
+        return f32x2{e8m0_to_f32(sp), e8m0_to_f32(sp >> 8)};
+    else
+        return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sp, 1.0f, false);
+}
+
 // Split a scale s into the operand handed to the exponent-only conversion
 // (its exponent is applied there) and the fp32 factor that completes it:
 // e2m1 * s == (e2m1 * 2^exp(cvt_scale)) * factor, exactly.  Zero and NaN
@@ -259,6 +279,11 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
 // rounded fp32 reciprocal when it is stored as a divisor.
 __device__ __forceinline__ float effective_global_scale(float stored, int is_divisor) {
     return is_divisor ? __fdiv_rn(1.0f, stored) : stored;
+}
+
+// Global scale of expert e; formats without one (MXFP4) pass no pointer: 1.
+__device__ __forceinline__ float global_scale_at(const float* gs, int e, int is_divisor) {
+    return gs ? effective_global_scale(gs[e], is_divisor) : 1.0f;
 }
 
 }  // namespace nvfp4

@@ -1,14 +1,15 @@
-// Launchers of the MFMA-bound kernel (kernels_mfma.h) for one activation type
-// and one pre-scale form: this unit is compiled four times, with
-// NVFP4_ACT_F16 = 0 (bf16) / 1 (fp16) and NVFP4_PRE = 0 / 1, so that its large
-// kernels build in parallel.  It is built without the register-form MFMA
+// Launchers of the MFMA-bound kernel (kernels_mfma.h) for one activation
+// type, one pre-scale form and one scale format: this unit is compiled eight
+// times, with NVFP4_ACT_F16 = 0 (bf16) / 1 (fp16), NVFP4_PRE = 0 / 1 and
+// NVFP4_MX = 0 (NVFP4) / 1 (MXFP4), so that its large kernels build in
+// parallel.  It is built without the register-form MFMA
 // flag of the other units (this kernel keeps its accumulators in the
 // accumulation registers).
 #include "kernels_mfma.h"
 #include "launch_mfma.h"
 
-#if !defined(NVFP4_ACT_F16) || !defined(NVFP4_PRE)
-#error "compile with -DNVFP4_ACT_F16=0|1 and -DNVFP4_PRE=0|1"
+#if !defined(NVFP4_ACT_F16) || !defined(NVFP4_PRE) || !defined(NVFP4_MX)
+#error "compile with -DNVFP4_ACT_F16=0|1, -DNVFP4_PRE=0|1 and -DNVFP4_MX=0|1"
 #endif
 
 namespace nvfp4 {
@@ -19,6 +20,7 @@ namespace {
 
 constexpr bool kF16 = NVFP4_ACT_F16 != 0;
 constexpr bool kPre = NVFP4_PRE != 0;
+constexpr bool kMx = NVFP4_MX != 0;
 
 template <int MS, bool KFULL>
 hipError_t launch_part(int64_t wgs, int64_t t0, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
@@ -27,7 +29,7 @@ hipError_t launch_part(int64_t wgs, int64_t t0, const Layout& L, const uint16_t*
     if (wgs == 0) return hipSuccess;
     // 16-byte output stores need 16-byte aligned rows
     const int vec = (ld_y % 8 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
-    hipLaunchKernelGGL((k_gemm_mfma<MS, KFULL, kF16, kPre>), dim3((unsigned)wgs), dim3(kMfmaWN * 64), 0, st, x, ld_x,
+    hipLaunchKernelGGL((k_gemm_mfma<MS, KFULL, kF16, kPre, kMx>), dim3((unsigned)wgs), dim3(kMfmaWN * 64), 0, st, x, ld_x,
                        make_view(L, blob), (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, gs, g_div, y, ld_y, (int)M,
                        (int)t0, vec, pre);
     return hipGetLastError();
@@ -46,16 +48,17 @@ hipError_t launch_k(const MfmaPlan& p, const Layout& L, const uint16_t* x, int64
 
 }  // namespace
 
-template <bool F16, bool PRE>
+template <bool F16, bool PRE, bool MX>
 hipError_t launch_mfma_t(const MfmaPlan& p, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
                          const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t M, const uint16_t* pre,
                          bool quarter, hipStream_t st) {
-    static_assert(F16 == kF16 && PRE == kPre, "this unit holds one form");
+    static_assert(F16 == kF16 && PRE == kPre && MX == kMx, "this unit holds one form");
+    if (L.mx != (int)MX) return hipErrorInvalidValue;
     return L.K % kChunkK == 0 ? launch_k<true>(p, L, x, ld_x, blob, gs, g_div, y, ld_y, M, pre, quarter, st)
                               : launch_k<false>(p, L, x, ld_x, blob, gs, g_div, y, ld_y, M, pre, quarter, st);
 }
 
-template hipError_t launch_mfma_t<kF16, kPre>(const MfmaPlan&, const Layout&, const uint16_t*, int64_t, const uint8_t*,
+template hipError_t launch_mfma_t<kF16, kPre, kMx>(const MfmaPlan&, const Layout&, const uint16_t*, int64_t, const uint8_t*,
                                               const float*, int, uint16_t*, int64_t, int64_t, const uint16_t*, bool,
                                               hipStream_t);
 

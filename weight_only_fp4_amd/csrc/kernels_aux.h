@@ -8,12 +8,14 @@ namespace nvfp4 {
 // One thread per (expert, row unit, K chunk, lane): gathers the 16 canonical
 // code bytes and the 2 scale bytes the lane owns in the repacked layout and
 // writes them with one 128-bit and one 16-bit store.  Positions past N or K
-// are written as zero.
+// are written as zero.  mx: the scales are E8M0 bytes, one per 32 K (ld_s >=
+// K / 32); the lane's 32-wide K group is one MXFP4 group and both of its
+// scale bytes take that group's byte.
 __global__ void __launch_bounds__(256) k_repack(const uint8_t* __restrict__ w, int64_t ld_w,
                                                 const uint8_t* __restrict__ s, int64_t ld_s,
                                                 int64_t N, int64_t K, int64_t NU, int64_t KC, int64_t total_lanes,
                                                 BlobView v, uint8_t* __restrict__ codes_out,
-                                                uint8_t* __restrict__ scales_out) {
+                                                uint8_t* __restrict__ scales_out, int mx) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= total_lanes) return;
     const int lane = (int)(t & 63);
@@ -37,18 +39,24 @@ __global__ void __launch_bounds__(256) k_repack(const uint8_t* __restrict__ w, i
             q[i >> 2] |= b << (8 * (i & 3));
         }
         const uint8_t* srow = s + (e * N + n) * ld_s;
-        const int64_t sb0 = c * (kChunkK / 16) + (lane >> 4) * 2;
-        const int64_t nblk = K / 16;
-        const uint32_t s0 = (sb0 < nblk) ? (uint32_t)srow[sb0] : 0u;
-        const uint32_t s1 = (sb0 + 1 < nblk) ? (uint32_t)srow[sb0 + 1] : 0u;
-        sc = s0 | (s1 << 8);
+        if (mx) {
+            const int64_t sb = c * (kChunkK / 32) + (lane >> 4);
+            const uint32_t s0 = (sb < K / 32) ? (uint32_t)srow[sb] : 0u;
+            sc = s0 | (s0 << 8);
+        } else {
+            const int64_t sb0 = c * (kChunkK / 16) + (lane >> 4) * 2;
+            const int64_t nblk = K / 16;
+            const uint32_t s0 = (sb0 < nblk) ? (uint32_t)srow[sb0] : 0u;
+            const uint32_t s1 = (sb0 + 1 < nblk) ? (uint32_t)srow[sb0 + 1] : 0u;
+            sc = s0 | (s1 << 8);
+        }
     }
     *reinterpret_cast<uint4*>(codes_out + blk * kCodeBlock + lane * 16) = make_uint4(q[0], q[1], q[2], q[3]);
     *reinterpret_cast<uint16_t*>(scales_out + blk * kScaleBlock + lane * 2) = (uint16_t)sc;
 }
 
 // Decode a repacked blob to bf16 [E][N][ld_out] with the GEMM kernels' decode
-// (decode8_bf16).  One thread per (expert, row unit, K chunk, lane).
+// (decode8_bf16; E4M3 or, with v.mx, E8M0 scales).  One thread per (expert, row unit, K chunk, lane).
 __global__ void __launch_bounds__(256) k_dequant(BlobView v, int64_t N, int64_t K, int64_t NU, int64_t KC,
                                                  int64_t total_lanes, uint16_t* __restrict__ out, int64_t ld_out) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -64,7 +72,8 @@ __global__ void __launch_bounds__(256) k_dequant(BlobView v, int64_t N, int64_t 
     if (n >= N) return;
     const uint4 q = *reinterpret_cast<const uint4*>(v.codes + blk * kCodeBlock + lane * 16);
     const uint32_t sc = *reinterpret_cast<const uint16_t*>(v.scales + blk * kScaleBlock + lane * 2);
-    const float s0 = e4m3_to_f32(sc & 0xFFu), s1 = e4m3_to_f32(sc >> 8);
+    const float s0 = v.mx ? e8m0_to_f32(sc) : e4m3_to_f32(sc & 0xFFu);
+    const float s1 = v.mx ? e8m0_to_f32(sc >> 8) : e4m3_to_f32(sc >> 8);
     const uint32_t qd[4] = {q.x, q.y, q.z, q.w};
     const int64_t k0 = c * kChunkK + (lane >> 4) * 32;
     uint16_t* row = out + (e * N + n) * ld_out;

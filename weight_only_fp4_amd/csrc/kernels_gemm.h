@@ -90,12 +90,21 @@ struct SmallSlot {
 };
 
 // Scale table in LDS: entry b = {operand for the exponent-only conversion,
-// remaining fp32 factor} of E4M3 byte b (split_scale).  Two LDS reads per
-// lane and chunk replace the bit decoding of its two scales.
-__device__ __forceinline__ void build_scale_table(float2* lut) {
+// remaining fp32 factor} of scale byte b (split_scale), an E4M3 byte or, with
+// mx, an E8M0 byte (a power of two: the conversion applies all of it and the
+// factor is 1, except 2^-127, an fp32 denormal, carried by the factor, and
+// NaN).  Two LDS reads per lane and chunk replace the bit decoding of its two
+// scales.
+__device__ __forceinline__ void build_scale_table(float2* lut, int mx) {
     for (int b = threadIdx.x; b < 256; b += blockDim.x) {
         float cs, f;
-        split_scale(e4m3_to_f32((uint32_t)b), cs, f);
+        if (mx) {
+            const bool special = b == 0 || b == 255;
+            cs = special ? 1.0f : e8m0_to_f32((uint32_t)b);
+            f = special ? e8m0_to_f32((uint32_t)b) : 1.0f;
+        } else {
+            split_scale(e4m3_to_f32((uint32_t)b), cs, f);
+        }
         lut[b] = make_float2(cs, f);
     }
 }
@@ -388,7 +397,7 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
     bool first = true;
     auto mid = [&]() {
         if (first) {
-            build_scale_table(lut);
+            build_scale_table(lut, bv.mx);
             // scale table ready.  Only LDS writes need to be visible, so the
             // barrier waits for lgkmcnt alone: the compiler's own barrier
             // would wait for every outstanding load (the ring's first slots)
@@ -418,7 +427,7 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
                                                                       RLD, lane, mid, rix);
         }
         __syncthreads();
-        const float gv = effective_global_scale(gscale[e], g_is_div);
+        const float gv = global_scale_at(gscale, e, g_is_div);
         auto store_y = [&](int t, float acc) {
             const int r = t / RLD, col = t % RLD;
             const int64_t n = (int64_t)u0 * kUnitN + col;

@@ -58,10 +58,20 @@ __device__ __forceinline__ void lds_copy16(uint32_t lds, const uint8_t* base, ui
 // acc += A . B for one 16 x 16 x 32 bf16 step, accumulating in place in
 // accumulation registers.  Written as inline assembly because the compiler,
 // left to itself, renames most accumulators of a 256-accumulator tile in
-// every chunk and copies them back through VGPRs at the loop edge.  The
-// compiler cannot see this hazard-wise: its operands are produced at least
-// one issue group before use, and the accumulators are read only after the
-// drain in mfma_drain.
+// every chunk and copies them back through VGPRs at the loop edge.
+//
+// The compiler inserts no wait states around an MFMA it cannot see.  CDNA3
+// and CDNA4 need two between a VALU write of a VGPR and an MFMA reading it as
+// a source; the issue groups below produce every operand at least one group
+// ahead, which the scheduler keeps apart in every form built, but only the
+// generated code can show it: the library build checks the assembly of every
+// form of this kernel (isa_check.py) and refuses to link one in which an
+// operand is written fewer than two wait states before its MFMA (a stale
+// operand read then depends on how the waves of the compute unit happen to
+// issue).  A fixed s_nop here would cost about a tenth of the prefill rate,
+// the loop being bound by instruction issue.  The accumulators are only ever
+// written by these statements (same size, full overlap: no wait needed
+// between them) and read after the drain in mfma_drain.
 template <bool F16>
 __device__ __forceinline__ void mfma_acc(f32x4& acc, const uint4& a, const uint4& b) {
     if constexpr (F16)
@@ -139,7 +149,7 @@ __device__ __forceinline__ void mfma_tile(int t, int MT, int NTn, int& mt, int& 
 // outcome depends on timing, and so on what else shares the compute unit).
 // The wave drains every copy before it exits, so no copy can land in the LDS
 // of a workgroup that starts on the compute unit after it.
-template <int MS, bool KFULL, bool F16 = false, bool PRE = false>
+template <int MS, bool KFULL, bool F16 = false, bool PRE = false, bool MX = false>
 __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                         int NU, int KC, int K, int N, const float* __restrict__ gscale,
                                                         int g_is_div, uint16_t* __restrict__ y, int64_t ld_y, int M,
@@ -321,7 +331,7 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
         }
     };
     auto scale_op = [&](const BRegs& b, int u) {   // scales of unit u of chunk b
-        const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(scale_pair(b.sw[u], lane), 1.0f, false);   // E4M3 x 2
+        const f32x2 v = scale_pair_f32<MX>(scale_pair(b.sw[u], lane));   // E4M3 (E8M0) x 2
         s0[u] = v.x;
         s1[u] = v.y;
     };
@@ -456,7 +466,7 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     // transposed across the four lane rows g and the four units j with two
     // lane-swap rounds, after which lane row g holds the 16 adjacent columns
     // 16 (u_w + g) .. + 15 of its row: two 16-byte stores per row block.
-    const float gv = effective_global_scale(gscale[0], g_is_div);
+    const float gv = global_scale_at(gscale, 0, g_is_div);
     static_for<0, MS>([&](auto msc) {
         constexpr int ms = decltype(msc)::value;
         uint32_t pk[NT][2];   // bf16 pairs of columns 4 g + 2 d, + 1 of unit j (then of unit g: 4 j + 2 d)

@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
         rows = rows_dense - row0;
     }
     if (rows > BM) rows = BM;
-    build_scale_table(lut);
+    build_scale_table(lut, bv.mx);
 
     // ---- K ranges: split s of the workgroup (grid z), part q of the wave
     const int S = sk.S, s = (int)blockIdx.z;
@@ -285,7 +285,7 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
         }
     }
 
-    const float gv = effective_global_scale(gscale[e], g_is_div);
+    const float gv = global_scale_at(gscale, e, g_is_div);
     // lane (r, g) of a part-0 wave holds rows 16 ms + 4 g + i of column 16 (u_w + j) + r
     auto store_y = [&]() {
 #pragma unroll

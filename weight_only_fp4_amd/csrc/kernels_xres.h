@@ -42,7 +42,7 @@ namespace nvfp4 {
 constexpr int kXresRowBytes = 256 + 16;                // one row of a staged chunk, padded
 constexpr int kXresWaveBytes = 16 * kXresRowBytes;     // a wave's staging area
 
-template <int CH, int U, int W, int D, bool FULL, bool F16 = false, bool PRE = false>
+template <int CH, int U, int W, int D, bool FULL, bool F16 = false, bool PRE = false, bool MX = false>
 __global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                       int NU, int KC, int K, int N, const float* __restrict__ gscale,
                                                       int g_is_div, uint16_t* __restrict__ y, int64_t ld_y, int rows,
@@ -137,7 +137,7 @@ __global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict
             load_item(it + DR, slot);
             __builtin_amdgcn_sched_barrier(0);
         }
-        f32x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(scale_pair(sv, lane), 1.0f, false);
+        f32x2 sc = scale_pair_f32<MX>(scale_pair(sv, lane));
         if (!FULL) {
             const bool have = c < nch;
             sc.x = have ? sc.x : 0.f;
@@ -198,7 +198,7 @@ __global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict
             v[j] = a;
         }
     }
-    const float gv = effective_global_scale(gscale[0], g_is_div);
+    const float gv = global_scale_at(gscale, 0, g_is_div);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int o = tid + j * W * 64, m = (o >> 4) & 15;

@@ -31,9 +31,10 @@ hipError_t launch_gemm_mfma(const MfmaPlan& plan, const Layout& L, const uint16_
                             const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t M, const uint16_t* pre,
                             bool quarter, hipStream_t st, bool f16);
 
-// The launch of one activation type (F16) and pre-scale form (PRE), defined
-// in the gemm_mfma.hip unit compiled for that form.
-template <bool F16, bool PRE>
+// The launch of one activation type (F16), pre-scale form (PRE) and scale
+// format (MX: E8M0 per 32, else E4M3 per 16), defined in the gemm_mfma.hip
+// unit compiled for that form.
+template <bool F16, bool PRE, bool MX>
 hipError_t launch_mfma_t(const MfmaPlan& plan, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
                          const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t M, const uint16_t* pre,
                          bool quarter, hipStream_t st);

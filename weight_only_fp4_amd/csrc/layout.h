@@ -19,6 +19,12 @@
 //
 // Total size: E * NU * KC * 1152 bytes, i.e. 0.5625 bytes per weight plus
 // padding.
+//
+// MXFP4 weights (one E8M0 scale per 32 K) use the same layout: a lane's 32
+// codes are exactly one MXFP4 group, and both of its scale bytes hold that
+// group's E8M0 byte.  The blob does not record its format; `mx` in the
+// layout and the view (set by the mxfp4_* entry points) selects the scale
+// decode.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -39,6 +45,7 @@ struct Layout {
     int64_t E, N, K;
     int64_t NU;   // row units (ceil(N / 16))
     int64_t KC;   // K chunks (ceil(K / 128))
+    int mx;       // scale bytes are E8M0 (MXFP4), not E4M3 (NVFP4)
     int64_t blocks() const { return E * NU * KC; }
     int64_t code_bytes() const { return blocks() * kCodeBlock; }
     int64_t total_bytes() const { return blocks() * (kCodeBlock + kScaleBlock); }
@@ -46,8 +53,8 @@ struct Layout {
     int64_t chunk_stride() const { return kChunkMajor ? NU : 1; }   // in blocks
 };
 
-inline Layout make_layout(int64_t E, int64_t N, int64_t K) {
-    return Layout{E, N, K, (N + kUnitN - 1) / kUnitN, (K + kChunkK - 1) / kChunkK};
+inline Layout make_layout(int64_t E, int64_t N, int64_t K, int mx = 0) {
+    return Layout{E, N, K, (N + kUnitN - 1) / kUnitN, (K + kChunkK - 1) / kChunkK, mx};
 }
 
 // What a kernel needs to address the blocks of a repacked blob.
@@ -57,13 +64,14 @@ struct BlobView {
     int64_t expert_blocks;   // blocks per expert (NU * KC)
     int64_t unit_stride;     // blocks between consecutive row units
     int64_t chunk_stride;    // blocks between consecutive K chunks
+    int mx;                  // scale bytes are E8M0 (MXFP4), not E4M3 (NVFP4)
     __host__ __device__ int64_t block(int64_t e, int64_t u, int64_t c) const {
         return e * expert_blocks + u * unit_stride + c * chunk_stride;
     }
 };
 
 inline BlobView make_view(const Layout& L, const uint8_t* blob) {
-    return BlobView{blob, blob + L.code_bytes(), L.NU * L.KC, L.unit_stride(), L.chunk_stride()};
+    return BlobView{blob, blob + L.code_bytes(), L.NU * L.KC, L.unit_stride(), L.chunk_stride(), L.mx};
 }
 
 }  // namespace nvfp4

@@ -34,11 +34,19 @@ MfmaPlan mfma_plan(const Layout& L, int64_t M) {
 hipError_t launch_gemm_mfma(const MfmaPlan& p, const Layout& L, const uint16_t* x, int64_t ld_x, const uint8_t* blob,
                             const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t M, const uint16_t* pre,
                             bool quarter, hipStream_t st, bool f16) {
-    if (f16)
-        return pre ? launch_mfma_t<true, true>(p, L, x, ld_x, blob, gs, g_div, y, ld_y, M, pre, quarter, st)
-                   : launch_mfma_t<true, false>(p, L, x, ld_x, blob, gs, g_div, y, ld_y, M, pre, quarter, st);
-    return pre ? launch_mfma_t<false, true>(p, L, x, ld_x, blob, gs, g_div, y, ld_y, M, pre, quarter, st)
-               : launch_mfma_t<false, false>(p, L, x, ld_x, blob, gs, g_div, y, ld_y, M, pre, quarter, st);
+#define NVFP4_MFMA_FORM(F16, PRE, MX) \
+    return launch_mfma_t<F16, PRE, MX>(p, L, x, ld_x, blob, gs, g_div, y, ld_y, M, pre, quarter, st)
+#define NVFP4_MFMA_PRE(F16, MX) \
+    if (pre) NVFP4_MFMA_FORM(F16, true, MX); \
+    NVFP4_MFMA_FORM(F16, false, MX)
+    if (f16) {
+        if (L.mx) { NVFP4_MFMA_PRE(true, true); }
+        NVFP4_MFMA_PRE(true, false);
+    }
+    if (L.mx) { NVFP4_MFMA_PRE(false, true); }
+    NVFP4_MFMA_PRE(false, false);
+#undef NVFP4_MFMA_PRE
+#undef NVFP4_MFMA_FORM
 }
 
 }  // namespace nvfp4

@@ -50,9 +50,12 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-nvfp4_status check_weight_shape(const char* fn, int64_t E, int64_t N, int64_t K) {
+// mx: MXFP4 weights (one E8M0 scale per 32 K) instead of NVFP4 (one E4M3 per 16).
+nvfp4_status check_weight_shape(const char* fn, int64_t E, int64_t N, int64_t K, int mx = 0) {
     if (E < 1 || E > kMaxExperts) return fail(NVFP4_ERR_INVALID_ARG, "%s: E = %lld must be in [1, %d]", fn, (long long)E, kMaxExperts);
     if (N < 0 || N > (int64_t)1 << 30) return fail(NVFP4_ERR_INVALID_ARG, "%s: N = %lld must be in [0, 2^30]", fn, (long long)N);
+    if (mx && (K < 32 || K % 32 != 0 || K > (int64_t)1 << 30))
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: K = %lld must be a positive multiple of 32 (one E8M0 scale per 32 K)", fn, (long long)K);
     if (K < 16 || K % 16 != 0 || K > (int64_t)1 << 30)
         return fail(NVFP4_ERR_INVALID_ARG, "%s: K = %lld must be a positive multiple of 16 (one E4M3 scale per 16 K)", fn, (long long)K);
     return NVFP4_OK;
@@ -73,15 +76,16 @@ constexpr int64_t kMfmaAuto = 256;
 constexpr int64_t kMfmaMinTiles = 48;
 
 // Shared checks of the activation / output / pre-scale / workspace arguments.
+// no_global: the format has no global scale (MXFP4; gs is NULL).
 nvfp4_status check_gemm_io(const char* fn, const void* x, int64_t ld_x, const void* pre, const void* w,
                            const void* gs, const void* y, int64_t ld_y, int64_t rows, int64_t N, int64_t K,
-                           const void* ws, int64_t ws_bytes, int64_t ws_need) {
+                           const void* ws, int64_t ws_bytes, int64_t ws_need, bool no_global = false) {
     if (rows < 0) return fail(NVFP4_ERR_INVALID_ARG, "%s: row count %lld is negative", fn, (long long)rows);
     if (ld_x < K) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_x = %lld < K = %lld", fn, (long long)ld_x, (long long)K);
     if (ld_y < N) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_y = %lld < N = %lld", fn, (long long)ld_y, (long long)N);
     // with no output columns (N == 0) the weights and the output hold no bytes
     if (!w && N > 0) return fail(NVFP4_ERR_INVALID_ARG, "%s: w_repacked is NULL", fn);
-    if (!gs) return fail(NVFP4_ERR_INVALID_ARG, "%s: global scale pointer is NULL", fn);
+    if (!gs && !no_global) return fail(NVFP4_ERR_INVALID_ARG, "%s: global scale pointer is NULL", fn);
     if (rows > 0 && !x) return fail(NVFP4_ERR_INVALID_ARG, "%s: x is NULL", fn);
     if (rows > 0 && N > 0 && !y) return fail(NVFP4_ERR_INVALID_ARG, "%s: y is NULL", fn);
     if (ld_x > kMaxLdX)
@@ -135,16 +139,23 @@ const char* const kXresLimits =
     "M <= 16, K <= 32768 and ceil(N / 16) * ceil(K / 4096) <= 2048 (at most eight 16-row units per workgroup "
     "for about one workgroup per compute unit)";
 
+// The activation-resident launch for the blob's scale format and the
+// activation type.
+nvfp4_status launch_xres_any(const XresShape& s, const Layout& L, const GemmArgs& a, bool f16) {
+    if (f16) return L.mx ? launch_xres<true, true>(s, L, a) : launch_xres<true, false>(s, L, a);
+    return L.mx ? launch_xres<false, true>(s, L, a) : launch_xres<false, false>(s, L, a);
+}
+
 nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void* w, const float* gs, int g_div,
                         void* y, int64_t ld_y, int64_t M, int64_t N, int64_t K, void* ws, int64_t ws_bytes,
-                        int variant, void* stream, const char* fn, bool f16) {
-    nvfp4_status s = check_weight_shape(fn, 1, N, K);
+                        int variant, void* stream, const char* fn, bool f16, int mx = 0) {
+    nvfp4_status s = check_weight_shape(fn, 1, N, K, mx);
     if (s != NVFP4_OK) return s;
     if (variant < kAuto || variant > kMfmaQuarter) return fail(NVFP4_ERR_INVALID_ARG, "%s: unknown variant %d", fn, variant);
     if (variant == kSmall && M > kSmallRows)
         return fail(NVFP4_ERR_INVALID_ARG, "%s: the small-M variant takes M <= %d (M = %lld)", fn, kSmallRows, (long long)M);
     if (M > (int64_t)1 << 31) return fail(NVFP4_ERR_INVALID_ARG, "%s: M = %lld too large", fn, (long long)M);
-    const Layout L = make_layout(1, N, K);
+    const Layout L = make_layout(1, N, K, mx);
     const bool empty = M == 0 || N == 0;
     if (variant == kResident && !empty && !xres_fits(L, M))
         return fail(NVFP4_ERR_INVALID_ARG, "%s: the activation-resident variant takes %s (M = %lld, N = %lld, K = %lld)",
@@ -172,7 +183,7 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
     if (split_tiles > kMaxSplitTiles)   // the planners never split grids this large
         return fail(NVFP4_ERR_INVALID_ARG, "%s: %lld split-K tiles exceed the %lld counters of a workspace", fn,
                     (long long)split_tiles, (long long)kMaxSplitTiles);
-    s = check_gemm_io(fn, x, ld_x, pre, w, gs, y, ld_y, M, N, K, ws, ws_bytes, wl.total);
+    s = check_gemm_io(fn, x, ld_x, pre, w, gs, y, ld_y, M, N, K, ws, ws_bytes, wl.total, mx != 0);
     if (s != NVFP4_OK) return s;
     if (empty) return ok();   // zero rows or zero columns: nothing is launched
     uint8_t* wsb = static_cast<uint8_t*>(ws);
@@ -183,7 +194,7 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
         case kResident: {
             const XresShape xs = xres_shape(L, M);
             a.sk = split_k(xs.S, wsb, wl);
-            return f16 ? launch_xres<true>(xs, L, a) : launch_xres<false>(xs, L, a);
+            return launch_xres_any(xs, L, a, f16);
         }
         case kSmall: {
             const SmallShape sm = small_m_shape(L, M, false);
@@ -213,17 +224,17 @@ nvfp4_status grouped_gemm(const char* fn, const void* x, int64_t ld_x, const int
                           const int32_t* expert_offsets, const void* pre_scale, const void* w_repacked,
                           const float* global_scales, int global_scale_is_divisor, void* y, int64_t ld_y, int64_t R,
                           int64_t E, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes, void* stream,
-                          bool f16) {
-    nvfp4_status s = check_weight_shape(fn, E, N, K);
+                          bool f16, int mx = 0) {
+    nvfp4_status s = check_weight_shape(fn, E, N, K, mx);
     if (s != NVFP4_OK) return s;
     s = check_gemm_io(fn, x, ld_x, pre_scale, w_repacked, global_scales, y, ld_y, R, N, K, workspace, workspace_bytes,
-                      0);
+                      0, mx != 0);
     if (s != NVFP4_OK) return s;
     if (!expert_offsets) return fail(NVFP4_ERR_INVALID_ARG, "%s: expert_offsets is NULL", fn);
     if (!aligned(expert_offsets, 4)) return fail(NVFP4_ERR_ALIGNMENT, "%s: expert_offsets must be 4-byte aligned", fn);
     if (R > (int64_t)1 << 31) return fail(NVFP4_ERR_INVALID_ARG, "%s: R = %lld exceeds int32 offsets", fn, (long long)R);
     if (R == 0 || N == 0) return ok();   // zero rows or zero columns: nothing is launched
-    const Layout L = make_layout(E, N, K);
+    const Layout L = make_layout(E, N, K, mx);
     const GemmArgs a{static_cast<const uint16_t*>(x), ld_x, static_cast<const uint8_t*>(w_repacked), global_scales,
                      global_scale_is_divisor != 0, static_cast<uint16_t*>(y), ld_y, R, expert_offsets, row_index,
                      static_cast<const uint16_t*>(pre_scale), SplitK{1, nullptr, nullptr},
@@ -311,43 +322,63 @@ int64_t nvfp4_repack_bytes(int64_t E, int64_t N, int64_t K) {
     return make_layout(E, N, K).total_bytes();
 }
 
-nvfp4_status nvfp4_repack(const uint8_t* w_packed, int64_t ld_w, const uint8_t* w_scale, int64_t ld_s, int64_t E,
-                          int64_t N, int64_t K, void* out, int64_t out_bytes, void* stream) {
-    const char* fn = "nvfp4_repack";
-    nvfp4_status s = check_weight_shape(fn, E, N, K);
+}  // extern "C"
+
+namespace {
+
+nvfp4_status repack_impl(const char* fn, const uint8_t* w_packed, int64_t ld_w, const uint8_t* w_scale, int64_t ld_s,
+                         int64_t E, int64_t N, int64_t K, void* out, int64_t out_bytes, void* stream, int mx) {
+    nvfp4_status s = check_weight_shape(fn, E, N, K, mx);
     if (s != NVFP4_OK) return s;
     if (N == 0) return ok();   // no rows: nothing to repack, nothing is launched
     if (!w_packed) return fail(NVFP4_ERR_INVALID_ARG, "%s: w_packed is NULL", fn);
     if (!w_scale) return fail(NVFP4_ERR_INVALID_ARG, "%s: w_scale is NULL", fn);
     if (!out) return fail(NVFP4_ERR_INVALID_ARG, "%s: out is NULL", fn);
     if (ld_w < K / 2) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_w = %lld < K/2 = %lld", fn, (long long)ld_w, (long long)(K / 2));
-    if (ld_s < K / 16) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_s = %lld < K/16 = %lld", fn, (long long)ld_s, (long long)(K / 16));
+    const int64_t group = mx ? 32 : 16;
+    if (ld_s < K / group)
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_s = %lld < K/%lld = %lld", fn, (long long)ld_s, (long long)group,
+                    (long long)(K / group));
     if (!aligned(out, 16)) return fail(NVFP4_ERR_ALIGNMENT, "%s: out must be 16-byte aligned", fn);
-    const Layout L = make_layout(E, N, K);
+    const Layout L = make_layout(E, N, K, mx);
     if (out_bytes < L.total_bytes())
         return fail(NVFP4_ERR_BUFFER_TOO_SMALL, "%s: out_bytes = %lld < %lld", fn, (long long)out_bytes, (long long)L.total_bytes());
     const int64_t lanes = L.blocks() * 64;
     uint8_t* o = static_cast<uint8_t*>(out);
     hipLaunchKernelGGL(k_repack, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       w_packed, ld_w, w_scale, ld_s, N, K, L.NU, L.KC, lanes, make_view(L, o), o, o + L.code_bytes());
+                       w_packed, ld_w, w_scale, ld_s, N, K, L.NU, L.KC, lanes, make_view(L, o), o, o + L.code_bytes(),
+                       mx);
     return launched(fn);
 }
 
-nvfp4_status nvfp4_dequant_bf16(const void* w_repacked, int64_t E, int64_t N, int64_t K, void* out, int64_t ld_out,
-                                void* stream) {
-    const char* fn = "nvfp4_dequant_bf16";
-    nvfp4_status s = check_weight_shape(fn, E, N, K);
+nvfp4_status dequant_impl(const char* fn, const void* w_repacked, int64_t E, int64_t N, int64_t K, void* out,
+                          int64_t ld_out, void* stream, int mx) {
+    nvfp4_status s = check_weight_shape(fn, E, N, K, mx);
     if (s != NVFP4_OK) return s;
     if (N == 0) return ok();
     if (!w_repacked || !out) return fail(NVFP4_ERR_INVALID_ARG, "%s: NULL pointer", fn);
     if (ld_out < K) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_out = %lld < K", fn, (long long)ld_out);
     if (!aligned(w_repacked, 16) || !aligned(out, 2)) return fail(NVFP4_ERR_ALIGNMENT, "%s: misaligned pointer", fn);
-    const Layout L = make_layout(E, N, K);
+    const Layout L = make_layout(E, N, K, mx);
     const int64_t lanes = L.blocks() * 64;
     const uint8_t* b = static_cast<const uint8_t*>(w_repacked);
     hipLaunchKernelGGL(k_dequant, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, static_cast<hipStream_t>(stream),
                        make_view(L, b), N, K, L.NU, L.KC, lanes, static_cast<uint16_t*>(out), ld_out);
     return launched(fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_repack(const uint8_t* w_packed, int64_t ld_w, const uint8_t* w_scale, int64_t ld_s, int64_t E,
+                          int64_t N, int64_t K, void* out, int64_t out_bytes, void* stream) {
+    return repack_impl("nvfp4_repack", w_packed, ld_w, w_scale, ld_s, E, N, K, out, out_bytes, stream, 0);
+}
+
+nvfp4_status nvfp4_dequant_bf16(const void* w_repacked, int64_t E, int64_t N, int64_t K, void* out, int64_t ld_out,
+                                void* stream) {
+    return dequant_impl("nvfp4_dequant_bf16", w_repacked, E, N, K, out, ld_out, stream, 0);
 }
 
 nvfp4_status nvfp4_bench_stream_read(const void* p, int64_t bytes, uint32_t* out, int64_t workgroups, int unroll,
@@ -575,6 +606,62 @@ nvfp4_status nvfp4_w4a16_gemm_noalloc(const void* x, int64_t ld_x, const void* p
     }
     return dense_gemm(x, ld_x, pre_scale, w_repacked, global_scale, global_scale_is_divisor != 0, y, ld_y, M, N, K,
                       ws, need > 0 ? kScratchBytes : 0, kAuto, stream, fn, false);
+}
+
+// ---------------------------------------------------------------- MXFP4 --
+// The same GEMMs on MXFP4 weights: one E8M0 scale per 32 K and no global
+// scale.  Repacked into the NVFP4 layout (the blob size and the workspace
+// sizes are those of the NVFP4 calls), decoded with E8M0 scales.
+
+int64_t mxfp4_repack_bytes(int64_t E, int64_t N, int64_t K) {
+    if (check_weight_shape("mxfp4_repack_bytes", E, N, K, 1) != NVFP4_OK) return -1;
+    return make_layout(E, N, K, 1).total_bytes();
+}
+
+nvfp4_status mxfp4_repack(const uint8_t* w_packed, int64_t ld_w, const uint8_t* w_scale, int64_t ld_s, int64_t E,
+                          int64_t N, int64_t K, void* out, int64_t out_bytes, void* stream) {
+    return repack_impl("mxfp4_repack", w_packed, ld_w, w_scale, ld_s, E, N, K, out, out_bytes, stream, 1);
+}
+
+nvfp4_status mxfp4_dequant_bf16(const void* w_repacked, int64_t E, int64_t N, int64_t K, void* out, int64_t ld_out,
+                                void* stream) {
+    return dequant_impl("mxfp4_dequant_bf16", w_repacked, E, N, K, out, ld_out, stream, 1);
+}
+
+nvfp4_status mxfp4_w4a16_gemm(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked, void* y,
+                              int64_t ld_y, int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                              void* stream) {
+    return dense_gemm(x, ld_x, pre_scale, w_repacked, nullptr, 0, y, ld_y, M, N, K, workspace, workspace_bytes, kAuto,
+                      stream, "mxfp4_w4a16_gemm", false, 1);
+}
+
+nvfp4_status mxfp4_w4a16_gemm_f16(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked, void* y,
+                                  int64_t ld_y, int64_t M, int64_t N, int64_t K, void* workspace,
+                                  int64_t workspace_bytes, void* stream) {
+    return dense_gemm(x, ld_x, pre_scale, w_repacked, nullptr, 0, y, ld_y, M, N, K, workspace, workspace_bytes, kAuto,
+                      stream, "mxfp4_w4a16_gemm_f16", true, 1);
+}
+
+nvfp4_status mxfp4_w4a16_gemm_variant(const void* x, int64_t ld_x, const void* pre_scale, const void* w_repacked,
+                                      void* y, int64_t ld_y, int64_t M, int64_t N, int64_t K, void* workspace,
+                                      int64_t workspace_bytes, int variant, int f16, void* stream) {
+    return dense_gemm(x, ld_x, pre_scale, w_repacked, nullptr, 0, y, ld_y, M, N, K, workspace, workspace_bytes,
+                      variant, stream, "mxfp4_w4a16_gemm_variant", f16 != 0, 1);
+}
+
+nvfp4_status mxfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t* expert_offsets, const void* pre_scale,
+                                      const void* w_repacked, void* y, int64_t ld_y, int64_t R, int64_t E, int64_t N,
+                                      int64_t K, void* workspace, int64_t workspace_bytes, void* stream) {
+    return grouped_gemm("mxfp4_w4a16_grouped_gemm", x, ld_x, nullptr, expert_offsets, pre_scale, w_repacked, nullptr, 0,
+                        y, ld_y, R, E, N, K, workspace, workspace_bytes, stream, false, 1);
+}
+
+nvfp4_status mxfp4_w4a16_grouped_gemm_f16(const void* x, int64_t ld_x, const int32_t* expert_offsets,
+                                          const void* pre_scale, const void* w_repacked, void* y, int64_t ld_y,
+                                          int64_t R, int64_t E, int64_t N, int64_t K, void* workspace,
+                                          int64_t workspace_bytes, void* stream) {
+    return grouped_gemm("mxfp4_w4a16_grouped_gemm_f16", x, ld_x, nullptr, expert_offsets, pre_scale, w_repacked,
+                        nullptr, 0, y, ld_y, R, E, N, K, workspace, workspace_bytes, stream, true, 1);
 }
 
 // ------------------------------------------------------------------ MoE --
