@@ -220,6 +220,27 @@ def make_moe_layer(name, T, *, seed=1004, E=128, topk=8, hidden=2048, inter=768)
     return wl
 
 
+def make_stream_read(name, nbytes, copies, workgroups, unroll):
+    """A plain read of nbytes per step (no GEMM): the ceiling a streaming kernel reaches on this device at the
+    size of a decode weight (33 MB) and of an LM-head weight (302 MB).  The buffer rotates over `copies`
+    copies, more than twice the 256 MB Infinity Cache, as the GEMM weights do."""
+    import torch
+    import weight_only_fp4_amd as nv
+    dev = "cuda:0"
+    nbytes = (nbytes + 15) // 16 * 16
+    bufs = [torch.full((nbytes,), 1, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    out = torch.zeros(workgroups, dtype=torch.int32, device=dev)
+
+    def launch(i):
+        nv.stream_read(bufs[i % copies], out, workgroups, unroll)
+
+    meta = {"bytes": nbytes, "workgroups": workgroups, "unroll": unroll, "copies": copies,
+            "note": "plain read, no GEMM: the streaming ceiling at this size"}
+    wl = Workload(name, "stream", "k_stream_read", float(nbytes), 0.0, launch, copies, meta, "hbm")
+    wl.tensors = dict(bufs=bufs, out=out)
+    return wl
+
+
 def workload_specs():
     """name -> builder (the headline first)."""
     return {
@@ -254,6 +275,10 @@ def workload_specs():
         "moe_fc2_T2048": lambda: make_grouped("moe_fc2_T2048", 2048, "fc2"),
         "moe_layer_T16": lambda: make_moe_layer("moe_layer_T16", 16),
         "moe_layer_T2048": lambda: make_moe_layer("moe_layer_T2048", 2048),
+        # the decode weight's size (33,619,972 B) and the LM-head weight's (302,268,420 B); launch shapes from
+        # a sweep of workgroups x loads in flight per lane
+        "stream_read_33MB": lambda: make_stream_read("stream_read_33MB", 33619972, 16, 8192, 2),
+        "stream_read_302MB": lambda: make_stream_read("stream_read_302MB", 302268420, 2, 8192, 8),
     }
 
 
@@ -367,6 +392,78 @@ def cpu_baseline(case, target_s=12.0):
     return {"value": round(wbytes / dt / 1e9, 4), "unit": "GB/s", "cores": thr, "kind": "oracle",
             "sample": f"{reps} whole calls of M={case.M}, N={case.N}, K={case.K} ({dt:.1f} s, fp64, {thr} threads)",
             "cpu_model": cpu_model(), "tiny_M4_N256_K512_one_thread_ms": round(tiny_ms, 3)}
+
+
+def cpu_per_config():
+    """The oracle, as is, once per configuration on host arrays drawn by the same generators as the GPU
+    workloads: whole calls where the oracle finishes in seconds (tiny, the decode shapes, the LM head, the ragged
+    shape, MoE T=16), a seeded subset of rows where it does not (prefill, MoE T=2048; labelled "subset").  Each
+    entry gives the rate in the workload's own unit (algorithmic GB/s for the HBM-bound shapes, GFLOP/s for the
+    MFMA-bound ones) over the rows the oracle computed."""
+    import numpy as np
+    import oracle
+    import synth
+    thr = oracle.max_threads()
+    res = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    def dense(name, c, rows, unit, subset_of=None):
+        x = c.x[:rows]
+        dt = timed(lambda: oracle.gemm(x, c.w, c.s, c.g_stored, c.g_is_divisor, c.pre))
+        if unit == "GB/s":
+            v = dense_bytes(rows, c.N, c.K, c.pre is not None) / dt / 1e9
+        else:
+            v = 2.0 * rows * c.N * c.K / dt / 1e9
+        res[name] = {"value": round(v, 4), "unit": unit, "seconds": round(dt, 3), "threads": thr,
+                     "sample": (f"subset: {rows} seeded rows of M={subset_of}" if subset_of else "whole call")
+                     + f", N={c.N}, K={c.K}"}
+
+    tiny = synth.tiny_case()
+    dense("tiny_M4_N256_K512", tiny, 4, "GB/s")
+    for N, K in ((14336, 4096), (4096, 14336)):
+        c = synth.decode_case(16, N, K)
+        for M in ((1, 8, 16) if N == 14336 else (1, 16)):
+            dense(f"decode_M{M}_N{N}_K{K}", c, M, "GB/s")
+    lm = synth.dense_case(64, 131072, 4096, 1003, g_stored=2688.0, g_is_divisor=True, prescale=True)
+    for M in (1, 64):
+        dense(f"lmhead_M{M}_N131072_K4096", lm, M, "GB/s")
+    del lm
+    dense("ragged_M33_N1000_K1040",
+          synth.dense_case(33, 1000, 1040, 1003, g_stored=2688.0, g_is_divisor=True, prescale=True), 33, "GB/s")
+    for M, N, K in ((4096, 14336, 4096), (8192, 17408, 5120)):
+        # the first 64 rows of a seeded draw stand for a seeded subset: rows are independent draws
+        c = synth.dense_case(64, N, K, 1002, scales="log_uniform", g_stored=1.0 / 2688.0)
+        dense(f"prefill_M{M}_N{N}_K{K}", c, 64, "GFLOP/s", subset_of=M)
+        del c
+    for T in (16, 2048):
+        for fc, (N, K) in (("fc1", (1536, 2048)), ("fc2", (2048, 768))):
+            c = synth.grouped_case(T, 128, 8, N, K, 1004, x_source="gather" if fc == "fc1" else "fresh")
+            counts = np.diff(c.offsets)
+            if T == 16:
+                x, off, label = c.x, c.offsets, f"whole call: R={c.R} rows over {int((counts > 0).sum())} experts"
+            else:
+                # one seeded row of every active expert
+                g = synth.rng(7)
+                act = np.nonzero(counts)[0]
+                pick = np.array([c.offsets[e] + g.integers(0, counts[e]) for e in act])
+                x = c.x[pick]
+                off = np.zeros(c.E + 1, dtype=np.int32)
+                off[1:] = np.cumsum(counts > 0)
+                label = f"subset: one seeded row of each of the {len(act)} active experts (of R={c.R})"
+            dt = timed(lambda: oracle.grouped_gemm(x, off, c.w, c.s, c.g_stored, False, None))
+            rows, nact = x.shape[0], int((np.diff(off) > 0).sum())
+            if T == 16:
+                v, unit = (nact * 0.5625 * N * K + 2.0 * rows * (K + N) + 8.0 * c.E + 4.0) / dt / 1e9, "GB/s"
+            else:
+                v, unit = 2.0 * rows * N * K / dt / 1e9, "GFLOP/s"
+            res[f"moe_{fc}_T{T}"] = {"value": round(v, 4), "unit": unit, "seconds": round(dt, 3), "threads": thr,
+                                     "sample": label + f", N={N}, K={K}"}
+            del c
+    return res
 
 
 def cpu_model():
@@ -539,6 +636,9 @@ def main():
     if not args.only and not args.no_cpu:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(host_case)
+        if not args.no_extra:
+            print("[bench] timing the CPU oracle per configuration", file=sys.stderr, flush=True)
+            out["cpu_baseline"]["per_config"] = cpu_per_config()
     print(json.dumps(out), flush=True)
 
 
