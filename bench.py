@@ -162,9 +162,10 @@ def make_grouped(name, T, fc, *, seed=1004, E=128, topk=8):
     return wl
 
 
-def make_moe_layer(name, T, *, seed=1004, E=128, topk=8, hidden=2048, inter=768):
-    """A whole MoE layer on the device: routing, FC1 with the token gather fused (N = 2 inter), gated SiLU,
-    FC2 (K = inter), top-k combine.  Weight copies rotate as for the grouped workloads."""
+def make_moe_layer(name, T, *, seed=1004, E=128, topk=8, hidden=2048, inter=768, fused=True):
+    """A whole MoE layer on the device: routing, FC1 with the token gather fused (N = 2 inter) and, when fused,
+    the gated SiLU in its epilogue (else a separate SiLU step), FC2 (K = inter), top-k combine.  Weight copies
+    rotate as for the grouped workloads."""
     import numpy as np
     import torch
     import synth
@@ -179,8 +180,9 @@ def make_moe_layer(name, T, *, seed=1004, E=128, topk=8, hidden=2048, inter=768)
     ids = torch.from_numpy(route.astype(np.int32)).to(dev)
     x = synth.device_normal_bf16((T, hidden), sd, dev)
     wts = torch.from_numpy(synth.rng(sd + 1).random((T, topk)).astype(np.float32)).to(dev)
-    b1 = nv.repack(synth.device_codes((E, 2 * inter, hidden // 2), sd + 2, dev),
-                   synth.device_scales((E, 2 * inter, hidden // 16), sd + 3, "pow2_mant", dev))
+    repack1 = nv.repack_gated if fused else nv.repack
+    b1 = repack1(synth.device_codes((E, 2 * inter, hidden // 2), sd + 2, dev),
+                 synth.device_scales((E, 2 * inter, hidden // 16), sd + 3, "pow2_mant", dev))
     b2 = nv.repack(synth.device_codes((E, hidden, inter // 2), sd + 4, dev),
                    synth.device_scales((E, hidden, inter // 16), sd + 5, "pow2_mant", dev))
     blobs = [(b1, b2)] + [(b1.clone(), b2.clone()) for _ in range(copies - 1)]
@@ -190,7 +192,7 @@ def make_moe_layer(name, T, *, seed=1004, E=128, topk=8, hidden=2048, inter=768)
     off = torch.empty(E + 1, dtype=torch.int32, device=dev)
     row_token = torch.empty(R, dtype=torch.int32, device=dev)
     token_row = torch.empty(R, dtype=torch.int32, device=dev)
-    h = torch.empty((R, 2 * inter), dtype=torch.bfloat16, device=dev)
+    h = None if fused else torch.empty((R, 2 * inter), dtype=torch.bfloat16, device=dev)
     a = torch.empty((R, inter), dtype=torch.bfloat16, device=dev)
     y2 = torch.empty((R, hidden), dtype=torch.bfloat16, device=dev)
     out = torch.empty((T, hidden), dtype=torch.bfloat16, device=dev)
@@ -204,8 +206,11 @@ def make_moe_layer(name, T, *, seed=1004, E=128, topk=8, hidden=2048, inter=768)
         w1, w2 = blobs[i % copies]
         nv._check(L.nvfp4_moe_route(nv._ptr(ids), T, topk, E, nv._ptr(off), nv._ptr(row_token), nv._ptr(token_row),
                                     nv._ptr(wsr), wsr.numel(), st()))
-        nv.grouped_gemm_gather(x, row_token, off, w1, E, 2 * inter, hidden, g1, out=h, workspace_buf=ws1)
-        nv.moe_silu_mul(h, out=a)
+        if fused:
+            nv.moe_fc1(x, row_token, off, w1, E, inter, hidden, g1, nv.MOE_SILU_GLU, out=a)
+        else:
+            nv.grouped_gemm_gather(x, row_token, off, w1, E, 2 * inter, hidden, g1, out=h, workspace_buf=ws1)
+            nv.moe_silu_mul(h, out=a)
         nv.grouped_gemm(a, off, w2, E, hidden, inter, g2, out=y2, workspace_buf=ws2)
         nv.moe_combine(y2, token_row, wts, out=out)
 
@@ -214,7 +219,8 @@ def make_moe_layer(name, T, *, seed=1004, E=128, topk=8, hidden=2048, inter=768)
     flops = 2.0 * R * hidden * (2 * inter) + 2.0 * R * inter * hidden
     bound = "hbm" if flops / ab < (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) else "mfma"
     meta = {"E": E, "topk": topk, "T": T, "R": R, "hidden": hidden, "inter": inter, "active_experts": active,
-            "weight_copies": copies, "steps_per_call": "route, FC1 (gather), SiLU, FC2, combine"}
+            "weight_copies": copies, "steps_per_call": "route, FC1 (gather) with the gated SiLU in its epilogue, FC2, "
+                                                       "combine" if fused else "route, FC1 (gather), SiLU, FC2, combine"}
     wl = Workload(name, "moe_layer", "moe_layer", ab, flops, launch, copies, meta, bound)
     wl.tensors = dict(x=x, out=out, blobs=blobs)
     return wl
@@ -275,6 +281,8 @@ def workload_specs():
         "moe_fc2_T2048": lambda: make_grouped("moe_fc2_T2048", 2048, "fc2"),
         "moe_layer_T16": lambda: make_moe_layer("moe_layer_T16", 16),
         "moe_layer_T2048": lambda: make_moe_layer("moe_layer_T2048", 2048),
+        "moe_layer_unfused_T16": lambda: make_moe_layer("moe_layer_unfused_T16", 16, fused=False),
+        "moe_layer_unfused_T2048": lambda: make_moe_layer("moe_layer_unfused_T2048", 2048, fused=False),
         # the decode weight's size (33,619,972 B) and the LM-head weight's (302,268,420 B); launch shapes from
         # a sweep of workgroups x loads in flight per lane
         "stream_read_33MB": lambda: make_stream_read("stream_read_33MB", 33619972, 16, 8192, 2),

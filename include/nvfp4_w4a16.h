@@ -160,6 +160,10 @@ nvfp4_status nvfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t
  *   nvfp4_moe_route -> nvfp4_w4a16_grouped_gemm_gather (FC1, N = 2 I)
  *   -> nvfp4_moe_silu_mul -> nvfp4_w4a16_grouped_gemm (FC2, K = I, N = Hd)
  *   -> nvfp4_moe_combine,
+ * or with the activation in FC1's epilogue (one step fewer, and FC1 writes
+ * I columns instead of 2 I):
+ *   nvfp4_moe_route -> nvfp4_moe_fc1 (gated weights from nvfp4_repack_gated)
+ *   -> nvfp4_w4a16_grouped_gemm (FC2) -> nvfp4_moe_combine,
  * every step stream-ordered, with no host synchronisation.
  *
  * Routing: topk_ids is device int32 [T][k] (row t: the k experts of token
@@ -216,6 +220,67 @@ nvfp4_status nvfp4_moe_silu_mul(const void* h, int64_t ld_h, int64_t R, int64_t 
  * Errors: R < 0, I < 1, ld_h < I, ld_a < I, NULL (R > 0) -> INVALID_ARG; odd
  * addresses -> ALIGNMENT. */
 nvfp4_status nvfp4_moe_relu2(const void* h, int64_t ld_h, int64_t R, int64_t I, void* a, int64_t ld_a, void* stream);
+
+/* Gated FC1 weights in the layout the fused FC1 reads.  The pages name two
+ * orders for the fused gate / up weight: gate first (SGLang's w13, the w1
+ * rows then the w3 rows: the SGLang compressed-tensors NVFP4 weight-only page,
+ * review discussion) and up first (TensorRT-LLM's w3_w1 / fc31: the inline
+ * review comments on "Support Nemotron-H nvfp4 ckpt on Hopper" and the
+ * Description of "Apply the NVFP4_AWQ pre-quant scale in MegaMoE CuteDSL").
+ * Input: canonical NVFP4 weights of E experts with 2 I rows each (as
+ * nvfp4_repack, N = 2 I), rows [0, I) the gate projection and [I, 2 I) the
+ * up projection when up_first = 0, the other way round when up_first = 1.
+ * Output: nvfp4_repack_gated_bytes(E, I, K) bytes (= nvfp4_repack_bytes(E,
+ * 2 I, K)), 16-byte aligned, whose 16-row units alternate gate / up: unit 2 j
+ * holds gate rows 16 j .. 16 j + 15 and unit 2 j + 1 the up rows of the same
+ * columns.  It is meant for nvfp4_moe_fc1 only.
+ * Errors: as nvfp4_repack, plus I < 0 or I not a multiple of 16, up_first not
+ * 0 or 1 -> INVALID_ARG. */
+int64_t nvfp4_repack_gated_bytes(int64_t E, int64_t I, int64_t K); /* < 0 if invalid */
+nvfp4_status nvfp4_repack_gated(const uint8_t* w_packed, int64_t ld_w, const uint8_t* w_scale, int64_t ld_s,
+                                int64_t E, int64_t I, int64_t K, int up_first, void* out, int64_t out_bytes,
+                                void* stream);
+
+/* FC1 with its activation applied in the GEMM's epilogue, so the 2 I-wide
+ * FC1 output is never written:
+ *   NVFP4_MOE_SILU_GLU: w_fc1 from nvfp4_repack_gated (E experts, I, K);
+ *     a[r][i] = RNE_bf16(silu(h_gate) * h_up) with h = RNE_bf16(g_e * acc)
+ *     of the gate and up columns i: bitwise what nvfp4_w4a16_grouped_gemm
+ *     (gather) followed by nvfp4_moe_silu_mul gives on the canonical weights;
+ *   NVFP4_MOE_RELU2: w_fc1 from nvfp4_repack (E, N = I, K); a[r][i] =
+ *     RNE_bf16(max(h, 0)^2), h = RNE_bf16(g_e * acc): bitwise the grouped GEMM
+ *     followed by nvfp4_moe_relu2.
+ * Rows: with row_token, grouped row r reads token row row_token[r] of x
+ * (bf16 [T][ld_x]) as in nvfp4_w4a16_grouped_gemm_gather; with row_token
+ * NULL, x holds the R grouped rows (T must equal R).  a is bf16 [R][ld_a] in
+ * grouped row order; expert_offsets, pre_scale, global_scales and the
+ * divisor flag as in nvfp4_w4a16_grouped_gemm.  No workspace.
+ * Errors: as nvfp4_w4a16_grouped_gemm_gather (with N = 2 I or I), plus an
+ * unknown activation, I < 0, I not a multiple of 16 (gated), ld_a < I,
+ * row_token NULL with T != R -> INVALID_ARG. */
+enum { NVFP4_MOE_SILU_GLU = 1, NVFP4_MOE_RELU2 = 2 };
+nvfp4_status nvfp4_moe_fc1(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
+                           const int32_t* expert_offsets, const void* pre_scale, const void* w_fc1,
+                           const float* global_scales, int global_scale_is_divisor, int activation, void* a,
+                           int64_t ld_a, int64_t R, int64_t E, int64_t I, int64_t K, void* stream);
+
+/* Test export: one grouped GEMM (activation 0: plain output, N columns) or
+ * fused FC1 (activation NVFP4_MOE_SILU_GLU on a gated blob, N = 2 I and I
+ * output columns; NVFP4_MOE_RELU2) on a chosen kernel, so that the kernels
+ * can be checked against each other on the same inputs: variant 0 the
+ * automatic choice, 1 the small-M kernel, 2 the tile kernel (64-row tiles),
+ * 3 the MFMA-bound kernel (256-row tiles per expert).  Rows as in
+ * nvfp4_moe_fc1 (row_token NULL: x holds the R grouped rows, T = R); f16:
+ * fp16 activations and output; mx: an MXFP4 blob (mxfp4_repack; the global
+ * scales are then not read and may be NULL); no workspace.  Errors: as the grouped GEMM,
+ * plus an unknown activation or variant, N not a multiple of 32 with the
+ * gated activation, mx not 0 or 1, and for variant 3 a blob of 2 GiB of
+ * codes or more or NVFP4_MOE_RELU2 (the tile kernel serves it) -> INVALID_ARG. */
+nvfp4_status nvfp4_w4a16_grouped_gemm_variant(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
+                                              const int32_t* expert_offsets, const void* pre_scale, const void* w,
+                                              const float* global_scales, int global_scale_is_divisor, int activation,
+                                              void* y, int64_t ld_y, int64_t R, int64_t E, int64_t N, int64_t K,
+                                              int variant, int f16, int mx, void* stream);
 
 /* Top-k weighted combine back to token order: out[t][c] =
  * RNE_bf16(sum_{j=0..k-1} topk_weights[t*k + j] * y[token_row[t*k + j]][c]),
@@ -393,6 +458,11 @@ nvfp4_status nvfp4_moe_relu2_f16(const void* h, int64_t ld_h, int64_t R, int64_t
                                  void* stream);
 nvfp4_status nvfp4_moe_combine_f16(const void* y, int64_t ld_y, const int32_t* token_row, const float* topk_weights,
                                    int64_t T, int64_t k, int64_t H, void* out, int64_t ld_o, void* stream);
+/* nvfp4_moe_fc1 with fp16 activations and output (RNE to fp16 throughout). */
+nvfp4_status nvfp4_moe_fc1_f16(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
+                               const int32_t* expert_offsets, const void* pre_scale, const void* w_fc1,
+                               const float* global_scales, int global_scale_is_divisor, int activation, void* a,
+                               int64_t ld_a, int64_t R, int64_t E, int64_t I, int64_t K, void* stream);
 
 #ifdef __cplusplus
 }

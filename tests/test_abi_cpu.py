@@ -232,3 +232,35 @@ def test_f16_entry_points_check_arguments_and_name_themselves():
     st = L.nvfp4_moe_silu_mul_f16(_p(A), 10, 4, 8, _p(A), 8, None)
     assert st == INVALID and "nvfp4_moe_silu_mul_f16" in L.nvfp4_last_error().decode()
 
+
+
+def test_gated_repack_and_fused_fc1_argument_errors():
+    """nvfp4_repack_gated and nvfp4_moe_fc1 reject bad arguments on the host; empty calls succeed."""
+    L = nv.lib()
+    assert L.nvfp4_repack_gated_bytes(4, 768, 2048) == L.nvfp4_repack_bytes(4, 1536, 2048)
+    assert L.nvfp4_repack_gated_bytes(4, 100, 2048) == -1                              # I not a multiple of 16
+    rg = lambda I=32, up=0, out=_p(A), nb=1 << 30: L.nvfp4_repack_gated(_p(A), 64, _p(A), 8, 2, I, 128, up, out, nb,
+                                                                        None)
+    assert rg(I=24) == INVALID and "multiple of 16" in L.nvfp4_last_error().decode()
+    assert rg(up=2) == INVALID and "up_first" in L.nvfp4_last_error().decode()
+    assert rg(nb=16) == SMALL
+    assert rg(out=_p(A + 8)) == ALIGN
+    assert rg(I=0) == OK                                                              # no rows: nothing to do
+    fc1 = L.nvfp4_moe_fc1
+    args = lambda **kw: [kw.get(n, d) for n, d in [
+        ("x", _p(A)), ("ld_x", 128), ("T", 16), ("rt", _p(A)), ("off", _p(A)), ("pre", None), ("w", _p(A)),
+        ("g", _p(A)), ("div", 0), ("act", 1), ("a", _p(A)), ("ld_a", 48), ("R", 32), ("E", 4), ("I", 48),
+        ("K", 128), ("st", None)]]
+    assert fc1(*args(act=0)) == INVALID and "activation" in L.nvfp4_last_error().decode()
+    assert fc1(*args(act=3)) == INVALID
+    assert fc1(*args(I=40, ld_a=40)) == INVALID and "multiple of 16" in L.nvfp4_last_error().decode()
+    assert fc1(*args(act=2, I=40, ld_a=40, R=0)) == OK                                # relu2: any I; no rows
+    assert fc1(*args(ld_a=40)) == INVALID and "ld_a" in L.nvfp4_last_error().decode()
+    assert fc1(*args(rt=None)) == INVALID and "T = R" in L.nvfp4_last_error().decode()
+    assert fc1(*args(rt=None, T=32, R=0)) == INVALID                                  # T != R without row_token
+    assert fc1(*args(rt=None, T=0, R=0)) == OK
+    assert fc1(*args(rt=_p(A + 2))) == ALIGN
+    assert fc1(*args(K=120)) == INVALID                                               # K % 16
+    assert fc1(*args(R=0)) == OK                                                      # zero rows: no launch
+    st = L.nvfp4_moe_fc1_f16(*args(act=0))
+    assert st == INVALID and "nvfp4_moe_fc1_f16" in L.nvfp4_last_error().decode()

@@ -77,3 +77,10 @@ def test_checker_flags_planted_hazards():
     ])
     assert len(hazards(copy)) == 1
     assert hazards(copy.replace("\ts_mov_b32 m0", "\ts_nop 2\n\ts_mov_b32 m0")) == []
+    # a scalar move rewriting the base in between: the copy reads the moved value (the form the copies use)
+    moved = copy.replace("\ts_nop 0\n\tglobal_load_lds_dwordx4 v69, s[44:45]",
+                         "\ts_mov_b64 s[44:45], s[0:1]\n\tglobal_load_lds_dwordx4 v69, s[44:45]")
+    assert hazards(moved) == []
+    # a compare reads its first operand: it does not hide the write
+    cmp = copy.replace("\t;;#ASMSTART", "\ts_cmp_eq_u32 s45, 0\n\t;;#ASMSTART")
+    assert len(hazards(cmp)) == 1

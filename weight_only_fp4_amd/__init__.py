@@ -105,6 +105,14 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_moe_combine_f16.restype = I
         L.nvfp4_w4a16_grouped_gemm_gather_f16.argtypes = L.nvfp4_w4a16_grouped_gemm_gather.argtypes
         L.nvfp4_w4a16_grouped_gemm_gather_f16.restype = I
+        L.nvfp4_repack_gated_bytes.argtypes, L.nvfp4_repack_gated_bytes.restype = [I64, I64, I64], I64
+        L.nvfp4_repack_gated.argtypes = [P, I64, P, I64, I64, I64, I64, I, P, I64, P]
+        L.nvfp4_repack_gated.restype = I
+        for f in (L.nvfp4_moe_fc1, L.nvfp4_moe_fc1_f16):
+            f.argtypes, f.restype = [P, I64, I64, P, P, P, P, P, I, I, P, I64, I64, I64, I64, I64, P], I
+        L.nvfp4_w4a16_grouped_gemm_variant.argtypes = [P, I64, I64, P, P, P, P, P, I, I, P, I64, I64, I64, I64, I64,
+                                                       I, I, I, P]
+        L.nvfp4_w4a16_grouped_gemm_variant.restype = I
         _lib = L
     return _lib
 
@@ -160,6 +168,27 @@ def repack(w_packed: torch.Tensor, w_scale: torch.Tensor) -> torch.Tensor:
     out = torch.empty(nbytes, dtype=torch.uint8, device=w_packed.device)
     _check(lib().nvfp4_repack(_ptr(w_packed), w_packed.stride(-2), _ptr(w_scale), w_scale.stride(-2), E, N, K,
                               _ptr(out), nbytes, _stream(w_packed.device)))
+    return out
+
+
+def repack_gated(w_packed: torch.Tensor, w_scale: torch.Tensor, up_first: bool = False) -> torch.Tensor:
+    """Gated FC1 weights, canonical uint8 [E, 2I, K/2] codes + E4M3 [E, 2I, K/16] scales with the gate projection in
+    rows [0, I) and the up projection in [I, 2I) (up_first: the other way round) -> blob for moe_fc1 (its 16-row
+    units alternate gate / up)."""
+    _dev("w_packed", w_packed, torch.uint8, 3)
+    _dev("w_scale", w_scale, (torch.uint8, torch.float8_e4m3fn), 3)
+    if w_scale.dtype != torch.uint8:
+        w_scale = w_scale.view(torch.uint8)
+    E, N2, K = w_packed.shape[0], w_packed.shape[1], w_packed.shape[2] * 2
+    if tuple(w_scale.shape) != (E, N2, K // 16) or N2 % 32:
+        raise ValueError(f"w_scale {tuple(w_scale.shape)} must match w_packed {tuple(w_packed.shape)}, 2I a multiple of 32")
+    for name, t in (("w_packed", w_packed), ("w_scale", w_scale)):
+        if t.stride(0) != t.shape[1] * t.stride(1):
+            raise ValueError(f"{name}: experts must be stored back to back (stride(0) == N * stride(1))")
+    nbytes = int(lib().nvfp4_repack_gated_bytes(E, N2 // 2, K))
+    out = torch.empty(nbytes, dtype=torch.uint8, device=w_packed.device)
+    _check(lib().nvfp4_repack_gated(_ptr(w_packed), w_packed.stride(1), _ptr(w_scale), w_scale.stride(1), E, N2 // 2,
+                                    K, int(bool(up_first)), _ptr(out), nbytes, _stream(w_packed.device)))
     return out
 
 
@@ -420,6 +449,66 @@ def grouped_gemm_gather(x, row_token, expert_offsets, blob, E, N, K, global_scal
     _check(fn(_ptr(x), x.stride(0), T, _ptr(row_token), _ptr(expert_offsets), _ptr(pre_scale), _ptr(blob),
               _ptr(global_scales), int(bool(divisor)), _ptr(out), out.stride(0), R, E, N, K, _ptr(workspace_buf),
               workspace_buf.numel(), _stream(x.device)))
+    return out
+
+
+MOE_SILU_GLU, MOE_RELU2 = 1, 2
+GROUPED_AUTO, GROUPED_SMALL_M, GROUPED_TILE, GROUPED_MFMA = 0, 1, 2, 3
+
+
+def grouped_gemm_variant(x, row_token, expert_offsets, blob, E, N, K, global_scales, variant, activation=0,
+                         divisor=False, pre_scale=None, out=None, mxfp4=False):
+    """Test export: the grouped GEMM (activation 0) or fused FC1 (MOE_SILU_GLU on a gated blob of N = 2I rows,
+    MOE_RELU2) on a chosen kernel (GROUPED_SMALL_M, GROUPED_TILE, GROUPED_MFMA or GROUPED_AUTO).  row_token None:
+    x holds the grouped rows.  mxfp4: an MXFP4 blob (global_scales not read; may be None)."""
+    dt = _act_dtype("x", x)
+    _dev("x", x, dt, 2)
+    _dev("expert_offsets", expert_offsets, torch.int32, 1)
+    T = x.shape[0]
+    R = row_token.shape[0] if row_token is not None else T
+    cols = N // 2 if activation == MOE_SILU_GLU else N
+    if out is None:
+        out = torch.zeros((R, cols), dtype=dt, device=x.device)
+    _check(lib().nvfp4_w4a16_grouped_gemm_variant(
+        _ptr(x), x.stride(0), T, _ptr(row_token), _ptr(expert_offsets), _ptr(pre_scale), _ptr(blob),
+        _ptr(global_scales), int(bool(divisor)), int(activation), _ptr(out), out.stride(0), R, E, N, K, int(variant),
+        int(dt == torch.float16), int(bool(mxfp4)), _stream(x.device)))
+    return out
+
+
+def moe_fc1(x, row_token, expert_offsets, blob, E, I, K, global_scales, activation=MOE_SILU_GLU, divisor=False,
+            pre_scale=None, out=None):
+    """FC1 of a MoE layer with its activation in the GEMM epilogue -> a [R, I] (x's type).  activation MOE_SILU_GLU:
+    blob from repack_gated; MOE_RELU2: blob from repack (N = I).  row_token None: x holds the R grouped rows."""
+    dt = _act_dtype("x", x)
+    _dev("x", x, dt, 2)
+    _dev("expert_offsets", expert_offsets, torch.int32, 1)
+    if expert_offsets.shape[0] != E + 1 or not expert_offsets.is_contiguous():
+        raise ValueError(f"expert_offsets must be a contiguous int32 [{E + 1}]")
+    if global_scales.numel() != E:
+        raise ValueError(f"global_scales must hold {E} values")
+    if x.shape[1] != K:
+        raise ValueError(f"x must be [T, {K}]")
+    T = x.shape[0]
+    if row_token is not None:
+        _dev("row_token", row_token, torch.int32, 1)
+        if not row_token.is_contiguous():
+            raise ValueError("row_token must be contiguous")
+        R = row_token.shape[0]
+    else:
+        R = T
+    if pre_scale is not None:
+        _dev("pre_scale", pre_scale, dt, 1)
+    if out is None:
+        out = torch.empty((R, I), dtype=dt, device=x.device)
+    else:
+        _dev("out", out, dt, 2)
+        if tuple(out.shape) != (R, I):
+            raise ValueError(f"out must be [{R}, {I}]")
+    fn = lib().nvfp4_moe_fc1_f16 if dt == torch.float16 else lib().nvfp4_moe_fc1
+    _check(fn(_ptr(x), x.stride(0), T, _ptr(row_token), _ptr(expert_offsets), _ptr(pre_scale), _ptr(blob),
+              _ptr(global_scales), int(bool(divisor)), int(activation), _ptr(out), out.stride(0), R, E, I, K,
+              _stream(x.device)))
     return out
 
 

@@ -196,6 +196,41 @@ __device__ __forceinline__ float act_to_f32(uint32_t h) {
     else return bf16_to_f32(h);
 }
 
+// MoE activations between FC1 and FC2, on values already rounded to the
+// activation type (FC1's outputs), in fp32.  The standalone glue kernels and
+// the FC1 epilogue (act below) share these, so the two paths agree bitwise.
+//   gated SiLU: silu(gate) * up, silu(v) = v / (1 + e^-v);
+//   squared ReLU (experts without a gate): max(h, 0)^2.
+//
+// Products that are then rounded to the output type pass through an empty
+// asm statement as fp32 values: the backend otherwise folds a multiply and
+// the following conversion to fp16 into one mixed-precision FMA
+// (v_fma_mixlo_f16, which rounds the exact product once; contraction off
+// does not stop it), in some kernels and not in others, so that two paths
+// computing the same output would differ in the last bit now and then.
+// Every output path thus rounds the fp32 product.
+__device__ __forceinline__ float fp32_value(float v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+__device__ __forceinline__ float silu_times(float gate, float up) {
+    return fp32_value(gate / (1.0f + expf(-gate)) * up);
+}
+__device__ __forceinline__ float relu_squared(float h) {
+    const float r = fmaxf(h, 0.0f);
+    return fp32_value(r * r);
+}
+// g * acc of an epilogue, as an fp32 value (see above)
+__device__ __forceinline__ float scale_acc(float g, float acc) { return fp32_value(g * acc); }
+
+// What a grouped GEMM's epilogue writes (template parameter ACT):
+//   kActNone     Y = RNE(g * acc);
+//   kActSiluGlu  the blob's 16-row units alternate gate / up (nvfp4_repack_gated),
+//                and output column 16 j + c is RNE(silu_times(h(2j, c), h(2j+1, c)))
+//                with h(u, c) = RNE(g * acc) of unit u, column c: N / 2 columns;
+//   kActRelu2    RNE(relu_squared(RNE(g * acc))).
+constexpr int kActNone = 0, kActSiluGlu = 1, kActRelu2 = 2;
+
 // fp32 pair -> bf16 (fp16 with F16) pair, round to nearest even with the
 // hardware conversion (one instruction per pair; a NaN stays NaN), first
 // value in the low half.

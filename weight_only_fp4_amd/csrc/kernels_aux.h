@@ -11,11 +11,17 @@ namespace nvfp4 {
 // are written as zero.  mx: the scales are E8M0 bytes, one per 32 K (ld_s >=
 // K / 32); the lane's 32-wide K group is one MXFP4 group and both of its
 // scale bytes take that group's byte.
+// gate_I > 0: a gated FC1 weight (N = 2 gate_I rows, gate_I a multiple of 16)
+// is laid out with its 16-row units alternating gate / up for the gated
+// epilogue: blob row 32 j + c (c < 16) is gate row 16 j + c and blob row
+// 32 j + 16 + c the matching up row.  In the canonical input the gate rows
+// come first (rows [0, I)) unless up_first, which puts the up rows there.
 __global__ void __launch_bounds__(256) k_repack(const uint8_t* __restrict__ w, int64_t ld_w,
                                                 const uint8_t* __restrict__ s, int64_t ld_s,
                                                 int64_t N, int64_t K, int64_t NU, int64_t KC, int64_t total_lanes,
                                                 BlobView v, uint8_t* __restrict__ codes_out,
-                                                uint8_t* __restrict__ scales_out, int mx) {
+                                                uint8_t* __restrict__ scales_out, int mx, int64_t gate_I,
+                                                int up_first) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= total_lanes) return;
     const int lane = (int)(t & 63);
@@ -31,14 +37,17 @@ __global__ void __launch_bounds__(256) k_repack(const uint8_t* __restrict__ w, i
     uint32_t q[4] = {0u, 0u, 0u, 0u};
     uint32_t sc = 0u;
     if (n < N) {
-        const uint8_t* row = w + (e * N + n) * ld_w;
+        // canonical row of blob row n
+        const int64_t half = (n >> 4) & 1;                           // 0: gate unit, 1: up unit
+        const int64_t src = gate_I > 0 ? (half ^ (int64_t)up_first) * gate_I + (n >> 5) * kUnitN + (n & 15) : n;
+        const uint8_t* row = w + (e * N + src) * ld_w;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int64_t j = kbyte0 + i;
             const uint32_t b = (j < kbytes) ? (uint32_t)row[j] : 0u;
             q[i >> 2] |= b << (8 * (i & 3));
         }
-        const uint8_t* srow = s + (e * N + n) * ld_s;
+        const uint8_t* srow = s + (e * N + src) * ld_s;
         if (mx) {
             const int64_t sb = c * (kChunkK / 32) + (lane >> 4);
             const uint32_t s0 = (sb < K / 32) ? (uint32_t)srow[sb] : 0u;

@@ -359,7 +359,11 @@ __device__ __forceinline__ void small_m_pass16(const uint16_t* __restrict__ xrow
 // MG == 0: each pass of up to 16 rows picks one or four row groups (grouped).
 // The first weight loads of a wave are issued before the scale table is
 // built, so the table build and its barrier run under the load latency.
-template <int MG, int NT, int W, int D, bool GROUPED, bool KFULL, bool F16 = false, bool PRE = false>
+// ACT (grouped form): the MoE activation the epilogue applies (kActNone,
+// kActSiluGlu with NT even: each workgroup holds gate / up unit pairs and
+// writes N / 2 columns, kActRelu2).
+template <int MG, int NT, int W, int D, bool GROUPED, bool KFULL, bool F16 = false, bool PRE = false,
+          int ACT = kActNone>
 __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                          int NU, int KC, int K,
                                                          int N, const float* __restrict__ gscale, int g_is_div,
@@ -431,14 +435,37 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
         auto store_y = [&](int t, float acc) {
             const int r = t / RLD, col = t % RLD;
             const int64_t n = (int64_t)u0 * kUnitN + col;
-            if (n < N) y[(row0 + p0 + r) * ld_y + n] = (uint16_t)round_out<F16>(gv * acc);
+            uint32_t v = round_out<F16>(scale_acc(gv, acc));
+            if constexpr (ACT == kActRelu2) v = round_out<F16>(relu_squared(act_to_f32<F16>(v)));
+            if (n < N) y[(row0 + p0 + r) * ld_y + n] = (uint16_t)v;
         };
         if (S == 1) {
-            for (int t = threadIdx.x; t < rows * RLD; t += W * 64) {
-                float acc = 0.f;
+            if constexpr (ACT == kActSiluGlu) {
+                // unit 2 j + 1 of the pair holds the up projection of unit 2 j's
+                // columns; output column 16 (u0 / 2 + j) + c, N / 2 columns
+                static_assert(NT % 2 == 0, "gate / up units come in pairs");
+                constexpr int kHalf = RLD / 2;
+                for (int t = threadIdx.x; t < rows * kHalf; t += W * 64) {
+                    const int r = t / kHalf, pj = (t % kHalf) >> 4, c = t & 15;
+                    const int tg = r * RLD + pj * 2 * kUnitN + c;
+                    float ag = 0.f, au = 0.f;
 #pragma unroll
-                for (int wi = 0; wi < W; ++wi) acc += red[wi][t];
-                store_y(t, acc);
+                    for (int wi = 0; wi < W; ++wi) {
+                        ag += red[wi][tg];
+                        au += red[wi][tg + kUnitN];
+                    }
+                    const int64_t n = ((int64_t)u0 / 2 + pj) * kUnitN + c;
+                    const float hg = act_to_f32<F16>(round_out<F16>(scale_acc(gv, ag)));
+                    const float hu = act_to_f32<F16>(round_out<F16>(scale_acc(gv, au)));
+                    if (n < N / 2) y[(row0 + p0 + r) * ld_y + n] = (uint16_t)round_out<F16>(silu_times(hg, hu));
+                }
+            } else {
+                for (int t = threadIdx.x; t < rows * RLD; t += W * 64) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int wi = 0; wi < W; ++wi) acc += red[wi][t];
+                    store_y(t, acc);
+                }
             }
             __syncthreads();
             continue;

@@ -49,9 +49,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // so that the compiler, which cannot tell which LDS bytes such a copy
 // writes, does not wait for every copy in flight before each LDS read; the
 // kernel waits for its own copies (vmcnt) before the barrier that publishes
-// them.  M0 carries the LDS base and needs one wait state.
+// them.  The compiler inserts no wait states around the statement, so it
+// carries its own: M0 (the LDS base) needs one after it is written, and the
+// base address is first copied by a scalar move into a scratch pair that the
+// load reads, because a vector instruction writing the base (as the compiler
+// does when it restores a spilled scalar with v_readlane) needs five wait
+// states before a memory instruction reads it, while a scalar read of it is
+// interlocked.  The move is also M0's wait state.
 __device__ __forceinline__ void lds_copy16(uint32_t lds, const uint8_t* base, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
+    uint64_t tmp;
+    asm volatile("s_mov_b32 m0, %1\n\ts_mov_b64 %0, %3\n\tglobal_load_lds_dwordx4 %2, %0"
+                 : "=&s"(tmp)
+                 : "s"(lds), "v"(voff), "s"(base)
                  : "memory", "m0");
 }
 
@@ -112,7 +121,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 __device__ __forceinline__ void lds_copy4(uint32_t lds, const uint8_t* base, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base)
+    uint64_t tmp;
+    asm volatile("s_mov_b32 m0, %1\n\ts_mov_b64 %0, %3\n\tglobal_load_lds_dword %2, %0"
+                 : "=&s"(tmp)
+                 : "s"(lds), "v"(voff), "s"(base)
                  : "memory", "m0");
 }
 
@@ -149,11 +161,26 @@ __device__ __forceinline__ void mfma_tile(int t, int MT, int NTn, int& mt, int& 
 // outcome depends on timing, and so on what else shares the compute unit).
 // The wave drains every copy before it exits, so no copy can land in the LDS
 // of a workgroup that starts on the compute unit after it.
-template <int MS, bool KFULL, bool F16 = false, bool PRE = false, bool MX = false>
+//
+// Grouped (MoE) form (GROUPED, 256-row tiles): the work items are (row tile of
+// an expert, in expert order; tile column), the row tiles counted from
+// expert_offsets by a prefix scan in every workgroup, and dealt to the XCDs
+// in contiguous ranges (workgroup id i takes item (i % 8) * per + i / 8,
+// per = ceil(items / 8); the host's grid holds 8 workgroups beyond the items
+// so every item has an id).  An expert's rows end anywhere: the row blocks of
+// 16 past its last row skip their MFMAs (the copies and the decode run as in
+// a whole tile, keeping the copy schedule), so an expert of m rows costs the
+// decode of its weights once per tile column and MFMAs for ceil(m / 16) row
+// blocks.  row_index (optional): grouped row r reads activation row
+// row_index[r].  ACT: the MoE activation of the epilogue (decode.h).
+template <int MS, bool KFULL, bool F16 = false, bool PRE = false, bool MX = false, bool GROUPED = false,
+          int ACT = kActNone>
 __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                         int NU, int KC, int K, int N, const float* __restrict__ gscale,
                                                         int g_is_div, uint16_t* __restrict__ y, int64_t ld_y, int M,
-                                                        int t0, int vec_store, const uint16_t* __restrict__ pre) {
+                                                        int t0, int vec_store, const uint16_t* __restrict__ pre,
+                                                        const int32_t* __restrict__ offsets = nullptr, int E = 0,
+                                                        const int32_t* __restrict__ row_index = nullptr) {
     constexpr int NT = kMfmaNT, WN = kMfmaWN;
     constexpr int kRows = 16 * MS;              // rows of this workgroup
     constexpr int kStage = kRows * 256;         // LDS bytes of one staged activation chunk
@@ -173,31 +200,83 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     // each XCD is given a contiguous range of the tile order instead, so the
     // ~32 workgroups an XCD runs together form a block of about 4 tile rows x
     // 8 tile columns whose activations and weights its own L2 holds.
-    const int xid = [&] {
-        const int n = (int)gridDim.x, q8 = n / 8, rem = n % 8, x = (int)blockIdx.x % 8, k = (int)blockIdx.x / 8;
-        return x * q8 + (x < rem ? x : rem) + k;
-    }();
-    int mt, nt;
-    mfma_tile(t0 + xid / kParts, (M + kMfmaTileRows - 1) / kMfmaTileRows, (NU + kMfmaUnits - 1) / kMfmaUnits, mt, nt);
-    const int m0 = mt * kMfmaTileRows + (xid % kParts) * kRows;
-    if (m0 >= M) return;                        // a lower part past the last row (uniform per workgroup)
+    int e = 0, nt, m0, mend;   // expert, tile column, first row, end of the rows (M, or the expert's end)
+    if constexpr (GROUPED) {
+        static_assert(MS == 16, "the grouped form runs whole 256-row tiles");
+        __shared__ int s_map[3];
+        if (tid == 0) s_map[0] = -1;
+        __syncthreads();
+        if (w == 0) {
+            // pass by < 0 counts the row tiles; pass by >= 0 finds row tile by's (expert, tile)
+            auto scan = [&](int by) {
+                int carry = 0;
+                for (int base = 0; base < E; base += 64) {
+                    const int ex = base + lane;
+                    const int tiles = ex < E ? (offsets[ex + 1] - offsets[ex] + kRows - 1) / kRows : 0;
+                    int v = tiles;
+#pragma unroll
+                    for (int d = 1; d < 64; d <<= 1) {
+                        const int t = __shfl_up(v, d);
+                        if (lane >= d) v += t;
+                    }
+                    const int incl = carry + v, excl = incl - tiles;
+                    if (by >= 0 && tiles > 0 && by >= excl && by < incl) {
+                        s_map[0] = ex;
+                        s_map[1] = by - excl;
+                    }
+                    carry += __shfl(v, 63);
+                }
+                return carry;
+            };
+            const int64_t cols = (NU + kMfmaUnits - 1) / kMfmaUnits;
+            const int64_t items = (int64_t)scan(-1) * cols, id = blockIdx.x;
+            const int64_t per = (items + 7) / 8, item = (id % 8) * per + id / 8;
+            if (id / 8 < per && item < items) {
+                scan((int)(item / cols));
+                if (lane == 0) s_map[2] = (int)(item % cols);
+            }
+        }
+        __syncthreads();
+        e = s_map[0];
+        if (e < 0) return;                      // past the last item (uniform per workgroup)
+        m0 = offsets[e] + s_map[1] * kRows;
+        mend = offsets[e + 1];
+        nt = s_map[2];
+    } else {
+        const int xid = [&] {
+            const int n = (int)gridDim.x, q8 = n / 8, rem = n % 8, xx = (int)blockIdx.x % 8, k = (int)blockIdx.x / 8;
+            return xx * q8 + (xx < rem ? xx : rem) + k;
+        }();
+        int mt;
+        mfma_tile(t0 + xid / kParts, (M + kMfmaTileRows - 1) / kMfmaTileRows, (NU + kMfmaUnits - 1) / kMfmaUnits, mt,
+                  nt);
+        m0 = mt * kMfmaTileRows + (xid % kParts) * kRows;
+        mend = M;
+        if (m0 >= M) return;                    // a lower part past the last row (uniform per workgroup)
+    }
+    // row blocks of 16 holding rows of this tile (the others skip their MFMAs)
+    const int msv = GROUPED ? (mend - m0 + 15) / 16 : MS;
     const int u_w = nt * kMfmaUnits + NT * w;   // this wave's first unit
 
     // ---- activation copies: copy i (0 .. 4 MS - 1) of a chunk moves rows
     // 4 i .. 4 i + 3; wave w issues copies w, w + 4, ..; lane l takes row
-    // 4 i + (l >> 4) and the piece stored in slot l & 15.  Rows past M read
-    // row M - 1 (never stored).  Offsets are 32-bit from the workgroup's
-    // first row (at most 255 rows of ld_x <= 2^23 elements: below 2^32 bytes).
+    // 4 i + (l >> 4) and the piece stored in slot l & 15.  Rows past mend read
+    // row mend - 1 (never stored).  Offsets are 32-bit from the workgroup's
+    // first row (at most 255 rows of ld_x <= 2^23 elements: below 2^32 bytes),
+    // or from x when gathering (row_index[r] * ld_x * 2 < 2^32: the host bounds
+    // the token count times ld_x).
     constexpr int kCopiesPerWave = kRows / 4 / WN;
     const int q = lane & 15;
+    const bool gather = GROUPED && row_index != nullptr;
     uint32_t a_src[kCopiesPerWave];   // byte offset of the lane's piece in chunk 0, per copy
 #pragma unroll
     for (int k = 0; k < kCopiesPerWave; ++k) {
         const int row = 4 * (w + WN * k) + (lane >> 4);
-        const int rrow = m0 + row < M ? row : M - 1 - m0;
-        a_src[k] = (uint32_t)(((int64_t)rrow * ld_x + (q ^ (row & 15)) * 8) * 2);
+        const int rrow = m0 + row < mend ? row : mend - 1 - m0;
+        const int64_t xrow = gather ? (int64_t)row_index[m0 + rrow] : (int64_t)rrow;
+        a_src[k] = (uint32_t)((xrow * ld_x + (q ^ (row & 15)) * 8) * 2);
     }
-    const uint8_t* xb = uniform_ptr(reinterpret_cast<const uint8_t*>(x + (int64_t)m0 * ld_x));
+    const uint8_t* xb = uniform_ptr(reinterpret_cast<const uint8_t*>(gather ? x : x + (int64_t)m0 * ld_x));
     auto copy_piece = [&](int c, int buf, int k) {   // copy w + 4 k of chunk c into stage buf
         const int i = w + WN * k, row = 4 * i + (lane >> 4);
         uint32_t off = a_src[k] + (uint32_t)(c * kChunkK * 2);
@@ -253,11 +332,11 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     const uint8_t* s_lo[NT / 2];
     uint32_t s_off[NT / 2];  // scale copy p moves unit 2p (lanes 0..31) and 2p + 1 (lanes 32..63)
 #pragma unroll
-    for (int j = 0; j < NT; ++j) cb[j] = bv.codes + bv.block(0, (u_w + j) < NU ? u_w + j : 0, 0) * kCodeBlock;
+    for (int j = 0; j < NT; ++j) cb[j] = bv.codes + bv.block(e, (u_w + j) < NU ? u_w + j : 0, 0) * kCodeBlock;
 #pragma unroll
     for (int p = 0; p < NT / 2; ++p) {
-        const uint8_t* s0p = bv.scales + bv.block(0, (u_w + 2 * p) < NU ? u_w + 2 * p : 0, 0) * kScaleBlock;
-        const uint8_t* s1p = bv.scales + bv.block(0, (u_w + 2 * p + 1) < NU ? u_w + 2 * p + 1 : 0, 0) * kScaleBlock;
+        const uint8_t* s0p = bv.scales + bv.block(e, (u_w + 2 * p) < NU ? u_w + 2 * p : 0, 0) * kScaleBlock;
+        const uint8_t* s1p = bv.scales + bv.block(e, (u_w + 2 * p + 1) < NU ? u_w + 2 * p + 1 : 0, 0) * kScaleBlock;
         s_lo[p] = s0p < s1p ? s0p : s1p;
         s_off[p] = (uint32_t)((lane < 32 ? s0p : s1p) - s_lo[p]) + (uint32_t)((lane & 31) * 4);
     }
@@ -393,7 +472,7 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
         DwordJob jobs[kJobs];
         static_for<0, NT>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
-            mfma_acc<F16>(acc[ms][j], bf[j], af[f % kRing]);
+            if (!GROUPED || ms < msv) mfma_acc<F16>(acc[ms][j], bf[j], af[f % kRing]);
             if constexpr (t < 3) {
                 static_for<d_lo, d_hi>([&](auto dc) {
                     constexpr int d = decltype(dc)::value;
@@ -466,14 +545,42 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     // transposed across the four lane rows g and the four units j with two
     // lane-swap rounds, after which lane row g holds the 16 adjacent columns
     // 16 (u_w + g) .. + 15 of its row: two 16-byte stores per row block.
-    const float gv = global_scale_at(gscale, 0, g_is_div);
+    const float gv = global_scale_at(gscale, e, g_is_div);
+    if constexpr (ACT == kActSiluGlu) {
+        // units u_w + 2 p (gate) and u_w + 2 p + 1 (up): lane (r, g) holds both
+        // for columns 4 g + i of the pair, output column 16 (u_w / 2 + p) + 4 g + i
+        // of N / 2 (u_w is a multiple of 4)
+        static_for<0, MS>([&](auto msc) {
+            constexpr int ms = decltype(msc)::value;
+            const int m = m0 + 16 * ms + r;
+            if (m < mend) {
+                uint16_t* yr = y + (int64_t)m * ld_y;
+#pragma unroll
+                for (int p = 0; p < NT / 2; ++p)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float hg = act_to_f32<F16>(round_out<F16>(scale_acc(gv, acc[ms][2 * p][i])));
+                        const float hu = act_to_f32<F16>(round_out<F16>(scale_acc(gv, acc[ms][2 * p + 1][i])));
+                        const int n = (u_w / 2 + p) * kUnitN + 4 * g + i;
+                        if (n < N / 2) yr[n] = (uint16_t)round_out<F16>(silu_times(hg, hu));
+                    }
+            }
+        });
+        return;
+    }
+    // the value stored for an accumulator (with kActRelu2, the squared ReLU of
+    // the rounded output, rounded again)
+    auto outv = [&](float a) {
+        if constexpr (ACT == kActRelu2) return relu_squared(act_to_f32<F16>(round_out<F16>(scale_acc(gv, a))));
+        else return scale_acc(gv, a);
+    };
     static_for<0, MS>([&](auto msc) {
         constexpr int ms = decltype(msc)::value;
         uint32_t pk[NT][2];   // bf16 pairs of columns 4 g + 2 d, + 1 of unit j (then of unit g: 4 j + 2 d)
         static_for<0, NT>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
-            pk[j][0] = pack_round2<F16>(gv * acc[ms][j][0], gv * acc[ms][j][1]);
-            pk[j][1] = pack_round2<F16>(gv * acc[ms][j][2], gv * acc[ms][j][3]);
+            pk[j][0] = pack_round2<F16>(outv(acc[ms][j][0]), outv(acc[ms][j][1]));
+            pk[j][1] = pack_round2<F16>(outv(acc[ms][j][2]), outv(acc[ms][j][3]));
         });
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
@@ -483,7 +590,7 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
             lane_swap16(pk[2][d], pk[3][d]);
         }
         const int m = m0 + 16 * ms + r;
-        if (m < M) {
+        if (m < mend) {
             uint16_t* yr = y + (int64_t)m * ld_y;
             const int n0 = (u_w + g) * kUnitN;
             if (vec_store && n0 + 15 < N) {

@@ -171,8 +171,7 @@ template <bool F16>
 __device__ __forceinline__ uint32_t silu_mul_pair(uint32_t g2, uint32_t u2) {
     const float g0 = act_to_f32<F16>(g2 & 0xFFFFu), g1 = act_to_f32<F16>(g2 >> 16);
     const float u0 = act_to_f32<F16>(u2 & 0xFFFFu), u1 = act_to_f32<F16>(u2 >> 16);
-    const float a0 = g0 / (1.0f + expf(-g0)) * u0, a1 = g1 / (1.0f + expf(-g1)) * u1;
-    return round_out<F16>(a0) | (round_out<F16>(a1) << 16);
+    return round_out<F16>(silu_times(g0, u0)) | (round_out<F16>(silu_times(g1, u1)) << 16);
 }
 
 template <bool VEC, bool F16 = false>
@@ -199,8 +198,8 @@ __global__ void k_moe_silu_mul(const uint16_t* __restrict__ h, int64_t ld_h, int
 // Thread: 8 columns, 16-byte loads and stores when VEC.
 template <bool F16>
 __device__ __forceinline__ uint32_t relu2_pair(uint32_t h2) {
-    const float a0 = fmaxf(act_to_f32<F16>(h2 & 0xFFFFu), 0.0f), a1 = fmaxf(act_to_f32<F16>(h2 >> 16), 0.0f);
-    return round_out<F16>(a0 * a0) | (round_out<F16>(a1 * a1) << 16);
+    return round_out<F16>(relu_squared(act_to_f32<F16>(h2 & 0xFFFFu))) |
+           (round_out<F16>(relu_squared(act_to_f32<F16>(h2 >> 16))) << 16);
 }
 
 template <bool VEC, bool F16 = false>

@@ -28,6 +28,17 @@
 //   Grouped (MoE) form: grid y has R/BM + E row-tile slots, mapped to
 //   (expert, tile) by a wave-wide prefix scan of the per-expert tile counts
 //   read from expert_offsets; surplus slots exit before touching weights.
+//   The work items (row tile in expert order, column group) are dealt to the
+//   eight XCDs in contiguous ranges: the hardware hands workgroup ids to the
+//   XCDs round robin, so id i takes item (i % 8) * per + i / 8 of the real
+//   items (per = ceil(items / 8); ids with i / 8 >= per exit, so no item runs
+//   twice, and the host's grid holds at least 8 workgroups more than there
+//   can be items, so that every item has an id).  The column groups of a row
+//   tile then run together on one XCD and share its activation rows in that
+//   XCD's L2, and an expert's row tiles follow each other there and share its
+//   weights.
+//   ACT: the MoE activation the epilogue applies (decode.h); with
+//   kActSiluGlu a wave's NT (even) units are gate / up pairs.
 #pragma once
 #include "decode.h"
 #include "kernels_gemm.h"
@@ -36,9 +47,11 @@
 namespace nvfp4 {
 
 constexpr int kTileLDA = 136;   // bf16 per LDS row of the activation stage (128 + 8 pad)
+constexpr int kXcds = 8;        // XCDs of the MI355X: workgroup ids are dealt to them round robin
 
 
-template <int MS, int NT, int UW, int KW, int D, bool GROUPED, bool KFULL, bool F16 = false, bool PRE = false>
+template <int MS, int NT, int UW, int KW, int D, bool GROUPED, bool KFULL, bool F16 = false, bool PRE = false,
+          int ACT = kActNone>
 __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                             int NU, int KC, int K, int N,
                                                             const float* __restrict__ gscale, int g_is_div,
@@ -71,34 +84,49 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
 
     // ---- which rows: dense m-tile, or (expert, m-tile) of the grouped form
     int e = 0;
+    int bx = (int)blockIdx.x;   // column group
     int64_t row0, rows;
     if (GROUPED) {
         if (tid == 0) s_map[0] = -1;
         __syncthreads();
         if (w == 0) {
-            const int by = (int)blockIdx.y;
-            int carry = 0;
-            for (int base = 0; base < E; base += 64) {
-                const int ex = base + lane;
-                const int cnt = ex < E ? (offsets[ex + 1] - offsets[ex]) : 0;
-                const int tiles = (cnt + BM - 1) / BM;
-                int v = tiles;
+            // prefix scan of the per-expert tile counts: pass 0 counts the
+            // row tiles, pass 1 finds this workgroup's (expert, tile)
+            auto scan = [&](int by) {
+                int carry = 0;
+                for (int base = 0; base < E; base += 64) {
+                    const int ex = base + lane;
+                    const int cnt = ex < E ? (offsets[ex + 1] - offsets[ex]) : 0;
+                    const int tiles = (cnt + BM - 1) / BM;
+                    int v = tiles;
 #pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const int t = __shfl_up(v, d);
-                    if (lane >= d) v += t;
+                    for (int d = 1; d < 64; d <<= 1) {
+                        const int t = __shfl_up(v, d);
+                        if (lane >= d) v += t;
+                    }
+                    const int incl = carry + v, excl = incl - tiles;
+                    if (by >= 0 && tiles > 0 && by >= excl && by < incl) {
+                        s_map[0] = ex;
+                        s_map[1] = by - excl;
+                    }
+                    carry += __shfl(v, 63);
                 }
-                const int incl = carry + v, excl = incl - tiles;
-                if (tiles > 0 && by >= excl && by < incl) {
-                    s_map[0] = ex;
-                    s_map[1] = by - excl;
-                }
-                carry += __shfl(v, 63);
+                return carry;
+            };
+            const int64_t groups = gridDim.x;
+            const int64_t items = (int64_t)scan(-1) * groups;
+            const int64_t id = (int64_t)blockIdx.y * groups + blockIdx.x;
+            const int64_t per = (items + kXcds - 1) / kXcds;
+            const int64_t item = (id % kXcds) * per + id / kXcds;
+            if (id / kXcds < per && item < items) {
+                scan((int)(item / groups));
+                if (lane == 0) s_map[2] = (int)(item % groups);
             }
         }
         __syncthreads();
         e = s_map[0];
-        if (e < 0) return;   // uniform: a slot past the last active tile
+        if (e < 0) return;   // uniform: past the last item
+        bx = s_map[2];
         row0 = (int64_t)offsets[e] + (int64_t)s_map[1] * BM;
         rows = (int64_t)offsets[e + 1] - row0;
     } else {
@@ -114,7 +142,7 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
     auto part_begin = [&](int qq) { return C0 + span * qq / KW; };
     const int c0 = part_begin(q), len = part_begin(q + 1) - c0;   // this wave's chunks [c0, c0 + len)
     const int steps = (span + KW - 1) / KW;                          // the longest part
-    const int u_w = (int)blockIdx.x * UG + uw * NT;                 // this wave's first unit
+    const int u_w = bx * UG + uw * NT;                             // this wave's first unit
     const int64_t cstr = bv.chunk_stride * kCodeBlock;
     const uint8_t* cb[NT];
     const uint8_t* sb[NT];
@@ -288,17 +316,39 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
     const float gv = global_scale_at(gscale, e, g_is_div);
     // lane (r, g) of a part-0 wave holds rows 16 ms + 4 g + i of column 16 (u_w + j) + r
     auto store_y = [&]() {
+        if constexpr (ACT == kActSiluGlu) {
+            // units u_w + j (even j: gate) and u_w + j + 1 (up) -> output
+            // column 16 (u_w + j) / 2 + r of N / 2
+            static_assert(NT % 2 == 0, "gate / up units come in pairs");
 #pragma unroll
-        for (int ms = 0; ms < MS; ++ms)
+            for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                const int64_t n = (int64_t)(u_w + j) * kUnitN + r;
+                for (int j = 0; j < NT; j += 2) {
+                    const int64_t n = (int64_t)((u_w + j) / 2) * kUnitN + r;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int m = ms * 16 + g * 4 + i;
-                    if (m < rows && n < N) y[(row0 + m) * ld_y + n] = (uint16_t)round_out<F16>(gv * acc[ms][j][i]);
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = ms * 16 + g * 4 + i;
+                        const float hg = act_to_f32<F16>(round_out<F16>(scale_acc(gv, acc[ms][j][i])));
+                        const float hu = act_to_f32<F16>(round_out<F16>(scale_acc(gv, acc[ms][j + 1][i])));
+                        if (m < rows && n < N / 2)
+                            y[(row0 + m) * ld_y + n] = (uint16_t)round_out<F16>(silu_times(hg, hu));
+                    }
                 }
-            }
+        } else {
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int64_t n = (int64_t)(u_w + j) * kUnitN + r;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = ms * 16 + g * 4 + i;
+                        uint32_t v = round_out<F16>(scale_acc(gv, acc[ms][j][i]));
+                        if constexpr (ACT == kActRelu2) v = round_out<F16>(relu_squared(act_to_f32<F16>(v)));
+                        if (m < rows && n < N) y[(row0 + m) * ld_y + n] = (uint16_t)v;
+                    }
+                }
+        }
     };
     if (S == 1) {
         if (q == 0) store_y();

@@ -203,7 +203,7 @@ __global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict
     for (int j = 0; j < PER; ++j) {
         const int o = tid + j * W * 64, m = (o >> 4) & 15;
         const int64_t col = (int64_t)(u0 + (o >> 8)) * kUnitN + (o & 15);
-        if (o < TILE && m < rows && col < N) y[(int64_t)m * ld_y + col] = (uint16_t)round_out<F16>(gv * v[j]);
+        if (o < TILE && m < rows && col < N) y[(int64_t)m * ld_y + col] = (uint16_t)round_out<F16>(scale_acc(gv, v[j]));
     }
 }
 

@@ -39,4 +39,17 @@ hipError_t launch_mfma_t(const MfmaPlan& plan, const Layout& L, const uint16_t* 
                          const float* gs, int g_div, uint16_t* y, int64_t ld_y, int64_t M, const uint16_t* pre,
                          bool quarter, hipStream_t st);
 
+// Grouped (MoE) form over E experts (L.E): rows [offsets[e], offsets[e+1])
+// use expert e (R rows in all); grouped row r reads activation row
+// row_index[r] when row_index is given.  act: the epilogue's MoE activation
+// (decode.h: kActNone, or kActSiluGlu on a gated blob).  One launch
+// of (R / 256 + E) x (tile columns) + 8 workgroups.
+hipError_t launch_gemm_mfma_grouped(const Layout& L, const uint16_t* x, int64_t ld_x, const int32_t* row_index,
+                                    const int32_t* offsets, int64_t R, const uint8_t* blob, const float* gs, int g_div,
+                                    uint16_t* y, int64_t ld_y, const uint16_t* pre, int act, hipStream_t st, bool f16);
+template <bool F16, bool PRE, bool MX>
+hipError_t launch_mfma_grouped_t(const Layout& L, const uint16_t* x, int64_t ld_x, const int32_t* row_index,
+                                 const int32_t* offsets, int64_t R, const uint8_t* blob, const float* gs, int g_div,
+                                 uint16_t* y, int64_t ld_y, const uint16_t* pre, int act, hipStream_t st);
+
 }  // namespace nvfp4

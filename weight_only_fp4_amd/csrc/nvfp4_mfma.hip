@@ -49,4 +49,22 @@ hipError_t launch_gemm_mfma(const MfmaPlan& p, const Layout& L, const uint16_t* 
 #undef NVFP4_MFMA_FORM
 }
 
+hipError_t launch_gemm_mfma_grouped(const Layout& L, const uint16_t* x, int64_t ld_x, const int32_t* row_index,
+                                    const int32_t* offsets, int64_t R, const uint8_t* blob, const float* gs, int g_div,
+                                    uint16_t* y, int64_t ld_y, const uint16_t* pre, int act, hipStream_t st, bool f16) {
+#define NVFP4_MFMA_GFORM(F16, PRE, MX) \
+    return launch_mfma_grouped_t<F16, PRE, MX>(L, x, ld_x, row_index, offsets, R, blob, gs, g_div, y, ld_y, pre, act, st)
+#define NVFP4_MFMA_GPRE(F16, MX) \
+    if (pre) NVFP4_MFMA_GFORM(F16, true, MX); \
+    NVFP4_MFMA_GFORM(F16, false, MX)
+    if (f16) {
+        if (L.mx) { NVFP4_MFMA_GPRE(true, true); }
+        NVFP4_MFMA_GPRE(true, false);
+    }
+    if (L.mx) { NVFP4_MFMA_GPRE(false, true); }
+    NVFP4_MFMA_GPRE(false, false);
+#undef NVFP4_MFMA_GPRE
+#undef NVFP4_MFMA_GFORM
+}
+
 }  // namespace nvfp4

@@ -216,6 +216,18 @@ nvfp4_status dense_gemm(const void* x, int64_t ld_x, const void* pre, const void
     }
 }
 
+// Grouped kernel choice (the test export nvfp4_w4a16_grouped_gemm_variant
+// forces one): automatic, small-M, tile, MFMA-bound.
+enum GroupedVariant { kGroupedAuto = 0, kGroupedSmall = 1, kGroupedTile = 2, kGroupedMfma = 3 };
+// Average rows per expert from which the automatic choice takes the MFMA-bound
+// kernel.  Measured (E = 128 or 64 experts of equal rows, N = 1536, K = 2048):
+// its 256-row workgroups take about the same time however few of their rows
+// an expert fills (16 to 512 rows: 242-250 us; latency-bound: a workgroup's
+// weight copies run one chunk ahead, and distinct experts share nothing in
+// L2), against 85, 93, 168, 300 and 295 us on the tile kernel at 16, 64, 128,
+// 256 and 512 rows per expert.
+constexpr int64_t kGroupedMfmaRowsPerExpert = 256;
+
 // Grouped GEMM, shared by the plain and the gathering entry points: the
 // activation has x_rows rows; grouped row r reads row row_index[r] of it
 // (row r itself when row_index is NULL).  The grouped kernels never split K,
@@ -224,26 +236,44 @@ nvfp4_status grouped_gemm(const char* fn, const void* x, int64_t ld_x, const int
                           const int32_t* expert_offsets, const void* pre_scale, const void* w_repacked,
                           const float* global_scales, int global_scale_is_divisor, void* y, int64_t ld_y, int64_t R,
                           int64_t E, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes, void* stream,
-                          bool f16, int mx = 0) {
+                          bool f16, int mx = 0, int act = kActNone, int variant = 0) {
     nvfp4_status s = check_weight_shape(fn, E, N, K, mx);
     if (s != NVFP4_OK) return s;
-    s = check_gemm_io(fn, x, ld_x, pre_scale, w_repacked, global_scales, y, ld_y, R, N, K, workspace, workspace_bytes,
-                      0, mx != 0);
+    // the gated epilogue writes N / 2 columns
+    s = check_gemm_io(fn, x, ld_x, pre_scale, w_repacked, global_scales, y, ld_y, R, act == kActSiluGlu ? N / 2 : N,
+                      K, workspace, workspace_bytes, 0, mx != 0);
     if (s != NVFP4_OK) return s;
     if (!expert_offsets) return fail(NVFP4_ERR_INVALID_ARG, "%s: expert_offsets is NULL", fn);
     if (!aligned(expert_offsets, 4)) return fail(NVFP4_ERR_ALIGNMENT, "%s: expert_offsets must be 4-byte aligned", fn);
     if (R > (int64_t)1 << 31) return fail(NVFP4_ERR_INVALID_ARG, "%s: R = %lld exceeds int32 offsets", fn, (long long)R);
     if (R == 0 || N == 0) return ok();   // zero rows or zero columns: nothing is launched
     const Layout L = make_layout(E, N, K, mx);
-    const GemmArgs a{static_cast<const uint16_t*>(x), ld_x, static_cast<const uint8_t*>(w_repacked), global_scales,
-                     global_scale_is_divisor != 0, static_cast<uint16_t*>(y), ld_y, R, expert_offsets, row_index,
-                     static_cast<const uint16_t*>(pre_scale), SplitK{1, nullptr, nullptr},
-                     static_cast<hipStream_t>(stream)};
-    // Few rows per expert on average: the weight stream dominates, use the small-M kernel (passes of 16 rows).
-    if (R <= (int64_t)kSmallRows * E) {
-        const SmallShape sm = small_m_shape(L, R, true);
+    GemmArgs a{static_cast<const uint16_t*>(x), ld_x, static_cast<const uint8_t*>(w_repacked), global_scales,
+               global_scale_is_divisor != 0, static_cast<uint16_t*>(y), ld_y, R, expert_offsets, row_index,
+               static_cast<const uint16_t*>(pre_scale), SplitK{1, nullptr, nullptr},
+               static_cast<hipStream_t>(stream)};
+    a.act = act;
+    // Kernel: few rows per expert on average: the weight stream dominates, the small-M kernel (passes of 16
+    // rows); many: the MFMA-bound kernel in 256-row tiles per expert (weights decoded once per expert and tile
+    // column); between them the tile kernel (64-row tiles).
+    const bool mfma_fits = L.code_bytes() < ((int64_t)1 << 31);
+    if (variant == kGroupedAuto) {
+        variant = R <= (int64_t)kSmallRows * E ? kGroupedSmall
+                : (mfma_fits && act != kActRelu2 && R >= kGroupedMfmaRowsPerExpert * E) ? kGroupedMfma : kGroupedTile;
+    }
+    if (variant == kGroupedSmall) {
+        const SmallShape sm = small_m_shape(L, R, true, act);
         return f16 ? launch_small<true>(sm, L, a, true) : launch_small<false>(sm, L, a, true);
     }
+    if (variant == kGroupedMfma) {
+        if (!mfma_fits) return fail(NVFP4_ERR_INVALID_ARG, "%s: the MFMA-bound kernel takes blobs below 2 GiB of codes", fn);
+        if (act == kActRelu2) return fail(NVFP4_ERR_INVALID_ARG, "%s: the MFMA-bound kernel has no squared-ReLU epilogue", fn);
+        const hipError_t e = launch_gemm_mfma_grouped(L, a.x, ld_x, row_index, expert_offsets, R, a.blob,
+                                                      global_scales, a.g_div, a.y, ld_y, a.pre, act, a.st, f16);
+        if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "%s: MFMA GEMM launch failed: %s", fn, hipGetErrorString(e));
+        return ok();
+    }
+    if (variant != kGroupedTile) return fail(NVFP4_ERR_INVALID_ARG, "%s: unknown variant %d", fn, variant);
     const TileShape t = tile_shape(L, R, true);
     return f16 ? launch_tile<true>(t, L, a, true) : launch_tile<false>(t, L, a, true);
 }
@@ -327,9 +357,13 @@ int64_t nvfp4_repack_bytes(int64_t E, int64_t N, int64_t K) {
 namespace {
 
 nvfp4_status repack_impl(const char* fn, const uint8_t* w_packed, int64_t ld_w, const uint8_t* w_scale, int64_t ld_s,
-                         int64_t E, int64_t N, int64_t K, void* out, int64_t out_bytes, void* stream, int mx) {
+                         int64_t E, int64_t N, int64_t K, void* out, int64_t out_bytes, void* stream, int mx,
+                         int64_t gate_I = 0, int up_first = 0) {
     nvfp4_status s = check_weight_shape(fn, E, N, K, mx);
     if (s != NVFP4_OK) return s;
+    if (gate_I > 0 && (N != 2 * gate_I || gate_I % kUnitN != 0))
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: the gated layout needs I = %lld to be a multiple of 16", fn,
+                    (long long)gate_I);
     if (N == 0) return ok();   // no rows: nothing to repack, nothing is launched
     if (!w_packed) return fail(NVFP4_ERR_INVALID_ARG, "%s: w_packed is NULL", fn);
     if (!w_scale) return fail(NVFP4_ERR_INVALID_ARG, "%s: w_scale is NULL", fn);
@@ -347,7 +381,7 @@ nvfp4_status repack_impl(const char* fn, const uint8_t* w_packed, int64_t ld_w, 
     uint8_t* o = static_cast<uint8_t*>(out);
     hipLaunchKernelGGL(k_repack, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, static_cast<hipStream_t>(stream),
                        w_packed, ld_w, w_scale, ld_s, N, K, L.NU, L.KC, lanes, make_view(L, o), o, o + L.code_bytes(),
-                       mx);
+                       mx, gate_I, up_first);
     return launched(fn);
 }
 
@@ -374,6 +408,21 @@ extern "C" {
 nvfp4_status nvfp4_repack(const uint8_t* w_packed, int64_t ld_w, const uint8_t* w_scale, int64_t ld_s, int64_t E,
                           int64_t N, int64_t K, void* out, int64_t out_bytes, void* stream) {
     return repack_impl("nvfp4_repack", w_packed, ld_w, w_scale, ld_s, E, N, K, out, out_bytes, stream, 0);
+}
+
+int64_t nvfp4_repack_gated_bytes(int64_t E, int64_t I, int64_t K) {
+    if (I < 0 || I % kUnitN != 0) return -1;
+    return nvfp4_repack_bytes(E, 2 * I, K);
+}
+
+nvfp4_status nvfp4_repack_gated(const uint8_t* w_packed, int64_t ld_w, const uint8_t* w_scale, int64_t ld_s,
+                                int64_t E, int64_t I, int64_t K, int up_first, void* out, int64_t out_bytes,
+                                void* stream) {
+    const char* fn = "nvfp4_repack_gated";
+    if (I < 0 || I % kUnitN != 0)
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: I = %lld must be a non-negative multiple of 16", fn, (long long)I);
+    if (up_first != 0 && up_first != 1) return fail(NVFP4_ERR_INVALID_ARG, "%s: up_first must be 0 or 1", fn);
+    return repack_impl(fn, w_packed, ld_w, w_scale, ld_s, E, 2 * I, K, out, out_bytes, stream, 0, I, up_first);
 }
 
 nvfp4_status nvfp4_dequant_bf16(const void* w_repacked, int64_t E, int64_t N, int64_t K, void* out, int64_t ld_out,
@@ -493,7 +542,7 @@ static nvfp4_status grouped_gemm_gather(const char* fn, const void* x, int64_t l
                                         const void* pre_scale, const void* w_repacked, const float* global_scales,
                                         int global_scale_is_divisor, void* y, int64_t ld_y, int64_t R, int64_t E,
                                         int64_t N, int64_t K, void* workspace, int64_t workspace_bytes, void* stream,
-                                        bool f16) {
+                                        bool f16, int act = kActNone, int variant = 0, int mx = 0) {
     if (T < 0) return fail(NVFP4_ERR_INVALID_ARG, "%s: token count %lld is negative", fn, (long long)T);
     if (R > 0 && !row_token) return fail(NVFP4_ERR_INVALID_ARG, "%s: row_token is NULL", fn);
     if (!aligned(row_token, 4)) return fail(NVFP4_ERR_ALIGNMENT, "%s: row_token must be 4-byte aligned", fn);
@@ -502,7 +551,35 @@ static nvfp4_status grouped_gemm_gather(const char* fn, const void* x, int64_t l
     if (T * ld_x >= ((int64_t)1 << 31))
         return fail(NVFP4_ERR_INVALID_ARG, "%s: T * ld_x = %lld must stay below 2^31", fn, (long long)(T * ld_x));
     return grouped_gemm(fn, x, ld_x, row_token, expert_offsets, pre_scale, w_repacked, global_scales,
-                        global_scale_is_divisor, y, ld_y, R, E, N, K, workspace, workspace_bytes, stream, f16);
+                        global_scale_is_divisor, y, ld_y, R, E, N, K, workspace, workspace_bytes, stream, f16, mx, act,
+                        variant);
+}
+
+// FC1 of a MoE layer with its activation in the epilogue: gated SiLU on a
+// blob from nvfp4_repack_gated (N = 2 I), or the squared ReLU on a plain
+// blob (N = I); row_token NULL: x holds the R grouped rows.
+static nvfp4_status moe_fc1(const char* fn, const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
+                            const int32_t* expert_offsets, const void* pre_scale, const void* w_fc1,
+                            const float* global_scales, int global_scale_is_divisor, int activation, void* a,
+                            int64_t ld_a, int64_t R, int64_t E, int64_t I, int64_t K, void* stream, bool f16) {
+    int act;
+    if (activation == NVFP4_MOE_SILU_GLU) act = kActSiluGlu;
+    else if (activation == NVFP4_MOE_RELU2) act = kActRelu2;
+    else return fail(NVFP4_ERR_INVALID_ARG, "%s: activation %d is not NVFP4_MOE_SILU_GLU or NVFP4_MOE_RELU2", fn,
+                     activation);
+    if (I < 0) return fail(NVFP4_ERR_INVALID_ARG, "%s: I = %lld is negative", fn, (long long)I);
+    if (act == kActSiluGlu && I % kUnitN != 0)
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: the gated layout needs I = %lld to be a multiple of 16", fn,
+                    (long long)I);
+    if (ld_a < I) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_a = %lld < I = %lld", fn, (long long)ld_a, (long long)I);
+    const int64_t N = act == kActSiluGlu ? 2 * I : I;
+    if (!row_token) {
+        if (T != R) return fail(NVFP4_ERR_INVALID_ARG, "%s: without row_token x holds the R grouped rows (T = R)", fn);
+        return grouped_gemm(fn, x, ld_x, nullptr, expert_offsets, pre_scale, w_fc1, global_scales,
+                            global_scale_is_divisor, a, ld_a, R, E, N, K, nullptr, 0, stream, f16, 0, act);
+    }
+    return grouped_gemm_gather(fn, x, ld_x, T, row_token, expert_offsets, pre_scale, w_fc1, global_scales,
+                               global_scale_is_divisor, a, ld_a, R, E, N, K, nullptr, 0, stream, f16, act);
 }
 
 nvfp4_status nvfp4_w4a16_grouped_gemm_gather(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
@@ -525,6 +602,50 @@ nvfp4_status nvfp4_w4a16_grouped_gemm_gather_f16(const void* x, int64_t ld_x, in
     return grouped_gemm_gather("nvfp4_w4a16_grouped_gemm_gather_f16", x, ld_x, T, row_token, expert_offsets,
                                pre_scale, w_repacked, global_scales, global_scale_is_divisor, y, ld_y, R, E, N, K,
                                workspace, workspace_bytes, stream, true);
+}
+
+nvfp4_status nvfp4_w4a16_grouped_gemm_variant(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
+                                              const int32_t* expert_offsets, const void* pre_scale, const void* w,
+                                              const float* global_scales, int global_scale_is_divisor, int activation,
+                                              void* y, int64_t ld_y, int64_t R, int64_t E, int64_t N, int64_t K,
+                                              int variant, int f16, int mx, void* stream) {
+    const char* fn = "nvfp4_w4a16_grouped_gemm_variant";
+    if (mx != 0 && mx != 1) return fail(NVFP4_ERR_INVALID_ARG, "%s: mx must be 0 or 1", fn);
+    int act;
+    if (activation == 0) act = kActNone;
+    else if (activation == NVFP4_MOE_SILU_GLU) act = kActSiluGlu;
+    else if (activation == NVFP4_MOE_RELU2) act = kActRelu2;
+    else return fail(NVFP4_ERR_INVALID_ARG, "%s: unknown activation %d", fn, activation);
+    if (variant < kGroupedAuto || variant > kGroupedMfma)
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: unknown variant %d", fn, variant);
+    if (act == kActSiluGlu && N % (2 * kUnitN) != 0)
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: the gated layout needs N = %lld to be a multiple of 32", fn,
+                    (long long)N);
+    if (!row_token) {
+        if (T != R) return fail(NVFP4_ERR_INVALID_ARG, "%s: without row_token x holds the R grouped rows (T = R)", fn);
+        return grouped_gemm(fn, x, ld_x, nullptr, expert_offsets, pre_scale, w, mx ? nullptr : global_scales,
+                            global_scale_is_divisor, y, ld_y, R, E, N, K, nullptr, 0, stream, f16 != 0, mx, act,
+                            variant);
+    }
+    return grouped_gemm_gather(fn, x, ld_x, T, row_token, expert_offsets, pre_scale, w, mx ? nullptr : global_scales,
+                               global_scale_is_divisor, y, ld_y, R, E, N, K, nullptr, 0, stream, f16 != 0, act,
+                               variant, mx);
+}
+
+nvfp4_status nvfp4_moe_fc1(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
+                           const int32_t* expert_offsets, const void* pre_scale, const void* w_fc1,
+                           const float* global_scales, int global_scale_is_divisor, int activation, void* a,
+                           int64_t ld_a, int64_t R, int64_t E, int64_t I, int64_t K, void* stream) {
+    return moe_fc1("nvfp4_moe_fc1", x, ld_x, T, row_token, expert_offsets, pre_scale, w_fc1, global_scales,
+                   global_scale_is_divisor, activation, a, ld_a, R, E, I, K, stream, false);
+}
+
+nvfp4_status nvfp4_moe_fc1_f16(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
+                               const int32_t* expert_offsets, const void* pre_scale, const void* w_fc1,
+                               const float* global_scales, int global_scale_is_divisor, int activation, void* a,
+                               int64_t ld_a, int64_t R, int64_t E, int64_t I, int64_t K, void* stream) {
+    return moe_fc1("nvfp4_moe_fc1_f16", x, ld_x, T, row_token, expert_offsets, pre_scale, w_fc1, global_scales,
+                   global_scale_is_divisor, activation, a, ld_a, R, E, I, K, stream, true);
 }
 
 // --------------------------------------------------- no-allocation entry --

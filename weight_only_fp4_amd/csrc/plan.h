@@ -37,6 +37,7 @@ struct GemmArgs {
     const uint16_t* pre;        // pre-quant scale [K] or NULL
     SplitK sk;
     hipStream_t st;
+    int act = kActNone;         // grouped forms: the MoE activation of the epilogue (decode.h)
 };
 
 // ---------------------------------------------------------------- small-M --
@@ -75,11 +76,12 @@ inline bool small_compiled(const SmallShape& s) {
 // (16x16x32 form, about two VALU operations per weight to decode) share each
 // activation fragment over four units per wave; the automatic choice sends
 // those rows to the activation-resident kernel.
-inline SmallShape small_m_shape(const Layout& L, int64_t rows, bool grouped) {
+inline SmallShape small_m_shape(const Layout& L, int64_t rows, bool grouped, int act = kActNone) {
     SmallShape s;
     s.S = 1;
     if (grouped) {
-        s.mg = 0; s.nt = 1; s.d = 4;
+        // the gated epilogue needs each gate / up unit pair in one workgroup
+        s.mg = 0; s.nt = act == kActSiluGlu ? 2 : 1; s.d = 4;
     } else if (rows <= 8) {
         s.mg = rows <= 4 ? 1 : 2; s.nt = L.NU >= 2048 ? 2 : 1; s.d = 4;
     } else {
@@ -95,7 +97,9 @@ inline SmallShape small_m_shape(const Layout& L, int64_t rows, bool grouped) {
     }
     s.w = 1;
     if (!grouped && s.nt == 2) return s;   // wide N: one wave per workgroup
-    const int64_t ctas = s.groups * (grouped ? (L.E + 1) / 2 : 1);
+    // grouped: sized by units, so that the paired (gated) form splits K over
+    // the same waves as the plain form and sums in the same order
+    const int64_t ctas = grouped ? L.NU * ((L.E + 1) / 2) : s.groups;
     // 16 waves cap a kernel at 128 VGPRs: only the one-row-group form fits
     const int wmax = s.mg == 1 ? 16 : 8;
     while (s.w < wmax && ctas * (2 * s.w) * s.d <= 8192 && L.KC >= 4 * (2 * s.w)) s.w *= 2;
@@ -122,7 +126,7 @@ inline TileShape tile_shape(const Layout& L, int64_t rows, bool grouped) {
     TileShape t;
     bool split = true;
     if (grouped) {
-        t.ms = 4; t.nt = 4; t.uw = 4; t.kw = 1; t.d = 2; split = false;
+        t.ms = 4; t.nt = 4; t.uw = 4; t.kw = 1; t.d = 3; split = false;
     } else if (rows <= 16) {
         t.ms = 1; t.nt = 1; t.uw = 4; t.kw = 4; t.d = 2;
     } else if (rows <= 32) {
@@ -137,7 +141,10 @@ inline TileShape tile_shape(const Layout& L, int64_t rows, bool grouped) {
         t.ms = 8; t.nt = 2; t.uw = 8; t.kw = 1; t.d = 2;
     }
     t.groups = (L.NU + t.ug() - 1) / t.ug();
-    t.mtiles = (rows + t.bm() - 1) / t.bm() + (grouped ? L.E : 0);
+    // grouped: row tiles are at most rows / BM + E; the kernel deals (row
+    // tile, column group) items to the XCDs in ranges of ceil(items / 8) and
+    // needs 8 workgroups beyond the item count for that
+    t.mtiles = (rows + t.bm() - 1) / t.bm() + (grouped ? L.E + (8 + t.groups - 1) / t.groups : 0);
     t.S = 1;
     while (split && t.S < 16 && t.tiles() * 2 * t.S <= 256 && L.KC >= 2 * t.kw * (2 * t.S)) t.S *= 2;
     return t;

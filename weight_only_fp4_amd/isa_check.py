@@ -12,7 +12,9 @@ The CDNA3/CDNA4 ISA requires:
   8 passes; 18 is taken here as the bound, above the 8-pass figure plus the
   extra issue cycles);
 * five wait states between a VALU write of an SGPR (v_readfirstlane, a
-  compare into an SGPR pair) and a copy reading that SGPR as its base address.
+  compare into an SGPR pair, v_readlane restoring a spilled scalar) and a copy
+  reading that SGPR as its base address, unless a scalar instruction writes
+  the SGPR again in between (the copy then reads that value).
 
 Whether the scheduler leaves enough independent instructions in between
 depends on the instantiation, so the build compiles each form of the kernel's
@@ -92,6 +94,19 @@ def _is_valu(op: str) -> bool:
     return op.startswith("v_") and not op.startswith("v_mfma")
 
 
+# scalar instructions whose first operand is a source, not a destination
+_NO_SCALAR_DEST = ("s_cmp", "s_bitcmp", "s_cbranch", "s_branch", "s_waitcnt", "s_nop", "s_barrier", "s_set",
+                   "s_sleep", "s_endpgm", "s_sendmsg")
+
+
+def _sgpr_dest(inst: str):
+    """SGPRs the instruction writes (its first operand, where that is a destination)."""
+    op, ops = inst.split()[0], _operands(inst)
+    if not ops or op.startswith(_NO_SCALAR_DEST):
+        return set()
+    return _sregs(ops[0])
+
+
 def hazards(text: str):
     """Every violation of the rules above in the MFMA-bound kernels of one
     assembly listing, as readable strings (empty: none)."""
@@ -121,13 +136,15 @@ def hazards(text: str):
             elif op.startswith("global_load_lds") and inasm:
                 used = set().union(*[_sregs(t) for t in _operands(s)])
                 ws, j = 0, i - 1
-                while j >= 0 and ws < VALU_SGPR_TO_VMEM:
+                while j >= 0 and ws < VALU_SGPR_TO_VMEM and used:
                     k2, s2, _ = L[j]
                     if k2 == "label":
                         found.append(f"{name}: branch target within {VALU_SGPR_TO_VMEM} wait states of '{s}'")
                         break
-                    if _is_valu(s2.split()[0]) and _operands(s2) and _sregs(_operands(s2)[0]) & used:
+                    dst = _sgpr_dest(s2)
+                    if _is_valu(s2.split()[0]) and dst & used:
                         found.append(f"{name}: '{s2}' {ws} wait states before '{s}'")
+                    used -= dst   # an earlier write of these no longer reaches the copy
                     ws += _wait_states(s2)
                     j -= 1
             elif not op.startswith("v_mfma") and any(_regs(t)[0] == "a" for t in _operands(s)):
