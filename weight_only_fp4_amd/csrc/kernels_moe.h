@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "combine.h"
 #include "decode.h"
 
 namespace nvfp4 {
@@ -231,36 +232,21 @@ __global__ void k_moe_combine(const uint16_t* __restrict__ y, int64_t ld_y, cons
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= T * per_row) return;
     const int64_t t = idx / per_row, c0 = (idx % per_row) * 8;
-    const bool full = VEC && c0 + 8 <= H;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-        const float wj = wt[t * k + j];
-        const uint16_t* yr = y + (int64_t)token_row[t * k + j] * ld_y + c0;
-        if (full) {
-            const uint4 v = *reinterpret_cast<const uint4*>(yr);
-            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    if (VEC && c0 + 8 <= H) {
+        combine_slots<F16>(token_row, wt, t * k, k, [&](int row) {
+            return *reinterpret_cast<const uint4*>(y + (int64_t)row * ld_y + c0);
+        }, acc);
+    } else {
+        combine_slots<F16>(token_row, wt, t * k, k, [&](int row) {
+            const uint16_t* yr = y + (int64_t)row * ld_y + c0;
+            uint32_t v[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[2 * e] = __builtin_fmaf(wj, act_to_f32<F16>(d[e] & 0xFFFFu), acc[2 * e]);
-                acc[2 * e + 1] = __builtin_fmaf(wj, act_to_f32<F16>(d[e] >> 16), acc[2 * e + 1]);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (c0 + e < H) acc[e] = __builtin_fmaf(wj, act_to_f32<F16>(yr[e]), acc[e]);
-        }
+            for (int e = 0; e < 8; ++e) v[e] = c0 + e < H ? yr[e] : 0u;
+            return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+        }, acc);
     }
-    uint16_t* orow = out + t * ld_o + c0;
-    if (full) {
-        uint32_t p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = round_out<F16>(acc[2 * e]) | (round_out<F16>(acc[2 * e + 1]) << 16);
-        *reinterpret_cast<uint4*>(orow) = make_uint4(p[0], p[1], p[2], p[3]);
-        return;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        if (c0 + e < H) orow[e] = (uint16_t)round_out<F16>(acc[e]);
+    combine_store<F16>(out + t * ld_o + c0, c0, H, acc);
 }
 
 }  // namespace nvfp4
