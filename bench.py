@@ -163,9 +163,9 @@ def make_grouped(name, T, fc, *, seed=1004, E=128, topk=8):
 
 
 def make_moe_layer(name, T, *, seed=1004, E=128, topk=8, hidden=2048, inter=768, fused=True):
-    """A whole MoE layer on the device: routing, FC1 with the token gather fused (N = 2 inter), FC2 (K = inter)
-    and the top-k combine; fused: the gated SiLU in FC1's epilogue and the combine in FC2's, else both as steps of
-    their own.  Weight copies rotate as for the grouped workloads."""
+    """A whole MoE layer on the device: routing, FC1 with the token gather fused (N = 2 inter) and, when fused,
+    the gated SiLU in its epilogue (else a separate SiLU step), FC2 (K = inter), top-k combine.  Weight copies
+    rotate as for the grouped workloads."""
     import numpy as np
     import torch
     import synth
@@ -194,13 +194,11 @@ def make_moe_layer(name, T, *, seed=1004, E=128, topk=8, hidden=2048, inter=768,
     token_row = torch.empty(R, dtype=torch.int32, device=dev)
     h = None if fused else torch.empty((R, 2 * inter), dtype=torch.bfloat16, device=dev)
     a = torch.empty((R, inter), dtype=torch.bfloat16, device=dev)
-    y2 = None if fused else torch.empty((R, hidden), dtype=torch.bfloat16, device=dev)
+    y2 = torch.empty((R, hidden), dtype=torch.bfloat16, device=dev)
     out = torch.empty((T, hidden), dtype=torch.bfloat16, device=dev)
     L = nv.lib()
     ws1 = nv.workspace(L.nvfp4_w4a16_grouped_gemm_gather_workspace_bytes(T, R, E, 2 * inter, hidden), dev)
     ws2 = nv.workspace(L.nvfp4_w4a16_grouped_gemm_workspace_bytes(R, E, hidden, inter), dev)
-    wsc = nv.workspace(L.nvfp4_moe_fc2_combine_workspace_bytes(T, topk, E, hidden, inter), dev)
-    ctr = torch.zeros(L.nvfp4_moe_fc2_combine_counters(T, hidden), dtype=torch.int32, device=dev)
     wsr = nv.workspace(L.nvfp4_moe_route_workspace_bytes(T, topk, E), dev)
     st = lambda: nv._stream(x.device)
 
@@ -210,21 +208,19 @@ def make_moe_layer(name, T, *, seed=1004, E=128, topk=8, hidden=2048, inter=768,
                                     nv._ptr(wsr), wsr.numel(), st()))
         if fused:
             nv.moe_fc1(x, row_token, off, w1, E, inter, hidden, g1, nv.MOE_SILU_GLU, out=a)
-            nv.moe_fc2_combine(a, off, row_token, token_row, wts, w2, E, hidden, inter, g2, out=out,
-                               workspace_buf=wsc, counters=ctr)
         else:
             nv.grouped_gemm_gather(x, row_token, off, w1, E, 2 * inter, hidden, g1, out=h, workspace_buf=ws1)
             nv.moe_silu_mul(h, out=a)
-            nv.grouped_gemm(a, off, w2, E, hidden, inter, g2, out=y2, workspace_buf=ws2)
-            nv.moe_combine(y2, token_row, wts, out=out)
+        nv.grouped_gemm(a, off, w2, E, hidden, inter, g2, out=y2, workspace_buf=ws2)
+        nv.moe_combine(y2, token_row, wts, out=out)
 
     # algorithmic bytes of the layer: active weights, the tokens in and out, routing ids and weights
     ab = w_bytes + 2.0 * T * hidden * 2 + 8.0 * T * topk
     flops = 2.0 * R * hidden * (2 * inter) + 2.0 * R * inter * hidden
     bound = "hbm" if flops / ab < (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) else "mfma"
     meta = {"E": E, "topk": topk, "T": T, "R": R, "hidden": hidden, "inter": inter, "active_experts": active,
-            "weight_copies": copies, "steps_per_call": "route, FC1 (gather) with the gated SiLU in its epilogue, FC2 "
-                                                       "with the combine in its epilogue" if fused else "route, FC1 (gather), SiLU, FC2, combine"}
+            "weight_copies": copies, "steps_per_call": "route, FC1 (gather) with the gated SiLU in its epilogue, FC2, "
+                                                       "combine" if fused else "route, FC1 (gather), SiLU, FC2, combine"}
     wl = Workload(name, "moe_layer", "moe_layer", ab, flops, launch, copies, meta, bound)
     wl.tensors = dict(x=x, out=out, blobs=blobs)
     return wl

@@ -161,9 +161,9 @@ nvfp4_status nvfp4_w4a16_grouped_gemm(const void* x, int64_t ld_x, const int32_t
  *   -> nvfp4_moe_silu_mul -> nvfp4_w4a16_grouped_gemm (FC2, K = I, N = Hd)
  *   -> nvfp4_moe_combine,
  * or with the activation in FC1's epilogue (one step fewer, and FC1 writes
- * I columns instead of 2 I) and the combine in FC2's:
+ * I columns instead of 2 I):
  *   nvfp4_moe_route -> nvfp4_moe_fc1 (gated weights from nvfp4_repack_gated)
- *   -> nvfp4_moe_fc2_combine,
+ *   -> nvfp4_w4a16_grouped_gemm (FC2) -> nvfp4_moe_combine,
  * every step stream-ordered, with no host synchronisation.
  *
  * Routing: topk_ids is device int32 [T][k] (row t: the k experts of token
@@ -291,39 +291,6 @@ nvfp4_status nvfp4_w4a16_grouped_gemm_variant(const void* x, int64_t ld_x, int64
  * INVALID_ARG; misaligned pointer -> ALIGNMENT. */
 nvfp4_status nvfp4_moe_combine(const void* y, int64_t ld_y, const int32_t* token_row, const float* topk_weights,
                                int64_t T, int64_t k, int64_t H, void* out, int64_t ld_o, void* stream);
-
-/* FC2 with the top-k combine in its epilogue: out[t][c] =
- * RNE_bf16(sum_{j=0..k-1} topk_weights[t*k + j] * y[token_row[t*k + j]][c])
- * with y = nvfp4_w4a16_grouped_gemm(a, ...) (FC2 in grouped row order,
- * rounded to bf16), accumulated in fp32 in slot order: bitwise
- * nvfp4_w4a16_grouped_gemm followed by nvfp4_moe_combine.  a: bf16 [T*k][ld_a]
- * (FC2's input in grouped row order, e.g. from nvfp4_moe_fc1); w_fc2: E
- * experts, N = H (the hidden size), K = I; expert_offsets, row_token and
- * token_row from nvfp4_moe_route; topk_weights: device fp32 [T][k]; out: bf16
- * [T][ld_o].  The workgroups producing a token's k rows exchange them through
- * the workspace and the last of them sums the token (a device-scope counter
- * per token and 16-column unit), so FC2's rows are never read back by another
- * kernel.
- * workspace: nvfp4_moe_fc2_combine_workspace_bytes(T, k, E, H, I) bytes,
- * 256-byte aligned, any contents (FC2's rows pass through it).
- * counters: device int32, at least nvfp4_moe_fc2_combine_counters(T, H)
- * entries, zero-filled before their first use.  They only ever hold arrival
- * counts and every call returns the entries it used to zero, so one array
- * serves calls of any shape one after another on a stream; calls that may
- * overlap in time need their own counters and workspaces.
- * Errors: T < 0, k < 1, k > E, T*k >= 2^31, ld_o < H, a NULL routing array
- * or output (T > 0), and the weight / activation checks of the grouped GEMM
- * -> INVALID_ARG; misaligned arrays -> ALIGNMENT; workspace or counters too
- * small -> BUFFER_TOO_SMALL.  T == 0 or H == 0 returns NVFP4_OK without
- * launching anything. */
-int64_t nvfp4_moe_fc2_combine_workspace_bytes(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I);
-int64_t nvfp4_moe_fc2_combine_counters(int64_t T, int64_t H);
-nvfp4_status nvfp4_moe_fc2_combine(const void* a, int64_t ld_a, const int32_t* expert_offsets,
-                                   const int32_t* row_token, const int32_t* token_row, const float* topk_weights,
-                                   const void* w_fc2, const float* global_scales, int global_scale_is_divisor,
-                                   void* out, int64_t ld_o, int64_t T, int64_t k, int64_t E, int64_t H, int64_t I,
-                                   void* workspace, int64_t workspace_bytes, int32_t* counters,
-                                   int64_t counter_count, void* stream);
 
 /* --------------------------------------------------------- test exports --
  * Decode a repacked blob back to bf16 [E][N][ld_out] in canonical order with
@@ -491,18 +458,11 @@ nvfp4_status nvfp4_moe_relu2_f16(const void* h, int64_t ld_h, int64_t R, int64_t
                                  void* stream);
 nvfp4_status nvfp4_moe_combine_f16(const void* y, int64_t ld_y, const int32_t* token_row, const float* topk_weights,
                                    int64_t T, int64_t k, int64_t H, void* out, int64_t ld_o, void* stream);
-/* nvfp4_moe_fc1 and nvfp4_moe_fc2_combine with fp16 activations and outputs
- * (RNE to fp16 throughout). */
+/* nvfp4_moe_fc1 with fp16 activations and output (RNE to fp16 throughout). */
 nvfp4_status nvfp4_moe_fc1_f16(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
                                const int32_t* expert_offsets, const void* pre_scale, const void* w_fc1,
                                const float* global_scales, int global_scale_is_divisor, int activation, void* a,
                                int64_t ld_a, int64_t R, int64_t E, int64_t I, int64_t K, void* stream);
-nvfp4_status nvfp4_moe_fc2_combine_f16(const void* a, int64_t ld_a, const int32_t* expert_offsets,
-                                       const int32_t* row_token, const int32_t* token_row, const float* topk_weights,
-                                       const void* w_fc2, const float* global_scales, int global_scale_is_divisor,
-                                       void* out, int64_t ld_o, int64_t T, int64_t k, int64_t E, int64_t H, int64_t I,
-                                       void* workspace, int64_t workspace_bytes, int32_t* counters,
-                                       int64_t counter_count, void* stream);
 
 #ifdef __cplusplus
 }

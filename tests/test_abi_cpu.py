@@ -264,41 +264,3 @@ def test_gated_repack_and_fused_fc1_argument_errors():
     assert fc1(*args(R=0)) == OK                                                      # zero rows: no launch
     st = L.nvfp4_moe_fc1_f16(*args(act=0))
     assert st == INVALID and "nvfp4_moe_fc1_f16" in L.nvfp4_last_error().decode()
-
-
-def test_fc2_combine_argument_errors():
-    """nvfp4_moe_fc2_combine rejects bad arguments and short buffers on the host; T = 0 succeeds."""
-    L = nv.lib()
-    wsb, cnt = L.nvfp4_moe_fc2_combine_workspace_bytes, L.nvfp4_moe_fc2_combine_counters
-    # T k rows of round_up(H, 8) 16-bit values, to a 256-byte boundary; one counter per token and 16 columns
-    assert wsb(16, 4, 8, 200, 64) == 16 * 4 * 200 * 2
-    assert wsb(3, 2, 8, 30, 64) == 512
-    assert cnt(16, 200) == 16 * 13 and cnt(3, 30) == 6 and cnt(5, 0) == 0
-    assert cnt(-1, 16) == -1
-    assert wsb(16, 9, 8, 256, 64) == -1                                               # k > E
-    assert wsb(16, 0, 8, 256, 64) == -1
-    assert wsb(-1, 2, 8, 256, 64) == -1
-    assert wsb(16, 2, 8, 256, 72) == -1                                               # I % 16
-    fc2 = L.nvfp4_moe_fc2_combine
-    need, nc = wsb(16, 4, 8, 256, 64), cnt(16, 256)
-    args = lambda **kw: [kw.get(n, d) for n, d in [
-        ("a", _p(A)), ("ld_a", 64), ("off", _p(A)), ("rt", _p(A)), ("tr", _p(A)), ("wt", _p(A)), ("w", _p(A)),
-        ("g", _p(A)), ("div", 0), ("out", _p(A)), ("ld_o", 256), ("T", 16), ("k", 4), ("E", 8), ("H", 256),
-        ("I", 64), ("ws", _p(A)), ("wsb", need), ("ctr", _p(A)), ("nc", nc), ("st", None)]]
-    assert fc2(*args(k=9)) == INVALID and "k = 9" in L.nvfp4_last_error().decode()
-    assert fc2(*args(ld_o=255)) == INVALID and "ld_o" in L.nvfp4_last_error().decode()
-    assert fc2(*args(tr=None)) == INVALID and "NULL" in L.nvfp4_last_error().decode()
-    assert fc2(*args(wt=_p(A + 2))) == ALIGN
-    assert fc2(*args(out=_p(A + 1))) == ALIGN
-    assert fc2(*args(ctr=_p(A + 2))) == ALIGN
-    assert fc2(*args(wsb=need - 1)) == SMALL
-    assert fc2(*args(ws=None)) == SMALL
-    assert fc2(*args(ws=_p(A + 16))) == ALIGN
-    assert fc2(*args(nc=nc - 1)) == SMALL and "counters" in L.nvfp4_last_error().decode()
-    assert fc2(*args(ctr=None)) == SMALL
-    assert fc2(*args(I=72)) == INVALID                                                # K % 16
-    assert fc2(*args(ld_a=32)) == INVALID                                             # ld_a < I
-    assert fc2(*args(off=None)) == INVALID and "expert_offsets" in L.nvfp4_last_error().decode()
-    assert fc2(*args(T=0, ws=None, wsb=0, rt=None, tr=None, wt=None, out=None, ctr=None, nc=0)) == OK  # no launch
-    st = L.nvfp4_moe_fc2_combine_f16(*args(k=0))
-    assert st == INVALID and "nvfp4_moe_fc2_combine_f16" in L.nvfp4_last_error().decode()

@@ -1,13 +1,11 @@
-"""The MoE FC1 with its activation in the GEMM epilogue (nvfp4_moe_fc1) and FC2 with the top-k combine in its
-epilogue (nvfp4_moe_fc2_combine) on the GPU.
+"""The MoE FC1 with its activation in the GEMM epilogue (nvfp4_moe_fc1) on the GPU.
 
-The fused FC1 rounds its outputs to the activation type and applies the same fp32 activation as the standalone
+The fused call rounds FC1's outputs to the activation type and applies the same fp32 activation as the standalone
 glue kernels, so it must equal, bitwise, the unfused chain (grouped GEMM with the gather, then nvfp4_moe_silu_mul or
 nvfp4_moe_relu2) on the canonical weights; the unfused chain is in turn checked against the oracle.  The gated blob
 is built from either gate / up order of the canonical FC1 weight (gate first, as SGLang's w13; up first, as
-TensorRT-LLM's w3_w1), which must give the same bytes.  The fused FC2 sums the same rounded FC2 outputs in the same
-fp32 order as nvfp4_moe_combine, so it too must equal the unfused chain bitwise.  At the benchmark's sizes the
-oracle is evaluated on sampled outputs."""
+TensorRT-LLM's w3_w1), which must give the same bytes.  At the benchmark's sizes the oracle is evaluated on
+sampled outputs."""
 import numpy as np
 import pytest
 import torch
@@ -166,115 +164,3 @@ def test_moe_layer_with_fused_fc1(T):
     out1 = nv.moe_combine(nv.grouped_gemm(a1, off, b2, E, Hd, I, f32_dev(g2)), token_row, wts)
     torch.cuda.synchronize()
     assert torch.equal(out1, out0)
-
-
-class Fc2Case:
-    """FC2's input in grouped row order (a [T k, I], as FC1 leaves it), routing, routing weights and one FC2
-    weight (E experts, H rows, I columns)."""
-
-    def __init__(self, T, E, topk, H, I, seed, act="bf16"):
-        g = synth.rng(seed)
-        self.T, self.E, self.topk, self.H, self.I, self.act = T, E, topk, H, I, act
-        self.a = synth.normal_act(g, (T * topk, I), act)
-        self.w = synth.random_codes(g, (E, H, I))
-        self.s = synth.scales_pow2_mant(g, (E, H, I // 16))
-        self.g = (np.exp2(g.integers(-2, 3, E).astype(np.float64)) / 2688).astype(np.float32)
-        self.wts = g.random((T, topk)).astype(np.float32)
-        self.ids = synth.zipf_routing(synth.rng(seed + 1), T, E, topk)
-
-    def dev(self):
-        off, row_token, token_row = nv.moe_route(i32_dev(self.ids), self.E)
-        blob = nv.repack(u8_dev(self.w), u8_dev(self.s))
-        wts = torch.from_numpy(self.wts).to(DEV)
-        return off, row_token, token_row, blob, wts, act_dev(self.a, self.act), f32_dev(self.g)
-
-
-def _fc2_unfused(c, off, token_row, blob, wts, a, g):
-    y = nv.grouped_gemm(a, off, blob, c.E, c.H, c.I, g)
-    return y, nv.moe_combine(y, token_row, wts)
-
-
-FC2_CASES = [   # (T, E, topk, H, I): R <= 16 E runs the small-M grouped kernel, above it the tile kernel
-    (16, 16, 4, 256, 192),
-    (16, 32, 4, 200, 96),      # H tail (12.5 column units)
-    (256, 16, 4, 256, 192),    # tile grouped kernel
-    (300, 8, 2, 600, 48),      # tile, H tail past two 256-column groups
-    (1, 4, 1, 16, 64),         # one token, one slot
-    (7, 8, 8, 40, 32),         # every expert in each token's top-k
-]
-
-
-@pytest.mark.parametrize("act", ["bf16", "f16"])
-@pytest.mark.parametrize("T,E,topk,H,I", FC2_CASES)
-def test_fc2_combine_equals_unfused_chain_and_oracle(T, E, topk, H, I, act):
-    """FC2 with the combine in its epilogue equals grouped GEMM + nvfp4_moe_combine bitwise (the same fp32 sum in
-    slot order over the same rounded FC2 outputs); the unfused FC2 and combine are checked against the oracle."""
-    c = Fc2Case(T, E, topk, H, I, seed=T * 7 + H + I, act=act)
-    say(f"fused FC2 combine T={T} E={E} k={topk} H={H} I={I} act={act}")
-    off, row_token, token_row, blob, wts, a, g = c.dev()
-    y, ref = _fc2_unfused(c, off, token_row, blob, wts, a, g)
-    ctr = torch.zeros(int(nv.lib().nvfp4_moe_fc2_combine_counters(T, H)), dtype=torch.int32, device=DEV)
-    out = nv.moe_fc2_combine(a, off, row_token, token_row, wts, blob, E, H, I, g, counters=ctr)
-    torch.cuda.synchronize()
-    assert out.dtype == a.dtype and out.shape == (T, H)
-    assert torch.equal(out, ref)
-    assert int(ctr.abs().sum()) == 0                                           # counters left zeroed
-    r_off, _, r_tr = oracle.moe_route(c.ids, E)
-    ref_y = (oracle.grouped_gemm if act == "bf16" else oracle.grouped_gemm_f16)(c.a, r_off, c.w, c.s, c.g)
-    ok, info = oracle.accept(to_f64(y), ref_y, out=act)
-    assert ok, ("fc2", info)
-    # small outputs: each element within the rounding interval of the fp32 bound of k fused multiply-adds
-    yb = bits16(y)
-    slack = (topk + 1) * 2.0 ** -24 * oracle.combine(yb & 0x7FFF, r_tr, np.abs(c.wts), act)
-    ok, info = oracle.accept(to_f64(out), oracle.combine(yb, r_tr, c.wts, act), out=act, slack=slack)
-    assert ok, ("combine", info)
-
-
-@pytest.mark.parametrize("act", ["bf16", "f16"])
-def test_fc2_combine_workspace_reuse(act):
-    """One workspace and one counter array over calls of different shapes in a row (tile path, small-M, a larger
-    tile call, other H and k): each equals the unfused chain, so every call found its counters zeroed by the one
-    before, whatever the earlier calls wrote through the workspace."""
-    E, I = 16, 128
-    cases = [Fc2Case(T, E, topk, H, I, seed=50 + T + H, act=act)
-             for T, topk, H in ((256, 4, 272), (16, 4, 272), (300, 4, 272), (40, 8, 1000), (300, 2, 64))]
-    L = nv.lib()
-    ws = torch.full((max(int(L.nvfp4_moe_fc2_combine_workspace_bytes(c.T, c.topk, E, c.H, I)) for c in cases),),
-                    0x5A, dtype=torch.uint8, device=DEV)
-    ctr = torch.zeros(max(int(L.nvfp4_moe_fc2_combine_counters(c.T, c.H)) for c in cases), dtype=torch.int32,
-                      device=DEV)
-    for c in cases:
-        say(f"fused FC2 combine, shared buffers T={c.T} k={c.topk} H={c.H} act={act}")
-        off, row_token, token_row, blob, wts, a, g = c.dev()
-        _, ref = _fc2_unfused(c, off, token_row, blob, wts, a, g)
-        out = nv.moe_fc2_combine(a, off, row_token, token_row, wts, blob, E, c.H, I, g, workspace_buf=ws,
-                                 counters=ctr)
-        torch.cuda.synchronize()
-        assert torch.equal(out, ref), (c.T, c.topk, c.H)
-        assert int(ctr.abs().sum()) == 0
-
-
-@pytest.mark.parametrize("T", [16, 2048])
-def test_fc2_combine_at_benchmark_size(T):
-    """E = 128, top-8, hidden 2048, I = 768: bitwise against the unfused chain; sampled combined outputs against
-    the oracle (each sample's k FC2 outputs computed on their own, rounded to bf16, then summed)."""
-    E, topk, H, I = 128, 8, 2048, 768
-    c = Fc2Case(T, E, topk, H, I, seed=2004 + T)
-    say(f"fused FC2 combine benchmark size T={T} R={T * topk}")
-    off, row_token, token_row, blob, wts, a, g = c.dev()
-    _, ref = _fc2_unfused(c, off, token_row, blob, wts, a, g)
-    out = nv.moe_fc2_combine(a, off, row_token, token_row, wts, blob, E, H, I, g)
-    out2 = nv.moe_fc2_combine(a, off, row_token, token_row, wts, blob, E, H, I, g)
-    torch.cuda.synchronize()
-    assert torch.equal(out, ref)
-    assert torch.equal(out2, ref)
-    r_off, _, r_tr = oracle.moe_route(c.ids, E)
-    rg = synth.rng(T + 5)
-    toks, cols = rg.integers(0, T, 64), rg.integers(0, H, 64)
-    rows = r_tr.reshape(T, topk)[toks]                                          # [samples, k] grouped rows
-    yk = oracle.grouped_gemm_sampled(c.a, r_off, c.w, c.s, c.g, False, None, rows.reshape(-1),
-                                     np.repeat(cols, topk))
-    yb = oracle.round_bf16_np(yk).reshape(-1, topk)
-    expect = (c.wts[toks].astype(np.float64) * yb).sum(axis=1)
-    ok, info = oracle.accept(to_f64(out)[toks, cols], expect)
-    assert ok, info

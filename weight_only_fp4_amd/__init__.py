@@ -113,12 +113,6 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_w4a16_grouped_gemm_variant.argtypes = [P, I64, I64, P, P, P, P, P, I, I, P, I64, I64, I64, I64, I64,
                                                        I, I, I, P]
         L.nvfp4_w4a16_grouped_gemm_variant.restype = I
-        L.nvfp4_moe_fc2_combine_workspace_bytes.argtypes = [I64, I64, I64, I64, I64]
-        L.nvfp4_moe_fc2_combine_workspace_bytes.restype = I64
-        L.nvfp4_moe_fc2_combine_counters.argtypes, L.nvfp4_moe_fc2_combine_counters.restype = [I64, I64], I64
-        for f in (L.nvfp4_moe_fc2_combine, L.nvfp4_moe_fc2_combine_f16):
-            f.argtypes = [P, I64, P, P, P, P, P, P, I, P, I64, I64, I64, I64, I64, I64, P, I64, P, I64, P]
-            f.restype = I
         _lib = L
     return _lib
 
@@ -515,37 +509,6 @@ def moe_fc1(x, row_token, expert_offsets, blob, E, I, K, global_scales, activati
     _check(fn(_ptr(x), x.stride(0), T, _ptr(row_token), _ptr(expert_offsets), _ptr(pre_scale), _ptr(blob),
               _ptr(global_scales), int(bool(divisor)), int(activation), _ptr(out), out.stride(0), R, E, I, K,
               _stream(x.device)))
-    return out
-
-
-def moe_fc2_combine(a, expert_offsets, row_token, token_row, topk_weights, blob, E, H, I, global_scales,
-                    divisor=False, out=None, workspace_buf=None, counters=None):
-    """FC2 with the top-k combine in its epilogue: a [T k, I] (grouped rows) -> out [T, H] (a's type).
-    workspace_buf: uint8 of moe_fc2_combine_workspace_bytes, any contents; counters: int32 of
-    moe_fc2_combine_counters(T, H) entries, zero-filled once (every call leaves them zero)."""
-    dt = _act_dtype("a", a)
-    _dev("a", a, dt, 2)
-    for name, t in (("expert_offsets", expert_offsets), ("row_token", row_token), ("token_row", token_row)):
-        _dev(name, t, torch.int32, 1)
-    _dev("topk_weights", topk_weights, torch.float32, 2)
-    T, k = topk_weights.shape
-    if a.shape != (T * k, I) or row_token.shape[0] != T * k or token_row.shape[0] != T * k:
-        raise ValueError(f"a must be [{T * k}, {I}] and the routing arrays hold {T * k} rows")
-    if out is None:
-        out = torch.empty((T, H), dtype=dt, device=a.device)
-    need = int(lib().nvfp4_moe_fc2_combine_workspace_bytes(T, k, E, H, I))
-    if need < 0:
-        raise ValueError(f"invalid shape T={T} k={k} E={E} H={H} I={I}")
-    if workspace_buf is None:
-        workspace_buf = torch.empty(max(need, 1), dtype=torch.uint8, device=a.device)
-    if counters is None:
-        counters = torch.zeros(max(int(lib().nvfp4_moe_fc2_combine_counters(T, H)), 1), dtype=torch.int32,
-                               device=a.device)
-    _dev("counters", counters, torch.int32, 1)
-    fn = lib().nvfp4_moe_fc2_combine_f16 if dt == torch.float16 else lib().nvfp4_moe_fc2_combine
-    _check(fn(_ptr(a), a.stride(0), _ptr(expert_offsets), _ptr(row_token), _ptr(token_row), _ptr(topk_weights),
-              _ptr(blob), _ptr(global_scales), int(bool(divisor)), _ptr(out), out.stride(0), T, k, E, H, I,
-              _ptr(workspace_buf), workspace_buf.numel(), _ptr(counters), counters.numel(), _stream(a.device)))
     return out
 
 

@@ -13,15 +13,15 @@ namespace {
 
 constexpr bool kF16 = NVFP4_ACT_F16 != 0;
 
-template <int MG, int NT, int W, int D, bool GROUPED, int ACT = kActNone, bool COMBINE = false>
+template <int MG, int NT, int W, int D, bool GROUPED, int ACT = kActNone>
 void launch_small_t(const SmallShape& s, const Layout& L, const GemmArgs& a) {
     const BlobView bv = make_view(L, a.blob);
     const dim3 grid((unsigned)s.groups, GROUPED ? (unsigned)L.E : 1u, (unsigned)s.S);
     const int64_t rows = GROUPED ? 0 : a.rows;
 #define NVFP4_SMALL_LAUNCH(KF, PRE)                                                                                \
-    hipLaunchKernelGGL((k_gemm_small_m<MG, NT, W, D, GROUPED, KF, kF16, PRE, ACT, COMBINE>), grid, dim3(W * 64), 0,  \
-                       a.st, a.x, a.ld_x, bv, (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, a.gs, a.g_div, a.y, a.ld_y,  \
-                       rows, a.offsets, a.sk, a.row_index, a.pre, a.cmb)
+    hipLaunchKernelGGL((k_gemm_small_m<MG, NT, W, D, GROUPED, KF, kF16, PRE, ACT>), grid, dim3(W * 64), 0, a.st,   \
+                       a.x, a.ld_x, bv, (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, a.gs, a.g_div, a.y, a.ld_y, rows, \
+                       a.offsets, a.sk, a.row_index, a.pre)
     if (L.K % kChunkK == 0) {
         if (a.pre) NVFP4_SMALL_LAUNCH(true, true);
         else NVFP4_SMALL_LAUNCH(true, false);
@@ -41,19 +41,16 @@ nvfp4_status launch_small(const SmallShape& s, const Layout& L, const GemmArgs& 
     if (grouped) {
         if ((a.act == kActSiluGlu) != (s.nt == 2))
             return fail(NVFP4_ERR_INVALID_ARG, "small-M GEMM: the gated epilogue takes unit pairs");
-#define NVFP4_SMALL_GROUPED(NT, ACT, CMB)                                        \
-    switch (s.w) {                                                             \
-        case 1: launch_small_t<0, NT, 1, 4, true, ACT, CMB>(s, L, a); break;   \
-        case 2: launch_small_t<0, NT, 2, 4, true, ACT, CMB>(s, L, a); break;   \
-        case 4: launch_small_t<0, NT, 4, 4, true, ACT, CMB>(s, L, a); break;   \
-        default: launch_small_t<0, NT, 8, 4, true, ACT, CMB>(s, L, a); break;  \
+#define NVFP4_SMALL_GROUPED(NT, ACT)                                        \
+    switch (s.w) {                                                        \
+        case 1: launch_small_t<0, NT, 1, 4, true, ACT>(s, L, a); break;   \
+        case 2: launch_small_t<0, NT, 2, 4, true, ACT>(s, L, a); break;   \
+        case 4: launch_small_t<0, NT, 4, 4, true, ACT>(s, L, a); break;   \
+        default: launch_small_t<0, NT, 8, 4, true, ACT>(s, L, a); break;  \
     }
-        if (a.cmb.counters != nullptr && a.act != kActNone)
-            return fail(NVFP4_ERR_INVALID_ARG, "small-M GEMM: the combine follows a plain FC2");
-        if (a.act == kActSiluGlu) NVFP4_SMALL_GROUPED(2, kActSiluGlu, false)
-        else if (a.act == kActRelu2) NVFP4_SMALL_GROUPED(1, kActRelu2, false)
-        else if (a.cmb.counters != nullptr) NVFP4_SMALL_GROUPED(1, kActNone, true)
-        else NVFP4_SMALL_GROUPED(1, kActNone, false)
+        if (a.act == kActSiluGlu) NVFP4_SMALL_GROUPED(2, kActSiluGlu)
+        else if (a.act == kActRelu2) NVFP4_SMALL_GROUPED(1, kActRelu2)
+        else NVFP4_SMALL_GROUPED(1, kActNone)
 #undef NVFP4_SMALL_GROUPED
         done = true;
     } else {

@@ -14,15 +14,15 @@ namespace {
 
 constexpr bool kF16 = NVFP4_ACT_F16 != 0;
 
-template <int MS, int NT, int UW, int KW, int D, bool GROUPED, int ACT = kActNone, bool COMBINE = false>
+template <int MS, int NT, int UW, int KW, int D, bool GROUPED, int ACT = kActNone>
 void launch_tile_t(const TileShape& t, const Layout& L, const GemmArgs& a) {
     const BlobView bv = make_view(L, a.blob);
     const dim3 grid((unsigned)t.groups, (unsigned)t.mtiles, (unsigned)t.S);
     const int64_t rows = GROUPED ? 0 : a.rows;
 #define NVFP4_TILE_LAUNCH(KF, PRE)                                                                                      \
-    hipLaunchKernelGGL((k_gemm_tile<MS, NT, UW, KW, D, GROUPED, KF, kF16, PRE, ACT, COMBINE>), grid,              \
-                       dim3(UW * KW * 64), 0, a.st, a.x, a.ld_x, bv, (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, a.gs,  \
-                       a.g_div, a.y, a.ld_y, rows, a.offsets, (int)L.E, a.sk, a.row_index, a.pre, a.cmb)
+    hipLaunchKernelGGL((k_gemm_tile<MS, NT, UW, KW, D, GROUPED, KF, kF16, PRE, ACT>), grid, dim3(UW * KW * 64), 0,  \
+                       a.st, a.x, a.ld_x, bv, (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, a.gs, a.g_div, a.y, a.ld_y, rows,  \
+                       a.offsets, (int)L.E, a.sk, a.row_index, a.pre)
     if (L.K % kChunkK == 0) {
         if (a.pre) NVFP4_TILE_LAUNCH(true, true);
         else NVFP4_TILE_LAUNCH(true, false);
@@ -44,11 +44,8 @@ nvfp4_status launch_tile(const TileShape& t, const Layout& L, const GemmArgs& a,
         // four units per wave (gate / up pairs stay in one wave), a 3-deep ring
         // (MoE T = 2048 FC1 / FC2: 188 / 113 us against 194 / 117 us with 2 deep;
         // deeper, narrower, shorter or taller tiles measured slower)
-        if (a.cmb.counters != nullptr && a.act != kActNone)
-            return fail(NVFP4_ERR_INVALID_ARG, "tile GEMM: the combine follows a plain FC2");
         if (a.act == kActSiluGlu) launch_tile_t<4, 4, 4, 1, 3, true, kActSiluGlu>(t, L, a);
         else if (a.act == kActRelu2) launch_tile_t<4, 4, 4, 1, 3, true, kActRelu2>(t, L, a);
-        else if (a.cmb.counters != nullptr) launch_tile_t<4, 4, 4, 1, 3, true, kActNone, true>(t, L, a);
         else launch_tile_t<4, 4, 4, 1, 3, true>(t, L, a);
     } else {
         if (t.ms == 1) launch_tile_t<1, 1, 4, 4, 2, false>(t, L, a);

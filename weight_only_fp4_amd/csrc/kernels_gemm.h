@@ -29,7 +29,6 @@
 // form reads expert_offsets on the device: one grid slice per expert, and
 // slices of experts without rows exit at once, so they read no weight bytes.
 #pragma once
-#include "combine.h"
 #include "decode.h"
 #include "layout.h"
 
@@ -75,66 +74,6 @@ __device__ __forceinline__ bool split_arrive(int* counters, int64_t tile, int S,
     }
     __syncthreads();
     return *s_flag == S - 1;
-}
-
-// Top-k combine fused into the epilogue of FC2 (grouped form): out[t, c] =
-// RNE(sum_j wt[t, j] * y[token_row[t k + j], c]), j = 0 .. k - 1 in slot
-// order, with y the FC2 output rounded to the activation type.  The k rows of
-// a token come from k experts, so from k workgroups of the same column block:
-// each stores its rows of y at device scope (the exchange buffer), waits for
-// the stores, and bumps the counter of (token, column block) of every row;
-// the workgroup that brings it to k sums the token's k rows for its columns
-// and writes out, and resets the counter.  Sums run in slot order from
-// values as stored, so the result is bitwise that of the standalone combine
-// whichever workgroup arrives last.
-struct CombineArgs {
-    const int32_t* row_token;   // token of grouped row r
-    const int32_t* token_row;   // grouped row of pair t k + j
-    const float* wt;            // routing weights [T][k]
-    uint16_t* out;              // [T][ld_o]
-    int64_t ld_o;
-    int* counters;              // [T][cbs], zero between calls (NULL: no combine)
-    int k, cbs;
-};
-
-// Every thread of the workgroup: this workgroup's rows r0 .. r0 + rows - 1
-// (grouped rows) of column block cb, columns [n0, n0 + cols) clipped to N,
-// have been stored to y at device scope by the calling threads.  Each row
-// counts its arrival on its token's counter for the block; the k-th arrival
-// sums the token's k rows (device-scope loads: they bypass this XCD's L2,
-// which may hold stale copies of lines other XCDs wrote) and resets the
-// counter.  n0, cols and ld_y are multiples of 8 and y's rows hold whole
-// 8-column groups.  s_tok: LDS scratch of `rows` ints.
-template <bool F16>
-__device__ __forceinline__ void combine_block(const CombineArgs& cm, const uint16_t* y, int64_t ld_y, int64_t r0,
-                                              int rows, int cb, int64_t n0, int cols, int64_t N, int* s_tok) {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's stores of y acknowledged
-    __syncthreads();
-    for (int r = threadIdx.x; r < rows; r += blockDim.x) {
-        const int tok = cm.row_token[r0 + r];
-        int* ctr = cm.counters + (int64_t)tok * cm.cbs + cb;
-        const int prev = atomicAdd(ctr, 1);
-        const bool last = prev == cm.k - 1;
-        if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_tok[r] = last ? tok : -1;
-    }
-    __syncthreads();
-    const int per = cols / 8;
-    for (int t = threadIdx.x; t < rows * per; t += blockDim.x) {
-        const int tok = s_tok[t / per];
-        const int64_t n = n0 + (int64_t)(t % per) * 8;
-        if (tok < 0 || n >= N) continue;
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        combine_slots<F16>(cm.token_row, cm.wt, (int64_t)tok * cm.k, cm.k, [&](int row) {
-            const uint64_t* p = reinterpret_cast<const uint64_t*>(y + (int64_t)row * ld_y + n);
-            const uint64_t lo = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const uint64_t hi = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            return make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
-        }, acc);
-        combine_store<F16>(cm.out + (int64_t)tok * cm.ld_o + n, n, N, acc);
-    }
-    __syncthreads();
 }
 
 // ----------------------------------------------------------------- small-M --
@@ -422,26 +361,22 @@ __device__ __forceinline__ void small_m_pass16(const uint16_t* __restrict__ xrow
 // built, so the table build and its barrier run under the load latency.
 // ACT (grouped form): the MoE activation the epilogue applies (kActNone,
 // kActSiluGlu with NT even: each workgroup holds gate / up unit pairs and
-// writes N / 2 columns, kActRelu2).  COMBINE (grouped, kActNone): y is the
-// exchange buffer of the fused top-k combine (combine_block), column block
-// blockIdx.x.
+// writes N / 2 columns, kActRelu2).
 template <int MG, int NT, int W, int D, bool GROUPED, bool KFULL, bool F16 = false, bool PRE = false,
-          int ACT = kActNone, bool COMBINE = false>
+          int ACT = kActNone>
 __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                          int NU, int KC, int K,
                                                          int N, const float* __restrict__ gscale, int g_is_div,
                                                          uint16_t* __restrict__ y, int64_t ld_y, int64_t rows_dense,
                                                          const int32_t* __restrict__ offsets, SplitK sk,
                                                          const int32_t* __restrict__ row_index,
-                                                         const uint16_t* __restrict__ pre, CombineArgs cmb) {
-    static_assert(!COMBINE || (GROUPED && ACT == kActNone), "the combine follows a plain grouped FC2");
+                                                         const uint16_t* __restrict__ pre) {
     constexpr int RLD = NT * 16;
     constexpr int kTileFloats = kSmallRows * RLD;
     constexpr int kPer = (kTileFloats + W * 64 - 1) / (W * 64);   // partial-tile floats per thread
     __shared__ float red[W][kTileFloats];
     __shared__ float2 lut[256];
     __shared__ int s_flag;
-    __shared__ int s_tok[COMBINE ? kSmallRows : 1];
     const int u0 = blockIdx.x * NT;
     const int e = GROUPED ? (int)blockIdx.y : 0;
     int64_t row0 = 0, count = rows_dense;
@@ -502,11 +437,7 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
             const int64_t n = (int64_t)u0 * kUnitN + col;
             uint32_t v = round_out<F16>(scale_acc(gv, acc));
             if constexpr (ACT == kActRelu2) v = round_out<F16>(relu_squared(act_to_f32<F16>(v)));
-            if (n < N) {
-                uint16_t* yp = y + (row0 + p0 + r) * ld_y + n;
-                if constexpr (COMBINE) __hip_atomic_store(yp, (uint16_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                else *yp = (uint16_t)v;
-            }
+            if (n < N) y[(row0 + p0 + r) * ld_y + n] = (uint16_t)v;
         };
         if (S == 1) {
             if constexpr (ACT == kActSiluGlu) {
@@ -535,9 +466,6 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
                     for (int wi = 0; wi < W; ++wi) acc += red[wi][t];
                     store_y(t, acc);
                 }
-                if constexpr (COMBINE)
-                    combine_block<F16>(cmb, y, ld_y, row0 + p0, rows, (int)blockIdx.x, (int64_t)u0 * kUnitN, RLD, N,
-                                       s_tok);
             }
             __syncthreads();
             continue;

@@ -38,9 +38,7 @@
 //   XCD's L2, and an expert's row tiles follow each other there and share its
 //   weights.
 //   ACT: the MoE activation the epilogue applies (decode.h); with
-//   kActSiluGlu a wave's NT (even) units are gate / up pairs.  COMBINE
-//   (grouped, kActNone): y is the exchange buffer of the fused top-k combine
-//   (combine_block in kernels_gemm.h), column block = the column group.
+//   kActSiluGlu a wave's NT (even) units are gate / up pairs.
 #pragma once
 #include "decode.h"
 #include "kernels_gemm.h"
@@ -53,15 +51,14 @@ constexpr int kXcds = 8;        // XCDs of the MI355X: workgroup ids are dealt t
 
 
 template <int MS, int NT, int UW, int KW, int D, bool GROUPED, bool KFULL, bool F16 = false, bool PRE = false,
-          int ACT = kActNone, bool COMBINE = false>
+          int ACT = kActNone>
 __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                             int NU, int KC, int K, int N,
                                                             const float* __restrict__ gscale, int g_is_div,
                                                             uint16_t* __restrict__ y, int64_t ld_y, int64_t rows_dense,
                                                             const int32_t* __restrict__ offsets, int E, SplitK sk,
                                                             const int32_t* __restrict__ row_index,
-                                                            const uint16_t* __restrict__ pre, CombineArgs cmb) {
-    static_assert(!COMBINE || (GROUPED && ACT == kActNone && KW == 1), "the combine follows a plain grouped FC2");
+                                                            const uint16_t* __restrict__ pre) {
     constexpr int W = UW * KW;                                     // waves per workgroup
     // Weights stream past the caches (non-temporal) when one row tile covers
     // all rows (tiles of up to 32 rows, dense): no other workgroup reads the
@@ -80,7 +77,6 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
     __shared__ __attribute__((aligned(16))) uint16_t As[2 * kStage];
     __shared__ float2 lut[256];
     __shared__ int s_map[3];
-    __shared__ int s_tok[COMBINE ? 16 * MS : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -349,20 +345,13 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
                         const int m = ms * 16 + g * 4 + i;
                         uint32_t v = round_out<F16>(scale_acc(gv, acc[ms][j][i]));
                         if constexpr (ACT == kActRelu2) v = round_out<F16>(relu_squared(act_to_f32<F16>(v)));
-                        if (m < rows && n < N) {
-                            uint16_t* yp = y + (row0 + m) * ld_y + n;
-                            if constexpr (COMBINE)
-                                __hip_atomic_store(yp, (uint16_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            else *yp = (uint16_t)v;
-                        }
+                        if (m < rows && n < N) y[(row0 + m) * ld_y + n] = (uint16_t)v;
                     }
                 }
         }
     };
     if (S == 1) {
         if (q == 0) store_y();
-        if constexpr (COMBINE)
-            combine_block<F16>(cmb, y, ld_y, row0, (int)rows, bx, (int64_t)bx * UG * kUnitN, UG * kUnitN, N, s_tok);
         return;
     }
 

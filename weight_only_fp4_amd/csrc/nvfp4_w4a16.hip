@@ -236,8 +236,7 @@ nvfp4_status grouped_gemm(const char* fn, const void* x, int64_t ld_x, const int
                           const int32_t* expert_offsets, const void* pre_scale, const void* w_repacked,
                           const float* global_scales, int global_scale_is_divisor, void* y, int64_t ld_y, int64_t R,
                           int64_t E, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes, void* stream,
-                          bool f16, int mx = 0, int act = kActNone, int variant = 0,
-                          const CombineArgs* cmb = nullptr) {
+                          bool f16, int mx = 0, int act = kActNone, int variant = 0) {
     nvfp4_status s = check_weight_shape(fn, E, N, K, mx);
     if (s != NVFP4_OK) return s;
     // the gated epilogue writes N / 2 columns
@@ -254,15 +253,13 @@ nvfp4_status grouped_gemm(const char* fn, const void* x, int64_t ld_x, const int
                static_cast<const uint16_t*>(pre_scale), SplitK{1, nullptr, nullptr},
                static_cast<hipStream_t>(stream)};
     a.act = act;
-    if (cmb) a.cmb = *cmb;
     // Kernel: few rows per expert on average: the weight stream dominates, the small-M kernel (passes of 16
     // rows); many: the MFMA-bound kernel in 256-row tiles per expert (weights decoded once per expert and tile
     // column); between them the tile kernel (64-row tiles).
     const bool mfma_fits = L.code_bytes() < ((int64_t)1 << 31);
     if (variant == kGroupedAuto) {
         variant = R <= (int64_t)kSmallRows * E ? kGroupedSmall
-                : (mfma_fits && act != kActRelu2 && !cmb && R >= kGroupedMfmaRowsPerExpert * E) ? kGroupedMfma
-                : kGroupedTile;
+                : (mfma_fits && act != kActRelu2 && R >= kGroupedMfmaRowsPerExpert * E) ? kGroupedMfma : kGroupedTile;
     }
     if (variant == kGroupedSmall) {
         const SmallShape sm = small_m_shape(L, R, true, act);
@@ -271,7 +268,6 @@ nvfp4_status grouped_gemm(const char* fn, const void* x, int64_t ld_x, const int
     if (variant == kGroupedMfma) {
         if (!mfma_fits) return fail(NVFP4_ERR_INVALID_ARG, "%s: the MFMA-bound kernel takes blobs below 2 GiB of codes", fn);
         if (act == kActRelu2) return fail(NVFP4_ERR_INVALID_ARG, "%s: the MFMA-bound kernel has no squared-ReLU epilogue", fn);
-        if (cmb) return fail(NVFP4_ERR_INVALID_ARG, "%s: the MFMA-bound kernel has no combine epilogue", fn);
         const hipError_t e = launch_gemm_mfma_grouped(L, a.x, ld_x, row_index, expert_offsets, R, a.blob,
                                                       global_scales, a.g_div, a.y, ld_y, a.pre, act, a.st, f16);
         if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "%s: MFMA GEMM launch failed: %s", fn, hipGetErrorString(e));
@@ -650,82 +646,6 @@ nvfp4_status nvfp4_moe_fc1_f16(const void* x, int64_t ld_x, int64_t T, const int
                                int64_t ld_a, int64_t R, int64_t E, int64_t I, int64_t K, void* stream) {
     return moe_fc1("nvfp4_moe_fc1_f16", x, ld_x, T, row_token, expert_offsets, pre_scale, w_fc1, global_scales,
                    global_scale_is_divisor, activation, a, ld_a, R, E, I, K, stream, true);
-}
-
-// ---- FC2 with the top-k combine in its epilogue.  Two buffers: the counters
-// (one int per token and 16-column unit; they only ever hold arrival counts,
-// which every call returns to zero, so one array serves calls of any shape in
-// turn) and the exchange buffer of FC2's outputs (T k rows of ld_ex 16-bit
-// values, ld_ex = H rounded up to 8; no requirement on its contents).
-static int64_t combine_ld(int64_t H) { return round_up(H, 8); }
-static int64_t combine_counters(int64_t T, int64_t H) { return T * ((H + kUnitN - 1) / kUnitN); }
-
-static nvfp4_status moe_fc2_combine(const char* fn, const void* a, int64_t ld_a, const int32_t* expert_offsets,
-                                    const int32_t* row_token, const int32_t* token_row, const float* topk_weights,
-                                    const void* w_fc2, const float* global_scales, int global_scale_is_divisor,
-                                    void* out, int64_t ld_o, int64_t T, int64_t k, int64_t E, int64_t H, int64_t I,
-                                    void* workspace, int64_t workspace_bytes, int32_t* counters,
-                                    int64_t counter_count, void* stream, bool f16) {
-    if (T < 0 || k < 1 || k > E)
-        return fail(NVFP4_ERR_INVALID_ARG, "%s: T = %lld, k = %lld, E = %lld", fn, (long long)T, (long long)k,
-                    (long long)E);
-    if (T * k >= ((int64_t)1 << 31)) return fail(NVFP4_ERR_INVALID_ARG, "%s: T * k must stay below 2^31", fn);
-    nvfp4_status s = check_weight_shape(fn, E, H, I);
-    if (s != NVFP4_OK) return s;
-    if (ld_o < H) return fail(NVFP4_ERR_INVALID_ARG, "%s: ld_o = %lld < H = %lld", fn, (long long)ld_o, (long long)H);
-    if (T > 0 && (!row_token || !token_row || !topk_weights || !out))
-        return fail(NVFP4_ERR_INVALID_ARG, "%s: NULL routing array or output", fn);
-    if (!aligned(row_token, 4) || !aligned(token_row, 4) || !aligned(topk_weights, 4) || !aligned(out, 2) ||
-        !aligned(counters, 4))
-        return fail(NVFP4_ERR_ALIGNMENT, "%s: misaligned routing array, output or counters", fn);
-    if (T == 0 || H == 0) return ok();
-    const int64_t need = nvfp4_moe_fc2_combine_workspace_bytes(T, k, E, H, I);
-    if (!workspace || workspace_bytes < need)
-        return fail(NVFP4_ERR_BUFFER_TOO_SMALL, "%s: workspace of %lld bytes is below the %lld bytes this call needs",
-                    fn, (long long)workspace_bytes, (long long)need);
-    if (!aligned(workspace, 256)) return fail(NVFP4_ERR_ALIGNMENT, "%s: workspace must be 256-byte aligned", fn);
-    if (!counters || counter_count < combine_counters(T, H))
-        return fail(NVFP4_ERR_BUFFER_TOO_SMALL, "%s: %lld counters are below the %lld this call needs", fn,
-                    (long long)counter_count, (long long)combine_counters(T, H));
-    CombineArgs cmb{row_token, token_row, topk_weights, static_cast<uint16_t*>(out), ld_o, counters, (int)k,
-                    (int)((H + kUnitN - 1) / kUnitN)};
-    return grouped_gemm(fn, a, ld_a, nullptr, expert_offsets, nullptr, w_fc2, global_scales, global_scale_is_divisor,
-                        workspace, combine_ld(H), T * k, E, H, I, nullptr, 0, stream, f16, 0, kActNone, kGroupedAuto,
-                        &cmb);
-}
-
-int64_t nvfp4_moe_fc2_combine_workspace_bytes(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I) {
-    if (T < 0 || k < 1 || k > E || T * k >= ((int64_t)1 << 31) ||
-        check_weight_shape("nvfp4_moe_fc2_combine_workspace_bytes", E, H, I) != NVFP4_OK)
-        return -1;
-    return round_up(T * k * combine_ld(H) * 2, 256);
-}
-
-int64_t nvfp4_moe_fc2_combine_counters(int64_t T, int64_t H) {
-    if (T < 0 || H < 0 || H > (int64_t)1 << 30) return -1;
-    return combine_counters(T, H);
-}
-
-nvfp4_status nvfp4_moe_fc2_combine(const void* a, int64_t ld_a, const int32_t* expert_offsets,
-                                   const int32_t* row_token, const int32_t* token_row, const float* topk_weights,
-                                   const void* w_fc2, const float* global_scales, int global_scale_is_divisor,
-                                   void* out, int64_t ld_o, int64_t T, int64_t k, int64_t E, int64_t H, int64_t I,
-                                   void* workspace, int64_t workspace_bytes, int32_t* counters,
-                                   int64_t counter_count, void* stream) {
-    return moe_fc2_combine("nvfp4_moe_fc2_combine", a, ld_a, expert_offsets, row_token, token_row, topk_weights,
-                           w_fc2, global_scales, global_scale_is_divisor, out, ld_o, T, k, E, H, I, workspace,
-                           workspace_bytes, counters, counter_count, stream, false);
-}
-
-nvfp4_status nvfp4_moe_fc2_combine_f16(const void* a, int64_t ld_a, const int32_t* expert_offsets,
-                                       const int32_t* row_token, const int32_t* token_row, const float* topk_weights,
-                                       const void* w_fc2, const float* global_scales, int global_scale_is_divisor,
-                                       void* out, int64_t ld_o, int64_t T, int64_t k, int64_t E, int64_t H, int64_t I,
-                                       void* workspace, int64_t workspace_bytes, int32_t* counters,
-                                       int64_t counter_count, void* stream) {
-    return moe_fc2_combine("nvfp4_moe_fc2_combine_f16", a, ld_a, expert_offsets, row_token, token_row, topk_weights,
-                           w_fc2, global_scales, global_scale_is_divisor, out, ld_o, T, k, E, H, I, workspace,
-                           workspace_bytes, counters, counter_count, stream, true);
 }
 
 // --------------------------------------------------- no-allocation entry --

@@ -38,7 +38,6 @@ struct GemmArgs {
     SplitK sk;
     hipStream_t st;
     int act = kActNone;         // grouped forms: the MoE activation of the epilogue (decode.h)
-    CombineArgs cmb{};          // grouped forms: the fused top-k combine (cmb.counters NULL: none)
 };
 
 // ---------------------------------------------------------------- small-M --
