@@ -50,7 +50,7 @@ nvfp4_status launch_tile(const TileShape& t, const Layout& L, const GemmArgs& a,
     } else {
         if (t.ms == 1) launch_tile_t<1, 1, 4, 4, 2, false>(t, L, a);
         else if (t.ms == 2) launch_tile_t<2, 1, 4, 2, 4, false>(t, L, a);
-        else if (t.ms == 4 && t.kw == 1) launch_tile_t<4, 4, 8, 1, 3, false>(t, L, a);
+        else if (t.ms == 4 && t.kw == 1) launch_tile_t<4, 4, 8, 1, 4, false>(t, L, a);
         else if (t.ms == 4) launch_tile_t<4, 1, 4, 4, 2, false>(t, L, a);
         else launch_tile_t<8, 2, 8, 1, 2, false>(t, L, a);
     }
