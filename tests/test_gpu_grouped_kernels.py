@@ -167,3 +167,24 @@ def test_grouped_auto_takes_mfma_for_many_rows_per_expert():
     blob = c.blob()
     torch.cuda.synchronize()
     assert torch.equal(c.run(blob, nv.GROUPED_AUTO), c.run(blob, nv.GROUPED_MFMA))
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+@pytest.mark.parametrize("K,pre", [(256, False), (272, True)])
+def test_grouped_small_m_four_row_passes(K, pre, act):
+    """At most one row per expert on average (R <= E) the small-M kernel runs its 4-row form, taking an expert's
+    rows in passes of 4: experts of 9, 5 and 4 rows (three, two and one passes) against the oracle, and the gated
+    SiLU epilogue bitwise against the plain output followed by the standalone SiLU."""
+    rows = [9, 5, 4, 3, 2, 1, 1, 1] + [0] * 24            # R = 26 <= E = 32
+    I = 48
+    c = Experts(rows, 2 * I, K, seed=K + 9 * pre, act=act, pre=pre)
+    say(f"grouped small-M 4-row passes K={K} pre={pre} act={act}")
+    plain = c.run(c.blob(), nv.GROUPED_SMALL_M)
+    auto = c.run(c.blob(), nv.GROUPED_AUTO)
+    fused = c.run(c.blob(gated=True), nv.GROUPED_SMALL_M, nv.MOE_SILU_GLU)
+    ref_silu = nv.moe_silu_mul(plain)
+    torch.cuda.synchronize()
+    assert torch.equal(auto, plain)
+    assert torch.equal(fused, ref_silu)
+    ok, info = oracle.accept(to_f64(plain), c.ref(), out=act)
+    assert ok, info

@@ -41,17 +41,26 @@ nvfp4_status launch_small(const SmallShape& s, const Layout& L, const GemmArgs& 
     if (grouped) {
         if ((a.act == kActSiluGlu) != (s.nt == 2))
             return fail(NVFP4_ERR_INVALID_ARG, "small-M GEMM: the gated epilogue takes unit pairs");
-#define NVFP4_SMALL_GROUPED(NT, ACT)                                        \
-    switch (s.w) {                                                        \
-        case 1: launch_small_t<0, NT, 1, 4, true, ACT>(s, L, a); break;   \
-        case 2: launch_small_t<0, NT, 2, 4, true, ACT>(s, L, a); break;   \
-        case 4: launch_small_t<0, NT, 4, 4, true, ACT>(s, L, a); break;   \
-        default: launch_small_t<0, NT, 8, 4, true, ACT>(s, L, a); break;  \
+#define NVFP4_SMALL_GROUPED_W(MG, NT, D, ACT)                                  \
+    switch (s.w) {                                                            \
+        case 1: launch_small_t<MG, NT, 1, D, true, ACT>(s, L, a); break;      \
+        case 2: launch_small_t<MG, NT, 2, D, true, ACT>(s, L, a); break;      \
+        case 4: launch_small_t<MG, NT, 4, D, true, ACT>(s, L, a); break;      \
+        default: launch_small_t<MG, NT, 8, D, true, ACT>(s, L, a); break;     \
     }
+#define NVFP4_SMALL_GROUPED(NT, ACT)                                           \
+    if (s.mg == 1) {                                                          \
+        NVFP4_SMALL_GROUPED_W(1, NT, (NT == 1 ? 6 : 4), ACT)                  \
+    } else {                                                                  \
+        NVFP4_SMALL_GROUPED_W(0, NT, 4, ACT)                                  \
+    }
+        if ((s.mg != 0 && s.mg != 1) || s.d != (s.mg == 1 && s.nt == 1 ? 6 : 4))
+            return fail(NVFP4_ERR_INVALID_ARG, "small-M GEMM: no grouped kernel for mg=%d d=%d", s.mg, s.d);
         if (a.act == kActSiluGlu) NVFP4_SMALL_GROUPED(2, kActSiluGlu)
         else if (a.act == kActRelu2) NVFP4_SMALL_GROUPED(1, kActRelu2)
         else NVFP4_SMALL_GROUPED(1, kActNone)
 #undef NVFP4_SMALL_GROUPED
+#undef NVFP4_SMALL_GROUPED_W
         done = true;
     } else {
 #define NVFP4_SMALL_DISPATCH(MG, NT, W, D)                             \

@@ -412,8 +412,11 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
         }
     };
 
-    for (int64_t p0 = 0; p0 < count; p0 += kSmallRows) {
-        const int rows = (int)((count - p0) < kSmallRows ? (count - p0) : kSmallRows);
+    // rows per pass: 16 for the dynamic form (MG = 0) and the 16-row form, 4 MG otherwise (a grouped
+    // expert with more rows takes several passes, each streaming its weights again)
+    constexpr int kPass = MG == 0 || MG == 16 ? kSmallRows : 4 * MG;
+    for (int64_t p0 = 0; p0 < count; p0 += kPass) {
+        const int rows = (int)((count - p0) < kPass ? (count - p0) : kPass);
         // grouped row r reads activation row row_index[r] when gathering
         const int32_t* rix = GROUPED && row_index ? row_index + row0 + p0 : nullptr;
         const uint16_t* xrow0 = rix ? x : x + (row0 + p0) * ld_x;
@@ -421,7 +424,7 @@ __global__ void __launch_bounds__(W * 64) k_gemm_small_m(const uint16_t* __restr
             small_m_pass16<NT, D, KFULL, F16, PRE>(xrow0, ld_x, rows, pre, ww, c0, c1, K, lut, red[w], RLD, lane, mid);
         } else if constexpr (MG > 0) {
             small_m_pass<MG, NT, D, KFULL, F16, PRE>(xrow0, ld_x, rows, pre, ww, c0, c1, K, lut, red[w], RLD, lane,
-                                                     mid);
+                                                     mid, rix);
         } else {
             if (rows <= 4)
                 small_m_pass<1, NT, D, KFULL, F16, PRE>(xrow0, ld_x, rows, pre, ww, c0, c1, K, lut, red[w], RLD, lane,
