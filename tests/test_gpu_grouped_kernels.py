@@ -188,3 +188,20 @@ def test_grouped_small_m_four_row_passes(K, pre, act):
     assert torch.equal(fused, ref_silu)
     ok, info = oracle.accept(to_f64(plain), c.ref(), out=act)
     assert ok, info
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_grouped_small_m_four_row_passes_relu2_and_formats(fmt):
+    """The 4-row form (R <= E) with MXFP4 weights and the squared-ReLU epilogue: the plain output against the
+    oracle, and the fused squared ReLU bitwise against the plain output followed by the standalone kernel."""
+    rows = [0, 7, 1, 0, 4, 2, 0, 3] + [0] * 12             # R = 17 <= E = 20
+    c = Experts(rows, 80, 320, seed=3 + len(fmt), fmt=fmt)
+    say(f"grouped small-M 4-row passes, squared ReLU, {fmt}")
+    blob = c.blob()
+    plain = c.run(blob, nv.GROUPED_SMALL_M)
+    fused = c.run(blob, nv.GROUPED_SMALL_M, nv.MOE_RELU2)
+    ref_relu2 = nv.moe_relu2(plain)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, ref_relu2)
+    ok, info = oracle.accept(to_f64(plain), c.ref())
+    assert ok, info
