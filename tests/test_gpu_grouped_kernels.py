@@ -205,3 +205,28 @@ def test_grouped_small_m_four_row_passes_relu2_and_formats(fmt):
     assert torch.equal(fused, ref_relu2)
     ok, info = oracle.accept(to_f64(plain), c.ref())
     assert ok, info
+
+
+@pytest.mark.parametrize("rows", [[3, 0, 9, 1, 2, 0, 1] + [0] * 9,    # R = 16 <= E: the 4-row small-M form
+                                  [40, 0, 300, 17]])
+def test_grouped_nan_scale_codes_propagate(rows):
+    """E4M3 NaN scale bytes (0x7F, 0xFF) in one expert's weight rows make exactly those output columns NaN for that
+    expert's rows, in every grouped kernel (4-row or dynamic small-M, tile, MFMA-bound); every other output matches
+    the oracle."""
+    N, K = 96, 256
+    c = Experts(rows, N, K, seed=len(rows) + sum(rows))
+    bad = [(0, 5, 2, 0x7F), (2, 40, 7, 0xFF), (2, 41, 0, 0x7F)]    # (expert, row n, scale block, byte)
+    for e, n, b, v in bad:
+        c.s[e, n, b] = v
+    say(f"grouped NaN scale codes rows={rows}")
+    blob = c.blob()
+    ref = c.ref()
+    nan = np.zeros(ref.shape, dtype=bool)
+    for e, n, _, _ in bad:
+        nan[c.offsets[e]:c.offsets[e + 1], n] = True
+    assert np.all(np.isnan(ref[nan]))
+    for v in KERNELS:
+        y = to_f64(c.run(blob, v))
+        assert np.array_equal(np.isnan(y), nan), v
+        ok, info = oracle.accept(np.where(nan, 0.0, y), np.where(nan, 0.0, ref))
+        assert ok, (v, info)
