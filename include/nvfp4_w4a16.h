@@ -403,6 +403,22 @@ nvfp4_status mxfp4_w4a16_grouped_gemm_f16(const void* x, int64_t ld_x, const int
                                           const void* pre_scale, const void* w_repacked, void* y, int64_t ld_y,
                                           int64_t R, int64_t E, int64_t N, int64_t K, void* workspace,
                                           int64_t workspace_bytes, void* stream);
+/* The fused MoE FC1 on MXFP4 weights: mxfp4_repack_gated is
+ * nvfp4_repack_gated with E8M0 scales [E][2 I][ld_s], ld_s >= K/32 (K a
+ * multiple of 32), and mxfp4_moe_fc1 is nvfp4_moe_fc1 without global scales,
+ * on a blob from mxfp4_repack_gated (NVFP4_MOE_SILU_GLU) or mxfp4_repack
+ * (NVFP4_MOE_RELU2): bitwise mxfp4_w4a16_grouped_gemm (with the row gather)
+ * followed by nvfp4_moe_silu_mul or nvfp4_moe_relu2.  Errors as those calls. */
+int64_t mxfp4_repack_gated_bytes(int64_t E, int64_t I, int64_t K); /* < 0 if invalid */
+nvfp4_status mxfp4_repack_gated(const uint8_t* w_packed, int64_t ld_w, const uint8_t* w_scale, int64_t ld_s,
+                                int64_t E, int64_t I, int64_t K, int up_first, void* out, int64_t out_bytes,
+                                void* stream);
+nvfp4_status mxfp4_moe_fc1(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
+                           const int32_t* expert_offsets, const void* pre_scale, const void* w_fc1, int activation,
+                           void* a, int64_t ld_a, int64_t R, int64_t E, int64_t I, int64_t K, void* stream);
+nvfp4_status mxfp4_moe_fc1_f16(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
+                               const int32_t* expert_offsets, const void* pre_scale, const void* w_fc1, int activation,
+                               void* a, int64_t ld_a, int64_t R, int64_t E, int64_t I, int64_t K, void* stream);
 /* Test exports: the decoded tile (as nvfp4_dequant_bf16, E8M0 scales) and the
  * dense GEMM with a forced kernel variant (as nvfp4_w4a16_gemm_variant; f16
  * selects fp16 activations and outputs). */

@@ -264,3 +264,33 @@ def test_gated_repack_and_fused_fc1_argument_errors():
     assert fc1(*args(R=0)) == OK                                                      # zero rows: no launch
     st = L.nvfp4_moe_fc1_f16(*args(act=0))
     assert st == INVALID and "nvfp4_moe_fc1_f16" in L.nvfp4_last_error().decode()
+
+
+def test_mxfp4_gated_repack_and_fused_fc1_argument_errors():
+    """mxfp4_repack_gated and mxfp4_moe_fc1 (no global scales) reject bad arguments on the host: K a multiple of 32,
+    I of 16, E8M0 scale rows of at least K/32 bytes; empty calls succeed."""
+    L = nv.lib()
+    assert L.mxfp4_repack_gated_bytes(4, 768, 2048) == L.mxfp4_repack_bytes(4, 1536, 2048)
+    assert L.mxfp4_repack_gated_bytes(4, 100, 2048) == -1                              # I not a multiple of 16
+    assert L.mxfp4_repack_gated_bytes(4, 32, 48) == -1                                 # K not a multiple of 32
+    rg = lambda I=32, K=128, ld_s=4, up=0, out=_p(A), nb=1 << 30: L.mxfp4_repack_gated(
+        _p(A), 64, _p(A), ld_s, 2, I, K, up, out, nb, None)
+    assert rg(I=24) == INVALID and "multiple of 16" in L.nvfp4_last_error().decode()
+    assert rg(up=2) == INVALID and "up_first" in L.nvfp4_last_error().decode()
+    assert rg(K=80) == INVALID and "mxfp4_repack_gated" in L.nvfp4_last_error().decode()
+    assert rg(ld_s=3) == INVALID and "K/32" in L.nvfp4_last_error().decode()
+    assert rg(nb=16) == SMALL
+    assert rg(out=_p(A + 8)) == ALIGN
+    assert rg(I=0) == OK
+    args = lambda **kw: [kw.get(n, d) for n, d in [
+        ("x", _p(A)), ("ld_x", 128), ("T", 16), ("rt", _p(A)), ("off", _p(A)), ("pre", None), ("w", _p(A)),
+        ("act", 1), ("a", _p(A)), ("ld_a", 48), ("R", 32), ("E", 4), ("I", 48), ("K", 128), ("st", None)]]
+    for fc1, name in ((L.mxfp4_moe_fc1, "mxfp4_moe_fc1"), (L.mxfp4_moe_fc1_f16, "mxfp4_moe_fc1_f16")):
+        assert fc1(*args(act=0)) == INVALID and name in L.nvfp4_last_error().decode()
+        assert fc1(*args(I=40, ld_a=40)) == INVALID and "multiple of 16" in L.nvfp4_last_error().decode()
+        assert fc1(*args(K=80, ld_x=80)) == INVALID                                   # K % 32
+        assert fc1(*args(ld_a=40)) == INVALID and "ld_a" in L.nvfp4_last_error().decode()
+        assert fc1(*args(rt=None)) == INVALID and "T = R" in L.nvfp4_last_error().decode()
+        assert fc1(*args(rt=_p(A + 2))) == ALIGN
+        assert fc1(*args(act=2, I=40, ld_a=40, R=0)) == OK                            # relu2: any I; no rows
+        assert fc1(*args(R=0)) == OK

@@ -114,6 +114,70 @@ def test_fused_relu2_equals_unfused_chain(T, E, topk, I, K, act):
     assert ok, info
 
 
+MX_CASES = [   # (T, E, topk, I, K, pre): the 4-row small-M form, the dynamic small-M form, the tile kernel
+    (3, 16, 4, 96, 256, False),
+    (16, 16, 4, 192, 288, True),      # K = 288: a K tail of one 32-wide MXFP4 group past 256
+    (256, 16, 4, 192, 256, True),
+]
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+@pytest.mark.parametrize("T,E,topk,I,K,pre", MX_CASES)
+def test_fused_silu_mxfp4_equals_unfused_chain_and_oracle(T, E, topk, I, K, pre, act):
+    """MXFP4 weights (E8M0 scale per 32 K, no global scale): mxfp4_moe_fc1 on either gate / up order equals the
+    MXFP4 grouped GEMM with the gather followed by the standalone SiLU, bitwise; that FC1 output matches the
+    oracle.  Scales stay at or below 2^-3 (with no global scale, larger ones take silu(gate) * up past fp16's
+    range)."""
+    g = synth.rng(T * 7 + I + K)
+    xt = synth.normal_act(g, (T, K), act)
+    w = synth.random_codes(g, (E, 2 * I, K))
+    s = synth.scales_e8m0(g, (E, 2 * I, K // 32), umin=-9, umax=-3)
+    pre_bits = synth.awq_prescale(g, K, act) if pre else None
+    ids = synth.zipf_routing(synth.rng(T * 7 + 1), T, E, topk)
+    r_off, r_rt, _ = oracle.moe_route(ids, E)
+    say(f"fused FC1 SiLU MXFP4 T={T} E={E} k={topk} I={I} K={K} pre={pre} act={act}")
+    off, row_token, _ = nv.moe_route(i32_dev(ids), E)
+    x = act_dev(xt, act)
+    p = None if pre_bits is None else act_dev(pre_bits, act)
+    blob = nv.repack_mxfp4(u8_dev(w), u8_dev(s))
+    gated = nv.repack_gated(u8_dev(w), u8_dev(s), mxfp4=True)
+    gated_uf = nv.repack_gated(u8_dev(_up_first(w)), u8_dev(_up_first(s)), up_first=True, mxfp4=True)
+    h = nv.grouped_gemm_variant(x, row_token, off, blob, E, 2 * I, K, None, nv.GROUPED_AUTO, pre_scale=p,
+                                mxfp4=True)
+    a_ref = nv.moe_silu_mul(h)
+    a = nv.moe_fc1(x, row_token, off, gated, E, I, K, None, nv.MOE_SILU_GLU, pre_scale=p, mxfp4=True)
+    a_uf = nv.moe_fc1(x, row_token, off, gated_uf, E, I, K, None, nv.MOE_SILU_GLU, pre_scale=p, mxfp4=True)
+    torch.cuda.synchronize()
+    assert torch.equal(gated, gated_uf)
+    assert torch.equal(a, a_ref)
+    assert torch.equal(a_uf, a_ref)
+    ref_h = (oracle.grouped_gemm if act == "bf16" else oracle.grouped_gemm_f16)(
+        xt[r_rt], r_off, w, s, np.ones(E, np.float32), False, pre_bits, fmt="mxfp4")
+    ok, info = oracle.accept(to_f64(h), ref_h, out=act)
+    assert ok, ("fc1", info)
+    ok, info = oracle.accept(to_f64(a), oracle.silu_mul(bits16(h), act), out=act)
+    assert ok, ("silu", info)
+
+
+@pytest.mark.parametrize("T", [3, 256])
+def test_fused_relu2_mxfp4_equals_unfused_chain(T):
+    E, topk, I, K = 8, 2, 80, 320
+    g = synth.rng(T + 5)
+    xt = synth.normal_act(g, (T, K), "bf16")
+    w = synth.random_codes(g, (E, I, K))
+    s = synth.scales_e8m0(g, (E, I, K // 32))
+    ids = synth.zipf_routing(synth.rng(T + 6), T, E, topk)
+    say(f"fused FC1 relu2 MXFP4 T={T} E={E} I={I} K={K}")
+    off, row_token, _ = nv.moe_route(i32_dev(ids), E)
+    x = act_dev(xt, "bf16")
+    blob = nv.repack_mxfp4(u8_dev(w), u8_dev(s))
+    h = nv.grouped_gemm_variant(x, row_token, off, blob, E, I, K, None, nv.GROUPED_AUTO, mxfp4=True)
+    a = nv.moe_fc1(x, row_token, off, blob, E, I, K, None, nv.MOE_RELU2, mxfp4=True)
+    ref = nv.moe_relu2(h)
+    torch.cuda.synchronize()
+    assert torch.equal(a, ref)
+
+
 @pytest.mark.parametrize("T", [16, 2048])
 def test_fused_silu_at_benchmark_size(T):
     """E = 128, top-8, hidden 2048, I = 768 (the benchmark's MoE layer): bitwise against the unfused chain, and

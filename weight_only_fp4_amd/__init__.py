@@ -110,6 +110,11 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_repack_gated.restype = I
         for f in (L.nvfp4_moe_fc1, L.nvfp4_moe_fc1_f16):
             f.argtypes, f.restype = [P, I64, I64, P, P, P, P, P, I, I, P, I64, I64, I64, I64, I64, P], I
+        L.mxfp4_repack_gated_bytes.argtypes, L.mxfp4_repack_gated_bytes.restype = [I64, I64, I64], I64
+        L.mxfp4_repack_gated.argtypes = L.nvfp4_repack_gated.argtypes
+        L.mxfp4_repack_gated.restype = I
+        for f in (L.mxfp4_moe_fc1, L.mxfp4_moe_fc1_f16):
+            f.argtypes, f.restype = [P, I64, I64, P, P, P, P, I, P, I64, I64, I64, I64, I64, P], I
         L.nvfp4_w4a16_grouped_gemm_variant.argtypes = [P, I64, I64, P, P, P, P, P, I, I, P, I64, I64, I64, I64, I64,
                                                        I, I, I, P]
         L.nvfp4_w4a16_grouped_gemm_variant.restype = I
@@ -171,24 +176,31 @@ def repack(w_packed: torch.Tensor, w_scale: torch.Tensor) -> torch.Tensor:
     return out
 
 
-def repack_gated(w_packed: torch.Tensor, w_scale: torch.Tensor, up_first: bool = False) -> torch.Tensor:
-    """Gated FC1 weights, canonical uint8 [E, 2I, K/2] codes + E4M3 [E, 2I, K/16] scales with the gate projection in
-    rows [0, I) and the up projection in [I, 2I) (up_first: the other way round) -> blob for moe_fc1 (its 16-row
-    units alternate gate / up)."""
+def repack_gated(w_packed: torch.Tensor, w_scale: torch.Tensor, up_first: bool = False,
+                 mxfp4: bool = False) -> torch.Tensor:
+    """Gated FC1 weights, canonical uint8 [E, 2I, K/2] codes + E4M3 [E, 2I, K/16] scales (mxfp4: E8M0 [E, 2I, K/32])
+    with the gate projection in rows [0, I) and the up projection in [I, 2I) (up_first: the other way round) -> blob
+    for moe_fc1 (its 16-row units alternate gate / up)."""
     _dev("w_packed", w_packed, torch.uint8, 3)
-    _dev("w_scale", w_scale, (torch.uint8, torch.float8_e4m3fn), 3)
+    _dev("w_scale", w_scale, (torch.uint8, torch.float8_e8m0fnu if mxfp4 else torch.float8_e4m3fn), 3)
     if w_scale.dtype != torch.uint8:
         w_scale = w_scale.view(torch.uint8)
     E, N2, K = w_packed.shape[0], w_packed.shape[1], w_packed.shape[2] * 2
-    if tuple(w_scale.shape) != (E, N2, K // 16) or N2 % 32:
-        raise ValueError(f"w_scale {tuple(w_scale.shape)} must match w_packed {tuple(w_packed.shape)}, 2I a multiple of 32")
+    blk = 32 if mxfp4 else 16
+    if tuple(w_scale.shape) != (E, N2, K // blk) or N2 % 32:
+        raise ValueError(f"w_scale {tuple(w_scale.shape)} must match w_packed {tuple(w_packed.shape)} (one scale per "
+                         f"{blk} K), 2I a multiple of 32")
     for name, t in (("w_packed", w_packed), ("w_scale", w_scale)):
         if t.stride(0) != t.shape[1] * t.stride(1):
             raise ValueError(f"{name}: experts must be stored back to back (stride(0) == N * stride(1))")
-    nbytes = int(lib().nvfp4_repack_gated_bytes(E, N2 // 2, K))
+    pre = "mxfp4" if mxfp4 else "nvfp4"
+    nbytes = int(getattr(lib(), pre + "_repack_gated_bytes")(E, N2 // 2, K))
+    if nbytes < 0:
+        raise ValueError(f"invalid gated weight shape E={E} 2I={N2} K={K} (K a positive multiple of {blk})")
     out = torch.empty(nbytes, dtype=torch.uint8, device=w_packed.device)
-    _check(lib().nvfp4_repack_gated(_ptr(w_packed), w_packed.stride(1), _ptr(w_scale), w_scale.stride(1), E, N2 // 2,
-                                    K, int(bool(up_first)), _ptr(out), nbytes, _stream(w_packed.device)))
+    _check(getattr(lib(), pre + "_repack_gated")(_ptr(w_packed), w_packed.stride(1), _ptr(w_scale), w_scale.stride(1),
+                                                 E, N2 // 2, K, int(bool(up_first)), _ptr(out), nbytes,
+                                                 _stream(w_packed.device)))
     return out
 
 
@@ -477,15 +489,18 @@ def grouped_gemm_variant(x, row_token, expert_offsets, blob, E, N, K, global_sca
 
 
 def moe_fc1(x, row_token, expert_offsets, blob, E, I, K, global_scales, activation=MOE_SILU_GLU, divisor=False,
-            pre_scale=None, out=None):
+            pre_scale=None, out=None, mxfp4=False):
     """FC1 of a MoE layer with its activation in the GEMM epilogue -> a [R, I] (x's type).  activation MOE_SILU_GLU:
-    blob from repack_gated; MOE_RELU2: blob from repack (N = I).  row_token None: x holds the R grouped rows."""
+    blob from repack_gated; MOE_RELU2: blob from repack (N = I).  row_token None: x holds the R grouped rows.
+    mxfp4: a blob from repack_gated(..., mxfp4=True) or repack_mxfp4, with no global scales (global_scales None)."""
     dt = _act_dtype("x", x)
     _dev("x", x, dt, 2)
     _dev("expert_offsets", expert_offsets, torch.int32, 1)
     if expert_offsets.shape[0] != E + 1 or not expert_offsets.is_contiguous():
         raise ValueError(f"expert_offsets must be a contiguous int32 [{E + 1}]")
-    if global_scales.numel() != E:
+    if mxfp4 and global_scales is not None:
+        raise ValueError("MXFP4 weights take no global scales (pass None)")
+    if not mxfp4 and (global_scales is None or global_scales.numel() != E):
         raise ValueError(f"global_scales must hold {E} values")
     if x.shape[1] != K:
         raise ValueError(f"x must be [T, {K}]")
@@ -505,6 +520,11 @@ def moe_fc1(x, row_token, expert_offsets, blob, E, I, K, global_scales, activati
         _dev("out", out, dt, 2)
         if tuple(out.shape) != (R, I):
             raise ValueError(f"out must be [{R}, {I}]")
+    if mxfp4:
+        fn = lib().mxfp4_moe_fc1_f16 if dt == torch.float16 else lib().mxfp4_moe_fc1
+        _check(fn(_ptr(x), x.stride(0), T, _ptr(row_token), _ptr(expert_offsets), _ptr(pre_scale), _ptr(blob),
+                  int(activation), _ptr(out), out.stride(0), R, E, I, K, _stream(x.device)))
+        return out
     fn = lib().nvfp4_moe_fc1_f16 if dt == torch.float16 else lib().nvfp4_moe_fc1
     _check(fn(_ptr(x), x.stride(0), T, _ptr(row_token), _ptr(expert_offsets), _ptr(pre_scale), _ptr(blob),
               _ptr(global_scales), int(bool(divisor)), int(activation), _ptr(out), out.stride(0), R, E, I, K,

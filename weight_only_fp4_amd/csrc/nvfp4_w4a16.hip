@@ -556,12 +556,14 @@ static nvfp4_status grouped_gemm_gather(const char* fn, const void* x, int64_t l
 }
 
 // FC1 of a MoE layer with its activation in the epilogue: gated SiLU on a
-// blob from nvfp4_repack_gated (N = 2 I), or the squared ReLU on a plain
-// blob (N = I); row_token NULL: x holds the R grouped rows.
+// blob from nvfp4_repack_gated / mxfp4_repack_gated (N = 2 I), or the
+// squared ReLU on a plain blob (N = I); row_token NULL: x holds the R
+// grouped rows.  mx: an MXFP4 blob (no global scales).
 static nvfp4_status moe_fc1(const char* fn, const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
                             const int32_t* expert_offsets, const void* pre_scale, const void* w_fc1,
                             const float* global_scales, int global_scale_is_divisor, int activation, void* a,
-                            int64_t ld_a, int64_t R, int64_t E, int64_t I, int64_t K, void* stream, bool f16) {
+                            int64_t ld_a, int64_t R, int64_t E, int64_t I, int64_t K, void* stream, bool f16,
+                            int mx = 0) {
     int act;
     if (activation == NVFP4_MOE_SILU_GLU) act = kActSiluGlu;
     else if (activation == NVFP4_MOE_RELU2) act = kActRelu2;
@@ -576,10 +578,11 @@ static nvfp4_status moe_fc1(const char* fn, const void* x, int64_t ld_x, int64_t
     if (!row_token) {
         if (T != R) return fail(NVFP4_ERR_INVALID_ARG, "%s: without row_token x holds the R grouped rows (T = R)", fn);
         return grouped_gemm(fn, x, ld_x, nullptr, expert_offsets, pre_scale, w_fc1, global_scales,
-                            global_scale_is_divisor, a, ld_a, R, E, N, K, nullptr, 0, stream, f16, 0, act);
+                            global_scale_is_divisor, a, ld_a, R, E, N, K, nullptr, 0, stream, f16, mx, act);
     }
     return grouped_gemm_gather(fn, x, ld_x, T, row_token, expert_offsets, pre_scale, w_fc1, global_scales,
-                               global_scale_is_divisor, a, ld_a, R, E, N, K, nullptr, 0, stream, f16, act);
+                               global_scale_is_divisor, a, ld_a, R, E, N, K, nullptr, 0, stream, f16, act,
+                               kGroupedAuto, mx);
 }
 
 nvfp4_status nvfp4_w4a16_grouped_gemm_gather(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
@@ -742,6 +745,35 @@ int64_t mxfp4_repack_bytes(int64_t E, int64_t N, int64_t K) {
 nvfp4_status mxfp4_repack(const uint8_t* w_packed, int64_t ld_w, const uint8_t* w_scale, int64_t ld_s, int64_t E,
                           int64_t N, int64_t K, void* out, int64_t out_bytes, void* stream) {
     return repack_impl("mxfp4_repack", w_packed, ld_w, w_scale, ld_s, E, N, K, out, out_bytes, stream, 1);
+}
+
+int64_t mxfp4_repack_gated_bytes(int64_t E, int64_t I, int64_t K) {
+    if (I < 0 || I % kUnitN != 0) return -1;
+    return mxfp4_repack_bytes(E, 2 * I, K);
+}
+
+nvfp4_status mxfp4_repack_gated(const uint8_t* w_packed, int64_t ld_w, const uint8_t* w_scale, int64_t ld_s,
+                                int64_t E, int64_t I, int64_t K, int up_first, void* out, int64_t out_bytes,
+                                void* stream) {
+    const char* fn = "mxfp4_repack_gated";
+    if (I < 0 || I % kUnitN != 0)
+        return fail(NVFP4_ERR_INVALID_ARG, "%s: I = %lld must be a non-negative multiple of 16", fn, (long long)I);
+    if (up_first != 0 && up_first != 1) return fail(NVFP4_ERR_INVALID_ARG, "%s: up_first must be 0 or 1", fn);
+    return repack_impl(fn, w_packed, ld_w, w_scale, ld_s, E, 2 * I, K, out, out_bytes, stream, 1, I, up_first);
+}
+
+nvfp4_status mxfp4_moe_fc1(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
+                           const int32_t* expert_offsets, const void* pre_scale, const void* w_fc1, int activation,
+                           void* a, int64_t ld_a, int64_t R, int64_t E, int64_t I, int64_t K, void* stream) {
+    return moe_fc1("mxfp4_moe_fc1", x, ld_x, T, row_token, expert_offsets, pre_scale, w_fc1, nullptr, 0, activation,
+                   a, ld_a, R, E, I, K, stream, false, 1);
+}
+
+nvfp4_status mxfp4_moe_fc1_f16(const void* x, int64_t ld_x, int64_t T, const int32_t* row_token,
+                               const int32_t* expert_offsets, const void* pre_scale, const void* w_fc1, int activation,
+                               void* a, int64_t ld_a, int64_t R, int64_t E, int64_t I, int64_t K, void* stream) {
+    return moe_fc1("mxfp4_moe_fc1_f16", x, ld_x, T, row_token, expert_offsets, pre_scale, w_fc1, nullptr, 0,
+                   activation, a, ld_a, R, E, I, K, stream, true, 1);
 }
 
 nvfp4_status mxfp4_dequant_bf16(const void* w_repacked, int64_t E, int64_t N, int64_t K, void* out, int64_t ld_out,
