@@ -65,10 +65,13 @@ __device__ __forceinline__ void split_scale(float s, float& cvt_scale, float& fa
 }
 
 // Round-to-nearest-even fp32 -> bf16 bit pattern (NaN kept quiet, sign kept).
+// Written as a select, not a branch: the compiler otherwise turns the NaN
+// test into divergent control flow around every rounding.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t rne = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t qnan = ((u >> 16) & 0x8000u) | 0x7FC0u;
+    return (u & 0x7FFFFFFFu) > 0x7F800000u ? qnan : rne;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }

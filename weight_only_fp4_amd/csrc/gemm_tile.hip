@@ -19,17 +19,21 @@ void launch_tile_t(const TileShape& t, const Layout& L, const GemmArgs& a) {
     const BlobView bv = make_view(L, a.blob);
     const dim3 grid((unsigned)t.groups, (unsigned)t.mtiles, (unsigned)t.S);
     const int64_t rows = GROUPED ? 0 : a.rows;
-#define NVFP4_TILE_LAUNCH(KF, PRE)                                                                                      \
-    hipLaunchKernelGGL((k_gemm_tile<MS, NT, UW, KW, D, GROUPED, KF, kF16, PRE, ACT>), grid, dim3(UW * KW * 64), 0,  \
+#define NVFP4_TILE_LAUNCH(KF, PRE, MX)                                                                                  \
+    hipLaunchKernelGGL((k_gemm_tile<MS, NT, UW, KW, D, GROUPED, KF, kF16, PRE, ACT, MX>), grid, dim3(UW * KW * 64), 0, \
                        a.st, a.x, a.ld_x, bv, (int)L.NU, (int)L.KC, (int)L.K, (int)L.N, a.gs, a.g_div, a.y, a.ld_y, rows,  \
                        a.offsets, (int)L.E, a.sk, a.row_index, a.pre)
+#define NVFP4_TILE_LAUNCH_FMT(KF, PRE)                                                                                  \
+    if (L.mx) NVFP4_TILE_LAUNCH(KF, PRE, true);                                                                         \
+    else NVFP4_TILE_LAUNCH(KF, PRE, false)
     if (L.K % kChunkK == 0) {
-        if (a.pre) NVFP4_TILE_LAUNCH(true, true);
-        else NVFP4_TILE_LAUNCH(true, false);
+        if (a.pre) { NVFP4_TILE_LAUNCH_FMT(true, true); }
+        else { NVFP4_TILE_LAUNCH_FMT(true, false); }
     } else {
-        if (a.pre) NVFP4_TILE_LAUNCH(false, true);
-        else NVFP4_TILE_LAUNCH(false, false);
+        if (a.pre) { NVFP4_TILE_LAUNCH_FMT(false, true); }
+        else { NVFP4_TILE_LAUNCH_FMT(false, false); }
     }
+#undef NVFP4_TILE_LAUNCH_FMT
 #undef NVFP4_TILE_LAUNCH
 }
 

@@ -51,7 +51,7 @@ constexpr int kXcds = 8;        // XCDs of the MI355X: workgroup ids are dealt t
 
 
 template <int MS, int NT, int UW, int KW, int D, bool GROUPED, bool KFULL, bool F16 = false, bool PRE = false,
-          int ACT = kActNone>
+          int ACT = kActNone, bool MX = false>
 __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                             int NU, int KC, int K, int N,
                                                             const float* __restrict__ gscale, int g_is_div,
@@ -75,7 +75,6 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
     static_assert(D >= 2, "the ring stages step i + 1 from another slot while refilling step i's");
     static_assert((KW - 1) * UW * kRedTile * 4 <= 2 * kStage * 2, "k-part reduction fits in the stage buffers");
     __shared__ __attribute__((aligned(16))) uint16_t As[2 * kStage];
-    __shared__ float2 lut[256];
     __shared__ int s_map[3];
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
@@ -124,17 +123,18 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
             }
         }
         __syncthreads();
-        e = s_map[0];
+        // the mapping is the same for the whole workgroup: reading it into
+        // scalar registers lets every weight address stay scalar
+        e = __builtin_amdgcn_readfirstlane(s_map[0]);
         if (e < 0) return;   // uniform: past the last item
-        bx = s_map[2];
-        row0 = (int64_t)offsets[e] + (int64_t)s_map[1] * BM;
+        bx = __builtin_amdgcn_readfirstlane(s_map[2]);
+        row0 = (int64_t)offsets[e] + (int64_t)__builtin_amdgcn_readfirstlane(s_map[1]) * BM;
         rows = (int64_t)offsets[e + 1] - row0;
     } else {
         row0 = (int64_t)blockIdx.y * BM;
         rows = rows_dense - row0;
     }
     if (rows > BM) rows = BM;
-    build_scale_table(lut, bv.mx);
 
     // ---- K ranges: split s of the workgroup (grid z), part q of the wave
     const int S = sk.S, s = (int)blockIdx.z;
@@ -231,12 +231,13 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
 
     auto compute = [&](const Slot& b, int buf) {
         const uint16_t* abase = &As[buf * kStage + q * BM * kTileLDA + r * kTileLDA + g * 32];
+        // the lane's two scales (lower and upper 16 k of its 32) as fp32, exact
         float sc[NT][2];
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            const float2 l0 = lut[b.sw[j] & 0xFFu], l1 = lut[(b.sw[j] >> 8) & 0xFFu];
-            sc[j][0] = __uint_as_float(__float_as_uint(l0.x) & 0x7F800000u) * l0.y;
-            sc[j][1] = __uint_as_float(__float_as_uint(l1.x) & 0x7F800000u) * l1.y;
+            const f32x2 sp = scale_pair_f32<MX>(b.sw[j]);
+            sc[j][0] = sp.x;
+            sc[j][1] = sp.y;
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -260,7 +261,7 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
 #pragma unroll
         for (int d = 0; d < D; ++d) load_slot(ring[d], d);
         store_a(0, ring[0], 0);
-        __syncthreads();   // scale table and first activation step ready
+        __syncthreads();   // first activation step ready
         // Step i (ring slot i % D, LDS buffer i & 1): stage step i + 1 into
         // the other buffer, refill the slot with step i + D, contract step i
         // (waves whose part is shorter skip its last step), then one barrier.
@@ -314,43 +315,80 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
     }
 
     const float gv = global_scale_at(gscale, e, g_is_div);
-    // lane (r, g) of a part-0 wave holds rows 16 ms + 4 g + i of column 16 (u_w + j) + r
-    auto store_y = [&]() {
+    // Lane (r, g) of a part-0 wave holds rows 16 ms + 4 g + i of column
+    // 16 (u_w + j) + r.  Output blocks of 16 columns: with kActSiluGlu the
+    // unit pair (u_w + 2 b, u_w + 2 b + 1) (gate, up) gives columns
+    // 16 (u_w / 2 + b) + r of N / 2, otherwise unit u_w + b gives columns
+    // 16 (u_w + b) + r of N.
+    static_assert(ACT != kActSiluGlu || NT % 2 == 0, "gate / up units come in pairs");
+    constexpr int OB = ACT == kActSiluGlu ? NT / 2 : NT;      // 16-column output blocks of a wave
+    const int64_t NO = ACT == kActSiluGlu ? N / 2 : N;        // output columns
+    const int64_t col0 = (int64_t)(ACT == kActSiluGlu ? u_w / 2 : u_w) * kUnitN;
+    auto out_value = [&](int ms, int b, int i) -> uint32_t {
         if constexpr (ACT == kActSiluGlu) {
-            // units u_w + j (even j: gate) and u_w + j + 1 (up) -> output
-            // column 16 (u_w + j) / 2 + r of N / 2
-            static_assert(NT % 2 == 0, "gate / up units come in pairs");
-#pragma unroll
-            for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-                for (int j = 0; j < NT; j += 2) {
-                    const int64_t n = (int64_t)((u_w + j) / 2) * kUnitN + r;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int m = ms * 16 + g * 4 + i;
-                        const float hg = act_to_f32<F16>(round_out<F16>(scale_acc(gv, acc[ms][j][i])));
-                        const float hu = act_to_f32<F16>(round_out<F16>(scale_acc(gv, acc[ms][j + 1][i])));
-                        if (m < rows && n < N / 2)
-                            y[(row0 + m) * ld_y + n] = (uint16_t)round_out<F16>(silu_times(hg, hu));
-                    }
-                }
+            const float hg = act_to_f32<F16>(round_out<F16>(scale_acc(gv, acc[ms][2 * b][i])));
+            const float hu = act_to_f32<F16>(round_out<F16>(scale_acc(gv, acc[ms][2 * b + 1][i])));
+            return round_out<F16>(silu_times(hg, hu));
         } else {
-#pragma unroll
-            for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    const int64_t n = (int64_t)(u_w + j) * kUnitN + r;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int m = ms * 16 + g * 4 + i;
-                        uint32_t v = round_out<F16>(scale_acc(gv, acc[ms][j][i]));
-                        if constexpr (ACT == kActRelu2) v = round_out<F16>(relu_squared(act_to_f32<F16>(v)));
-                        if (m < rows && n < N) y[(row0 + m) * ld_y + n] = (uint16_t)v;
-                    }
-                }
+            uint32_t v = round_out<F16>(scale_acc(gv, acc[ms][b][i]));
+            if constexpr (ACT == kActRelu2) v = round_out<F16>(relu_squared(act_to_f32<F16>(v)));
+            return v;
         }
     };
+    // One 16-bit store per output (any alignment).
+    auto store_y_scalar = [&]() {
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+            for (int b = 0; b < OB; ++b) {
+                const int64_t n = col0 + b * kUnitN + r;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = ms * 16 + g * 4 + i;
+                    const uint32_t v = out_value(ms, b, i);
+                    if (m < rows && n < NO) y[(row0 + m) * ld_y + n] = (uint16_t)v;
+                }
+            }
+    };
+    // Through LDS: a wave stages each 16-row block of its outputs in its own
+    // slice of the (idle) stage buffers and writes it back as 16-byte row
+    // pieces, 8 columns each.  Needs y 16-byte aligned and ld_y and the
+    // output width multiples of 8; the slice is private to the wave, so only
+    // the wave's own LDS accesses are ordered (lgkmcnt) between the phases.
+    constexpr int OC = OB * kUnitN;                 // output columns of a wave
+    constexpr int OLD = OC + 8;                     // 16-bit values per staged row (rows stay 16-byte aligned)
+    constexpr int PPR = OC / 8;                     // 16-byte pieces per row
+    constexpr int PPL = (16 * PPR + 63) / 64;       // pieces per lane and 16-row block
+    static_assert(UW * KW * 16 * OLD <= 2 * kStage, "each wave's 16-row output slice fits in the stage buffers");
+    auto store_y_vec = [&]() {
+        uint16_t* o = &As[w * 16 * OLD];
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+#pragma unroll
+            for (int b = 0; b < OB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[(g * 4 + i) * OLD + b * kUnitN + r] = (uint16_t)out_value(ms, b, i);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int t = 0; t < PPL; ++t) {
+                const int p = lane + 64 * t;
+                if ((16 * PPR) % 64 != 0 && p >= 16 * PPR) break;
+                const int rr = p / PPR, cp = p % PPR;
+                const uint4 v = *reinterpret_cast<const uint4*>(&o[rr * OLD + cp * 8]);
+                const int m = ms * 16 + rr;
+                const int64_t n = col0 + cp * 8;
+                if (m < rows && n < NO) *reinterpret_cast<uint4*>(y + (row0 + m) * ld_y + n) = v;
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read back before the next block's writes
+        }
+    };
+    const bool vec_out = ((reinterpret_cast<uintptr_t>(y) | (uintptr_t)(ld_y * 2)) & 15u) == 0 && NO % 8 == 0;
+    auto store_y = [&]() {
+        if (vec_out) store_y_vec();
+        else store_y_scalar();
+    };
     if (S == 1) {
+        if (KW > 1) __syncthreads();   // the k-part sums have been read from the stage buffers
         if (q == 0) store_y();
         return;
     }
