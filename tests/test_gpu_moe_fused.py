@@ -178,6 +178,32 @@ def test_fused_relu2_mxfp4_equals_unfused_chain(T):
     assert torch.equal(a, ref)
 
 
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+def test_fused_fc1_outputs_any_alignment(act):
+    """The tile kernel's epilogue (16-byte row pieces through LDS for aligned outputs, single values otherwise):
+    the fused SiLU into an output with an odd row stride equals the contiguous output bitwise and leaves its
+    padding alone; the squared ReLU with I = 196 (not a multiple of 8) equals the unfused chain."""
+    T, E, topk, I, K = 256, 16, 4, 192, 256
+    c = Fc1Case(T, E, topk, I, K, seed=77, act=act)
+    say(f"fused FC1 output alignment act={act}")
+    off, row_token, x, _ = c.dev()
+    g = f32_dev(c.g)
+    w, s = u8_dev(c.w), u8_dev(c.s)
+    gated = nv.repack_gated(w, s)
+    a = nv.moe_fc1(x, row_token, off, gated, E, I, K, g, nv.MOE_SILU_GLU)
+    big = torch.full((T * topk, I + 3), 7.0, dtype=x.dtype, device=DEV)
+    nv.moe_fc1(x, row_token, off, gated, E, I, K, g, nv.MOE_SILU_GLU, out=big[:, :I])
+    I2 = 196
+    blob2 = nv.repack(u8_dev(c.w[:, :I2]), u8_dev(c.s[:, :I2]))
+    h2 = nv.grouped_gemm_gather(x, row_token, off, blob2, E, I2, K, g)
+    r2 = nv.moe_fc1(x, row_token, off, blob2, E, I2, K, g, nv.MOE_RELU2)
+    ref2 = nv.moe_relu2(h2)
+    torch.cuda.synchronize()
+    assert torch.equal(big[:, :I], a)
+    assert torch.all(big[:, I:] == 7.0)
+    assert torch.equal(r2, ref2)
+
+
 @pytest.mark.parametrize("T", [16, 2048])
 def test_fused_silu_at_benchmark_size(T):
     """E = 128, top-8, hidden 2048, I = 768 (the benchmark's MoE layer): bitwise against the unfused chain, and

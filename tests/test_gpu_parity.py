@@ -425,6 +425,30 @@ def test_strided_io_and_untouched_padding(variant):
     assert torch.all(ybig[:, 40:] == 5.0)
 
 
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+@pytest.mark.parametrize("M", [10, 20, 70, 200])
+def test_tile_outputs_any_alignment(M, act):
+    """The tile kernel stages its outputs through LDS and writes 16-byte row pieces when the output is 16-byte
+    aligned with a row stride and a width that are multiples of 8, and one value at a time otherwise.  Each row
+    count takes another tile shape.  An output with an odd row stride gives the same bits as a contiguous one and
+    leaves its padding alone; a width that is not a multiple of 8 (N = 1004) matches the oracle."""
+    dt = torch.bfloat16 if act == "bf16" else torch.float16
+    c = synth.dense_case(M, 1000, 384, seed=31 + M, act=act)
+    say(f"tile outputs any alignment M={M} act={act}")
+    d = DenseDev(c)
+    y = d.run(nv.VARIANT_LARGE_M)
+    ybig = torch.full((M, 1003), 7.0, dtype=dt, device=DEV)
+    d.run(nv.VARIANT_LARGE_M, out=ybig[:, :1000])
+    c2 = synth.dense_case(M, 1004, 384, seed=37 + M, act=act)
+    y2 = DenseDev(c2).run(nv.VARIANT_LARGE_M)
+    torch.cuda.synchronize()
+    assert torch.equal(ybig[:, :1000], y)
+    assert torch.all(ybig[:, 1000:] == 7.0)
+    ref = (oracle.gemm if act == "bf16" else oracle.gemm_f16)(c2.x, c2.w, c2.s, c2.g_stored, False, None)
+    ok, info = oracle.accept(to_f64(y2), ref, out=act)
+    assert ok, info
+
+
 def test_nan_scale_codes_propagate():
     """E4M3 NaN scale bytes (0x7F, 0xFF) decode to NaN (read literally): the decoded tile holds NaN exactly on
     their blocks, every output column whose weights hold one is NaN in every variant, and the other columns are
