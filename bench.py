@@ -535,8 +535,8 @@ def sanity_parity(case, y):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1 (the multi-GPU sharding is "
-                                   "described in DESIGN.md and not built)", "n_gpus": args.gpus}), flush=True)
+        print(json.dumps({"error": "the benchmark runs on one GPU: --gpus must be 1 (sharding the GEMM across "
+                                   "GPUs is not implemented)", "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     if args.list:
         print("\n".join(workload_specs()))
