@@ -403,7 +403,8 @@ nvfp4_status mxfp4_w4a16_grouped_gemm_f16(const void* x, int64_t ld_x, const int
                                           const void* pre_scale, const void* w_repacked, void* y, int64_t ld_y,
                                           int64_t R, int64_t E, int64_t N, int64_t K, void* workspace,
                                           int64_t workspace_bytes, void* stream);
-/* The fused MoE FC1 on MXFP4 weights: mxfp4_repack_gated is
+/* The fused MoE FC1 on MXFP4 weights (the weight format of the section above,
+ * in the MoE FC1 that nvfp4_moe_fc1 cites): mxfp4_repack_gated is
  * nvfp4_repack_gated with E8M0 scales [E][2 I][ld_s], ld_s >= K/32 (K a
  * multiple of 32), and mxfp4_moe_fc1 is nvfp4_moe_fc1 without global scales,
  * on a blob from mxfp4_repack_gated (NVFP4_MOE_SILU_GLU) or mxfp4_repack
