@@ -73,12 +73,16 @@ class Workload:
         self.meta, self.bound = meta, bound
 
 
-def dense_bytes(M, N, K, pre):
+def dense_bytes(M, N, K, pre, mxfp4=False):
+    """Algorithmic bytes of one dense call: the weight codes (N K / 2) and scales (one byte per 16 K, MXFP4 one
+    per 32), the activation, the output, the pre-scale and the global scale (NVFP4)."""
+    if mxfp4:
+        return 0.53125 * N * K + 2.0 * M * K + 2.0 * M * N + (2.0 * K if pre else 0.0)
     return 0.5625 * N * K + 2.0 * M * K + 2.0 * M * N + (2.0 * K if pre else 0.0) + 4.0
 
 
 def make_dense(name, M, N, K, *, seed, scales="pow2_mant", g_stored=1.0 / 2688.0, divisor=False, prescale=False,
-               copies=1, host_case=None, f16=False):
+               copies=1, host_case=None, f16=False, mxfp4=False):
     import torch
     import synth
     import weight_only_fp4_amd as nv
@@ -93,28 +97,32 @@ def make_dense(name, M, N, K, *, seed, scales="pow2_mant", g_stored=1.0 / 2688.0
     else:
         x = synth.device_normal_bf16((M, K), seed, dev)
         w = synth.device_codes((N, K // 2), seed + 1, dev)
-        s = synth.device_scales((N, K // 16), seed + 2, scales, dev)
+        s = (synth.device_scales((N, K // 32), seed + 2, "e8m0", dev) if mxfp4
+             else synth.device_scales((N, K // 16), seed + 2, scales, dev))
         pre = synth.device_prescale(K, seed + 3, dev) if prescale else None
         if f16:   # the fp16 form: the same draws, rounded to fp16
             x = x.to(torch.float16)
             pre = None if pre is None else pre.to(torch.float16)
     g = torch.tensor([g_stored], dtype=torch.float32, device=dev)
-    blob = nv.repack(w, s)
+    blob = nv.repack_mxfp4(w, s) if mxfp4 else nv.repack(w, s)
     del w, s
     blobs = [blob] + [blob.clone() for _ in range(copies - 1)]
     y = torch.empty((M, N), dtype=x.dtype, device=dev)
     ws = nv.workspace(nv.gemm_workspace_bytes(M, N, K), dev)
 
     def launch(i):
-        nv.gemm(x, blobs[i % copies], N, K, g, divisor, pre, out=y, workspace_buf=ws)
+        if mxfp4:
+            nv.gemm_mxfp4(x, blobs[i % copies], N, K, pre, out=y, workspace_buf=ws)
+        else:
+            nv.gemm(x, blobs[i % copies], N, K, g, divisor, pre, out=y, workspace_buf=ws)
 
     # the kernel the automatic dispatch runs, as the library reports it
     kernel = nv.VARIANT_KERNELS[nv.gemm_plan(M, N, K)]
     flops = 2.0 * M * N * K
-    ab = dense_bytes(M, N, K, pre is not None)
+    ab = dense_bytes(M, N, K, pre is not None, mxfp4)
     bound = "hbm" if flops / ab < (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) else "mfma"
     meta = {"M": M, "N": N, "K": K, "prescale": pre is not None, "divisor": bool(divisor), "weight_copies": copies,
-            "activation": "f16" if f16 else "bf16"}
+            "activation": "f16" if f16 else "bf16", "weights": "mxfp4" if mxfp4 else "nvfp4"}
     wl = Workload(name, "dense", kernel, ab, flops, launch, copies, meta, bound)
     wl.tensors = dict(x=x, y=y, g=g, blobs=blobs)
     return wl
@@ -275,6 +283,11 @@ def workload_specs():
                                                           seed=1001, g_stored=1 / (448 * 6), copies=16, f16=True),
         "prefill_f16_M4096_N14336_K4096": lambda: make_dense("prefill_f16_M4096_N14336_K4096", 4096, 14336, 4096,
                                                              seed=1002, scales="log_uniform", copies=1, f16=True),
+        # MXFP4 weights (E8M0 scale per 32 K, no global scale) on the same kernels
+        "decode_mxfp4_M16_N14336_K4096": lambda: make_dense("decode_mxfp4_M16_N14336_K4096", 16, 14336, 4096,
+                                                            seed=1001, copies=16, mxfp4=True),
+        "prefill_mxfp4_M4096_N14336_K4096": lambda: make_dense("prefill_mxfp4_M4096_N14336_K4096", 4096, 14336,
+                                                               4096, seed=1002, copies=1, mxfp4=True),
         "moe_fc1_T16": lambda: make_grouped("moe_fc1_T16", 16, "fc1"),
         "moe_fc2_T16": lambda: make_grouped("moe_fc2_T16", 16, "fc2"),
         "moe_fc1_T2048": lambda: make_grouped("moe_fc1_T2048", 2048, "fc1"),

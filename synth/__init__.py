@@ -258,7 +258,11 @@ def device_codes(shape, seed: int, device="cuda") -> torch.Tensor:
 
 
 def device_scales(shape, seed: int, kind: str = "pow2_mant", device="cuda") -> torch.Tensor:
+    """Scale bytes on the device: 'pow2_mant' and 'log_uniform' E4M3 as on the host; 'e8m0' MXFP4 scales
+    2^u, u uniform in [-9, 2] (byte u + 127)."""
     g = _tgen(seed, device)
+    if kind == "e8m0":
+        return (torch.randint(-9, 3, shape, device=device, generator=g) + 127).to(torch.uint8)
     if kind == "pow2_mant":
         u = torch.randint(-4, 3, shape, device=device, generator=g)
         m = torch.randint(0, 8, shape, device=device, generator=g)

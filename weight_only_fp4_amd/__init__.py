@@ -223,15 +223,17 @@ def _act_dtype(name, t):
 
 
 def _gemm_args(x, blob, N, K, global_scale, pre_scale, out, rows_name="M"):
-    """Checks shared by the GEMM calls.  x is bf16 or fp16; pre_scale and out must have x's dtype."""
+    """Checks shared by the GEMM calls.  x is bf16 or fp16; pre_scale and out must have x's dtype; global_scale
+    None for the formats without one (MXFP4)."""
     if not isinstance(x, torch.Tensor) or x.dtype not in _ACT_DTYPES:
         raise ValueError("x must be a bf16 or fp16 tensor")
     dt = x.dtype
     _dev("x", x, dt, 2)
     _dev("blob", blob, torch.uint8, 1)
-    _dev("global_scale", global_scale, torch.float32)
-    if not global_scale.is_contiguous():
-        raise ValueError("global_scale must be contiguous")
+    if global_scale is not None:
+        _dev("global_scale", global_scale, torch.float32)
+        if not global_scale.is_contiguous():
+            raise ValueError("global_scale must be contiguous")
     if x.shape[1] != K:
         raise ValueError(f"x has {x.shape[1]} columns, K = {K}")
     if pre_scale is not None:
@@ -341,8 +343,7 @@ def dequant_mxfp4(blob: torch.Tensor, E: int, N: int, K: int) -> torch.Tensor:
 
 def gemm_variant_mxfp4(x, blob, N, K, pre_scale=None, out=None, workspace_buf=None, variant=VARIANT_AUTO):
     """Y[M, N] = (x (.) pre_scale) . dequant_mxfp4(W)^T in x's dtype (bf16 or fp16), no global scale."""
-    one = torch.ones(1, dtype=torch.float32, device=x.device) if isinstance(x, torch.Tensor) and x.is_cuda else None
-    M, out = _gemm_args(x, blob, N, K, one, pre_scale, out)
+    M, out = _gemm_args(x, blob, N, K, None, pre_scale, out)
     need = gemm_workspace_bytes(M, N, K)
     if need < 0:
         raise ValueError(f"invalid GEMM shape M={M} N={N} K={K}")
@@ -365,8 +366,7 @@ def grouped_gemm_mxfp4(x, expert_offsets, blob, E, N, K, pre_scale=None, out=Non
         raise ValueError(f"expert_offsets must be a contiguous int32 [{E + 1}]")
     if out is None and isinstance(x, torch.Tensor) and x.dtype in _ACT_DTYPES:
         out = torch.zeros((x.shape[0], N), dtype=x.dtype, device=x.device)
-    one = torch.ones(1, dtype=torch.float32, device=x.device)
-    R, out = _gemm_args(x, blob, N, K, one, pre_scale, out)
+    R, out = _gemm_args(x, blob, N, K, None, pre_scale, out)
     fn = lib().mxfp4_w4a16_grouped_gemm_f16 if x.dtype == torch.float16 else lib().mxfp4_w4a16_grouped_gemm
     _check(fn(_ptr(x), x.stride(0), _ptr(expert_offsets), _ptr(pre_scale), _ptr(blob), _ptr(out), out.stride(0), R, E,
               N, K, None, 0, _stream(x.device)))
