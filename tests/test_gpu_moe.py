@@ -35,8 +35,10 @@ def routing(T, k, E, seed):
 
 
 @pytest.mark.parametrize("T,k,E", [(16, 8, 128), (2048, 8, 128), (1, 1, 1), (300, 4, 4), (1500, 2, 1000),
-                                   (7, 5, 5)])
+                                   (7, 5, 5), (5000, 8, 128), (4096, 8, 64)])
 def test_route_bit_exact(T, k, E):
+    """One workgroup (up to 1024 pairs), count + place with the scan folded into place (up to 32 blocks of 1024
+    pairs: T = 2048 and 4096 at k = 8), and count + scan + place (T = 5000 at k = 8: 40 blocks)."""
     say(f"route T={T} k={k} E={E}")
     ids = routing(T, k, E, seed=T + E)
     off, row_token, token_row = nv.moe_route(i32_dev(ids), E)

@@ -19,8 +19,10 @@ constexpr int kRouteMaxExperts = kRouteThreads;     // one expert per thread in 
 //   offsets[e]     = number of pairs with an expert below e (offsets[E] = P),
 //   row_token[r]   = token of grouped row r,
 //   token_row[p]   = grouped row of pair p.
-// Three launches over blocks of kRouteThreads pairs (block b: pairs
-// 1024 b .. 1024 b + 1023, wave w of its workgroup: 64 of them):
+// Launches over blocks of kRouteThreads pairs (block b: pairs
+// 1024 b .. 1024 b + 1023, wave w of its workgroup: 64 of them; one block
+// is one launch of place alone, up to kRouteRawBlocks blocks count + place
+// with the scan done inside place):
 //   count  - per block and expert, the number of pairs (hist[b][e]);
 //   scan   - offsets, and each block's first row per expert
 //            (hist[b][e] = offsets[e] + the pairs of e in blocks before b);
@@ -114,12 +116,19 @@ __global__ void __launch_bounds__(kRouteThreads) k_moe_route_scan(int32_t* __res
 }
 
 // hist == NULL: a single block (P <= kRouteThreads) that also derives the
-// offsets from its own counts, so routing takes one launch.
+// offsets from its own counts, so routing takes one launch.  raw_blocks > 0:
+// hist holds the raw per-block counts of the raw_blocks blocks (no scan
+// launch); every workgroup sums them per expert itself (at most
+// kRouteRawBlocks loads per expert thread), scans the totals into the
+// offsets (workgroup 0 stores them) and adds the counts of the blocks before
+// its own.  Otherwise hist holds each block's first row per expert.
+constexpr int kRouteRawBlocks = 32;
 __global__ void __launch_bounds__(kRouteThreads) k_moe_route_place(const int32_t* __restrict__ ids, int64_t P, int E,
                                                                     const int32_t* __restrict__ hist,
                                                                     int32_t* __restrict__ row_token,
                                                                     int32_t* __restrict__ token_row, int k,
-                                                                    int32_t* __restrict__ offsets) {
+                                                                    int32_t* __restrict__ offsets,
+                                                                    int raw_blocks = 0) {
     __shared__ int cnt[kRouteWaves * kRouteMaxExperts];   // [wave][expert], row stride E
     __shared__ int wsum[kRouteWaves];
     const int tid = threadIdx.x, w = tid >> 6;
@@ -144,9 +153,28 @@ __global__ void __launch_bounds__(kRouteThreads) k_moe_route_place(const int32_t
         first = route_block_scan(tid < E ? total : 0, wsum);
         if (tid < E) offsets[tid] = first;
         if (tid == 0) offsets[E] = (int)P;
+    } else if (raw_blocks > 0) {
+        // expert tid: its total over all blocks and over the blocks before this one
+        int all = 0, before = 0;
+        if (tid < E) {
+            int c2[kRouteRawBlocks];
+#pragma unroll
+            for (int b = 0; b < kRouteRawBlocks; ++b) c2[b] = b < raw_blocks ? hist[(int64_t)b * E + tid] : 0;
+#pragma unroll
+            for (int b = 0; b < kRouteRawBlocks; ++b) {
+                all += c2[b];
+                before += b < (int)blockIdx.x ? c2[b] : 0;
+            }
+        }
+        const int off_e = route_block_scan(tid < E ? all : 0, wsum);
+        if (blockIdx.x == 0) {
+            if (tid < E) offsets[tid] = off_e;
+            if (tid == 0) offsets[E] = (int)P;
+        }
+        first = off_e + before;
     }
     if (tid < E) {
-        int run = hist ? hist[(int64_t)blockIdx.x * E + tid] : first;
+        int run = (hist && raw_blocks == 0) ? hist[(int64_t)blockIdx.x * E + tid] : first;
 #pragma unroll
         for (int ww = 0; ww < kRouteWaves; ++ww) {
             cnt[ww * E + tid] = run;

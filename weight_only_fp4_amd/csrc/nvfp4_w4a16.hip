@@ -854,9 +854,14 @@ nvfp4_status nvfp4_moe_route(const int32_t* topk_ids, int64_t T, int64_t k, int6
         return launched(fn);
     }
     hipLaunchKernelGGL(k_moe_route_count, dim3((unsigned)blocks), dim3(kRouteThreads), 0, st, topk_ids, P, (int)E, hist);
+    if (blocks <= kRouteRawBlocks) {   // the place workgroups scan the raw counts themselves: no scan launch
+        hipLaunchKernelGGL(k_moe_route_place, dim3((unsigned)blocks), dim3(kRouteThreads), 0, st, topk_ids, P, (int)E,
+                           (const int32_t*)hist, row_token, token_row, (int)k, expert_offsets, (int)blocks);
+        return launched(fn);
+    }
     hipLaunchKernelGGL(k_moe_route_scan, dim3(1), dim3(kRouteThreads), 0, st, hist, blocks, (int)E, P, expert_offsets);
     hipLaunchKernelGGL(k_moe_route_place, dim3((unsigned)blocks), dim3(kRouteThreads), 0, st, topk_ids, P, (int)E,
-                       hist, row_token, token_row, (int)k, expert_offsets);
+                       (const int32_t*)hist, row_token, token_row, (int)k, expert_offsets, 0);
     return launched(fn);
 }
 
