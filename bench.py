@@ -170,10 +170,11 @@ def make_grouped(name, T, fc, *, seed=1004, E=128, topk=8):
     return wl
 
 
-def make_moe_layer(name, T, *, seed=1004, E=128, topk=8, hidden=2048, inter=768, fused=True):
+def make_moe_layer(name, T, *, seed=1004, E=128, topk=8, hidden=2048, inter=768, fused=True, mxfp4=False):
     """A whole MoE layer on the device: routing, FC1 with the token gather fused (N = 2 inter) and, when fused,
     the gated SiLU in its epilogue (else a separate SiLU step), FC2 (K = inter), top-k combine.  Weight copies
-    rotate as for the grouped workloads."""
+    rotate as for the grouped workloads.  mxfp4: both projections in MXFP4 (fused form only)."""
+    assert fused or not mxfp4
     import numpy as np
     import torch
     import synth
@@ -182,17 +183,23 @@ def make_moe_layer(name, T, *, seed=1004, E=128, topk=8, hidden=2048, inter=768,
     route = synth.zipf_routing(synth.rng(synth.routing_seed(seed)), T, E, topk)
     counts = np.bincount(route.reshape(-1), minlength=E)
     R, active = T * topk, int(np.count_nonzero(counts))
-    w_bytes = active * 0.5625 * (2 * inter * hidden + hidden * inter)
+    w_bytes = active * (0.53125 if mxfp4 else 0.5625) * (2 * inter * hidden + hidden * inter)
     copies = max(1, -(-(512 << 20) // int(w_bytes)))
     sd = seed * 10 + 5
     ids = torch.from_numpy(route.astype(np.int32)).to(dev)
     x = synth.device_normal_bf16((T, hidden), sd, dev)
     wts = torch.from_numpy(synth.rng(sd + 1).random((T, topk)).astype(np.float32)).to(dev)
-    repack1 = nv.repack_gated if fused else nv.repack
-    b1 = repack1(synth.device_codes((E, 2 * inter, hidden // 2), sd + 2, dev),
-                 synth.device_scales((E, 2 * inter, hidden // 16), sd + 3, "pow2_mant", dev))
-    b2 = nv.repack(synth.device_codes((E, hidden, inter // 2), sd + 4, dev),
-                   synth.device_scales((E, hidden, inter // 16), sd + 5, "pow2_mant", dev))
+    if mxfp4:
+        b1 = nv.repack_gated(synth.device_codes((E, 2 * inter, hidden // 2), sd + 2, dev),
+                             synth.device_scales((E, 2 * inter, hidden // 32), sd + 3, "e8m0", dev), mxfp4=True)
+        b2 = nv.repack_mxfp4(synth.device_codes((E, hidden, inter // 2), sd + 4, dev),
+                             synth.device_scales((E, hidden, inter // 32), sd + 5, "e8m0", dev))
+    else:
+        repack1 = nv.repack_gated if fused else nv.repack
+        b1 = repack1(synth.device_codes((E, 2 * inter, hidden // 2), sd + 2, dev),
+                     synth.device_scales((E, 2 * inter, hidden // 16), sd + 3, "pow2_mant", dev))
+        b2 = nv.repack(synth.device_codes((E, hidden, inter // 2), sd + 4, dev),
+                       synth.device_scales((E, hidden, inter // 16), sd + 5, "pow2_mant", dev))
     blobs = [(b1, b2)] + [(b1.clone(), b2.clone()) for _ in range(copies - 1)]
     v = synth.rng(sd + 6).integers(-2, 3, size=(2, E))
     g1 = torch.tensor((np.exp2(v[0].astype(np.float64)) / 2688.0).astype(np.float32), device=dev)
@@ -214,12 +221,16 @@ def make_moe_layer(name, T, *, seed=1004, E=128, topk=8, hidden=2048, inter=768,
         w1, w2 = blobs[i % copies]
         nv._check(L.nvfp4_moe_route(nv._ptr(ids), T, topk, E, nv._ptr(off), nv._ptr(row_token), nv._ptr(token_row),
                                     nv._ptr(wsr), wsr.numel(), st()))
-        if fused:
-            nv.moe_fc1(x, row_token, off, w1, E, inter, hidden, g1, nv.MOE_SILU_GLU, out=a)
+        if mxfp4:
+            nv.moe_fc1(x, row_token, off, w1, E, inter, hidden, None, nv.MOE_SILU_GLU, out=a, mxfp4=True)
+            nv.grouped_gemm_mxfp4(a, off, w2, E, hidden, inter, out=y2)
         else:
-            nv.grouped_gemm_gather(x, row_token, off, w1, E, 2 * inter, hidden, g1, out=h, workspace_buf=ws1)
-            nv.moe_silu_mul(h, out=a)
-        nv.grouped_gemm(a, off, w2, E, hidden, inter, g2, out=y2, workspace_buf=ws2)
+            if fused:
+                nv.moe_fc1(x, row_token, off, w1, E, inter, hidden, g1, nv.MOE_SILU_GLU, out=a)
+            else:
+                nv.grouped_gemm_gather(x, row_token, off, w1, E, 2 * inter, hidden, g1, out=h, workspace_buf=ws1)
+                nv.moe_silu_mul(h, out=a)
+            nv.grouped_gemm(a, off, w2, E, hidden, inter, g2, out=y2, workspace_buf=ws2)
         nv.moe_combine(y2, token_row, wts, out=out)
 
     # algorithmic bytes of the layer: active weights, the tokens in and out, routing ids and weights
@@ -227,8 +238,9 @@ def make_moe_layer(name, T, *, seed=1004, E=128, topk=8, hidden=2048, inter=768,
     flops = 2.0 * R * hidden * (2 * inter) + 2.0 * R * inter * hidden
     bound = "hbm" if flops / ab < (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9) else "mfma"
     meta = {"E": E, "topk": topk, "T": T, "R": R, "hidden": hidden, "inter": inter, "active_experts": active,
-            "weight_copies": copies, "steps_per_call": "route, FC1 (gather) with the gated SiLU in its epilogue, FC2, "
-                                                       "combine" if fused else "route, FC1 (gather), SiLU, FC2, combine"}
+            "weight_copies": copies, "weights": "mxfp4" if mxfp4 else "nvfp4",
+            "steps_per_call": "route, FC1 (gather) with the gated SiLU in its epilogue, FC2, "
+                              "combine" if fused else "route, FC1 (gather), SiLU, FC2, combine"}
     wl = Workload(name, "moe_layer", "moe_layer", ab, flops, launch, copies, meta, bound)
     wl.tensors = dict(x=x, out=out, blobs=blobs)
     return wl
@@ -294,6 +306,7 @@ def workload_specs():
         "moe_fc2_T2048": lambda: make_grouped("moe_fc2_T2048", 2048, "fc2"),
         "moe_layer_T16": lambda: make_moe_layer("moe_layer_T16", 16),
         "moe_layer_T2048": lambda: make_moe_layer("moe_layer_T2048", 2048),
+        "moe_layer_mxfp4_T2048": lambda: make_moe_layer("moe_layer_mxfp4_T2048", 2048, mxfp4=True),
         "moe_layer_unfused_T16": lambda: make_moe_layer("moe_layer_unfused_T16", 16, fused=False),
         "moe_layer_unfused_T2048": lambda: make_moe_layer("moe_layer_unfused_T2048", 2048, fused=False),
         # the decode weight's size (33,619,972 B) and the LM-head weight's (302,268,420 B); launch shapes from

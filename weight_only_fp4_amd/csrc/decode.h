@@ -47,10 +47,13 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
 // that the NVFP4 loops carry no test of it.
 template <bool MX>
 __device__ __forceinline__ f32x2 scale_pair_f32(uint32_t sp) {
-    if constexpr (MX)
-        return f32x2{e8m0_to_f32(sp), e8m0_to_f32(sp >> 8)};
-    else
+    if constexpr (MX) {
+        // the repack stores the lane's one E8M0 group scale in both bytes: convert it once
+        const float v = e8m0_to_f32(sp);
+        return f32x2{v, v};
+    } else {
         return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sp, 1.0f, false);
+    }
 }
 
 // Split a scale s into the operand handed to the exponent-only conversion
