@@ -157,6 +157,34 @@ __device__ __forceinline__ uint4 decode8(uint32_t codes, float scale) {
     return r;
 }
 
+// Eight E2M1 codes of one dword times a power-of-two scale (an E8M0 value,
+// MXFP4), the scale applied inside the conversion: one operation per two
+// values.  For every E8M0 byte this gives the bits decode8 gives (exact
+// products; 2^-127 and overflow to infinity included), except the NaN code,
+// which is NaN either way but of the other sign (checked over all 16 codes x
+// 256 bytes on the device, bf16 and fp16).
+template <bool F16>
+__device__ __forceinline__ uint4 decode8_pow2(uint32_t codes, float scale) {
+    if constexpr (F16)
+        return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 0)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 1)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 2)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 3)));
+    else
+        return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3)));
+}
+
+// The GEMM kernels' decode of one code dword: E8M0 scales (MX) in the
+// conversion, E4M3 scales by fp32 multiplies.
+template <bool F16, bool MX>
+__device__ __forceinline__ uint4 decode8_fmt(uint32_t codes, float scale) {
+    if constexpr (MX) return decode8_pow2<F16>(codes, scale);
+    else return decode8<F16>(codes, scale);
+}
+
 // Four E2M1 codes (bytes BYTE, BYTE + 1) times 2^exp(cvt_scale) -> four values, exact.
 template <bool F16, int BYTE>
 __device__ __forceinline__ s16x4 decode4_pow2(uint32_t codes, float cvt_scale) {

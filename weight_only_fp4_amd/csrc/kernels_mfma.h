@@ -396,6 +396,22 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
         const int u = d >> 2, e = d & 3;
         const uint32_t cw = t == 0 ? b.cw[u].x : t == 1 ? b.cw[u].y : t == 2 ? b.cw[u].z : b.cw[u].w;
         const float sc = t < 2 ? s0[u] : s1[u];
+        if constexpr (MX) {
+            // E8M0: the scale is applied in the conversion, one operation per dword
+            if (op == 0) {
+                const uint32_t v =
+                    F16 ? (e == 0 ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sc, 0))
+                         : e == 1 ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sc, 1))
+                         : e == 2 ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sc, 2))
+                                  : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sc, 3)))
+                        : (e == 0 ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 0))
+                         : e == 1 ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 1))
+                         : e == 2 ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 2))
+                                  : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 3)));
+                set_dword(nb[u], e, v);
+            }
+            return;
+        }
         if (op == 0) {
             jb.p = e == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0)
                  : e == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1)

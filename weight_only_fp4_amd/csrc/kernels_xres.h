@@ -146,7 +146,7 @@ __global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const uint32_t d = t == 0 ? cv.x : t == 1 ? cv.y : t == 2 ? cv.z : cv.w;
-            acc[u] = mma16<F16>(xr[c][t], decode8<F16>(d, t < 2 ? sc.x : sc.y), acc[u]);
+            acc[u] = mma16<F16>(xr[c][t], decode8_fmt<F16, MX>(d, t < 2 ? sc.x : sc.y), acc[u]);
         }
     }
 
