@@ -148,3 +148,47 @@ def test_grouped_parity(T, E, topk, N, K, act):
     f = oracle.grouped_gemm_f16 if act == "f16" else oracle.grouped_gemm
     ref = f(gc.x, gc.offsets, gc.w, gc.s, None, False, gc.pre, fmt="mxfp4")
     accept_or_fail(to_f64(y), ref, ("mxfp4 grouped", T, E, act))
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+def test_nan_scale_code_propagates_in_every_kernel(act):
+    """The E8M0 NaN code (0xFF) on a 32-wide K group makes exactly its output column NaN in every dense variant
+    (M = 4, 16 and 300 reach the small-M, activation-resident, tile and MFMA-bound kernels) and in the grouped
+    kernels (small-M and tile), for that expert's rows only; every other output matches the oracle.  The kernels
+    apply E8M0 scales inside the E2M1 conversion, so this pins that the NaN code still gives NaN there."""
+    bad = [(3, 0), (17, 5), (40, 7)]                     # (row n, 32-wide K group)
+    for M in (4, 16, 300):
+        c = synth.dense_case(M, 64, 256, seed=91 + M, act=act, fmt="mxfp4")
+        s = c.s.copy()
+        for n, b in bad:
+            s[n, b] = 0xFF
+        c.s = s
+        say(f"mxfp4 nan scale code dense M={M} {act}")
+        x = act_dev(c.x, act)
+        blob = nv.repack_mxfp4(u8_dev(c.w), u8_dev(c.s))
+        ref = (oracle.gemm_f16 if act == "f16" else oracle.gemm)(c.x, c.w, c.s, 1.0, False, None, fmt="mxfp4")
+        nan_cols = sorted({n for n, _ in bad})
+        assert np.all(np.isnan(ref[:, nan_cols]))
+        keep = [n for n in range(c.N) if n not in nan_cols]
+        for v in nv.gemm_variants(M, c.N, c.K):
+            y = to_f64(nv.gemm_variant_mxfp4(x, blob, c.N, c.K, variant=v))
+            assert np.array_equal(np.isnan(y), np.isnan(ref)), (M, v)
+            accept_or_fail(y[:, keep], ref[:, keep], ("mxfp4 nan code", M, act, v))
+    for T in (16, 256):                                  # grouped small-M and tile paths
+        gc = synth.grouped_case(T=T, E=4, topk=2, N=64, K=256, seed=T + 5, act=act, fmt="mxfp4")
+        w_s = gc.s.copy()
+        for n, b in bad:
+            w_s[1, n, b] = 0xFF                          # expert 1 only
+        say(f"mxfp4 nan scale code grouped T={T} {act}")
+        x = act_dev(gc.x, act)
+        off = torch.from_numpy(gc.offsets.astype(np.int32)).to(DEV)
+        blob = nv.repack_mxfp4(u8_dev(gc.w), u8_dev(w_s))
+        y = to_f64(nv.grouped_gemm_mxfp4(x, off, blob, 4, 64, 256))
+        f = oracle.grouped_gemm_f16 if act == "f16" else oracle.grouped_gemm
+        ref = f(gc.x, gc.offsets, gc.w, w_s, None, False, None, fmt="mxfp4")
+        nan = np.zeros(ref.shape, dtype=bool)
+        for n, _ in bad:
+            nan[gc.offsets[1]:gc.offsets[2], n] = True
+        assert np.array_equal(np.isnan(ref), nan)
+        assert np.array_equal(np.isnan(y), nan), T
+        accept_or_fail(np.where(nan, 0.0, y), np.where(nan, 0.0, ref), ("mxfp4 nan code grouped", T, act))
