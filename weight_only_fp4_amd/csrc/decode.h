@@ -177,6 +177,32 @@ __device__ __forceinline__ uint4 decode8_pow2(uint32_t codes, float scale) {
                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3)));
 }
 
+// fp16 decode of E4M3-scaled codes in two operations per two values: the
+// scale's power of two goes into the conversion (its exponent only), its
+// significand factor (1.mmm; the whole scale for zero and NaN, see
+// split_scale) multiplies the fp16 pairs.  e2m1 * 2^exp(s) and e2m1 * s lie in
+// [2^-10, 2688] with at most 6 significant bits, so both are exact in fp16 and
+// the values equal decode8<true>'s (NaN scales give NaN either way).
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+struct HalfScale {
+    float cvt;    // operand of the conversion (its exponent is applied)
+    f16x2v f;     // the significand factor, twice
+};
+__device__ __forceinline__ HalfScale half_scale(float s) {
+    float cs, f;
+    split_scale(s, cs, f);
+    const _Float16 h = (_Float16)f;
+    return HalfScale{cs, f16x2v{h, h}};
+}
+__device__ __forceinline__ uint4 decode8_f16_split(uint32_t codes, const HalfScale& h) {
+    const f16x2v a = __builtin_bit_cast(f16x2v, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, h.cvt, 0)) * h.f;
+    const f16x2v b = __builtin_bit_cast(f16x2v, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, h.cvt, 1)) * h.f;
+    const f16x2v c = __builtin_bit_cast(f16x2v, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, h.cvt, 2)) * h.f;
+    const f16x2v d = __builtin_bit_cast(f16x2v, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, h.cvt, 3)) * h.f;
+    return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+                      __builtin_bit_cast(uint32_t, d));
+}
+
 // The GEMM kernels' decode of one code dword: E8M0 scales (MX) in the
 // conversion, E4M3 scales by fp32 multiplies.
 template <bool F16, bool MX>

@@ -143,10 +143,20 @@ __global__ void __launch_bounds__(W * 64) k_gemm_xres(const uint16_t* __restrict
             sc.x = have ? sc.x : 0.f;
             sc.y = have ? sc.y : 0.f;
         }
+        if constexpr (F16 && !MX) {
+            // fp16 with E4M3 scales: the scale's power of two in the conversion, its significand by fp16 pairs
+            const HalfScale h0 = half_scale(sc.x), h1 = half_scale(sc.y);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint32_t d = t == 0 ? cv.x : t == 1 ? cv.y : t == 2 ? cv.z : cv.w;
-            acc[u] = mma16<F16>(xr[c][t], decode8_fmt<F16, MX>(d, t < 2 ? sc.x : sc.y), acc[u]);
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t d = t == 0 ? cv.x : t == 1 ? cv.y : t == 2 ? cv.z : cv.w;
+                acc[u] = mma16<F16>(xr[c][t], decode8_f16_split(d, t < 2 ? h0 : h1), acc[u]);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t d = t == 0 ? cv.x : t == 1 ? cv.y : t == 2 ? cv.z : cv.w;
+                acc[u] = mma16<F16>(xr[c][t], decode8_fmt<F16, MX>(d, t < 2 ? sc.x : sc.y), acc[u]);
+            }
         }
     }
 
