@@ -369,6 +369,9 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     };
 
     float s0[NT], s1[NT];     // full scales of the lane's two 16-k blocks, per unit
+    // fp16 with E4M3 scales: s0 / s1 hold the conversion operands and these the significand factors (half_scale)
+    f16x2v sf0[NT], sf1[NT];
+    constexpr bool kSplitF16 = F16 && !MX;
 
     f32x4 acc[MS][NT];
 #pragma unroll
@@ -384,6 +387,7 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     struct DwordJob {
         f32x2 p;
         float x, y;
+        uint32_t h;   // kSplitF16: the converted fp16 pair before its factor
     };
     auto set_dword = [](uint4& v, int d, uint32_t val) {
         if (d == 0) v.x = val;
@@ -412,6 +416,19 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
             }
             return;
         }
+        if constexpr (kSplitF16) {
+            // the scale's power of two in the conversion, its significand as a packed fp16 multiply
+            if (op == 0) {
+                jb.h = e == 0 ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sc, 0))
+                     : e == 1 ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sc, 1))
+                     : e == 2 ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sc, 2))
+                              : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sc, 3));
+            } else if (op == 1) {
+                const f16x2v f = t < 2 ? sf0[u] : sf1[u];
+                set_dword(nb[u], e, __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2v, jb.h) * f));
+            }
+            return;
+        }
         if (op == 0) {
             jb.p = e == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0)
                  : e == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1)
@@ -427,8 +444,16 @@ __global__ void __launch_bounds__(kMfmaWN * 64) k_gemm_mfma(const uint16_t* __re
     };
     auto scale_op = [&](const BRegs& b, int u) {   // scales of unit u of chunk b
         const f32x2 v = scale_pair_f32<MX>(scale_pair(b.sw[u], lane));   // E4M3 (E8M0) x 2
-        s0[u] = v.x;
-        s1[u] = v.y;
+        if constexpr (kSplitF16) {
+            const HalfScale h0 = half_scale(v.x), h1 = half_scale(v.y);
+            s0[u] = h0.cvt;
+            s1[u] = h1.cvt;
+            sf0[u] = h0.f;
+            sf1[u] = h1.f;
+        } else {
+            s0[u] = v.x;
+            s1[u] = v.y;
+        }
     };
 
     // ---- activation fragments: group f = MS t + ms reads fragment f + 3

@@ -245,7 +245,8 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 const uint32_t d = t == 0 ? b.cw[j].x : t == 1 ? b.cw[j].y : t == 2 ? b.cw[j].z : b.cw[j].w;
-                bf[j] = decode8_fmt<F16, MX>(d, sc[j][t >> 1]);
+                if constexpr (F16 && !MX) bf[j] = decode8_f16_split(d, half_scale(sc[j][t >> 1]));
+                else bf[j] = decode8_fmt<F16, MX>(d, sc[j][t >> 1]);
             }
 #pragma unroll
             for (int ms = 0; ms < MS; ++ms) {
