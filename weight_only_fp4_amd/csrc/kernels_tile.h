@@ -48,6 +48,7 @@ namespace nvfp4 {
 
 constexpr int kTileLDA = 136;   // bf16 per LDS row of the activation stage (128 + 8 pad)
 constexpr int kXcds = 8;        // XCDs of the MI355X: workgroup ids are dealt to them round robin
+constexpr int kTileScanFastE = 256;   // grouped tile mapping: expert counts up to this scan in registers
 
 
 template <int MS, int NT, int UW, int KW, int D, bool GROUPED, bool KFULL, bool F16 = false, bool PRE = false,
@@ -75,7 +76,7 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
     static_assert(D >= 2, "the ring stages step i + 1 from another slot while refilling step i's");
     static_assert((KW - 1) * UW * kRedTile * 4 <= 2 * kStage * 2, "k-part reduction fits in the stage buffers");
     __shared__ __attribute__((aligned(16))) uint16_t As[2 * kStage];
-    __shared__ int s_map[3];
+    __shared__ int s_map[5];   // expert, its row tile, column group, the expert's first and end row
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -89,37 +90,85 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
         if (tid == 0) s_map[0] = -1;
         __syncthreads();
         if (w == 0) {
-            // prefix scan of the per-expert tile counts: pass 0 counts the
-            // row tiles, pass 1 finds this workgroup's (expert, tile)
-            auto scan = [&](int by) {
+            const int64_t groups = gridDim.x;
+            const int64_t id = (int64_t)blockIdx.y * groups + blockIdx.x;
+            // item of this workgroup once the total is known: items are dealt
+            // to the XCDs in contiguous ranges (id % kXcds picks the range)
+            auto item_of = [&](int total, int64_t& item) {
+                const int64_t items = (int64_t)total * groups, per = (items + kXcds - 1) / kXcds;
+                item = (id % kXcds) * per + id / kXcds;
+                return id / kXcds < per && item < items;
+            };
+            if (E <= kTileScanFastE) {
+                // up to kTileScanFastE experts: every offset is loaded at once
+                // (one memory round trip) and both passes scan registers
+                constexpr int NB = kTileScanFastE / 64;
+                int lo[NB], hi[NB], tl[NB], incl[NB];
+#pragma unroll
+                for (int i = 0; i < NB; ++i) {
+                    const int ex = 64 * i + lane;
+                    lo[i] = ex < E ? offsets[ex] : 0;
+                    hi[i] = ex < E ? offsets[ex + 1] : 0;
+                }
                 int carry = 0;
-                for (int base = 0; base < E; base += 64) {
-                    const int ex = base + lane;
-                    const int cnt = ex < E ? (offsets[ex + 1] - offsets[ex]) : 0;
-                    const int tiles = (cnt + BM - 1) / BM;
-                    int v = tiles;
+#pragma unroll
+                for (int i = 0; i < NB; ++i) {
+                    tl[i] = (hi[i] - lo[i] + BM - 1) / BM;
+                    int v = tl[i];
 #pragma unroll
                     for (int d = 1; d < 64; d <<= 1) {
                         const int t = __shfl_up(v, d);
                         if (lane >= d) v += t;
                     }
-                    const int incl = carry + v, excl = incl - tiles;
-                    if (by >= 0 && tiles > 0 && by >= excl && by < incl) {
-                        s_map[0] = ex;
-                        s_map[1] = by - excl;
-                    }
+                    incl[i] = carry + v;
                     carry += __shfl(v, 63);
                 }
-                return carry;
-            };
-            const int64_t groups = gridDim.x;
-            const int64_t items = (int64_t)scan(-1) * groups;
-            const int64_t id = (int64_t)blockIdx.y * groups + blockIdx.x;
-            const int64_t per = (items + kXcds - 1) / kXcds;
-            const int64_t item = (id % kXcds) * per + id / kXcds;
-            if (id / kXcds < per && item < items) {
-                scan((int)(item / groups));
-                if (lane == 0) s_map[2] = (int)(item % groups);
+                int64_t item;
+                if (item_of(carry, item)) {
+                    const int by = (int)(item / groups);
+#pragma unroll
+                    for (int i = 0; i < NB; ++i) {
+                        const int excl = incl[i] - tl[i];
+                        if (tl[i] > 0 && by >= excl && by < incl[i]) {
+                            s_map[0] = 64 * i + lane;
+                            s_map[1] = by - excl;
+                            s_map[3] = lo[i];
+                            s_map[4] = hi[i];
+                        }
+                    }
+                    if (lane == 0) s_map[2] = (int)(item % groups);
+                }
+            } else {
+                // prefix scan of the per-expert tile counts: pass 0 counts the
+                // row tiles, pass 1 finds this workgroup's (expert, tile)
+                auto scan = [&](int by) {
+                    int carry = 0;
+                    for (int base = 0; base < E; base += 64) {
+                        const int ex = base + lane;
+                        const int lo = ex < E ? offsets[ex] : 0, hi = ex < E ? offsets[ex + 1] : 0;
+                        const int tiles = (hi - lo + BM - 1) / BM;
+                        int v = tiles;
+#pragma unroll
+                        for (int d = 1; d < 64; d <<= 1) {
+                            const int t = __shfl_up(v, d);
+                            if (lane >= d) v += t;
+                        }
+                        const int incl = carry + v, excl = incl - tiles;
+                        if (by >= 0 && tiles > 0 && by >= excl && by < incl) {
+                            s_map[0] = ex;
+                            s_map[1] = by - excl;
+                            s_map[3] = lo;
+                            s_map[4] = hi;
+                        }
+                        carry += __shfl(v, 63);
+                    }
+                    return carry;
+                };
+                int64_t item;
+                if (item_of(scan(-1), item)) {
+                    scan((int)(item / groups));
+                    if (lane == 0) s_map[2] = (int)(item % groups);
+                }
             }
         }
         __syncthreads();
@@ -128,8 +177,8 @@ __global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __re
         e = __builtin_amdgcn_readfirstlane(s_map[0]);
         if (e < 0) return;   // uniform: past the last item
         bx = __builtin_amdgcn_readfirstlane(s_map[2]);
-        row0 = (int64_t)offsets[e] + (int64_t)__builtin_amdgcn_readfirstlane(s_map[1]) * BM;
-        rows = (int64_t)offsets[e + 1] - row0;
+        row0 = (int64_t)__builtin_amdgcn_readfirstlane(s_map[3]) + (int64_t)__builtin_amdgcn_readfirstlane(s_map[1]) * BM;
+        rows = (int64_t)__builtin_amdgcn_readfirstlane(s_map[4]) - row0;
     } else {
         row0 = (int64_t)blockIdx.y * BM;
         rows = rows_dense - row0;
