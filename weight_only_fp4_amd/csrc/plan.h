@@ -258,8 +258,9 @@ inline SplitK split_k(int S, uint8_t* ws, const Workspace& wl) {
 // ---------------------------------------------------------------- launchers --
 // One translation unit per family and activation type (F16) defines each;
 // the activation-resident family has one per scale format (MX) too.  The
-// small-M and tile families read their scales through a table in LDS built
-// for the blob's format, so they take it at run time.
+// small-M family reads its scales through a table in LDS built for the
+// blob's format, and the tile launcher picks the kernel compiled for it, so
+// both take the format at run time.
 template <bool F16>
 nvfp4_status launch_small(const SmallShape& s, const Layout& L, const GemmArgs& a, bool grouped);
 template <bool F16>
