@@ -332,13 +332,24 @@ __device__ __forceinline__ void small_m_pass16(const uint16_t* __restrict__ xrow
         for (int j = 0; j < NT; ++j) {
             const uint32_t sp = scale_pair(s.sw[j], lane);
             const float2 l0 = lut[sp & 0xFFu], l1 = lut[(sp >> 8) & 0xFFu];
-            // the full scale: 2^exponent(conversion operand) times the factor, exact
-            const float s0 = __uint_as_float(__float_as_uint(l0.x) & 0x7F800000u) * l0.y;
-            const float s1 = __uint_as_float(__float_as_uint(l1.x) & 0x7F800000u) * l1.y;
-            acc[j] = mma16<F16>(a[0], decode8<F16>(s.cw[j].x, s0), acc[j]);
-            acc[j] = mma16<F16>(a[1], decode8<F16>(s.cw[j].y, s0), acc[j]);
-            acc[j] = mma16<F16>(a[2], decode8<F16>(s.cw[j].z, s1), acc[j]);
-            acc[j] = mma16<F16>(a[3], decode8<F16>(s.cw[j].w, s1), acc[j]);
+            if constexpr (F16) {
+                // the table's split as is: exponent in the conversion, the factor
+                // (exact in fp16, or 0 / NaN for the special bytes) by fp16 pairs
+                const _Float16 f0 = (_Float16)l0.y, f1 = (_Float16)l1.y;
+                const HalfScale h0{l0.x, f16x2v{f0, f0}}, h1{l1.x, f16x2v{f1, f1}};
+                acc[j] = mma16<F16>(a[0], decode8_f16_split(s.cw[j].x, h0), acc[j]);
+                acc[j] = mma16<F16>(a[1], decode8_f16_split(s.cw[j].y, h0), acc[j]);
+                acc[j] = mma16<F16>(a[2], decode8_f16_split(s.cw[j].z, h1), acc[j]);
+                acc[j] = mma16<F16>(a[3], decode8_f16_split(s.cw[j].w, h1), acc[j]);
+            } else {
+                // the full scale: 2^exponent(conversion operand) times the factor, exact
+                const float s0 = __uint_as_float(__float_as_uint(l0.x) & 0x7F800000u) * l0.y;
+                const float s1 = __uint_as_float(__float_as_uint(l1.x) & 0x7F800000u) * l1.y;
+                acc[j] = mma16<F16>(a[0], decode8<F16>(s.cw[j].x, s0), acc[j]);
+                acc[j] = mma16<F16>(a[1], decode8<F16>(s.cw[j].y, s0), acc[j]);
+                acc[j] = mma16<F16>(a[2], decode8<F16>(s.cw[j].z, s1), acc[j]);
+                acc[j] = mma16<F16>(a[3], decode8<F16>(s.cw[j].w, s1), acc[j]);
+            }
         }
     };
     run_ring<D, Slot16<NT>>(c1 - c0, load, use, mid);
