@@ -53,7 +53,7 @@ constexpr int kTileScanFastE = 256;   // grouped tile mapping: expert counts up 
 
 template <int MS, int NT, int UW, int KW, int D, bool GROUPED, bool KFULL, bool F16 = false, bool PRE = false,
           int ACT = kActNone, bool MX = false>
-__global__ void __launch_bounds__(UW * KW * 64) k_gemm_tile(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
+__global__ void __launch_bounds__(UW * KW * 64, GROUPED ? 2 : 1) k_gemm_tile(const uint16_t* __restrict__ x, int64_t ld_x, BlobView bv,
                                                             int NU, int KC, int K, int N,
                                                             const float* __restrict__ gscale, int g_is_div,
                                                             uint16_t* __restrict__ y, int64_t ld_y, int64_t rows_dense,
