@@ -50,11 +50,12 @@ struct SmallShape {
     int64_t groups;   // workgroups along N (units / nt)
 };
 
-// (mg, nt, w, d) for the dense form; the grouped form is always (0, 1, w, 4).
+// (mg, nt, w, d) for the dense form, exactly the shapes small_m_shape picks;
+// the grouped form is always (0, 1, w, 4).
 #define NVFP4_SMALL_CONFIGS(X) \
     X(1, 1, 1, 4) X(1, 1, 2, 4) X(1, 1, 4, 4) X(1, 1, 8, 4) X(1, 1, 16, 4) X(1, 2, 1, 4) \
-    X(2, 1, 1, 4) X(2, 1, 2, 4) X(2, 1, 4, 4) X(2, 1, 8, 4) X(2, 2, 1, 4) X(2, 2, 2, 4) X(2, 2, 4, 4) X(2, 2, 8, 4) \
-    X(16, 2, 4, 2) X(16, 2, 8, 2) X(16, 4, 4, 2) X(16, 4, 8, 2) X(16, 8, 4, 2) X(16, 8, 8, 2)
+    X(2, 1, 1, 4) X(2, 1, 2, 4) X(2, 1, 4, 4) X(2, 1, 8, 4) X(2, 2, 1, 4) \
+    X(16, 4, 4, 2)
 
 // Is (mg, nt, w, d) one of the compiled dense shapes?
 inline bool small_compiled(const SmallShape& s) {
